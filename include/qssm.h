@@ -1,0 +1,327 @@
+/*
+ * qssm.h — C ABI of libqssm, the quantized state-space scan library for AMD MI355X (gfx950).
+ *
+ * What the library computes (sources, by page title and section):
+ *  - "Quamba2: A Robust and Scalable Post-training Quantization Framework for Selective State
+ *    Space Models", abstract and method summary (offline steps 1-4): 8-bit quantization of the
+ *    input x of the linear recurrence with per-group scales over sorted and clustered channels,
+ *    per-state-group quantization of the input-dependent B and C, weights rearranged offline in
+ *    cluster order so the SSM output is unchanged; W8A8 for Mamba1 and Mamba2 backbones,
+ *    prefill and generation.
+ *  - "Quantizing Small-Scale State-Space Models for Edge AI", abstract: quantized S4D layer;
+ *    the state matrix A and the internal state are the sensitive parts; per-component precision.
+ *  - SSDi8 (post-training quantization for the Mamba-2 structured state-space duality), abstract:
+ *    a persistent INT8 path through the chunked SSD form, with activations quantized at
+ *    cost-effective points.
+ *  - Quamba-SE soft-edge quantization (blog post), sections 2.1, 2.2 and 4.1: a three-scale
+ *    8-bit code (scale/4, scale, scale*4) with the mode in the top bits.
+ *
+ * The recurrence, per channel d and state n:
+ *     h_t = exp(delta_t * A) * h_{t-1} + delta_t * B_t * x_t,     y_t = sum_n C_t * h_t + D * x_t
+ * with int8 x, B, C (dequantized as scale * code), fp32 delta/A/D, a higher-precision state and
+ * a dequantized (fp32 or fp16) output.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller, unless the comment says "host".
+ *    Shapes are row-major (the last index is contiguous). Outputs must not alias inputs.
+ *  - Calls validate their arguments on the host first. On a bad argument they return a
+ *    non-zero qssm_status, launch nothing, and leave a message for qssm_last_error().
+ *  - Launches are asynchronous on the given stream; nothing synchronizes. A device fault shows up
+ *    at the caller's next synchronization. A failed launch returns QSSM_ERR_DEVICE.
+ *  - No C++ exception ever crosses this boundary.
+ *  - The library allocates no device memory. Entry points that need scratch take a caller-provided
+ *    workspace whose size a *_workspace_size call reports.
+ *
+ * Quantization rule used everywhere (int8 codes, bit-exact):
+ *     q = clamp(RNE(v / s), -128, 127)
+ *  where v / s is the exact rational quotient of the fp32 values and RNE rounds half to even.
+ *  NaN encodes as 0; +-Inf saturate. A scale s is valid when it is finite and
+ *  2^-100 <= s <= 2^100; every code of a group whose scale is not valid is 0.
+ */
+#ifndef QSSM_H
+#define QSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSSM_VERSION 100 /* 1.0.0 */
+
+typedef int32_t qssm_status;
+enum {
+  QSSM_OK = 0,
+  QSSM_ERR_INVALID_ARG = 1, /* null required pointer, bad shape, bad enum value */
+  QSSM_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
+  QSSM_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than *_workspace_size */
+  QSSM_ERR_DEVICE = 4       /* the HIP runtime reported an error at launch */
+};
+
+/* Element types of optional-precision buffers. */
+enum { QSSM_F32 = 0, QSSM_F16 = 1, QSSM_I16 = 2 };
+
+/* Encodings of the scan input x. */
+enum {
+  QSSM_X_INT8 = 0,    /* int8 code, value = s[g] * q */
+  QSSM_X_SOFTEDGE = 1 /* three-scale soft-edge byte, see qssm_softedge_encode */
+};
+
+/* ---------------------------------------------------------------------------------------------
+ * a1. Per-group int8 quantization of the scan input x over sorted, clustered channel groups.
+ * Quamba2, abstract and method steps 1-2 (sort and cluster x channels; per-group scales).
+ *
+ * x is viewed as [outer, C, inner] fp32. Output channel c takes input channel perm[c]
+ * (perm == NULL: identity) and belongs to group group_of[c] < G:
+ *     q[o, c, i] = quant(x[o, perm[c], i], scales[group_of[c]])
+ * compute_scales == 0: scales[G] is an input (static, calibrated offline).
+ * compute_scales != 0: scales[G] is an output, computed first on the device from the tensor
+ *     itself: scales[g] = fl32(absmax_g / 127) with absmax_g the largest finite |x| of group g
+ *     (after the permutation); a group with absmax 0 gets scale 1; the result is clamped to
+ *     [2^-100, 2^100].
+ * q: int8 [outer, C, inner]. 1 <= G <= 256, perm must be a permutation of 0..C-1.
+ * Empty tensors (outer, C or inner == 0) are valid and launch nothing (compute_scales then writes
+ * scale 1 for every group).
+ */
+qssm_status qssm_quant_group_x(const float* x, int64_t outer, int64_t C, int64_t inner,
+                               const int32_t* perm, const uint8_t* group_of, int32_t G,
+                               float* scales, int32_t compute_scales, int8_t* q,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * a2. Per-state-group int8 quantization of the input-dependent B or C.
+ * Quamba2, abstract and method step 3 (per-state-group quantization of B and C).
+ *
+ * bc is viewed as [outer, Gbc, N, inner] fp32 (Gbc = number of B/C groups of the model, N = state
+ * size). State n of B/C group g uses scale scales[g * (N / gs) + n / gs]; N % gs == 0.
+ * compute_scales has the same meaning as in qssm_quant_group_x, one scale per (g, state group).
+ * q: int8 [outer, Gbc, N, inner].
+ */
+qssm_status qssm_quant_state_group_BC(const float* bc, int64_t outer, int32_t Gbc, int32_t N,
+                                      int64_t inner, int32_t gs, float* scales,
+                                      int32_t compute_scales, int8_t* q, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * a3. Soft-edge three-scale 8-bit code. Quamba-SE blog, section 2.1 (three modes: scale/4 for
+ * |v| < L, scale for the middle, scale*4 for |v| > H), section 2.2 (classifier and byte layout:
+ * 0xxxxxxx standard, 10xxxxxx small, 11xxxxxx large), section 4.1 (thresholds).
+ *
+ * Per group g with base scale s = s[g] and thresholds L = L[g], H = H[g]:
+ *   small    (|v| < L and not |v| > H): q = clamp(RNE(v / (s/4)), -32, 31), byte = 0x80 | (q & 0x3F)
+ *   large    (|v| > H and not |v| < L): q = clamp(RNE(v / (s*4)), -32, 31), byte = 0xC0 | (q & 0x3F)
+ *   standard (otherwise):               q = clamp(RNE(v / s),     -64, 63), byte = q & 0x7F
+ * NaN encodes as 0x00; +-Inf fall in the large mode and saturate (0xDF / 0xE0). A group whose
+ * base scale is not valid (see above) encodes every value as 0x00.
+ * x / out: fp32 [outer, C, inner]; code: uint8 [outer, C, inner]; perm and group_of as in a1.
+ * Decode: 0xxxxxxx -> sext7 * s, 10xxxxxx -> sext6 * (s/4), 11xxxxxx -> sext6 * (s*4), each one
+ * fp32 multiply (correctly rounded). A group with an invalid scale decodes to 0.
+ */
+qssm_status qssm_softedge_encode(const float* x, int64_t outer, int64_t C, int64_t inner,
+                                 const int32_t* perm, const uint8_t* group_of, int32_t G,
+                                 const float* s, const float* L, const float* H, uint8_t* code,
+                                 hipStream_t stream);
+qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, int64_t inner,
+                                 const uint8_t* group_of, int32_t G, const float* s, float* out,
+                                 hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * a4-a7. Mamba1 selective scan with int8 (or soft-edge) x and int8 B, C (W8A8 recurrence).
+ * Quamba2, abstract (8-bit linear recurrence for the Mamba1 backbone).
+ *
+ * Layouts: x, delta, y [B, D, L]; A [D, N]; Bq, Cq [B, Gbc, N, L] (channel d uses B/C group
+ * d / (D / Gbc)); Dskip [D]; h0, h_last [B, D, N] fp32.
+ * Per (b, d, n), t = 0 .. L-1, with xh = dequantized x, Bh/Ch = dequantized B/C:
+ *     h = exp(delta * A[d,n]) * h + delta * Bh[n,t] * xh,   y[t] = sum_n Ch[n,t] * h + Dskip[d] * xh
+ * h starts from h0 (zero when NULL); h_last receives the final state when not NULL.
+ * The state and all arithmetic are fp32. y is fp32 or fp16 (y_dtype).
+ * Workspace: qssm_scan_workspace_size bytes (dequantized B and C staging).
+ */
+typedef struct qssm_scan_args {
+  int64_t batch, seqlen, dim, dstate; /* B, L, D, N */
+  int32_t x_code;                     /* QSSM_X_INT8 or QSSM_X_SOFTEDGE */
+  int32_t x_groups;                   /* G, 1..256 */
+  const void* x;                      /* int8 or soft-edge uint8 codes [B, D, L] */
+  const uint8_t* x_group_of;          /* [D] group of each channel */
+  const float* x_scales;              /* [G] scale (soft-edge: base scale) */
+  const float* delta;                 /* [B, D, L] fp32 */
+  const float* A;                     /* [D, N] fp32 */
+  int32_t bc_groups;                  /* Gbc, D % Gbc == 0 */
+  int32_t bc_group_size;              /* gs, N % gs == 0 */
+  const int8_t* Bq;                   /* [B, Gbc, N, L] */
+  const int8_t* Cq;                   /* [B, Gbc, N, L] */
+  const float* B_scales;              /* [Gbc * N / gs] */
+  const float* C_scales;              /* [Gbc * N / gs] */
+  const float* Dskip;                 /* [D] or NULL */
+  const float* h0;                    /* [B, D, N] or NULL */
+  void* y;                            /* [B, D, L], y_dtype */
+  int32_t y_dtype;                    /* QSSM_F32 or QSSM_F16 */
+  float* h_last;                      /* [B, D, N] or NULL */
+} qssm_scan_args;
+
+size_t qssm_scan_workspace_size(const qssm_scan_args* a);
+qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * a5-a7 (S4D form). Diagonal LTI scan with int8 parameters and input.
+ * "Quantizing Small-Scale State-Space Models for Edge AI", abstract (S4D under PTQ; A and the
+ * state are sensitive; heterogeneous per-component precision).
+ *
+ * Input: when wq != NULL, uq is [B, L] int8 (a scalar sequence) lifted to H channels by int8
+ *   weights:  u[b,h,t] = (u_scale[0] * w_scale[0]) * (uq[b,t] * wq[h]);
+ *   when wq == NULL, uq is [B, H, L] and u[b,h,t] = u_scale[h] * uq[b,h,t].
+ * Parameters, per channel h and state n (int8 [H, N] planes, one scale per channel and plane):
+ *   Ah = A_re_s[h]*A_re[h,n] + i*A_im_s[h]*A_im[h,n], Bh and Ch likewise; dt = exp(log_dt[h]).
+ * Zero-order hold: Abar = exp(dt*Ah), Bbar = (Abar - 1) / Ah * Bh  (dt * Bh when Ah == 0).
+ * Recurrence: h_t = Abar * h_{t-1} + Bbar * u_t (complex), y_t = Re(sum_n Ch * h_t) + Dskip[h]*u_t.
+ * State: QSSM_F32 keeps complex fp32; QSSM_I16 rounds each real and imaginary part to
+ *   state_scale[h] * clamp(RNE(part / state_scale[h]), -32768, 32767) after every step.
+ * h0 / h_last: [B, H, N] complex, interleaved (re, im): float pairs (F32) or int16 code pairs (I16).
+ * y: fp32 [B, H, L].
+ */
+typedef struct qssm_s4d_args {
+  int64_t batch, seqlen, channels, dstate; /* B, L, H, N */
+  const int8_t* uq;
+  const float* u_scale;
+  const int8_t* wq;
+  const float* w_scale;
+  const int8_t *A_re, *A_im, *B_re, *B_im, *C_re, *C_im; /* [H, N] */
+  const float *A_re_s, *A_im_s, *B_re_s, *B_im_s, *C_re_s, *C_im_s; /* [H] */
+  const float* log_dt;      /* [H] */
+  const float* Dskip;       /* [H] or NULL */
+  int32_t state_dtype;      /* QSSM_F32 or QSSM_I16 */
+  const float* state_scale; /* [H], required for QSSM_I16 */
+  const void* h0;           /* or NULL */
+  float* y;                 /* [B, H, L] */
+  void* h_last;             /* or NULL */
+} qssm_s4d_args;
+
+qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * a8-a13. Mamba2 SSD chunked form with an int8 path.
+ * SSDi8 abstract (persistent INT8 path through SSD; requantization at cost-effective points);
+ * Quamba2 abstract (W8A8 for the Mamba2 backbone).
+ *
+ * Layouts: xq, y [B, L, nh, P]; delta [B, L, nh]; A, Dskip [nh]; Bq, Cq [B, L, Gbc, N] (head h
+ * uses group h / (nh / Gbc)); h0, h_last [B, nh, P, N] fp32. x channel (h, p) has group
+ * x_group_of[h * P + p].
+ * The result equals the sequential recurrence with A[h] shared by all (p, n) of head h, computed
+ * per chunk of `chunk` steps (chunks start at t = 0, the last may be partial):
+ *   cum_i = sum_{k<=i} delta_k * A[h];  G = Ch Bh^T (int8 MFMA, int32 accumulation per state group);
+ *   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh;  chunk state from an int8
+ *   requantization of the decay-weighted x (int8 MFMA over time);  inter-chunk state passing in
+ *   fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;  y = Y_intra + Y_inter + Dskip * xh.
+ * Requires chunk == 256, P == 64, N == 128, gs == 16 in this build (else QSSM_ERR_UNSUPPORTED).
+ */
+typedef struct qssm_ssd_args {
+  int64_t batch, seqlen, nheads, headdim, dstate; /* B, L, nh, P, N */
+  int32_t ngroups;                                /* Gbc, nh % Gbc == 0 */
+  int32_t chunk;                                  /* Q */
+  int32_t x_groups;                               /* G, 1..256 */
+  const int8_t* xq;                               /* [B, L, nh, P] */
+  const uint8_t* x_group_of;                      /* [nh * P] */
+  const float* x_scales;                          /* [G] */
+  const float* delta;                             /* [B, L, nh] */
+  const float* A;                                 /* [nh] */
+  const float* Dskip;                             /* [nh] or NULL */
+  int32_t bc_group_size;                          /* gs */
+  const int8_t* Bq;                               /* [B, L, Gbc, N] */
+  const int8_t* Cq;                               /* [B, L, Gbc, N] */
+  const float* B_scales;                          /* [Gbc * N / gs] */
+  const float* C_scales;                          /* [Gbc * N / gs] */
+  const float* h0;                                /* [B, nh, P, N] or NULL */
+  void* y;                                        /* [B, L, nh, P], y_dtype */
+  int32_t y_dtype;                                /* QSSM_F32 or QSSM_F16 */
+  float* h_last;                                  /* [B, nh, P, N] or NULL */
+  int32_t fused;                                  /* reserved, must be 0 */
+} qssm_ssd_args;
+
+size_t qssm_ssd_workspace_size(const qssm_ssd_args* a);
+qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * a14. Fused decode state update (one new token per sequence), Mamba2-shaped.
+ * Quamba2, abstract (W8A8 generation stage).
+ *
+ * Per call, with static scales: x [B, nh, P], B and C [B, Gbc, N] fp32 are quantized with the a1
+ * and a2 rules (x channel (h, p) in group x_group_of[h*P + p]; B/C state n of group g in state
+ * group g * (N/gs) + n/gs), then for every (b, h, p, n), g = h / (nh / Gbc):
+ *     dA = exp(delta[b,h] * A[h]);  state = dA * state + delta[b,h] * xh[p] * Bh[n]
+ *     y[b,h,p] = sum_n Ch[n] * state + Dskip[h] * xh[p]
+ * state [B, nh, P, N] is read and written in place, fp32 or fp16 (state_dtype; fp16 is rounded
+ * to nearest even on store, arithmetic is fp32). y: fp32 [B, nh, P].
+ * xq_out [B, nh, P], Bq_out / Cq_out [B, Gbc, N] receive the codes when not NULL.
+ */
+typedef struct qssm_update_args {
+  int64_t batch, nheads, headdim, dstate; /* B, nh, P, N */
+  int32_t ngroups;                        /* Gbc */
+  int32_t x_groups;                       /* G */
+  const float* x;                         /* [B, nh, P] */
+  const uint8_t* x_group_of;              /* [nh * P] */
+  const float* x_scales;                  /* [G] */
+  const float* B;                         /* [B, Gbc, N] */
+  const float* C;                         /* [B, Gbc, N] */
+  int32_t bc_group_size;                  /* gs */
+  const float* B_scales;                  /* [Gbc * N / gs] */
+  const float* C_scales;                  /* [Gbc * N / gs] */
+  const float* delta;                     /* [B, nh] */
+  const float* A;                         /* [nh] */
+  const float* Dskip;                     /* [nh] or NULL */
+  int32_t state_dtype;                    /* QSSM_F32 or QSSM_F16 */
+  void* state;                            /* [B, nh, P, N] in/out */
+  float* y;                               /* [B, nh, P] */
+  int8_t* xq_out;                         /* [B, nh, P] or NULL */
+  int8_t* Bq_out;                         /* [B, Gbc, N] or NULL */
+  int8_t* Cq_out;                         /* [B, Gbc, N] or NULL */
+} qssm_update_args;
+
+qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Host-side offline calibration (CPU only; every pointer below is a HOST pointer).
+ * Quamba2, method steps 1-2 (offline activation statistics; sort and cluster the x channels);
+ * Quamba-SE, section 4.1 (L at the 5th and H at the 99.9th percentile, EMA with alpha = 0.1).
+ */
+
+/* absmax_out[c] = largest finite |x[o, c, i]| over o and i of a host tensor [outer, C, inner]. */
+qssm_status qssm_calib_channel_absmax(const float* x, int64_t outer, int64_t C, int64_t inner,
+                                      float* absmax_out);
+
+/* scales[i] = fl32(absmax[i] / 127); absmax 0 -> 1; clamped to [2^-100, 2^100].
+ * absmax values must be finite and >= 0. */
+qssm_status qssm_calib_scales(const float* absmax, int64_t n, float* scales);
+
+/* Sort channels by absmax ascending (stable) and split the sorted list into G contiguous groups
+ * with the least total within-group squared deviation (exact 1-D k-means by dynamic programming;
+ * ties go to the smallest split index). perm_out[c] = source channel of sorted position c;
+ * group_of_out[c] = group of sorted position c (ascending with magnitude). 1 <= G <= min(C, 256). */
+qssm_status qssm_calib_cluster_channels(const float* absmax, int32_t C, int32_t G,
+                                        int32_t* perm_out, uint8_t* group_of_out);
+
+/* Soft-edge thresholds of one group from samples v[n] (finite values):
+ *   L_new = P5(|v|), H_new = P99.9(|v|) (linear interpolation between order statistics),
+ *   computed in fp64. When ema_state[0..1] holds a previous (L, H) and ema_valid != 0:
+ *   L = alpha * L_new + (1 - alpha) * L_prev (same for H), else L = L_new.
+ *   ema_state (fp64, in/out) receives the new (L, H); L_out, H_out are fl32 of them;
+ *   s_out = fl32(H_out / 63) (so standard codes span [-H, H]); s_out = 1 if H_out is 0. */
+qssm_status qssm_calib_softedge(const float* v, int64_t n, double alpha, int32_t ema_valid,
+                                double* ema_state, float* s_out, float* L_out, float* H_out);
+
+/* ---------------------------------------------------------------------------------------------
+ * Library information. */
+const char* qssm_status_string(qssm_status s);
+/* Message of the last failing call on this host thread ("" if none). */
+const char* qssm_last_error(void);
+int32_t qssm_version(void);
+/* sizeof of the argument structs as compiled (0: scan, 1: s4d, 2: ssd, 3: update), so bindings can
+ * check their layout. Returns 0 for an unknown kind. */
+size_t qssm_args_size(int32_t kind);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSSM_H */
