@@ -1,0 +1,319 @@
+"""Benchmark of the quantized state-space hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c1|c2|c5|c5f16]
+
+One step = one pass of the whole hot path of the workload over one batch of synthetic input that is
+already resident in HBM: for the Mamba1 layers, quantize x (gathered into cluster order), quantize B
+and C, run the W8A8 scan; for S4D, quantize the input then scan; for the SSD layer, quantize x, B, C
+then run the chunked SSD; for decode, one fused state update of every sequence.
+
+Prints one JSON line: throughput in state-updates/s (B*L*D*N per step), the dominant kernel's
+roofline figures measured with HIP events on the launch stream, and the oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantized scan state-updates/s (B·L·D·N) + % of HBM peak, 1 MI355X"
+
+
+# ------------------------------------------------------------------------------------------------
+# workloads
+
+class Workload:
+    name = ""
+    dominant = ""           # kernel timed for the roofline
+    bound = "hbm"
+    config: dict = {}
+
+    def setup(self, dev): ...
+    def step(self, timer): ...
+    def updates(self): ...
+    def dominant_bytes(self): ...
+    def cpu_baseline(self): ...
+
+
+class Mamba1(Workload):
+    def __init__(self, soft_edge=False):
+        self.soft = soft_edge
+        self.name = "mamba1-130m-layer-w8a8" + ("-softedge-x" if soft_edge else "")
+        self.dominant = "k_scan_m1 (+ k_stage_bc)"
+
+    def setup(self, dev):
+        import qssm_synth as synth
+        import quantized_state_space_amd as qs
+        import quantized_state_space_amd.workloads as wl
+        self.inp = synth.c3_inputs()
+        xc = qs.QSSM_X_SOFTEDGE if self.soft else qs.QSSM_X_INT8
+        self.lay = wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc)
+        B, D, L, N, Gbc = self.lay.shape
+        self.dims = (B, D, L, N, Gbc)
+        self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
+                       "x_groups": 8, "x_code": "soft-edge 3-scale u8" if self.soft else "int8",
+                       "bc_state_groups": N // 4, "state": "f32", "y": "f32"}
+
+    def step(self, timer):
+        self.lay.quantize()
+        timer.start()
+        self.lay.scan()
+        timer.stop()
+
+    def updates(self):
+        B, D, L, N, _ = self.dims
+        return B * D * L * N
+
+    def dominant_bytes(self):
+        B, D, L, N, Gbc = self.dims
+        # x codes, delta, B/C codes, A, D in; y and h_last out (each once)
+        return B * D * L * (1 + 4 + 4) + 2 * B * Gbc * N * L + 4 * D * N + 4 * D + 4 * B * D * N
+
+    def cpu_baseline(self):
+        import oracle.pipelines as op
+        cal = op.mamba1_calib(self.inp, 8, 4, soft_edge=self.soft)
+        t = time.perf_counter()
+        op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=cal)
+        dt = time.perf_counter() - t
+        return self.updates() / dt, "full workload (all 8 x 1536 channels x 2048 steps), quantize + dequantize + fp64 scan"
+
+
+class Tiny(Mamba1):
+    def __init__(self):
+        self.soft = False
+        self.name = "tiny-mamba1-w8a8"
+        self.dominant = "k_scan_m1 (+ k_stage_bc)"
+
+    def setup(self, dev):
+        import qssm_synth as synth
+        import quantized_state_space_amd.workloads as wl
+        self.inp = synth.c1_inputs()
+        self.lay = wl.Mamba1Layer(self.inp, 1, 4, dev, dynamic_scales=True)
+        self.dims = self.lay.shape
+        B, D, L, N, _ = self.dims
+        self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
+                       "x_groups": 1, "bc_state_groups": 4, "state": "f32", "y": "f32"}
+
+    def cpu_baseline(self):
+        import oracle.pipelines as op
+        t = time.perf_counter()
+        for _ in range(20):
+            op.mamba1(self.inp, G=1, gs=4, dynamic=True)
+        return 20 * self.updates() / (time.perf_counter() - t), "full workload x20"
+
+
+class S4d(Workload):
+    def __init__(self, i16=False):
+        self.i16 = i16
+        self.name = "s4d-smnist-shaped" + ("-int16-state" if i16 else "")
+        self.dominant = "k_s4d"
+        self.bound = "alu"
+
+    def setup(self, dev):
+        import qssm_synth as synth
+        import quantized_state_space_amd as qs
+        import quantized_state_space_amd.workloads as wl
+        self.inp = synth.s4d_inputs()
+        ss = None
+        self.lay = wl.S4dLayer(self.inp, dev, state_dtype=qs.QSSM_I16 if self.i16 else qs.QSSM_F32,
+                               state_scale=ss)
+        self.ss = ss
+        B, L, H, N = self.lay.shape
+        self.dims = (B, L, H, N)
+        self.config = {"workload": self.name, "batch": B, "seqlen": L, "channels": H,
+                       "d_state_complex": N, "state": "int16" if self.i16 else "f32", "y": "f32"}
+
+    def step(self, timer):
+        import quantized_state_space_amd as qs
+        qs.qssm_quant_group_x(self.lay.u_f, _zero(self.lay.u_f.device), 1, self.lay.u_scale,
+                              self.lay.uq)
+        timer.start()
+        qs.qssm_s4d_scan(self.lay.args)
+        timer.stop()
+
+    def updates(self):
+        B, L, H, N = self.dims
+        return B * L * H * N
+
+    def dominant_bytes(self):
+        B, L, H, N = self.dims
+        return B * L + H + 6 * H * N + 4 * 8 * H + 4 * B * H * L + 8 * B * H * N
+
+    def flops(self):  # complex update Abar*h + Bbar*u (10 flops) + readout Re(C h) (4 flops)
+        return 14.0 * self.updates()
+
+    def cpu_baseline(self):
+        import oracle.pipelines as op
+        t = time.perf_counter()
+        op.s4d(self.inp, state_scale=self.ss)
+        return self.updates() / (time.perf_counter() - t), "full workload, fp64 complex scan"
+
+
+class Decode(Workload):
+    def __init__(self, f16=False):
+        self.f16 = f16
+        self.name = "mamba2-8b-decode" + ("-fp16-state" if f16 else "")
+        self.dominant = "k_state_update"
+
+    def setup(self, dev):
+        import torch
+        import qssm_synth as synth
+        import quantized_state_space_amd as qs
+        import quantized_state_space_amd.workloads as wl
+        self.params = synth.decode_params()
+        self.lay = wl.DecodeLayer(self.params, dev, state_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32)
+        B, nh, P, N, Gbc = self.lay.shape
+        self.dims = self.lay.shape
+        self.nsteps = 64
+        self.inputs = [synth.decode_step_inputs(k) for k in range(self.nsteps)]
+        # all 64 tokens resident in HBM; one argument block per token
+        self.dev_inputs = []
+        self.args = []
+        for k, inp in enumerate(self.inputs):
+            d = {n: torch.from_numpy(inp[n]).to(dev) for n in ("x", "B", "C", "delta")}
+            self.dev_inputs.append(d)
+            self.args.append(qs.update_args(d["x"], self.lay.group_t, self.lay.xs, d["B"], d["C"],
+                                            self.lay.bs, self.lay.cs, 16, d["delta"], self.lay.A,
+                                            self.lay.state, self.lay.y, Dskip=self.lay.D))
+        self.k = 0
+        self.config = {"workload": self.name, "batch": B, "heads": nh, "headdim": P, "d_state": N,
+                       "ngroups": Gbc, "tokens": self.nsteps, "state": "f16" if self.f16 else "f32"}
+
+    def step(self, timer):
+        import quantized_state_space_amd as qs
+        timer.start()
+        qs.qssm_state_update(self.args[self.k % self.nsteps])
+        timer.stop()
+        self.k += 1
+
+    def updates(self):
+        B, nh, P, N, _ = self.dims
+        return B * nh * P * N
+
+    def dominant_bytes(self):
+        B, nh, P, N, Gbc = self.dims
+        sb = 2 if self.f16 else 4
+        return 2 * sb * B * nh * P * N + 4 * (2 * B * nh * P + 2 * B * Gbc * N + B * nh)
+
+    def cpu_baseline(self):
+        import oracle.pipelines as op
+        sample = np.arange(16)
+        t = time.perf_counter()
+        op.decode(self.params, self.inputs[:8], batches=sample)
+        dt = time.perf_counter() - t
+        B, nh, P, N, _ = self.dims
+        return 8 * len(sample) * nh * P * N / dt, "16 of 256 sequences x 8 tokens (fp64 state)"
+
+
+_zc = {}
+
+
+def _zero(device):
+    import torch
+    k = str(device)
+    if k not in _zc:
+        _zc[k] = torch.zeros(1, dtype=torch.uint8, device=device)
+    return _zc[k]
+
+
+WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Tiny,
+             "c2": lambda: S4d(False), "c5": lambda: Decode(False),
+             "c5f16": lambda: Decode(True)}
+
+
+# ------------------------------------------------------------------------------------------------
+
+class EventTimer:
+    """HIP events around the dominant call, recorded on the stream the library launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+        self.active = False
+
+    def start(self):
+        if self.active:
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record(self.torch.cuda.current_stream())
+            self.pairs.append([e, None])
+
+    def stop(self):
+        if self.active:
+            e = self.torch.cuda.Event(enable_timing=True)
+            e.record(self.torch.cuda.current_stream())
+            self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the sharding plan is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_state_space_amd as qs
+    qs.load()
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]()
+    wl.setup(dev)
+    timer = EventTimer(torch)
+    for _ in range(args.warmup):
+        wl.step(timer)
+    torch.cuda.synchronize()
+    timer.active = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = timer.mean_ms()
+
+    ups = wl.updates()
+    value = ups * args.steps / elapsed
+    nbytes = wl.dominant_bytes()
+    if wl.bound == "alu":
+        # fp32 vector peak of MI355X: 256 CUs x 2.4 GHz x 256 flop/clk (packed FMA)
+        achieved = wl.flops() / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": 157.3, "unit": "TFLOP/s",
+                "frac": round(achieved / 157.3, 4), "traffic": None}
+    else:
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = wl.dominant
+    roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["algorithmic_bytes"] = int(nbytes)
+
+    out = {"metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic", "config": wl.config, "roofline": roof,
+           "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if not args.no_cpu_baseline:
+        v, sample = wl.cpu_baseline()
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        out["cpu_baseline"] = {"value": v, "unit": "state-updates/s", "cores": threads,
+                               "kind": "oracle", "sample": sample}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

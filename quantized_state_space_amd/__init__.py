@@ -1,0 +1,358 @@
+"""Python binding of libqssm (ctypes): the C entry points under the same names.
+
+Argument marshalling only: every step of the hot path runs in the library's HIP kernels. Tensors
+are torch tensors on the GPU (PyTorch provides device memory and streams); they are checked for
+dtype, device and contiguity and passed as raw pointers with the current HIP stream. There is no
+fallback: if ``libqssm.so`` is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqssm.so")
+
+QSSM_OK, QSSM_ERR_INVALID_ARG, QSSM_ERR_UNSUPPORTED, QSSM_ERR_WORKSPACE, QSSM_ERR_DEVICE = range(5)
+QSSM_F32, QSSM_F16, QSSM_I16 = 0, 1, 2
+QSSM_X_INT8, QSSM_X_SOFTEDGE = 0, 1
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+class QssmError(RuntimeError):
+    def __init__(self, name, status, message):
+        super().__init__(f"{name} failed with status {status}: {message}")
+        self.status = status
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("dim", _I64), ("dstate", _I64),
+                ("x_code", _I32), ("x_groups", _I32), ("x", _P), ("x_group_of", _P),
+                ("x_scales", _P), ("delta", _P), ("A", _P), ("bc_groups", _I32),
+                ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P), ("C_scales", _P),
+                ("Dskip", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P)]
+
+
+class S4dArgs(ctypes.Structure):
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("channels", _I64), ("dstate", _I64),
+                ("uq", _P), ("u_scale", _P), ("wq", _P), ("w_scale", _P),
+                ("A_re", _P), ("A_im", _P), ("B_re", _P), ("B_im", _P), ("C_re", _P), ("C_im", _P),
+                ("A_re_s", _P), ("A_im_s", _P), ("B_re_s", _P), ("B_im_s", _P), ("C_re_s", _P),
+                ("C_im_s", _P), ("log_dt", _P), ("Dskip", _P), ("state_dtype", _I32),
+                ("state_scale", _P), ("h0", _P), ("y", _P), ("h_last", _P)]
+
+
+class SsdArgs(ctypes.Structure):
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("nheads", _I64), ("headdim", _I64),
+                ("dstate", _I64), ("ngroups", _I32), ("chunk", _I32), ("x_groups", _I32),
+                ("xq", _P), ("x_group_of", _P), ("x_scales", _P), ("delta", _P), ("A", _P),
+                ("Dskip", _P), ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P),
+                ("C_scales", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
+                ("fused", _I32)]
+
+
+class UpdateArgs(ctypes.Structure):
+    _fields_ = [("batch", _I64), ("nheads", _I64), ("headdim", _I64), ("dstate", _I64),
+                ("ngroups", _I32), ("x_groups", _I32), ("x", _P), ("x_group_of", _P),
+                ("x_scales", _P), ("B", _P), ("C", _P), ("bc_group_size", _I32),
+                ("B_scales", _P), ("C_scales", _P), ("delta", _P), ("A", _P), ("Dskip", _P),
+                ("state_dtype", _I32), ("state", _P), ("y", _P), ("xq_out", _P), ("Bq_out", _P),
+                ("Cq_out", _P)]
+
+
+ARG_STRUCTS = {0: ScanArgs, 1: S4dArgs, 2: SsdArgs, 3: UpdateArgs}
+
+# Every symbol include/qssm.h declares, with its ctypes signature.
+SIGNATURES = {
+    "qssm_quant_group_x": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I32, _P, _P]),
+    "qssm_quant_state_group_BC": (_I32, [_P, _I64, _I32, _I32, _I64, _I32, _P, _I32, _P, _P]),
+    "qssm_softedge_encode": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _P]),
+    "qssm_softedge_decode": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P]),
+    "qssm_scan_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScanArgs)]),
+    "qssm_scan_w8a8": (_I32, [ctypes.POINTER(ScanArgs), _P, ctypes.c_size_t, _P]),
+    "qssm_s4d_scan": (_I32, [ctypes.POINTER(S4dArgs), _P]),
+    "qssm_ssd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SsdArgs)]),
+    "qssm_ssd_chunk_int8": (_I32, [ctypes.POINTER(SsdArgs), _P, ctypes.c_size_t, _P]),
+    "qssm_state_update": (_I32, [ctypes.POINTER(UpdateArgs), _P]),
+    "qssm_calib_channel_absmax": (_I32, [_P, _I64, _I64, _I64, _P]),
+    "qssm_calib_scales": (_I32, [_P, _I64, _P]),
+    "qssm_calib_cluster_channels": (_I32, [_P, _I32, _I32, _P, _P]),
+    "qssm_calib_softedge": (_I32, [_P, _I64, ctypes.c_double, _I32, _P, _P, _P, _P]),
+    "qssm_status_string": (ctypes.c_char_p, [_I32]),
+    "qssm_last_error": (ctypes.c_char_p, []),
+    "qssm_version": (_I32, []),
+    "qssm_args_size": (ctypes.c_size_t, [_I32]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libqssm.so (built in-tree by ``__graft_entry__.build()``). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        for kind, st in ARG_STRUCTS.items():
+            if lib.qssm_args_size(kind) != ctypes.sizeof(st):
+                raise ImportError(f"argument struct {st.__name__} layout mismatch")
+        _lib = lib
+    return _lib
+
+
+def _check(name, status):
+    if status != QSSM_OK:
+        raise QssmError(name, status, load().qssm_last_error().decode())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor", optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _t():
+    import torch
+    return torch
+
+
+# ------------------------------------------------------------------------------------------------
+# Quantizers and soft-edge code
+
+def qssm_quant_group_x(x, group_of, G, scales, q, perm=None, compute_scales=False, stream=None):
+    """x: float32 [outer, C, inner]; q: int8, same shape; scales float32 [G] (in or out)."""
+    torch = _t()
+    outer, C, inner = x.shape
+    _check("qssm_quant_group_x", load().qssm_quant_group_x(
+        _ptr(x, torch.float32, "x"), outer, C, inner, _ptr(perm, torch.int32, "perm", True),
+        _ptr(group_of, torch.uint8, "group_of"), G, _ptr(scales, torch.float32, "scales"),
+        int(bool(compute_scales)), _ptr(q, torch.int8, "q"), _stream(stream)))
+    return q
+
+
+def qssm_quant_state_group_BC(bc, gs, scales, q, compute_scales=False, stream=None):
+    """bc: float32 [outer, Gbc, N, inner]; q int8 same shape; scales [Gbc * N / gs]."""
+    torch = _t()
+    outer, Gbc, N, inner = bc.shape
+    _check("qssm_quant_state_group_BC", load().qssm_quant_state_group_BC(
+        _ptr(bc, torch.float32, "bc"), outer, Gbc, N, inner, gs,
+        _ptr(scales, torch.float32, "scales"), int(bool(compute_scales)),
+        _ptr(q, torch.int8, "q"), _stream(stream)))
+    return q
+
+
+def qssm_softedge_encode(x, group_of, G, s, L, H, code, perm=None, stream=None):
+    torch = _t()
+    outer, C, inner = x.shape
+    _check("qssm_softedge_encode", load().qssm_softedge_encode(
+        _ptr(x, torch.float32, "x"), outer, C, inner, _ptr(perm, torch.int32, "perm", True),
+        _ptr(group_of, torch.uint8, "group_of"), G, _ptr(s, torch.float32, "s"),
+        _ptr(L, torch.float32, "L"), _ptr(H, torch.float32, "H"), _ptr(code, torch.uint8, "code"),
+        _stream(stream)))
+    return code
+
+
+def qssm_softedge_decode(code, group_of, G, s, out, stream=None):
+    torch = _t()
+    outer, C, inner = code.shape
+    _check("qssm_softedge_decode", load().qssm_softedge_decode(
+        _ptr(code, torch.uint8, "code"), outer, C, inner, _ptr(group_of, torch.uint8, "group_of"),
+        G, _ptr(s, torch.float32, "s"), _ptr(out, torch.float32, "out"), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# Recurrences
+
+def _fill(st, **kw):
+    for k, v in kw.items():
+        setattr(st, k, v)
+    return st
+
+
+def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, y,
+              Dskip=None, h0=None, h_last=None):
+    """Builds ScanArgs for x [B, D, L] codes, Bq/Cq [B, Gbc, N, L]."""
+    torch = _t()
+    B, D, L = x.shape
+    N = A.shape[1]
+    Gbc = Bq.shape[1]
+    xdt = torch.int8 if x_code == QSSM_X_INT8 else torch.uint8
+    ydt = QSSM_F32 if y.dtype == torch.float32 else QSSM_F16
+    return _fill(ScanArgs(), batch=B, seqlen=L, dim=D, dstate=N, x_code=x_code,
+                 x_groups=int(x_scales.numel()), x=_ptr(x, xdt, "x"),
+                 x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
+                 x_scales=_ptr(x_scales, torch.float32, "x_scales"),
+                 delta=_ptr(delta, torch.float32, "delta"), A=_ptr(A, torch.float32, "A"),
+                 bc_groups=Gbc, bc_group_size=gs, Bq=_ptr(Bq, torch.int8, "Bq"),
+                 Cq=_ptr(Cq, torch.int8, "Cq"), B_scales=_ptr(B_scales, torch.float32, "B_scales"),
+                 C_scales=_ptr(C_scales, torch.float32, "C_scales"),
+                 Dskip=_ptr(Dskip, torch.float32, "Dskip", True),
+                 h0=_ptr(h0, torch.float32, "h0", True), y=_ptr(y, None, "y"), y_dtype=ydt,
+                 h_last=_ptr(h_last, torch.float32, "h_last", True))
+
+
+def qssm_scan_workspace_size(args):
+    return load().qssm_scan_workspace_size(ctypes.byref(args))
+
+
+def qssm_scan_w8a8(args, workspace, stream=None):
+    torch = _t()
+    _check("qssm_scan_w8a8", load().qssm_scan_w8a8(
+        ctypes.byref(args), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))
+
+
+def s4d_args(uq, u_scale, params, scales, log_dt, y, wq=None, w_scale=None, Dskip=None,
+             state_dtype=QSSM_F32, state_scale=None, h0=None, h_last=None, channels=None):
+    """params: dict of int8 [H, N] planes A_re, A_im, B_re, B_im, C_re, C_im;
+    scales: dict of float32 [H] with the same keys."""
+    torch = _t()
+    H, N = params["A_re"].shape
+    B = uq.shape[0]
+    L = uq.shape[-1]
+    kw = {k: _ptr(params[k], torch.int8, k) for k in ("A_re", "A_im", "B_re", "B_im", "C_re", "C_im")}
+    kw.update({k + "_s": _ptr(scales[k], torch.float32, k + "_s")
+               for k in ("A_re", "A_im", "B_re", "B_im", "C_re", "C_im")})
+    st_t = torch.float32 if state_dtype == QSSM_F32 else torch.int16
+    return _fill(S4dArgs(), batch=B, seqlen=L, channels=H, dstate=N, uq=_ptr(uq, torch.int8, "uq"),
+                 u_scale=_ptr(u_scale, torch.float32, "u_scale"), wq=_ptr(wq, torch.int8, "wq", True),
+                 w_scale=_ptr(w_scale, torch.float32, "w_scale", True),
+                 log_dt=_ptr(log_dt, torch.float32, "log_dt"),
+                 Dskip=_ptr(Dskip, torch.float32, "Dskip", True), state_dtype=state_dtype,
+                 state_scale=_ptr(state_scale, torch.float32, "state_scale", True),
+                 h0=_ptr(h0, st_t, "h0", True), y=_ptr(y, torch.float32, "y"),
+                 h_last=_ptr(h_last, st_t, "h_last", True), **kw)
+
+
+def qssm_s4d_scan(args, stream=None):
+    _check("qssm_s4d_scan", load().qssm_s4d_scan(ctypes.byref(args), _stream(stream)))
+
+
+def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, chunk, y,
+             Dskip=None, h0=None, h_last=None):
+    torch = _t()
+    B, L, nh, P = xq.shape
+    Gbc, N = Bq.shape[2], Bq.shape[3]
+    ydt = QSSM_F32 if y.dtype == torch.float32 else QSSM_F16
+    return _fill(SsdArgs(), batch=B, seqlen=L, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
+                 chunk=chunk, x_groups=int(x_scales.numel()), xq=_ptr(xq, torch.int8, "xq"),
+                 x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
+                 x_scales=_ptr(x_scales, torch.float32, "x_scales"),
+                 delta=_ptr(delta, torch.float32, "delta"), A=_ptr(A, torch.float32, "A"),
+                 Dskip=_ptr(Dskip, torch.float32, "Dskip", True), bc_group_size=gs,
+                 Bq=_ptr(Bq, torch.int8, "Bq"), Cq=_ptr(Cq, torch.int8, "Cq"),
+                 B_scales=_ptr(B_scales, torch.float32, "B_scales"),
+                 C_scales=_ptr(C_scales, torch.float32, "C_scales"),
+                 h0=_ptr(h0, torch.float32, "h0", True), y=_ptr(y, None, "y"), y_dtype=ydt,
+                 h_last=_ptr(h_last, torch.float32, "h_last", True), fused=0)
+
+
+def qssm_ssd_workspace_size(args):
+    return load().qssm_ssd_workspace_size(ctypes.byref(args))
+
+
+def qssm_ssd_chunk_int8(args, workspace, stream=None):
+    torch = _t()
+    _check("qssm_ssd_chunk_int8", load().qssm_ssd_chunk_int8(
+        ctypes.byref(args), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))
+
+
+def update_args(x, x_group_of, x_scales, Bm, Cm, B_scales, C_scales, gs, delta, A, state, y,
+                Dskip=None, xq_out=None, Bq_out=None, Cq_out=None):
+    torch = _t()
+    B, nh, P = x.shape
+    Gbc, N = Bm.shape[1], Bm.shape[2]
+    sdt = QSSM_F32 if state.dtype == torch.float32 else QSSM_F16
+    return _fill(UpdateArgs(), batch=B, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
+                 x_groups=int(x_scales.numel()), x=_ptr(x, torch.float32, "x"),
+                 x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
+                 x_scales=_ptr(x_scales, torch.float32, "x_scales"), B=_ptr(Bm, torch.float32, "B"),
+                 C=_ptr(Cm, torch.float32, "C"), bc_group_size=gs,
+                 B_scales=_ptr(B_scales, torch.float32, "B_scales"),
+                 C_scales=_ptr(C_scales, torch.float32, "C_scales"),
+                 delta=_ptr(delta, torch.float32, "delta"), A=_ptr(A, torch.float32, "A"),
+                 Dskip=_ptr(Dskip, torch.float32, "Dskip", True), state_dtype=sdt,
+                 state=_ptr(state, None, "state"), y=_ptr(y, torch.float32, "y"),
+                 xq_out=_ptr(xq_out, torch.int8, "xq_out", True),
+                 Bq_out=_ptr(Bq_out, torch.int8, "Bq_out", True),
+                 Cq_out=_ptr(Cq_out, torch.int8, "Cq_out", True))
+
+
+def qssm_state_update(args, stream=None):
+    _check("qssm_state_update", load().qssm_state_update(ctypes.byref(args), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------------
+# Host calibration (numpy arrays on the CPU)
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def qssm_calib_channel_absmax(x):
+    import numpy as np
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    outer, C, inner = x.shape
+    out = np.empty(C, dtype=np.float32)
+    _check("qssm_calib_channel_absmax",
+           load().qssm_calib_channel_absmax(_np_ptr(x), outer, C, inner, _np_ptr(out)))
+    return out
+
+
+def qssm_calib_scales(absmax):
+    import numpy as np
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    out = np.empty_like(a)
+    _check("qssm_calib_scales", load().qssm_calib_scales(_np_ptr(a), a.size, _np_ptr(out)))
+    return out
+
+
+def qssm_calib_cluster_channels(absmax, G):
+    import numpy as np
+    a = np.ascontiguousarray(absmax, dtype=np.float32)
+    perm = np.empty(a.size, dtype=np.int32)
+    grp = np.empty(a.size, dtype=np.uint8)
+    _check("qssm_calib_cluster_channels",
+           load().qssm_calib_cluster_channels(_np_ptr(a), a.size, G, _np_ptr(perm), _np_ptr(grp)))
+    return perm, grp
+
+
+def qssm_calib_softedge(v, alpha=0.1, ema_state=None):
+    """Returns (s, L, H, ema_state); pass ema_state back to blend the next batch."""
+    import numpy as np
+    v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1)
+    st = np.zeros(2, dtype=np.float64) if ema_state is None else np.array(ema_state, np.float64)
+    s = np.zeros(1, np.float32)
+    L = np.zeros(1, np.float32)
+    H = np.zeros(1, np.float32)
+    _check("qssm_calib_softedge", load().qssm_calib_softedge(
+        _np_ptr(v), v.size, float(alpha), int(ema_state is not None), _np_ptr(st), _np_ptr(s),
+        _np_ptr(L), _np_ptr(H)))
+    return s[0], L[0], H[0], st

@@ -1,0 +1,90 @@
+// Shared device helpers and host-side error handling of libqssm (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "qssm.h"
+
+namespace qssm {
+
+// ---------------------------------------------------------------------------------------------
+// Host: error reporting (thread-local message, never an exception across the ABI).
+qssm_status fail(qssm_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+// Maps a pending launch error to QSSM_ERR_DEVICE (with the runtime's message).
+qssm_status launch_status(const char* what);
+
+// Ceil division for launch geometry.
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------------------------
+// Device: the quantization rule.
+//
+// q = clamp(RNE(v / s), lo, hi) with v / s the exact rational quotient (Quamba2's 8-bit codes,
+// rounding half to even, saturating). The fp32 division is correctly rounded, and rounding is
+// monotone, so rint() of the fp32 quotient f differs from the exact RNE only when f itself is a
+// half-integer k + 1/2 while the exact quotient is not: then the sign of the exact remainder
+// v - f*s, which one fused multiply-add yields without intermediate rounding, decides the side.
+// Valid scales lie in [2^-100, 2^100]; there every non-zero remainder is at least 2^-149 in
+// magnitude, so its sign survives the final rounding of the fma.
+__device__ __forceinline__ bool scale_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+
+__device__ __forceinline__ int rne_sat(float v, float s, float lo, float hi) {
+  float f = v / s;
+  float r = rintf(f);
+  if (fabsf(f - r) == 0.5f) {
+    float rem = fmaf(-f, s, v);
+    if (rem > 0.0f) r = f + 0.5f;
+    else if (rem < 0.0f) r = f - 0.5f;
+  }
+  r = fminf(fmaxf(r, lo), hi);
+  return (v != v) ? 0 : (int)r;  // NaN encodes as 0
+}
+
+__device__ __forceinline__ int8_t quant8(float v, float s) {
+  return scale_ok(s) ? (int8_t)rne_sat(v, s, -128.0f, 127.0f) : (int8_t)0;
+}
+
+// Soft-edge byte (Quamba-SE blog, 2.1 and 2.2): strict |v| < L selects scale/4 with a 6-bit
+// payload (tag 10), |v| > H selects scale*4 (tag 11), anything else (including both tests true)
+// the base scale with a 7-bit payload (tag 0). Payloads are two's complement.
+__device__ __forceinline__ uint8_t softedge_code(float v, float s, float L, float H) {
+  if (!scale_ok(s) || v != v) return 0;
+  float a = fabsf(v);
+  bool small = a < L, large = a > H;
+  if (small && !large) return (uint8_t)(0x80 | (rne_sat(v, s * 0.25f, -32.0f, 31.0f) & 0x3F));
+  if (large && !small) return (uint8_t)(0xC0 | (rne_sat(v, s * 4.0f, -32.0f, 31.0f) & 0x3F));
+  return (uint8_t)(rne_sat(v, s, -64.0f, 63.0f) & 0x7F);
+}
+
+// Value of a soft-edge byte as one correctly rounded fp32 product (0 for an invalid scale).
+__device__ __forceinline__ float softedge_value(uint32_t b, float s) {
+  if (!scale_ok(s)) return 0.0f;
+  if ((b & 0x80u) == 0) {
+    int q = (b & 0x40u) ? (int)(b & 0x7Fu) - 128 : (int)(b & 0x7Fu);
+    return (float)q * s;
+  }
+  int q = (b & 0x20u) ? (int)(b & 0x3Fu) - 64 : (int)(b & 0x3Fu);
+  return (float)q * ((b & 0x40u) ? s * 4.0f : s * 0.25f);
+}
+
+// Scale from a group absmax (device side of compute_scales): fl32(absmax / 127), 0 -> 1,
+// clamped to the valid range.
+__device__ __forceinline__ float scale_from_absmax(float a) {
+  if (a == 0.0f) return 1.0f;
+  float s = a / 127.0f;
+  return fminf(fmaxf(s, 0x1p-100f), 0x1p100f);
+}
+
+// |v| if finite, else 0 (absmax ignores NaN and infinities).
+__device__ __forceinline__ float finite_abs(float v) {
+  float a = fabsf(v);
+  return (a <= 3.402823466e38f) ? a : 0.0f;
+}
+
+// Wave-uniform value in an SGPR (so loads indexed by it can go through the scalar cache).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace qssm

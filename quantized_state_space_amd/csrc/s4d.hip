@@ -1,0 +1,205 @@
+// a5-a7, S4D form: diagonal LTI scan with int8 parameters and input, fp32 or int16 state.
+//
+// "Quantizing Small-Scale State-Space Models for Edge AI", abstract: an S4D layer with quantized
+// parameters and activations, where A and the internal state are the sensitive parts and components
+// may use different precisions. Per channel h and complex state n:
+//   Abar = exp(dt Ah), Bbar = (Abar - 1)/Ah Bh (zero-order hold), h_t = Abar h_{t-1} + Bbar u_t,
+//   y_t = Re(sum_n Ch h_t) + D u_t.
+//
+// Mapping: one wave per (batch, channel) chain set, lane = state n (N <= 64 * NPL). The input u_t
+// is the same for every lane of the wave, so it is read with scalar loads. Each lane keeps its
+// complex state, Abar, Bbar, Ch in registers (computed once in the prologue, with expm1 for
+// Abar - 1 to keep small dt accurate). The readout sum over states is a transpose through LDS:
+// lane n writes its term for 64 steps, then lane t sums row t.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+using namespace qssm;
+
+namespace {
+
+constexpr int kBlk = 64;  // time steps per readout block
+
+struct S4dParams {
+  int64_t B, L, H, N;
+  const int8_t* uq;
+  const float* u_scale;
+  const int8_t* wq;
+  const float* w_scale;
+  const int8_t *Are, *Aim, *Bre, *Bim, *Cre, *Cim;
+  const float *sAre, *sAim, *sBre, *sBim, *sCre, *sCim;
+  const float* log_dt;
+  const float* Dskip;
+  const float* state_scale;
+  const void* h0;
+  float* y;
+  void* h_last;
+};
+
+__device__ __forceinline__ float deq(int8_t q, float s) { return scale_ok(s) ? (float)q * s : 0.0f; }
+
+__device__ __forceinline__ float q16(float v, float s, float inv) {
+  return s * fminf(fmaxf(rintf(v * inv), -32768.0f), 32767.0f);
+}
+
+template <int NPL, int I16>
+__global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
+  __shared__ float red[4][kBlk][kBlk + 1];
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int64_t chain = (int64_t)blockIdx.x * 4 + w;
+  const bool active = chain < p.B * p.H;
+  const int64_t cc = active ? chain : 0;
+  const int64_t b = cc / p.H, hh = cc % p.H;
+  const int64_t L = p.L;
+
+  float ar[NPL], ai[NPL], br[NPL], bi[NPL], cr[NPL], ci[NPL], hr[NPL], hi[NPL];
+  const float dt = expf(p.log_dt[hh]);
+  const float ss = I16 ? p.state_scale[hh] : 1.0f;
+  const float sinv = I16 ? 1.0f / ss : 1.0f;
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const int64_t n = lane + 64 * k;
+    const bool on = n < p.N;
+    const int64_t pi = hh * p.N + (on ? n : 0);
+    const float Ar = on ? deq(p.Are[pi], p.sAre[hh]) : 0.0f;
+    const float Ai = on ? deq(p.Aim[pi], p.sAim[hh]) : 0.0f;
+    const float Br = on ? deq(p.Bre[pi], p.sBre[hh]) : 0.0f;
+    const float Bi = on ? deq(p.Bim[pi], p.sBim[hh]) : 0.0f;
+    cr[k] = on ? deq(p.Cre[pi], p.sCre[hh]) : 0.0f;
+    ci[k] = on ? deq(p.Cim[pi], p.sCim[hh]) : 0.0f;
+    // zero-order hold
+    const float re = dt * Ar, im = dt * Ai;
+    float sn, cs, sh, ch;
+    sincosf(im, &sn, &cs);
+    sincosf(0.5f * im, &sh, &ch);
+    const float er = expf(re);
+    ar[k] = er * cs;
+    ai[k] = er * sn;
+    const float em1_re = fmaf(expm1f(re), cs, -2.0f * sh * sh);  // Re(Abar - 1)
+    const float em1_im = er * sn;                                 // Im(Abar - 1)
+    const float den = Ar * Ar + Ai * Ai;
+    if (den == 0.0f) {
+      br[k] = dt * Br;
+      bi[k] = dt * Bi;
+    } else {
+      // (Abar - 1) / Ah
+      const float qr = (em1_re * Ar + em1_im * Ai) / den;
+      const float qi = (em1_im * Ar - em1_re * Ai) / den;
+      br[k] = qr * Br - qi * Bi;
+      bi[k] = qr * Bi + qi * Br;
+    }
+    hr[k] = 0.0f;
+    hi[k] = 0.0f;
+    if (p.h0 && on) {
+      const int64_t si = (b * p.H + hh) * p.N + n;
+      if (I16) {
+        const short2 v = reinterpret_cast<const short2*>(p.h0)[si];
+        hr[k] = ss * (float)v.x;
+        hi[k] = ss * (float)v.y;
+      } else {
+        const float2 v = reinterpret_cast<const float2*>(p.h0)[si];
+        hr[k] = v.x;
+        hi[k] = v.y;
+      }
+    }
+  }
+
+  // input scale: lifted scalar input, or per-channel input
+  const bool lifted = p.wq != nullptr;
+  float us;
+  const int8_t* urow;
+  if (lifted) {
+    us = p.u_scale[0] * p.w_scale[0];
+    us = (scale_ok(p.u_scale[0]) && scale_ok(p.w_scale[0])) ? us * (float)p.wq[hh] : 0.0f;
+    urow = p.uq + b * L;
+  } else {
+    us = scale_ok(p.u_scale[hh]) ? p.u_scale[hh] : 0.0f;
+    urow = p.uq + (b * p.H + hh) * L;
+  }
+  const float Dd = p.Dskip ? p.Dskip[hh] : 0.0f;
+
+  for (int64_t tb = 0; tb < L; tb += kBlk) {
+    const int nt = (int)((L - tb) < kBlk ? (L - tb) : kBlk);
+    // lane t holds the input of step tb + t; the loop broadcasts it with readlane (an SGPR)
+    const float u_lane = (lane < nt) ? us * (float)urow[tb + lane] : 0.0f;
+    for (int t = 0; t < nt; ++t) {
+      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_lane), t));
+      float yp = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) {
+        const float nr = fmaf(ar[k], hr[k], fmaf(-ai[k], hi[k], br[k] * u));
+        const float ni = fmaf(ar[k], hi[k], fmaf(ai[k], hr[k], bi[k] * u));
+        if (I16) {
+          hr[k] = q16(nr, ss, sinv);
+          hi[k] = q16(ni, ss, sinv);
+        } else {
+          hr[k] = nr;
+          hi[k] = ni;
+        }
+        yp = fmaf(cr[k], hr[k], fmaf(-ci[k], hi[k], yp));
+      }
+      red[w][t][lane] = yp;
+    }
+    __syncthreads();
+    if (lane < nt) {
+      float s = 0.0f;
+#pragma unroll 16
+      for (int j = 0; j < 64; ++j) s += red[w][lane][j];
+      if (active) p.y[(b * p.H + hh) * L + tb + lane] = fmaf(Dd, u_lane, s);
+    }
+    __syncthreads();
+  }
+
+  if (active && p.h_last) {
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int64_t n = lane + 64 * k;
+      if (n < p.N) {
+        const int64_t si = (b * p.H + hh) * p.N + n;
+        if (I16) {
+          reinterpret_cast<short2*>(p.h_last)[si] =
+              make_short2((short)rintf(hr[k] * sinv), (short)rintf(hi[k] * sinv));
+        } else {
+          reinterpret_cast<float2*>(p.h_last)[si] = make_float2(hr[k], hi[k]);
+        }
+      }
+    }
+  }
+}
+
+template <int NPL>
+qssm_status launch_s4d(const S4dParams& p, int i16, hipStream_t st) {
+  const unsigned grid = (unsigned)cdiv(p.B * p.H, 4);
+  if (i16) k_s4d<NPL, 1><<<grid, 256, 0, st>>>(p);
+  else k_s4d<NPL, 0><<<grid, 256, 0, st>>>(p);
+  return launch_status("s4d_scan");
+}
+
+}  // namespace
+
+extern "C" qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream) {
+  clear_error();
+  if (!a) return fail(QSSM_ERR_INVALID_ARG, "args is null");
+  if (a->batch < 0 || a->seqlen < 0 || a->channels < 1 || a->dstate < 1)
+    return fail(QSSM_ERR_INVALID_ARG, "bad shape");
+  if (a->dstate > 256) return fail(QSSM_ERR_UNSUPPORTED, "dstate above 256");
+  if (a->state_dtype != QSSM_F32 && a->state_dtype != QSSM_I16)
+    return fail(QSSM_ERR_INVALID_ARG, "state_dtype must be QSSM_F32 or QSSM_I16");
+  if (a->state_dtype == QSSM_I16 && !a->state_scale)
+    return fail(QSSM_ERR_INVALID_ARG, "QSSM_I16 needs state_scale");
+  if (a->batch == 0) return QSSM_OK;
+  if (!a->uq || !a->u_scale || (a->wq && !a->w_scale) || !a->A_re || !a->A_im || !a->B_re ||
+      !a->B_im || !a->C_re || !a->C_im || !a->A_re_s || !a->A_im_s || !a->B_re_s || !a->B_im_s ||
+      !a->C_re_s || !a->C_im_s || !a->log_dt || (a->seqlen > 0 && !a->y))
+    return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
+  S4dParams p{a->batch, a->seqlen, a->channels, a->dstate, a->uq, a->u_scale, a->wq, a->w_scale,
+              a->A_re, a->A_im, a->B_re, a->B_im, a->C_re, a->C_im, a->A_re_s, a->A_im_s,
+              a->B_re_s, a->B_im_s, a->C_re_s, a->C_im_s, a->log_dt, a->Dskip, a->state_scale,
+              a->h0, a->y, a->h_last};
+  const int i16 = a->state_dtype == QSSM_I16;
+  if (a->dstate <= 64) return launch_s4d<1>(p, i16, stream);
+  if (a->dstate <= 128) return launch_s4d<2>(p, i16, stream);
+  return launch_s4d<4>(p, i16, stream);
+}

@@ -1,0 +1,173 @@
+// a14: fused decode state update (generation stage), Mamba2-shaped.
+//
+// Quamba2, abstract: W8A8 generation for the Mamba2 backbone. One token per sequence: x, B and C
+// are quantized with static scales (the a1/a2 rule), then for every state element of head h
+//     state = exp(delta A_h) state + delta xh[p] Bh[n],    y[p] = sum_n Ch[n] state + D_h xh[p]
+//
+// The state (P x N per (b, h), fp32 or fp16) is the only large operand: the kernel is one
+// streaming read-modify-write pass over it. A workgroup owns one (b, h) state tile: it quantizes
+// and dequantizes the P x values and the N B/C values of its group into LDS once, then each thread
+// updates 4 consecutive states per 16-byte (fp32) / 8-byte (fp16) access with fully coalesced
+// wave accesses, and the readout sum over n is a shuffle reduction among the lanes sharing a row.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+using namespace qssm;
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct UpdParams {
+  int64_t B, nh, P, N;
+  int32_t Gbc, hpg, gs;
+  const float* x;
+  const uint8_t* x_group_of;
+  const float* x_scales;
+  const float* Bm;
+  const float* Cm;
+  const float* B_scales;
+  const float* C_scales;
+  const float* delta;
+  const float* A;
+  const float* Dskip;
+  void* state;
+  float* y;
+  int8_t* xq_out;
+  int8_t* Bq_out;
+  int8_t* Cq_out;
+};
+
+template <int F16, int R>  // R = N / 4 lanes share one state row
+__global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
+  extern __shared__ float smem[];
+  float* xs = smem;          // [P]
+  float* bs = xs + p.P;      // [N]
+  float* cs = bs + p.N;      // [N]
+
+  const int64_t bh = blockIdx.x;  // b * nh + h
+  const int64_t b = bh / p.nh, h = bh % p.nh;
+  const int64_t g = h / p.hpg;
+  const int ngs = (int)(p.N / p.gs);
+  const bool write_bc = (h % p.hpg) == 0;  // one head per group publishes the B/C codes
+
+  for (int64_t k = threadIdx.x; k < p.P; k += kThreads) {
+    const int64_t i = bh * p.P + k;
+    const float s = p.x_scales[p.x_group_of[h * p.P + k]];
+    const int8_t q = quant8(p.x[i], s);
+    if (p.xq_out) p.xq_out[i] = q;
+    xs[k] = scale_ok(s) ? (float)q * s : 0.0f;
+  }
+  for (int64_t n = threadIdx.x; n < p.N; n += kThreads) {
+    const int64_t i = (b * p.Gbc + g) * p.N + n;
+    const float sb = p.B_scales[g * ngs + n / p.gs];
+    const float sc = p.C_scales[g * ngs + n / p.gs];
+    const int8_t qb = quant8(p.Bm[i], sb), qc = quant8(p.Cm[i], sc);
+    if (write_bc) {
+      if (p.Bq_out) p.Bq_out[i] = qb;
+      if (p.Cq_out) p.Cq_out[i] = qc;
+    }
+    bs[n] = scale_ok(sb) ? (float)qb * sb : 0.0f;
+    cs[n] = scale_ok(sc) ? (float)qc * sc : 0.0f;
+  }
+  __syncthreads();
+
+  const float dt = p.delta[bh];
+  const float dA = expf(dt * p.A[h]);
+  const float Dh = p.Dskip ? p.Dskip[h] : 0.0f;
+  const int64_t n4 = p.N / 4;
+  const int64_t total4 = p.P * n4;  // 4-element chunks of the tile
+  const int lane = threadIdx.x & 63;
+
+  for (int64_t base = 0; base < total4; base += kThreads) {
+    const int64_t f = base + threadIdx.x;
+    const bool on = f < total4;
+    const int64_t row = on ? f / n4 : 0;
+    const int64_t n0 = on ? (f - row * n4) * 4 : 0;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    if (on) {
+      if (F16) {
+        const uint2 raw = reinterpret_cast<const uint2*>(p.state)[bh * total4 + f];
+        const __half2 lo = *reinterpret_cast<const __half2*>(&raw.x);
+        const __half2 hi = *reinterpret_cast<const __half2*>(&raw.y);
+        s[0] = __low2float(lo); s[1] = __high2float(lo);
+        s[2] = __low2float(hi); s[3] = __high2float(hi);
+      } else {
+        const float4 v = reinterpret_cast<const float4*>(p.state)[bh * total4 + f];
+        s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
+      }
+    }
+    const float dtx = dt * xs[row];
+    float yp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s[k] = fmaf(dA, s[k], dtx * bs[n0 + k]);
+      yp = fmaf(cs[n0 + k], s[k], yp);
+    }
+    if (on) {
+      if (F16) {
+        __half2 lo = __floats2half2_rn(s[0], s[1]);
+        __half2 hi = __floats2half2_rn(s[2], s[3]);
+        uint2 raw;
+        raw.x = *reinterpret_cast<const unsigned*>(&lo);
+        raw.y = *reinterpret_cast<const unsigned*>(&hi);
+        reinterpret_cast<uint2*>(p.state)[bh * total4 + f] = raw;
+      } else {
+        reinterpret_cast<float4*>(p.state)[bh * total4 + f] = make_float4(s[0], s[1], s[2], s[3]);
+      }
+    }
+    // rows occupy R consecutive lanes (R divides 64 and kThreads): reduce within them
+#pragma unroll
+    for (int off = R / 2; off > 0; off >>= 1) yp += __shfl_xor(yp, off, 64);
+    if (on && (lane % R) == 0) p.y[bh * p.P + row] = fmaf(Dh, xs[row], yp);
+  }
+}
+
+template <int R>
+qssm_status launch_r(const UpdParams& p, int f16, hipStream_t st) {
+  const size_t smem = (size_t)(p.P + 2 * p.N) * sizeof(float);
+  const unsigned grid = (unsigned)(p.B * p.nh);
+  if (f16) k_state_update<1, R><<<grid, kThreads, smem, st>>>(p);
+  else k_state_update<0, R><<<grid, kThreads, smem, st>>>(p);
+  return launch_status("state_update");
+}
+
+}  // namespace
+
+extern "C" qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t stream) {
+  clear_error();
+  if (!a) return fail(QSSM_ERR_INVALID_ARG, "args is null");
+  const int64_t B = a->batch, nh = a->nheads, P = a->headdim, N = a->dstate;
+  if (B < 0 || nh < 1 || P < 1 || N < 1) return fail(QSSM_ERR_INVALID_ARG, "bad shape");
+  if (a->ngroups < 1 || nh % a->ngroups != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "ngroups must divide nheads");
+  if (a->bc_group_size < 1 || N % a->bc_group_size != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "bc_group_size must divide dstate");
+  if (a->x_groups < 1 || a->x_groups > 256) return fail(QSSM_ERR_INVALID_ARG, "x_groups not in 1..256");
+  if (a->state_dtype != QSSM_F32 && a->state_dtype != QSSM_F16)
+    return fail(QSSM_ERR_INVALID_ARG, "state_dtype must be QSSM_F32 or QSSM_F16");
+  const int64_t R = N / 4;
+  if (N % 4 != 0 || !(R == 1 || R == 2 || R == 4 || R == 8 || R == 16 || R == 32 || R == 64))
+    return fail(QSSM_ERR_UNSUPPORTED, "dstate must be 4 * 2^k with 4 <= dstate <= 256");
+  if ((P + 2 * N) * 4 > 64 * 1024) return fail(QSSM_ERR_UNSUPPORTED, "headdim too large");
+  if (B == 0) return QSSM_OK;
+  if (!a->x || !a->x_group_of || !a->x_scales || !a->B || !a->C || !a->B_scales || !a->C_scales ||
+      !a->delta || !a->A || !a->state || !a->y)
+    return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
+  if ((uintptr_t)a->state % 16 != 0) return fail(QSSM_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  if (B * nh > 0x7fffffffLL) return fail(QSSM_ERR_INVALID_ARG, "batch * nheads too large");
+  UpdParams p{B, nh, P, N, a->ngroups, (int32_t)(nh / a->ngroups), a->bc_group_size, a->x,
+              a->x_group_of, a->x_scales, a->B, a->C, a->B_scales, a->C_scales, a->delta, a->A,
+              a->Dskip, a->state, a->y, a->xq_out, a->Bq_out, a->Cq_out};
+  const int f16 = a->state_dtype == QSSM_F16;
+  switch (R) {
+    case 1: return launch_r<1>(p, f16, stream);
+    case 2: return launch_r<2>(p, f16, stream);
+    case 4: return launch_r<4>(p, f16, stream);
+    case 8: return launch_r<8>(p, f16, stream);
+    case 16: return launch_r<16>(p, f16, stream);
+    case 32: return launch_r<32>(p, f16, stream);
+    default: return launch_r<64>(p, f16, stream);
+  }
+}

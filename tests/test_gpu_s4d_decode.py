@@ -1,0 +1,145 @@
+"""GPU parity of the S4D LTI scan (fp32 and int16 state) and of the fused decode state update
+(fp32 and fp16 state) against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.pipelines as op
+import qssm_synth as synth
+
+pytestmark = pytest.mark.gpu
+
+
+def assert_rows_close(y, ref, tol, what="y"):
+    err = oracle.rowwise_error(y, ref)
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= tol, f"{what}: max row error {err.max():.3e} at row {worst}"
+
+
+# ------------------------------------------------------------------------------------------------
+# S4D
+
+def s4d_layer(dev, inp, **kw):
+    import quantized_state_space_amd.workloads as wl
+    return wl.S4dLayer(inp, dev, **kw)
+
+
+def check_s4d_codes(lay, ref):
+    assert np.array_equal(lay.uq.cpu().numpy()[:, 0, :], ref["uq"])
+    assert np.array_equal(lay.wq.cpu().numpy().ravel(), ref["wq"])
+    for k in op.PLANES:
+        assert np.array_equal(lay.params[k].cpu().numpy(), ref["codes"][k]), k
+        assert np.array_equal(lay.scales[k].cpu().numpy(), ref["scales"][k]), k
+
+
+@pytest.mark.parametrize("shape", [dict(batch=16, seqlen=784, channels=128, dstate=64),
+                                   dict(batch=3, seqlen=130, channels=5, dstate=64),
+                                   dict(batch=2, seqlen=65, channels=4, dstate=100),
+                                   dict(batch=1, seqlen=64, channels=3, dstate=17)])
+def test_s4d_fp32_state(dev, shape):
+    import torch
+    print(f"\n[s4d fp32 {shape}]", flush=True)
+    inp = synth.s4d_inputs(cfg=2, with_h0=True, **shape)
+    lay = s4d_layer(dev, inp, with_h0=True)
+    lay.step()
+    torch.cuda.synchronize()
+    ref = op.s4d(inp, with_h0=True)
+    check_s4d_codes(lay, ref)
+    assert_rows_close(lay.y.cpu().numpy(), ref["y"], 2e-3)
+    hl = lay.h_last.cpu().numpy()
+    assert_rows_close(hl[..., 0] + 1j * hl[..., 1], ref["h_last"], 2e-3, "h_last")
+
+
+def test_s4d_int16_state(dev):
+    import torch
+    print("\n[s4d int16 state, full size]", flush=True)
+    inp = synth.s4d_inputs(cfg=2, with_h0=True)
+    ss = op.s4d_state_scale(inp)
+    from quantized_state_space_amd import QSSM_I16
+    lay = s4d_layer(dev, inp, state_dtype=QSSM_I16, state_scale=ss, with_h0=True)
+    lay.step()
+    torch.cuda.synchronize()
+    ref = op.s4d(inp, state_scale=ss, with_h0=True)
+    check_s4d_codes(lay, ref)
+    assert_rows_close(lay.y.cpu().numpy(), ref["y"], 1e-2)
+    hl = lay.h_last.cpu().numpy().astype(np.float64) * ss[None, :, None, None]
+    assert_rows_close(hl[..., 0] + 1j * hl[..., 1], ref["h_last"], 1e-2, "h_last")
+
+
+# ------------------------------------------------------------------------------------------------
+# Decode
+
+def decode_run(dev, params, steps, state_dtype, sample=None, groups_per_block=8):
+    import torch
+    import quantized_state_space_amd.workloads as wl
+    lay = wl.DecodeLayer(params, dev, state_dtype=state_dtype, emit_codes=True,
+                         groups_per_block=groups_per_block)
+    got = dict(xq=[], Bq=[], Cq=[], y=[])
+    sel = slice(None) if sample is None else sample
+    for inp in steps:
+        lay.load_inputs(inp)
+        lay.step()
+        torch.cuda.synchronize()
+        for k, v in zip(("xq", "Bq", "Cq"), lay.codes):
+            got[k].append(v.cpu().numpy())
+        got["y"].append(lay.y.cpu().numpy()[sel])
+    got["state"] = lay.state[sel].float().cpu().numpy() if sample is None else \
+        lay.state[torch.as_tensor(sample, device=lay.state.device)].float().cpu().numpy()
+    return lay, got
+
+
+@pytest.mark.parametrize("state", ["f32", "f16"])
+def test_decode_small(dev, state):
+    import quantized_state_space_amd as qs
+    print(f"\n[decode small {state}]", flush=True)
+    dims = dict(batch=6, nheads=16, headdim=64, dstate=128, ngroups=2)
+    params = synth.decode_params(cfg=15, **dims)
+    steps = [synth.decode_step_inputs(k, cfg=15, **dims) for k in range(5)]
+    sd = qs.QSSM_F32 if state == "f32" else qs.QSSM_F16
+    if sd == qs.QSSM_F16:  # the fp16 state starts from the fp16-rounded initial state on both sides
+        params["state0"] = params["state0"].astype(np.float16).astype(np.float32)
+    lay, got = decode_run(dev, params, steps, sd)
+    ref = op.decode(params, steps)
+    assert np.array_equal(lay.group_of, ref["group_of"])
+    assert np.array_equal(lay.xs.cpu().numpy(), ref["xs"])
+    tol = 2e-3 if state == "f32" else 1e-2
+    for k in range(len(steps)):
+        for name in ("xq", "Bq", "Cq"):
+            assert np.array_equal(got[name][k], ref[name][k]), (name, k)
+        assert_rows_close(got["y"][k], ref["y"][k], tol)
+    assert_rows_close(got["state"], ref["state"], tol, "state")
+
+
+def test_decode_other_shapes(dev):
+    import quantized_state_space_amd as qs
+    print("\n[decode N=16 P=7]", flush=True)
+    dims = dict(batch=3, nheads=4, headdim=7, dstate=16, ngroups=4)
+    params = synth.decode_params(cfg=16, **dims)
+    steps = [synth.decode_step_inputs(k, cfg=16, **dims) for k in range(3)]
+    lay, got = decode_run(dev, params, steps, qs.QSSM_F32, groups_per_block=2)
+    ref = op.decode(params, steps, groups_per_block=2)
+    for k in range(len(steps)):
+        for name in ("xq", "Bq", "Cq"):
+            assert np.array_equal(got[name][k], ref[name][k]), (name, k)
+        assert_rows_close(got["y"][k], ref["y"][k], 2e-3)
+    assert_rows_close(got["state"], ref["state"], 2e-3, "state")
+
+
+def test_decode_full_size_sampled(dev):
+    """Mamba2-8B-shaped decode (B=256, nh=128, P=64, N=128, fp32 state), 8 steps, launched as the
+    benchmark does; codes of every sequence bit-exact, y and state of sampled sequences."""
+    import quantized_state_space_amd as qs
+    print("\n[decode full size]", flush=True)
+    params = synth.decode_params(cfg=5)
+    steps = [synth.decode_step_inputs(k, cfg=5) for k in range(8)]
+    sample = np.array([0, 77, 255])
+    lay, got = decode_run(dev, params, steps, qs.QSSM_F32, sample=sample)
+    ref = op.decode(params, steps, batches=sample)
+    full = op.decode(params, steps[:1], batches=np.arange(256))  # codes of every sequence, step 0
+    for name in ("xq", "Bq", "Cq"):
+        assert np.array_equal(got[name][0], full[name][0]), name
+    for k in range(len(steps)):
+        for name in ("xq", "Bq", "Cq"):
+            assert np.array_equal(got[name][k][sample], ref[name][k]), (name, k)
+        assert_rows_close(got["y"][k], ref["y"][k], 2e-3)
+    assert_rows_close(got["state"], ref["state"], 2e-3, "state")

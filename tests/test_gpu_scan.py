@@ -1,0 +1,136 @@
+"""GPU parity of the Mamba1 W8A8 selective scan (quantize x, B, C, then scan) against the oracle:
+bit-exact codes and scales, outputs within the fp32-state tolerance per (b, channel) row."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.pipelines as op
+import qssm_synth as synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 2e-3   # max relative error per row, fp32 state
+TOL_F16_OUT = 2e-3  # fp16 output rounding (2^-11 relative) stays inside the same bar
+
+
+def layer(dev, inp, G, gs, **kw):
+    import quantized_state_space_amd.workloads as wl
+    return wl.Mamba1Layer(inp, G, gs, dev, **kw)
+
+
+def check_codes(lay, ref, soft_edge=False):
+    import torch
+    torch.cuda.synchronize()
+    assert np.array_equal(lay.perm, ref["perm"]) and np.array_equal(lay.group_of, ref["group_of"])
+    assert np.array_equal(lay.xs.cpu().numpy(), ref["xs"])
+    assert np.array_equal(lay.bs.cpu().numpy(), ref["bs"])
+    assert np.array_equal(lay.cs.cpu().numpy(), ref["cs"])
+    got_x = lay.xq.cpu().numpy()
+    assert np.array_equal(got_x.view(np.uint8), np.asarray(ref["xq"]).view(np.uint8))
+    assert np.array_equal(lay.Bq.cpu().numpy(), ref["Bq"])
+    assert np.array_equal(lay.Cq.cpu().numpy(), ref["Cq"])
+
+
+def assert_rows_close(y, ref, tol, what="y"):
+    err = oracle.rowwise_error(y, ref)
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= tol, f"{what}: max row error {err.max():.3e} at row {worst}"
+    return err.max()
+
+
+def test_c1_tiny_dynamic_scales(dev):
+    """Tiny Mamba1 layer: B=1, L=256, D=64, N=16, per-tensor x scale, 4 state groups of 4, scales
+    from the tensors themselves (computed on the device)."""
+    print("\n[c1 tiny mamba1]", flush=True)
+    inp = synth.c1_inputs()
+    lay = layer(dev, inp, G=1, gs=4, dynamic_scales=True)
+    lay.step()
+    ref = op.mamba1(inp, G=1, gs=4, dynamic=True)
+    check_codes(lay, ref)
+    assert_rows_close(lay.y.cpu().numpy(), ref["y"], TOL_F32)
+    assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
+
+
+@pytest.mark.parametrize("B,D,L,N,G,soft", [(2, 100, 300, 16, 3, False), (1, 64, 77, 4, 2, False),
+                                             (2, 192, 64, 8, 5, False), (1, 128, 200, 32, 4, False),
+                                             (1, 64, 129, 64, 2, False), (2, 130, 301, 16, 4, True)])
+def test_ragged_shapes_static_scales(dev, B, D, L, N, G, soft):
+    print(f"\n[mamba1 B={B} D={D} L={L} N={N} G={G} softedge={soft}]", flush=True)
+    import quantized_state_space_amd as qs
+    inp = synth.mamba1_inputs(cfg=11, batch=B, seqlen=L, dim=D, dstate=N, x_dist="student_t",
+                              calib_batch=1, with_h0=True)
+    gs = 4 if N >= 4 else 1
+    xc = qs.QSSM_X_SOFTEDGE if soft else qs.QSSM_X_INT8
+    lay = layer(dev, inp, G=G, gs=gs, x_code=xc, with_h0=True)
+    lay.step()
+    ref = op.mamba1(inp, G=G, gs=gs, soft_edge=soft, with_h0=True)
+    if soft:
+        assert np.array_equal(lay.sL.cpu().numpy(), ref["L"])
+        assert np.array_equal(lay.sH.cpu().numpy(), ref["H"])
+    check_codes(lay, ref)
+    assert_rows_close(lay.y.cpu().numpy(), ref["y"], TOL_F32)
+    assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
+
+
+def test_fp16_output(dev):
+    import quantized_state_space_amd as qs
+    print("\n[mamba1 fp16 y]", flush=True)
+    inp = synth.mamba1_inputs(cfg=12, batch=1, seqlen=160, dim=64, dstate=16, calib_batch=1)
+    lay = layer(dev, inp, G=2, gs=4, y_dtype=qs.QSSM_F16)
+    lay.step()
+    ref = op.mamba1(inp, G=2, gs=4)
+    assert_rows_close(lay.y.float().cpu().numpy(), ref["y"], TOL_F16_OUT)
+
+
+def test_split_resume_and_determinism(dev):
+    """scan(L) == scan(L1) then scan(L2, h0 = h_last); two runs are bitwise identical."""
+    import torch
+    import quantized_state_space_amd as qs
+    print("\n[mamba1 resume]", flush=True)
+    inp = synth.mamba1_inputs(cfg=13, batch=2, seqlen=96, dim=64, dstate=16, calib_batch=1)
+    lay = layer(dev, inp, G=2, gs=4)
+    lay.step()
+    torch.cuda.synchronize()
+    y_full, h_full = lay.y.clone(), lay.h_last.clone()
+    lay.scan()
+    torch.cuda.synchronize()
+    assert torch.equal(lay.y, y_full) and torch.equal(lay.h_last, h_full)
+    L1 = 40
+    outs = []
+    h0 = None
+    for sl in (slice(0, L1), slice(L1, 96)):
+        xq = lay.xq[..., sl].contiguous()
+        y = torch.empty_like(xq, dtype=torch.float32)
+        hl = torch.empty_like(h_full)
+        a = qs.scan_args(xq, qs.QSSM_X_INT8, lay.group_t, lay.xs, lay.delta[..., sl].contiguous(),
+                         lay.A, lay.Bq[..., sl].contiguous(), lay.Cq[..., sl].contiguous(), lay.bs,
+                         lay.cs, 4, y, Dskip=lay.D, h0=h0, h_last=hl)
+        ws = torch.empty(qs.qssm_scan_workspace_size(a), dtype=torch.uint8, device=dev)
+        qs.qssm_scan_w8a8(a, ws)
+        outs.append(y)
+        h0 = hl
+    torch.cuda.synchronize()
+    y2 = torch.cat(outs, dim=-1).cpu().numpy()
+    assert_rows_close(y2, y_full.cpu().numpy().astype(np.float64), 1e-5)
+    assert_rows_close(h0.cpu().numpy(), h_full.cpu().numpy().astype(np.float64), 1e-5)
+
+
+@pytest.mark.parametrize("soft", [False, True])
+def test_c3_full_size_sampled(dev, soft):
+    """Mamba1-130M-shaped layer (B=8, L=2048, D=1536, N=16, 8 clustered x groups), launched exactly
+    as the benchmark does: every code bit-exact, y and h_last checked on sampled (b, channel) rows."""
+    import quantized_state_space_amd as qs
+    print(f"\n[c3 full size softedge={soft}]", flush=True)
+    inp = synth.c3_inputs()
+    lay = layer(dev, inp, G=8, gs=4, x_code=qs.QSSM_X_SOFTEDGE if soft else qs.QSSM_X_INT8)
+    lay.step()
+    r = np.random.default_rng(3)
+    bsel = np.repeat(np.arange(8), 6)
+    dsel = np.concatenate([r.choice(1536, 6, replace=False) for _ in range(8)])
+    dsel[:2] = [0, 1535]
+    ref = op.mamba1(inp, G=8, gs=4, soft_edge=soft, rows=(bsel, dsel))
+    check_codes(lay, ref)
+    y = lay.y.cpu().numpy()[bsel, dsel]
+    h = lay.h_last.cpu().numpy()[bsel, dsel]
+    assert_rows_close(y, ref["y_rows"], TOL_F32)
+    assert_rows_close(h, ref["h_rows"], TOL_F32, "h_last")
