@@ -165,9 +165,10 @@ def s4d(inp, state_scale=None, with_h0=False):
     return dict(uq=uq, wq=wq, su=su, sw=sw, codes=codes, scales=scales, y=y, h_last=hl)
 
 
-def s4d_state_scale(inp, headroom=1.25):
+def s4d_state_scale(inp, headroom=1.25, with_h0=False):
     """Per-channel int16 state scale from the fp64 run: headroom * max |Re|, |Im| of the state over
-    (b, t, n) / 32767 (the state sensitivity reading of the S4D page)."""
+    (b, t, n) / 32767 (the state sensitivity reading of the S4D page). A channel whose state never
+    leaves 0 gets the smallest valid scale."""
     u = inp["u"]
     B, L = u.shape
     H, N = inp["A_re"].shape
@@ -182,10 +183,13 @@ def s4d_state_scale(inp, headroom=1.25):
     for h in range(H):
         Ab, Bb = s4d_zoh(deq["A_re"][h] + 1j * deq["A_im"][h], deq["B_re"][h] + 1j * deq["B_im"][h], dt[h])
         st = np.zeros((B, N), np.complex128)
+        if with_h0:
+            st = inp["h0_re"][:, h].astype(np.float64) + 1j * inp["h0_im"][:, h].astype(np.float64)
+            m[h] = max(np.abs(st.real).max(), np.abs(st.imag).max())
         for t in range(L):
             st = Ab[None, :] * st + Bb[None, :] * uh[:, h, t][:, None]
             m[h] = max(m[h], np.abs(st.real).max(), np.abs(st.imag).max())
-    return (headroom * m / 32767.0).astype(np.float32)
+    return np.maximum(headroom * m / 32767.0, 2.0 ** -100).astype(np.float32)
 
 
 # ------------------------------------------------------------------------------------------------

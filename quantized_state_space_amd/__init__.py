@@ -189,9 +189,12 @@ def qssm_softedge_decode(code, group_of, G, s, out, stream=None):
 # ------------------------------------------------------------------------------------------------
 # Recurrences
 
-def _fill(st, **kw):
+def _fill(st, keep=(), **kw):
+    """Sets the fields of an argument struct. The struct keeps a reference to every tensor whose
+    address it holds (`keep`), so temporaries passed by the caller outlive the struct."""
     for k, v in kw.items():
         setattr(st, k, v)
+    st._keep = [t for t in keep if t is not None]
     return st
 
 
@@ -204,7 +207,8 @@ def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_sca
     Gbc = Bq.shape[1]
     xdt = torch.int8 if x_code == QSSM_X_INT8 else torch.uint8
     ydt = QSSM_F32 if y.dtype == torch.float32 else QSSM_F16
-    return _fill(ScanArgs(), batch=B, seqlen=L, dim=D, dstate=N, x_code=x_code,
+    keep = (x, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last)
+    return _fill(ScanArgs(), keep=keep, batch=B, seqlen=L, dim=D, dstate=N, x_code=x_code,
                  x_groups=int(x_scales.numel()), x=_ptr(x, xdt, "x"),
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"),
@@ -240,7 +244,9 @@ def s4d_args(uq, u_scale, params, scales, log_dt, y, wq=None, w_scale=None, Dski
     kw.update({k + "_s": _ptr(scales[k], torch.float32, k + "_s")
                for k in ("A_re", "A_im", "B_re", "B_im", "C_re", "C_im")})
     st_t = torch.float32 if state_dtype == QSSM_F32 else torch.int16
-    return _fill(S4dArgs(), batch=B, seqlen=L, channels=H, dstate=N, uq=_ptr(uq, torch.int8, "uq"),
+    keep = (uq, u_scale, log_dt, y, wq, w_scale, Dskip, state_scale, h0, h_last,
+            *params.values(), *scales.values())
+    return _fill(S4dArgs(), keep=keep, batch=B, seqlen=L, channels=H, dstate=N, uq=_ptr(uq, torch.int8, "uq"),
                  u_scale=_ptr(u_scale, torch.float32, "u_scale"), wq=_ptr(wq, torch.int8, "wq", True),
                  w_scale=_ptr(w_scale, torch.float32, "w_scale", True),
                  log_dt=_ptr(log_dt, torch.float32, "log_dt"),
@@ -260,7 +266,8 @@ def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs,
     B, L, nh, P = xq.shape
     Gbc, N = Bq.shape[2], Bq.shape[3]
     ydt = QSSM_F32 if y.dtype == torch.float32 else QSSM_F16
-    return _fill(SsdArgs(), batch=B, seqlen=L, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
+    keep = (xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last)
+    return _fill(SsdArgs(), keep=keep, batch=B, seqlen=L, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
                  chunk=chunk, x_groups=int(x_scales.numel()), xq=_ptr(xq, torch.int8, "xq"),
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"),
@@ -290,7 +297,9 @@ def update_args(x, x_group_of, x_scales, Bm, Cm, B_scales, C_scales, gs, delta, 
     B, nh, P = x.shape
     Gbc, N = Bm.shape[1], Bm.shape[2]
     sdt = QSSM_F32 if state.dtype == torch.float32 else QSSM_F16
-    return _fill(UpdateArgs(), batch=B, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
+    keep = (x, x_group_of, x_scales, Bm, Cm, B_scales, C_scales, delta, A, state, y, Dskip, xq_out,
+            Bq_out, Cq_out)
+    return _fill(UpdateArgs(), keep=keep, batch=B, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
                  x_groups=int(x_scales.numel()), x=_ptr(x, torch.float32, "x"),
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"), B=_ptr(Bm, torch.float32, "B"),

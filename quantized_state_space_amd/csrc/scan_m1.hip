@@ -26,6 +26,7 @@ using namespace qssm;
 namespace {
 
 constexpr int kT = 32;          // time steps per block
+constexpr int kPadRows = 64;    // zero rows after L in every staged plane (>= kT + largest batch)
 constexpr int kLanes = 64;      // channels per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -39,44 +40,42 @@ struct ScanParams {
   const float* x_scales;
   const float* delta;
   const float* A;
-  const float* stage;  // [B, Gbc, N/4, L, 8]: (Bh[4], Ch[4]) per state quad and step
+  const float* stage;  // [B, Gbc, N/NS, L, 2*NS]: (Bh[NS], Ch[NS]) per wave plane and step
   const float* Dskip;
   const float* h0;
   void* y;
   float* h_last;
 };
 
-// Dequantize B and C once into the staging layout read by the scan.
+// Dequantize B and C once into the staging layout read by the scan: for every (b, g), the states
+// are cut into planes of `ns` consecutive states (the states one wave owns), and each plane stores
+// per step the ns B values followed by the ns C values: [B, Gbc, N/ns, L, 2*ns] fp32.
 __global__ __launch_bounds__(256) void k_stage_bc(const int8_t* __restrict__ Bq,
                                                   const int8_t* __restrict__ Cq,
                                                   const float* __restrict__ Bs,
                                                   const float* __restrict__ Cs, int64_t B,
-                                                  int Gbc, int N, int64_t L, int gs,
+                                                  int Gbc, int N, int64_t L, int gs, int ns,
                                                   float* __restrict__ stage) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over (b, g, quad, t)
-  const int nq = N / 4;
-  const int64_t total = B * Gbc * nq * L;
+  const int64_t Lp = L + kPadRows;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over (b, g, n, t < Lp)
+  const int64_t total = B * Gbc * N * Lp;
   if (idx >= total) return;
-  const int64_t t = idx % L;
-  const int64_t r = idx / L;  // (b, g, quad)
-  const int quad = (int)(r % nq);
-  const int64_t bg = r / nq;
+  const int64_t t = idx % Lp;
+  const int64_t r = idx / Lp;  // (b, g, n)
+  const int n = (int)(r % N);
+  const int64_t bg = r / N;
   const int g = (int)(bg % Gbc);
   const int ngs = N / gs;
-  float4 vb, vc;
-  float* pb = &vb.x;
-  float* pc = &vc.x;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int n = quad * 4 + k;
-    const int64_t src = (bg * N + n) * L + t;
-    const float sb = Bs[g * ngs + n / gs], sc = Cs[g * ngs + n / gs];
-    pb[k] = scale_ok(sb) ? (float)Bq[src] * sb : 0.0f;
-    pc[k] = scale_ok(sc) ? (float)Cq[src] * sc : 0.0f;
+  const float sb = Bs[g * ngs + n / gs], sc = Cs[g * ngs + n / gs];
+  float vb = 0.0f, vc = 0.0f;  // rows past L are zero (read by the last batches, times delta = 0)
+  if (t < L) {
+    vb = scale_ok(sb) ? (float)Bq[r * L + t] * sb : 0.0f;
+    vc = scale_ok(sc) ? (float)Cq[r * L + t] * sc : 0.0f;
   }
-  float4* dst = reinterpret_cast<float4*>(stage + idx * 8);
-  dst[0] = vb;
-  dst[1] = vc;
+  const int plane = n / ns, k = n % ns;
+  float* dst = stage + (((bg * (N / ns) + plane) * Lp + t) * (2 * ns));
+  dst[k] = vb;
+  dst[ns + k] = vc;
 }
 
 template <int XCODE>
@@ -85,9 +84,10 @@ __device__ __forceinline__ float xval(uint32_t byte, float s) {
   return (float)(int8_t)(byte & 0xFFu) * s;
 }
 
-template <int NS, int W, int XCODE, int YF16>
+template <int NS, int W, int XCODE, int YF16, int kBatch>
 __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   __shared__ float ybuf[2][W][kT][kLanes];
+  constexpr int kS = 2 * NS;  // staged floats per step
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -114,10 +114,10 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 
   const float* __restrict__ drow = p.delta + (b * p.D + dc) * L;
   const uint8_t* __restrict__ xrow = reinterpret_cast<const uint8_t*>(p.x) + (b * p.D + dc) * L;
-  // this wave's state quads for (b, g): quad-plane stride L*8 floats. Read through the constant
-  // address space: the addresses are wave-uniform, so these become scalar (SMEM) loads.
-  const cfloat* st = (const cfloat*)(
-      p.stage + (((b * p.Gbc + g) * (p.N / 4) + w * (NS / 4)) * L) * 8);
+  // this wave's plane of staged (Bh, Ch): kS floats per step, read through the constant address
+  // space (wave-uniform addresses -> scalar loads into SGPRs)
+  const cfloat* st =
+      (const cfloat*)(p.stage + ((b * p.Gbc + g) * (p.N / NS) + w) * (L + kPadRows) * kS);
   const bool vec_ok = (L % 16) == 0;
 
   float dl[kT];
@@ -155,29 +155,48 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     }
   };
 
+  // Scalar loads return out of order, so waiting for one means waiting for all: the staged values
+  // are fetched one batch of steps ahead and the loop drains the scalar queue (lgkmcnt 0) once per
+  // batch, right before issuing the next batch, so each batch's latency hides behind the previous
+  // batch's arithmetic. Steps past L read the zero pad rows (times delta = 0).
+  float bcur[kBatch][kS], bnxt[kBatch][kS];
+  auto sload = [&](int t0, float (&dst)[kBatch][kS]) {
+    const cfloat* src = st + (int64_t)t0 * kS;
+#pragma unroll
+    for (int s2 = 0; s2 < kBatch; ++s2)
+#pragma unroll
+      for (int j = 0; j < kS; ++j) dst[s2][j] = src[s2 * kS + j];
+  };
+
   load_block(0, dl, xq);
+  sload(0, bcur);
   int buf = 0;
   for (int64_t tb = 0; tb < L; tb += kT) {
     if (tb + kT < L) load_block(tb + kT, dn, xn);
 
 #pragma unroll
-    for (int t = 0; t < kT; ++t) {
-      // steps past L (ragged tail) reuse row L-1: finite values times delta = 0 leave h unchanged
-      const int64_t trow = (tb + t < L) ? tb + t : L - 1;
-      const cfloat* bc = st + trow * 8;
-      const float xh = xval<XCODE>((xq[t / 4] >> (8 * (t % 4))) & 0xFFu, sx);
-      const float dt = dl[t];
-      const float dtx = dt * xh;
-      float yp = 0.0f;
+    for (int bt = 0; bt < kT; bt += kBatch) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the current batch has landed
+      sload((int)tb + bt + kBatch, bnxt);
 #pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const cfloat* q4 = bc + (k / 4) * L * 8;
-        const float bh = q4[k % 4], ch = q4[4 + k % 4];
-        const float dA = __builtin_amdgcn_exp2f(dt * a2[k]);
-        h[k] = fmaf(dA, h[k], dtx * bh);
-        yp = fmaf(ch, h[k], yp);
+      for (int s2 = 0; s2 < kBatch; ++s2) {
+        const int t = bt + s2;
+        const float xh = xval<XCODE>((xq[t / 4] >> (8 * (t % 4))) & 0xFFu, sx);
+        const float dt = dl[t];
+        const float dtx = dt * xh;
+        float yp;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          const float dA = __builtin_amdgcn_exp2f(dt * a2[k]);
+          h[k] = fmaf(dA, h[k], dtx * bcur[s2][k]);
+          yp = (k == 0) ? bcur[s2][NS] * h[0] : fmaf(bcur[s2][NS + k], h[k], yp);
+        }
+        ybuf[buf][w][t][lane] = yp;
       }
-      ybuf[buf][w][t][lane] = yp;
+#pragma unroll
+      for (int s2 = 0; s2 < kBatch; ++s2)
+#pragma unroll
+        for (int j = 0; j < kS; ++j) bcur[s2][j] = bnxt[s2][j];
     }
     __syncthreads();
 
@@ -187,11 +206,11 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int t = w * kPer + j;
-      float s = 0.0f;
+      float sum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < W; ++ww) s += ybuf[buf][ww][t][lane];
+      for (int ww = 0; ww < W; ++ww) sum += ybuf[buf][ww][t][lane];
       const float xh = xval<XCODE>((xq[t / 4] >> (8 * (t % 4))) & 0xFFu, sx);
-      yo[j] = fmaf(Dd, xh, s);
+      yo[j] = fmaf(Dd, xh, sum);
     }
     const int64_t t0 = tb + w * kPer;
     if (valid) {
@@ -227,23 +246,26 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   }
 }
 
-template <int NS, int W>
+template <int NS, int W, int BATCH>
 qssm_status launch_scan(const ScanParams& p, int xcode, int yf16, hipStream_t st) {
   dim3 grid((unsigned)cdiv(p.D, kLanes), (unsigned)p.B);
   dim3 block(64 * W);
   if (xcode == QSSM_X_INT8) {
-    if (yf16) k_scan_m1<NS, W, QSSM_X_INT8, 1><<<grid, block, 0, st>>>(p);
-    else k_scan_m1<NS, W, QSSM_X_INT8, 0><<<grid, block, 0, st>>>(p);
+    if (yf16) k_scan_m1<NS, W, QSSM_X_INT8, 1, BATCH><<<grid, block, 0, st>>>(p);
+    else k_scan_m1<NS, W, QSSM_X_INT8, 0, BATCH><<<grid, block, 0, st>>>(p);
   } else {
-    if (yf16) k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 1><<<grid, block, 0, st>>>(p);
-    else k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 0><<<grid, block, 0, st>>>(p);
+    if (yf16) k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 1, BATCH><<<grid, block, 0, st>>>(p);
+    else k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 0, BATCH><<<grid, block, 0, st>>>(p);
   }
   return launch_status("scan_w8a8");
 }
 
+// states per wave for a state size N (the workgroup has N / NS waves)
+int states_per_wave(int64_t N) { return N == 8 ? 2 : (N == 64 ? 8 : 4); }
+
 size_t stage_bytes(const qssm_scan_args* a) {
-  return (size_t)a->batch * (size_t)a->bc_groups * (size_t)a->dstate * (size_t)a->seqlen * 2 *
-         sizeof(float);
+  return (size_t)a->batch * (size_t)a->bc_groups * (size_t)a->dstate *
+         (size_t)(a->seqlen + kPadRows) * 2 * sizeof(float);
 }
 
 }  // namespace
@@ -261,6 +283,7 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
   if (!a) return fail(QSSM_ERR_INVALID_ARG, "args is null");
   const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
   if (B < 0 || L < 0 || D < 1 || N < 1) return fail(QSSM_ERR_INVALID_ARG, "bad shape");
+  if (L > 0x7fffff00LL) return fail(QSSM_ERR_UNSUPPORTED, "seqlen must be below 2^31 - 256");
   if (a->x_code != QSSM_X_INT8 && a->x_code != QSSM_X_SOFTEDGE)
     return fail(QSSM_ERR_INVALID_ARG, "x_code must be QSSM_X_INT8 or QSSM_X_SOFTEDGE");
   if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16)
@@ -288,10 +311,11 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
   if ((size_t)((char*)stage - (char*)ws) + need > ws_bytes)
     return fail(QSSM_ERR_WORKSPACE, "workspace too small after 256-byte alignment");
 
-  const int64_t nstage = B * a->bc_groups * (N / 4) * L;
+  const int ns = states_per_wave(N);
+  const int64_t nstage = B * a->bc_groups * N * (L + kPadRows);
   if (nstage > 0) {
     k_stage_bc<<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
-        a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
+        a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size, ns,
         stage);
     if (qssm_status s = launch_status("scan_w8a8 staging")) return s;
   }
@@ -301,11 +325,11 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
                a->y, a->h_last};
   const int yf16 = a->y_dtype == QSSM_F16;
   switch (N) {
-    case 4: return launch_scan<4, 1>(p, a->x_code, yf16, stream);
-    case 8: return launch_scan<4, 2>(p, a->x_code, yf16, stream);
-    case 16: return launch_scan<4, 4>(p, a->x_code, yf16, stream);
-    case 32: return launch_scan<8, 4>(p, a->x_code, yf16, stream);
-    default: return launch_scan<16, 4>(p, a->x_code, yf16, stream);
+    case 4: return launch_scan<4, 1, 8>(p, a->x_code, yf16, stream);
+    case 8: return launch_scan<2, 4, 16>(p, a->x_code, yf16, stream);
+    case 16: return launch_scan<4, 4, 8>(p, a->x_code, yf16, stream);
+    case 32: return launch_scan<4, 8, 8>(p, a->x_code, yf16, stream);
+    default: return launch_scan<8, 8, 4>(p, a->x_code, yf16, stream);
   }
 }
 

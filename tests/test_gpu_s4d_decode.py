@@ -54,7 +54,7 @@ def test_s4d_int16_state(dev):
     import torch
     print("\n[s4d int16 state, full size]", flush=True)
     inp = synth.s4d_inputs(cfg=2, with_h0=True)
-    ss = op.s4d_state_scale(inp)
+    ss = op.s4d_state_scale(inp, with_h0=True)
     from quantized_state_space_amd import QSSM_I16
     lay = s4d_layer(dev, inp, state_dtype=QSSM_I16, state_scale=ss, with_h0=True)
     lay.step()
@@ -62,8 +62,17 @@ def test_s4d_int16_state(dev):
     ref = op.s4d(inp, state_scale=ss, with_h0=True)
     check_s4d_codes(lay, ref)
     assert_rows_close(lay.y.cpu().numpy(), ref["y"], 1e-2)
+    # the int16 state is quantized per channel: compare it per channel (over batch and states),
+    # i.e. relative to the range its codes span
     hl = lay.h_last.cpu().numpy().astype(np.float64) * ss[None, :, None, None]
-    assert_rows_close(hl[..., 0] + 1j * hl[..., 1], ref["h_last"], 1e-2, "h_last")
+    got = (hl[..., 0] + 1j * hl[..., 1]).transpose(1, 0, 2).reshape(hl.shape[1], -1)
+    want = ref["h_last"].transpose(1, 0, 2).reshape(hl.shape[1], -1)
+    # both sides round the state to the int16 grid after every step, but from fp32 vs fp64
+    # accumulators, so individual codes may drift by a few quanta: allow 1e-2 of the channel's
+    # range or 8 quanta, whichever is larger
+    diff = np.abs(got - want).max(axis=1)
+    bound = np.maximum(1e-2 * np.abs(want).max(axis=1), 8.0 * ss.astype(np.float64))
+    assert np.all(diff <= bound), (diff / bound).max()
 
 
 # ------------------------------------------------------------------------------------------------
