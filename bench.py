@@ -1,6 +1,6 @@
 """Benchmark of the quantized state-space hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c1|c2|c5|c5f16]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c1|c2|c4|c4f16|c5|c5f16]
 
 One step = one pass of the whole hot path of the workload over one batch of synthetic input that is
 already resident in HBM: for the Mamba1 layers, quantize x (gathered into cluster order), quantize B
@@ -213,6 +213,52 @@ class Decode(Workload):
         return 8 * len(sample) * nh * P * N / dt, "16 of 256 sequences x 8 tokens (fp64 state)"
 
 
+class Ssd(Workload):
+    def __init__(self, f16=False):
+        self.f16 = f16
+        self.name = "mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "")
+        self.dominant = "k_ssd_chunk_state + k_ssd_state_pass + k_ssd_output"
+
+    def setup(self, dev):
+        import qssm_synth as synth
+        import quantized_state_space_amd as qs
+        import quantized_state_space_amd.workloads as wl
+        self.inp = synth.ssd_inputs(cfg=4, calib_len=256)
+        self.lay = wl.SsdLayer(self.inp, dev, y_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32)
+        B, L, nh, P, N, Gbc = self.lay.shape
+        self.dims = self.lay.shape
+        self.config = {"workload": self.name, "batch": B, "seqlen": L, "heads": nh, "headdim": P,
+                       "d_state": N, "ngroups": Gbc, "chunk": 256, "x_groups": int(self.lay.G),
+                       "bc_state_groups": N // 16, "state": "f32", "y": "f16" if self.f16 else "f32"}
+
+    def step(self, timer):
+        self.lay.quantize()
+        timer.start()
+        self.lay.scan()
+        timer.stop()
+
+    def updates(self):
+        B, L, nh, P, N, _ = self.dims
+        return B * L * nh * P * N
+
+    def dominant_bytes(self):
+        B, L, nh, P, N, Gbc = self.dims
+        yb = 2 if self.f16 else 4
+        # x codes, delta, B/C codes, A, D in; y out; h_last out (each once)
+        return B * L * nh * P * (1 + yb) + 4 * B * L * nh + 2 * B * L * Gbc * N + 8 * nh + \
+            4 * B * nh * P * N
+
+    def cpu_baseline(self):
+        import oracle.pipelines as op
+        heads = np.array([0, 64])
+        t = time.perf_counter()
+        op.ssd(self.inp, heads=heads)
+        dt = time.perf_counter() - t
+        B, L, nh, P, N, _ = self.dims
+        return B * L * len(heads) * P * N / dt, "2 of 128 heads (all batches, full length), " \
+            "int8-state chunked form incl. quantizing the layer's x, B, C"
+
+
 _zc = {}
 
 
@@ -225,7 +271,8 @@ def _zero(device):
 
 
 WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Tiny,
-             "c2": lambda: S4d(False), "c5": lambda: Decode(False),
+             "c2": lambda: S4d(False), "c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
+             "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True)}
 
 

@@ -211,11 +211,18 @@ qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
  * The result equals the sequential recurrence with A[h] shared by all (p, n) of head h, computed
  * per chunk of `chunk` steps (chunks start at t = 0, the last may be partial):
  *   cum_i = sum_{k<=i} delta_k * A[h];  G = Ch Bh^T (int8 MFMA, int32 accumulation per state group);
- *   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh;  chunk state from an int8
- *   requantization of the decay-weighted x (int8 MFMA over time);  inter-chunk state passing in
- *   fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;  y = Y_intra + Y_inter + Dskip * xh.
+ *   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh  (fp16 operands, fp32 accumulate);
+ *   chunk state S = sum_j w_j xh_j Bh_j^T with w_j = delta_j exp(cum_last - cum_j), contracted over
+ *   time on MFMA: state_mma == QSSM_MMA_F16 uses fp16 operands fp16(w_j * qx) and the exact B codes
+ *   (fp32 accumulate); state_mma == QSSM_MMA_I8 requantizes the weighted x per (b, chunk, head) to
+ *   r = sat8(RNE(qx * w_j / w_max)) and runs int8 MFMA with int32 accumulate (faster operands, but
+ *   the rounding of r is a floating-point decision inside the contraction);
+ *   inter-chunk state passing in fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;
+ *   y = Y_intra + Y_inter + Dskip * xh.
  * Requires chunk == 256, P == 64, N == 128, gs == 16 in this build (else QSSM_ERR_UNSUPPORTED).
  */
+enum { QSSM_MMA_F16 = 0, QSSM_MMA_I8 = 1 };
+
 typedef struct qssm_ssd_args {
   int64_t batch, seqlen, nheads, headdim, dstate; /* B, L, nh, P, N */
   int32_t ngroups;                                /* Gbc, nh % Gbc == 0 */
@@ -237,6 +244,7 @@ typedef struct qssm_ssd_args {
   int32_t y_dtype;                                /* QSSM_F32 or QSSM_F16 */
   float* h_last;                                  /* [B, nh, P, N] or NULL */
   int32_t fused;                                  /* reserved, must be 0 */
+  int32_t state_mma;                              /* QSSM_MMA_F16 (default) or QSSM_MMA_I8 */
 } qssm_ssd_args;
 
 size_t qssm_ssd_workspace_size(const qssm_ssd_args* a);

@@ -195,11 +195,12 @@ def s4d_state_scale(inp, headroom=1.25, with_h0=False):
 # ------------------------------------------------------------------------------------------------
 # SSD
 
-def ssd(inp, chunk=256, gs=16, groups_per_block=8, with_h0=False, heads=None, int8_state=True,
+def ssd(inp, chunk=256, gs=16, groups_per_block=8, with_h0=False, heads=None, int8_state=False,
         exact=False):
     """Oracle SSD layer. heads: optional subset of head indices (the recurrence of each head is
-    independent; B/C groups follow the head). Returns codes, scales and fp64 y / h_last (for the
-    selected heads: y [B, L, len(heads), P])."""
+    independent; B/C groups follow the head). int8_state selects the requantized int8 chunk state;
+    exact=True runs the plain sequential scan instead of the chunked form. Returns codes, scales and
+    fp64 y / h_last (for the selected heads: y [B, L, len(heads), P])."""
     x = inp["x"]
     B, L, nh, P = x.shape
     Gbc, N = inp["B"].shape[2], inp["B"].shape[3]

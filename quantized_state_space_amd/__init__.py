@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libqssm.so")
 QSSM_OK, QSSM_ERR_INVALID_ARG, QSSM_ERR_UNSUPPORTED, QSSM_ERR_WORKSPACE, QSSM_ERR_DEVICE = range(5)
 QSSM_F32, QSSM_F16, QSSM_I16 = 0, 1, 2
 QSSM_X_INT8, QSSM_X_SOFTEDGE = 0, 1
+QSSM_MMA_F16, QSSM_MMA_I8 = 0, 1
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -51,7 +52,7 @@ class SsdArgs(ctypes.Structure):
                 ("xq", _P), ("x_group_of", _P), ("x_scales", _P), ("delta", _P), ("A", _P),
                 ("Dskip", _P), ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P),
                 ("C_scales", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
-                ("fused", _I32)]
+                ("fused", _I32), ("state_mma", _I32)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -261,7 +262,7 @@ def qssm_s4d_scan(args, stream=None):
 
 
 def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, chunk, y,
-             Dskip=None, h0=None, h_last=None):
+             Dskip=None, h0=None, h_last=None, state_mma=QSSM_MMA_F16):
     torch = _t()
     B, L, nh, P = xq.shape
     Gbc, N = Bq.shape[2], Bq.shape[3]
@@ -277,7 +278,8 @@ def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs,
                  B_scales=_ptr(B_scales, torch.float32, "B_scales"),
                  C_scales=_ptr(C_scales, torch.float32, "C_scales"),
                  h0=_ptr(h0, torch.float32, "h0", True), y=_ptr(y, None, "y"), y_dtype=ydt,
-                 h_last=_ptr(h_last, torch.float32, "h_last", True), fused=0)
+                 h_last=_ptr(h_last, torch.float32, "h_last", True), fused=0,
+                 state_mma=state_mma)
 
 
 def qssm_ssd_workspace_size(args):

@@ -1,21 +1,664 @@
-// a8-a13: Mamba2 SSD chunked form with an int8 path (work in progress: entry points validate and
-// report QSSM_ERR_UNSUPPORTED until the kernels land).
+// a8-a13: Mamba2 SSD chunked form with an int8 path.
+//
+// SSDi8 (abstract): a persistent INT8 path through the structured state-space duality, with
+// activations quantized at cost-effective points; Quamba2 (abstract): W8A8 for the Mamba2 backbone.
+// Per batch b, head h (B/C group g), chunk of Q = 256 steps with local indices i, j:
+//   cum_i   = sum_{k<=i} delta_k A_h
+//   G       = Ch Bh^T                               int8 MFMA, int32 per state group, fp32 scales
+//   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh           fp16 MFMA, fp32 accumulate
+//   S       = sum_j w_j xh_j Bh_j^T,  w_j = delta_j e^{cum_Q - cum_j}
+//             fp16 MFMA over time on fp16(w_j qx) and the B codes (default), or int8 MFMA on the
+//             requantized r = sat8(RNE(qx * w_j / w_max)) (option)
+//   H_c     = exp(cum_Q) H_{c-1} + S                  fp32 state passing
+//   Y_inter = exp(cum_i) Ch . H_{c-1}^T               fp16 MFMA
+//   y       = Y_intra + Y_inter + D_h xh
+//
+// Three kernels (the chunk states make one round trip through the workspace):
+//   K1 k_ssd_chunk_state  one workgroup per (b, chunk, B/C group): B chunk transposed in LDS once,
+//                         then per head the weighted x tile and a 64x128x256 MFMA product.
+//   K2 k_ssd_state_pass   per (b, h) state element: sequential over chunks, replaces each chunk
+//                         state by the state entering that chunk.
+//   K3 k_ssd_output       one workgroup per (b, chunk, B/C group): G^T is built once with int8 MFMA
+//                         and kept in registers (4 waves x 9 causal 32x32 tiles); per head the
+//                         inter-chunk product, the intra-chunk product and the D term.
+// MFMA lane layouts (verified on gfx950): operand lane l holds row/column l%32 and a run of
+// consecutive k at offset (K/2)*(l/32); the 32x32 accumulator register r of lane l is element
+// (8*(r/4) + 4*(l/32) + r%4, l%32).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
 
 using namespace qssm;
 
+namespace {
+
+constexpr int kQ = 256;   // chunk length
+constexpr int kP = 64;    // head dim
+constexpr int kN = 128;   // state size
+constexpr int kGS = 16;   // state-group size (one int8 MFMA K step)
+constexpr int kNSG = kN / kGS;
+constexpr int kRow256 = 272;  // padded bytes of a [*][256] int8 LDS row
+constexpr int kRow128 = 136;  // padded bytes of a [*][128] int8 LDS row
+constexpr int kXtRow = 260;   // padded halves of a [*][256] fp16 LDS row (520 bytes)
+constexpr int kHsRow = 136;   // padded halves of a [*][128] fp16 LDS row (272 bytes)
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+struct SsdParams {
+  int64_t B, L, nh, nc;
+  int32_t Gbc, hpg, yf16;
+  const int8_t* xq;
+  const uint8_t* x_group_of;
+  const float* x_scales;
+  const float* delta;
+  const float* A;
+  const float* Dskip;
+  const int8_t* Bq;
+  const int8_t* Cq;
+  const float* B_scales;
+  const float* C_scales;
+  const float* h0;
+  void* y;
+  float* h_last;
+  float* S;    // [B, nc, nh, P, N]: chunk states, then the states entering each chunk
+  float* dec;  // [B, nc, nh]: exp(cum at the last step of the chunk)
+};
+
+__device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
+
+// Inclusive prefix sum over the 256 threads of the block (one value each, in thread order).
+__device__ __forceinline__ float block_scan(float v, float* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) sh[w] = v;
+  __syncthreads();
+  float pre = 0.0f;
+  for (int k = 0; k < w; ++k) pre += sh[k];
+  __syncthreads();
+  return v + pre;
+}
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  __syncthreads();
+  return m;
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t d, int e) { return (d >> (8 * e)) & 0xFFu; }
+
+__device__ __forceinline__ v8h i8x8_to_h(int64_t v) {
+  v8h o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (_Float16)(float)(int8_t)((v >> (8 * e)) & 0xFF);
+  return o;
+}
+
+
+// 16 dwords (row r holds 4 bytes, columns 0..3) -> column e as 16 bytes (rows 0..15).
+__device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
+  uint4 o;
+  o.x = byte_of(d[0], e) | byte_of(d[1], e) << 8 | byte_of(d[2], e) << 16 | byte_of(d[3], e) << 24;
+  o.y = byte_of(d[4], e) | byte_of(d[5], e) << 8 | byte_of(d[6], e) << 16 | byte_of(d[7], e) << 24;
+  o.z = byte_of(d[8], e) | byte_of(d[9], e) << 8 | byte_of(d[10], e) << 16 | byte_of(d[11], e) << 24;
+  o.w = byte_of(d[12], e) | byte_of(d[13], e) << 8 | byte_of(d[14], e) << 16 | byte_of(d[15], e) << 24;
+  return o;
+}
+
+// ---------------------------------------------------------------------------------------------
+// K1: chunk states, S[p][n] = sum_j w_j xh_j[p] Bh_j[n], w_j = delta_j exp(cum_last - cum_j).
+// I8 = false: fp16 operands fp16(w_j * qx[j][p]) and the exact B codes, fp32 accumulate; the x and
+//             B scales are applied in the epilogue.
+// I8 = true:  the weighted x is requantized per (b, chunk, head), r = sat8(RNE(qx * w_j / w_max)),
+//             int8 MFMA with int32 accumulate, epilogue w_max * sx * sB.
+constexpr int kXwRow = 264;  // padded halves of a [*][256] fp16 LDS row (528 bytes)
+
+template <bool I8>
+struct K1Smem {
+  int8_t qBT[kN * kRow256];  // B chunk transposed, [n][j]
+  int8_t rT[I8 ? kP * kRow256 : 16];                  // requantized x, [p][j] (I8)
+  _Float16 xw[I8 ? 8 : kP * kXwRow];                  // weighted x, [p][j] (fp16)
+  float wv[kQ];                                       // w_j (fp16 path) or w_j / w_max (I8)
+  float sh[8];
+};
+
+template <bool I8>
+__global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  K1Smem<I8>& s = *reinterpret_cast<K1Smem<I8>*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t c = blockIdx.x;
+  const int64_t b = blockIdx.y / p.Gbc;
+  const int g = (int)(blockIdx.y % p.Gbc);
+  const int64_t t0 = c * kQ;
+  const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
+
+  // B chunk of group g, transposed to [n][j]; rows past the sequence are zero
+  for (int u = tid; u < 16 * (kN / 4); u += 256) {
+    const int jb = u / (kN / 4), n4 = u % (kN / 4);
+    uint32_t d[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = jb * 16 + r;
+      d[r] = (j < q) ? *reinterpret_cast<const uint32_t*>(
+                           p.Bq + ((b * p.L + t0 + j) * p.Gbc + g) * kN + n4 * 4)
+                     : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<uint4*>(s.qBT + (n4 * 4 + e) * kRow256 + jb * 16) = column16(d, e);
+  }
+
+  const int n = w * 32 + (lane & 31);  // this lane's output column (state)
+  const float sB = valid_or_zero(p.B_scales[g * kNSG + n / kGS]);
+  const int kh = lane >> 5;
+
+  for (int hh = 0; hh < p.hpg; ++hh) {
+    const int64_t h = (int64_t)g * p.hpg + hh;
+    const float Ah = p.A[h];
+    const int j = tid;
+    const float dt = (j < q) ? p.delta[(b * p.L + t0 + j) * p.nh + h] : 0.0f;
+    const float cum = block_scan(dt * Ah, s.sh);
+    if (j == q - 1) s.sh[4] = cum;
+    __syncthreads();
+    const float cum_last = s.sh[4];
+    const float wj = (j < q) ? dt * expf(cum_last - cum) : 0.0f;
+    float wmax = 1.0f;
+    if (I8) {
+      wmax = block_max(wj, s.sh);
+      s.wv[j] = (wmax > 0.0f) ? wj / wmax : 0.0f;
+    } else {
+      s.wv[j] = wj;
+    }
+    if (tid == 0) p.dec[(b * p.nc + c) * p.nh + h] = expf(cum_last);
+    __syncthreads();
+
+    // weighted x tile, transposed [p][j]
+    {
+      const int jb = tid / 16, p4 = tid % 16;
+      uint32_t raw[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = jb * 16 + r;
+        raw[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(
+                                p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
+                          : 0u;
+      }
+      if (I8) {
+        uint32_t d[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float rt = s.wv[jb * 16 + r];
+          uint32_t word = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = (float)(int8_t)byte_of(raw[r], e) * rt;
+            const int rq = (int)fminf(fmaxf(rintf(v), -128.0f), 127.0f);
+            word |= ((uint32_t)rq & 0xFFu) << (8 * e);
+          }
+          d[r] = word;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint4*>(s.rT + (p4 * 4 + e) * kRow256 + jb * 16) = column16(d, e);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v8h lo, hi;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            lo[r] = (_Float16)((float)(int8_t)byte_of(raw[r], e) * s.wv[jb * 16 + r]);
+            hi[r] = (_Float16)((float)(int8_t)byte_of(raw[8 + r], e) * s.wv[jb * 16 + 8 + r]);
+          }
+          _Float16* dst = s.xw + (p4 * 4 + e) * kXwRow + jb * 16;
+          *reinterpret_cast<v8h*>(dst) = lo;
+          *reinterpret_cast<v8h*>(dst + 8) = hi;
+        }
+      }
+    }
+    __syncthreads();
+
+    // S[p][n] for p in two 32-row tiles; wave w owns state columns [32w, 32w + 32)
+    float* Sout = p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
+    if (I8) {
+      v16i acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int ks = 0; ks < kQ / 32; ++ks) {
+        const int ko = ks * 32 + 16 * kh;
+        const v4i bv = *reinterpret_cast<const v4i*>(s.qBT + n * kRow256 + ko);
+        const v4i a0 = *reinterpret_cast<const v4i*>(s.rT + (lane & 31) * kRow256 + ko);
+        const v4i a1 = *reinterpret_cast<const v4i*>(s.rT + (32 + (lane & 31)) * kRow256 + ko);
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bv, acc1, 0, 0, 0);
+      }
+      const float wsb = wmax * sB;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
+        const float sx0 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + prow]]);
+        const float sx1 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + 32 + prow]]);
+        Sout[prow * kN + n] = wsb * sx0 * (float)acc0[r];
+        Sout[(32 + prow) * kN + n] = wsb * sx1 * (float)acc1[r];
+      }
+    } else {
+      v16f acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int ks = 0; ks < kQ / 16; ++ks) {
+        const int ko = ks * 16 + 8 * kh;
+        const v8h bv = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qBT + n * kRow256 + ko));
+        const v8h a0 = *reinterpret_cast<const v8h*>(s.xw + (lane & 31) * kXwRow + ko);
+        const v8h a1 = *reinterpret_cast<const v8h*>(s.xw + (32 + (lane & 31)) * kXwRow + ko);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bv, acc1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
+        const float sx0 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + prow]]);
+        const float sx1 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + 32 + prow]]);
+        Sout[prow * kN + n] = sB * sx0 * acc0[r];
+        Sout[(32 + prow) * kN + n] = sB * sx1 * acc1[r];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// K2: inter-chunk state passing, H_c = dec_c H_{c-1} + S_c. Slot c of S receives H_{c-1}.
+__global__ __launch_bounds__(256) void k_ssd_state_pass(SsdParams p) {
+  constexpr int kE4 = kP * kN / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.B * p.nh * kE4) return;
+  const int64_t e4 = idx % kE4, bh = idx / kE4;
+  const int64_t b = bh / p.nh, h = bh % p.nh;
+  float4 H = p.h0 ? reinterpret_cast<const float4*>(p.h0)[bh * kE4 + e4]
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t c = 0; c < p.nc; ++c) {
+    float4* slot = reinterpret_cast<float4*>(p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN)) + e4;
+    const float4 s = *slot;
+    *slot = H;
+    const float d = p.dec[(b * p.nc + c) * p.nh + h];
+    H = make_float4(fmaf(d, H.x, s.x), fmaf(d, H.y, s.y), fmaf(d, H.z, s.z), fmaf(d, H.w, s.w));
+  }
+  if (p.h_last) reinterpret_cast<float4*>(p.h_last)[bh * kE4 + e4] = H;
+}
+
+// ---------------------------------------------------------------------------------------------
+// K3: chunk outputs.
+struct K3Smem {
+  int8_t qB[kQ * kRow128];  // B chunk rows [j][n]
+  int8_t qC[kQ * kRow128];  // C chunk rows [i][n]
+  _Float16 xT[kP * kXtRow];  // x codes of the head, [p][j] (exact in fp16)
+  _Float16 Hs[kP * kHsRow];  // sC(n) * H_prev[p][n]
+  float cum[kQ];
+  float dtv[kQ];
+  float ecum[kQ];   // exp(cum_i)
+  float cjv[kQ];    // exp(cum at the end of j's 32-block - cum_j) * delta_j
+  float sxs[kP];
+  float sh[8];
+};
+
+
+// Wave w (of 4) owns the query blocks w and 7 - w: 9 causal tiles (I, J <= I) in all, enumerated
+// as t = 0..8 -> (I, J) = (w, t) for t <= w, else (7 - w, t - w - 1). The tile index t is static
+// (registers), I and J are wave-uniform values (uniform branches).
+__device__ __forceinline__ void tile_of(int w, int t, int& I, int& J, int& ii) {
+  if (t <= w) { I = w; J = t; ii = 0; }
+  else { I = 7 - w; J = t - w - 1; ii = 1; }
+}
+
+// Compiler-only fence: keeps one tile's work from being interleaved with the next tile's.
+__device__ __forceinline__ void tile_fence() { __asm__ volatile("" ::: "memory"); }
+
+__device__ __forceinline__ void build_g_tile(v16f& G, const K3Smem& s, const float* sBC, int I,
+                                             int J, int lane) {
+  const int kofs = 8 * (lane >> 5);
+  G = v16f{};
+#pragma unroll
+  for (int sg = 0; sg < kNSG; ++sg) {
+    int64_t a = *reinterpret_cast<const int64_t*>(s.qB + (J * 32 + (lane & 31)) * kRow128 + sg * kGS + kofs);
+    int64_t bq = *reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 + sg * kGS + kofs);
+    // empty asm that reads G and "rewrites" this group's operands: the MFMA of state group sg
+    // cannot issue before the epilogue of group sg - 1, so one int32 accumulator is live at a time
+    __asm__ volatile("" : "+v"(a), "+v"(bq) : "v"(G));
+    const v16i acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bq, v16i{}, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) G[r] = fmaf(sBC[sg], (float)acc[r], G[r]);
+  }
+}
+
+// M tile = G o exp(cum_i - cum_j) [j <= i] o delta_j as two fp16 A operands (k-slots follow the
+// accumulator rows of G, see the B operand gather below)
+__device__ __forceinline__ void m_tile(const v16f& G, const K3Smem& s, int I, int J, int lane,
+                                       v8h& a0, v8h& a1) {
+  const int i = I * 32 + (lane & 31);  // this lane's query row
+  const float ci = s.cum[i];
+  float m[16];
+  if (J < I) {
+    // both factors are at most 1 (cum does not increase): no overflow for long decays
+    const float ri = __expf(ci - s.cum[J * 32 + 31]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = J * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+      m[r] = G[r] * (ri * s.cjv[j]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = J * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+      m[r] = (j <= i) ? G[r] * (__expf(ci - s.cum[j]) * s.dtv[j]) : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a0[e] = (_Float16)m[e];
+    a1[e] = (_Float16)m[8 + e];
+  }
+}
+
+// x B operand for MFMA mm of tile column block J: lane l supplies column p and the 8 j's whose G
+// accumulator rows sit in registers 8 mm .. 8 mm + 7 of the same lane half
+__device__ __forceinline__ v8h x_operand(const K3Smem& s, int J, int mm, int pt, int lane) {
+  const int j0 = J * 32 + 16 * mm + 4 * (lane >> 5);
+  const _Float16* row = s.xT + (pt * 32 + (lane & 31)) * kXtRow;
+  const v4h lo = *reinterpret_cast<const v4h*>(row + j0);
+  const v4h hi = *reinterpret_cast<const v4h*>(row + j0 + 8);
+  return v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  K3Smem& s = *reinterpret_cast<K3Smem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int64_t c = blockIdx.x;
+  const int64_t b = blockIdx.y / p.Gbc;
+  const int g = (int)(blockIdx.y % p.Gbc);
+  const int64_t t0 = c * kQ;
+  const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
+  const int kofs = 8 * (lane >> 5);
+
+  // B and C chunk rows of group g (zero past the sequence), 8-byte LDS stores
+  {
+    const int j = tid;
+    const int64_t* bsrc = reinterpret_cast<const int64_t*>(p.Bq + ((b * p.L + t0 + j) * p.Gbc + g) * kN);
+    const int64_t* csrc = reinterpret_cast<const int64_t*>(p.Cq + ((b * p.L + t0 + j) * p.Gbc + g) * kN);
+#pragma unroll
+    for (int k = 0; k < kN / 8; ++k) {
+      *reinterpret_cast<int64_t*>(s.qB + j * kRow128 + 8 * k) = (j < q) ? bsrc[k] : 0;
+      *reinterpret_cast<int64_t*>(s.qC + j * kRow128 + 8 * k) = (j < q) ? csrc[k] : 0;
+    }
+  }
+  float sBC[kNSG];  // sB * sC per state group (wave-uniform)
+#pragma unroll
+  for (int sg = 0; sg < kNSG; ++sg)
+    sBC[sg] = valid_or_zero(p.B_scales[g * kNSG + sg]) * valid_or_zero(p.C_scales[g * kNSG + sg]);
+  __syncthreads();
+
+  v16f G[9];
+#pragma unroll
+  for (int t = 0; t < 9; ++t) {
+    int I, J, ii;
+    tile_of(w, t, I, J, ii);
+    build_g_tile(G[t], s, sBC, I, J, lane);
+    tile_fence();
+  }
+
+  const int rs = (int)(p.nh * kP);  // row stride of y in elements
+  const bool full = q == kQ;
+  for (int hh = 0; hh < p.hpg; ++hh) {
+    const int64_t h = (int64_t)g * p.hpg + hh;
+    // decay terms of head h
+    const int j = tid;
+    const float dt = (j < q) ? p.delta[(b * p.L + t0 + j) * p.nh + h] : 0.0f;
+    const float cum = block_scan(dt * p.A[h], s.sh);
+    s.cum[j] = cum;
+    s.dtv[j] = dt;
+    s.ecum[j] = expf(cum);
+    if (tid < kP) s.sxs[tid] = valid_or_zero(p.x_scales[p.x_group_of[h * kP + tid]]);
+    __syncthreads();
+    s.cjv[j] = expf(s.cum[j | 31] - cum) * dt;
+    // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale)
+    {
+      const int jb = tid / 16, p4 = tid % 16;
+      uint32_t d[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = jb * 16 + r;
+        d[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
+                        : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pc = p4 * 4 + e;
+        const bool on = s.sxs[pc] > 0.0f;
+        _Float16* dst = s.xT + pc * kXtRow + jb * 16;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          v4h v;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            v[k] = on ? (_Float16)(float)(int8_t)byte_of(d[4 * r4 + k], e) : (_Float16)0.0f;
+          *reinterpret_cast<v4h*>(dst + 4 * r4) = v;
+        }
+      }
+    }
+    // state entering the chunk, scaled by sC(n), fp16 [p][n]
+    {
+      const float4* Hsrc = reinterpret_cast<const float4*>(p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e4 = tid + 256 * k;
+        const int pr = (4 * e4) / kN, n0 = (4 * e4) % kN;
+        const float sc = valid_or_zero(p.C_scales[g * kNSG + n0 / kGS]);
+        const float4 v = Hsrc[e4];
+        const v4h hv = {(_Float16)(sc * v.x), (_Float16)(sc * v.y), (_Float16)(sc * v.z), (_Float16)(sc * v.w)};
+        *reinterpret_cast<v4h*>(s.Hs + pr * kHsRow + n0) = hv;
+      }
+    }
+    __syncthreads();
+
+    // Opaque copies of the lane and wave ids: the tile addresses below do not depend on the head,
+    // and hoisting all of them out of the head loop would keep them live across it (spills).
+    int lane = tid & 63;
+    __asm__ volatile("" : "+v"(lane));
+    int w = uniform(tid >> 6);
+    __asm__ volatile("" : "+s"(w));
+    const int kofs = 8 * (lane >> 5);
+    v16f Y[2][2] = {};
+    // Y_inter = exp(cum_i) * qC[i, :] . Hs[:, p]
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int I = ii ? 7 - w : w;
+#pragma unroll
+      for (int ks = 0; ks < kN / 16; ++ks) {
+        const int64_t cv = *reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 + ks * 16 + kofs);
+        const v8h a = i8x8_to_h(cv);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const v8h bv = *reinterpret_cast<const v8h*>(s.Hs + (pt * 32 + (lane & 31)) * kHsRow + ks * 16 + kofs);
+          Y[ii][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bv, Y[ii][pt], 0, 0, 0);
+        }
+      }
+      // row scale exp(cum_i), column scale 1 / sx[p] (the intra part accumulates raw x codes)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const float sx = s.sxs[pt * 32 + (lane & 31)];
+        const float inv = (sx > 0.0f) ? 1.0f / sx : 1.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+          Y[ii][pt][r] *= s.ecum[i] * inv;
+        }
+      }
+    }
+    // Y_intra on top, tile by tile
+#pragma unroll
+    for (int t = 0; t < 9; ++t) {
+      tile_fence();
+      int I, J, ii;
+      tile_of(w, t, I, J, ii);
+      v8h a0, a1;
+      m_tile(G[t], s, I, J, lane, a0, a1);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const v8h b0 = x_operand(s, J, 0, pt, lane);
+        const v8h b1 = x_operand(s, J, 1, pt, lane);
+        if (ii == 0) {
+          Y[0][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[0][pt], 0, 0, 0);
+          Y[0][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[0][pt], 0, 0, 0);
+        } else {
+          Y[1][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[1][pt], 0, 0, 0);
+          Y[1][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[1][pt], 0, 0, 0);
+        }
+      }
+    }
+    tile_fence();
+    // y = sx * acc + D * xh; rows past the sequence (ragged last chunk) are not stored
+    const float Dh = p.Dskip ? p.Dskip[h] : 0.0f;
+    const int64_t base = ((b * p.L + t0) * p.nh + h) * kP;  // y[b, t0, h, 0]
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int I = ii ? 7 - w : w;
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const int pc = pt * 32 + (lane & 31);
+        const float sx = s.sxs[pc];
+        const float mult = (sx > 0.0f) ? sx : 1.0f;
+        float yv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+          yv[r] = fmaf(Dh, sx * (float)s.xT[pc * kXtRow + i], mult * Y[ii][pt][r]);
+        }
+        if (p.yf16) {
+          __half* yb = reinterpret_cast<__half*>(p.y) + base + pc;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (full || i < q) yb[i * rs] = __float2half_rn(yv[r]);
+          }
+        } else {
+          float* yb = reinterpret_cast<float*>(p.y) + base + pc;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (full || i < q) yb[i * rs] = yv[r];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+struct WsLayout {
+  size_t s_bytes, dec_off, total;
+};
+
+WsLayout ws_layout(const qssm_ssd_args* a) {
+  const int64_t nc = (a->seqlen + kQ - 1) / kQ;
+  WsLayout w;
+  w.s_bytes = (size_t)a->batch * nc * a->nheads * kP * kN * sizeof(float);
+  w.dec_off = (w.s_bytes + 255) & ~(size_t)255;
+  w.total = w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 256;
+  return w;
+}
+
+}  // namespace
+
 extern "C" {
 
-size_t qssm_ssd_workspace_size(const qssm_ssd_args* a) { return a ? 0 : 0; }
+size_t qssm_ssd_workspace_size(const qssm_ssd_args* a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->nheads < 1) return 0;
+  return ws_layout(a).total + 256;
+}
 
 qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  (void)ws; (void)ws_bytes; (void)stream;
   clear_error();
   if (!a) return fail(QSSM_ERR_INVALID_ARG, "args is null");
-  return fail(QSSM_ERR_UNSUPPORTED, "SSD chunked kernels are not built yet");
+  const int64_t B = a->batch, L = a->seqlen, nh = a->nheads;
+  if (B < 0 || L < 0 || nh < 1 || a->headdim < 1 || a->dstate < 1)
+    return fail(QSSM_ERR_INVALID_ARG, "bad shape");
+  if (a->ngroups < 1 || nh % a->ngroups != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "ngroups must divide nheads");
+  if (a->x_groups < 1 || a->x_groups > 256) return fail(QSSM_ERR_INVALID_ARG, "x_groups not in 1..256");
+  if (a->bc_group_size < 1 || a->dstate % a->bc_group_size != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "bc_group_size must divide dstate");
+  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16)
+    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32 or QSSM_F16");
+  if (a->fused != 0) return fail(QSSM_ERR_UNSUPPORTED, "fused must be 0");
+  if (a->state_mma != QSSM_MMA_F16 && a->state_mma != QSSM_MMA_I8)
+    return fail(QSSM_ERR_INVALID_ARG, "state_mma must be QSSM_MMA_F16 or QSSM_MMA_I8");
+  if (a->chunk != kQ || a->headdim != kP || a->dstate != kN || a->bc_group_size != kGS)
+    return fail(QSSM_ERR_UNSUPPORTED,
+                "this build implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
+  if (L > ((int64_t)1 << 40)) return fail(QSSM_ERR_UNSUPPORTED, "seqlen too large");
+  if (B == 0) return QSSM_OK;
+  if (!a->xq || !a->x_group_of || !a->x_scales || !a->delta || !a->A || !a->Bq || !a->Cq ||
+      !a->B_scales || !a->C_scales || !a->y)
+    return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
+  if (((uintptr_t)a->xq | (uintptr_t)a->Bq | (uintptr_t)a->Cq) % 16 != 0 ||
+      (a->h0 && (uintptr_t)a->h0 % 16 != 0) || (a->h_last && (uintptr_t)a->h_last % 16 != 0))
+    return fail(QSSM_ERR_INVALID_ARG, "xq, Bq, Cq, h0 and h_last must be 16-byte aligned");
+  const WsLayout wl = ws_layout(a);
+  if (!ws || ws_bytes < wl.total + 256)
+    return fail(QSSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total + 256,
+                ws_bytes);
+  char* base = reinterpret_cast<char*>(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  const int64_t nc = (L + kQ - 1) / kQ;
+  SsdParams p{B, L, nh, nc, a->ngroups, (int32_t)(nh / a->ngroups), a->y_dtype == QSSM_F16,
+              a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
+              a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
+              reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + wl.dec_off)};
+  if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff)
+    return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
+  const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
+  if (nc > 0) {
+    static bool lds1_raised[2] = {false, false};
+    const int i8 = a->state_mma == QSSM_MMA_I8;
+    const void* k1 = i8 ? reinterpret_cast<const void*>(&k_ssd_chunk_state<true>)
+                        : reinterpret_cast<const void*>(&k_ssd_chunk_state<false>);
+    const size_t k1_lds = i8 ? sizeof(K1Smem<true>) : sizeof(K1Smem<false>);
+    if (!lds1_raised[i8]) {
+      if (hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)k1_lds) !=
+          hipSuccess)
+        return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD chunk-state kernel");
+      lds1_raised[i8] = true;
+    }
+    if (i8) k_ssd_chunk_state<true><<<grid, 256, k1_lds, stream>>>(p);
+    else k_ssd_chunk_state<false><<<grid, 256, k1_lds, stream>>>(p);
+    if (qssm_status s = launch_status("ssd chunk state")) return s;
+  }
+  k_ssd_state_pass<<<(unsigned)cdiv(B * nh * (kP * kN / 4), 256), 256, 0, stream>>>(p);
+  if (qssm_status s = launch_status("ssd state passing")) return s;
+  if (nc > 0) {
+    static bool lds_raised = false;  // per process; the attribute is per kernel function
+    if (!lds_raised) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ssd_output),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sizeof(K3Smem)) != hipSuccess)
+        return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD output kernel");
+      lds_raised = true;
+    }
+    k_ssd_output<<<grid, 256, sizeof(K3Smem), stream>>>(p);
+    if (qssm_status s = launch_status("ssd output")) return s;
+  }
+  return QSSM_OK;
 }
 
 }  // extern "C"

@@ -235,7 +235,7 @@ class SsdLayer:
     chunked SSD."""
 
     def __init__(self, inp, device, chunk=256, gs=16, groups_per_block=8, y_dtype=QSSM_F32,
-                 with_h0=False):
+                 with_h0=False, state_mma=0):
         import torch
         dev = device
         x = inp["x"]
@@ -264,7 +264,7 @@ class SsdLayer:
         self.h_last = torch.empty((B, nh, P, N), dtype=torch.float32, device=dev)
         self.args = ssd_args(self.xq, self.group_t, self.xs, self.delta, self.A, self.Bq, self.Cq,
                              self.bs, self.cs, gs, chunk, self.y, Dskip=self.D, h0=self.h0,
-                             h_last=self.h_last)
+                             h_last=self.h_last, state_mma=state_mma)
         self.ws = torch.empty(max(qssm_ssd_workspace_size(self.args), 1), dtype=torch.uint8,
                               device=dev)
 

@@ -62,17 +62,30 @@ def test_s4d_int16_state(dev):
     ref = op.s4d(inp, state_scale=ss, with_h0=True)
     check_s4d_codes(lay, ref)
     assert_rows_close(lay.y.cpu().numpy(), ref["y"], 1e-2)
-    # the int16 state is quantized per channel: compare it per channel (over batch and states),
-    # i.e. relative to the range its codes span
+    # Both sides round the state to the int16 grid after every step, from fp32 (kernel) and fp64
+    # (oracle) accumulators. Once one rounding decision differs, the two trajectories round
+    # independently: their difference d evolves as d <- Abar d + (e1 - e2) with each rounding error
+    # uniform in [-q/2, q/2] per component, so after L steps its per-component variance is at most
+    # q^2 / 6 * sum_{k<L} |Abar|^(2k). The final state is held to 8 such standard deviations (of the
+    # complex difference) on top of 1e-2 of the channel's range.
     hl = lay.h_last.cpu().numpy().astype(np.float64) * ss[None, :, None, None]
-    got = (hl[..., 0] + 1j * hl[..., 1]).transpose(1, 0, 2).reshape(hl.shape[1], -1)
-    want = ref["h_last"].transpose(1, 0, 2).reshape(hl.shape[1], -1)
-    # both sides round the state to the int16 grid after every step, but from fp32 vs fp64
-    # accumulators, so individual codes may drift by a few quanta: allow 1e-2 of the channel's
-    # range or 8 quanta, whichever is larger
-    diff = np.abs(got - want).max(axis=1)
-    bound = np.maximum(1e-2 * np.abs(want).max(axis=1), 8.0 * ss.astype(np.float64))
-    assert np.all(diff <= bound), (diff / bound).max()
+    got = hl[..., 0] + 1j * hl[..., 1]                                  # [B, H, N]
+    want = ref["h_last"]
+    H, N = inp["A_re"].shape
+    L = inp["u"].shape[1]
+    deq = {k: ref["scales"][k].astype(np.float64)[:, None] * ref["codes"][k] for k in op.PLANES}
+    dt = np.exp(inp["log_dt"].astype(np.float64))
+    walk = np.empty((H, N))
+    for h in range(H):
+        Ab, _ = oracle.s4d_zoh(deq["A_re"][h] + 1j * deq["A_im"][h],
+                               deq["B_re"][h] + 1j * deq["B_im"][h], dt[h])
+        r2 = np.abs(Ab) ** 2
+        walk[h] = np.sqrt(2.0 / 6.0 * np.where(r2 < 1.0, (1.0 - r2 ** L) / np.maximum(1.0 - r2, 1e-300), L))
+    rng_ch = np.abs(want).max(axis=(0, 2))                               # [H]
+    bound = 1e-2 * rng_ch[None, :, None] + 8.0 * ss.astype(np.float64)[None, :, None] * walk[None]
+    ratio = np.abs(got - want) / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, f"h_last: {ratio.max():.3f} of the bound at (b, h, n) = {worst}"
 
 
 # ------------------------------------------------------------------------------------------------
