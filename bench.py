@@ -24,6 +24,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# fp32 VALU issue rate of MI355X without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (lane-instructions per second; an FMA counts once). The recurrences' instruction mix (an exp per
+# update, dependent FMAs) has no packed form in this build.
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "quantized scan state-updates/s (B·L·D·N) + % of HBM peak, 1 MI355X"
 
 
@@ -44,10 +48,15 @@ class Workload:
 
 
 class Mamba1(Workload):
+    # per state update: v_mul (delta * A log2 e), v_exp_f32, v_mul (delta x * B), two FMAs (state
+    # and readout)
+    ops_per_update = 5
+
     def __init__(self, soft_edge=False):
         self.soft = soft_edge
         self.name = "mamba1-130m-layer-w8a8" + ("-softedge-x" if soft_edge else "")
-        self.dominant = "k_scan_m1 (+ k_stage_bc)"
+        self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
+        self.bound = "alu"
 
     def setup(self, dev):
         import qssm_synth as synth
@@ -55,22 +64,30 @@ class Mamba1(Workload):
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.c3_inputs()
         xc = qs.QSSM_X_SOFTEDGE if self.soft else qs.QSSM_X_INT8
-        self.lay = wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc)
-        B, D, L, N, Gbc = self.lay.shape
+        # two copies of every buffer, used in turn, so that one step's 350 MB of traffic cannot be
+        # served from the previous step's lines in the 256 MB last-level cache
+        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc) for _ in range(2)]
+        self.k = 0
+        B, D, L, N, Gbc = self.layers[0].shape
         self.dims = (B, D, L, N, Gbc)
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
                        "x_groups": 8, "x_code": "soft-edge 3-scale u8" if self.soft else "int8",
                        "bc_state_groups": N // 4, "state": "f32", "y": "f32"}
 
     def step(self, timer):
-        self.lay.quantize()
+        lay = self.layers[self.k % len(self.layers)]
+        self.k += 1
+        lay.quantize()
         timer.start()
-        self.lay.scan()
+        lay.scan()
         timer.stop()
 
     def updates(self):
         B, D, L, N, _ = self.dims
         return B * D * L * N
+
+    def ops(self):
+        return self.ops_per_update * self.updates()
 
     def dominant_bytes(self):
         B, D, L, N, Gbc = self.dims
@@ -80,41 +97,40 @@ class Mamba1(Workload):
     def cpu_baseline(self):
         import oracle.pipelines as op
         cal = op.mamba1_calib(self.inp, 8, 4, soft_edge=self.soft)
-        t = time.perf_counter()
-        op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=cal)
-        dt = time.perf_counter() - t
-        return self.updates() / dt, "full workload (all 8 x 1536 channels x 2048 steps), quantize + dequantize + fp64 scan"
+        reps, dt = timed_reps(lambda: op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=cal))
+        return reps * self.updates() / dt, f"full workload (8 x 1536 channels x 2048 steps) x {reps}: " \
+            "quantize, dequantize, fp64 scan"
 
 
 class Tiny(Mamba1):
     def __init__(self):
         self.soft = False
         self.name = "tiny-mamba1-w8a8"
-        self.dominant = "k_scan_m1 (+ k_stage_bc)"
+        self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
+        self.bound = "alu"
 
     def setup(self, dev):
         import qssm_synth as synth
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.c1_inputs()
-        self.lay = wl.Mamba1Layer(self.inp, 1, 4, dev, dynamic_scales=True)
-        self.dims = self.lay.shape
+        self.layers = [wl.Mamba1Layer(self.inp, 1, 4, dev, dynamic_scales=True)]
+        self.k = 0
+        self.dims = self.layers[0].shape
         B, D, L, N, _ = self.dims
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
                        "x_groups": 1, "bc_state_groups": 4, "state": "f32", "y": "f32"}
 
     def cpu_baseline(self):
         import oracle.pipelines as op
-        t = time.perf_counter()
-        for _ in range(20):
-            op.mamba1(self.inp, G=1, gs=4, dynamic=True)
-        return 20 * self.updates() / (time.perf_counter() - t), "full workload x20"
+        reps, dt = timed_reps(lambda: op.mamba1(self.inp, G=1, gs=4, dynamic=True))
+        return reps * self.updates() / dt, f"full workload x {reps}"
 
 
 class S4d(Workload):
     def __init__(self, i16=False):
         self.i16 = i16
         self.name = "s4d-smnist-shaped" + ("-int16-state" if i16 else "")
-        self.dominant = "k_s4d"
+        self.dominant = "qssm_s4d_scan: k_s4d"
         self.bound = "alu"
 
     def setup(self, dev):
@@ -147,21 +163,23 @@ class S4d(Workload):
         B, L, H, N = self.dims
         return B * L + H + 6 * H * N + 4 * 8 * H + 4 * B * H * L + 8 * B * H * N
 
-    def flops(self):  # complex update Abar*h + Bbar*u (10 flops) + readout Re(C h) (4 flops)
-        return 14.0 * self.updates()
+    # per complex state update: Bbar u (2 mul), Abar h + Bbar u (4 FMA-class), Re(C h) (2 FMA-class)
+    ops_per_update = 8
+
+    def ops(self):
+        return self.ops_per_update * self.updates()
 
     def cpu_baseline(self):
         import oracle.pipelines as op
-        t = time.perf_counter()
-        op.s4d(self.inp, state_scale=self.ss)
-        return self.updates() / (time.perf_counter() - t), "full workload, fp64 complex scan"
+        reps, dt = timed_reps(lambda: op.s4d(self.inp, state_scale=self.ss))
+        return reps * self.updates() / dt, f"full workload x {reps}, fp64 complex scan"
 
 
 class Decode(Workload):
     def __init__(self, f16=False):
         self.f16 = f16
         self.name = "mamba2-8b-decode" + ("-fp16-state" if f16 else "")
-        self.dominant = "k_state_update"
+        self.dominant = "qssm_state_update: k_state_update"
 
     def setup(self, dev):
         import torch
@@ -206,18 +224,17 @@ class Decode(Workload):
     def cpu_baseline(self):
         import oracle.pipelines as op
         sample = np.arange(16)
-        t = time.perf_counter()
-        op.decode(self.params, self.inputs[:8], batches=sample)
-        dt = time.perf_counter() - t
+        reps, dt = timed_reps(lambda: op.decode(self.params, self.inputs[:8], batches=sample))
         B, nh, P, N, _ = self.dims
-        return 8 * len(sample) * nh * P * N / dt, "16 of 256 sequences x 8 tokens (fp64 state)"
+        return reps * 8 * len(sample) * nh * P * N / dt, \
+            f"16 of 256 sequences x 8 tokens (fp64 state) x {reps}"
 
 
 class Ssd(Workload):
     def __init__(self, f16=False):
         self.f16 = f16
         self.name = "mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "")
-        self.dominant = "k_ssd_chunk_state + k_ssd_state_pass + k_ssd_output"
+        self.dominant = "qssm_ssd_chunk_int8: k_ssd_chunk_state + k_ssd_state_pass + k_ssd_output"
 
     def setup(self, dev):
         import qssm_synth as synth
@@ -251,15 +268,24 @@ class Ssd(Workload):
     def cpu_baseline(self):
         import oracle.pipelines as op
         heads = np.array([0, 64])
-        t = time.perf_counter()
-        op.ssd(self.inp, heads=heads)
-        dt = time.perf_counter() - t
+        reps, dt = timed_reps(lambda: op.ssd(self.inp, heads=heads))
         B, L, nh, P, N, _ = self.dims
-        return B * L * len(heads) * P * N / dt, "2 of 128 heads (all batches, full length), " \
-            "int8-state chunked form incl. quantizing the layer's x, B, C"
+        return reps * B * L * len(heads) * P * N / dt, f"2 of 128 heads (all batches, full " \
+            f"length) x {reps}: fp64 chunked form incl. quantizing the layer's x, B, C"
 
 
 _zc = {}
+
+
+def timed_reps(fn, min_seconds=10.0):
+    """Runs fn until at least min_seconds of wall time have passed; returns (reps, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return reps, dt
 
 
 def _zero(device):
@@ -277,6 +303,50 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 
 
 # ------------------------------------------------------------------------------------------------
+
+# HBM traffic of one call of the dominant entry point, from two rocprofv3 counter runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, summed over the call's kernels), each divided by
+# the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
+# workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
+TRAFFIC = {
+    "c3": (163175667, 113849088, "fe5bcf10865f2b40"),
+    "c2": (277656, 7472288, "125950742ed91549"),
+    "c4": (1284972839, 1090787952, "ff13912165beae6a"),
+    "c5": (1100189192, 1082564232, "045f735b9b546c01"),
+}
+TRAFFIC_SOURCES = {
+    "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"], "c2": ["s4d.hip"],
+    "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c5": ["state_update.hip"],
+    "c5f16": ["state_update.hip"],
+}
+
+
+def sources_digest(workload):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[workload] + ["common.hpp"]:
+        with open(os.path.join(ROOT, "quantized_state_space_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """Counter-measured HBM bytes per call, or None when none were taken for these sources."""
+    t = TRAFFIC.get(workload)
+    if t is None or t[2] != sources_digest(workload):
+        return None
+    return int(t[0] + t[1])
+
+
+def copy_probe(torch, dev, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of nbytes, the reference kernel for scaling the counters."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": nbytes, "reps": reps}), flush=True)
+
 
 class EventTimer:
     """HIP events around the dominant call, recorded on the stream the library launches on."""
@@ -309,7 +379,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the traffic counters)")
+    ap.add_argument("--print-digest", action="store_true",
+                    help="print the kernel-source digest of the workload and exit")
     args = ap.parse_args()
+    if args.print_digest:
+        print(sources_digest(args.workload))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the sharding plan is described in DESIGN.md)", file=sys.stderr)
@@ -319,6 +396,9 @@ def main():
     import quantized_state_space_amd as qs
     qs.load()
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(torch, dev)
+        return
     wl = WORKLOADS[args.workload]()
     wl.setup(dev)
     timer = EventTimer(torch)
@@ -337,26 +417,31 @@ def main():
     value = ups * args.steps / elapsed
     nbytes = wl.dominant_bytes()
     if wl.bound == "alu":
-        # fp32 vector peak of MI355X: 256 CUs x 2.4 GHz x 256 flop/clk (packed FMA)
-        achieved = wl.flops() / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": 157.3, "unit": "TFLOP/s",
-                "frac": round(achieved / 157.3, 4), "traffic": None}
+        achieved = wl.ops() / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "T VALU lane-ops/s", "frac": round(achieved / VALU_PEAK_TOPS, 4)}
     else:
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
     roof["kernel"] = wl.dominant
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
     roof["algorithmic_bytes"] = int(nbytes)
+    if wl.bound == "alu":
+        roof["ops_per_update"] = wl.ops_per_update
 
     out = {"metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic", "config": wl.config, "roofline": roof,
-           "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+           "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "timing": "HIP events on the launch stream around every timed call of the dominant "
+                     "entry point; value from the wall clock over the timed steps"}
     if not args.no_cpu_baseline:
         v, sample = wl.cpu_baseline()
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        import oracle
+        threads = oracle.max_threads()
         out["cpu_baseline"] = {"value": v, "unit": "state-updates/s", "cores": threads,
                                "kind": "oracle", "sample": sample}
     print(json.dumps(out), flush=True)

@@ -51,6 +51,13 @@ def lib():
     return _lib
 
 
+def max_threads() -> int:
+    """OpenMP threads of the oracle's parallel loops (independent chains only)."""
+    f = lib().orc_max_threads
+    f.restype = ctypes.c_int
+    return int(f())
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32

@@ -23,6 +23,7 @@
  * from the exact quotient of fp32 operands).
  */
 #include <complex.h>
+#include <omp.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -406,3 +407,6 @@ EXPORT void orc_decode_step(int64_t B, int64_t nh, int64_t P, int64_t N, int64_t
       }
     }
 }
+
+/* Number of OpenMP threads the parallel loops above use (for reporting the baseline's cores). */
+EXPORT int orc_max_threads(void) { return omp_get_max_threads(); }
