@@ -29,9 +29,9 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // v - f*s, which one fused multiply-add yields without intermediate rounding, decides the side.
 // Valid scales lie in [2^-100, 2^100]; there every non-zero remainder is at least 2^-149 in
 // magnitude, so its sign survives the final rounding of the fma.
-__device__ __forceinline__ bool scale_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+__host__ __device__ __forceinline__ bool scale_ok(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
 
-__device__ __forceinline__ int rne_sat(float v, float s, float lo, float hi) {
+__host__ __device__ __forceinline__ int rne_sat(float v, float s, float lo, float hi) {
   float f = v / s;
   float r = rintf(f);
   if (fabsf(f - r) == 0.5f) {
@@ -43,14 +43,50 @@ __device__ __forceinline__ int rne_sat(float v, float s, float lo, float hi) {
   return (v != v) ? 0 : (int)r;  // NaN encodes as 0
 }
 
-__device__ __forceinline__ int8_t quant8(float v, float s) {
+__host__ __device__ __forceinline__ int8_t quant8(float v, float s) {
   return scale_ok(s) ? (int8_t)rne_sat(v, s, -128.0f, 127.0f) : (int8_t)0;
+}
+
+// The same rule from a reciprocal r ~ 1/s (any r with |v*r - v/s| < 1/100 for |v/s| <= 256
+// works; fl32(1/s) gives |v*r - v/s| <= 2^-23 |v/s| <= 3.1e-5). Let f = v*r clamped to
+// [-256, 256] (beyond that the code saturates anyway) and c = rint(f). If f is more than 0.49
+// from both neighbouring half-integers, the exact quotient d lies strictly between c - 1/2 and
+// c + 1/2 and RNE(d) = c. Otherwise d may sit on or beyond the half-integer b = c +- 1/2 on f's
+// side of c. The exact v - b*s is a multiple of 2^-149 (b is a multiple of 1/2 and s >= 2^-102 in
+// every use), so the single rounding of fmaf(-b, s, v) keeps its sign and its zero-ness:
+// beyond b moves to the neighbour c +- 1, exactly on b is a tie resolved to the even neighbour.
+// The rare near-boundary branch is skipped by a whole wave when none of its lanes needs it.
+// Returns the unsaturated code as a float; the caller clamps and handles NaN and invalid scales.
+__host__ __device__ __forceinline__ float rne_recip(float v, float s, float r) {
+  const float f = fminf(fmaxf(v * r, -256.0f), 256.0f);
+  float c = rintf(f);
+  const float t = f - c;
+  if (fabsf(t) > 0.49f) {
+    const float h = copysignf(0.5f, t);
+    const float e = fmaf(-(c + h), s, v);
+    const float eh = (h > 0.0f) ? e : -e;        // > 0: beyond the boundary on f's side
+    const bool odd = (c * 0.5f) != rintf(c * 0.5f);
+    if (eh > 0.0f || (eh == 0.0f && odd)) c += h + h;
+  }
+  return c;
+}
+
+__host__ __device__ __forceinline__ int rne_sat_recip(float v, float s, float r, int lo, int hi) {
+  const float c = fminf(fmaxf(rne_recip(v, s, r), (float)lo), (float)hi);
+  return (v == v) ? (int)c : 0;  // NaN encodes as 0
+}
+
+// Reciprocal used with rne_sat_recip; 0 marks a scale outside the valid range (codes 0).
+__host__ __device__ __forceinline__ float recip_or_zero(float s) { return scale_ok(s) ? 1.0f / s : 0.0f; }
+
+__host__ __device__ __forceinline__ int8_t quant8_r(float v, float s, float r) {
+  return (r != 0.0f) ? (int8_t)rne_sat_recip(v, s, r, -128, 127) : (int8_t)0;
 }
 
 // Soft-edge byte (Quamba-SE blog, 2.1 and 2.2): strict |v| < L selects scale/4 with a 6-bit
 // payload (tag 10), |v| > H selects scale*4 (tag 11), anything else (including both tests true)
 // the base scale with a 7-bit payload (tag 0). Payloads are two's complement.
-__device__ __forceinline__ uint8_t softedge_code(float v, float s, float L, float H) {
+__host__ __device__ __forceinline__ uint8_t softedge_code(float v, float s, float L, float H) {
   if (!scale_ok(s) || v != v) return 0;
   float a = fabsf(v);
   bool small = a < L, large = a > H;
@@ -59,8 +95,24 @@ __device__ __forceinline__ uint8_t softedge_code(float v, float s, float L, floa
   return (uint8_t)(rne_sat(v, s, -64.0f, 63.0f) & 0x7F);
 }
 
+// softedge_code from a reciprocal (r = recip_or_zero(s)): the small and large modes scale s and r
+// by exact powers of two.
+__host__ __device__ __forceinline__ uint8_t softedge_code_r(float v, float s, float r, float L, float H) {
+  if (r == 0.0f) return 0;
+  const float a = fabsf(v);
+  const bool small = a < L, large = a > H;
+  const bool sm = small && !large, lg = large && !small;
+  const float ss = sm ? 0.25f * s : (lg ? 4.0f * s : s);
+  const float rr = sm ? 4.0f * r : (lg ? 0.25f * r : r);
+  const int lim = (sm || lg) ? 32 : 64;
+  const int q = rne_sat_recip(v, ss, rr, -lim, lim - 1);
+  const uint32_t code = sm ? (0x80u | ((uint32_t)q & 0x3Fu))
+                           : (lg ? (0xC0u | ((uint32_t)q & 0x3Fu)) : ((uint32_t)q & 0x7Fu));
+  return (uint8_t)code;  // NaN: neither small nor large, payload 0
+}
+
 // Value of a soft-edge byte as one correctly rounded fp32 product (0 for an invalid scale).
-__device__ __forceinline__ float softedge_value(uint32_t b, float s) {
+__host__ __device__ __forceinline__ float softedge_value(uint32_t b, float s) {
   if (!scale_ok(s)) return 0.0f;
   if ((b & 0x80u) == 0) {
     int q = (b & 0x40u) ? (int)(b & 0x7Fu) - 128 : (int)(b & 0x7Fu);

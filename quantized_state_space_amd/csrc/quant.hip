@@ -18,8 +18,17 @@ constexpr int kThreads = 256;
 constexpr int kVec = 16;          // elements per thread
 constexpr int kMaxLdsGroups = 1024;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 enum Op { OP_QUANT = 0, OP_ABSMAX = 1, OP_SOFTEDGE = 2 };
 enum Map { MAP_GROUP = 0, MAP_STATE = 1 };
+// ROWS: inner % 16 == 0, a thread's 16 elements share one channel row.
+// CHANNELS: inner == 1 and a thread's 16 elements are 16 consecutive channels of one scale
+//           lookup pattern (C % 16 == 0, no permutation; STATE also needs N % 16 == 0 and
+//           gs % 16 == 0, GROUP a 16-byte aligned group map).
+// GENERIC: any other shape, element by element.
+enum Layout { L_ROWS = 0, L_CHANNELS = 1, L_GENERIC = 2 };
 
 struct Geometry {
   int64_t total, C, inner;
@@ -29,114 +38,176 @@ struct Geometry {
   int32_t nscales;
 };
 
+// a / b, in 32-bit arithmetic when both fit (the common case), else 64-bit.
+__device__ __forceinline__ int64_t div_fast(int64_t a, int64_t b) {
+  if (((uint64_t)a | (uint64_t)b) >> 32 == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 template <int MAP>
 __device__ __forceinline__ int scale_index(const Geometry& g, int64_t c) {
   if (MAP == MAP_GROUP) return g.group_of[c];
-  int64_t grp = c / g.N, n = c - grp * g.N;
-  return (int)(grp * g.ngs + n / g.gs);
+  const int64_t grp = div_fast(c, g.N), n = c - grp * g.N;
+  return (int)(grp * g.ngs + div_fast(n, g.gs));
 }
 
-// Visits the kVec elements of one thread: calls f(k, value, scale_index) for each valid one.
-template <int MAP, typename F>
-__device__ __forceinline__ int visit(const Geometry& g, const float* __restrict__ x, int64_t e0,
-                                     F&& f) {
-  const int64_t row = e0 / g.inner;
-  int64_t i = e0 - row * g.inner;
-  int64_t c = row % g.C, o = row / g.C;
-  const int nvalid = (int)((g.total - e0) < kVec ? (g.total - e0) : kVec);
-  if (g.inner % kVec == 0) {
-    // all elements share one channel row
-    const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
-    const int si = scale_index<MAP>(g, c);
-    const float4* p = reinterpret_cast<const float4*>(x + (o * g.C + src) * g.inner + i);
-#pragma unroll
-    for (int k = 0; k < kVec / 4; ++k) {
-      float4 v = p[k];
-      f(4 * k + 0, v.x, si);
-      f(4 * k + 1, v.y, si);
-      f(4 * k + 2, v.z, si);
-      f(4 * k + 3, v.w, si);
-    }
-    return kVec;
-  }
-  const bool contiguous = !(MAP == MAP_GROUP && g.perm) && nvalid == kVec;
+// The kVec elements of one thread: values, their scale indices (one index when the layout makes
+// it uniform over the thread), and how many are valid.
+template <int MAP, int LAYOUT>
+struct Tile {
+  static constexpr bool kUniform = LAYOUT == L_ROWS || (LAYOUT == L_CHANNELS && MAP == MAP_STATE);
   float v[kVec];
-  if (contiguous) {
-    const float4* p = reinterpret_cast<const float4*>(x + e0);
+  int si[kUniform ? 1 : kVec];
+  int n;
+};
+
+template <int MAP, int LAYOUT>
+__device__ __forceinline__ void load_tile(const Geometry& g, const float* __restrict__ x,
+                                          int64_t e0, Tile<MAP, LAYOUT>& t) {
+  if (LAYOUT == L_ROWS || LAYOUT == L_CHANNELS) {
+    const f32x4* p;
+    if (LAYOUT == L_ROWS) {
+      const int64_t row = div_fast(e0, g.inner);
+      const int64_t i = e0 - row * g.inner;
+      const int64_t o = div_fast(row, g.C), c = row - o * g.C;
+      const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
+      t.si[0] = scale_index<MAP>(g, c);
+      p = reinterpret_cast<const f32x4*>(x + (o * g.C + src) * g.inner + i);
+    } else {
+      const int64_t o = div_fast(e0, g.C), c0 = e0 - o * g.C;
+      if (MAP == MAP_GROUP) {
+        const u32x4 gid = *reinterpret_cast<const u32x4*>(g.group_of + c0);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) t.si[k % (Tile<MAP, LAYOUT>::kUniform ? 1 : kVec)] =
+            (int)((gid[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+      } else {
+        t.si[0] = scale_index<MAP>(g, c0);
+      }
+      p = reinterpret_cast<const f32x4*>(x + e0);
+    }
 #pragma unroll
     for (int k = 0; k < kVec / 4; ++k) {
-      float4 t = p[k];
-      v[4 * k] = t.x; v[4 * k + 1] = t.y; v[4 * k + 2] = t.z; v[4 * k + 3] = t.w;
+      const f32x4 q = __builtin_nontemporal_load(p + k);
+      t.v[4 * k] = q.x; t.v[4 * k + 1] = q.y; t.v[4 * k + 2] = q.z; t.v[4 * k + 3] = q.w;
+    }
+    t.n = kVec;
+    return;
+  }
+  const int64_t row = div_fast(e0, g.inner);
+  int64_t i = e0 - row * g.inner;
+  int64_t o = div_fast(row, g.C), c = row - o * g.C;
+  t.n = (int)((g.total - e0) < kVec ? (g.total - e0) : kVec);
+  const bool contiguous = !(MAP == MAP_GROUP && g.perm) && t.n == kVec;
+  if (contiguous) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(x + e0);
+#pragma unroll
+    for (int k = 0; k < kVec / 4; ++k) {
+      const f32x4 q = p[k];
+      t.v[4 * k] = q.x; t.v[4 * k + 1] = q.y; t.v[4 * k + 2] = q.z; t.v[4 * k + 3] = q.w;
     }
   }
 #pragma unroll
   for (int k = 0; k < kVec; ++k) {
-    if (k < nvalid) {
-      float val;
-      if (contiguous) {
-        val = v[k];
-      } else {
+    if (k < t.n) {
+      if (!contiguous) {
         const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
-        val = x[(o * g.C + src) * g.inner + i];
+        t.v[k] = x[(o * g.C + src) * g.inner + i];
       }
-      f(k, val, scale_index<MAP>(g, c));
+      t.si[k] = scale_index<MAP>(g, c);
       if (++i == g.inner) { i = 0; if (++c == g.C) { c = 0; ++o; } }
     }
   }
-  return nvalid;
 }
 
-template <int OP, int MAP>
+template <int OP>
+__device__ __forceinline__ uint32_t encode(float v, float2 sr, float2 lh) {
+  if (OP == OP_QUANT) return (uint32_t)(uint8_t)quant8_r(v, sr.x, sr.y);
+  return softedge_code_r(v, sr.x, sr.y, lh.x, lh.y);
+}
+
+template <int OP, int MAP, int LAYOUT>
 __global__ __launch_bounds__(kThreads) void k_elementwise(
     const float* __restrict__ x, Geometry g, const float* __restrict__ scales,
     const float* __restrict__ Lth, const float* __restrict__ Hth, void* __restrict__ out) {
-  __shared__ float s_scale[kMaxLdsGroups];
-  __shared__ float s_L[OP == OP_SOFTEDGE ? kMaxLdsGroups : 1];
-  __shared__ float s_H[OP == OP_SOFTEDGE ? kMaxLdsGroups : 1];
+  __shared__ float2 s_sr[OP == OP_ABSMAX ? 1 : kMaxLdsGroups];  // (s, 1/s or 0 if invalid)
+  __shared__ float2 s_LH[OP == OP_SOFTEDGE ? kMaxLdsGroups : 1];
   __shared__ unsigned s_max[OP == OP_ABSMAX ? kMaxLdsGroups : 1];
   const bool lds = g.nscales <= kMaxLdsGroups;
   if (lds) {
     for (int k = threadIdx.x; k < g.nscales; k += kThreads) {
-      if (OP == OP_ABSMAX) s_max[k] = 0u;
-      else s_scale[k] = scales[k];
-      if (OP == OP_SOFTEDGE) { s_L[k] = Lth[k]; s_H[k] = Hth[k]; }
+      if (OP == OP_ABSMAX) {
+        s_max[k] = 0u;
+      } else {
+        const float sc = scales[k];
+        s_sr[k] = make_float2(sc, recip_or_zero(sc));
+      }
+      if (OP == OP_SOFTEDGE) s_LH[k] = make_float2(Lth[k], Hth[k]);
     }
     __syncthreads();
   }
+  auto scale_of = [&](int si) -> float2 {
+    if (lds) return s_sr[si];
+    const float sc = scales[si];
+    return make_float2(sc, recip_or_zero(sc));
+  };
+  auto thresholds_of = [&](int si) -> float2 {
+    if (OP != OP_SOFTEDGE) return make_float2(0.0f, 0.0f);
+    return lds ? s_LH[si] : make_float2(Lth[si], Hth[si]);
+  };
+  constexpr bool kUniform = Tile<MAP, LAYOUT>::kUniform;
   const int64_t e0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kVec;
   if (e0 < g.total) {
+    Tile<MAP, LAYOUT> t;
+    load_tile<MAP, LAYOUT>(g, x, e0, t);
     if (OP == OP_ABSMAX) {
-      // running max per scale index; consecutive elements usually share it
-      int cur = -1;
-      float m = 0.0f;
-      auto flush = [&]() {
-        if (cur >= 0 && m > 0.0f) {
-          if (lds) atomicMax(&s_max[cur], __float_as_uint(m));
-          else atomicMax(reinterpret_cast<unsigned*>(out) + cur, __float_as_uint(m));
+      unsigned* gmax = reinterpret_cast<unsigned*>(out);
+      auto push = [&](int si, float m) {
+        if (m > 0.0f) {
+          if (lds) atomicMax(&s_max[si], __float_as_uint(m));
+          else atomicMax(gmax + si, __float_as_uint(m));
         }
       };
-      visit<MAP>(g, x, e0, [&](int, float v, int si) {
-        if (si != cur) { flush(); cur = si; m = 0.0f; }
-        m = fmaxf(m, finite_abs(v));
-      });
-      flush();
-    } else {
-      alignas(16) uint8_t res[kVec];
-      const int n = visit<MAP>(g, x, e0, [&](int k, float v, int si) {
-        const float s = lds ? s_scale[si] : scales[si];
-        if (OP == OP_QUANT) {
-          res[k] = (uint8_t)quant8(v, s);
-        } else {
-          const float L = lds ? s_L[si] : Lth[si];
-          const float H = lds ? s_H[si] : Hth[si];
-          res[k] = softedge_code(v, s, L, H);
-        }
-      });
-      uint8_t* o8 = reinterpret_cast<uint8_t*>(out) + e0;
-      if (n == kVec) {
-        *reinterpret_cast<uint4*>(o8) = *reinterpret_cast<const uint4*>(res);
+      if (kUniform) {
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) m = fmaxf(m, finite_abs(t.v[k]));
+        push(t.si[0], m);
       } else {
-        for (int k = 0; k < n; ++k) o8[k] = res[k];
+        // running max per scale index; consecutive elements usually share it
+        int cur = t.si[0];
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          if (k < t.n) {
+            const int si = t.si[kUniform ? 0 : k];
+            if (si != cur) { push(cur, m); cur = si; m = 0.0f; }
+            m = fmaxf(m, finite_abs(t.v[k]));
+          }
+        }
+        push(cur, m);
+      }
+    } else {
+      uint32_t packed[kVec / 4] = {0u, 0u, 0u, 0u};
+      if (kUniform) {
+        const float2 sr = scale_of(t.si[0]);
+        const float2 lh = thresholds_of(t.si[0]);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) packed[k >> 2] |= encode<OP>(t.v[k], sr, lh) << (8 * (k & 3));
+      } else {
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          if (k < t.n) {
+            const int si = t.si[kUniform ? 0 : k];
+            packed[k >> 2] |= encode<OP>(t.v[k], scale_of(si), thresholds_of(si)) << (8 * (k & 3));
+          }
+        }
+      }
+      uint8_t* o8 = reinterpret_cast<uint8_t*>(out) + e0;
+      if (t.n == kVec) {
+        const u32x4 pk = {packed[0], packed[1], packed[2], packed[3]};
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(o8));
+      } else {
+        for (int k = 0; k < t.n; ++k) o8[k] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
       }
     }
   }
@@ -199,19 +270,42 @@ qssm_status check_extents(int64_t outer, int64_t C, int64_t inner) {
 }
 
 template <int OP, int MAP>
+int choose_layout(const Geometry& g) {
+  if (g.inner % kVec == 0) return L_ROWS;
+  if (g.inner == 1 && g.C % kVec == 0) {
+    if (MAP == MAP_GROUP && !g.perm && (reinterpret_cast<uintptr_t>(g.group_of) % 16) == 0)
+      return L_CHANNELS;
+    if (MAP == MAP_STATE && g.N % kVec == 0 && g.gs % kVec == 0) return L_CHANNELS;
+  }
+  return L_GENERIC;
+}
+
+template <int OP, int MAP, int LAYOUT>
+void launch_elementwise(const float* x, const Geometry& g, const float* scales, const float* L,
+                        const float* H, void* out, hipStream_t st) {
+  const unsigned blocks = (unsigned)cdiv(g.total, (int64_t)kThreads * kVec);
+  k_elementwise<OP, MAP, LAYOUT><<<blocks, kThreads, 0, st>>>(x, g, scales, L, H, out);
+}
+
+template <int OP, int MAP>
+void launch_any(int layout, const float* x, const Geometry& g, const float* scales, const float* L,
+                const float* H, void* out, hipStream_t st) {
+  if (layout == L_ROWS) launch_elementwise<OP, MAP, L_ROWS>(x, g, scales, L, H, out, st);
+  else if (layout == L_CHANNELS) launch_elementwise<OP, MAP, L_CHANNELS>(x, g, scales, L, H, out, st);
+  else launch_elementwise<OP, MAP, L_GENERIC>(x, g, scales, L, H, out, st);
+}
+
+template <int OP, int MAP>
 qssm_status launch(const float* x, const Geometry& g, float* scales, int compute_scales,
                    const float* L, const float* H, void* out, hipStream_t st) {
+  const int layout = choose_layout<OP, MAP>(g);
   if (compute_scales) {
     k_fill_u32<<<(unsigned)cdiv(g.nscales, 256), 256, 0, st>>>(
         reinterpret_cast<unsigned*>(scales), g.nscales, 0u);
-    if (g.total > 0)
-      k_elementwise<OP_ABSMAX, MAP><<<(unsigned)cdiv(g.total, (int64_t)kThreads * kVec), kThreads,
-                                      0, st>>>(x, g, nullptr, nullptr, nullptr, scales);
+    if (g.total > 0) launch_any<OP_ABSMAX, MAP>(layout, x, g, nullptr, nullptr, nullptr, scales, st);
     k_finalize_scales<<<(unsigned)cdiv(g.nscales, 256), 256, 0, st>>>(scales, g.nscales);
   }
-  if (g.total > 0)
-    k_elementwise<OP, MAP><<<(unsigned)cdiv(g.total, (int64_t)kThreads * kVec), kThreads, 0,
-                             st>>>(x, g, scales, L, H, out);
+  if (g.total > 0) launch_any<OP, MAP>(layout, x, g, scales, L, H, out, st);
   return launch_status("quantize");
 }
 
