@@ -30,7 +30,7 @@ constexpr int kPadRows = 64;    // zero rows after L in every staged plane (>= k
 constexpr int kLanes = 64;      // channels per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef const float __attribute__((address_space(4))) cfloat;  // constant (scalar-loadable) memory
+typedef const uint32_t __attribute__((address_space(4))) cu32;  // constant (scalar-loadable) memory
 
 struct ScanParams {
   int64_t B, L, D, N;
@@ -40,22 +40,30 @@ struct ScanParams {
   const float* x_scales;
   const float* delta;
   const float* A;
-  const float* stage;  // [B, Gbc, N/NS, L, 2*NS]: (Bh[NS], Ch[NS]) per wave plane and step
+  const void* stage;  // [B, Gbc, N/NS, L + pad, 2*NS]: (B[NS], C[NS]) per wave plane and step
+  const float* B_scales;  // [Gbc, N / gs]
+  const float* C_scales;
   const float* Dskip;
   const float* h0;
   void* y;
   float* h_last;
 };
 
-// Dequantize B and C once into the staging layout read by the scan: for every (b, g), the states
-// are cut into planes of `ns` consecutive states (the states one wave owns), and each plane stores
-// per step the ns B values followed by the ns C values: [B, Gbc, N/ns, L, 2*ns] fp32.
+// Stage B and C once into the layout read by the scan: for every (b, g), the states are cut into
+// planes of `ns` consecutive states (the states one wave owns), and each plane stores per step the
+// ns B values followed by the ns C values.
+//  * CODE16 = false: dequantized fp32 values, [B, Gbc, N/ns, L + pad, 2*ns] floats.
+//  * CODE16 = true: the int8 codes as fp16 (exact), [B, Gbc, N/ns, L + pad, 2*ns] halves; used
+//    when every plane lies inside one state group, so that its scales factor out of the plane's
+//    chains (the scan applies them once per output). Codes of a group whose scale is not valid
+//    are staged as 0.
+template <bool CODE16>
 __global__ __launch_bounds__(256) void k_stage_bc(const int8_t* __restrict__ Bq,
                                                   const int8_t* __restrict__ Cq,
                                                   const float* __restrict__ Bs,
                                                   const float* __restrict__ Cs, int64_t B,
                                                   int Gbc, int N, int64_t L, int gs, int ns,
-                                                  float* __restrict__ stage) {
+                                                  void* __restrict__ stage) {
   const int64_t Lp = L + kPadRows;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over (b, g, n, t < Lp)
   const int64_t total = B * Gbc * N * Lp;
@@ -67,27 +75,34 @@ __global__ __launch_bounds__(256) void k_stage_bc(const int8_t* __restrict__ Bq,
   const int g = (int)(bg % Gbc);
   const int ngs = N / gs;
   const float sb = Bs[g * ngs + n / gs], sc = Cs[g * ngs + n / gs];
-  float vb = 0.0f, vc = 0.0f;  // rows past L are zero (read by the last batches, times delta = 0)
-  if (t < L) {
-    vb = scale_ok(sb) ? (float)Bq[r * L + t] * sb : 0.0f;
-    vc = scale_ok(sc) ? (float)Cq[r * L + t] * sc : 0.0f;
-  }
   const int plane = n / ns, k = n % ns;
-  float* dst = stage + (((bg * (N / ns) + plane) * Lp + t) * (2 * ns));
-  dst[k] = vb;
-  dst[ns + k] = vc;
+  const int64_t row = ((bg * (N / ns) + plane) * Lp + t) * (2 * ns);
+  // rows past L are zero (read by the last batches, times delta = 0)
+  const int qb = (t < L && scale_ok(sb)) ? (int)Bq[r * L + t] : 0;
+  const int qc = (t < L && scale_ok(sc)) ? (int)Cq[r * L + t] : 0;
+  if (CODE16) {
+    _Float16* dst = reinterpret_cast<_Float16*>(stage) + row;
+    dst[k] = (_Float16)qb;
+    dst[ns + k] = (_Float16)qc;
+  } else {
+    float* dst = reinterpret_cast<float*>(stage) + row;
+    dst[k] = scale_ok(sb) ? (float)qb * sb : 0.0f;
+    dst[ns + k] = scale_ok(sc) ? (float)qc * sc : 0.0f;
+  }
 }
 
+// Unscaled x value of a code byte: the int8 code, or the soft-edge code times its mode factor
+// (1, 1/4 or 4; exact), so that the dequantized value is sx * xunit.
 template <int XCODE>
-__device__ __forceinline__ float xval(uint32_t byte, float s) {
-  if (XCODE == QSSM_X_SOFTEDGE) return softedge_value(byte, s);
-  return (float)(int8_t)(byte & 0xFFu) * s;
+__device__ __forceinline__ float xunit(uint32_t byte) {  // NOLINT
+  if (XCODE == QSSM_X_SOFTEDGE) return softedge_value(byte & 0xFFu, 1.0f);
+  return (float)(int8_t)(byte & 0xFFu);
 }
 
-template <int NS, int W, int XCODE, int YF16, int kBatch>
+template <int NS, int W, int XCODE, int YF16, int kBatch, int PFD, bool CODE16>
 __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   __shared__ float ybuf[2][W][kT][kLanes];
-  constexpr int kS = 2 * NS;  // staged floats per step
+  constexpr int kS = CODE16 ? NS : 2 * NS;  // staged 32-bit words per step
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -99,10 +114,29 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   const int64_t L = p.L;
   const int g = uniform((int)(d0 / p.dpg));
 
-  // x scale (int8 value = s * q; soft-edge base scale), a valid scale is required, else 0
+  // Scales. x: per channel (lane); a channel whose scale is not valid has every x value 0, so its
+  // codes are masked to 0 and its scale taken as 0. With fp16 codes staged, the B and C scales of
+  // the wave's state group multiply the step input (B) and the wave's partial output (C); an
+  // invalid one is 0 (its codes are staged as 0 as well).
   float sx = p.x_scales[p.x_group_of[dc]];
-  if (XCODE == QSSM_X_INT8 && !scale_ok(sx)) sx = 0.0f;
-  const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
+  const bool sx_ok = scale_ok(sx);
+  const uint32_t xmask = sx_ok ? 0xFFFFFFFFu : 0u;
+  if (!sx_ok) sx = 0.0f;
+  const int ngs = (int)(p.N / p.gs);
+  float su = sx;         // scale of the per-step input dt * x * B of this wave's chains
+  float wC[W];           // scale of each wave's partial output
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) wC[ww] = 1.0f;
+  if (CODE16) {
+    const float sb = p.B_scales[g * ngs + (w * NS) / p.gs];
+    su = sx * (scale_ok(sb) ? sb : 0.0f);
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const float sc = p.C_scales[g * ngs + (ww * NS) / p.gs];
+      wC[ww] = scale_ok(sc) ? sc : 0.0f;
+    }
+  }
+  const float Dsx = (p.Dskip ? p.Dskip[dc] : 0.0f) * sx;
 
   float a2[NS], h[NS];
 #pragma unroll
@@ -114,16 +148,12 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 
   const float* __restrict__ drow = p.delta + (b * p.D + dc) * L;
   const uint8_t* __restrict__ xrow = reinterpret_cast<const uint8_t*>(p.x) + (b * p.D + dc) * L;
-  // this wave's plane of staged (Bh, Ch): kS floats per step, read through the constant address
+  // this wave's plane of staged (B, C): kS words per step, read through the constant address
   // space (wave-uniform addresses -> scalar loads into SGPRs)
-  const cfloat* st =
-      (const cfloat*)(p.stage + ((b * p.Gbc + g) * (p.N / NS) + w) * (L + kPadRows) * kS);
+  const uint32_t* stg = reinterpret_cast<const uint32_t*>(p.stage) +
+                        ((b * p.Gbc + g) * (p.N / NS) + w) * (L + kPadRows) * kS;
+  const cu32* st = (const cu32*)stg;
   const bool vec_ok = (L % 16) == 0;
-
-  float dl[kT];
-  uint32_t xq[kT / 4];
-  float dn[kT] = {};
-  uint32_t xn[kT / 4] = {};
 
   auto load_block = [&](int64_t tb, float* dv, uint32_t* xv) {
     if (vec_ok && tb + kT <= L) {
@@ -159,37 +189,67 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   // are fetched one batch of steps ahead and the loop drains the scalar queue (lgkmcnt 0) once per
   // batch, right before issuing the next batch, so each batch's latency hides behind the previous
   // batch's arithmetic. Steps past L read the zero pad rows (times delta = 0).
-  float bcur[kBatch][kS], bnxt[kBatch][kS];
-  auto sload = [&](int t0, float (&dst)[kBatch][kS]) {
-    const cfloat* src = st + (int64_t)t0 * kS;
+  uint32_t bcur[kBatch][kS], bnxt[kBatch][kS];
+  auto sload = [&](int64_t t0, uint32_t (&dst)[kBatch][kS]) {
+    const cu32* src = st + t0 * kS;
 #pragma unroll
     for (int s2 = 0; s2 < kBatch; ++s2)
 #pragma unroll
       for (int j = 0; j < kS; ++j) dst[s2][j] = src[s2 * kS + j];
   };
+  // B and C operand k of a staged step
+  auto opB = [&](const uint32_t (&row)[kS], int k) -> float {
+    if (CODE16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(row[k / 2] >> (16 * (k % 2))));
+    return __uint_as_float(row[k]);
+  };
+  auto opC = [&](const uint32_t (&row)[kS], int k) -> float {
+    if (CODE16)
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(row[NS / 2 + k / 2] >> (16 * (k % 2))));
+    return __uint_as_float(row[NS + k]);
+  };
 
+  float dl[kT], dn[kT];
+  uint32_t xq[kT / 4], xn[kT / 4];
+#pragma unroll
+  for (int k = 0; k < kT; ++k) dn[k] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kT / 4; ++k) xn[k] = 0u;
   load_block(0, dl, xq);
   sload(0, bcur);
   int buf = 0;
   for (int64_t tb = 0; tb < L; tb += kT) {
+    // (masking the codes of the current block here, not at load time, keeps the next block's
+    // loads in flight during this block's arithmetic)
+#pragma unroll
+    for (int k = 0; k < kT / 4; ++k) xq[k] &= xmask;
     if (tb + kT < L) load_block(tb + kT, dn, xn);
+    // Pull the staged rows of the block PFD blocks ahead into L2 with one vector load per
+    // 128-byte line, so that the scalar loads of that block hit L2 instead of going to memory.
+    // The loaded value is only consumed (without use) after this block's arithmetic.
+    uint32_t pf = 0u;
+    if (PFD > 0) {
+      const int64_t tp = tb + (int64_t)PFD * kT;
+      constexpr int kLines = (kT * kS * 4 + 127) / 128;
+      if (tp < L && lane < kLines) pf = stg[tp * kS + lane * 32];
+    }
 
 #pragma unroll
     for (int bt = 0; bt < kT; bt += kBatch) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the current batch has landed
-      sload((int)tb + bt + kBatch, bnxt);
+      sload(tb + bt + kBatch, bnxt);
 #pragma unroll
       for (int s2 = 0; s2 < kBatch; ++s2) {
         const int t = bt + s2;
-        const float xh = xval<XCODE>((xq[t / 4] >> (8 * (t % 4))) & 0xFFu, sx);
         const float dt = dl[t];
-        const float dtx = dt * xh;
+        const float u = dt * xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))) * su;
         float yp;
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
           const float dA = __builtin_amdgcn_exp2f(dt * a2[k]);
-          h[k] = fmaf(dA, h[k], dtx * bcur[s2][k]);
-          yp = (k == 0) ? bcur[s2][NS] * h[0] : fmaf(bcur[s2][NS + k], h[k], yp);
+          // fma with a zero addend keeps the fp16 operand in a mixed-precision fma
+          const float in = CODE16 ? fmaf(u, opB(bcur[s2], k), 0.0f) : u * opB(bcur[s2], k);
+          h[k] = fmaf(dA, h[k], in);
+          yp = (k == 0) ? opC(bcur[s2], 0) * h[0] : fmaf(opC(bcur[s2], k), h[k], yp);
         }
         ybuf[buf][w][t][lane] = yp;
       }
@@ -198,6 +258,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 #pragma unroll
         for (int j = 0; j < kS; ++j) bcur[s2][j] = bnxt[s2][j];
     }
+    if (PFD > 0) asm volatile("" ::"v"(pf));
     __syncthreads();
 
     // combine: wave w finalizes steps [w*kT/W, (w+1)*kT/W) of every channel of the block
@@ -208,9 +269,9 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       const int t = w * kPer + j;
       float sum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < W; ++ww) sum += ybuf[buf][ww][t][lane];
-      const float xh = xval<XCODE>((xq[t / 4] >> (8 * (t % 4))) & 0xFFu, sx);
-      yo[j] = fmaf(Dd, xh, sum);
+      for (int ww = 0; ww < W; ++ww)
+        sum = CODE16 ? fmaf(wC[ww], ybuf[buf][ww][t][lane], sum) : sum + ybuf[buf][ww][t][lane];
+      yo[j] = fmaf(Dsx, xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))), sum);
     }
     const int64_t t0 = tb + w * kPer;
     if (valid) {
@@ -246,17 +307,25 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   }
 }
 
-template <int NS, int W, int BATCH>
-qssm_status launch_scan(const ScanParams& p, int xcode, int yf16, hipStream_t st) {
+template <int NS, int W, int BATCH, bool CODE16>
+void launch_scan_t(const ScanParams& p, int xcode, int yf16, dim3 grid, dim3 block, hipStream_t st) {
+  if (xcode == QSSM_X_INT8) {
+    if (yf16) k_scan_m1<NS, W, QSSM_X_INT8, 1, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+    else k_scan_m1<NS, W, QSSM_X_INT8, 0, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+  } else {
+    if (yf16) k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 1, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+    else k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 0, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+  }
+}
+
+// BATCH16 / BATCH32: steps per scalar-load batch with fp16 codes / fp32 values staged (two
+// batches of kS words per step must fit the SGPR budget next to the kernel's other scalars)
+template <int NS, int W, int BATCH16, int BATCH32>
+qssm_status launch_scan(const ScanParams& p, int xcode, int yf16, bool code16, hipStream_t st) {
   dim3 grid((unsigned)cdiv(p.D, kLanes), (unsigned)p.B);
   dim3 block(64 * W);
-  if (xcode == QSSM_X_INT8) {
-    if (yf16) k_scan_m1<NS, W, QSSM_X_INT8, 1, BATCH><<<grid, block, 0, st>>>(p);
-    else k_scan_m1<NS, W, QSSM_X_INT8, 0, BATCH><<<grid, block, 0, st>>>(p);
-  } else {
-    if (yf16) k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 1, BATCH><<<grid, block, 0, st>>>(p);
-    else k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 0, BATCH><<<grid, block, 0, st>>>(p);
-  }
+  if (code16) launch_scan_t<NS, W, BATCH16, true>(p, xcode, yf16, grid, block, st);
+  else launch_scan_t<NS, W, BATCH32, false>(p, xcode, yf16, grid, block, st);
   return launch_status("scan_w8a8");
 }
 
@@ -312,24 +381,31 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
     return fail(QSSM_ERR_WORKSPACE, "workspace too small after 256-byte alignment");
 
   const int ns = states_per_wave(N);
+  // fp16 codes when every wave's states lie inside one B/C state group
+  const bool code16 = (a->bc_group_size % ns) == 0;
   const int64_t nstage = B * a->bc_groups * N * (L + kPadRows);
   if (nstage > 0) {
-    k_stage_bc<<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
-        a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size, ns,
-        stage);
+    if (code16)
+      k_stage_bc<true><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
+          a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
+          ns, stage);
+    else
+      k_stage_bc<false><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
+          a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
+          ns, stage);
     if (qssm_status s = launch_status("scan_w8a8 staging")) return s;
   }
 
   ScanParams p{B, L, D, N, a->x_groups, a->bc_groups, a->bc_group_size, (int32_t)dpg,
-               a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->Dskip, a->h0,
-               a->y, a->h_last};
+               a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->B_scales,
+               a->C_scales, a->Dskip, a->h0, a->y, a->h_last};
   const int yf16 = a->y_dtype == QSSM_F16;
   switch (N) {
-    case 4: return launch_scan<4, 1, 8>(p, a->x_code, yf16, stream);
-    case 8: return launch_scan<2, 4, 16>(p, a->x_code, yf16, stream);
-    case 16: return launch_scan<4, 4, 8>(p, a->x_code, yf16, stream);
-    case 32: return launch_scan<4, 8, 8>(p, a->x_code, yf16, stream);
-    default: return launch_scan<8, 8, 4>(p, a->x_code, yf16, stream);
+    case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yf16, code16, stream);
+    case 8: return launch_scan<2, 4, 16, 16>(p, a->x_code, yf16, code16, stream);
+    case 16: return launch_scan<4, 4, 8, 8>(p, a->x_code, yf16, code16, stream);
+    case 32: return launch_scan<4, 8, 8, 8>(p, a->x_code, yf16, code16, stream);
+    default: return launch_scan<8, 8, 4, 4>(p, a->x_code, yf16, code16, stream);
   }
 }
 

@@ -51,15 +51,24 @@ def test_c1_tiny_dynamic_scales(dev):
     assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
 
 
-@pytest.mark.parametrize("B,D,L,N,G,soft", [(2, 100, 300, 16, 3, False), (1, 64, 77, 4, 2, False),
-                                             (2, 192, 64, 8, 5, False), (1, 128, 200, 32, 4, False),
-                                             (1, 64, 129, 64, 2, False), (2, 130, 301, 16, 4, True)])
-def test_ragged_shapes_static_scales(dev, B, D, L, N, G, soft):
-    print(f"\n[mamba1 B={B} D={D} L={L} N={N} G={G} softedge={soft}]", flush=True)
+# gs: B/C state-group size. The kernel stages B/C as fp16 codes when each wave's states lie in one
+# group (gs a multiple of the states per wave: 4, or 2 for N = 8, or 8 for N = 64) and as
+# dequantized fp32 values otherwise; both layouts are covered.
+@pytest.mark.parametrize("B,D,L,N,G,soft,gs", [(2, 100, 300, 16, 3, False, 4),
+                                                (1, 64, 77, 4, 2, False, 4),
+                                                (2, 192, 64, 8, 5, False, 4),
+                                                (1, 128, 200, 32, 4, False, 4),
+                                                (1, 64, 129, 64, 2, False, 4),
+                                                (1, 64, 129, 64, 2, False, 16),
+                                                (2, 100, 300, 16, 3, False, 2),
+                                                (1, 64, 70, 16, 2, False, 16),
+                                                (2, 130, 301, 16, 4, True, 4),
+                                                (1, 70, 99, 16, 3, True, 1)])
+def test_ragged_shapes_static_scales(dev, B, D, L, N, G, soft, gs):
+    print(f"\n[mamba1 B={B} D={D} L={L} N={N} G={G} softedge={soft} gs={gs}]", flush=True)
     import quantized_state_space_amd as qs
     inp = synth.mamba1_inputs(cfg=11, batch=B, seqlen=L, dim=D, dstate=N, x_dist="student_t",
                               calib_batch=1, with_h0=True)
-    gs = 4 if N >= 4 else 1
     xc = qs.QSSM_X_SOFTEDGE if soft else qs.QSSM_X_INT8
     lay = layer(dev, inp, G=G, gs=gs, x_code=xc, with_h0=True)
     lay.step()
@@ -67,6 +76,30 @@ def test_ragged_shapes_static_scales(dev, B, D, L, N, G, soft):
     if soft:
         assert np.array_equal(lay.sL.cpu().numpy(), ref["L"])
         assert np.array_equal(lay.sH.cpu().numpy(), ref["H"])
+    check_codes(lay, ref)
+    assert_rows_close(lay.y.cpu().numpy(), ref["y"], TOL_F32)
+    assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
+
+
+@pytest.mark.parametrize("code16", [True, False])
+def test_invalid_scales_zero_their_values(dev, code16):
+    """A group whose scale is outside [2^-100, 2^100] contributes zeros: an x group (its channels
+    then only carry the decaying initial state), a B state group and a C state group."""
+    import torch
+    print(f"\n[mamba1 invalid scales code16={code16}]", flush=True)
+    gs = 4 if code16 else 2
+    inp = synth.mamba1_inputs(cfg=14, batch=2, seqlen=150, dim=128, dstate=16, calib_batch=1,
+                              with_h0=True)
+    lay = layer(dev, inp, G=4, gs=gs, with_h0=True)
+    cal = op.mamba1_calib(inp, 4, gs)
+    assert np.array_equal(lay.xs.cpu().numpy(), cal["xs"])
+    cal["xs"] = cal["xs"].copy(); cal["xs"][1] = 0.0
+    cal["bs"] = cal["bs"].copy(); cal["bs"][2] = np.float32(1e-35)
+    cal["cs"] = cal["cs"].copy(); cal["cs"][0] = np.float32(2.0 ** 101)
+    for t, v in ((lay.xs, cal["xs"]), (lay.bs, cal["bs"]), (lay.cs, cal["cs"])):
+        t.copy_(torch.from_numpy(v))
+    lay.step()
+    ref = op.mamba1(inp, G=4, gs=gs, with_h0=True, calib=cal)
     check_codes(lay, ref)
     assert_rows_close(lay.y.cpu().numpy(), ref["y"], TOL_F32)
     assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
