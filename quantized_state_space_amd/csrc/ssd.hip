@@ -64,8 +64,9 @@ struct SsdParams {
   const float* h0;
   void* y;
   float* h_last;
-  float* S;    // [B, nc, nh, P, N]: chunk states, then the states entering each chunk
-  float* dec;  // [B, nc, nh]: exp(cum at the last step of the chunk)
+  float* S;       // [B, nc, nh, P, N]: chunk states
+  float* dec;     // [B, nc, nh]: exp(cum at the last step of the chunk)
+  _Float16* Hh;   // [B, nc, nh, P, N]: sC(n) * state entering the chunk, fp16 (K3's operand)
 };
 
 __device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
@@ -277,19 +278,25 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// K2: inter-chunk state passing, H_c = dec_c H_{c-1} + S_c. Slot c of S receives H_{c-1}.
+// K2: inter-chunk state passing, H_c = dec_c H_{c-1} + S_c in fp32. The state entering chunk c,
+// scaled by the C scale of its state group, goes to slot c of Hh in fp16: exactly the operand of
+// the inter-chunk product in K3 (which rounds it to fp16 anyway), at half the bytes.
 __global__ __launch_bounds__(256) void k_ssd_state_pass(SsdParams p) {
   constexpr int kE4 = kP * kN / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= p.B * p.nh * kE4) return;
   const int64_t e4 = idx % kE4, bh = idx / kE4;
   const int64_t b = bh / p.nh, h = bh % p.nh;
+  const int g = (int)(h / p.hpg);
+  const float sc = valid_or_zero(p.C_scales[g * kNSG + ((4 * e4) % kN) / kGS]);
   float4 H = p.h0 ? reinterpret_cast<const float4*>(p.h0)[bh * kE4 + e4]
                   : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t c = 0; c < p.nc; ++c) {
-    float4* slot = reinterpret_cast<float4*>(p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN)) + e4;
-    const float4 s = *slot;
-    *slot = H;
+    const int64_t slot = ((b * p.nc + c) * p.nh + h) * (int64_t)kE4 + e4;
+    const float4 s = reinterpret_cast<const float4*>(p.S)[slot];
+    const v4h hv = {(_Float16)(sc * H.x), (_Float16)(sc * H.y), (_Float16)(sc * H.z),
+                    (_Float16)(sc * H.w)};
+    reinterpret_cast<v4h*>(p.Hh)[slot] = hv;
     const float d = p.dec[(b * p.nc + c) * p.nh + h];
     H = make_float4(fmaf(d, H.x, s.x), fmaf(d, H.y, s.y), fmaf(d, H.z, s.z), fmaf(d, H.w, s.w));
   }
@@ -379,6 +386,20 @@ __device__ __forceinline__ v8h x_operand(const K3Smem& s, int J, int mm, int pt,
   return v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Loads of one head's delta and x codes into registers (see the head loop of k_ssd_output).
+__device__ __forceinline__ void k3_fetch_head(const SsdParams& p, int64_t b, int64_t c, int64_t t0,
+                                              int q, int64_t h, int tid, float& dt,
+                                              uint32_t (&x)[16]) {
+  const int jb = tid / 16, p4 = tid % 16;
+  dt = (tid < q) ? p.delta[(b * p.L + t0 + tid) * p.nh + h] : 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int jj = jb * 16 + r;
+    x[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
+                    : 0u;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   K3Smem& s = *reinterpret_cast<K3Smem*>(smem_raw);
@@ -419,57 +440,52 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
 
   const int rs = (int)(p.nh * kP);  // row stride of y in elements
   const bool full = q == kQ;
+  // Per-head inputs are fetched one head ahead into registers (delta of step tid, 16 rows x 4
+  // x codes) so that their latency hides behind the previous head's arithmetic; they are written
+  // to LDS after the barrier that ends that head. (The fp16 entering state is read at the head's
+  // start: registers for it as well would exceed the kernel's budget.)
+  const int jb = tid / 16, p4 = tid % 16;
+  float pf_dt;
+  uint32_t pf_x[16];
+  k3_fetch_head(p, b, c, t0, q, (int64_t)g * p.hpg, tid, pf_dt, pf_x);
   for (int hh = 0; hh < p.hpg; ++hh) {
     const int64_t h = (int64_t)g * p.hpg + hh;
     // decay terms of head h
     const int j = tid;
-    const float dt = (j < q) ? p.delta[(b * p.L + t0 + j) * p.nh + h] : 0.0f;
+    const float dt = pf_dt;
     const float cum = block_scan(dt * p.A[h], s.sh);
     s.cum[j] = cum;
     s.dtv[j] = dt;
     s.ecum[j] = expf(cum);
     if (tid < kP) s.sxs[tid] = valid_or_zero(p.x_scales[p.x_group_of[h * kP + tid]]);
+    // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves)
+    {
+      const uint4* hsrc = reinterpret_cast<const uint4*>(p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = tid + 256 * k;
+        *reinterpret_cast<uint4*>(s.Hs + (u / 16) * kHsRow + (u % 16) * 8) = hsrc[u];
+      }
+    }
     __syncthreads();
     s.cjv[j] = expf(s.cum[j | 31] - cum) * dt;
     // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale)
-    {
-      const int jb = tid / 16, p4 = tid % 16;
-      uint32_t d[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jj = jb * 16 + r;
-        d[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
-                        : 0u;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int pc = p4 * 4 + e;
+      const bool on = s.sxs[pc] > 0.0f;
+      _Float16* dst = s.xT + pc * kXtRow + jb * 16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pc = p4 * 4 + e;
-        const bool on = s.sxs[pc] > 0.0f;
-        _Float16* dst = s.xT + pc * kXtRow + jb * 16;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        v4h v;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          v4h v;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            v[k] = on ? (_Float16)(float)(int8_t)byte_of(d[4 * r4 + k], e) : (_Float16)0.0f;
-          *reinterpret_cast<v4h*>(dst + 4 * r4) = v;
-        }
-      }
-    }
-    // state entering the chunk, scaled by sC(n), fp16 [p][n]
-    {
-      const float4* Hsrc = reinterpret_cast<const float4*>(p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e4 = tid + 256 * k;
-        const int pr = (4 * e4) / kN, n0 = (4 * e4) % kN;
-        const float sc = valid_or_zero(p.C_scales[g * kNSG + n0 / kGS]);
-        const float4 v = Hsrc[e4];
-        const v4h hv = {(_Float16)(sc * v.x), (_Float16)(sc * v.y), (_Float16)(sc * v.z), (_Float16)(sc * v.w)};
-        *reinterpret_cast<v4h*>(s.Hs + pr * kHsRow + n0) = hv;
+        for (int k = 0; k < 4; ++k)
+          v[k] = on ? (_Float16)(float)(int8_t)byte_of(pf_x[4 * r4 + k], e) : (_Float16)0.0f;
+        *reinterpret_cast<v4h*>(dst + 4 * r4) = v;
       }
     }
     __syncthreads();
+    if (hh + 1 < p.hpg) k3_fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x);
 
     // Opaque copies of the lane and wave ids: the tile addresses below do not depend on the head,
     // and hoisting all of them out of the head loop would keep them live across it (spills).
@@ -546,17 +562,33 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
         }
         if (p.yf16) {
           __half* yb = reinterpret_cast<__half*>(p.y) + base + pc;
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            if (full || i < q) yb[i * rs] = __float2half_rn(yv[r]);
+            for (int r = 0; r < 16; ++r) {
+              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+              yb[i * rs] = __float2half_rn(yv[r]);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+              if (i < q) yb[i * rs] = __float2half_rn(yv[r]);
+            }
           }
         } else {
           float* yb = reinterpret_cast<float*>(p.y) + base + pc;
+          if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            if (full || i < q) yb[i * rs] = yv[r];
+            for (int r = 0; r < 16; ++r) {
+              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+              yb[i * rs] = yv[r];
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+              if (i < q) yb[i * rs] = yv[r];
+            }
           }
         }
       }
@@ -566,15 +598,18 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
 }
 
 struct WsLayout {
-  size_t s_bytes, dec_off, total;
+  size_t s_bytes, dec_off, hh_off, total;
 };
 
+// workspace: S (fp32 chunk states), dec, Hh (fp16 entering states), each 256-byte aligned
 WsLayout ws_layout(const qssm_ssd_args* a) {
   const int64_t nc = (a->seqlen + kQ - 1) / kQ;
+  const size_t elems = (size_t)a->batch * nc * a->nheads * kP * kN;
   WsLayout w;
-  w.s_bytes = (size_t)a->batch * nc * a->nheads * kP * kN * sizeof(float);
+  w.s_bytes = elems * sizeof(float);
   w.dec_off = (w.s_bytes + 255) & ~(size_t)255;
-  w.total = w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 256;
+  w.hh_off = (w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
+  w.total = w.hh_off + elems * sizeof(_Float16) + 256;
   return w;
 }
 
@@ -624,7 +659,8 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   SsdParams p{B, L, nh, nc, a->ngroups, (int32_t)(nh / a->ngroups), a->y_dtype == QSSM_F16,
               a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
-              reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + wl.dec_off)};
+              reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + wl.dec_off),
+              reinterpret_cast<_Float16*>(base + wl.hh_off)};
   if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff)
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
   const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
