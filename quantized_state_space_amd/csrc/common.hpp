@@ -47,12 +47,11 @@ __host__ __device__ __forceinline__ int8_t quant8(float v, float s) {
   return scale_ok(s) ? (int8_t)rne_sat(v, s, -128.0f, 127.0f) : (int8_t)0;
 }
 
-// The same rule from a reciprocal r ~ 1/s (any r with |v*r - v/s| < 1/100 for |v/s| <= 256
-// works; fl32(1/s) gives |v*r - v/s| <= 2^-23 |v/s| <= 3.1e-5). Let f = v*r clamped to
-// [-256, 256] (beyond that the code saturates anyway) and c = rint(f). If f is more than 0.49
-// from both neighbouring half-integers, the exact quotient d lies strictly between c - 1/2 and
-// c + 1/2 and RNE(d) = c. Otherwise d may sit on or beyond the half-integer b = c +- 1/2 on f's
-// side of c. The exact v - b*s is a multiple of 2^-149 (b is a multiple of 1/2 and s >= 2^-102 in
+// The same rule from a reciprocal r = fl32(1/s), for which |v*r - v/s| <= 2^-23 |v/s| + 2^-48 |v/s|
+// <= 3.1e-5 when |v/s| <= 256. Let f = v*r clamped to [-256, 256] (beyond that the code saturates
+// anyway) and c = rint(f). If |f - c| <= 1/2 - 2^-14, the exact quotient d lies within
+// 1/2 - 2^-14 + 3.1e-5 < 1/2 of c and RNE(d) = c. Otherwise d may sit on or beyond the
+// half-integer b = c +- 1/2 on f's side of c (d is within 1/2 of f). The exact v - b*s is a multiple of 2^-149 (b is a multiple of 1/2 and s >= 2^-102 in
 // every use), so the single rounding of fmaf(-b, s, v) keeps its sign and its zero-ness:
 // beyond b moves to the neighbour c +- 1, exactly on b is a tie resolved to the even neighbour.
 // The rare near-boundary branch is skipped by a whole wave when none of its lanes needs it.
@@ -61,7 +60,7 @@ __host__ __device__ __forceinline__ float rne_recip(float v, float s, float r) {
   const float f = fminf(fmaxf(v * r, -256.0f), 256.0f);
   float c = rintf(f);
   const float t = f - c;
-  if (fabsf(t) > 0.49f) {
+  if (fabsf(t) > 0.5f - 0x1p-14f) {
     const float h = copysignf(0.5f, t);
     const float e = fmaf(-(c + h), s, v);
     const float eh = (h > 0.0f) ? e : -e;        // > 0: beyond the boundary on f's side

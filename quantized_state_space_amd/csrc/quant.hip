@@ -15,18 +15,22 @@ using namespace qssm;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 16;          // elements per thread
+constexpr int kChunks = 4;        // chunks of 4 elements per thread
+constexpr int kBlockElems = kThreads * kChunks * 4;
 constexpr int kMaxLdsGroups = 1024;
+constexpr int kDecVec = 16;       // elements per thread of the soft-edge decoder
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Op { OP_QUANT = 0, OP_ABSMAX = 1, OP_SOFTEDGE = 2 };
 enum Map { MAP_GROUP = 0, MAP_STATE = 1 };
-// ROWS: inner % 16 == 0, a thread's 16 elements share one channel row.
-// CHANNELS: inner == 1 and a thread's 16 elements are 16 consecutive channels of one scale
-//           lookup pattern (C % 16 == 0, no permutation; STATE also needs N % 16 == 0 and
-//           gs % 16 == 0, GROUP a 16-byte aligned group map).
+// Work split: thread t of block x handles chunks k = 0..3 of 4 consecutive elements at
+// e = x * kBlockElems + (k * kThreads + t) * 4, so that every load and store instruction of a
+// wave covers one contiguous run (64 lanes x 16 bytes in, x 4 bytes out).
+// ROWS: inner % 4 == 0, a chunk lies in one channel row (one scale).
+// CHANNELS: inner == 1, C % 4 == 0, no permutation, the group map 4-byte aligned; a chunk is 4
+//           consecutive channels (4 group ids from one 4-byte load; for STATE, gs % 4 == 0 gives
+//           one scale per chunk).
 // GENERIC: any other shape, element by element.
 enum Layout { L_ROWS = 0, L_CHANNELS = 1, L_GENERIC = 2 };
 
@@ -51,69 +55,52 @@ __device__ __forceinline__ int scale_index(const Geometry& g, int64_t c) {
   return (int)(grp * g.ngs + div_fast(n, g.gs));
 }
 
-// The kVec elements of one thread: values, their scale indices (one index when the layout makes
-// it uniform over the thread), and how many are valid.
+// One chunk: up to 4 values, their scale indices (one when uniform), how many are valid.
 template <int MAP, int LAYOUT>
-struct Tile {
+struct Chunk {
   static constexpr bool kUniform = LAYOUT == L_ROWS || (LAYOUT == L_CHANNELS && MAP == MAP_STATE);
-  float v[kVec];
-  int si[kUniform ? 1 : kVec];
+  f32x4 v;
+  int si[kUniform ? 1 : 4];
   int n;
 };
 
 template <int MAP, int LAYOUT>
-__device__ __forceinline__ void load_tile(const Geometry& g, const float* __restrict__ x,
-                                          int64_t e0, Tile<MAP, LAYOUT>& t) {
-  if (LAYOUT == L_ROWS || LAYOUT == L_CHANNELS) {
-    const f32x4* p;
-    if (LAYOUT == L_ROWS) {
-      const int64_t row = div_fast(e0, g.inner);
-      const int64_t i = e0 - row * g.inner;
-      const int64_t o = div_fast(row, g.C), c = row - o * g.C;
-      const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
-      t.si[0] = scale_index<MAP>(g, c);
-      p = reinterpret_cast<const f32x4*>(x + (o * g.C + src) * g.inner + i);
-    } else {
-      const int64_t o = div_fast(e0, g.C), c0 = e0 - o * g.C;
-      if (MAP == MAP_GROUP) {
-        const u32x4 gid = *reinterpret_cast<const u32x4*>(g.group_of + c0);
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) t.si[k % (Tile<MAP, LAYOUT>::kUniform ? 1 : kVec)] =
-            (int)((gid[k >> 2] >> (8 * (k & 3))) & 0xFFu);
-      } else {
-        t.si[0] = scale_index<MAP>(g, c0);
-      }
-      p = reinterpret_cast<const f32x4*>(x + e0);
-    }
-#pragma unroll
-    for (int k = 0; k < kVec / 4; ++k) {
-      const f32x4 q = __builtin_nontemporal_load(p + k);
-      t.v[4 * k] = q.x; t.v[4 * k + 1] = q.y; t.v[4 * k + 2] = q.z; t.v[4 * k + 3] = q.w;
-    }
-    t.n = kVec;
+__device__ __forceinline__ void load_chunk(const Geometry& g, const float* __restrict__ x,
+                                           int64_t e, Chunk<MAP, LAYOUT>& ch) {
+  if (LAYOUT == L_ROWS) {
+    const int64_t row = div_fast(e, g.inner);
+    const int64_t i = e - row * g.inner;
+    const int64_t o = div_fast(row, g.C), c = row - o * g.C;
+    const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
+    ch.si[0] = scale_index<MAP>(g, c);
+    ch.v = *reinterpret_cast<const f32x4*>(x + (o * g.C + src) * g.inner + i);
+    ch.n = 4;
     return;
   }
-  const int64_t row = div_fast(e0, g.inner);
-  int64_t i = e0 - row * g.inner;
-  int64_t o = div_fast(row, g.C), c = row - o * g.C;
-  t.n = (int)((g.total - e0) < kVec ? (g.total - e0) : kVec);
-  const bool contiguous = !(MAP == MAP_GROUP && g.perm) && t.n == kVec;
-  if (contiguous) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(x + e0);
+  if (LAYOUT == L_CHANNELS) {
+    const int64_t o = div_fast(e, g.C), c0 = e - o * g.C;
+    if (MAP == MAP_GROUP) {
+      const uint32_t gid = *reinterpret_cast<const uint32_t*>(g.group_of + c0);
 #pragma unroll
-    for (int k = 0; k < kVec / 4; ++k) {
-      const f32x4 q = p[k];
-      t.v[4 * k] = q.x; t.v[4 * k + 1] = q.y; t.v[4 * k + 2] = q.z; t.v[4 * k + 3] = q.w;
+      for (int k = 0; k < 4; ++k) ch.si[k % (Chunk<MAP, LAYOUT>::kUniform ? 1 : 4)] = (int)((gid >> (8 * k)) & 0xFFu);
+    } else {
+      ch.si[0] = scale_index<MAP>(g, c0);
     }
+    ch.v = *reinterpret_cast<const f32x4*>(x + e);
+    ch.n = 4;
+    return;
   }
+  const int64_t row = div_fast(e, g.inner);
+  int64_t i = e - row * g.inner;
+  int64_t o = div_fast(row, g.C), c = row - o * g.C;
+  ch.n = (int)((g.total - e) < 4 ? (g.total - e) : 4);
 #pragma unroll
-  for (int k = 0; k < kVec; ++k) {
-    if (k < t.n) {
-      if (!contiguous) {
-        const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
-        t.v[k] = x[(o * g.C + src) * g.inner + i];
-      }
-      t.si[k] = scale_index<MAP>(g, c);
+  for (int k = 0; k < 4; ++k) {
+    ch.v[k] = 0.0f;
+    if (k < ch.n) {
+      const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
+      ch.v[k] = x[(o * g.C + src) * g.inner + i];
+      ch.si[Chunk<MAP, LAYOUT>::kUniform ? 0 : k] = scale_index<MAP>(g, c);
       if (++i == g.inner) { i = 0; if (++c == g.C) { c = 0; ++o; } }
     }
   }
@@ -154,11 +141,18 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
     if (OP != OP_SOFTEDGE) return make_float2(0.0f, 0.0f);
     return lds ? s_LH[si] : make_float2(Lth[si], Hth[si]);
   };
-  constexpr bool kUniform = Tile<MAP, LAYOUT>::kUniform;
-  const int64_t e0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kVec;
-  if (e0 < g.total) {
-    Tile<MAP, LAYOUT> t;
-    load_tile<MAP, LAYOUT>(g, x, e0, t);
+  constexpr bool kUniform = Chunk<MAP, LAYOUT>::kUniform;
+  Chunk<MAP, LAYOUT> ch[kChunks];
+  int64_t e[kChunks];
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    e[k] = (int64_t)blockIdx.x * kBlockElems + ((int64_t)k * kThreads + threadIdx.x) * 4;
+    if (e[k] < g.total) load_chunk<MAP, LAYOUT>(g, x, e[k], ch[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < kChunks; ++k) {
+    if (e[k] >= g.total) continue;
+    const Chunk<MAP, LAYOUT>& c = ch[k];
     if (OP == OP_ABSMAX) {
       unsigned* gmax = reinterpret_cast<unsigned*>(out);
       auto push = [&](int si, float m) {
@@ -170,44 +164,34 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
       if (kUniform) {
         float m = 0.0f;
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) m = fmaxf(m, finite_abs(t.v[k]));
-        push(t.si[0], m);
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, finite_abs(c.v[i]));
+        push(c.si[0], m);
       } else {
-        // running max per scale index; consecutive elements usually share it
-        int cur = t.si[0];
-        float m = 0.0f;
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-          if (k < t.n) {
-            const int si = t.si[kUniform ? 0 : k];
-            if (si != cur) { push(cur, m); cur = si; m = 0.0f; }
-            m = fmaxf(m, finite_abs(t.v[k]));
-          }
-        }
-        push(cur, m);
+        for (int i = 0; i < 4; ++i)
+          if (i < c.n) push(c.si[kUniform ? 0 : i], finite_abs(c.v[i]));
       }
     } else {
-      uint32_t packed[kVec / 4] = {0u, 0u, 0u, 0u};
+      uint32_t word = 0u;
       if (kUniform) {
-        const float2 sr = scale_of(t.si[0]);
-        const float2 lh = thresholds_of(t.si[0]);
+        const float2 sr = scale_of(c.si[0]);
+        const float2 lh = thresholds_of(c.si[0]);
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) packed[k >> 2] |= encode<OP>(t.v[k], sr, lh) << (8 * (k & 3));
+        for (int i = 0; i < 4; ++i) word |= encode<OP>(c.v[i], sr, lh) << (8 * i);
       } else {
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-          if (k < t.n) {
-            const int si = t.si[kUniform ? 0 : k];
-            packed[k >> 2] |= encode<OP>(t.v[k], scale_of(si), thresholds_of(si)) << (8 * (k & 3));
+        for (int i = 0; i < 4; ++i) {
+          if (i < c.n) {
+            const int si = c.si[kUniform ? 0 : i];
+            word |= encode<OP>(c.v[i], scale_of(si), thresholds_of(si)) << (8 * i);
           }
         }
       }
-      uint8_t* o8 = reinterpret_cast<uint8_t*>(out) + e0;
-      if (t.n == kVec) {
-        const u32x4 pk = {packed[0], packed[1], packed[2], packed[3]};
-        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(o8));
+      uint8_t* o8 = reinterpret_cast<uint8_t*>(out) + e[k];
+      if (c.n == 4) {
+        *reinterpret_cast<uint32_t*>(o8) = word;
       } else {
-        for (int k = 0; k < t.n; ++k) o8[k] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
+        for (int i = 0; i < c.n; ++i) o8[i] = (uint8_t)(word >> (8 * i));
       }
     }
   }
@@ -237,25 +221,25 @@ __global__ __launch_bounds__(kThreads) void k_softedge_decode(
   __shared__ float s_scale[256];
   for (int k = threadIdx.x; k < nscales; k += kThreads) s_scale[k] = s[k];
   __syncthreads();
-  const int64_t e0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kVec;
+  const int64_t e0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kDecVec;
   if (e0 >= total) return;
   const int64_t row = e0 / inner;
   int64_t i = e0 - row * inner, c = row % C;
-  const int n = (int)((total - e0) < kVec ? (total - e0) : kVec);
-  alignas(16) uint8_t b[kVec];
-  if (n == kVec) *reinterpret_cast<uint4*>(b) = *reinterpret_cast<const uint4*>(code + e0);
+  const int n = (int)((total - e0) < kDecVec ? (total - e0) : kDecVec);
+  alignas(16) uint8_t b[kDecVec];
+  if (n == kDecVec) *reinterpret_cast<uint4*>(b) = *reinterpret_cast<const uint4*>(code + e0);
   else for (int k = 0; k < n; ++k) b[k] = code[e0 + k];
-  alignas(16) float v[kVec];
+  alignas(16) float v[kDecVec];
 #pragma unroll
-  for (int k = 0; k < kVec; ++k) {
+  for (int k = 0; k < kDecVec; ++k) {
     if (k < n) {
       v[k] = softedge_value(b[k], s_scale[group_of[c]]);
       if (++i == inner) { i = 0; if (++c == C) c = 0; }
     }
   }
-  if (n == kVec) {
+  if (n == kDecVec) {
 #pragma unroll
-    for (int k = 0; k < kVec / 4; ++k)
+    for (int k = 0; k < kDecVec / 4; ++k)
       reinterpret_cast<float4*>(out + e0)[k] = reinterpret_cast<const float4*>(v)[k];
   } else {
     for (int k = 0; k < n; ++k) out[e0 + k] = v[k];
@@ -271,11 +255,11 @@ qssm_status check_extents(int64_t outer, int64_t C, int64_t inner) {
 
 template <int OP, int MAP>
 int choose_layout(const Geometry& g) {
-  if (g.inner % kVec == 0) return L_ROWS;
-  if (g.inner == 1 && g.C % kVec == 0) {
-    if (MAP == MAP_GROUP && !g.perm && (reinterpret_cast<uintptr_t>(g.group_of) % 16) == 0)
+  if (g.inner % 4 == 0) return L_ROWS;
+  if (g.inner == 1 && g.C % 4 == 0) {
+    if (MAP == MAP_GROUP && !g.perm && (reinterpret_cast<uintptr_t>(g.group_of) % 4) == 0)
       return L_CHANNELS;
-    if (MAP == MAP_STATE && g.N % kVec == 0 && g.gs % kVec == 0) return L_CHANNELS;
+    if (MAP == MAP_STATE && g.N % 4 == 0 && g.gs % 4 == 0) return L_CHANNELS;
   }
   return L_GENERIC;
 }
@@ -283,7 +267,7 @@ int choose_layout(const Geometry& g) {
 template <int OP, int MAP, int LAYOUT>
 void launch_elementwise(const float* x, const Geometry& g, const float* scales, const float* L,
                         const float* H, void* out, hipStream_t st) {
-  const unsigned blocks = (unsigned)cdiv(g.total, (int64_t)kThreads * kVec);
+  const unsigned blocks = (unsigned)cdiv(g.total, (int64_t)kBlockElems);
   k_elementwise<OP, MAP, LAYOUT><<<blocks, kThreads, 0, st>>>(x, g, scales, L, H, out);
 }
 
@@ -372,7 +356,7 @@ qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, 
   if (total > 0 && (!code || !out || !group_of))
     return fail(QSSM_ERR_INVALID_ARG, "null tensor pointer");
   if (total > 0)
-    k_softedge_decode<<<(unsigned)cdiv(total, (int64_t)kThreads * kVec), kThreads, 0, stream>>>(
+    k_softedge_decode<<<(unsigned)cdiv(total, (int64_t)kThreads * kDecVec), kThreads, 0, stream>>>(
         code, total, C, inner, group_of, G, s, out);
   return launch_status("softedge_decode");
 }
