@@ -118,6 +118,22 @@ __device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
   return o;
 }
 
+// Loads of one head's delta (step tid) and x codes (rows 16 (tid / 16) .. + 15, codes
+// 4 (tid % 16) .. + 3) into registers, issued one head ahead of their use in K1 and K3.
+__device__ __forceinline__ void fetch_head(const SsdParams& p, int64_t b, int64_t c, int64_t t0,
+                                              int q, int64_t h, int tid, float& dt,
+                                              uint32_t (&x)[16], float& sx) {
+  const int jb = tid / 16, p4 = tid % 16;
+  dt = (tid < q) ? p.delta[(b * p.L + t0 + tid) * p.nh + h] : 0.0f;
+  sx = valid_or_zero(p.x_scales[p.x_group_of[h * kP + (tid & (kP - 1))]]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int jj = jb * 16 + r;
+    x[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
+                    : 0u;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // K1: chunk states, S[p][n] = sum_j w_j xh_j[p] Bh_j[n], w_j = delta_j exp(cum_last - cum_j).
 // I8 = false: fp16 operands fp16(w_j * qx[j][p]) and the exact B codes, fp32 accumulate; the x and
@@ -132,6 +148,7 @@ struct K1Smem {
   int8_t rT[I8 ? kP * kRow256 : 16];                  // requantized x, [p][j] (I8)
   _Float16 xw[I8 ? 8 : kP * kXwRow];                  // weighted x, [p][j] (fp16)
   float wv[kQ];                                       // w_j (fp16 path) or w_j / w_max (I8)
+  float sxs[kP];                                      // x scale of each channel of the head
   float sh[8];
 };
 
@@ -166,11 +183,14 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
   const float sB = valid_or_zero(p.B_scales[g * kNSG + n / kGS]);
   const int kh = lane >> 5;
 
+  float pf_dt, pf_sx;
+  uint32_t pf_x[16];
+  fetch_head(p, b, c, t0, q, (int64_t)g * p.hpg, tid, pf_dt, pf_x, pf_sx);
   for (int hh = 0; hh < p.hpg; ++hh) {
     const int64_t h = (int64_t)g * p.hpg + hh;
     const float Ah = p.A[h];
     const int j = tid;
-    const float dt = (j < q) ? p.delta[(b * p.L + t0 + j) * p.nh + h] : 0.0f;
+    const float dt = pf_dt;
     const float cum = block_scan(dt * Ah, s.sh);
     if (j == q - 1) s.sh[4] = cum;
     __syncthreads();
@@ -184,19 +204,13 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
       s.wv[j] = wj;
     }
     if (tid == 0) p.dec[(b * p.nc + c) * p.nh + h] = expf(cum_last);
+    if (tid < kP) s.sxs[tid] = pf_sx;
     __syncthreads();
 
     // weighted x tile, transposed [p][j]
     {
       const int jb = tid / 16, p4 = tid % 16;
-      uint32_t raw[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jj = jb * 16 + r;
-        raw[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(
-                                p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
-                          : 0u;
-      }
+      const uint32_t (&raw)[16] = pf_x;
       if (I8) {
         uint32_t d[16];
 #pragma unroll
@@ -230,6 +244,7 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
       }
     }
     __syncthreads();
+    if (hh + 1 < p.hpg) fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x, pf_sx);
 
     // S[p][n] for p in two 32-row tiles; wave w owns state columns [32w, 32w + 32)
     float* Sout = p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
@@ -248,8 +263,8 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        const float sx0 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + prow]]);
-        const float sx1 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + 32 + prow]]);
+        const float sx0 = s.sxs[prow];
+        const float sx1 = s.sxs[32 + prow];
         Sout[prow * kN + n] = wsb * sx0 * (float)acc0[r];
         Sout[(32 + prow) * kN + n] = wsb * sx1 * (float)acc1[r];
       }
@@ -267,8 +282,8 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        const float sx0 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + prow]]);
-        const float sx1 = valid_or_zero(p.x_scales[p.x_group_of[h * kP + 32 + prow]]);
+        const float sx0 = s.sxs[prow];
+        const float sx1 = s.sxs[32 + prow];
         Sout[prow * kN + n] = sB * sx0 * acc0[r];
         Sout[(32 + prow) * kN + n] = sB * sx1 * acc1[r];
       }
@@ -386,20 +401,6 @@ __device__ __forceinline__ v8h x_operand(const K3Smem& s, int J, int mm, int pt,
   return v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Loads of one head's delta and x codes into registers (see the head loop of k_ssd_output).
-__device__ __forceinline__ void k3_fetch_head(const SsdParams& p, int64_t b, int64_t c, int64_t t0,
-                                              int q, int64_t h, int tid, float& dt,
-                                              uint32_t (&x)[16]) {
-  const int jb = tid / 16, p4 = tid % 16;
-  dt = (tid < q) ? p.delta[(b * p.L + t0 + tid) * p.nh + h] : 0.0f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int jj = jb * 16 + r;
-    x[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
-                    : 0u;
-  }
-}
-
 __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   K3Smem& s = *reinterpret_cast<K3Smem*>(smem_raw);
@@ -445,9 +446,9 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
   // to LDS after the barrier that ends that head. (The fp16 entering state is read at the head's
   // start: registers for it as well would exceed the kernel's budget.)
   const int jb = tid / 16, p4 = tid % 16;
-  float pf_dt;
+  float pf_dt, pf_sx;
   uint32_t pf_x[16];
-  k3_fetch_head(p, b, c, t0, q, (int64_t)g * p.hpg, tid, pf_dt, pf_x);
+  fetch_head(p, b, c, t0, q, (int64_t)g * p.hpg, tid, pf_dt, pf_x, pf_sx);
   for (int hh = 0; hh < p.hpg; ++hh) {
     const int64_t h = (int64_t)g * p.hpg + hh;
     // decay terms of head h
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
     s.cum[j] = cum;
     s.dtv[j] = dt;
     s.ecum[j] = expf(cum);
-    if (tid < kP) s.sxs[tid] = valid_or_zero(p.x_scales[p.x_group_of[h * kP + tid]]);
+    if (tid < kP) s.sxs[tid] = pf_sx;
     // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves)
     {
       const uint4* hsrc = reinterpret_cast<const uint4*>(p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN));
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
       }
     }
     __syncthreads();
-    if (hh + 1 < p.hpg) k3_fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x);
+    if (hh + 1 < p.hpg) fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x, pf_sx);
 
     // Opaque copies of the lane and wave ids: the tile addresses below do not depend on the head,
     // and hoisting all of them out of the head loop would keep them live across it (spills).
