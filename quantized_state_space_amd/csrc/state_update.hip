@@ -7,8 +7,8 @@
 // The state (P x N per (b, h), fp32 or fp16) is the only large operand: the kernel is one
 // streaming read-modify-write pass over it. A workgroup owns one (b, h) state tile: it quantizes
 // and dequantizes the P x values and the N B/C values of its group into LDS once, then each thread
-// updates 4 consecutive states per 16-byte (fp32) / 8-byte (fp16) access with fully coalesced
-// wave accesses, and the readout sum over n is a shuffle reduction among the lanes sharing a row.
+// updates 4 (fp32) or 8 (fp16) consecutive states per 16-byte access with fully coalesced wave
+// accesses, and the readout sum over n is a shuffle reduction among the lanes sharing a row.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -39,8 +39,11 @@ struct UpdParams {
   int8_t* Cq_out;
 };
 
-template <int F16, int R>  // R = N / 4 lanes share one state row
+// CH consecutive states per thread access: 4 for fp32 (16 bytes), 8 for fp16 (16 bytes).
+// R = N / CH lanes share one state row.
+template <int F16, int R>
 __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
+  constexpr int CH = F16 ? 8 : 4;
   extern __shared__ float smem[];
   float* xs = smem;          // [P]
   float* bs = xs + p.P;      // [N]
@@ -76,46 +79,54 @@ __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
   const float dt = p.delta[bh];
   const float dA = expf(dt * p.A[h]);
   const float Dh = p.Dskip ? p.Dskip[h] : 0.0f;
-  const int64_t n4 = p.N / 4;
-  const int64_t total4 = p.P * n4;  // 4-element chunks of the tile
+  const int64_t nch = p.N / CH;
+  const int64_t total = p.P * nch;  // CH-element chunks of the tile
   const int lane = threadIdx.x & 63;
 
-  for (int64_t base = 0; base < total4; base += kThreads) {
+  for (int64_t base = 0; base < total; base += kThreads) {
     const int64_t f = base + threadIdx.x;
-    const bool on = f < total4;
-    const int64_t row = on ? f / n4 : 0;
-    const int64_t n0 = on ? (f - row * n4) * 4 : 0;
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
-    if (on) {
-      if (F16) {
-        const uint2 raw = reinterpret_cast<const uint2*>(p.state)[bh * total4 + f];
-        const __half2 lo = *reinterpret_cast<const __half2*>(&raw.x);
-        const __half2 hi = *reinterpret_cast<const __half2*>(&raw.y);
-        s[0] = __low2float(lo); s[1] = __high2float(lo);
-        s[2] = __low2float(hi); s[3] = __high2float(hi);
-      } else {
-        const float4 v = reinterpret_cast<const float4*>(p.state)[bh * total4 + f];
-        s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
+    const bool on = f < total;
+    const int64_t row = on ? f / nch : 0;
+    const int64_t n0 = on ? (f - row * nch) * CH : 0;
+    float s[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) s[k] = 0.0f;
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (on) raw = reinterpret_cast<const uint4*>(p.state)[bh * total + f];
+    if (F16) {
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const __half2 v = *reinterpret_cast<const __half2*>(&w[k]);
+        s[2 * k] = __low2float(v);
+        s[2 * k + 1] = __high2float(v);
       }
+    } else {
+      s[0] = __uint_as_float(raw.x); s[1] = __uint_as_float(raw.y);
+      s[2] = __uint_as_float(raw.z); s[3] = __uint_as_float(raw.w);
     }
     const float dtx = dt * xs[row];
     float yp = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < CH; ++k) {
       s[k] = fmaf(dA, s[k], dtx * bs[n0 + k]);
       yp = fmaf(cs[n0 + k], s[k], yp);
     }
     if (on) {
+      uint4 out;
       if (F16) {
-        __half2 lo = __floats2half2_rn(s[0], s[1]);
-        __half2 hi = __floats2half2_rn(s[2], s[3]);
-        uint2 raw;
-        raw.x = *reinterpret_cast<const unsigned*>(&lo);
-        raw.y = *reinterpret_cast<const unsigned*>(&hi);
-        reinterpret_cast<uint2*>(p.state)[bh * total4 + f] = raw;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const __half2 v = __floats2half2_rn(s[2 * k], s[2 * k + 1]);
+          w[k] = *reinterpret_cast<const uint32_t*>(&v);
+        }
+        out = make_uint4(w[0], w[1], w[2], w[3]);
       } else {
-        reinterpret_cast<float4*>(p.state)[bh * total4 + f] = make_float4(s[0], s[1], s[2], s[3]);
+        out = make_uint4(__float_as_uint(s[0]), __float_as_uint(s[1]), __float_as_uint(s[2]),
+                         __float_as_uint(s[3]));
       }
+      reinterpret_cast<uint4*>(p.state)[bh * total + f] = out;
     }
     // rows occupy R consecutive lanes (R divides 64 and kThreads): reduce within them
 #pragma unroll
@@ -128,8 +139,11 @@ template <int R>
 qssm_status launch_r(const UpdParams& p, int f16, hipStream_t st) {
   const size_t smem = (size_t)(p.P + 2 * p.N) * sizeof(float);
   const unsigned grid = (unsigned)(p.B * p.nh);
-  if (f16) k_state_update<1, R><<<grid, kThreads, smem, st>>>(p);
-  else k_state_update<0, R><<<grid, kThreads, smem, st>>>(p);
+  if (f16) {
+    if constexpr (R % 2 == 0) k_state_update<1, R / 2><<<grid, kThreads, smem, st>>>(p);
+  } else {
+    k_state_update<0, R><<<grid, kThreads, smem, st>>>(p);
+  }
   return launch_status("state_update");
 }
 
@@ -150,6 +164,8 @@ extern "C" qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t 
   const int64_t R = N / 4;
   if (N % 4 != 0 || !(R == 1 || R == 2 || R == 4 || R == 8 || R == 16 || R == 32 || R == 64))
     return fail(QSSM_ERR_UNSUPPORTED, "dstate must be 4 * 2^k with 4 <= dstate <= 256");
+  if (a->state_dtype == QSSM_F16 && N < 8)
+    return fail(QSSM_ERR_UNSUPPORTED, "an fp16 state needs dstate >= 8");
   if ((P + 2 * N) * 4 > 64 * 1024) return fail(QSSM_ERR_UNSUPPORTED, "headdim too large");
   if (B == 0) return QSSM_OK;
   if (!a->x || !a->x_group_of || !a->x_scales || !a->B || !a->C || !a->B_scales || !a->C_scales ||

@@ -102,6 +102,8 @@ def test_other_entry_point_argument_errors():
     assert lib.qssm_state_update(ctypes.byref(u), None) == qs.QSSM_ERR_INVALID_ARG  # ngroups
     u.ngroups = 2
     assert lib.qssm_state_update(ctypes.byref(u), None) == qs.QSSM_ERR_UNSUPPORTED  # dstate 12
+    u.dstate, u.bc_group_size, u.state_dtype = 4, 4, qs.QSSM_F16
+    assert lib.qssm_state_update(ctypes.byref(u), None) == qs.QSSM_ERR_UNSUPPORTED  # fp16, N < 8
     sd = qs.SsdArgs(batch=1, seqlen=8, nheads=2, headdim=64, dstate=128, ngroups=1, chunk=256,
                     x_groups=1, bc_group_size=16, y_dtype=0)
     assert lib.qssm_ssd_chunk_int8(ctypes.byref(sd), None, 0, None) != qs.QSSM_OK
