@@ -217,6 +217,13 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   load_block(0, dl, xq);
   sload(0, bcur);
   int buf = 0;
+  // exp(delta A) of the next two steps, by step parity
+  float dAr[2][NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    dAr[0][k] = __builtin_amdgcn_exp2f(dl[0] * a2[k]);
+    dAr[1][k] = __builtin_amdgcn_exp2f(dl[1] * a2[k]);
+  }
   for (int64_t tb = 0; tb < L; tb += kT) {
     // (masking the codes of the current block here, not at load time, keeps the next block's
     // loads in flight during this block's arithmetic)
@@ -242,14 +249,21 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
         const int t = bt + s2;
         const float dt = dl[t];
         const float u = dt * xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))) * su;
+        float dA[NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) dA[k] = dAr[t % 2][k];
+        // exp of the step two ahead (this block's, or the next block's first two), so that its
+        // latency is covered by two steps of arithmetic
+        const float dt2 = (t + 2 < kT) ? dl[t + 2] : dn[t + 2 - kT];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) dAr[t % 2][k] = __builtin_amdgcn_exp2f(dt2 * a2[k]);
         float yp;
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-          const float dA = __builtin_amdgcn_exp2f(dt * a2[k]);
           // fma with a zero addend keeps the fp16 operand in a mixed-precision fma
           const float in = CODE16 ? fmaf(u, opB(bcur[s2], k), 0.0f) : u * opB(bcur[s2], k);
-          h[k] = fmaf(dA, h[k], in);
-          yp = (k == 0) ? opC(bcur[s2], 0) * h[0] : fmaf(opC(bcur[s2], k), h[k], yp);
+          h[k] = fmaf(dA[k], h[k], in);
+          yp = fmaf(opC(bcur[s2], k), h[k], k == 0 ? 0.0f : yp);
         }
         ybuf[buf][w][t][lane] = yp;
       }
