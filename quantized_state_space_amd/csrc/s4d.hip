@@ -6,11 +6,13 @@
 //   Abar = exp(dt Ah), Bbar = (Abar - 1)/Ah Bh (zero-order hold), h_t = Abar h_{t-1} + Bbar u_t,
 //   y_t = Re(sum_n Ch h_t) + D u_t.
 //
-// Mapping: one wave per (batch, channel) chain set, lane = state n (N <= 64 * NPL). The input u_t
-// is the same for every lane of the wave, so it is read with scalar loads. Each lane keeps its
-// complex state, Abar, Bbar, Ch in registers (computed once in the prologue, with expm1 for
-// Abar - 1 to keep small dt accurate). The readout sum over states is a transpose through LDS:
-// lane n writes its term for 64 steps, then lane t sums row t.
+// Mapping: one wave per (batch, channel) chain set, lane = state n (N <= 64 * NPL). The input code
+// of each step is the same for every lane: per block of 64 steps, lane t converts code t once and
+// the step loop reads it from LDS. Each lane keeps its complex state, Abar, Bbar, C in registers
+// (computed once in the prologue, with expm1 for Abar - 1 to keep small dt accurate); the input
+// scale is folded into Bbar. With an fp32 state the chain runs on g = h / Bbar' (one complex
+// multiply-add per step, no input product), converted back for h_last. The readout sum over states
+// is a transpose through LDS: lane n writes its term for 64 steps, then lane t sums row t.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -43,9 +45,53 @@ __device__ __forceinline__ float q16(float v, float s, float inv) {
   return s * fminf(fmaxf(rintf(v * inv), -32768.0f), 32767.0f);
 }
 
+// Runs the steps [tb, tb + nt) of one readout block. G = true: the lane's chain is kept as
+// g = h / Bbar' (Bbar' = Bbar times the input scale), so an update is g = Abar g + q_t (two fmas
+// and a multiply-add for the complex product, no input multiply) and the readout uses
+// C' = C Bbar'. G = false: the state h itself (needed for the int16 grid). q_t, the raw input
+// code of step t, is read from LDS (the same address for every lane).
+template <int NPL, int I16, bool G, bool FULL>
+__device__ __forceinline__ void s4d_block(int nt, const float* __restrict__ ub, float (&ar)[NPL],
+                                          float (&ai)[NPL], float (&br)[NPL], float (&bi)[NPL],
+                                          float (&cr)[NPL], float (&ci)[NPL], float (&hr)[NPL],
+                                          float (&hi)[NPL], float ss, float sinv,
+                                          float (*red)[kBlk + 1], int lane) {
+  auto step = [&](int t) {
+    const float q = ub[t];
+    float yp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      float nr, ni;
+      if (G) {
+        nr = fmaf(ar[k], hr[k], fmaf(-ai[k], hi[k], q));
+        ni = fmaf(ar[k], hi[k], ai[k] * hr[k]);
+      } else {
+        nr = fmaf(ar[k], hr[k], fmaf(-ai[k], hi[k], br[k] * q));
+        ni = fmaf(ar[k], hi[k], fmaf(ai[k], hr[k], bi[k] * q));
+      }
+      if (I16) {
+        hr[k] = q16(nr, ss, sinv);
+        hi[k] = q16(ni, ss, sinv);
+      } else {
+        hr[k] = nr;
+        hi[k] = ni;
+      }
+      yp = fmaf(cr[k], hr[k], fmaf(-ci[k], hi[k], yp));
+    }
+    red[t][lane] = yp;
+  };
+  if (FULL) {
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) step(t);
+  } else {
+    for (int t = 0; t < nt; ++t) step(t);
+  }
+}
+
 template <int NPL, int I16>
 __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
   __shared__ float red[4][kBlk][kBlk + 1];
+  __shared__ __align__(16) float ubuf[4][kBlk];
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int64_t chain = (int64_t)blockIdx.x * 4 + w;
@@ -54,10 +100,25 @@ __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
   const int64_t b = cc / p.H, hh = cc % p.H;
   const int64_t L = p.L;
 
+  // input scale: lifted scalar input (u = su sw qw_h q_t), or per-channel input (u = su_h q_t)
+  const bool lifted = p.wq != nullptr;
+  float us;
+  const int8_t* urow;
+  if (lifted) {
+    us = p.u_scale[0] * p.w_scale[0];
+    us = (scale_ok(p.u_scale[0]) && scale_ok(p.w_scale[0])) ? us * (float)p.wq[hh] : 0.0f;
+    urow = p.uq + b * L;
+  } else {
+    us = scale_ok(p.u_scale[hh]) ? p.u_scale[hh] : 0.0f;
+    urow = p.uq + (b * p.H + hh) * L;
+  }
+  const float Dd = p.Dskip ? p.Dskip[hh] : 0.0f;
+
   float ar[NPL], ai[NPL], br[NPL], bi[NPL], cr[NPL], ci[NPL], hr[NPL], hi[NPL];
   const float dt = expf(p.log_dt[hh]);
   const float ss = I16 ? p.state_scale[hh] : 1.0f;
   const float sinv = I16 ? 1.0f / ss : 1.0f;
+  bool zero_b = false;  // some state of this lane has Bbar' = 0
 #pragma unroll
   for (int k = 0; k < NPL; ++k) {
     const int64_t n = lane + 64 * k;
@@ -90,6 +151,10 @@ __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
       br[k] = qr * Br - qi * Bi;
       bi[k] = qr * Bi + qi * Br;
     }
+    // the input scale moves into Bbar: the loop feeds the raw code
+    br[k] *= us;
+    bi[k] *= us;
+    if (on && br[k] == 0.0f && bi[k] == 0.0f) zero_b = true;
     hr[k] = 0.0f;
     hi[k] = 0.0f;
     if (p.h0 && on) {
@@ -105,49 +170,44 @@ __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
       }
     }
   }
-
-  // input scale: lifted scalar input, or per-channel input
-  const bool lifted = p.wq != nullptr;
-  float us;
-  const int8_t* urow;
-  if (lifted) {
-    us = p.u_scale[0] * p.w_scale[0];
-    us = (scale_ok(p.u_scale[0]) && scale_ok(p.w_scale[0])) ? us * (float)p.wq[hh] : 0.0f;
-    urow = p.uq + b * L;
-  } else {
-    us = scale_ok(p.u_scale[hh]) ? p.u_scale[hh] : 0.0f;
-    urow = p.uq + (b * p.H + hh) * L;
+  // fp32 state: run g = h / Bbar' unless a state of the wave has Bbar' = 0 (a uniform choice)
+  const bool gform = !I16 && !__builtin_amdgcn_ballot_w64(zero_b);
+  if (gform) {
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const float m = br[k] * br[k] + bi[k] * bi[k];
+      const bool on = lane + 64 * k < p.N;
+      // g0 = h0 / Bbar' ; C' = C Bbar'
+      const float gr = on ? (hr[k] * br[k] + hi[k] * bi[k]) / m : 0.0f;
+      const float gi = on ? (hi[k] * br[k] - hr[k] * bi[k]) / m : 0.0f;
+      const float c2r = cr[k] * br[k] - ci[k] * bi[k];
+      const float c2i = cr[k] * bi[k] + ci[k] * br[k];
+      hr[k] = gr;
+      hi[k] = gi;
+      cr[k] = c2r;
+      ci[k] = c2i;
+    }
   }
-  const float Dd = p.Dskip ? p.Dskip[hh] : 0.0f;
 
   for (int64_t tb = 0; tb < L; tb += kBlk) {
     const int nt = (int)((L - tb) < kBlk ? (L - tb) : kBlk);
-    // lane t holds the input of step tb + t; the loop broadcasts it with readlane (an SGPR)
-    const float u_lane = (lane < nt) ? us * (float)urow[tb + lane] : 0.0f;
-    for (int t = 0; t < nt; ++t) {
-      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u_lane), t));
-      float yp = 0.0f;
-#pragma unroll
-      for (int k = 0; k < NPL; ++k) {
-        const float nr = fmaf(ar[k], hr[k], fmaf(-ai[k], hi[k], br[k] * u));
-        const float ni = fmaf(ar[k], hi[k], fmaf(ai[k], hr[k], bi[k] * u));
-        if (I16) {
-          hr[k] = q16(nr, ss, sinv);
-          hi[k] = q16(ni, ss, sinv);
-        } else {
-          hr[k] = nr;
-          hi[k] = ni;
-        }
-        yp = fmaf(cr[k], hr[k], fmaf(-ci[k], hi[k], yp));
-      }
-      red[w][t][lane] = yp;
+    // lane t converts the code of step tb + t once; the loop reads it back from LDS
+    const float q_lane = (lane < nt) ? (float)urow[tb + lane] : 0.0f;
+    ubuf[w][lane] = q_lane;
+    __syncthreads();
+    if (gform) {
+      if (nt == kBlk) s4d_block<NPL, 0, true, true>(nt, ubuf[w], ar, ai, br, bi, cr, ci, hr, hi, ss, sinv, red[w], lane);
+      else s4d_block<NPL, 0, true, false>(nt, ubuf[w], ar, ai, br, bi, cr, ci, hr, hi, ss, sinv, red[w], lane);
+    } else {
+      if (nt == kBlk) s4d_block<NPL, I16, false, true>(nt, ubuf[w], ar, ai, br, bi, cr, ci, hr, hi, ss, sinv, red[w], lane);
+      else s4d_block<NPL, I16, false, false>(nt, ubuf[w], ar, ai, br, bi, cr, ci, hr, hi, ss, sinv, red[w], lane);
     }
     __syncthreads();
     if (lane < nt) {
-      float s = 0.0f;
+      float sum = 0.0f;
 #pragma unroll 16
-      for (int j = 0; j < 64; ++j) s += red[w][lane][j];
-      if (active) p.y[(b * p.H + hh) * L + tb + lane] = fmaf(Dd, u_lane, s);
+      for (int j = 0; j < 64; ++j) sum += red[w][lane][j];
+      if (active) p.y[(b * p.H + hh) * L + tb + lane] = fmaf(Dd * us, q_lane, sum);
     }
     __syncthreads();
   }
@@ -157,12 +217,17 @@ __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
     for (int k = 0; k < NPL; ++k) {
       const int64_t n = lane + 64 * k;
       if (n < p.N) {
+        float fr = hr[k], fi = hi[k];
+        if (gform) {  // h = Bbar' g
+          fr = br[k] * hr[k] - bi[k] * hi[k];
+          fi = br[k] * hi[k] + bi[k] * hr[k];
+        }
         const int64_t si = (b * p.H + hh) * p.N + n;
         if (I16) {
           reinterpret_cast<short2*>(p.h_last)[si] =
-              make_short2((short)rintf(hr[k] * sinv), (short)rintf(hi[k] * sinv));
+              make_short2((short)rintf(fr * sinv), (short)rintf(fi * sinv));
         } else {
-          reinterpret_cast<float2*>(p.h_last)[si] = make_float2(hr[k], hi[k]);
+          reinterpret_cast<float2*>(p.h_last)[si] = make_float2(fr, fi);
         }
       }
     }
