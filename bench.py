@@ -310,10 +310,10 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (163175667, 113849088, "fe5bcf10865f2b40"),
-    "c2": (277656, 7472288, "125950742ed91549"),
-    "c4": (1284972839, 1090787952, "ff13912165beae6a"),
-    "c5": (1100189192, 1082564232, "045f735b9b546c01"),
+    "c3": (139083153, 110238048, "22668164ae914305"),
+    "c2": (369686, 7472208, "1af91dec259fc264"),
+    "c4": (1038708454, 956576264, "5a45487fe13d938a"),
+    "c5": (1100194426, 1082565320, "5c4dad04e617f92c"),
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"], "c2": ["s4d.hip"],
