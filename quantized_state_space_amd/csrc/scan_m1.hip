@@ -25,7 +25,7 @@ using namespace qssm;
 
 namespace {
 
-constexpr int kT = 32;          // time steps per block
+constexpr int kT = 16;          // time steps per block
 constexpr int kPadRows = 64;    // zero rows after L in every staged plane (>= kT + largest batch)
 constexpr int kLanes = 64;      // channels per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
