@@ -19,8 +19,9 @@
 //   K2 k_ssd_state_pass   per (b, h) state element: sequential over chunks, replaces each chunk
 //                         state by the state entering that chunk.
 //   K3 k_ssd_output       one workgroup per (b, chunk, B/C group): G^T is built once with int8 MFMA
-//                         and kept in registers (4 waves x 9 causal 32x32 tiles); per head the
-//                         inter-chunk product, the intra-chunk product and the D term.
+//                         and kept in registers (8 waves, one query block of causal 32x32 tiles
+//                         each, two waves per SIMD); per head the inter-chunk product, the
+//                         intra-chunk product and the D term.
 // MFMA lane layouts (verified on gfx950): operand lane l holds row/column l%32 and a run of
 // consecutive k at offset (K/2)*(l/32); the 32x32 accumulator register r of lane l is element
 // (8*(r/4) + 4*(l/32) + r%4, l%32).
@@ -126,11 +127,15 @@ __device__ __forceinline__ void fetch_head(const SsdParams& p, int64_t b, int64_
   const int jb = tid / 16, p4 = tid % 16;
   dt = (tid < q) ? p.delta[(b * p.L + t0 + tid) * p.nh + h] : 0.0f;
   sx = valid_or_zero(p.x_scales[p.x_group_of[h * kP + (tid & (kP - 1))]]);
+  // rows advance by one time step; the opaque stride keeps the 16 row addresses from being
+  // precomputed once for all heads (they would stay live across the caller's head loop)
+  int64_t step = p.nh * kP;
+  __asm__ volatile("" : "+s"(step));
+  const int8_t* row = p.xq + ((b * p.L + t0 + jb * 16) * p.nh + h) * kP + p4 * 4;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int jj = jb * 16 + r;
-    x[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(p.xq + ((b * p.L + t0 + jj) * p.nh + h) * kP + p4 * 4)
-                    : 0u;
+    x[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(row + r * step) : 0u;
   }
 }
 
@@ -334,14 +339,6 @@ struct K3Smem {
 };
 
 
-// Wave w (of 4) owns the query blocks w and 7 - w: 9 causal tiles (I, J <= I) in all, enumerated
-// as t = 0..8 -> (I, J) = (w, t) for t <= w, else (7 - w, t - w - 1). The tile index t is static
-// (registers), I and J are wave-uniform values (uniform branches).
-__device__ __forceinline__ void tile_of(int w, int t, int& I, int& J, int& ii) {
-  if (t <= w) { I = w; J = t; ii = 0; }
-  else { I = 7 - w; J = t - w - 1; ii = 1; }
-}
-
 // Compiler-only fence: keeps one tile's work from being interleaved with the next tile's.
 __device__ __forceinline__ void tile_fence() { __asm__ volatile("" ::: "memory"); }
 
@@ -362,10 +359,31 @@ __device__ __forceinline__ void build_g_tile(v16f& G, const K3Smem& s, const flo
   }
 }
 
+// G tile kept as fp16 (accumulator order): the M tile below is rounded to fp16 anyway.
+struct GTile {
+  v8h lo, hi;
+};
+
+__device__ __forceinline__ GTile pack_g(const v16f& G) {
+  GTile t;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    t.lo[e] = (_Float16)G[e];
+    t.hi[e] = (_Float16)G[8 + e];
+  }
+  return t;
+}
+
 // M tile = G o exp(cum_i - cum_j) [j <= i] o delta_j as two fp16 A operands (k-slots follow the
 // accumulator rows of G, see the B operand gather below)
-__device__ __forceinline__ void m_tile(const v16f& G, const K3Smem& s, int I, int J, int lane,
+__device__ __forceinline__ void m_tile(const GTile& Gt, const K3Smem& s, int I, int J, int lane,
                                        v8h& a0, v8h& a1) {
+  float G[16];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    G[e] = (float)Gt.lo[e];
+    G[8 + e] = (float)Gt.hi[e];
+  }
   const int i = I * 32 + (lane & 31);  // this lane's query row
   const float ci = s.cum[i];
   float m[16];
@@ -401,20 +419,38 @@ __device__ __forceinline__ v8h x_operand(const K3Smem& s, int J, int mm, int pt,
   return v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
+// Inclusive prefix sum of 256 values held by threads 0..255 of a 512-thread block (waves 4..7
+// take part in the barriers; their result is meaningless).
+__device__ __forceinline__ float block_scan_256(float v, float* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63 && w < 4) sh[w] = v;
+  __syncthreads();
+  float pre = 0.0f;
+  for (int k = 0; k < w && k < 4; ++k) pre += sh[k];
+  __syncthreads();
+  return v + pre;
+}
+
+// Eight waves; wave v owns query block I = v (v < 4) or 11 - v (v >= 4), so that the two waves
+// on one SIMD (v and v + 4) hold blocks s and 7 - s: 9 causal tiles per SIMD. A wave keeps the
+// G tiles (I, J <= I) of its block in registers and produces all 64 output columns of it.
+__global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   K3Smem& s = *reinterpret_cast<K3Smem*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = uniform(tid >> 6);
+  const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
   const int64_t b = blockIdx.y / p.Gbc;
   const int g = (int)(blockIdx.y % p.Gbc);
   const int64_t t0 = c * kQ;
   const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
-  const int kofs = 8 * (lane >> 5);
 
   // B and C chunk rows of group g (zero past the sequence), 8-byte LDS stores
-  {
+  if (tid < kQ) {
     const int j = tid;
     const int64_t* bsrc = reinterpret_cast<const int64_t*>(p.Bq + ((b * p.L + t0 + j) * p.Gbc + g) * kN);
     const int64_t* csrc = reinterpret_cast<const int64_t*>(p.Cq + ((b * p.L + t0 + j) * p.Gbc + g) * kN);
@@ -430,116 +466,117 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
     sBC[sg] = valid_or_zero(p.B_scales[g * kNSG + sg]) * valid_or_zero(p.C_scales[g * kNSG + sg]);
   __syncthreads();
 
-  v16f G[9];
+  GTile G[8];
+  {
+    const int lane = tid & 63;
+    const int v = uniform(tid >> 6);
+    const int I = v < 4 ? v : 11 - v;
 #pragma unroll
-  for (int t = 0; t < 9; ++t) {
-    int I, J, ii;
-    tile_of(w, t, I, J, ii);
-    build_g_tile(G[t], s, sBC, I, J, lane);
-    tile_fence();
+    for (int J = 0; J < 8; ++J) {
+      if (J <= I) {
+        v16f Gf;
+        build_g_tile(Gf, s, sBC, I, J, lane);
+        G[J] = pack_g(Gf);
+      }
+      tile_fence();
+    }
   }
 
   const int rs = (int)(p.nh * kP);  // row stride of y in elements
   const bool full = q == kQ;
-  // Per-head inputs are fetched one head ahead into registers (delta of step tid, 16 rows x 4
-  // x codes) so that their latency hides behind the previous head's arithmetic; they are written
-  // to LDS after the barrier that ends that head. (The fp16 entering state is read at the head's
-  // start: registers for it as well would exceed the kernel's budget.)
-  const int jb = tid / 16, p4 = tid % 16;
-  float pf_dt, pf_sx;
-  uint32_t pf_x[16];
-  fetch_head(p, b, c, t0, q, (int64_t)g * p.hpg, tid, pf_dt, pf_x, pf_sx);
+  // Per-head inputs are loaded at the head's start by threads 0..255 (delta of step tid, 16 rows
+  // x 4 x codes, the head's x scales, and the fp16 entering state by all threads); with two
+  // waves per SIMD the other wave hides part of their latency.
+  const int jb = (tid & 255) / 16, p4 = tid % 16;
   for (int hh = 0; hh < p.hpg; ++hh) {
     const int64_t h = (int64_t)g * p.hpg + hh;
+    float pf_dt = 0.0f, pf_sx = 0.0f;
+    uint32_t pf_x[16];
+    if (tid < kQ) fetch_head(p, b, c, t0, q, h, tid, pf_dt, pf_x, pf_sx);
     // decay terms of head h
-    const int j = tid;
+    const int j = tid & 255;
     const float dt = pf_dt;
-    const float cum = block_scan(dt * p.A[h], s.sh);
-    s.cum[j] = cum;
-    s.dtv[j] = dt;
-    s.ecum[j] = expf(cum);
+    const float cum = block_scan_256(dt * p.A[h], s.sh);
+    if (tid < kQ) {
+      s.cum[j] = cum;
+      s.dtv[j] = dt;
+      s.ecum[j] = expf(cum);
+    }
     if (tid < kP) s.sxs[tid] = pf_sx;
     // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves)
     {
       const uint4* hsrc = reinterpret_cast<const uint4*>(p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN));
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int u = tid + 256 * k;
+      for (int k = 0; k < 2; ++k) {
+        const int u = tid + 512 * k;
         *reinterpret_cast<uint4*>(s.Hs + (u / 16) * kHsRow + (u % 16) * 8) = hsrc[u];
       }
     }
     __syncthreads();
-    s.cjv[j] = expf(s.cum[j | 31] - cum) * dt;
-    // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale)
+    if (tid < kQ) {
+      s.cjv[j] = expf(s.cum[j | 31] - cum) * dt;
+      // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pc = p4 * 4 + e;
-      const bool on = s.sxs[pc] > 0.0f;
-      _Float16* dst = s.xT + pc * kXtRow + jb * 16;
+      for (int e = 0; e < 4; ++e) {
+        const int pc = p4 * 4 + e;
+        const bool on = s.sxs[pc] > 0.0f;
+        _Float16* dst = s.xT + pc * kXtRow + jb * 16;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        v4h v;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          v4h vv;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          v[k] = on ? (_Float16)(float)(int8_t)byte_of(pf_x[4 * r4 + k], e) : (_Float16)0.0f;
-        *reinterpret_cast<v4h*>(dst + 4 * r4) = v;
+          for (int k = 0; k < 4; ++k)
+            vv[k] = on ? (_Float16)(float)(int8_t)byte_of(pf_x[4 * r4 + k], e) : (_Float16)0.0f;
+          *reinterpret_cast<v4h*>(dst + 4 * r4) = vv;
+        }
       }
     }
     __syncthreads();
-    if (hh + 1 < p.hpg) fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x, pf_sx);
 
     // Opaque copies of the lane and wave ids: the tile addresses below do not depend on the head,
     // and hoisting all of them out of the head loop would keep them live across it (spills).
     int lane = tid & 63;
     __asm__ volatile("" : "+v"(lane));
-    int w = uniform(tid >> 6);
-    __asm__ volatile("" : "+s"(w));
+    int v = uniform(tid >> 6);
+    __asm__ volatile("" : "+s"(v));
+    const int I = v < 4 ? v : 11 - v;
     const int kofs = 8 * (lane >> 5);
-    v16f Y[2][2] = {};
+    v16f Y[2] = {};
     // Y_inter = exp(cum_i) * qC[i, :] . Hs[:, p]
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int I = ii ? 7 - w : w;
-#pragma unroll
-      for (int ks = 0; ks < kN / 16; ++ks) {
-        const int64_t cv = *reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 + ks * 16 + kofs);
-        const v8h a = i8x8_to_h(cv);
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const v8h bv = *reinterpret_cast<const v8h*>(s.Hs + (pt * 32 + (lane & 31)) * kHsRow + ks * 16 + kofs);
-          Y[ii][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bv, Y[ii][pt], 0, 0, 0);
-        }
-      }
-      // row scale exp(cum_i), column scale 1 / sx[p] (the intra part accumulates raw x codes)
+    for (int ks = 0; ks < kN / 16; ++ks) {
+      const int64_t cv = *reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 + ks * 16 + kofs);
+      const v8h a = i8x8_to_h(cv);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        const float sx = s.sxs[pt * 32 + (lane & 31)];
-        const float inv = (sx > 0.0f) ? 1.0f / sx : 1.0f;
+        const v8h bv = *reinterpret_cast<const v8h*>(s.Hs + (pt * 32 + (lane & 31)) * kHsRow + ks * 16 + kofs);
+        Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bv, Y[pt], 0, 0, 0);
+      }
+    }
+    // row scale exp(cum_i), column scale 1 / sx[p] (the intra part accumulates raw x codes)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-          Y[ii][pt][r] *= s.ecum[i] * inv;
-        }
+    for (int pt = 0; pt < 2; ++pt) {
+      const float sx = s.sxs[pt * 32 + (lane & 31)];
+      const float inv = (sx > 0.0f) ? 1.0f / sx : 1.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+        Y[pt][r] *= s.ecum[i] * inv;
       }
     }
     // Y_intra on top, tile by tile
 #pragma unroll
-    for (int t = 0; t < 9; ++t) {
+    for (int J = 0; J < 8; ++J) {
       tile_fence();
-      int I, J, ii;
-      tile_of(w, t, I, J, ii);
-      v8h a0, a1;
-      m_tile(G[t], s, I, J, lane, a0, a1);
+      if (J <= I) {
+        v8h a0, a1;
+        m_tile(G[J], s, I, J, lane, a0, a1);
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const v8h b0 = x_operand(s, J, 0, pt, lane);
-        const v8h b1 = x_operand(s, J, 1, pt, lane);
-        if (ii == 0) {
-          Y[0][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[0][pt], 0, 0, 0);
-          Y[0][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[0][pt], 0, 0, 0);
-        } else {
-          Y[1][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[1][pt], 0, 0, 0);
-          Y[1][pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[1][pt], 0, 0, 0);
+        for (int pt = 0; pt < 2; ++pt) {
+          const v8h b0 = x_operand(s, J, 0, pt, lane);
+          const v8h b1 = x_operand(s, J, 1, pt, lane);
+          Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[pt], 0, 0, 0);
+          Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[pt], 0, 0, 0);
         }
       }
     }
@@ -548,48 +585,44 @@ __global__ __launch_bounds__(256) void k_ssd_output(SsdParams p) {
     const float Dh = p.Dskip ? p.Dskip[h] : 0.0f;
     const int64_t base = ((b * p.L + t0) * p.nh + h) * kP;  // y[b, t0, h, 0]
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int I = ii ? 7 - w : w;
+    for (int pt = 0; pt < 2; ++pt) {
+      const int pc = pt * 32 + (lane & 31);
+      const float sx = s.sxs[pc];
+      const float mult = (sx > 0.0f) ? sx : 1.0f;
+      float yv[16];
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const int pc = pt * 32 + (lane & 31);
-        const float sx = s.sxs[pc];
-        const float mult = (sx > 0.0f) ? sx : 1.0f;
-        float yv[16];
+      for (int r = 0; r < 16; ++r) {
+        const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+        yv[r] = fmaf(Dh, sx * (float)s.xT[pc * kXtRow + i], mult * Y[pt][r]);
+      }
+      if (p.yf16) {
+        __half* yb = reinterpret_cast<__half*>(p.y) + base + pc;
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-          yv[r] = fmaf(Dh, sx * (float)s.xT[pc * kXtRow + i], mult * Y[ii][pt][r]);
-        }
-        if (p.yf16) {
-          __half* yb = reinterpret_cast<__half*>(p.y) + base + pc;
-          if (full) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-              yb[i * rs] = __float2half_rn(yv[r]);
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-              if (i < q) yb[i * rs] = __float2half_rn(yv[r]);
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            yb[i * rs] = __float2half_rn(yv[r]);
           }
         } else {
-          float* yb = reinterpret_cast<float*>(p.y) + base + pc;
-          if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-              yb[i * rs] = yv[r];
-            }
-          } else {
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (i < q) yb[i * rs] = __float2half_rn(yv[r]);
+          }
+        }
+      } else {
+        float* yb = reinterpret_cast<float*>(p.y) + base + pc;
+        if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-              if (i < q) yb[i * rs] = yv[r];
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            yb[i * rs] = yv[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (i < q) yb[i * rs] = yv[r];
           }
         }
       }
@@ -692,7 +725,7 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
         return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD output kernel");
       lds_raised = true;
     }
-    k_ssd_output<<<grid, 256, sizeof(K3Smem), stream>>>(p);
+    k_ssd_output<<<grid, 512, sizeof(K3Smem), stream>>>(p);
     if (qssm_status s = launch_status("ssd output")) return s;
   }
   return QSSM_OK;
