@@ -1,6 +1,7 @@
 """Benchmark of the quantized state-space hot path on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c1|c2|c4|c4f16|c5|c5f16]
+                [--only] [--no-cpu-baseline]
 
 One step = one pass of the whole hot path of the workload over one batch of synthetic input that is
 already resident in HBM: for the Mamba1 layers, quantize x (gathered into cluster order), quantize B
@@ -9,6 +10,8 @@ then run the chunked SSD; for decode, one fused state update of every sequence.
 
 Prints one JSON line: throughput in state-updates/s (B*L*D*N per step), the dominant kernel's
 roofline figures measured with HIP events on the launch stream, and the oracle timed on this host.
+Unless --only is given, the line also carries a short run of the other configurations
+(other_configs: S4D, soft-edge Mamba1, SSD, decode fp32 and fp16) with their own rooflines.
 """
 from __future__ import annotations
 
@@ -373,6 +376,42 @@ class EventTimer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
 
 
+def run_workload(torch, dev, name, steps, warmup):
+    """Sets up workload `name`, runs warmup + timed steps; returns (workload, results)."""
+    wl = WORKLOADS[name]()
+    wl.setup(dev)
+    timer = EventTimer(torch)
+    for _ in range(warmup):
+        wl.step(timer)
+    torch.cuda.synchronize()
+    timer.active = True
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wl.step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = timer.mean_ms()
+    nbytes = wl.dominant_bytes()
+    if wl.bound == "alu":
+        achieved = wl.ops() / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "T VALU lane-ops/s", "frac": round(achieved / VALU_PEAK_TOPS, 4)}
+    else:
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(name)
+    roof["kernel"] = wl.dominant
+    roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["algorithmic_bytes"] = int(nbytes)
+    if wl.bound == "alu":
+        roof["ops_per_update"] = wl.ops_per_update
+    res = {"value": wl.updates() * steps / elapsed, "ms_per_step": elapsed * 1e3 / steps,
+           "roofline": roof,
+           "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return wl, res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +419,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", dest="all_configs", action="store_true", default=True,
+                    help="also run the other configurations briefly (default)")
+    ap.add_argument("--only", dest="all_configs", action="store_false",
+                    help="run the selected workload only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (reference for the traffic counters)")
     ap.add_argument("--print-digest", action="store_true",
@@ -400,43 +443,12 @@ def main():
     if args.copy_probe:
         copy_probe(torch, dev)
         return
-    wl = WORKLOADS[args.workload]()
-    wl.setup(dev)
-    timer = EventTimer(torch)
-    for _ in range(args.warmup):
-        wl.step(timer)
-    torch.cuda.synchronize()
-    timer.active = True
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        wl.step(timer)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern_ms = timer.mean_ms()
-
-    ups = wl.updates()
-    value = ups * args.steps / elapsed
-    nbytes = wl.dominant_bytes()
-    if wl.bound == "alu":
-        achieved = wl.ops() / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                "unit": "T VALU lane-ops/s", "frac": round(achieved / VALU_PEAK_TOPS, 4)}
-    else:
-        achieved = nbytes / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = wl.dominant
-    roof["kernel_us"] = round(kern_ms * 1e3, 2)
-    roof["algorithmic_bytes"] = int(nbytes)
-    if wl.bound == "alu":
-        roof["ops_per_update"] = wl.ops_per_update
-
-    out = {"metric": METRIC, "value": value, "unit": "state-updates/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+    wl, res = run_workload(torch, dev, args.workload, args.steps, args.warmup)
+    out = {"metric": METRIC, "value": res["value"], "unit": "state-updates/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-           "data": "synthetic", "config": wl.config, "roofline": roof,
-           "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "data": "synthetic", "config": wl.config, "roofline": res["roofline"],
+           "hbm_frac_dominant": res["hbm_frac_dominant"],
            "timing": "HIP events on the launch stream around every timed call of the dominant "
                      "entry point; value from the wall clock over the timed steps"}
     if not args.no_cpu_baseline:
@@ -445,6 +457,21 @@ def main():
         threads = oracle.max_threads()
         out["cpu_baseline"] = {"value": v, "unit": "state-updates/s", "cores": threads,
                                "kind": "oracle", "sample": sample}
+    del wl
+    if args.all_configs:
+        # the other configurations of the same metric, briefly (same protocol, fewer steps)
+        others = {}
+        for name in ("c2", "c3se", "c4", "c5", "c5f16"):
+            if name == args.workload:
+                continue
+            w2, r2 = run_workload(torch, dev, name, min(args.steps, 10), min(args.warmup, 2))
+            others[name] = {"workload": w2.config["workload"], "value": r2["value"],
+                            "ms_per_step": r2["ms_per_step"],
+                            "roofline": {k: r2["roofline"][k] for k in
+                                         ("bound", "achieved", "peak", "unit", "frac", "kernel_us")}}
+            del w2
+            torch.cuda.empty_cache()
+        out["other_configs"] = others
     print(json.dumps(out), flush=True)
 
 

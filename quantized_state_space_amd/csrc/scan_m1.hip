@@ -93,9 +93,17 @@ __global__ __launch_bounds__(256) void k_stage_bc(const int8_t* __restrict__ Bq,
 
 // Unscaled x value of a code byte: the int8 code, or the soft-edge code times its mode factor
 // (1, 1/4 or 4; exact), so that the dequantized value is sx * xunit.
+// Branch-free soft-edge decode for base scale 1: tag 0 -> 7-bit payload, tag 10 -> 6-bit payload
+// times 1/4, tag 11 -> 6-bit payload times 4 (the layout of softedge_value).
 template <int XCODE>
-__device__ __forceinline__ float xunit(uint32_t byte) {  // NOLINT
-  if (XCODE == QSSM_X_SOFTEDGE) return softedge_value(byte & 0xFFu, 1.0f);
+__device__ __forceinline__ float xunit(uint32_t byte) {
+  if (XCODE == QSSM_X_SOFTEDGE) {
+    const int q7 = __builtin_amdgcn_sbfe((int)byte, 0, 7);
+    const int q6 = __builtin_amdgcn_sbfe((int)byte, 0, 6);
+    const bool tagged = (byte & 0x80u) != 0;
+    const float m = tagged ? ((byte & 0x40u) ? 4.0f : 0.25f) : 1.0f;
+    return (float)(tagged ? q6 : q7) * m;
+  }
   return (float)(int8_t)(byte & 0xFFu);
 }
 
