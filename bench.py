@@ -313,9 +313,9 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (139083153, 110238048, "22668164ae914305"),
+    "c3": (150804017, 133339792, "141cc03f43175d53"),
     "c2": (369686, 7472208, "1af91dec259fc264"),
-    "c4": (1038708454, 956576264, "5a45487fe13d938a"),
+    "c4": (1041268800, 956580040, "7be46f1797dd35cb"),
     "c5": (1100194426, 1082565320, "5c4dad04e617f92c"),
 }
 TRAFFIC_SOURCES = {
