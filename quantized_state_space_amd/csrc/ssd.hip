@@ -21,7 +21,8 @@
 //   K3 k_ssd_output       one workgroup per (b, chunk, B/C group): G^T is built once with int8 MFMA
 //                         and kept in registers (8 waves, one query block of causal 32x32 tiles
 //                         each, two waves per SIMD); per head the inter-chunk product, the
-//                         intra-chunk product and the D term.
+//                         intra-chunk product and the D term, with the next head's inputs
+//                         arriving in LDS by direct loads meanwhile.
 // MFMA lane layouts (verified on gfx950): operand lane l holds row/column l%32 and a run of
 // consecutive k at offset (K/2)*(l/32); the 32x32 accumulator register r of lane l is element
 // (8*(r/4) + 4*(l/32) + r%4, l%32).
@@ -68,6 +69,7 @@ struct SsdParams {
   float* S;       // [B, nc, nh, P, N]: chunk states
   float* dec;     // [B, nc, nh]: exp(cum at the last step of the chunk)
   _Float16* Hh;   // [B, nc, nh, P, N]: sC(n) * state entering the chunk, fp16 (K3's operand)
+  float* sxt;     // [nh, P]: x scale of each channel, 0 where invalid (written by K1, read by K3)
 };
 
 __device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
@@ -120,7 +122,7 @@ __device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
 }
 
 // Loads of one head's delta (step tid) and x codes (rows 16 (tid / 16) .. + 15, codes
-// 4 (tid % 16) .. + 3) into registers, issued one head ahead of their use in K1 and K3.
+// 4 (tid % 16) .. + 3) into registers, issued one head ahead of their use in K1.
 __device__ __forceinline__ void fetch_head(const SsdParams& p, int64_t b, int64_t c, int64_t t0,
                                               int q, int64_t h, int tid, float& dt,
                                               uint32_t (&x)[16], float& sx) {
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
     }
     if (tid == 0) p.dec[(b * p.nc + c) * p.nh + h] = expf(cum_last);
     if (tid < kP) s.sxs[tid] = pf_sx;
+    if (b == 0 && c == 0 && tid < kP) p.sxt[h * kP + tid] = pf_sx;
     __syncthreads();
 
     // weighted x tile, transposed [p][j]
@@ -330,11 +333,20 @@ struct K3Smem {
   int8_t qC[kQ * kRow128];  // C chunk rows [i][n]
   _Float16 xT[kP * kXtRow];  // x codes of the head, [p][j] (exact in fp16)
   _Float16 Hs[kP * kHsRow];  // sC(n) * H_prev[p][n]
+  // The next head's inputs, written by direct global-to-LDS loads while the current head computes:
+  // x codes in 1 KB blocks of 16 rows (row r of block jb at slot (r + jb) % 16, so that the
+  // transposing reads below hit distinct banks), the entering state as stored in Hh, delta, sx.
+  int8_t stx[kQ * kP];
+  _Float16 sth[kP * kN];
+  float stdt[kQ];
+  float stsx[kP];
+  float stad[2];  // A_h and D_h
   float cum[kQ];
   float dtv[kQ];
   float ecum[kQ];   // exp(cum_i)
   float cjv[kQ];    // exp(cum at the end of j's 32-block - cum_j) * delta_j
   float sxs[kP];
+  float dh;  // D_h of the current head
   float sh[8];
 };
 
@@ -419,6 +431,14 @@ __device__ __forceinline__ v8h x_operand(const K3Smem& s, int J, int mm, int pt,
   return v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Workgroup barrier that orders LDS only: outstanding global stores (and the direct LDS loads,
+// which every wave waits for itself with vmcnt before it arrives) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum of 256 values held by threads 0..255 of a 512-thread block (waves 4..7
 // take part in the barriers; their result is meaningless).
 __device__ __forceinline__ float block_scan_256(float v, float* sh) {
@@ -429,16 +449,62 @@ __device__ __forceinline__ float block_scan_256(float v, float* sh) {
     if (lane >= off) v += o;
   }
   if (lane == 63 && w < 4) sh[w] = v;
-  __syncthreads();
+  lds_barrier();
   float pre = 0.0f;
   for (int k = 0; k < w && k < 4; ++k) pre += sh[k];
-  __syncthreads();
+  lds_barrier();
   return v + pre;
+}
+
+// Issues the direct global-to-LDS loads of head h's inputs into the staging area (no registers
+// are held: the loads complete in the background and are waited for with vmcnt before use). Rows
+// past the sequence are clamped to the last valid row here and masked by the consumer.
+__device__ __forceinline__ void stage_head(const SsdParams& p, K3Smem& s, int64_t b, int64_t c,
+                                           int64_t t0, int q, int64_t h, int wave, int lane) {
+  // LDS destinations are wave-uniform (they go to M0): byte offsets from the staging base, made
+  // uniform explicitly
+  unsigned char* const base = reinterpret_cast<unsigned char*>(&s);
+  // an opaque lane id: the per-lane source addresses are recomputed at each call instead of being
+  // hoisted out of the caller's head loop, where they would stay live across the products
+  __asm__ volatile("" : "+v"(lane));
+  // x codes: wave w fills blocks 2w and 2w + 1 (16 rows of 64 bytes each, 4 lanes per row)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int jb = 2 * wave + k;
+    const int r = ((lane >> 2) - jb) & 15;
+    const int j = min(jb * 16 + r, q - 1);
+    const int8_t* src = p.xq + ((b * p.L + t0 + j) * p.nh + h) * kP + (lane & 3) * 16;
+    const int dst = uniform((int)offsetof(K3Smem, stx) + jb * 1024);
+    __builtin_amdgcn_global_load_lds(src, base + dst, 16, 0, 0);
+  }
+  // entering state: 16 KB contiguous, 1 KB per instruction
+  const _Float16* hsrc = p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int blk = 2 * wave + k;
+    const int dst = uniform((int)offsetof(K3Smem, sth) + blk * 1024);
+    __builtin_amdgcn_global_load_lds(hsrc + blk * 512 + lane * 8, base + dst, 16, 0, 0);
+  }
+  if (wave < 4) {  // delta of steps 64 w .. 64 w + 63
+    const int j = min(wave * 64 + lane, q - 1);
+    const int dst = uniform((int)offsetof(K3Smem, stdt) + wave * 256);
+    __builtin_amdgcn_global_load_lds(p.delta + (b * p.L + t0 + j) * p.nh + h, base + dst, 4, 0, 0);
+  } else if (wave == 4) {
+    const int dst = uniform((int)offsetof(K3Smem, stsx));
+    __builtin_amdgcn_global_load_lds(p.sxt + h * kP + lane, base + dst, 4, 0, 0);
+  } else if (wave == 5 && lane == 0) {
+    const int dst = uniform((int)offsetof(K3Smem, stad));
+    __builtin_amdgcn_global_load_lds(p.A + h, base + dst, 4, 0, 0);
+  } else if (wave == 6 && lane == 0 && p.Dskip) {
+    const int dst = uniform((int)offsetof(K3Smem, stad) + 4);
+    __builtin_amdgcn_global_load_lds(p.Dskip + h, base + dst, 4, 0, 0);
+  }
 }
 
 // Eight waves; wave v owns query block I = v (v < 4) or 11 - v (v >= 4), so that the two waves
 // on one SIMD (v and v + 4) hold blocks s and 7 - s: 9 causal tiles per SIMD. A wave keeps the
-// G tiles (I, J <= I) of its block in registers and produces all 64 output columns of it.
+// G tiles (I, J <= I) of its block in registers and produces all 64 output columns of it. Each
+// head's inputs arrive in LDS by direct loads issued during the previous head's products.
 __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   K3Smem& s = *reinterpret_cast<K3Smem*>(smem_raw);
@@ -464,7 +530,9 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
 #pragma unroll
   for (int sg = 0; sg < kNSG; ++sg)
     sBC[sg] = valid_or_zero(p.B_scales[g * kNSG + sg]) * valid_or_zero(p.C_scales[g * kNSG + sg]);
-  __syncthreads();
+  lds_barrier();
+  // the first head's inputs load while G is built
+  stage_head(p, s, b, c, t0, q, (int64_t)g * p.hpg, uniform(tid >> 6), tid & 63);
 
   GTile G[8];
   {
@@ -481,57 +549,63 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       tile_fence();
     }
   }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const int rs = (int)(p.nh * kP);  // row stride of y in elements
   const bool full = q == kQ;
-  // Per-head inputs are loaded at the head's start by threads 0..255 (delta of step tid, 16 rows
-  // x 4 x codes, the head's x scales, and the fp16 entering state by all threads); with two
-  // waves per SIMD the other wave hides part of their latency.
-  const int jb = (tid & 255) / 16, p4 = tid % 16;
   for (int hh = 0; hh < p.hpg; ++hh) {
     const int64_t h = (int64_t)g * p.hpg + hh;
-    float pf_dt = 0.0f, pf_sx = 0.0f;
-    uint32_t pf_x[16];
-    if (tid < kQ) fetch_head(p, b, c, t0, q, h, tid, pf_dt, pf_x, pf_sx);
+    // every wave has waited for its own staging loads of head h and is done with head h - 1
+    lds_barrier();
     // decay terms of head h
     const int j = tid & 255;
-    const float dt = pf_dt;
-    const float cum = block_scan_256(dt * p.A[h], s.sh);
+    const float dt = (tid < q) ? s.stdt[j] : 0.0f;
+    const float cum = block_scan_256(dt * s.stad[0], s.sh);
     if (tid < kQ) {
       s.cum[j] = cum;
       s.dtv[j] = dt;
       s.ecum[j] = expf(cum);
+      // exp(cum at the end of j's 32-block - cum_j) * delta_j; that step sits in this wave
+      const float cl = __shfl(cum, (tid & 63) | 31, 64);
+      s.cjv[j] = expf(cl - cum) * dt;
     }
-    if (tid < kP) s.sxs[tid] = pf_sx;
-    // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves)
-    {
-      const uint4* hsrc = reinterpret_cast<const uint4*>(p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN));
+    if (tid < kP) s.sxs[tid] = s.stsx[tid];
+    if (tid == 0) s.dh = p.Dskip ? s.stad[1] : 0.0f;
+    // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves), into padded rows
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int u = tid + 512 * k;
-        *reinterpret_cast<uint4*>(s.Hs + (u / 16) * kHsRow + (u % 16) * 8) = hsrc[u];
-      }
+    for (int k = 0; k < 2; ++k) {
+      const int u = tid + 512 * k;
+      *reinterpret_cast<uint4*>(s.Hs + (u / 16) * kHsRow + (u % 16) * 8) =
+          *reinterpret_cast<const uint4*>(s.sth + u * 8);
     }
-    __syncthreads();
     if (tid < kQ) {
-      s.cjv[j] = expf(s.cum[j | 31] - cum) * dt;
-      // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale)
+      // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale and past the
+      // sequence): thread (jb, p4) takes rows 16 jb .. 16 jb + 15, channels 4 p4 .. 4 p4 + 3
+      const int jb = tid / 16, p4 = tid % 16;
+      uint32_t raw[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t d = *reinterpret_cast<const uint32_t*>(s.stx + jb * 1024 + ((r + jb) & 15) * 64 + p4 * 4);
+        raw[r] = (jb * 16 + r < q) ? d : 0u;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pc = p4 * 4 + e;
-        const bool on = s.sxs[pc] > 0.0f;
+        const bool on = s.stsx[pc] > 0.0f;
         _Float16* dst = s.xT + pc * kXtRow + jb * 16;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           v4h vv;
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            vv[k] = on ? (_Float16)(float)(int8_t)byte_of(pf_x[4 * r4 + k], e) : (_Float16)0.0f;
+            vv[k] = on ? (_Float16)(float)(int8_t)byte_of(raw[4 * r4 + k], e) : (_Float16)0.0f;
           *reinterpret_cast<v4h*>(dst + 4 * r4) = vv;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+    // the staging area is free: the next head's inputs load during this head's products
+    if (hh + 1 < p.hpg) stage_head(p, s, b, c, t0, q, h + 1, uniform(tid >> 6), tid & 63);
 
     // Opaque copies of the lane and wave ids: the tile addresses below do not depend on the head,
     // and hoisting all of them out of the head loop would keep them live across it (spills).
@@ -569,6 +643,9 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     for (int J = 0; J < 8; ++J) {
       tile_fence();
       if (J <= I) {
+        // opaque per head: keeps the fp32 widening of the G tile inside the head loop (hoisted,
+        // the widened copies of all tiles would stay live and spill)
+        __asm__ volatile("" : "+v"(G[J].lo), "+v"(G[J].hi));
         v8h a0, a1;
         m_tile(G[J], s, I, J, lane, a0, a1);
 #pragma unroll
@@ -581,8 +658,11 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       }
     }
     tile_fence();
+    // the staging loads were issued long before; waiting here keeps the y stores below out of
+    // the count waited for at the next head's start
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // y = sx * acc + D * xh; rows past the sequence (ragged last chunk) are not stored
-    const float Dh = p.Dskip ? p.Dskip[h] : 0.0f;
+    const float Dh = s.dh;
     const int64_t base = ((b * p.L + t0) * p.nh + h) * kP;  // y[b, t0, h, 0]
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
@@ -627,15 +707,14 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
         }
       }
     }
-    __syncthreads();
   }
 }
 
 struct WsLayout {
-  size_t s_bytes, dec_off, hh_off, total;
+  size_t s_bytes, dec_off, hh_off, sx_off, total;
 };
 
-// workspace: S (fp32 chunk states), dec, Hh (fp16 entering states), each 256-byte aligned
+// workspace: S (fp32 chunk states), dec, Hh (fp16 entering states), sxt, each 256-byte aligned
 WsLayout ws_layout(const qssm_ssd_args* a) {
   const int64_t nc = (a->seqlen + kQ - 1) / kQ;
   const size_t elems = (size_t)a->batch * nc * a->nheads * kP * kN;
@@ -643,7 +722,8 @@ WsLayout ws_layout(const qssm_ssd_args* a) {
   w.s_bytes = elems * sizeof(float);
   w.dec_off = (w.s_bytes + 255) & ~(size_t)255;
   w.hh_off = (w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
-  w.total = w.hh_off + elems * sizeof(_Float16) + 256;
+  w.sx_off = (w.hh_off + elems * sizeof(_Float16) + 255) & ~(size_t)255;
+  w.total = w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 256;
   return w;
 }
 
@@ -694,7 +774,8 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
               a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
               reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + wl.dec_off),
-              reinterpret_cast<_Float16*>(base + wl.hh_off)};
+              reinterpret_cast<_Float16*>(base + wl.hh_off),
+              reinterpret_cast<float*>(base + wl.sx_off)};
   if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff)
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
   const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
