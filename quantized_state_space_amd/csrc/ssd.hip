@@ -43,6 +43,7 @@ constexpr int kRow256 = 272;  // padded bytes of a [*][256] int8 LDS row
 constexpr int kRow128 = 136;  // padded bytes of a [*][128] int8 LDS row
 constexpr int kXtRow = 260;   // padded halves of a [*][256] fp16 LDS row (520 bytes)
 constexpr int kHsRow = 136;   // padded halves of a [*][128] fp16 LDS row (272 bytes)
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -340,15 +341,18 @@ struct K3Smem {
   _Float16 sth[kP * kN];
   float stdt[kQ];
   float stsx[kP];
-  float stad[2];  // A_h and D_h
   float cum[kQ];
   float dtv[kQ];
   float ecum[kQ];   // exp(cum_i)
   float cjv[kQ];    // exp(cum at the end of j's 32-block - cum_j) * delta_j
   float sxs[kP];
-  float dh;  // D_h of the current head
+  float stad[2];  // staged A_h and D_h
+  float dh;       // D_h of the current head
   float sh[8];
 };
+static_assert(offsetof(K3Smem, cum) % 16 == 0 && offsetof(K3Smem, dtv) % 16 == 0 &&
+                  offsetof(K3Smem, ecum) % 16 == 0 && offsetof(K3Smem, cjv) % 16 == 0,
+              "16-byte vector reads of the decay terms");
 
 
 // Compiler-only fence: keeps one tile's work from being interleaved with the next tile's.
@@ -387,37 +391,44 @@ __device__ __forceinline__ GTile pack_g(const v16f& G) {
 }
 
 // M tile = G o exp(cum_i - cum_j) [j <= i] o delta_j as two fp16 A operands (k-slots follow the
-// accumulator rows of G, see the B operand gather below)
+// accumulator rows of G, see the B operand gather below). Register r of lane l holds column
+// j = 32 J + 4 (l / 32) + 8 (r / 4) + r % 4, so the column terms come in runs of four (16-byte
+// reads, the same address for each half-wave). Each element is one mixed-precision fma from the
+// fp16 G value, rounded once to fp16.
 __device__ __forceinline__ void m_tile(const GTile& Gt, const K3Smem& s, int I, int J, int lane,
                                        v8h& a0, v8h& a1) {
-  float G[16];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    G[e] = (float)Gt.lo[e];
-    G[8 + e] = (float)Gt.hi[e];
-  }
+  typedef float v4f __attribute__((ext_vector_type(4)));
   const int i = I * 32 + (lane & 31);  // this lane's query row
+  const int jb = J * 32 + 4 * (lane >> 5);
   const float ci = s.cum[i];
-  float m[16];
+  float f[16];
   if (J < I) {
     // both factors are at most 1 (cum does not increase): no overflow for long decays
     const float ri = __expf(ci - s.cum[J * 32 + 31]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = J * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-      m[r] = G[r] * (ri * s.cjv[j]);
+    for (int q = 0; q < 4; ++q) {
+      const v4f c4 = *reinterpret_cast<const v4f*>(s.cjv + jb + 8 * q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) f[4 * q + k] = ri * c4[k];
     }
   } else {
+    // diagonal tile, branch-free: past the diagonal cum_j <= cum_i, the clamped exponent is 0
+    // and the select discards the value
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = J * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-      m[r] = (j <= i) ? G[r] * (__expf(ci - s.cum[j]) * s.dtv[j]) : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const v4f c4 = *reinterpret_cast<const v4f*>(s.cum + jb + 8 * q);
+      const v4f d4 = *reinterpret_cast<const v4f*>(s.dtv + jb + 8 * q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e = __expf(fminf(ci - c4[k], 0.0f)) * d4[k];
+        f[4 * q + k] = (jb + 8 * q + k <= i) ? e : 0.0f;
+      }
     }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a0[e] = (_Float16)m[e];
-    a1[e] = (_Float16)m[8 + e];
+    a0[e] = (_Float16)fmaf((float)Gt.lo[e], f[e], 0.0f);
+    a1[e] = (_Float16)fmaf((float)Gt.hi[e], f[8 + e], 0.0f);
   }
 }
 
@@ -613,7 +624,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     __asm__ volatile("" : "+v"(lane));
     int v = uniform(tid >> 6);
     __asm__ volatile("" : "+s"(v));
-    const int I = v < 4 ? v : 11 - v;
+    const int I = uniform(v < 4 ? v : 11 - v);  // (the asm output is not known to be uniform)
     const int kofs = 8 * (lane >> 5);
     v16f Y[2] = {};
     // Y_inter = exp(cum_i) * qC[i, :] . Hs[:, p]
@@ -627,15 +638,23 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
         Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bv, Y[pt], 0, 0, 0);
       }
     }
-    // row scale exp(cum_i), column scale 1 / sx[p] (the intra part accumulates raw x codes)
+    // row scale exp(cum_i), column scale 1 / sx[p] (the intra part accumulates raw x codes);
+    // register r holds row i = 32 I + 4 (lane / 32) + 8 (r / 4) + r % 4
+    {
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      float er[16];
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      const float sx = s.sxs[pt * 32 + (lane & 31)];
-      const float inv = (sx > 0.0f) ? 1.0f / sx : 1.0f;
+      for (int q = 0; q < 4; ++q) {
+        const v4f e4 = *reinterpret_cast<const v4f*>(s.ecum + I * 32 + 4 * (lane >> 5) + 8 * q);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        Y[pt][r] *= s.ecum[i] * inv;
+        for (int k = 0; k < 4; ++k) er[4 * q + k] = e4[k];
+      }
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const float sx = s.sxs[pt * 32 + (lane & 31)];
+        const float inv = (sx > 0.0f) ? 1.0f / sx : 1.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Y[pt][r] *= er[r] * inv;
       }
     }
     // Y_intra on top, tile by tile
@@ -669,41 +688,41 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       const int pc = pt * 32 + (lane & 31);
       const float sx = s.sxs[pc];
       const float mult = (sx > 0.0f) ? sx : 1.0f;
+      const float Dsx = Dh * sx;
       float yv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        yv[r] = fmaf(Dh, sx * (float)s.xT[pc * kXtRow + i], mult * Y[pt][r]);
+      for (int q = 0; q < 4; ++q) {
+        const v4h x4 = *reinterpret_cast<const v4h*>(s.xT + pc * kXtRow + I * 32 + 4 * (lane >> 5) + 8 * q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) yv[4 * q + k] = fmaf(Dsx, (float)x4[k], mult * Y[pt][4 * q + k]);
       }
+      // register r holds row 32 I + 8 (r / 4) + r % 4 + 4 (lane / 32): buffer stores with the
+      // head's y block as the resource, a per-register wave-uniform row offset (soffset) and one
+      // per-lane offset, so the stores need no per-lane 64-bit address arithmetic (all offsets fit
+      // 32 bits: nheads <= 2^14 is checked on the host)
+      const int ilane = 4 * (lane >> 5);
+      const int esz = p.yf16 ? 2 : 4;
+      const uint64_t ya = reinterpret_cast<uint64_t>(static_cast<char*>(p.y) + base * esz);
+      void* const yblk = reinterpret_cast<void*>(
+          ((uint64_t)(uint32_t)uniform((int)(ya >> 32)) << 32) | (uint32_t)uniform((int)ya));
+      const __amdgpu_buffer_rsrc_t yrs =
+          __builtin_amdgcn_make_buffer_rsrc(yblk, (short)0, 0x7FFFFFFF, kBufferWord3);
+      const int voff = (ilane * rs + pc) * esz;
       if (p.yf16) {
-        __half* yb = reinterpret_cast<__half*>(p.y) + base + pc;
-        if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            yb[i * rs] = __float2half_rn(yv[r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            if (i < q) yb[i * rs] = __float2half_rn(yv[r]);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+          if (full || ir + ilane < q)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, __float2half_rn(yv[r])),
+                                                  yrs, voff, uniform(ir * rs * 2), 0);
         }
       } else {
-        float* yb = reinterpret_cast<float*>(p.y) + base + pc;
-        if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            yb[i * rs] = yv[r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = I * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            if (i < q) yb[i * rs] = yv[r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+          if (full || ir + ilane < q)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
+                                                  uniform(ir * rs * 4), 0);
         }
       }
     }
@@ -757,6 +776,7 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
     return fail(QSSM_ERR_UNSUPPORTED,
                 "this build implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
   if (L > ((int64_t)1 << 40)) return fail(QSSM_ERR_UNSUPPORTED, "seqlen too large");
+  if (nh > (1 << 14)) return fail(QSSM_ERR_UNSUPPORTED, "nheads too large");
   if (B == 0) return QSSM_OK;
   if (!a->xq || !a->x_group_of || !a->x_scales || !a->delta || !a->A || !a->Bq || !a->Cq ||
       !a->B_scales || !a->C_scales || !a->y)
