@@ -44,6 +44,10 @@ constexpr int kRow128 = 136;  // padded bytes of a [*][128] int8 LDS row
 constexpr int kXtRow = 260;   // padded halves of a [*][256] fp16 LDS row (520 bytes)
 constexpr int kHsRow = 136;   // padded halves of a [*][128] fp16 LDS row (272 bytes)
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued through the builtin, not
+// inline asm, so that the compiler's wait insertion sees the direct LDS loads completed and does not
+// add a vmcnt(0) of its own at the next LDS barrier (which would also wait for the y stores).
+constexpr int kVmcnt0 = 0x0F70;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -467,6 +471,15 @@ __device__ __forceinline__ float block_scan_256(float v, float* sh) {
   return v + pre;
 }
 
+// Row r (0..15) of a 16-row x block jb sits at slot ((r ^ ((r >> 3) << 1)) + jb) & 15 of its 1 KB
+// staging block (a bijection). With eight rows per thread in the transposing reads, the four row
+// blocks a wave reads at one step land in four distinct 64-byte bank groups. stx_row inverts it.
+__device__ __forceinline__ int stx_slot(int r, int jb) { return ((r ^ ((r >> 3) << 1)) + jb) & 15; }
+__device__ __forceinline__ int stx_row(int slot, int jb) {
+  const int t = (slot - jb) & 15;
+  return t ^ ((t >> 3) << 1);
+}
+
 // Issues the direct global-to-LDS loads of head h's inputs into the staging area (no registers
 // are held: the loads complete in the background and are waited for with vmcnt before use). Rows
 // past the sequence are clamped to the last valid row here and masked by the consumer.
@@ -478,11 +491,12 @@ __device__ __forceinline__ void stage_head(const SsdParams& p, K3Smem& s, int64_
   // an opaque lane id: the per-lane source addresses are recomputed at each call instead of being
   // hoisted out of the caller's head loop, where they would stay live across the products
   __asm__ volatile("" : "+v"(lane));
-  // x codes: wave w fills blocks 2w and 2w + 1 (16 rows of 64 bytes each, 4 lanes per row)
+  // x codes: wave w fills blocks 2w and 2w + 1 (16 rows of 64 bytes each, 4 lanes per row);
+  // lane l writes slot l / 4 of its block, which holds row stx_row(l / 4, block)
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int jb = 2 * wave + k;
-    const int r = ((lane >> 2) - jb) & 15;
+    const int r = stx_row(lane >> 2, jb);
     const int j = min(jb * 16 + r, q - 1);
     const int8_t* src = p.xq + ((b * p.L + t0 + j) * p.nh + h) * kP + (lane & 3) * 16;
     const int dst = uniform((int)offsetof(K3Smem, stx) + jb * 1024);
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       tile_fence();
     }
   }
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
   const int rs = (int)(p.nh * kP);  // row stride of y in elements
   const bool full = q == kQ;
@@ -589,23 +603,24 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       *reinterpret_cast<uint4*>(s.Hs + (u / 16) * kHsRow + (u % 16) * 8) =
           *reinterpret_cast<const uint4*>(s.sth + u * 8);
     }
-    if (tid < kQ) {
+    {
       // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale and past the
-      // sequence): thread (jb, p4) takes rows 16 jb .. 16 jb + 15, channels 4 p4 .. 4 p4 + 3
-      const int jb = tid / 16, p4 = tid % 16;
-      uint32_t raw[16];
+      // sequence): thread (jh, p4) takes rows 8 jh .. 8 jh + 7, channels 4 p4 .. 4 p4 + 3
+      const int jh = tid / 16, p4 = tid % 16;
+      const int jb = jh >> 1, r0 = 8 * (jh & 1);
+      uint32_t raw[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(s.stx + jb * 1024 + ((r + jb) & 15) * 64 + p4 * 4);
-        raw[r] = (jb * 16 + r < q) ? d : 0u;
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t d = *reinterpret_cast<const uint32_t*>(s.stx + jb * 1024 + stx_slot(r0 + r, jb) * 64 + p4 * 4);
+        raw[r] = (jh * 8 + r < q) ? d : 0u;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pc = p4 * 4 + e;
         const bool on = s.stsx[pc] > 0.0f;
-        _Float16* dst = s.xT + pc * kXtRow + jb * 16;
+        _Float16* dst = s.xT + pc * kXtRow + jh * 8;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
+        for (int r4 = 0; r4 < 2; ++r4) {
           v4h vv;
 #pragma unroll
           for (int k = 0; k < 4; ++k)
@@ -679,7 +694,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     tile_fence();
     // the staging loads were issued long before; waiting here keeps the y stores below out of
     // the count waited for at the next head's start
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     // y = sx * acc + D * xh; rows past the sequence (ragged last chunk) are not stored
     const float Dh = s.dh;
     const int64_t base = ((b * p.L + t0) * p.nh + h) * kP;  // y[b, t0, h, 0]
@@ -708,21 +723,40 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       const __amdgpu_buffer_rsrc_t yrs =
           __builtin_amdgcn_make_buffer_rsrc(yblk, (short)0, 0x7FFFFFFF, kBufferWord3);
       const int voff = (ilane * rs + pc) * esz;
+      // the full-chunk path stores unconditionally; the ragged last chunk masks rows past q
       if (p.yf16) {
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-          if (full || ir + ilane < q)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, __float2half_rn(yv[r])),
-                                                  yrs, voff, uniform(ir * rs * 2), 0);
+          for (int r = 0; r < 16; ++r) {
+            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+            __builtin_amdgcn_raw_buffer_store_b16(
+                __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), 0);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+            if (ir + ilane < q)
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), 0);
+          }
         }
       } else {
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-          if (full || ir + ilane < q)
+          for (int r = 0; r < 16; ++r) {
+            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
                                                   uniform(ir * rs * 4), 0);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+            if (ir + ilane < q)
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
+                                                    uniform(ir * rs * 4), 0);
+          }
         }
       }
     }
