@@ -75,6 +75,7 @@ struct SsdParams {
   float* dec;     // [B, nc, nh]: exp(cum at the last step of the chunk)
   _Float16* Hh;   // [B, nc, nh, P, N]: sC(n) * state entering the chunk, fp16 (K3's operand)
   float* sxt;     // [nh, P]: x scale of each channel, 0 where invalid (written by K1, read by K3)
+  float* cumw;    // [B, nc, nh, Q]: cumulative sum of delta * A within the chunk (K1 -> K3)
 };
 
 __device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
     const int j = tid;
     const float dt = pf_dt;
     const float cum = block_scan(dt * Ah, s.sh);
+    p.cumw[((b * p.nc + c) * p.nh + h) * kQ + j] = cum;
     if (j == q - 1) s.sh[4] = cum;
     __syncthreads();
     const float cum_last = s.sh[4];
@@ -344,17 +346,18 @@ struct K3Smem {
   int8_t stx[kQ * kP];
   _Float16 sth[kP * kN];
   float stdt[kQ];
+  float stcum[kQ];
   float stsx[kP];
   float cum[kQ];
   float dtv[kQ];
   float ecum[kQ];   // exp(cum_i)
   float cjv[kQ];    // exp(cum at the end of j's 32-block - cum_j) * delta_j
   float sxs[kP];
-  float stad[2];  // staged A_h and D_h
-  float dh;       // D_h of the current head
-  float sh[8];
+  float stad;  // staged D_h
+  float dh;    // D_h of the current head
 };
-static_assert(offsetof(K3Smem, cum) % 16 == 0 && offsetof(K3Smem, dtv) % 16 == 0 &&
+static_assert(offsetof(K3Smem, stcum) % 16 == 0 && offsetof(K3Smem, cum) % 16 == 0 &&
+                  offsetof(K3Smem, dtv) % 16 == 0 &&
                   offsetof(K3Smem, ecum) % 16 == 0 && offsetof(K3Smem, cjv) % 16 == 0,
               "16-byte vector reads of the decay terms");
 
@@ -454,23 +457,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Inclusive prefix sum of 256 values held by threads 0..255 of a 512-thread block (waves 4..7
-// take part in the barriers; their result is meaningless).
-__device__ __forceinline__ float block_scan_256(float v, float* sh) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63 && w < 4) sh[w] = v;
-  lds_barrier();
-  float pre = 0.0f;
-  for (int k = 0; k < w && k < 4; ++k) pre += sh[k];
-  lds_barrier();
-  return v + pre;
-}
-
 // Row r (0..15) of a 16-row x block jb sits at slot ((r ^ ((r >> 3) << 1)) + jb) & 15 of its 1 KB
 // staging block (a bijection). With eight rows per thread in the transposing reads, the four row
 // blocks a wave reads at one step land in four distinct 64-byte bank groups. stx_row inverts it.
@@ -517,11 +503,12 @@ __device__ __forceinline__ void stage_head(const SsdParams& p, K3Smem& s, int64_
   } else if (wave == 4) {
     const int dst = uniform((int)offsetof(K3Smem, stsx));
     __builtin_amdgcn_global_load_lds(p.sxt + h * kP + lane, base + dst, 4, 0, 0);
-  } else if (wave == 5 && lane == 0) {
-    const int dst = uniform((int)offsetof(K3Smem, stad));
-    __builtin_amdgcn_global_load_lds(p.A + h, base + dst, 4, 0, 0);
+  } else if (wave == 5) {  // the chunk's cumulative decay exponents, 1 KB contiguous
+    const int dst = uniform((int)offsetof(K3Smem, stcum));
+    __builtin_amdgcn_global_load_lds(p.cumw + ((b * p.nc + c) * p.nh + h) * kQ + lane * 4, base + dst,
+                                     16, 0, 0);
   } else if (wave == 6 && lane == 0 && p.Dskip) {
-    const int dst = uniform((int)offsetof(K3Smem, stad) + 4);
+    const int dst = uniform((int)offsetof(K3Smem, stad));
     __builtin_amdgcn_global_load_lds(p.Dskip + h, base + dst, 4, 0, 0);
   }
 }
@@ -583,10 +570,10 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     // every wave has waited for its own staging loads of head h and is done with head h - 1
     lds_barrier();
     // decay terms of head h
-    const int j = tid & 255;
-    const float dt = (tid < q) ? s.stdt[j] : 0.0f;
-    const float cum = block_scan_256(dt * s.stad[0], s.sh);
     if (tid < kQ) {
+      const int j = tid;
+      const float dt = (tid < q) ? s.stdt[j] : 0.0f;
+      const float cum = s.stcum[j];
       s.cum[j] = cum;
       s.dtv[j] = dt;
       s.ecum[j] = expf(cum);
@@ -595,7 +582,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       s.cjv[j] = expf(cl - cum) * dt;
     }
     if (tid < kP) s.sxs[tid] = s.stsx[tid];
-    if (tid == 0) s.dh = p.Dskip ? s.stad[1] : 0.0f;
+    if (tid == 0) s.dh = p.Dskip ? s.stad : 0.0f;
     // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves), into padded rows
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -764,10 +751,11 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
 }
 
 struct WsLayout {
-  size_t s_bytes, dec_off, hh_off, sx_off, total;
+  size_t s_bytes, dec_off, hh_off, sx_off, cum_off, total;
 };
 
-// workspace: S (fp32 chunk states), dec, Hh (fp16 entering states), sxt, each 256-byte aligned
+// workspace: S (fp32 chunk states), dec, Hh (fp16 entering states), sxt, cumw, each 256-byte
+// aligned
 WsLayout ws_layout(const qssm_ssd_args* a) {
   const int64_t nc = (a->seqlen + kQ - 1) / kQ;
   const size_t elems = (size_t)a->batch * nc * a->nheads * kP * kN;
@@ -776,7 +764,8 @@ WsLayout ws_layout(const qssm_ssd_args* a) {
   w.dec_off = (w.s_bytes + 255) & ~(size_t)255;
   w.hh_off = (w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
   w.sx_off = (w.hh_off + elems * sizeof(_Float16) + 255) & ~(size_t)255;
-  w.total = w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 256;
+  w.cum_off = (w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 255) & ~(size_t)255;
+  w.total = w.cum_off + (size_t)a->batch * nc * a->nheads * kQ * sizeof(float) + 256;
   return w;
 }
 
@@ -829,7 +818,8 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
               reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + wl.dec_off),
               reinterpret_cast<_Float16*>(base + wl.hh_off),
-              reinterpret_cast<float*>(base + wl.sx_off)};
+              reinterpret_cast<float*>(base + wl.sx_off),
+              reinterpret_cast<float*>(base + wl.cum_off)};
   if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff)
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
   const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
