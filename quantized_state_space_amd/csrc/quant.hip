@@ -4,8 +4,9 @@
 // channels; B and C with one scale per state group. Quamba-SE blog (2.1, 2.2): three-scale byte.
 //
 // These are HBM-bound elementwise passes (4 bytes in, 1 byte out per element). Each thread handles
-// 16 consecutive output elements: one 16-byte store and, whenever the source run is contiguous,
-// four 16-byte loads. The per-group scales (and soft-edge thresholds) of a launch are staged in LDS.
+// four chunks of 4 consecutive elements a block-width apart (16-byte loads, 4-byte stores, every
+// wave instruction one contiguous run). The per-group scales (and soft-edge thresholds) of a launch
+// are staged in LDS when they fit.
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -40,7 +41,13 @@ struct Geometry {
   const uint8_t* group_of;  // MAP_GROUP
   int32_t N, gs, ngs;       // MAP_STATE: channel c = g*N + n -> scale g*ngs + n/gs
   int32_t nscales;
+  // Advance of (position in row, channel, outer index) between a thread's consecutive chunks,
+  // kStride = kThreads * 4 elements apart (set on the host): stride % inner, (stride / inner) % C,
+  // stride / inner / C.
+  int64_t step_i, step_c, step_o;
 };
+
+constexpr int64_t kStride = (int64_t)kThreads * 4;
 
 // a / b, in 32-bit arithmetic when both fit (the common case), else 64-bit.
 __device__ __forceinline__ int64_t div_fast(int64_t a, int64_t b) {
@@ -64,13 +71,13 @@ struct Chunk {
   int n;
 };
 
+// ROWS and CHANNELS: the chunk at element e sits at in-row index i, channel c, outer index o
+// (tracked incrementally by the caller).
 template <int MAP, int LAYOUT>
 __device__ __forceinline__ void load_chunk(const Geometry& g, const float* __restrict__ x,
-                                           int64_t e, Chunk<MAP, LAYOUT>& ch) {
+                                           int64_t e, int64_t i, int64_t c, int64_t o,
+                                           Chunk<MAP, LAYOUT>& ch) {
   if (LAYOUT == L_ROWS) {
-    const int64_t row = div_fast(e, g.inner);
-    const int64_t i = e - row * g.inner;
-    const int64_t o = div_fast(row, g.C), c = row - o * g.C;
     const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
     ch.si[0] = scale_index<MAP>(g, c);
     ch.v = *reinterpret_cast<const f32x4*>(x + (o * g.C + src) * g.inner + i);
@@ -78,7 +85,7 @@ __device__ __forceinline__ void load_chunk(const Geometry& g, const float* __res
     return;
   }
   if (LAYOUT == L_CHANNELS) {
-    const int64_t o = div_fast(e, g.C), c0 = e - o * g.C;
+    const int64_t c0 = c;
     if (MAP == MAP_GROUP) {
       const uint32_t gid = *reinterpret_cast<const uint32_t*>(g.group_of + c0);
 #pragma unroll
@@ -90,6 +97,12 @@ __device__ __forceinline__ void load_chunk(const Geometry& g, const float* __res
     ch.n = 4;
     return;
   }
+}
+
+// GENERIC: element by element from e.
+template <int MAP, int LAYOUT>
+__device__ __forceinline__ void load_chunk(const Geometry& g, const float* __restrict__ x,
+                                           int64_t e, Chunk<MAP, LAYOUT>& ch) {
   const int64_t row = div_fast(e, g.inner);
   int64_t i = e - row * g.inner;
   int64_t o = div_fast(row, g.C), c = row - o * g.C;
@@ -112,14 +125,52 @@ __device__ __forceinline__ uint32_t encode(float v, float2 sr, float2 lh) {
   return softedge_code_r(v, sr.x, sr.y, lh.x, lh.y);
 }
 
-template <int OP, int MAP, int LAYOUT>
+// Four int8 codes (quant8_r of each value, packed little-endian) with one wave-level branch for
+// the rare near-boundary correction instead of one per value. Per value the arithmetic is that of
+// rne_recip / rne_sat_recip: the clamp of v*r to [-256, 256] is a med3 (the same for non-NaN
+// values; a NaN value, or r = 0 for an invalid scale, yields code 0 whatever it computes).
+__device__ __forceinline__ uint32_t quant4(f32x4 v, const float (&s)[4], const float (&r)[4]) {
+  float c[4], f[4];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = __builtin_amdgcn_fmed3f(v[i] * r[i], -256.0f, 256.0f);
+    c[i] = rintf(f[i]);
+    any |= fabsf(f[i] - c[i]) > 0.5f - 0x1p-14f;
+  }
+  if (any) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t = f[i] - c[i];
+      if (fabsf(t) > 0.5f - 0x1p-14f) {
+        const float h = copysignf(0.5f, t);
+        const float e = fmaf(-(c[i] + h), s[i], v[i]);
+        const float eh = (h > 0.0f) ? e : -e;
+        const bool odd = (c[i] * 0.5f) != rintf(c[i] * 0.5f);
+        if (eh > 0.0f || (eh == 0.0f && odd)) c[i] += h + h;
+      }
+    }
+  }
+  int q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = (int)__builtin_amdgcn_fmed3f(c[i], -128.0f, 127.0f);
+    q[i] = (r[i] != 0.0f && v[i] == v[i]) ? qi : 0;
+  }
+  // bytes: [q0, q1, 0, 0] and [q2, q3, 0, 0], then the low halves side by side
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x0c0c0400u);
+  return lo | (hi << 16);
+}
+
+template <int OP, int MAP, int LAYOUT, bool LDS>
 __global__ __launch_bounds__(kThreads) void k_elementwise(
     const float* __restrict__ x, Geometry g, const float* __restrict__ scales,
     const float* __restrict__ Lth, const float* __restrict__ Hth, void* __restrict__ out) {
-  __shared__ float2 s_sr[OP == OP_ABSMAX ? 1 : kMaxLdsGroups];  // (s, 1/s or 0 if invalid)
-  __shared__ float2 s_LH[OP == OP_SOFTEDGE ? kMaxLdsGroups : 1];
-  __shared__ unsigned s_max[OP == OP_ABSMAX ? kMaxLdsGroups : 1];
-  const bool lds = g.nscales <= kMaxLdsGroups;
+  __shared__ float2 s_sr[OP == OP_ABSMAX || !LDS ? 1 : kMaxLdsGroups];  // (s, 1/s or 0 if invalid)
+  __shared__ float2 s_LH[OP == OP_SOFTEDGE && LDS ? kMaxLdsGroups : 1];
+  __shared__ unsigned s_max[OP == OP_ABSMAX && LDS ? kMaxLdsGroups : 1];
+  constexpr bool lds = LDS;  // the launch picks LDS when g.nscales <= kMaxLdsGroups
   if (lds) {
     for (int k = threadIdx.x; k < g.nscales; k += kThreads) {
       if (OP == OP_ABSMAX) {
@@ -142,12 +193,38 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
     return lds ? s_LH[si] : make_float2(Lth[si], Hth[si]);
   };
   constexpr bool kUniform = Chunk<MAP, LAYOUT>::kUniform;
+  constexpr bool kStepped = LAYOUT != L_GENERIC;
   Chunk<MAP, LAYOUT> ch[kChunks];
   int64_t e[kChunks];
+  // position of the thread's first chunk; later chunks step by kStride elements
+  int64_t pi = 0, pc = 0, po = 0;
+  if (kStepped) {
+    const int64_t e0 = (int64_t)blockIdx.x * kBlockElems + (int64_t)threadIdx.x * 4;
+    const int64_t row = div_fast(e0, g.inner);
+    pi = e0 - row * g.inner;
+    po = div_fast(row, g.C);
+    pc = row - po * g.C;
+  }
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
     e[k] = (int64_t)blockIdx.x * kBlockElems + ((int64_t)k * kThreads + threadIdx.x) * 4;
-    if (e[k] < g.total) load_chunk<MAP, LAYOUT>(g, x, e[k], ch[k]);
+    if (kStepped) {
+      if (e[k] < g.total) load_chunk<MAP, LAYOUT>(g, x, e[k], pi, pc, po, ch[k]);
+      pi += g.step_i;
+      int64_t cc = pc + g.step_c;
+      if (pi >= g.inner) {
+        pi -= g.inner;
+        ++cc;
+      }
+      if (cc >= g.C) {
+        cc -= g.C;
+        ++po;
+      }
+      pc = cc;
+      po += g.step_o;
+    } else if (e[k] < g.total) {
+      load_chunk<MAP, LAYOUT>(g, x, e[k], ch[k]);
+    }
   }
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
@@ -171,6 +248,15 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
         for (int i = 0; i < 4; ++i)
           if (i < c.n) push(c.si[kUniform ? 0 : i], finite_abs(c.v[i]));
       }
+    } else if (OP == OP_QUANT && kStepped) {
+      float sv[4], rv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 sr = scale_of(c.si[kUniform ? 0 : i]);
+        sv[i] = sr.x;
+        rv[i] = sr.y;
+      }
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(out) + e[k]) = quant4(c.v, sv, rv);
     } else {
       uint32_t word = 0u;
       if (kUniform) {
@@ -268,7 +354,10 @@ template <int OP, int MAP, int LAYOUT>
 void launch_elementwise(const float* x, const Geometry& g, const float* scales, const float* L,
                         const float* H, void* out, hipStream_t st) {
   const unsigned blocks = (unsigned)cdiv(g.total, (int64_t)kBlockElems);
-  k_elementwise<OP, MAP, LAYOUT><<<blocks, kThreads, 0, st>>>(x, g, scales, L, H, out);
+  if (g.nscales <= kMaxLdsGroups)
+    k_elementwise<OP, MAP, LAYOUT, true><<<blocks, kThreads, 0, st>>>(x, g, scales, L, H, out);
+  else
+    k_elementwise<OP, MAP, LAYOUT, false><<<blocks, kThreads, 0, st>>>(x, g, scales, L, H, out);
 }
 
 template <int OP, int MAP>
@@ -280,9 +369,14 @@ void launch_any(int layout, const float* x, const Geometry& g, const float* scal
 }
 
 template <int OP, int MAP>
-qssm_status launch(const float* x, const Geometry& g, float* scales, int compute_scales,
+qssm_status launch(const float* x, Geometry g, float* scales, int compute_scales,
                    const float* L, const float* H, void* out, hipStream_t st) {
   const int layout = choose_layout<OP, MAP>(g);
+  if (g.inner > 0 && g.C > 0) {
+    g.step_i = kStride % g.inner;
+    g.step_c = (kStride / g.inner) % g.C;
+    g.step_o = kStride / g.inner / g.C;
+  }
   if (compute_scales) {
     k_fill_u32<<<(unsigned)cdiv(g.nscales, 256), 256, 0, st>>>(
         reinterpret_cast<unsigned*>(scales), g.nscales, 0u);
