@@ -123,26 +123,31 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   const int g = uniform((int)(d0 / p.dpg));
 
   // Scales. x: per channel (lane); a channel whose scale is not valid has every x value 0, so its
-  // codes are masked to 0 and its scale taken as 0. With fp16 codes staged, the B and C scales of
-  // the wave's state group multiply the step input (B) and the wave's partial output (C); an
-  // invalid one is 0 (its codes are staged as 0 as well).
+  // codes are masked to 0 and its scale taken as 0. The chains run in input units: a wave's chain
+  // holds h / su, with su the scale of its per-step input (sx, times the B scale of the wave's
+  // state group when fp16 codes are staged), so each step adds dt * x_code * B; su and the C scale
+  // multiply the wave's partial output once, in the combine. An invalid B or C scale is 0 (its
+  // codes are staged as 0 as well); a zero su (no input reaches the chain) is replaced by 1.
   float sx = p.x_scales[p.x_group_of[dc]];
   const bool sx_ok = scale_ok(sx);
   const uint32_t xmask = sx_ok ? 0xFFFFFFFFu : 0u;
   if (!sx_ok) sx = 0.0f;
   const int ngs = (int)(p.N / p.gs);
-  float su = sx;         // scale of the per-step input dt * x * B of this wave's chains
-  float wC[W];           // scale of each wave's partial output
+  float cf[W];     // factor of each wave's partial output (C scale x that wave's su)
+  float su = 1.0f;  // this wave's su
 #pragma unroll
-  for (int ww = 0; ww < W; ++ww) wC[ww] = 1.0f;
-  if (CODE16) {
-    const float sb = p.B_scales[g * ngs + (w * NS) / p.gs];
-    su = sx * (scale_ok(sb) ? sb : 0.0f);
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const float sc = p.C_scales[g * ngs + (ww * NS) / p.gs];
-      wC[ww] = scale_ok(sc) ? sc : 0.0f;
+  for (int ww = 0; ww < W; ++ww) {
+    float sb = 1.0f, sc = 1.0f;
+    if (CODE16) {
+      sb = p.B_scales[g * ngs + (ww * NS) / p.gs];
+      sb = scale_ok(sb) ? sb : 0.0f;
+      sc = p.C_scales[g * ngs + (ww * NS) / p.gs];
+      sc = scale_ok(sc) ? sc : 0.0f;
     }
+    float s = sx * sb;
+    if (s == 0.0f) s = 1.0f;
+    cf[ww] = sc * s;
+    if (ww == w) su = s;
   }
   const float Dsx = (p.Dskip ? p.Dskip[dc] : 0.0f) * sx;
 
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   for (int k = 0; k < NS; ++k) {
     const int n = w * NS + k;
     a2[k] = p.A[dc * p.N + n] * kLog2e;
-    h[k] = p.h0 ? p.h0[(b * p.D + dc) * p.N + n] : 0.0f;
+    h[k] = p.h0 ? p.h0[(b * p.D + dc) * p.N + n] / su : 0.0f;
   }
 
   const float* __restrict__ drow = p.delta + (b * p.D + dc) * L;
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       for (int s2 = 0; s2 < kBatch; ++s2) {
         const int t = bt + s2;
         const float dt = dl[t];
-        const float u = dt * xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))) * su;
+        const float u = dt * xunit<XCODE>(xq[t / 4] >> (8 * (t % 4)));
         float dA[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) dA[k] = dAr[t % 2][k];
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       float sum = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < W; ++ww)
-        sum = CODE16 ? fmaf(wC[ww], ybuf[buf][ww][t][lane], sum) : sum + ybuf[buf][ww][t][lane];
+        sum = fmaf(cf[ww], ybuf[buf][ww][t][lane], sum);
       yo[j] = fmaf(Dsx, xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))), sum);
     }
     const int64_t t0 = tb + w * kPer;
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 
   if (valid && p.h_last) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) p.h_last[(b * p.D + d) * p.N + w * NS + k] = h[k];
+    for (int k = 0; k < NS; ++k) p.h_last[(b * p.D + d) * p.N + w * NS + k] = h[k] * su;
   }
 }
 
