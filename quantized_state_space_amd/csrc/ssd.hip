@@ -561,6 +561,17 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       tile_fence();
     }
   }
+  // the C codes of this wave's query block as fp16 A operands of the inter-chunk product (the
+  // same for every head)
+  v8h QC[kN / 16];
+  {
+    const int lane = tid & 63;
+    const int I = uniform(uniform(tid >> 6) < 4 ? uniform(tid >> 6) : 11 - uniform(tid >> 6));
+#pragma unroll
+    for (int ks = 0; ks < kN / 16; ++ks)
+      QC[ks] = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 +
+                                                           ks * 16 + 8 * (lane >> 5)));
+  }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
   const int rs = (int)(p.nh * kP);  // row stride of y in elements
@@ -632,8 +643,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     // Y_inter = exp(cum_i) * qC[i, :] . Hs[:, p]
 #pragma unroll
     for (int ks = 0; ks < kN / 16; ++ks) {
-      const int64_t cv = *reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 + ks * 16 + kofs);
-      const v8h a = i8x8_to_h(cv);
+      const v8h a = QC[ks];
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const v8h bv = *reinterpret_cast<const v8h*>(s.Hs + (pt * 32 + (lane & 31)) * kHsRow + ks * 16 + kofs);
