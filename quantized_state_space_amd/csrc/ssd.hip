@@ -195,6 +195,14 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
   const int n = w * 32 + (lane & 31);  // this lane's output column (state)
   const float sB = valid_or_zero(p.B_scales[g * kNSG + n / kGS]);
   const int kh = lane >> 5;
+  // fp16 path: the B codes of this lane's column as fp16 B operands, converted once for all heads
+  v8h BB[I8 ? 1 : kQ / 16];
+  if (!I8) {
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kQ / 16; ++ks)
+      BB[ks] = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qBT + n * kRow256 + ks * 16 + 8 * kh));
+  }
 
   float pf_dt, pf_sx;
   uint32_t pf_x[16];
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 #pragma unroll
       for (int ks = 0; ks < kQ / 16; ++ks) {
         const int ko = ks * 16 + 8 * kh;
-        const v8h bv = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qBT + n * kRow256 + ko));
+        const v8h bv = BB[ks];
         const v8h a0 = *reinterpret_cast<const v8h*>(s.xw + (lane & 31) * kXwRow + ko);
         const v8h a1 = *reinterpret_cast<const v8h*>(s.xw + (32 + (lane & 31)) * kXwRow + ko);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bv, acc0, 0, 0, 0);
