@@ -313,9 +313,9 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (150804017, 133339792, "141cc03f43175d53"),
+    "c3": (183269500, 133800464, "32b57a7b5f75dd3d"),
     "c2": (369686, 7472208, "1af91dec259fc264"),
-    "c4": (1041268800, 956580040, "7be46f1797dd35cb"),
+    "c4": (1038047256, 964999656, "c948989d1e789790"),
     "c5": (1100194426, 1082565320, "5c4dad04e617f92c"),
 }
 TRAFFIC_SOURCES = {
