@@ -6,7 +6,8 @@
 //   cum_i   = sum_{k<=i} delta_k A_h
 //   G       = Ch Bh^T                               int8 MFMA, int32 per state group, fp32 scales
 //   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh           fp16 MFMA, fp32 accumulate
-//   S       = sum_j w_j xh_j Bh_j^T,  w_j = delta_j e^{cum_Q - cum_j}
+//   S       = sum_j w_j xh_j Bh_j^T,  w_j = delta_j e^{cum_Q - cum_j}  (kept as F sx sB S16, S16
+//             fp16 in code units over a per-head bound that rules out overflow)
 //             fp16 MFMA over time on fp16(w_j qx) and the B codes (default), or int8 MFMA on the
 //             requantized r = sat8(RNE(qx * w_j / w_max)) (option)
 //   H_c     = exp(cum_Q) H_{c-1} + S                  fp32 state passing
@@ -71,7 +72,8 @@ struct SsdParams {
   const float* h0;
   void* y;
   float* h_last;
-  float* S;       // [B, nc, nh, P, N]: chunk states
+  _Float16* S;    // [B, nc, nh, P, N]: chunk states in code units over F, fp16 (see K1)
+  float* F;       // [B, nc, nh]: chunk state factor, S = F * sx[p] * sB[n] * S16
   float* dec;     // [B, nc, nh]: exp(cum at the last step of the chunk)
   _Float16* Hh;   // [B, nc, nh, P, N]: sC(n) * state entering the chunk, fp16 (K3's operand)
   float* sxt;     // [nh, P]: x scale of each channel, 0 where invalid (written by K1, read by K3)
@@ -149,10 +151,15 @@ __device__ __forceinline__ void fetch_head(const SsdParams& p, int64_t b, int64_
 
 // ---------------------------------------------------------------------------------------------
 // K1: chunk states, S[p][n] = sum_j w_j xh_j[p] Bh_j[n], w_j = delta_j exp(cum_last - cum_j).
-// I8 = false: fp16 operands fp16(w_j * qx[j][p]) and the exact B codes, fp32 accumulate; the x and
-//             B scales are applied in the epilogue.
+// I8 = false: fp16 operands fp16(w_j * qx[j][p]) and the exact B codes, fp32 accumulate. The
+//             accumulator is at most 127^2 sum_j w_j (times 1 + 2^-11 for the fp16 operand) in
+//             magnitude, so acc / sum_j w_j fits fp16 (|.| < 16200); it is stored so, with
+//             F = sum_j w_j.
 // I8 = true:  the weighted x is requantized per (b, chunk, head), r = sat8(RNE(qx * w_j / w_max)),
-//             int8 MFMA with int32 accumulate, epilogue w_max * sx * sB.
+//             int8 MFMA with int32 accumulate (|acc| <= 127^2 * 256); stored as fp16(acc / 256)
+//             with F = 256 w_max.
+// Either way S = F * sx[p] * sB[n] * S16 (fp16 keeps a relative precision of 2^-11; the factors
+// are applied in fp32 by K2).
 constexpr int kXwRow = 264;  // padded halves of a [*][256] fp16 LDS row (528 bytes)
 
 template <bool I8>
@@ -161,8 +168,7 @@ struct K1Smem {
   int8_t rT[I8 ? kP * kRow256 : 16];                  // requantized x, [p][j] (I8)
   _Float16 xw[I8 ? 8 : kP * kXwRow];                  // weighted x, [p][j] (fp16)
   float wv[kQ];                                       // w_j (fp16 path) or w_j / w_max (I8)
-  float sxs[kP];                                      // x scale of each channel of the head
-  float sh[8];
+  float sh[12];
 };
 
 template <bool I8>
@@ -193,7 +199,6 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
   }
 
   const int n = w * 32 + (lane & 31);  // this lane's output column (state)
-  const float sB = valid_or_zero(p.B_scales[g * kNSG + n / kGS]);
   const int kh = lane >> 5;
   // fp16 path: the B codes of this lane's column as fp16 B operands, converted once for all heads
   v8h BB[I8 ? 1 : kQ / 16];
@@ -224,9 +229,13 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
       s.wv[j] = (wmax > 0.0f) ? wj / wmax : 0.0f;
     } else {
       s.wv[j] = wj;
+      // per-wave partial sums of w_j, combined after the barrier below
+      float ws = wj;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off, 64);
+      if (lane == 0) s.sh[8 + w] = ws;
     }
     if (tid == 0) p.dec[(b * p.nc + c) * p.nh + h] = expf(cum_last);
-    if (tid < kP) s.sxs[tid] = pf_sx;
     if (b == 0 && c == 0 && tid < kP) p.sxt[h * kP + tid] = pf_sx;
     __syncthreads();
 
@@ -269,8 +278,8 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
     __syncthreads();
     if (hh + 1 < p.hpg) fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x, pf_sx);
 
-    // S[p][n] for p in two 32-row tiles; wave w owns state columns [32w, 32w + 32)
-    float* Sout = p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
+    // S16[p][n] for p in two 32-row tiles; wave w owns state columns [32w, 32w + 32)
+    _Float16* Sout = p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
     if (I8) {
       v16i acc0 = {}, acc1 = {};
 #pragma unroll
@@ -282,14 +291,12 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
         acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bv, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bv, acc1, 0, 0, 0);
       }
-      const float wsb = wmax * sB;
+      if (tid == 0) p.F[(b * p.nc + c) * p.nh + h] = 256.0f * wmax;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        const float sx0 = s.sxs[prow];
-        const float sx1 = s.sxs[32 + prow];
-        Sout[prow * kN + n] = wsb * sx0 * (float)acc0[r];
-        Sout[(32 + prow) * kN + n] = wsb * sx1 * (float)acc1[r];
+        Sout[prow * kN + n] = (_Float16)((float)acc0[r] * (1.0f / 256.0f));
+        Sout[(32 + prow) * kN + n] = (_Float16)((float)acc1[r] * (1.0f / 256.0f));
       }
     } else {
       v16f acc0 = {}, acc1 = {};
@@ -302,13 +309,14 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bv, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bv, acc1, 0, 0, 0);
       }
+      const float wsum = s.sh[8] + s.sh[9] + s.sh[10] + s.sh[11];
+      const float inv = (wsum > 0.0f) ? 1.0f / wsum : 0.0f;
+      if (tid == 0) p.F[(b * p.nc + c) * p.nh + h] = wsum;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        const float sx0 = s.sxs[prow];
-        const float sx1 = s.sxs[32 + prow];
-        Sout[prow * kN + n] = sB * sx0 * acc0[r];
-        Sout[(32 + prow) * kN + n] = sB * sx1 * acc1[r];
+        Sout[prow * kN + n] = (_Float16)(acc0[r] * inv);
+        Sout[(32 + prow) * kN + n] = (_Float16)(acc1[r] * inv);
       }
     }
     __syncthreads();
@@ -316,9 +324,10 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// K2: inter-chunk state passing, H_c = dec_c H_{c-1} + S_c in fp32. The state entering chunk c,
-// scaled by the C scale of its state group, goes to slot c of Hh in fp16: exactly the operand of
-// the inter-chunk product in K3 (which rounds it to fp16 anyway), at half the bytes.
+// K2: inter-chunk state passing, H_c = dec_c H_{c-1} + S_c in fp32, S_c = F sx[p] sB[n] S16. The
+// state entering chunk c, scaled by the C scale of its state group, goes to slot c of Hh in fp16:
+// exactly the operand of the inter-chunk product in K3 (which rounds it to fp16 anyway), at half
+// the bytes.
 __global__ __launch_bounds__(256) void k_ssd_state_pass(SsdParams p) {
   constexpr int kE4 = kP * kN / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -326,12 +335,17 @@ __global__ __launch_bounds__(256) void k_ssd_state_pass(SsdParams p) {
   const int64_t e4 = idx % kE4, bh = idx / kE4;
   const int64_t b = bh / p.nh, h = bh % p.nh;
   const int g = (int)(h / p.hpg);
-  const float sc = valid_or_zero(p.C_scales[g * kNSG + ((4 * e4) % kN) / kGS]);
+  const int sgi = g * kNSG + (int)((4 * e4) % kN) / kGS;  // the 4 states share one state group
+  const float sc = valid_or_zero(p.C_scales[sgi]);
+  const float sxb = p.sxt[h * kP + (4 * e4) / kN] * valid_or_zero(p.B_scales[sgi]);
   float4 H = p.h0 ? reinterpret_cast<const float4*>(p.h0)[bh * kE4 + e4]
                   : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t c = 0; c < p.nc; ++c) {
     const int64_t slot = ((b * p.nc + c) * p.nh + h) * (int64_t)kE4 + e4;
-    const float4 s = reinterpret_cast<const float4*>(p.S)[slot];
+    const v4h s16 = reinterpret_cast<const v4h*>(p.S)[slot];
+    const float f = p.F[(b * p.nc + c) * p.nh + h] * sxb;
+    const float4 s = make_float4(f * (float)s16[0], f * (float)s16[1], f * (float)s16[2],
+                                 f * (float)s16[3]);
     const v4h hv = {(_Float16)(sc * H.x), (_Float16)(sc * H.y), (_Float16)(sc * H.z),
                     (_Float16)(sc * H.w)};
     reinterpret_cast<v4h*>(p.Hh)[slot] = hv;
@@ -769,17 +783,18 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
 }
 
 struct WsLayout {
-  size_t s_bytes, dec_off, hh_off, sx_off, cum_off, total;
+  size_t s_bytes, f_off, dec_off, hh_off, sx_off, cum_off, total;
 };
 
-// workspace: S (fp32 chunk states), dec, Hh (fp16 entering states), sxt, cumw, each 256-byte
-// aligned
+// workspace: S16 (fp16 chunk states), F, dec, Hh (fp16 entering states), sxt, cumw, each
+// 256-byte aligned
 WsLayout ws_layout(const qssm_ssd_args* a) {
   const int64_t nc = (a->seqlen + kQ - 1) / kQ;
   const size_t elems = (size_t)a->batch * nc * a->nheads * kP * kN;
   WsLayout w;
-  w.s_bytes = elems * sizeof(float);
-  w.dec_off = (w.s_bytes + 255) & ~(size_t)255;
+  w.s_bytes = elems * sizeof(_Float16);
+  w.f_off = (w.s_bytes + 255) & ~(size_t)255;
+  w.dec_off = (w.f_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
   w.hh_off = (w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
   w.sx_off = (w.hh_off + elems * sizeof(_Float16) + 255) & ~(size_t)255;
   w.cum_off = (w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 255) & ~(size_t)255;
@@ -834,7 +849,8 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   SsdParams p{B, L, nh, nc, a->ngroups, (int32_t)(nh / a->ngroups), a->y_dtype == QSSM_F16,
               a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
-              reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + wl.dec_off),
+              reinterpret_cast<_Float16*>(base), reinterpret_cast<float*>(base + wl.f_off),
+              reinterpret_cast<float*>(base + wl.dec_off),
               reinterpret_cast<_Float16*>(base + wl.hh_off),
               reinterpret_cast<float*>(base + wl.sx_off),
               reinterpret_cast<float*>(base + wl.cum_off)};
