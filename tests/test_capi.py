@@ -107,6 +107,15 @@ def test_other_entry_point_argument_errors():
     sd = qs.SsdArgs(batch=1, seqlen=8, nheads=2, headdim=64, dstate=128, ngroups=1, chunk=256,
                     x_groups=1, bc_group_size=16, y_dtype=0)
     assert lib.qssm_ssd_chunk_int8(ctypes.byref(sd), None, 0, None) != qs.QSSM_OK
+    # y offsets are 32-bit in the output kernel: more than 2^14 heads is refused before launch
+    sd.nheads, sd.ngroups = (1 << 14) + 2, 2
+    assert lib.qssm_ssd_chunk_int8(ctypes.byref(sd), None, 0, None) == qs.QSSM_ERR_UNSUPPORTED
+    assert b"nheads" in lib.qssm_last_error()
+    # the workspace size covers the fp16 chunk states, their factors and the staged tables
+    sd.nheads, sd.ngroups, sd.seqlen, sd.batch = 4, 1, 600, 2
+    nc, nh = 3, 4
+    assert lib.qssm_ssd_workspace_size(ctypes.byref(sd)) >= (
+        2 * nc * nh * 64 * 128 * 2 * 2 + 2 * nc * nh * 4 * 2 + nh * 64 * 4 + 2 * nc * nh * 256 * 4)
 
 
 # ------------------------------------------------------------------------------------------------
