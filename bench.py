@@ -315,7 +315,7 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 TRAFFIC = {
     "c3": (183269500, 133800464, "32b57a7b5f75dd3d"),
     "c2": (369686, 7472208, "1af91dec259fc264"),
-    "c4": (1038047256, 964999656, "c948989d1e789790"),
+    "c4": (837545297, 831044048, "23d599aa12fa8b3a"),
     "c5": (1100194426, 1082565320, "5c4dad04e617f92c"),
 }
 TRAFFIC_SOURCES = {
