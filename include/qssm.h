@@ -263,8 +263,9 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* workspace, size_t 
  * state [B, nh, P, N] is read and written in place, fp32 or fp16 (state_dtype; fp16 is rounded
  * to nearest even on store, arithmetic is fp32). y: fp32 [B, nh, P].
  * xq_out [B, nh, P], Bq_out / Cq_out [B, Gbc, N] receive the codes when not NULL.
- * Supported: N = 4 * 2^k with 4 <= N <= 256 (N >= 8 for an fp16 state), (P + 2N) * 4 bytes
- * <= 64 KiB; state 16-byte aligned. Other shapes return QSSM_ERR_UNSUPPORTED.
+ * Supported: N = 4 * 2^k with 4 <= N <= 256 (N >= 8 for an fp16 state), (P rounded up to a
+ * multiple of 4, + 2N) * 4 bytes <= 64 KiB; state 16-byte aligned. Other shapes return
+ * QSSM_ERR_UNSUPPORTED.
  */
 typedef struct qssm_update_args {
   int64_t batch, nheads, headdim, dstate; /* B, nh, P, N */

@@ -45,9 +45,9 @@ template <int F16, int R>
 __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
   constexpr int CH = F16 ? 8 : 4;
   extern __shared__ float smem[];
-  float* xs = smem;          // [P]
-  float* bs = xs + p.P;      // [N]
-  float* cs = bs + p.N;      // [N]
+  float* xs = smem;                    // [P], padded to a multiple of 4
+  float* bs = xs + ((p.P + 3) & ~3);   // [N], 16-byte aligned (N % 4 == 0)
+  float* cs = bs + p.N;                // [N]
 
   const int64_t bh = blockIdx.x;  // b * nh + h
   const int64_t b = bh / p.nh, h = bh % p.nh;
@@ -106,11 +106,20 @@ __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
       s[2] = __uint_as_float(raw.z); s[3] = __uint_as_float(raw.w);
     }
     const float dtx = dt * xs[row];
+    // B and C of the CH states in 16-byte LDS reads (n0 and the N-float arrays are 4-aligned)
+    float bv[CH], cv[CH];
+#pragma unroll
+    for (int k4 = 0; k4 < CH / 4; ++k4) {
+      const float4 b4 = *reinterpret_cast<const float4*>(bs + n0 + 4 * k4);
+      const float4 c4 = *reinterpret_cast<const float4*>(cs + n0 + 4 * k4);
+      bv[4 * k4] = b4.x; bv[4 * k4 + 1] = b4.y; bv[4 * k4 + 2] = b4.z; bv[4 * k4 + 3] = b4.w;
+      cv[4 * k4] = c4.x; cv[4 * k4 + 1] = c4.y; cv[4 * k4 + 2] = c4.z; cv[4 * k4 + 3] = c4.w;
+    }
     float yp = 0.0f;
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      s[k] = fmaf(dA, s[k], dtx * bs[n0 + k]);
-      yp = fmaf(cs[n0 + k], s[k], yp);
+      s[k] = fmaf(dA, s[k], dtx * bv[k]);
+      yp = fmaf(cv[k], s[k], yp);
     }
     if (on) {
       uint4 out;
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
 
 template <int R>
 qssm_status launch_r(const UpdParams& p, int f16, hipStream_t st) {
-  const size_t smem = (size_t)(p.P + 2 * p.N) * sizeof(float);
+  const size_t smem = (size_t)(((p.P + 3) & ~3) + 2 * p.N) * sizeof(float);
   const unsigned grid = (unsigned)(p.B * p.nh);
   if (f16) {
     if constexpr (R % 2 == 0) k_state_update<1, R / 2><<<grid, kThreads, smem, st>>>(p);
@@ -166,7 +175,7 @@ extern "C" qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t 
     return fail(QSSM_ERR_UNSUPPORTED, "dstate must be 4 * 2^k with 4 <= dstate <= 256");
   if (a->state_dtype == QSSM_F16 && N < 8)
     return fail(QSSM_ERR_UNSUPPORTED, "an fp16 state needs dstate >= 8");
-  if ((P + 2 * N) * 4 > 64 * 1024) return fail(QSSM_ERR_UNSUPPORTED, "headdim too large");
+  if ((((P + 3) & ~3) + 2 * N) * 4 > 64 * 1024) return fail(QSSM_ERR_UNSUPPORTED, "headdim too large");
   if (B == 0) return QSSM_OK;
   if (!a->x || !a->x_group_of || !a->x_scales || !a->B || !a->C || !a->B_scales || !a->C_scales ||
       !a->delta || !a->A || !a->state || !a->y)
