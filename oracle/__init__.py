@@ -389,9 +389,10 @@ def decode_step(xh, Bh, Ch, delta, A, state, Dskip=None):
 
 def rowwise_error(y, ref, axis=-1):
     """Per-row normwise error: max|y - r| / max(max|r|, 1e-6 * max_all|r|) along `axis`.
-    Returns the array of per-row errors."""
-    y = np.asarray(y, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
+    Complex inputs (the S4D state) use the modulus. Returns the array of per-row errors."""
+    dt = np.complex128 if (np.iscomplexobj(y) or np.iscomplexobj(ref)) else np.float64
+    y = np.asarray(y, dtype=dt)
+    ref = np.asarray(ref, dtype=dt)
     floor = 1e-6 * max(np.abs(ref).max(initial=0.0), 1e-300)
     num = np.abs(y - ref).max(axis=axis)
     den = np.maximum(np.abs(ref).max(axis=axis), floor)

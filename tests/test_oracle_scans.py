@@ -317,3 +317,18 @@ def test_decode_zero_delta():
     np.testing.assert_array_equal(st, st0)
     np.testing.assert_allclose(y, np.einsum("bhpn,bn->bhp", st0, Cm[:, 0]) + D[None, :, None] * x,
                                rtol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------------
+# the per-row error measure used by every parity test
+
+def test_rowwise_error_measure():
+    # max |y - r| over the row divided by max |r| of the row
+    assert np.allclose(oracle.rowwise_error([[1.0, 2.0], [3.0, 5.0]], [[1.0, 4.0], [3.0, 4.0]]),
+                       [0.5, 0.25])
+    # complex rows (the S4D state) are measured by the modulus: an error in the imaginary part
+    # alone counts in full
+    assert np.allclose(oracle.rowwise_error([[1.0 + 1.0j, 0.0]], [[1.0 + 0.0j, 0.0]]), [1.0])
+    assert np.allclose(oracle.rowwise_error([[3.0 + 4.0j]], [[0.0 + 0.0j]], axis=-1) > 1e6, [True])
+    # an all-zero reference row is floored at 1e-6 of the largest reference value
+    assert np.allclose(oracle.rowwise_error([[1e-3], [2.0]], [[0.0], [2.0]]), [500.0, 0.0])
