@@ -22,6 +22,7 @@ using namespace qssm;
 namespace {
 
 constexpr int kBlk = 64;  // time steps per readout block
+constexpr int kRed = kBlk + 4;  // padded row of the readout transpose (16-byte rows, no conflicts)
 
 struct S4dParams {
   int64_t B, L, H, N;
@@ -55,7 +56,7 @@ __device__ __forceinline__ void s4d_block(int nt, const float* __restrict__ ub, 
                                           float (&ai)[NPL], float (&br)[NPL], float (&bi)[NPL],
                                           float (&cr)[NPL], float (&ci)[NPL], float (&hr)[NPL],
                                           float (&hi)[NPL], float ss, float sinv,
-                                          float (*red)[kBlk + 1], int lane) {
+                                          float (*red)[kRed], int lane) {
   auto step = [&](int t) {
     const float q = ub[t];
     float yp = 0.0f;
@@ -90,7 +91,7 @@ __device__ __forceinline__ void s4d_block(int nt, const float* __restrict__ ub, 
 
 template <int NPL, int I16>
 __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
-  __shared__ float red[4][kBlk][kBlk + 1];
+  __shared__ __align__(16) float red[4][kBlk][kRed];
   __shared__ __align__(16) float ubuf[4][kBlk];
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -204,9 +205,18 @@ __global__ __launch_bounds__(256) void k_s4d(S4dParams p) {
     }
     __syncthreads();
     if (lane < nt) {
-      float sum = 0.0f;
-#pragma unroll 16
-      for (int j = 0; j < 64; ++j) sum += red[w][lane][j];
+      // row `lane` holds the 64 lanes' partials of step tb + lane: 16-byte reads, four sums
+      const float4* row = reinterpret_cast<const float4*>(&red[w][lane][0]);
+      float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+      for (int j4 = 0; j4 < kBlk / 4; ++j4) {
+        const float4 v = row[j4];
+        s0 += v.x;
+        s1 += v.y;
+        s2 += v.z;
+        s3 += v.w;
+      }
+      const float sum = (s0 + s1) + (s2 + s3);
       if (active) p.y[(b * p.H + hh) * L + tb + lane] = fmaf(Dd * us, q_lane, sum);
     }
     __syncthreads();
