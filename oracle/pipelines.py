@@ -196,17 +196,22 @@ def s4d_state_scale(inp, headroom=1.25, with_h0=False):
 # SSD
 
 def ssd(inp, chunk=256, gs=16, groups_per_block=8, with_h0=False, heads=None, int8_state=False,
-        exact=False):
+        exact=False, calib=None):
     """Oracle SSD layer. heads: optional subset of head indices (the recurrence of each head is
     independent; B/C groups follow the head). int8_state selects the requantized int8 chunk state;
-    exact=True runs the plain sequential scan instead of the chunked form. Returns codes, scales and
-    fp64 y / h_last (for the selected heads: y [B, L, len(heads), P])."""
+    exact=True runs the plain sequential scan instead of the chunked form. calib: optional
+    (group_of, xs, bs, cs) used instead of the calibration from inp (tests set scales outside the
+    valid range this way). Returns codes, scales and fp64 y / h_last (for the selected heads:
+    y [B, L, len(heads), P])."""
     x = inp["x"]
     B, L, nh, P = x.shape
     Gbc, N = inp["B"].shape[2], inp["B"].shape[3]
-    group_of, xs = calib_ssd_x(inp["x_cal"], nh, P, Gbc, groups_per_block)
-    bs = state_group_scales(np.moveaxis(inp["B_cal"], 1, -1), gs)
-    cs = state_group_scales(np.moveaxis(inp["C_cal"], 1, -1), gs)
+    if calib is None:
+        group_of, xs = calib_ssd_x(inp["x_cal"], nh, P, Gbc, groups_per_block)
+        bs = state_group_scales(np.moveaxis(inp["B_cal"], 1, -1), gs)
+        cs = state_group_scales(np.moveaxis(inp["C_cal"], 1, -1), gs)
+    else:
+        group_of, xs, bs, cs = calib
     xq = quant_group_x(x.reshape(B * L, nh * P, 1), group_of, xs).reshape(x.shape)
     Bq = quant_state_group(inp["B"].reshape(B * L, Gbc, N, 1), gs, bs).reshape(inp["B"].shape)
     Cq = quant_state_group(inp["C"].reshape(B * L, Gbc, N, 1), gs, cs).reshape(inp["C"].shape)

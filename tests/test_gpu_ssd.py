@@ -109,6 +109,28 @@ def test_ssd_int8_state_generic(dev):
     check(lay, ref, tol=1e-2, tol_h=None)
 
 
+def test_ssd_invalid_scales_one_head_per_group(dev):
+    """One head per B/C group (the head loops run once), and scales outside [2^-100, 2^100]: an x
+    group (its channels then carry only the inter-chunk state and no D term), a B state group and a
+    C state group contribute zeros. The oracle takes the same scales."""
+    import torch
+    print("\n[ssd invalid scales, one head per group]", flush=True)
+    inp = synth.ssd_inputs(cfg=47, batch=2, seqlen=300, nheads=3, headdim=64, dstate=128,
+                           ngroups=3, calib_len=256, with_h0=True)
+    import quantized_state_space_amd.workloads as wl
+    lay = wl.SsdLayer(inp, dev, with_h0=True)
+    xs, bs, cs = (t.cpu().numpy().copy() for t in (lay.xs, lay.bs, lay.cs))
+    xs[2] = 0.0
+    bs[5] = np.float32(1e-35)
+    cs[9] = np.float32(2.0 ** 101)
+    for t, v in ((lay.xs, xs), (lay.bs, bs), (lay.cs, cs)):
+        t.copy_(torch.from_numpy(v))
+    lay.step()
+    torch.cuda.synchronize()
+    ref = op.ssd(inp, with_h0=True, calib=(lay.group_of, xs, bs, cs))
+    check(lay, ref)
+
+
 def test_ssd_bad_state_mma(dev):
     import quantized_state_space_amd as qs
     inp = synth.ssd_inputs(cfg=46, batch=1, seqlen=64, nheads=4, headdim=64, dstate=128, ngroups=2,
