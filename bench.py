@@ -314,9 +314,9 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
     "c3": (183269500, 133800464, "32b57a7b5f75dd3d"),
-    "c2": (369686, 7472208, "1af91dec259fc264"),
+    "c2": (375062, 7472128, "a34de708f6ebadea"),
     "c4": (837545297, 831044048, "23d599aa12fa8b3a"),
-    "c5": (1100194426, 1082565320, "5c4dad04e617f92c"),
+    "c5": (1100171354, 1082578296, "9519b8cd5a6cb5ec"),
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"], "c2": ["s4d.hip"],
