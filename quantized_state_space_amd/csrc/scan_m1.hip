@@ -111,6 +111,13 @@ template <int NS, int W, int XCODE, int YF16, int kBatch, int PFD, bool CODE16>
 __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   __shared__ float ybuf[2][W][kT][kLanes];
   constexpr int kS = CODE16 ? NS : 2 * NS;  // staged 32-bit words per step
+  // Soft-edge codes: instead of every wave decoding every step, wave w decodes steps
+  // [w kT/W, (w+1) kT/W) of the next block and shares them through LDS (per lane 16 values in a
+  // row padded to 20 floats: conflict-free 16-byte accesses); the per-block barrier orders it.
+  constexpr bool kShareX = XCODE == QSSM_X_SOFTEDGE;
+  constexpr int kXdRow = 20;
+  constexpr int kPerX = kT / W;
+  __shared__ __align__(16) float xd[kShareX ? 2 : 1][kShareX ? kLanes : 1][kShareX ? kXdRow : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -230,6 +237,26 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   load_block(0, dl, xq);
   sload(0, bcur);
   int buf = 0;
+  // decoded x units of the next block, this wave's share, into LDS buffer nb
+  auto share_x = [&](const uint32_t (&codes)[kT / 4], int nb) {
+    if (kShareX) {
+      float v[kPerX];
+#pragma unroll
+      for (int j = 0; j < kPerX; ++j) {
+        const int t = w * kPerX + j;  // w is wave-uniform: a runtime register index is avoided
+        uint32_t word = 0u;            // by selecting the word with uniform compares
+#pragma unroll
+        for (int k = 0; k < kT / 4; ++k) word = (t / 4 == k) ? codes[k] : word;
+        v[j] = xunit<XCODE>((word & xmask) >> (8 * (t % 4)));
+      }
+#pragma unroll
+      for (int j = 0; j < kPerX; ++j) xd[nb][lane][w * kPerX + j] = v[j];
+    }
+  };
+  if (kShareX) {
+    share_x(xq, 0);
+    __syncthreads();
+  }
   // exp(delta A) of the next two steps, by step parity
   float dAr[2][NS];
 #pragma unroll
@@ -252,6 +279,14 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       constexpr int kLines = (kT * kS * 4 + 127) / 128;
       if (tp < L && lane < kLines) pf = stg[tp * kS + lane * 32];
     }
+    float xcur[kShareX ? kT : 1];  // this block's decoded x units (soft-edge)
+    if (kShareX) {
+#pragma unroll
+      for (int k = 0; k < kT / 4; ++k) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&xd[buf][lane][4 * k]);
+        xcur[4 * k] = v4.x; xcur[4 * k + 1] = v4.y; xcur[4 * k + 2] = v4.z; xcur[4 * k + 3] = v4.w;
+      }
+    }
 
 #pragma unroll
     for (int bt = 0; bt < kT; bt += kBatch) {
@@ -261,7 +296,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       for (int s2 = 0; s2 < kBatch; ++s2) {
         const int t = bt + s2;
         const float dt = dl[t];
-        const float u = dt * xunit<XCODE>(xq[t / 4] >> (8 * (t % 4)));
+        const float u = dt * (kShareX ? xcur[kShareX ? t : 0] : xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))));
         float dA[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) dA[k] = dAr[t % 2][k];
@@ -286,6 +321,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
         for (int j = 0; j < kS; ++j) bcur[s2][j] = bnxt[s2][j];
     }
     if (PFD > 0) asm volatile("" ::"v"(pf));
+    if (kShareX && tb + kT < L) share_x(xn, buf ^ 1);
     __syncthreads();
 
     // combine: wave w finalizes steps [w*kT/W, (w+1)*kT/W) of every channel of the block
@@ -298,7 +334,8 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 #pragma unroll
       for (int ww = 0; ww < W; ++ww)
         sum = fmaf(cf[ww], ybuf[buf][ww][t][lane], sum);
-      yo[j] = fmaf(Dsx, xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))), sum);
+      const float xu = kShareX ? xd[buf][lane][kShareX ? t : 0] : xunit<XCODE>(xq[t / 4] >> (8 * (t % 4)));
+      yo[j] = fmaf(Dsx, xu, sum);
     }
     const int64_t t0 = tb + w * kPer;
     if (valid) {
