@@ -6,19 +6,20 @@
 //   cum_i   = sum_{k<=i} delta_k A_h
 //   G       = Ch Bh^T                               int8 MFMA, int32 per state group, fp32 scales
 //   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh           fp16 MFMA, fp32 accumulate
-//   S       = sum_j w_j xh_j Bh_j^T,  w_j = delta_j e^{cum_Q - cum_j}  (kept as F sx sB S16, S16
-//             fp16 in code units over a per-head bound that rules out overflow)
+//   S       = sum_j w_j xh_j Bh_j^T,  w_j = delta_j e^{cum_Q - cum_j}
 //             fp16 MFMA over time on fp16(w_j qx) and the B codes (default), or int8 MFMA on the
-//             requantized r = sat8(RNE(qx * w_j / w_max)) (option)
+//             requantized r = sat8(RNE(qx * w_j / w_max)) (option); kept as F sx sB S16, S16 in
+//             fp16, code units over a per-head bound that rules out overflow
 //   H_c     = exp(cum_Q) H_{c-1} + S                  fp32 state passing
 //   Y_inter = exp(cum_i) Ch . H_{c-1}^T               fp16 MFMA
 //   y       = Y_intra + Y_inter + D_h xh
 //
 // Three kernels (the chunk states make one round trip through the workspace):
-//   K1 k_ssd_chunk_state  one workgroup per (b, chunk, B/C group): B chunk transposed in LDS once,
-//                         then per head the weighted x tile and a 64x128x256 MFMA product.
-//   K2 k_ssd_state_pass   per (b, h) state element: sequential over chunks, replaces each chunk
-//                         state by the state entering that chunk.
+//   K1 k_ssd_chunk_state  one workgroup per (b, chunk, B/C group): B chunk transposed once into
+//                         fp16 operands held in registers, then per head the chunk's cumsum
+//                         (also written out for K3), the weighted x tile and a 64x128x256 MFMA.
+//   K2 k_ssd_state_pass   per (b, h) state element: sequential over chunks, writes the state
+//                         entering each chunk (fp16, C-scaled) and the final state.
 //   K3 k_ssd_output       one workgroup per (b, chunk, B/C group): G^T is built once with int8 MFMA
 //                         and kept in registers (8 waves, one query block of causal 32x32 tiles
 //                         each, two waves per SIMD); per head the inter-chunk product, the
