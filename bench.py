@@ -313,7 +313,7 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (183269500, 133800464, "32b57a7b5f75dd3d"),
+    "c3": (151247333, 132492472, "47a81748e88a908b"),
     "c2": (375062, 7472128, "54d40f6eb5529519"),
     "c4": (837545297, 831044048, "0df0a3fb4b8a3fed"),
     "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
