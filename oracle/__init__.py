@@ -260,16 +260,24 @@ def softedge_decode_f32(code, group_of, s):
 # ------------------------------------------------------------------------------------------------
 # Dequantization (exact in fp64: an fp32 scale times an 8-bit integer)
 
+def _usable_scales(scales):
+    """fp64 scales, an invalid one (outside [2^-100, 2^100], or NaN) taken as 0: every value of
+    its group is 0 (its codes are 0, and 0 * inf would be NaN)."""
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    ok = (s >= 2.0 ** -100) & (s <= 2.0 ** 100)
+    return np.where(ok, s, 0.0)
+
+
 def dequant_group(q, group_of, scales):
     """q [outer, C, inner] -> fp64 values scale[group_of[c]] * q."""
-    s = np.asarray(scales, dtype=np.float32).astype(np.float64)[np.asarray(group_of)]
+    s = _usable_scales(scales)[np.asarray(group_of)]
     return s[None, :, None] * np.asarray(q, dtype=np.float64)
 
 
 def dequant_state_group(q, gs, scales):
     """q [outer, Gbc, N, inner] -> fp64 values."""
     outer, Gbc, N, inner = q.shape
-    s = np.asarray(scales, dtype=np.float32).astype(np.float64).reshape(Gbc, N // gs)
+    s = _usable_scales(scales).reshape(Gbc, N // gs)
     s = np.repeat(s, gs, axis=1)
     return s[None, :, :, None] * np.asarray(q, dtype=np.float64)
 

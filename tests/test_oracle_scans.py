@@ -119,6 +119,23 @@ def test_integer_codes_with_unit_scales_are_the_unquantized_scan():
     np.testing.assert_array_equal(ya, yb)
 
 
+def test_invalid_scale_groups_dequantize_to_zero():
+    """A group whose scale is outside [2^-100, 2^100] (or NaN) holds codes 0 and values 0 (not
+    0 * inf = NaN); the range ends themselves are valid."""
+    q = np.full((1, 6, 3), 5, np.int8)
+    scales = np.array([np.inf, np.nan, 2.0 ** 101, 1e-35, 2.0 ** -100, 2.0 ** 100], np.float32)
+    v = oracle.dequant_group(q, np.arange(6, dtype=np.uint8), scales)
+    np.testing.assert_array_equal(v[0, :4], 0.0)
+    np.testing.assert_array_equal(v[0, 4], 5 * 2.0 ** -100)
+    np.testing.assert_array_equal(v[0, 5], 5 * 2.0 ** 100)
+    x = np.full((1, 6, 3), 3.0, np.float32)
+    assert not oracle.quant_group_x(x, np.arange(6, dtype=np.uint8), scales)[0, :4].any()
+    qb = np.full((1, 1, 4, 2), -7, np.int8)
+    vb = oracle.dequant_state_group(qb, 2, np.array([np.inf, 0.5], np.float32))
+    np.testing.assert_array_equal(vb[0, 0, :2], 0.0)
+    np.testing.assert_array_equal(vb[0, 0, 2:], -3.5)
+
+
 # ------------------------------------------------------------------------------------------------
 # S4D
 
