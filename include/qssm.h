@@ -135,6 +135,8 @@ qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, 
  * Per (b, d, n), t = 0 .. L-1, with xh = dequantized x, Bh/Ch = dequantized B/C:
  *     h = exp(delta * A[d,n]) * h + delta * Bh[n,t] * xh,   y[t] = sum_n Ch[n,t] * h + Dskip[d] * xh
  * h starts from h0 (zero when NULL); h_last receives the final state when not NULL.
+ * seqlen == 0 is valid: x, delta, Bq, Cq and y are then not accessed (they may be NULL) and
+ * h_last receives h0 (or zeros).
  * The state and all arithmetic are fp32. y is fp32 or fp16 (y_dtype).
  * Workspace: qssm_scan_workspace_size bytes (dequantized B and C staging).
  */
@@ -179,7 +181,8 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* workspace, size_t work
  * State: QSSM_F32 keeps complex fp32; QSSM_I16 rounds each real and imaginary part to
  *   state_scale[h] * clamp(RNE(part / state_scale[h]), -32768, 32767) after every step.
  * h0 / h_last: [B, H, N] complex, interleaved (re, im): float pairs (F32) or int16 code pairs (I16).
- * y: fp32 [B, H, L].
+ * y: fp32 [B, H, L]. seqlen == 0 is valid: uq and y are then not accessed (they may be NULL) and
+ * h_last receives h0 (or zeros).
  */
 typedef struct qssm_s4d_args {
   int64_t batch, seqlen, channels, dstate; /* B, L, H, N */
@@ -220,6 +223,8 @@ qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
  *   inter-chunk state passing in fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;
  *   y = Y_intra + Y_inter + Dskip * xh.
  * Requires chunk == 256, P == 64, N == 128, gs == 16 in this build (else QSSM_ERR_UNSUPPORTED).
+ * seqlen == 0 is valid: xq, delta, Bq, Cq and y are then not accessed (they may be NULL) and
+ * h_last receives h0 (or zeros).
  */
 enum { QSSM_MMA_F16 = 0, QSSM_MMA_I8 = 1 };
 

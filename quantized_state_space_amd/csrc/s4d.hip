@@ -265,7 +265,8 @@ extern "C" qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream)
   if (a->state_dtype == QSSM_I16 && !a->state_scale)
     return fail(QSSM_ERR_INVALID_ARG, "QSSM_I16 needs state_scale");
   if (a->batch == 0) return QSSM_OK;
-  if (!a->uq || !a->u_scale || (a->wq && !a->w_scale) || !a->A_re || !a->A_im || !a->B_re ||
+  // the input and output sequences are not touched when seqlen == 0 and may then be null
+  if ((a->seqlen > 0 && !a->uq) || !a->u_scale || (a->wq && !a->w_scale) || !a->A_re || !a->A_im || !a->B_re ||
       !a->B_im || !a->C_re || !a->C_im || !a->A_re_s || !a->A_im_s || !a->B_re_s || !a->B_im_s ||
       !a->C_re_s || !a->C_im_s || !a->log_dt || (a->seqlen > 0 && !a->y))
     return fail(QSSM_ERR_INVALID_ARG, "null required pointer");

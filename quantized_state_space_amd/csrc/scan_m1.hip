@@ -432,8 +432,9 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
   if (N != 4 && N != 8 && N != 16 && N != 32 && N != 64)
     return fail(QSSM_ERR_UNSUPPORTED, "dstate must be 4, 8, 16, 32 or 64");
   if (B == 0) return QSSM_OK;
-  if (!a->x || !a->x_group_of || !a->x_scales || !a->delta || !a->A || !a->Bq || !a->Cq ||
-      !a->B_scales || !a->C_scales || !a->y)
+  // the per-step buffers are not touched when L == 0 and may then be null
+  if (!a->x_group_of || !a->x_scales || !a->A || !a->B_scales || !a->C_scales ||
+      (L > 0 && (!a->x || !a->delta || !a->Bq || !a->Cq || !a->y)))
     return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
   if (((uintptr_t)a->x | (uintptr_t)a->delta | (uintptr_t)a->y) % 16 != 0)
     return fail(QSSM_ERR_INVALID_ARG, "x, delta and y must be 16-byte aligned");

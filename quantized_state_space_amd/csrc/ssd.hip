@@ -835,8 +835,9 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   if (L > ((int64_t)1 << 40)) return fail(QSSM_ERR_UNSUPPORTED, "seqlen too large");
   if (nh > (1 << 14)) return fail(QSSM_ERR_UNSUPPORTED, "nheads too large");
   if (B == 0) return QSSM_OK;
-  if (!a->xq || !a->x_group_of || !a->x_scales || !a->delta || !a->A || !a->Bq || !a->Cq ||
-      !a->B_scales || !a->C_scales || !a->y)
+  // the per-step buffers are not touched when L == 0 and may then be null
+  if (!a->x_group_of || !a->x_scales || !a->A || !a->B_scales || !a->C_scales ||
+      (L > 0 && (!a->xq || !a->delta || !a->Bq || !a->Cq || !a->y)))
     return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
   if (((uintptr_t)a->xq | (uintptr_t)a->Bq | (uintptr_t)a->Cq) % 16 != 0 ||
       (a->h0 && (uintptr_t)a->h0 % 16 != 0) || (a->h_last && (uintptr_t)a->h_last % 16 != 0))

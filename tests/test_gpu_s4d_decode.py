@@ -165,3 +165,20 @@ def test_decode_full_size_sampled(dev):
             assert np.array_equal(got[name][k][sample], ref[name][k]), (name, k)
         assert_rows_close(got["y"][k], ref["y"][k], 2e-3)
     assert_rows_close(got["state"], ref["state"], 2e-3, "state")
+
+
+def test_s4d_empty_sequence(dev):
+    """L = 0: no input read, no output written, h_last = h0 (through the kernel's state form)."""
+    import torch
+    import quantized_state_space_amd as qs
+    print("\n[s4d L=0]", flush=True)
+    inp = synth.s4d_inputs(cfg=2, with_h0=True, batch=3, seqlen=8, channels=5, dstate=64)
+    lay = s4d_layer(dev, inp, with_h0=True)
+    B, L, H, N = lay.shape
+    hl = torch.full_like(lay.h_last, float("nan"))
+    a = qs.s4d_args(torch.empty((B, 1, 0), dtype=torch.int8, device=dev), lay.u_scale, lay.params,
+                    lay.scales, lay.log_dt, torch.empty((B, H, 0), device=dev), wq=lay.wq.view(H),
+                    w_scale=lay.w_scale, Dskip=lay.D, h0=lay.h0, h_last=hl)
+    qs.qssm_s4d_scan(a)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(hl, lay.h0, rtol=1e-5, atol=1e-6)

@@ -167,3 +167,25 @@ def test_c3_full_size_sampled(dev, soft):
     h = lay.h_last.cpu().numpy()[bsel, dsel]
     assert_rows_close(y, ref["y_rows"], TOL_F32)
     assert_rows_close(h, ref["h_rows"], TOL_F32, "h_last")
+
+
+def test_empty_sequence(dev):
+    """L = 0: nothing is read or written per step (those buffers are empty), h_last = h0."""
+    import torch
+    import quantized_state_space_amd as qs
+    print("\n[mamba1 L=0]", flush=True)
+    B, D, N = 2, 96, 16
+    g = torch.Generator().manual_seed(5)
+    A = (-torch.rand((D, N), generator=g) - 0.1).to(dev)
+    h0 = torch.randn((B, D, N), generator=g).to(dev)
+    h_last = torch.full((B, D, N), float("nan"), device=dev)
+    e8 = torch.empty((B, D, 0), dtype=torch.int8, device=dev)
+    ebc = torch.empty((B, 1, N, 0), dtype=torch.int8, device=dev)
+    one = torch.ones(N // 4, device=dev)
+    a = qs.scan_args(e8, qs.QSSM_X_INT8, torch.zeros(D, dtype=torch.uint8, device=dev),
+                     torch.ones(1, device=dev), torch.empty((B, D, 0), device=dev), A, ebc, ebc,
+                     one, one, 4, torch.empty((B, D, 0), device=dev), h0=h0, h_last=h_last)
+    ws = torch.empty(qs.qssm_scan_workspace_size(a), dtype=torch.uint8, device=dev)
+    qs.qssm_scan_w8a8(a, ws)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(h_last, h0, rtol=1e-6, atol=0)

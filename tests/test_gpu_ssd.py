@@ -171,3 +171,24 @@ def test_ssd_full_size_sampled_heads(dev):
     heads = np.array([0, 37, 127])
     ref = op.ssd(inp, heads=heads)
     check(lay, ref, heads=heads)
+
+
+def test_ssd_empty_sequence(dev):
+    """L = 0: no chunk, nothing read or written per step, h_last = h0 exactly."""
+    import torch
+    import quantized_state_space_amd as qs
+    print("\n[ssd L=0]", flush=True)
+    B, nh, P, N, Gbc = 2, 16, 64, 128, 2
+    g = torch.Generator().manual_seed(6)
+    h0 = torch.randn((B, nh, P, N), generator=g).to(dev)
+    h_last = torch.full_like(h0, float("nan"))
+    xq = torch.empty((B, 0, nh, P), dtype=torch.int8, device=dev)
+    bc = torch.empty((B, 0, Gbc, N), dtype=torch.int8, device=dev)
+    sc = torch.ones(Gbc * N // 16, device=dev)
+    a = qs.ssd_args(xq, torch.zeros(nh * P, dtype=torch.uint8, device=dev), torch.ones(1, device=dev),
+                    torch.empty((B, 0, nh), device=dev), -torch.ones(nh, device=dev), bc, bc, sc, sc,
+                    16, 256, torch.empty((B, 0, nh, P), device=dev), h0=h0, h_last=h_last)
+    ws = torch.empty(max(qs.qssm_ssd_workspace_size(a), 1), dtype=torch.uint8, device=dev)
+    qs.qssm_ssd_chunk_int8(a, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h_last, h0)
