@@ -9,6 +9,8 @@
 // are staged in LDS when they fit.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 using namespace qssm;
@@ -71,33 +73,10 @@ struct Chunk {
   int n;
 };
 
-// ROWS and CHANNELS: the chunk at element e sits at in-row index i, channel c, outer index o
-// (tracked incrementally by the caller).
-template <int MAP, int LAYOUT>
-__device__ __forceinline__ void load_chunk(const Geometry& g, const float* __restrict__ x,
-                                           int64_t e, int64_t i, int64_t c, int64_t o,
-                                           Chunk<MAP, LAYOUT>& ch) {
-  if (LAYOUT == L_ROWS) {
-    const int64_t src = (MAP == MAP_GROUP && g.perm) ? g.perm[c] : c;
-    ch.si[0] = scale_index<MAP>(g, c);
-    ch.v = *reinterpret_cast<const f32x4*>(x + (o * g.C + src) * g.inner + i);
-    ch.n = 4;
-    return;
-  }
-  if (LAYOUT == L_CHANNELS) {
-    const int64_t c0 = c;
-    if (MAP == MAP_GROUP) {
-      const uint32_t gid = *reinterpret_cast<const uint32_t*>(g.group_of + c0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ch.si[k % (Chunk<MAP, LAYOUT>::kUniform ? 1 : 4)] = (int)((gid >> (8 * k)) & 0xFFu);
-    } else {
-      ch.si[0] = scale_index<MAP>(g, c0);
-    }
-    ch.v = *reinterpret_cast<const f32x4*>(x + e);
-    ch.n = 4;
-    return;
-  }
-}
+// ROWS and CHANNELS are loaded in phases, so that a thread's loads of all its chunks are in
+// flight together instead of one chunk's index load, wait, value load, and so on: first the index
+// loads of every chunk (permutation entry, group map entry or word; the channel c of a chunk is
+// always in range, so they need no guard), then the value loads, then the group ids are unpacked.
 
 // GENERIC: element by element from e.
 template <int MAP, int LAYOUT>
@@ -171,18 +150,6 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
   __shared__ float2 s_LH[OP == OP_SOFTEDGE && LDS ? kMaxLdsGroups : 1];
   __shared__ unsigned s_max[OP == OP_ABSMAX && LDS ? kMaxLdsGroups : 1];
   constexpr bool lds = LDS;  // the launch picks LDS when g.nscales <= kMaxLdsGroups
-  if (lds) {
-    for (int k = threadIdx.x; k < g.nscales; k += kThreads) {
-      if (OP == OP_ABSMAX) {
-        s_max[k] = 0u;
-      } else {
-        const float sc = scales[k];
-        s_sr[k] = make_float2(sc, recip_or_zero(sc));
-      }
-      if (OP == OP_SOFTEDGE) s_LH[k] = make_float2(Lth[k], Hth[k]);
-    }
-    __syncthreads();
-  }
   auto scale_of = [&](int si) -> float2 {
     if (lds) return s_sr[si];
     const float sc = scales[si];
@@ -205,26 +172,70 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
     po = div_fast(row, g.C);
     pc = row - po * g.C;
   }
+  int64_t off[kChunks];    // element offset of each chunk's values
+  int64_t src[kChunks];    // ROWS: source channel of each chunk
+  uint32_t gidw[kChunks];  // CHANNELS with a group map: the 4 group ids of each chunk
+  // index phase, branch-free (the permutation test is hoisted: one copy of the loop per case)
+  auto index_phase = [&](auto use_perm) {
 #pragma unroll
-  for (int k = 0; k < kChunks; ++k) {
-    e[k] = (int64_t)blockIdx.x * kBlockElems + ((int64_t)k * kThreads + threadIdx.x) * 4;
-    if (kStepped) {
-      if (e[k] < g.total) load_chunk<MAP, LAYOUT>(g, x, e[k], pi, pc, po, ch[k]);
+    for (int k = 0; k < kChunks; ++k) {
+      e[k] = (int64_t)blockIdx.x * kBlockElems + ((int64_t)k * kThreads + threadIdx.x) * 4;
+      ch[k].n = 4;
+      if (LAYOUT == L_ROWS) {
+        src[k] = decltype(use_perm)::value ? (int64_t)g.perm[pc] : pc;
+        ch[k].si[0] = scale_index<MAP>(g, pc);
+        off[k] = po * g.C * g.inner + pi;  // plus src * inner once the index has arrived
+      } else {
+        if (MAP == MAP_GROUP) gidw[k] = *reinterpret_cast<const uint32_t*>(g.group_of + pc);
+        else ch[k].si[0] = scale_index<MAP>(g, pc);
+        off[k] = e[k];
+      }
       pi += g.step_i;
-      int64_t cc = pc + g.step_c;
-      if (pi >= g.inner) {
-        pi -= g.inner;
-        ++cc;
-      }
-      if (cc >= g.C) {
-        cc -= g.C;
-        ++po;
-      }
-      pc = cc;
-      po += g.step_o;
-    } else if (e[k] < g.total) {
-      load_chunk<MAP, LAYOUT>(g, x, e[k], ch[k]);
+      const bool wrap_i = pi >= g.inner;
+      pi = wrap_i ? pi - g.inner : pi;
+      const int64_t cc = pc + g.step_c + (wrap_i ? 1 : 0);
+      const bool wrap_c = cc >= g.C;
+      pc = wrap_c ? cc - g.C : cc;
+      po += g.step_o + (wrap_c ? 1 : 0);
     }
+  };
+  if (kStepped) {
+    if (LAYOUT == L_ROWS && MAP == MAP_GROUP && g.perm) index_phase(std::true_type{});
+    else index_phase(std::false_type{});
+  } else {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      e[k] = (int64_t)blockIdx.x * kBlockElems + ((int64_t)k * kThreads + threadIdx.x) * 4;
+      if (e[k] < g.total) load_chunk<MAP, LAYOUT>(g, x, e[k], ch[k]);
+    }
+  }
+  if (kStepped) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      if (LAYOUT == L_ROWS) off[k] += src[k] * g.inner;
+      if (e[k] < g.total) ch[k].v = *reinterpret_cast<const f32x4*>(x + off[k]);
+    }
+    if (LAYOUT == L_CHANNELS && MAP == MAP_GROUP) {
+#pragma unroll
+      for (int k = 0; k < kChunks; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ch[k].si[j % (Chunk<MAP, LAYOUT>::kUniform ? 1 : 4)] = (int)((gidw[k] >> (8 * j)) & 0xFFu);
+    }
+  }
+  // The per-group scales are staged after the chunk loads are issued, so that the two memory
+  // latencies overlap instead of adding up.
+  if (lds) {
+    for (int k = threadIdx.x; k < g.nscales; k += kThreads) {
+      if (OP == OP_ABSMAX) {
+        s_max[k] = 0u;
+      } else {
+        const float sc = scales[k];
+        s_sr[k] = make_float2(sc, recip_or_zero(sc));
+      }
+      if (OP == OP_SOFTEDGE) s_LH[k] = make_float2(Lth[k], Hth[k]);
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int k = 0; k < kChunks; ++k) {
