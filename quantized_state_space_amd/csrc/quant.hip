@@ -4,7 +4,7 @@
 // channels; B and C with one scale per state group. Quamba-SE blog (2.1, 2.2): three-scale byte.
 //
 // These are HBM-bound elementwise passes (4 bytes in, 1 byte out per element). Each thread handles
-// four chunks of 4 consecutive elements a block-width apart (16-byte loads, 4-byte stores, every
+// two chunks of 4 consecutive elements a block-width apart (16-byte loads, 4-byte stores, every
 // wave instruction one contiguous run). The per-group scales (and soft-edge thresholds) of a launch
 // are staged in LDS when they fit.
 #include <hip/hip_runtime.h>
@@ -18,7 +18,7 @@ using namespace qssm;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunks = 4;        // chunks of 4 elements per thread
+constexpr int kChunks = 2;        // chunks of 4 elements per thread
 constexpr int kBlockElems = kThreads * kChunks * 4;
 constexpr int kMaxLdsGroups = 1024;
 constexpr int kDecVec = 16;       // elements per thread of the soft-edge decoder
@@ -27,7 +27,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Op { OP_QUANT = 0, OP_ABSMAX = 1, OP_SOFTEDGE = 2 };
 enum Map { MAP_GROUP = 0, MAP_STATE = 1 };
-// Work split: thread t of block x handles chunks k = 0..3 of 4 consecutive elements at
+// Work split: thread t of block x handles chunks k = 0..kChunks-1 of 4 consecutive elements at
 // e = x * kBlockElems + (k * kThreads + t) * 4, so that every load and store instruction of a
 // wave covers one contiguous run (64 lanes x 16 bytes in, x 4 bytes out).
 // ROWS: inner % 4 == 0, a chunk lies in one channel row (one scale).
