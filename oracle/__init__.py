@@ -11,9 +11,8 @@ Sources (page title, section):
   SSDi8 abstract: the chunked SSD form with an INT8 path.
   Quamba-SE soft-edge blog, sections 2.1, 2.2 and 4.1: three-scale code, byte layout, thresholds.
 
-Parity status of each function is listed in the design doc; every function here is pinned by a test in
-``tests/test_oracle_*.py`` except the int8 chunk state of the SSD form away from its exact special
-case ("parity unpinned" there, see ``ssd_chunked``).
+Every function here is pinned by a test in ``tests/test_oracle_*.py`` against something other
+than itself (closed forms, special cases, brute force, library routines, error bounds).
 """
 from __future__ import annotations
 
@@ -340,8 +339,9 @@ def ssd_chunked(xh, delta, A, Bh, Ch, chunk, Dskip=None, h0=None, int8_state=Fal
                 sx=None):
     """Mamba2 SSD chunked form in fp64. xh [B, L, nh, P]; delta [B, L, nh]; A [nh];
     Bh, Ch [B, L, Gbc, N]; h0 [B, nh, P, N]. int8_state=True selects the requantized chunk state
-    (needs the codes qx [B, L, nh, P] and per-channel scales sx [nh*P]); that mode is exact only in
-    its special case (integral weighted codes) and is otherwise "parity unpinned".
+    (needs the codes qx [B, L, nh, P] and per-channel scales sx [nh*P]); that mode is exact in its
+    special case (integral weighted codes) and otherwise pinned by its requantization error bound
+    and the absence of rounding bias.
     Returns (y [B, L, nh, P], h_last [B, nh, P, N])."""
     xh = _c(xh, np.float64)
     Bsz, L, nh, P = xh.shape

@@ -300,6 +300,75 @@ def test_ssd_int8_state_error_is_small_generic():
     assert np.abs(y1 - y0).max() < 0.05 * np.abs(y0).max()
 
 
+@pytest.mark.parametrize("L,chunk", [(40, 64), (64, 16)])
+def test_ssd_int8_state_within_its_requantization_bound(L, chunk):
+    """Generic pin of the int8 chunk state. Since |qx| <= 128 and w_j <= w_max, qx*w_j/w_max lies
+    in [-128, 127]: the saturation never acts and each requantized code r = RNE(qx*w_j/w_max) is
+    within 1/2 of it, so per chunk
+        |S_int8[p,n] - S_exact[p,n]| <= sx[p] * w_max / 2 * sum_j |B_j[n]|,
+    and over chunks the state error is that chunk bound carried by the chunk decays. The bound is
+    computed here from the method's definitions (cumsum, weights, decays) with h0 = 0, and the
+    error must also reach a sizeable fraction of it (an exact or over-smoothed state would not)."""
+    r = np.random.default_rng(17)
+    p = ssd_small(seed=17, L=L, P=6, N=7, h0=False)
+    B, _, nh, P = p["xh"].shape
+    Gbc, N = p["Bh"].shape[2], p["Bh"].shape[3]
+    sx = r.uniform(0.005, 0.05, nh * P)
+    qx = r.integers(-128, 128, (B, L, nh, P)).astype(np.int8)
+    p["xh"] = qx * sx.reshape(nh, P)
+    _, h_exact = oracle.ssd_chunked(chunk=chunk, **p)
+    _, h_int8 = oracle.ssd_chunked(chunk=chunk, int8_state=True, qx=qx, sx=sx, **p)
+    hpg = nh // Gbc
+    worst = 0.0
+    for b, h in itertools.product(range(B), range(nh)):
+        g = h // hpg
+        bound = np.zeros((P, N))
+        for t0 in range(0, L, chunk):
+            dt = p["delta"][b, t0:t0 + chunk, h]
+            cum = np.cumsum(dt * p["A"][h])
+            w = dt * np.exp(cum[-1] - cum)
+            absB = np.abs(p["Bh"][b, t0:t0 + chunk, g, :]).sum(axis=0)
+            chunk_bound = sx[h * P:(h + 1) * P, None] * (w.max() / 2) * absB[None, :]
+            bound = np.exp(cum[-1]) * bound + chunk_bound
+        err = np.abs(h_int8[b, h] - h_exact[b, h])
+        assert np.all(err <= bound * (1 + 1e-9) + 1e-15), (b, h)
+        worst = max(worst, (err / bound).max())
+    assert worst > 0.05
+
+
+def test_ssd_int8_state_rounding_is_unbiased():
+    """Round-to-nearest-even of the requantized codes has no bias: with B >= 0 and x codes >= 0
+    every rounding error enters the chunk state with the same sign of weight, so a floor, ceiling
+    or truncation would move
+    the state by about the whole bound of the test above in one direction, while RNE errors
+    average out (the mean signed error stays a small fraction of the mean bound)."""
+    r = np.random.default_rng(18)
+    p = ssd_small(seed=18, L=64, P=6, N=7, h0=False)
+    B, L, nh, P = p["xh"].shape
+    p["Bh"] = np.abs(p["Bh"])
+    # weak decay and delta in [0.3, 0.6]: every w_j / w_max lies in about [0.5, 1], so the
+    # fractional parts of the scaled codes spread evenly (small weights would all round to 0,
+    # a one-sided error of the method itself, not of its rounding rule)
+    p["A"] = np.full(nh, -0.01)
+    p["delta"] = r.uniform(0.3, 0.6, (B, L, nh))
+    sx = r.uniform(0.005, 0.05, nh * P)
+    qx = r.integers(0, 128, (B, L, nh, P)).astype(np.int8)  # one sign: truncation is biased too
+    p["xh"] = qx * sx.reshape(nh, P)
+    _, h_exact = oracle.ssd_chunked(chunk=L, **p)
+    _, h_int8 = oracle.ssd_chunked(chunk=L, int8_state=True, qx=qx, sx=sx, **p)
+    Gbc = p["Bh"].shape[2]
+    signed, bounds = [], []
+    for b, h in itertools.product(range(B), range(nh)):
+        dt = p["delta"][b, :, h]
+        cum = np.cumsum(dt * p["A"][h])
+        w = dt * np.exp(cum[-1] - cum)
+        absB = p["Bh"][b, :, h // (nh // Gbc), :].sum(axis=0)
+        bounds.append(sx[h * P:(h + 1) * P, None] * (w.max() / 2) * absB[None, :])
+        signed.append(h_int8[b, h] - h_exact[b, h])
+    ratio = np.mean(signed) / np.mean(bounds)
+    assert abs(ratio) < 0.2, ratio
+
+
 # ------------------------------------------------------------------------------------------------
 # Decode
 
