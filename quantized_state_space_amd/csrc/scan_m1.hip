@@ -228,15 +228,14 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     return __uint_as_float(row[NS + k]);
   };
 
-  float dl[kT], dn[kT];
-  uint32_t xq[kT / 4], xn[kT / 4];
+  float dlA[kT], dlB[kT];
+  uint32_t xqA[kT / 4], xqB[kT / 4];
 #pragma unroll
-  for (int k = 0; k < kT; ++k) dn[k] = 0.0f;
+  for (int k = 0; k < kT; ++k) dlB[k] = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kT / 4; ++k) xn[k] = 0u;
-  load_block(0, dl, xq);
+  for (int k = 0; k < kT / 4; ++k) xqB[k] = 0u;
+  load_block(0, dlA, xqA);
   sload(0, bcur);
-  int buf = 0;
   // decoded x units of the next block, this wave's share, into LDS buffer nb
   auto share_x = [&](const uint32_t (&codes)[kT / 4], int nb) {
     if (kShareX) {
@@ -254,17 +253,21 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     }
   };
   if (kShareX) {
-    share_x(xq, 0);
+    share_x(xqA, 0);
     __syncthreads();
   }
   // exp(delta A) of the next two steps, by step parity
   float dAr[2][NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    dAr[0][k] = __builtin_amdgcn_exp2f(dl[0] * a2[k]);
-    dAr[1][k] = __builtin_amdgcn_exp2f(dl[1] * a2[k]);
+    dAr[0][k] = __builtin_amdgcn_exp2f(dlA[0] * a2[k]);
+    dAr[1][k] = __builtin_amdgcn_exp2f(dlA[1] * a2[k]);
   }
-  for (int64_t tb = 0; tb < L; tb += kT) {
+  // One block of kT steps: dl/xq hold this block's delta and x codes, dn/xn receive the next
+  // block's; buf selects the LDS buffers. The block loop is unrolled twice with the two register
+  // sets swapping roles, so that no copy of the next block's values is needed between blocks.
+  auto block = [&](int64_t tb, float (&dl)[kT], float (&dn)[kT], uint32_t (&xq)[kT / 4],
+                   uint32_t (&xn)[kT / 4], const int buf) {
     // (masking the codes of the current block here, not at load time, keeps the next block's
     // loads in flight during this block's arithmetic)
 #pragma unroll
@@ -358,11 +361,10 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
         }
       }
     }
-    buf ^= 1;
-#pragma unroll
-    for (int k = 0; k < kT; ++k) dl[k] = dn[k];
-#pragma unroll
-    for (int k = 0; k < kT / 4; ++k) xq[k] = xn[k];
+  };
+  for (int64_t tb = 0; tb < L; tb += 2 * kT) {
+    block(tb, dlA, dlB, xqA, xqB, 0);
+    if (tb + kT < L) block(tb + kT, dlB, dlA, xqB, xqA, 1);
   }
 
   if (valid && p.h_last) {
