@@ -313,7 +313,7 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (152353703, 133335320, "82afc0b17bc5bcc1"),
+    "c3": (152494307, 133467016, "d0c881c42d987e32"),
     "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
     "c4": (837572496, 831044408, "ee0b45599748a4ba"),
     "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
