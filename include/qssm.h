@@ -36,7 +36,8 @@
  *     q = clamp(RNE(v / s), -128, 127)
  *  where v / s is the exact rational quotient of the fp32 values and RNE rounds half to even.
  *  NaN encodes as 0; +-Inf saturate. A scale s is valid when it is finite and
- *  2^-100 <= s <= 2^100; every code of a group whose scale is not valid is 0.
+ *  2^-100 <= s <= 2^100; every code of a group whose scale is not valid is 0, and the scans
+ *  take every value of such a group (x, B or C) as 0.
  */
 #ifndef QSSM_H
 #define QSSM_H
