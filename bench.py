@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # fp32 VALU issue rate of MI355X without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 # (lane-instructions per second; an FMA counts once). The recurrences' instruction mix (an exp per
-# update, dependent FMAs) has no packed form in this build.
+# update, dependent FMAs) is compiled without packed fp32 instructions.
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "quantized scan state-updates/s (B·L·D·N) + % of HBM peak, 1 MI355X"
 
@@ -315,7 +315,7 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 TRAFFIC = {
     "c3": (152494307, 133467016, "d0c881c42d987e32"),
     "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
-    "c4": (837572496, 831044408, "ee0b45599748a4ba"),
+    "c4": (837572496, 831044408, "b5ebe2e3b0c0020a"),
     "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
 }
 TRAFFIC_SOURCES = {
@@ -438,8 +438,8 @@ def main():
         print(sources_digest(args.workload))
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the sharding plan is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; "
+              "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

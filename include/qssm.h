@@ -56,7 +56,7 @@ typedef int32_t qssm_status;
 enum {
   QSSM_OK = 0,
   QSSM_ERR_INVALID_ARG = 1, /* null required pointer, bad shape, bad enum value */
-  QSSM_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
+  QSSM_ERR_UNSUPPORTED = 2, /* a valid request this library version does not implement */
   QSSM_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than *_workspace_size */
   QSSM_ERR_DEVICE = 4       /* the HIP runtime reported an error at launch */
 };
@@ -223,7 +223,7 @@ qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
  *   the rounding of r is a floating-point decision inside the contraction);
  *   inter-chunk state passing in fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;
  *   y = Y_intra + Y_inter + Dskip * xh.
- * Requires chunk == 256, P == 64, N == 128, gs == 16 in this build (else QSSM_ERR_UNSUPPORTED).
+ * Requires chunk == 256, P == 64, N == 128, gs == 16 in this version (else QSSM_ERR_UNSUPPORTED).
  * seqlen == 0 is valid: xq, delta, Bq, Cq and y are then not accessed (they may be NULL) and
  * h_last receives h0 (or zeros).
  */

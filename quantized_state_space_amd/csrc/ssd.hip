@@ -831,7 +831,7 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
     return fail(QSSM_ERR_INVALID_ARG, "state_mma must be QSSM_MMA_F16 or QSSM_MMA_I8");
   if (a->chunk != kQ || a->headdim != kP || a->dstate != kN || a->bc_group_size != kGS)
     return fail(QSSM_ERR_UNSUPPORTED,
-                "this build implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
+                "the library implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
   if (L > ((int64_t)1 << 40)) return fail(QSSM_ERR_UNSUPPORTED, "seqlen too large");
   if (nh > (1 << 14)) return fail(QSSM_ERR_UNSUPPORTED, "nheads too large");
   if (B == 0) return QSSM_OK;
