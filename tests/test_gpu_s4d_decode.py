@@ -32,10 +32,13 @@ def check_s4d_codes(lay, ref):
         assert np.array_equal(lay.scales[k].cpu().numpy(), ref["scales"][k]), k
 
 
+# dstate covers the three lane layouts (up to 64, 128 and 256 states: 1, 2 or 4 per lane)
 @pytest.mark.parametrize("shape", [dict(batch=16, seqlen=784, channels=128, dstate=64),
                                    dict(batch=3, seqlen=130, channels=5, dstate=64),
                                    dict(batch=2, seqlen=65, channels=4, dstate=100),
-                                   dict(batch=1, seqlen=64, channels=3, dstate=17)])
+                                   dict(batch=1, seqlen=64, channels=3, dstate=17),
+                                   dict(batch=2, seqlen=97, channels=3, dstate=200),
+                                   dict(batch=1, seqlen=70, channels=2, dstate=256)])
 def test_s4d_fp32_state(dev, shape):
     import torch
     print(f"\n[s4d fp32 {shape}]", flush=True)
@@ -50,10 +53,12 @@ def test_s4d_fp32_state(dev, shape):
     assert_rows_close(hl[..., 0] + 1j * hl[..., 1], ref["h_last"], 2e-3, "h_last")
 
 
-def test_s4d_int16_state(dev):
+@pytest.mark.parametrize("shape", [dict(), dict(batch=2, seqlen=150, channels=3, dstate=100),
+                                   dict(batch=2, seqlen=90, channels=2, dstate=256)])
+def test_s4d_int16_state(dev, shape):
     import torch
-    print("\n[s4d int16 state, full size]", flush=True)
-    inp = synth.s4d_inputs(cfg=2, with_h0=True)
+    print(f"\n[s4d int16 state {shape or 'full size'}]", flush=True)
+    inp = synth.s4d_inputs(cfg=2, with_h0=True, **shape)
     ss = op.s4d_state_scale(inp, with_h0=True)
     from quantized_state_space_amd import QSSM_I16
     lay = s4d_layer(dev, inp, state_dtype=QSSM_I16, state_scale=ss, with_h0=True)
@@ -91,10 +96,10 @@ def test_s4d_int16_state(dev):
 # ------------------------------------------------------------------------------------------------
 # Decode
 
-def decode_run(dev, params, steps, state_dtype, sample=None, groups_per_block=8):
+def decode_run(dev, params, steps, state_dtype, sample=None, groups_per_block=8, gs=16):
     import torch
     import quantized_state_space_amd.workloads as wl
-    lay = wl.DecodeLayer(params, dev, state_dtype=state_dtype, emit_codes=True,
+    lay = wl.DecodeLayer(params, dev, gs=gs, state_dtype=state_dtype, emit_codes=True,
                          groups_per_block=groups_per_block)
     got = dict(xq=[], Bq=[], Cq=[], y=[])
     sel = slice(None) if sample is None else sample
@@ -145,6 +150,29 @@ def test_decode_other_shapes(dev):
             assert np.array_equal(got[name][k], ref[name][k]), (name, k)
         assert_rows_close(got["y"][k], ref["y"][k], 2e-3)
     assert_rows_close(got["state"], ref["state"], 2e-3, "state")
+
+
+# every state size the kernel has a lane layout for (R = N / 4 lanes per state row; fp16 from N = 8)
+@pytest.mark.parametrize("N,state", [(4, "f32"), (8, "f32"), (8, "f16"), (32, "f32"), (32, "f16"),
+                                     (64, "f16"), (256, "f32"), (256, "f16")])
+def test_decode_state_sizes(dev, N, state):
+    import quantized_state_space_amd as qs
+    print(f"\n[decode N={N} {state}]", flush=True)
+    dims = dict(batch=3, nheads=4, headdim=33, dstate=N, ngroups=2)
+    params = synth.decode_params(cfg=17, **dims)
+    steps = [synth.decode_step_inputs(k, cfg=17, **dims) for k in range(3)]
+    sd = qs.QSSM_F32 if state == "f32" else qs.QSSM_F16
+    if sd == qs.QSSM_F16:
+        params["state0"] = params["state0"].astype(np.float16).astype(np.float32)
+    gs = min(N, 16)  # B/C state-group size
+    lay, got = decode_run(dev, params, steps, sd, groups_per_block=2, gs=gs)
+    ref = op.decode(params, steps, gs=gs, groups_per_block=2)
+    tol = 2e-3 if state == "f32" else 1e-2
+    for k in range(len(steps)):
+        for name in ("xq", "Bq", "Cq"):
+            assert np.array_equal(got[name][k], ref[name][k]), (name, k)
+        assert_rows_close(got["y"][k], ref["y"][k], tol)
+    assert_rows_close(got["state"], ref["state"], tol, "state")
 
 
 def test_decode_full_size_sampled(dev):
