@@ -474,7 +474,8 @@ def main():
             others[name] = {"workload": w2.config["workload"], "value": r2["value"],
                             "ms_per_step": r2["ms_per_step"],
                             "roofline": {k: r2["roofline"][k] for k in
-                                         ("bound", "achieved", "peak", "unit", "frac", "kernel_us")}}
+                                         ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                          "kernel_us")}}
             del w2
             torch.cuda.empty_cache()
         out["other_configs"] = others
