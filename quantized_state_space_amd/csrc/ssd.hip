@@ -46,6 +46,7 @@ constexpr int kRow128 = 136;  // padded bytes of a [*][128] int8 LDS row
 constexpr int kXtRow = 260;   // padded halves of a [*][256] fp16 LDS row (520 bytes)
 constexpr int kHsRow = 136;   // padded halves of a [*][128] fp16 LDS row (272 bytes)
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
+constexpr int kYPolicy = 2;  // cache policy of the y stores: nontemporal (streaming)
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued through the builtin, not
 // inline asm, so that the compiler's wait insertion sees the direct LDS loads completed and does not
 // add a vmcnt(0) of its own at the next LDS barrier (which would also wait for the y stores).
@@ -316,8 +317,8 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        Sout[prow * kN + n] = (_Float16)(acc0[r] * inv);
-        Sout[(32 + prow) * kN + n] = (_Float16)(acc1[r] * inv);
+        __builtin_nontemporal_store((_Float16)(acc0[r] * inv), &Sout[prow * kN + n]);
+        __builtin_nontemporal_store((_Float16)(acc1[r] * inv), &Sout[(32 + prow) * kN + n]);
       }
     }
     __syncthreads();
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
           for (int r = 0; r < 16; ++r) {
             const int ir = I * 32 + 8 * (r / 4) + (r % 4);
             __builtin_amdgcn_raw_buffer_store_b16(
-                __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), 0);
+                __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), kYPolicy);
           }
         } else {
 #pragma unroll
@@ -758,7 +759,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
             const int ir = I * 32 + 8 * (r / 4) + (r % 4);
             if (ir + ilane < q)
               __builtin_amdgcn_raw_buffer_store_b16(
-                  __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), 0);
+                  __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), kYPolicy);
           }
         }
       } else {
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
           for (int r = 0; r < 16; ++r) {
             const int ir = I * 32 + 8 * (r / 4) + (r % 4);
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
-                                                  uniform(ir * rs * 4), 0);
+                                                  uniform(ir * rs * 4), kYPolicy);
           }
         } else {
 #pragma unroll
@@ -775,7 +776,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
             const int ir = I * 32 + 8 * (r / 4) + (r % 4);
             if (ir + ilane < q)
               __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
-                                                    uniform(ir * rs * 4), 0);
+                                                    uniform(ir * rs * 4), kYPolicy);
           }
         }
       }
