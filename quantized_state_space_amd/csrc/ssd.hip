@@ -25,6 +25,8 @@
 //                         each, two waves per SIMD); per head the inter-chunk product, the
 //                         intra-chunk product and the D term, with the next head's inputs
 //                         arriving in LDS by direct loads meanwhile.
+// The chunk states (K1) and y (K3) are written with nontemporal stores: they stream past the
+// caches instead of evicting staged inputs or leaving dirty lines for the next kernel.
 // MFMA lane layouts (verified on gfx950): operand lane l holds row/column l%32 and a run of
 // consecutive k at offset (K/2)*(l/32); the 32x32 accumulator register r of lane l is element
 // (8*(r/4) + 4*(l/32) + r%4, l%32).
@@ -297,8 +299,9 @@ __global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        Sout[prow * kN + n] = (_Float16)((float)acc0[r] * (1.0f / 256.0f));
-        Sout[(32 + prow) * kN + n] = (_Float16)((float)acc1[r] * (1.0f / 256.0f));
+        __builtin_nontemporal_store((_Float16)((float)acc0[r] * (1.0f / 256.0f)), &Sout[prow * kN + n]);
+        __builtin_nontemporal_store((_Float16)((float)acc1[r] * (1.0f / 256.0f)),
+                                    &Sout[(32 + prow) * kN + n]);
       }
     } else {
       v16f acc0 = {}, acc1 = {};
