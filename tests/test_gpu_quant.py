@@ -34,6 +34,7 @@ CASES = [  # (outer, C, inner, G, with_perm)
     (16, 8192, 1, 64, False),   # SSD-shaped x (channel axis contiguous)
     (5, 129, 1, 7, True),       # channel axis contiguous with a gather
     (1, 1, 17, 1, False),
+    (2, 600, 12, 256, True),    # the largest group count
 ]
 
 
@@ -83,8 +84,10 @@ def test_quant_empty_tensor(dev):
     assert s.cpu().tolist() == [1.0, 1.0]
 
 
+# (the last two have more scales than the LDS table holds: the scales are read from memory)
 @pytest.mark.parametrize("outer,Gbc,N,inner,gs", [(1, 1, 16, 256, 4), (2, 8, 128, 1, 16),
-                                                  (3, 2, 12, 33, 3), (64, 8, 128, 1, 128)])
+                                                  (3, 2, 12, 33, 3), (64, 8, 128, 1, 128),
+                                                  (2, 16, 128, 8, 1), (3, 9, 256, 1, 2)])
 def test_quant_state_group_bit_exact(dev, outer, Gbc, N, inner, gs):
     import torch
     import quantized_state_space_amd as qs
