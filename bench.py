@@ -315,7 +315,7 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Ti
 TRAFFIC = {
     "c3": (152494307, 133467016, "d0c881c42d987e32"),
     "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
-    "c4": (692105038, 858799064, "77fcd1dd1e985b19"),
+    "c4": (692105038, 858799064, "1771bfe3189ad294"),
     "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
 }
 TRAFFIC_SOURCES = {

@@ -32,6 +32,8 @@
 // (8*(r/4) + 4*(l/32) + r%4, l%32).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "common.hpp"
 
 using namespace qssm;
@@ -787,6 +789,23 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   }
 }
 
+// The dynamic-LDS limit of a kernel is raised once per device (hipFuncSetAttribute applies on the
+// current device; two threads racing both make the same idempotent call).
+constexpr int kMaxDevices = 64;
+enum { kAttrK1F16 = 0, kAttrK1I8 = 1, kAttrK3 = 2 };
+std::atomic<bool> g_lds_raised[3][kMaxDevices];
+
+bool raise_lds_limit(int which, const void* fn, size_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && g_lds_raised[which][dev].load(std::memory_order_acquire)) return true;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+    return false;
+  if (cached) g_lds_raised[which][dev].store(true, std::memory_order_release);
+  return true;
+}
+
 struct WsLayout {
   size_t s_bytes, f_off, dec_off, hh_off, sx_off, cum_off, total;
 };
@@ -864,17 +883,12 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
   const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
   if (nc > 0) {
-    static bool lds1_raised[2] = {false, false};
     const int i8 = a->state_mma == QSSM_MMA_I8;
     const void* k1 = i8 ? reinterpret_cast<const void*>(&k_ssd_chunk_state<true>)
                         : reinterpret_cast<const void*>(&k_ssd_chunk_state<false>);
     const size_t k1_lds = i8 ? sizeof(K1Smem<true>) : sizeof(K1Smem<false>);
-    if (!lds1_raised[i8]) {
-      if (hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)k1_lds) !=
-          hipSuccess)
-        return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD chunk-state kernel");
-      lds1_raised[i8] = true;
-    }
+    if (!raise_lds_limit(i8 ? kAttrK1I8 : kAttrK1F16, k1, k1_lds))
+      return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD chunk-state kernel");
     if (i8) k_ssd_chunk_state<true><<<grid, 256, k1_lds, stream>>>(p);
     else k_ssd_chunk_state<false><<<grid, 256, k1_lds, stream>>>(p);
     if (qssm_status s = launch_status("ssd chunk state")) return s;
@@ -882,14 +896,8 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   k_ssd_state_pass<<<(unsigned)cdiv(B * nh * (kP * kN / 4), 256), 256, 0, stream>>>(p);
   if (qssm_status s = launch_status("ssd state passing")) return s;
   if (nc > 0) {
-    static bool lds_raised = false;  // per process; the attribute is per kernel function
-    if (!lds_raised) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ssd_output),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sizeof(K3Smem)) != hipSuccess)
-        return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD output kernel");
-      lds_raised = true;
-    }
+    if (!raise_lds_limit(kAttrK3, reinterpret_cast<const void*>(&k_ssd_output), sizeof(K3Smem)))
+      return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD output kernel");
     k_ssd_output<<<grid, 512, sizeof(K3Smem), stream>>>(p);
     if (qssm_status s = launch_status("ssd output")) return s;
   }
