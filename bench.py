@@ -476,7 +476,7 @@ def main():
         for name in ("c2", "c3se", "c4", "c5", "c5f16"):
             if name == args.workload:
                 continue
-            w2, r2 = run_workload(torch, dev, name, min(args.steps, 10), min(args.warmup, 2))
+            w2, r2 = run_workload(torch, dev, name, min(args.steps, 30), min(args.warmup, 3))
             others[name] = {"workload": w2.config["workload"], "value": r2["value"],
                             "ms_per_step": r2["ms_per_step"],
                             "roofline": {k: r2["roofline"][k] for k in
