@@ -189,3 +189,18 @@ def test_empty_sequence(dev):
     qs.qssm_scan_w8a8(a, ws)
     torch.cuda.synchronize()
     torch.testing.assert_close(h_last, h0, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("D,N,Gbc", [(256, 16, 4), (128, 8, 2), (192, 32, 3)])
+def test_several_bc_groups(dev, D, N, Gbc):
+    """B and C with several groups, each shared by D / Gbc consecutive channels (multiples of 64:
+    one workgroup's channels share one group). Scales from the tensors themselves, channels in
+    their original order (a cluster permutation would have to stay inside each B/C group)."""
+    print(f"\n[mamba1 D={D} N={N} Gbc={Gbc}]", flush=True)
+    inp = synth.mamba1_inputs(cfg=24, batch=2, seqlen=200, dim=D, dstate=N, bc_groups=Gbc)
+    lay = layer(dev, inp, G=2, gs=4 if N >= 4 else N, dynamic_scales=True, perm=False)
+    lay.step()
+    ref = op.mamba1(inp, G=2, gs=4 if N >= 4 else N, dynamic=True)
+    check_codes(lay, ref)
+    assert_rows_close(lay.y.cpu().numpy(), ref["y"], TOL_F32)
+    assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
