@@ -75,6 +75,11 @@ class Mamba1Layer:
         x = inp["x"]
         B, D, L = x.shape
         Gbc, N = inp["B"].shape[1], inp["B"].shape[2]
+        if Gbc > 1 and not (dynamic_scales and not perm):
+            # the cluster permutation is over all channels; with several B/C groups it would move
+            # channels out of their group
+            raise ValueError("several B/C groups need channels in their original order "
+                             "(dynamic_scales=True, perm=False)")
         self.shape = (B, D, L, N, Gbc)
         if dynamic_scales:
             self.perm = np.arange(D, dtype=np.int32)
