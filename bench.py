@@ -317,6 +317,9 @@ TRAFFIC = {
     "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
     "c4": (692105038, 858799064, "1771bfe3189ad294"),
     "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
+    "c3se": (154302738, 133851528, "d0c881c42d987e32"),
+    "c4f16": (683357980, 694246608, "1771bfe3189ad294"),
+    "c5f16": (563235239, 545288304, "2d61ee22651a7256"),
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"], "c2": ["s4d.hip"],
