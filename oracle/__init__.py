@@ -8,7 +8,8 @@ Sources (page title, section):
   Quamba2 (Chiang et al.), abstract and method steps 1-4: per-group x scales over sorted and
     clustered channels, per-state-group B/C scales, offline rearrangement, W8A8 recurrence.
   "Quantizing Small-Scale State-Space Models for Edge AI", abstract: the quantized S4D layer.
-  SSDi8 abstract: the chunked SSD form with an INT8 path.
+  SSDi8 abstract: the chunked SSD form with an INT8 path, persistent int8 outputs and a
+    per-channel error-correction term.
   Quamba-SE soft-edge blog, sections 2.1, 2.2 and 4.1: three-scale code, byte layout, thresholds.
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py`` against something other
@@ -390,6 +391,31 @@ def decode_step(xh, Bh, Ch, delta, A, state, Dskip=None):
                               _ptr(_c(delta, np.float64)), _ptr(_c(A, np.float64)),
                               _ptr(_c(Dskip, np.float64)), _ptr(state), _ptr(y))
     return y
+
+
+# ------------------------------------------------------------------------------------------------
+# Persistent int8 output (SSDi8 abstract: the layer hands the next W8A8 module int8 activations,
+# and an error-correction term from per-channel error statistics)
+
+def requant_output(y, group_of, scales, bias=None):
+    """Int8 codes of a layer output y [outer, C, inner] for the next W8A8 module: the per-channel
+    correction bias[c] is added, then channel c is quantized with scales[group_of[c]] by the
+    int8 rule (exact quotient, round half to even, saturation, an invalid scale gives 0).
+    The decision is taken in fp32, the precision the output is produced in: v = fl32(fl32(y) +
+    bias[c]), then the exact quotient v / s."""
+    y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
+    outer, C, inner = y32.shape
+    b = np.zeros(C, np.float32) if bias is None else np.asarray(bias, dtype=np.float32)
+    v = (y32 + b[None, :, None]).astype(np.float32)
+    s = np.asarray(scales, dtype=np.float32)[np.asarray(group_of, dtype=np.int64)]
+    return quant_code(v, np.broadcast_to(s[None, :, None], v.shape))
+
+
+def channel_error_mean(ref, approx):
+    """Per-channel error statistic of a quantized path: mean over outer and inner of ref - approx,
+    for [outer, C, inner] arrays, accumulated in fp64 (the correction term's calibration)."""
+    d = np.asarray(ref, dtype=np.float64) - np.asarray(approx, dtype=np.float64)
+    return d.mean(axis=(0, 2))
 
 
 # ------------------------------------------------------------------------------------------------
