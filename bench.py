@@ -1,6 +1,6 @@
 """Benchmark of the quantized state-space hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c1|c2|c4|c4f16|c5|c5f16]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c3i8y|c1|c2|c4|c4f16|c5|c5f16]
                 [--only] [--no-cpu-baseline]
 
 One step = one pass of the whole hot path of the workload over one batch of synthetic input that is
@@ -55,9 +55,11 @@ class Mamba1(Workload):
     # and readout)
     ops_per_update = 5
 
-    def __init__(self, soft_edge=False):
+    def __init__(self, soft_edge=False, y_int8=False):
         self.soft = soft_edge
-        self.name = "mamba1-130m-layer-w8a8" + ("-softedge-x" if soft_edge else "")
+        self.y_int8 = y_int8
+        self.name = ("mamba1-130m-layer-w8a8" + ("-softedge-x" if soft_edge else "") +
+                     ("-int8-y" if y_int8 else ""))
         self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
         self.bound = "alu"
 
@@ -69,13 +71,31 @@ class Mamba1(Workload):
         xc = qs.QSSM_X_SOFTEDGE if self.soft else qs.QSSM_X_INT8
         # two copies of every buffer, used in turn, so that one step's 350 MB of traffic cannot be
         # served from the previous step's lines in the 256 MB last-level cache
-        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc) for _ in range(2)]
+        y_out = None
+        if self.y_int8:
+            # int8 output for the next W8A8 module: 8 clustered output groups calibrated on one
+            # fp32-output pass, and a seeded per-channel correction term (~1% of a channel's range)
+            import numpy as np
+            import torch
+            cal = wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc)
+            cal.step()
+            y = cal.y.cpu().numpy()
+            del cal
+            torch.cuda.empty_cache()
+            yg, ys = wl.calib_y_groups(y, 8)
+            ch = qs.qssm_calib_channel_absmax(y)
+            yb = (synth.rng(3, 12).standard_normal(ch.size) * 0.01 * ch).astype(np.float32)
+            y_out = (yg, ys, yb)
+        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc, y_out=y_out)
+                       for _ in range(2)]
         self.k = 0
         B, D, L, N, Gbc = self.layers[0].shape
         self.dims = (B, D, L, N, Gbc)
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
                        "x_groups": 8, "x_code": "soft-edge 3-scale u8" if self.soft else "int8",
-                       "bc_state_groups": N // 4, "state": "f32", "y": "f32"}
+                       "bc_state_groups": N // 4, "state": "f32",
+                       "y": "int8, 8 output groups + per-channel correction" if self.y_int8
+                       else "f32"}
 
     def step(self, timer):
         lay = self.layers[self.k % len(self.layers)]
@@ -94,8 +114,12 @@ class Mamba1(Workload):
 
     def dominant_bytes(self):
         B, D, L, N, Gbc = self.dims
-        # x codes, delta, B/C codes, A, D in; y and h_last out (each once)
-        return B * D * L * (1 + 4 + 4) + 2 * B * Gbc * N * L + 4 * D * N + 4 * D + 4 * B * D * N
+        # x codes, delta, B/C codes, A, D in; y and h_last out (each once); an int8 y adds the
+        # output groups, scales and correction terms
+        yb = 1 if self.y_int8 else 4
+        extra = (D + 4 * 8 + 4 * D) if self.y_int8 else 0
+        return (B * D * L * (1 + 4 + yb) + 2 * B * Gbc * N * L + 4 * D * N + 4 * D + 4 * B * D * N
+                + extra)
 
     def cpu_baseline(self):
         import oracle.pipelines as op
@@ -300,7 +324,8 @@ def _zero(device):
     return _zc[k]
 
 
-WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True), "c1": Tiny,
+WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True),
+             "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
              "c2": lambda: S4d(False), "c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
              "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True)}
@@ -322,7 +347,8 @@ TRAFFIC = {
     "c5f16": (563235239, 545288304, "2d61ee22651a7256"),
 }
 TRAFFIC_SOURCES = {
-    "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"], "c2": ["s4d.hip"],
+    "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
+    "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"],
     "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c5": ["state_update.hip"],
     "c5f16": ["state_update.hip"],
 }
@@ -476,7 +502,7 @@ def main():
     if args.all_configs:
         # the other configurations of the same metric, briefly (same protocol, fewer steps)
         others = {}
-        for name in ("c2", "c3se", "c4", "c5", "c5f16"):
+        for name in ("c2", "c3se", "c3i8y", "c4", "c5", "c5f16"):
             if name == args.workload:
                 continue
             w2, r2 = run_workload(torch, dev, name, min(args.steps, 30), min(args.warmup, 3))

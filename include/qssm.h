@@ -62,7 +62,7 @@ enum {
 };
 
 /* Element types of optional-precision buffers. */
-enum { QSSM_F32 = 0, QSSM_F16 = 1, QSSM_I16 = 2 };
+enum { QSSM_F32 = 0, QSSM_F16 = 1, QSSM_I16 = 2, QSSM_I8 = 3 };
 
 /* Encodings of the scan input x. */
 enum {
@@ -138,7 +138,15 @@ qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, 
  * h starts from h0 (zero when NULL); h_last receives the final state when not NULL.
  * seqlen == 0 is valid: x, delta, Bq, Cq and y are then not accessed (they may be NULL) and
  * h_last receives h0 (or zeros).
- * The state and all arithmetic are fp32. y is fp32 or fp16 (y_dtype).
+ * The state and all arithmetic are fp32. y is fp32 or fp16 (y_dtype), or int8 codes for the
+ * next W8A8 module (QSSM_I8; SSDi8, abstract: a persistent int8 path, and an error-correction
+ * term from per-channel error statistics):
+ *     y_code[b,d,t] = clamp(RNE(v / s), -128, 127),  v = fl32(y[b,d,t] + y_bias[d]),
+ *     s = y_scales[y_group_of[d]]
+ * by the quantization rule above (exact quotient; an invalid scale gives codes 0), where y[b,d,t]
+ * is the fp32 value the QSSM_F32 output would hold. y_bias (NULL = no correction) is the
+ * calibrated correction term, e.g. from qssm_calib_channel_error_mean. The y_* fields are read
+ * only for QSSM_I8.
  * Workspace: qssm_scan_workspace_size bytes (dequantized B and C staging).
  */
 typedef struct qssm_scan_args {
@@ -159,8 +167,12 @@ typedef struct qssm_scan_args {
   const float* Dskip;                 /* [D] or NULL */
   const float* h0;                    /* [B, D, N] or NULL */
   void* y;                            /* [B, D, L], y_dtype */
-  int32_t y_dtype;                    /* QSSM_F32 or QSSM_F16 */
+  int32_t y_dtype;                    /* QSSM_F32, QSSM_F16 or QSSM_I8 */
   float* h_last;                      /* [B, D, N] or NULL */
+  int32_t y_groups;                   /* QSSM_I8: Gy, 1..256 */
+  const uint8_t* y_group_of;          /* QSSM_I8: [D] output group (< y_groups) of each channel */
+  const float* y_scales;              /* QSSM_I8: [Gy] static output scales */
+  const float* y_bias;                /* QSSM_I8: [D] correction added before quantizing, or NULL */
 } qssm_scan_args;
 
 size_t qssm_scan_workspace_size(const qssm_scan_args* a);
@@ -327,6 +339,13 @@ qssm_status qssm_calib_cluster_channels(const float* absmax, int32_t C, int32_t 
  *   s_out = fl32(H_out / 63) (so standard codes span [-H, H]); s_out = 1 if H_out is 0. */
 qssm_status qssm_calib_softedge(const float* v, int64_t n, double alpha, int32_t ema_valid,
                                 double* ema_state, float* s_out, float* L_out, float* H_out);
+
+/* Error-correction term (SSDi8, abstract: per-channel error statistics): for host tensors
+ * ref, approx [outer, C, inner] (the unquantized layer's output and the W8A8 path's output on a
+ * calibration draw), mean_out[c] = fl32 of the mean over o and i of (ref - approx), accumulated
+ * in fp64. Values must be finite; outer * inner >= 1. */
+qssm_status qssm_calib_channel_error_mean(const float* ref, const float* approx, int64_t outer,
+                                          int64_t C, int64_t inner, float* mean_out);
 
 /* ---------------------------------------------------------------------------------------------
  * Library information. */

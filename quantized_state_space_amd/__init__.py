@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqssm.so")
 
 QSSM_OK, QSSM_ERR_INVALID_ARG, QSSM_ERR_UNSUPPORTED, QSSM_ERR_WORKSPACE, QSSM_ERR_DEVICE = range(5)
-QSSM_F32, QSSM_F16, QSSM_I16 = 0, 1, 2
+QSSM_F32, QSSM_F16, QSSM_I16, QSSM_I8 = 0, 1, 2, 3
 QSSM_X_INT8, QSSM_X_SOFTEDGE = 0, 1
 QSSM_MMA_F16, QSSM_MMA_I8 = 0, 1
 
@@ -34,7 +34,8 @@ class ScanArgs(ctypes.Structure):
                 ("x_code", _I32), ("x_groups", _I32), ("x", _P), ("x_group_of", _P),
                 ("x_scales", _P), ("delta", _P), ("A", _P), ("bc_groups", _I32),
                 ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P), ("C_scales", _P),
-                ("Dskip", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P)]
+                ("Dskip", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
+                ("y_groups", _I32), ("y_group_of", _P), ("y_scales", _P), ("y_bias", _P)]
 
 
 class S4dArgs(ctypes.Structure):
@@ -82,6 +83,7 @@ SIGNATURES = {
     "qssm_calib_scales": (_I32, [_P, _I64, _P]),
     "qssm_calib_cluster_channels": (_I32, [_P, _I32, _I32, _P, _P]),
     "qssm_calib_softedge": (_I32, [_P, _I64, ctypes.c_double, _I32, _P, _P, _P, _P]),
+    "qssm_calib_channel_error_mean": (_I32, [_P, _P, _I64, _I64, _I64, _P]),
     "qssm_status_string": (ctypes.c_char_p, [_I32]),
     "qssm_last_error": (ctypes.c_char_p, []),
     "qssm_version": (_I32, []),
@@ -200,16 +202,23 @@ def _fill(st, keep=(), **kw):
 
 
 def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, y,
-              Dskip=None, h0=None, h_last=None):
-    """Builds ScanArgs for x [B, D, L] codes, Bq/Cq [B, Gbc, N, L]."""
+              Dskip=None, h0=None, h_last=None, y_group_of=None, y_scales=None, y_bias=None):
+    """Builds ScanArgs for x [B, D, L] codes, Bq/Cq [B, Gbc, N, L]. An int8 y takes the output
+    group map, scales and (optional) correction bias."""
     torch = _t()
     B, D, L = x.shape
     N = A.shape[1]
     Gbc = Bq.shape[1]
     xdt = torch.int8 if x_code == QSSM_X_INT8 else torch.uint8
-    ydt = QSSM_F32 if y.dtype == torch.float32 else QSSM_F16
-    keep = (x, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last)
+    ydt = {torch.float32: QSSM_F32, torch.float16: QSSM_F16, torch.int8: QSSM_I8}.get(y.dtype, -1)
+    yq = ydt == QSSM_I8
+    keep = (x, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last,
+            y_group_of, y_scales, y_bias)
     return _fill(ScanArgs(), keep=keep, batch=B, seqlen=L, dim=D, dstate=N, x_code=x_code,
+                 y_groups=int(y_scales.numel()) if (yq and y_scales is not None) else 0,
+                 y_group_of=_ptr(y_group_of, torch.uint8, "y_group_of", not yq),
+                 y_scales=_ptr(y_scales, torch.float32, "y_scales", not yq),
+                 y_bias=_ptr(y_bias, torch.float32, "y_bias", True),
                  x_groups=int(x_scales.numel()), x=_ptr(x, xdt, "x"),
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"),
@@ -353,6 +362,20 @@ def qssm_calib_cluster_channels(absmax, G):
     _check("qssm_calib_cluster_channels",
            load().qssm_calib_cluster_channels(_np_ptr(a), a.size, G, _np_ptr(perm), _np_ptr(grp)))
     return perm, grp
+
+
+def qssm_calib_channel_error_mean(ref, approx):
+    """Per-channel mean of ref - approx over axes 0 and 2 of [outer, C, inner] host arrays."""
+    import numpy as np
+    r = np.ascontiguousarray(ref, dtype=np.float32)
+    a = np.ascontiguousarray(approx, dtype=np.float32)
+    if r.shape != a.shape or r.ndim != 3:
+        raise ValueError("ref and approx must be [outer, C, inner] arrays of one shape")
+    outer, C, inner = r.shape
+    out = np.empty(C, dtype=np.float32)
+    _check("qssm_calib_channel_error_mean", load().qssm_calib_channel_error_mean(
+        _np_ptr(r), _np_ptr(a), outer, C, inner, _np_ptr(out)))
+    return out
 
 
 def qssm_calib_softedge(v, alpha=0.1, ema_state=None):

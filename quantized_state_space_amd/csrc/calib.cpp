@@ -153,4 +153,25 @@ qssm_status qssm_calib_softedge(const float* v, int64_t n, double alpha, int32_t
   return QSSM_OK;
 }
 
+qssm_status qssm_calib_channel_error_mean(const float* ref, const float* approx, int64_t outer,
+                                          int64_t C, int64_t inner, float* mean_out) {
+  qssm::clear_error();
+  if (outer < 1 || C < 1 || inner < 1) return fail(QSSM_ERR_INVALID_ARG, "bad shape");
+  if (!ref || !approx || !mean_out) return fail(QSSM_ERR_INVALID_ARG, "null pointer");
+  std::vector<double> sum(C, 0.0);
+  for (int64_t o = 0; o < outer; ++o)
+    for (int64_t c = 0; c < C; ++c) {
+      const int64_t base = (o * C + c) * inner;
+      for (int64_t i = 0; i < inner; ++i) {
+        const float r = ref[base + i], q = approx[base + i];
+        if (!std::isfinite(r) || !std::isfinite(q))
+          return fail(QSSM_ERR_INVALID_ARG, "value %lld not finite", (long long)(base + i));
+        sum[c] += (double)r - (double)q;
+      }
+    }
+  const double n = (double)outer * (double)inner;
+  for (int64_t c = 0; c < C; ++c) mean_out[c] = (float)(sum[c] / n);
+  return QSSM_OK;
+}
+
 }  // extern "C"

@@ -47,7 +47,12 @@ struct ScanParams {
   const float* h0;
   void* y;
   float* h_last;
+  const uint8_t* y_group_of;  // int8 output: [D] output group of each channel
+  const float* y_scales;      // int8 output: [Gy] static output scales
+  const float* y_bias;        // int8 output: [D] correction term, or NULL
 };
+
+enum { kYF32 = 0, kYF16 = 1, kYI8 = 2 };  // output forms of the scan
 
 // Stage B and C once into the layout read by the scan: for every (b, g), the states are cut into
 // planes of `ns` consecutive states (the states one wave owns), and each plane stores per step the
@@ -107,7 +112,7 @@ __device__ __forceinline__ float xunit(uint32_t byte) {
   return (float)(int8_t)(byte & 0xFFu);
 }
 
-template <int NS, int W, int XCODE, int YF16, int kBatch, int PFD, bool CODE16>
+template <int NS, int W, int XCODE, int YOUT, int kBatch, int PFD, bool CODE16>
 __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   __shared__ float ybuf[2][W][kT][kLanes];
   constexpr int kS = CODE16 ? NS : 2 * NS;  // staged 32-bit words per step
@@ -157,6 +162,14 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     if (ww == w) su = s;
   }
   const float Dsx = (p.Dskip ? p.Dskip[dc] : 0.0f) * sx;
+  // int8 output: this channel's output scale (its reciprocal, 0 for an invalid scale) and
+  // correction term
+  float sy = 1.0f, ry = 0.0f, yb = 0.0f;
+  if (YOUT == kYI8) {
+    sy = p.y_scales[p.y_group_of[dc]];
+    ry = recip_or_zero(sy);
+    yb = p.y_bias ? p.y_bias[dc] : 0.0f;
+  }
 
   float a2[NS], h[NS];
 #pragma unroll
@@ -342,7 +355,23 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     }
     const int64_t t0 = tb + w * kPer;
     if (valid) {
-      if (YF16) {
+      if (YOUT == kYI8) {
+        int8_t* yr = reinterpret_cast<int8_t*>(p.y) + (b * p.D + d) * L;
+        uint32_t code[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) code[j] = (uint8_t)quant8_r(yo[j] + yb, sy, ry);
+        if (vec_ok && t0 + kPer <= L && kPer % 4 == 0) {
+          // t0 is a multiple of kPer and L of 16: the words are aligned
+#pragma unroll
+          for (int j = 0; j < kPer / 4; ++j)
+            reinterpret_cast<uint32_t*>(yr + t0)[j] = code[4 * j] | (code[4 * j + 1] << 8) |
+                                                      (code[4 * j + 2] << 16) | (code[4 * j + 3] << 24);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kPer; ++j)
+            if (t0 + j < L) yr[t0 + j] = (int8_t)code[j];
+        }
+      } else if (YOUT == kYF16) {
         __half* yr = reinterpret_cast<__half*>(p.y) + (b * p.D + d) * L;
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
@@ -373,25 +402,27 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   }
 }
 
+template <int NS, int W, int BATCH, bool CODE16, int XCODE>
+void launch_scan_x(const ScanParams& p, int yout, dim3 grid, dim3 block, hipStream_t st) {
+  if (yout == kYF16) k_scan_m1<NS, W, XCODE, kYF16, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+  else if (yout == kYI8) k_scan_m1<NS, W, XCODE, kYI8, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+  else k_scan_m1<NS, W, XCODE, kYF32, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+}
+
 template <int NS, int W, int BATCH, bool CODE16>
-void launch_scan_t(const ScanParams& p, int xcode, int yf16, dim3 grid, dim3 block, hipStream_t st) {
-  if (xcode == QSSM_X_INT8) {
-    if (yf16) k_scan_m1<NS, W, QSSM_X_INT8, 1, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
-    else k_scan_m1<NS, W, QSSM_X_INT8, 0, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
-  } else {
-    if (yf16) k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 1, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
-    else k_scan_m1<NS, W, QSSM_X_SOFTEDGE, 0, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
-  }
+void launch_scan_t(const ScanParams& p, int xcode, int yout, dim3 grid, dim3 block, hipStream_t st) {
+  if (xcode == QSSM_X_INT8) launch_scan_x<NS, W, BATCH, CODE16, QSSM_X_INT8>(p, yout, grid, block, st);
+  else launch_scan_x<NS, W, BATCH, CODE16, QSSM_X_SOFTEDGE>(p, yout, grid, block, st);
 }
 
 // BATCH16 / BATCH32: steps per scalar-load batch with fp16 codes / fp32 values staged (two
 // batches of kS words per step must fit the SGPR budget next to the kernel's other scalars)
 template <int NS, int W, int BATCH16, int BATCH32>
-qssm_status launch_scan(const ScanParams& p, int xcode, int yf16, bool code16, hipStream_t st) {
+qssm_status launch_scan(const ScanParams& p, int xcode, int yout, bool code16, hipStream_t st) {
   dim3 grid((unsigned)cdiv(p.D, kLanes), (unsigned)p.B);
   dim3 block(64 * W);
-  if (code16) launch_scan_t<NS, W, BATCH16, true>(p, xcode, yf16, grid, block, st);
-  else launch_scan_t<NS, W, BATCH32, false>(p, xcode, yf16, grid, block, st);
+  if (code16) launch_scan_t<NS, W, BATCH16, true>(p, xcode, yout, grid, block, st);
+  else launch_scan_t<NS, W, BATCH32, false>(p, xcode, yout, grid, block, st);
   return launch_status("scan_w8a8");
 }
 
@@ -421,8 +452,14 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
   if (L > 0x7fffff00LL) return fail(QSSM_ERR_UNSUPPORTED, "seqlen must be below 2^31 - 256");
   if (a->x_code != QSSM_X_INT8 && a->x_code != QSSM_X_SOFTEDGE)
     return fail(QSSM_ERR_INVALID_ARG, "x_code must be QSSM_X_INT8 or QSSM_X_SOFTEDGE");
-  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16)
-    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32 or QSSM_F16");
+  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16 && a->y_dtype != QSSM_I8)
+    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32, QSSM_F16 or QSSM_I8");
+  if (a->y_dtype == QSSM_I8) {
+    if (a->y_groups < 1 || a->y_groups > 256)
+      return fail(QSSM_ERR_INVALID_ARG, "y_groups not in 1..256");
+    if (!a->y_group_of || !a->y_scales)
+      return fail(QSSM_ERR_INVALID_ARG, "QSSM_I8 output needs y_group_of and y_scales");
+  }
   if (a->x_groups < 1 || a->x_groups > 256) return fail(QSSM_ERR_INVALID_ARG, "x_groups not in 1..256");
   if (a->bc_groups < 1 || D % a->bc_groups != 0)
     return fail(QSSM_ERR_INVALID_ARG, "bc_groups must divide D");
@@ -465,14 +502,15 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
 
   ScanParams p{B, L, D, N, a->x_groups, a->bc_groups, a->bc_group_size, (int32_t)dpg,
                a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->B_scales,
-               a->C_scales, a->Dskip, a->h0, a->y, a->h_last};
-  const int yf16 = a->y_dtype == QSSM_F16;
+               a->C_scales, a->Dskip, a->h0, a->y, a->h_last, a->y_group_of, a->y_scales,
+               a->y_bias};
+  const int yout = a->y_dtype == QSSM_F16 ? kYF16 : (a->y_dtype == QSSM_I8 ? kYI8 : kYF32);
   switch (N) {
-    case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yf16, code16, stream);
-    case 8: return launch_scan<2, 4, 16, 16>(p, a->x_code, yf16, code16, stream);
-    case 16: return launch_scan<4, 4, 8, 8>(p, a->x_code, yf16, code16, stream);
-    case 32: return launch_scan<4, 8, 8, 8>(p, a->x_code, yf16, code16, stream);
-    default: return launch_scan<8, 8, 4, 4>(p, a->x_code, yf16, code16, stream);
+    case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yout, code16, stream);
+    case 8: return launch_scan<2, 4, 16, 16>(p, a->x_code, yout, code16, stream);
+    case 16: return launch_scan<4, 4, 8, 8>(p, a->x_code, yout, code16, stream);
+    case 32: return launch_scan<4, 8, 8, 8>(p, a->x_code, yout, code16, stream);
+    default: return launch_scan<8, 8, 4, 4>(p, a->x_code, yout, code16, stream);
   }
 }
 

@@ -48,6 +48,19 @@ def calib_state_groups(bc_cal, gs):
     return qssm_calib_scales(g_abs)
 
 
+def calib_y_groups(y_cal, G):
+    """Static scales of a layer's int8 output from a calibration output [outer, C, inner]: the
+    channels are clustered by absmax as x's are (Quamba2 steps 1-2) but stay in place, so the
+    result is the group of each channel in its own order, and one scale per group."""
+    ch = qssm_calib_channel_absmax(y_cal)
+    perm, grp = qssm_calib_cluster_channels(ch, G)
+    group_of = np.empty(ch.size, np.uint8)
+    group_of[perm] = grp
+    g_abs = np.zeros(G, dtype=np.float32)
+    np.maximum.at(g_abs, group_of.astype(np.int64), ch)
+    return group_of, qssm_calib_scales(g_abs)
+
+
 def calib_softedge(x_cal, perm, group_of, G):
     """Per-group soft-edge (s, L, H) from the calibration tensor in cluster order."""
     xs = np.asarray(x_cal)[:, perm, :]
@@ -67,7 +80,9 @@ class Mamba1Layer:
     cluster order), quantize B and C, run the W8A8 scan."""
 
     def __init__(self, inp, G, gs, device, x_code=QSSM_X_INT8, dynamic_scales=False,
-                 y_dtype=QSSM_F32, with_h0=False, perm=True):
+                 y_dtype=QSSM_F32, with_h0=False, perm=True, y_out=None):
+        """y_out = (group_of [D] uint8, scales [Gy] fp32, bias [D] fp32 or None), in the layer's
+        channel order: the scan then writes int8 y codes for the next W8A8 module."""
         import torch
         self.inp = inp
         self.G, self.gs, self.x_code = G, gs, x_code
@@ -112,12 +127,19 @@ class Mamba1Layer:
                               device=dev)
         self.Bq = torch.empty(inp["B"].shape, dtype=torch.int8, device=dev)
         self.Cq = torch.empty(inp["C"].shape, dtype=torch.int8, device=dev)
-        self.y = torch.empty((B, D, L), dtype=torch.float32 if y_dtype == QSSM_F32 else torch.float16,
-                             device=dev)
+        ydt = torch.float32 if y_dtype == QSSM_F32 else torch.float16
+        self.y_out = None
+        if y_out is not None:
+            ydt = torch.int8
+            yg, ys, yb = y_out
+            self.y_out = (_dev(np.asarray(yg, np.uint8), dev), _dev(np.asarray(ys, np.float32), dev),
+                          None if yb is None else _dev(np.asarray(yb, np.float32), dev))
+        self.y = torch.empty((B, D, L), dtype=ydt, device=dev)
         self.h_last = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+        yo = self.y_out or (None, None, None)
         self.args = scan_args(self.xq, x_code, self.group_t, self.xs, self.delta, self.A, self.Bq,
                               self.Cq, self.bs, self.cs, gs, self.y, Dskip=self.D, h0=self.h0,
-                              h_last=self.h_last)
+                              h_last=self.h_last, y_group_of=yo[0], y_scales=yo[1], y_bias=yo[2])
         self.ws = torch.empty(qssm_scan_workspace_size(self.args), dtype=torch.uint8, device=dev)
 
     def quantize(self):

@@ -135,6 +135,23 @@ def test_channel_absmax_and_scales_match_oracle():
         qs.qssm_calib_scales(np.array([np.nan], np.float32))
 
 
+def test_channel_error_mean_matches_oracle():
+    """Both accumulate the differences in fp64 (in different orders) and round the mean to fp32:
+    equal to within one fp32 rounding of the mean."""
+    r = np.random.default_rng(8)
+    ref = r.standard_normal((3, 40, 257)).astype(np.float32)
+    approx = (ref + 0.01 * r.standard_normal(ref.shape) + np.linspace(-0.1, 0.1, 40)[None, :, None]
+              ).astype(np.float32)
+    got = qs.qssm_calib_channel_error_mean(ref, approx)
+    want = oracle.channel_error_mean(ref, approx)
+    assert got.dtype == np.float32
+    assert np.all(np.abs(got - want) <= np.spacing(np.abs(want).astype(np.float32)))
+    bad = ref.copy()
+    bad[1, 2, 3] = np.inf
+    with pytest.raises(qs.QssmError, match="not finite"):
+        qs.qssm_calib_channel_error_mean(bad, approx)
+
+
 @pytest.mark.parametrize("C,G,seed", [(12, 4, 0), (64, 1, 1), (96, 8, 2), (1536, 8, 3), (300, 7, 4)])
 def test_cluster_matches_oracle(C, G, seed):
     r = np.random.default_rng(seed)

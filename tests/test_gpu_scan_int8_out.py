@@ -1,0 +1,134 @@
+"""GPU parity of the Mamba1 scan's int8 output (the persistent int8 path of the SSDi8 abstract:
+y + a per-channel correction term, quantized with static per-group scales for the next W8A8 module).
+
+Two checks:
+- against the oracle: the kernel's y is fp32 and the oracle's fp64, so a value whose v / s lies
+  within Y_NEAR code units of a rounding boundary may round either way; every other code must be
+  equal, and none may differ by more than one (y's measured row error, ~1e-6 of a row's largest
+  value, moves v / s by under 1e-4 code units);
+- against the library's own fp32 output: the int8 codes equal the library's exact quantizer applied
+  to fl32(y_f32 + bias) bit for bit, since both runs compute the same fp32 y."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.pipelines as op
+import qssm_synth as synth
+
+pytestmark = pytest.mark.gpu
+
+Y_NEAR = 0.002
+
+
+def layer(dev, inp, G, gs, **kw):
+    import quantized_state_space_amd.workloads as wl
+    return wl.Mamba1Layer(inp, G, gs, dev, **kw)
+
+
+def y_calib(y64, Gy, seed, spread=(1.0,)):
+    """Output groups from the oracle's y (clustered channel absmax, channels in place), one scale per
+    group (group absmax times a factor from `spread`, < 1 to force saturation), and a seeded
+    per-channel correction bias of about 1% of each channel's largest |y|."""
+    y32 = np.asarray(y64, np.float64).astype(np.float32)
+    absmax = oracle.finite_absmax(y32, axis=(0, 2))
+    perm, grp = oracle.cluster_channels(absmax, Gy)
+    group_of = np.empty(absmax.size, np.uint8)
+    group_of[perm] = grp
+    g_abs = np.zeros(Gy, np.float32)
+    np.maximum.at(g_abs, group_of.astype(np.int64), absmax)
+    f = np.resize(np.asarray(spread, np.float32), Gy)
+    scales = oracle.scale_from_absmax((g_abs * f).astype(np.float32))
+    bias = (synth.rng(seed, 12).standard_normal(absmax.size) * 0.01 * absmax).astype(np.float32)
+    return group_of, scales, bias
+
+
+def check_codes_vs_oracle(got, y64, group_of, scales, bias):
+    want = oracle.requant_output(y64, group_of, scales, bias)
+    y32 = np.asarray(y64, np.float64).astype(np.float32)
+    v = (y32 + bias[None, :, None]).astype(np.float32).astype(np.float64)
+    s = np.asarray(scales, np.float64)[np.asarray(group_of, np.int64)][None, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = v / s
+        near = np.abs(r - np.floor(r) - 0.5) < Y_NEAR
+    diff = got.astype(np.int32) - want.astype(np.int32)
+    far_bad = np.count_nonzero(diff[~near])
+    print(f"  codes: {got.size} checked, {np.count_nonzero(near)} near a boundary, "
+          f"{np.count_nonzero(diff)} differ", flush=True)
+    assert far_bad == 0, f"{far_bad} codes away from a rounding boundary differ"
+    assert np.abs(diff).max(initial=0) <= 1
+    assert np.count_nonzero(near) < 0.01 * got.size
+
+
+@pytest.mark.parametrize("B,D,L,N,G,gs,Gy,spread", [(2, 128, 300, 16, 4, 4, 4, (1.0, 0.5)),
+                                                    (1, 64, 77, 4, 2, 4, 1, (1.0,)),
+                                                    (2, 192, 64, 8, 5, 4, 3, (0.3, 1.0, 1.0)),
+                                                    (1, 128, 200, 64, 4, 8, 2, (1.0, 0.7)),
+                                                    (1, 70, 99, 16, 3, 1, 2, (1.0,))])
+def test_int8_output_vs_oracle(dev, B, D, L, N, G, gs, Gy, spread):
+    import torch
+    print(f"\n[mamba1 int8 y B={B} D={D} L={L} N={N} Gy={Gy}]", flush=True)
+    inp = synth.mamba1_inputs(cfg=31, batch=B, seqlen=L, dim=D, dstate=N, x_dist="student_t",
+                              calib_batch=1, with_h0=True)
+    ref = op.mamba1(inp, G=G, gs=gs, with_h0=True)
+    yg, ys, yb = y_calib(ref["y"], Gy, 31, spread)
+    lay = layer(dev, inp, G=G, gs=gs, with_h0=True, y_out=(yg, ys, yb))
+    lay.step()
+    torch.cuda.synchronize()
+    assert lay.y.dtype == torch.int8
+    check_codes_vs_oracle(lay.y.cpu().numpy(), ref["y"], yg, ys, yb)
+    # the state is the same as with an fp32 output
+    err = oracle.rowwise_error(lay.h_last.cpu().numpy(), ref["h_last"])
+    assert err.max() <= 2e-3
+
+
+def test_int8_output_invalid_scale_and_no_bias(dev):
+    """An output group whose scale is outside [2^-100, 2^100] gets codes 0; no bias is the same as
+    a zero bias."""
+    import torch
+    print("\n[mamba1 int8 y invalid scale]", flush=True)
+    inp = synth.mamba1_inputs(cfg=32, batch=2, seqlen=128, dim=128, dstate=16, calib_batch=1)
+    ref = op.mamba1(inp, G=2, gs=4)
+    yg, ys, _ = y_calib(ref["y"], 3, 32)
+    ys = ys.copy()
+    ys[1] = np.float32(1e-35)
+    lay = layer(dev, inp, G=2, gs=4, y_out=(yg, ys, None))
+    lay.step()
+    torch.cuda.synchronize()
+    got = lay.y.cpu().numpy()
+    assert not got[:, yg == 1].any()
+    check_codes_vs_oracle(got, ref["y"], yg, ys, np.zeros(128, np.float32))
+
+
+@pytest.mark.parametrize("soft", [False, True])
+def test_c3_int8_output_full_size(dev, soft):
+    """Mamba1-130M-shaped layer (B=8, L=2048, D=1536, N=16) with an int8 output in 8 groups, as the
+    benchmark's int8-output workload runs it: the codes equal the library's exact quantizer over
+    the fp32-output run bit for bit, and sampled rows match the oracle."""
+    import torch
+    import quantized_state_space_amd as qs
+    print(f"\n[c3 int8 y full size softedge={soft}]", flush=True)
+    xc = qs.QSSM_X_SOFTEDGE if soft else qs.QSSM_X_INT8
+    inp = synth.c3_inputs()
+    D, Gy = 1536, 8
+    r = np.random.default_rng(4)
+    bsel = np.repeat(np.arange(8), 6)
+    dsel = np.concatenate([r.choice(D, 6, replace=False) for _ in range(8)])
+    ref = op.mamba1(inp, G=8, gs=4, soft_edge=soft, rows=(bsel, dsel))
+    # output groups: contiguous channel blocks; scales from the oracle's sampled rows, the first
+    # two groups scaled down so that they saturate
+    yg = (np.arange(D) * Gy // D).astype(np.uint8)
+    top = np.float32(np.abs(ref["y_rows"]).max())
+    ys = oracle.scale_from_absmax((top * np.float32([0.25, 0.5, 1, 1, 1, 1, 2, 1])).astype(np.float32))
+    yb = (synth.rng(33, 12).standard_normal(D) * 0.01 * top).astype(np.float32)
+    lay_f = layer(dev, inp, G=8, gs=4, x_code=xc)
+    lay_q = layer(dev, inp, G=8, gs=4, x_code=xc, y_out=(yg, ys, yb))
+    lay_f.step()
+    lay_q.step()
+    yb_t, yg_t, ys_t = (torch.from_numpy(a).to(dev) for a in (yb, yg, ys))
+    v = lay_f.y + yb_t[None, :, None]
+    want = torch.empty_like(lay_q.y)
+    qs.qssm_quant_group_x(v, yg_t, Gy, ys_t, want)
+    torch.cuda.synchronize()
+    assert torch.equal(lay_q.y, want)
+    got_rows = lay_q.y.cpu().numpy()[bsel, dsel]
+    check_codes_vs_oracle(got_rows[None], ref["y_rows"][None], yg[dsel], ys, yb[dsel])
