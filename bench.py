@@ -338,12 +338,12 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True),
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (151143646, 133477168, "5ae630ea6a8668c9"),
+    "c3": (152089444, 132508472, "82855a741382f2d7"),
     "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
     "c4": (692105038, 858799064, "1771bfe3189ad294"),
     "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
-    "c3se": (154502753, 133967152, "5ae630ea6a8668c9"),
-    "c3i8y": (315987830, 164880400, "5ae630ea6a8668c9"),
+    "c3se": (152357308, 132879688, "82855a741382f2d7"),
+    "c3i8y": (135567360, 27820032, "82855a741382f2d7"),
     "c4f16": (683357980, 694246608, "1771bfe3189ad294"),
     "c5f16": (563235239, 545288304, "2d61ee22651a7256"),
 }

@@ -123,6 +123,12 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   constexpr int kXdRow = 20;
   constexpr int kPerX = kT / W;
   __shared__ __align__(16) float xd[kShareX ? 2 : 1][kShareX ? kLanes : 1][kShareX ? kXdRow : 1];
+  // int8 output: the codes of eight blocks (128 steps) gather per channel in LDS (rows padded to
+  // 132 bytes) and leave as whole 128-byte lines, two groups of blocks in turn
+  constexpr bool kGather = YOUT == kYI8;
+  constexpr int kGrpBlocks = 8;
+  constexpr int kRowB = kGrpBlocks * kT + 4;
+  __shared__ __align__(16) uint8_t ycode[kGather ? 2 : 1][kGather ? kLanes : 1][kGather ? kRowB : 4];
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -276,6 +282,25 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     dAr[0][k] = __builtin_amdgcn_exp2f(dlA[0] * a2[k]);
     dAr[1][k] = __builtin_amdgcn_exp2f(dlA[1] * a2[k]);
   }
+  // Store the gathered codes of block group grp (steps [grp*128, grp*128 + 128) of the 64
+  // channels): 16-byte pieces, eight per channel row, spread over the workgroup's threads.
+  auto flush_codes = [&](int64_t grp) {
+    const int gb = (int)(grp & 1);
+    const int64_t tg = grp * (kGrpBlocks * kT);
+    for (int idx = threadIdx.x; idx < kLanes * 8; idx += 64 * W) {
+      const int row = idx >> 3, piece = idx & 7;
+      const int64_t dd = d0 + row;
+      const int64_t t = tg + piece * 16;
+      if (dd >= p.D || t >= L) continue;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(&ycode[gb][row][piece * 16]);
+      int8_t* dst = reinterpret_cast<int8_t*>(p.y) + (b * p.D + dd) * L + t;
+      if (vec_ok && t + 16 <= L) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(src[0], src[1], src[2], src[3]);
+      } else {
+        for (int j = 0; j < 16 && t + j < L; ++j) dst[j] = (int8_t)ycode[gb][row][piece * 16 + j];
+      }
+    }
+  };
   // One block of kT steps: dl/xq hold this block's delta and x codes, dn/xn receive the next
   // block's; buf selects the LDS buffers. The block loop is unrolled twice with the two register
   // sets swapping roles, so that no copy of the next block's values is needed between blocks.
@@ -354,24 +379,26 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       yo[j] = fmaf(Dsx, xu, sum);
     }
     const int64_t t0 = tb + w * kPer;
-    if (valid) {
-      if (YOUT == kYI8) {
-        int8_t* yr = reinterpret_cast<int8_t*>(p.y) + (b * p.D + d) * L;
-        uint32_t code[kPer];
+    if (kGather) {
+      // the previous group's codes, complete since this block's barrier, leave first; this
+      // block's codes go to the other buffer
+      const int64_t blk = tb / kT;
+      if (blk % kGrpBlocks == 0 && blk > 0) flush_codes(blk / kGrpBlocks - 1);
+      uint32_t code[kPer];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) code[j] = (uint8_t)quant8_r(yo[j] + yb, sy, ry);
-        if (vec_ok && t0 + kPer <= L && kPer % 4 == 0) {
-          // t0 is a multiple of kPer and L of 16: the words are aligned
+      for (int j = 0; j < kPer; ++j) code[j] = (uint8_t)quant8_r(yo[j] + yb, sy, ry);
+      uint8_t* crow = &ycode[(blk / kGrpBlocks) & 1][lane][(blk % kGrpBlocks) * kT + w * kPer];
+      if (kPer % 4 == 0) {
 #pragma unroll
-          for (int j = 0; j < kPer / 4; ++j)
-            reinterpret_cast<uint32_t*>(yr + t0)[j] = code[4 * j] | (code[4 * j + 1] << 8) |
-                                                      (code[4 * j + 2] << 16) | (code[4 * j + 3] << 24);
-        } else {
+        for (int j = 0; j < kPer / 4; ++j)
+          reinterpret_cast<uint32_t*>(crow)[j] = code[4 * j] | (code[4 * j + 1] << 8) |
+                                                 (code[4 * j + 2] << 16) | (code[4 * j + 3] << 24);
+      } else {
 #pragma unroll
-          for (int j = 0; j < kPer; ++j)
-            if (t0 + j < L) yr[t0 + j] = (int8_t)code[j];
-        }
-      } else if (YOUT == kYF16) {
+        for (int j = 0; j < kPer; ++j) crow[j] = (uint8_t)code[j];
+      }
+    } else if (valid) {
+      if (YOUT == kYF16) {
         __half* yr = reinterpret_cast<__half*>(p.y) + (b * p.D + d) * L;
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
@@ -394,6 +421,11 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   for (int64_t tb = 0; tb < L; tb += 2 * kT) {
     block(tb, dlA, dlB, xqA, xqB, 0);
     if (tb + kT < L) block(tb + kT, dlB, dlA, xqB, xqA, 1);
+  }
+  if (kGather && L > 0) {
+    // the last (possibly partial) group
+    __syncthreads();
+    flush_codes((L - 1) / (kGrpBlocks * kT));
   }
 
   if (valid && p.h_last) {
