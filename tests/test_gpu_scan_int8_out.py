@@ -132,3 +132,33 @@ def test_c3_int8_output_full_size(dev, soft):
     assert torch.equal(lay_q.y, want)
     got_rows = lay_q.y.cpu().numpy()[bsel, dsel]
     check_codes_vs_oracle(got_rows[None], ref["y_rows"][None], yg[dsel], ys, yb[dsel])
+
+
+def _random_cases(n, seed=77):
+    r = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        N = int(r.choice([4, 8, 16, 32, 64]))
+        gs = int(r.choice([g for g in (1, 2, 4, 8, 16) if N % g == 0]))
+        D = int(r.integers(8, 260))
+        G = int(r.integers(1, min(D, 8) + 1))
+        Gy = int(r.integers(1, min(D, 8) + 1))
+        out.append((k, int(r.integers(1, 4)), D, int(r.integers(1, 700)), N, G, gs, Gy))
+    return out
+
+
+@pytest.mark.parametrize("k,B,D,L,N,G,gs,Gy", _random_cases(6))
+def test_int8_output_random_shapes(dev, k, B, D, L, N, G, gs, Gy):
+    """Seeded random shapes (ragged D and L, every supported state size, both B/C staging
+    layouts): the int8 output against the oracle, and the state as with an fp32 output."""
+    import torch
+    print(f"\n[mamba1 int8 y random {k}: B={B} D={D} L={L} N={N} G={G} gs={gs} Gy={Gy}]", flush=True)
+    inp = synth.mamba1_inputs(cfg=100 + k, batch=B, seqlen=L, dim=D, dstate=N, calib_batch=1,
+                              with_h0=True)
+    ref = op.mamba1(inp, G=G, gs=gs, with_h0=True)
+    yg, ys, yb = y_calib(ref["y"], Gy, 100 + k, (1.0, 0.6))
+    lay = layer(dev, inp, G=G, gs=gs, with_h0=True, y_out=(yg, ys, yb))
+    lay.step()
+    torch.cuda.synchronize()
+    check_codes_vs_oracle(lay.y.cpu().numpy(), ref["y"], yg, ys, yb)
+    assert oracle.rowwise_error(lay.h_last.cpu().numpy(), ref["h_last"]).max() <= 2e-3
