@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 100 /* 1.0.0 */
+#define QSSM_VERSION 110 /* 1.1.0: int8 scan output fields appended to qssm_scan_args */
 
 typedef int32_t qssm_status;
 enum {

@@ -42,7 +42,7 @@ def test_struct_layouts_and_version():
     for kind, st in qs.ARG_STRUCTS.items():
         assert lib.qssm_args_size(kind) == ctypes.sizeof(st)
     assert lib.qssm_args_size(99) == 0
-    assert lib.qssm_version() == 100
+    assert lib.qssm_version() == 110
     assert lib.qssm_status_string(qs.QSSM_ERR_WORKSPACE) == b"workspace missing or too small"
 
 
