@@ -418,3 +418,70 @@ def test_rowwise_error_measure():
     assert np.allclose(oracle.rowwise_error([[3.0 + 4.0j]], [[0.0 + 0.0j]], axis=-1) > 1e6, [True])
     # an all-zero reference row is floored at 1e-6 of the largest reference value
     assert np.allclose(oracle.rowwise_error([[1e-3], [2.0]], [[0.0], [2.0]]), [500.0, 0.0])
+
+
+# ------------------------------------------------------------------------------------------------
+# int16 S4D state: worked closed forms (A = 0, so Abar = 1 and Bbar = dt * B exactly) and a
+# deterministic rounding-error bound against the unrounded fp64 run
+
+def s4d_const_increment(inc_re, inc_im, s, L, C=1.0 + 0.5j, D=0.25):
+    """One channel, one state, A = 0, dt = 1, B = (inc_re + i inc_im) * s, u = 1 at every step."""
+    u = np.ones((1, 1, L))
+    Ah = np.zeros((1, 1), np.complex128)
+    Bh = np.full((1, 1), (inc_re + 1j * inc_im) * s)
+    Ch = np.full((1, 1), C)
+    return oracle.s4d_scan(u, Ah, Bh, Ch, np.ones(1), Dskip=np.full(1, D),
+                           state_scale=np.full(1, s))
+
+
+def test_s4d_int16_dead_zone():
+    """Increments of 0.3 grid steps round back to 0 after every step: the int16 state never leaves
+    0, y is the D term alone. (Rounding before adding the input would hold 0.3 s; rounding only at
+    the readout would let the state grow as 0.3 t s.)"""
+    s = 2.0 ** -10
+    y, hl = s4d_const_increment(0.3, -0.3, s, 40)
+    assert np.all(hl == 0)
+    assert np.all(y == 0.25)
+
+
+def test_s4d_int16_exact_walk_and_saturation():
+    """Increments of 0.6 grid steps (real part): h_t = round(h_{t-1} + 0.6) = t exactly. Increments
+    of -1000.25 grid steps (imaginary part): -1000 t until the code saturates at -32768 (t = 33),
+    where it stays. Every y_t is Re(C h_t) + D with those exact states."""
+    s = 2.0 ** -12
+    L = 50
+    C, D = 1.0 + 0.5j, 0.25
+    y, hl = s4d_const_increment(0.6, -1000.25, s, L, C=C, D=D)
+    t = np.arange(1, L + 1)
+    h = t * s + 1j * np.maximum(-1000.0 * t, -32768.0) * s
+    np.testing.assert_array_equal(hl[0, 0, 0], h[-1])
+    np.testing.assert_array_equal(y[0, 0], (C * h).real + D)
+    # positive saturation at +32767
+    y2, hl2 = s4d_const_increment(1000.25, 0.0, s, L, C=C, D=D)
+    h2 = np.minimum(1000.0 * t, 32767.0) * s
+    np.testing.assert_array_equal(hl2[0, 0, 0], h2[-1] + 0j)
+    np.testing.assert_array_equal(y2[0, 0], C.real * h2 + D)
+
+
+def test_s4d_int16_error_bound_against_fp64():
+    """Generic channels: per step each part is rounded by at most s/2, so the state error obeys
+    e_t = Abar e_{t-1} + r_t with |r_t| <= s / sqrt(2), hence |e_t| <= s / sqrt(2) * sum_{k<t}
+    |Abar|^k, and |y_t - y_t(fp64)| <= sum_n |C_n| |e_t,n|. Checked at every step (states below
+    the saturation limit); the int16 run must also sit on the grid and differ from the fp64 run."""
+    u, Ah, Bh, Ch, dt, D = s4d_small(seed=12, L=60)
+    B, H, L = u.shape
+    s = np.full(H, 2.0 ** -9)
+    yq, hq = oracle.s4d_scan(u, Ah, Bh, Ch, dt, Dskip=D, state_scale=s)
+    y, hl = oracle.s4d_scan(u, Ah, Bh, Ch, dt, Dskip=D)
+    for h in range(H):
+        Ab, _ = oracle.s4d_zoh(Ah[h], Bh[h], dt[h])
+        geo = np.cumsum(np.abs(Ab)[None, :] ** np.arange(L)[:, None], axis=0)   # [t, n]
+        ebound = s[h] / np.sqrt(2.0) * geo
+        ybound = (np.abs(Ch[h])[None, :] * ebound).sum(axis=1)
+        for b in range(B):
+            assert np.all(np.abs(yq[b, h] - y[b, h]) <= ybound * (1 + 1e-9) + 1e-12)
+            assert np.all(np.abs(hq[b, h] - hl[b, h]) <= ebound[-1] * (1 + 1e-9) + 1e-12)
+            assert np.all(np.abs(hl[b, h].real) < 30000 * s[h])
+    grid = np.concatenate([hq.real.ravel(), hq.imag.ravel()]) / s[0]
+    assert np.array_equal(grid, np.rint(grid))
+    assert not np.array_equal(hq, hl)
