@@ -31,6 +31,7 @@
  *  - No C++ exception ever crosses this boundary.
  *  - The library allocates no device memory. Entry points that need scratch take a caller-provided
  *    workspace whose size a *_workspace_size call reports.
+ *  - Group maps hold indices below the group count; a larger index is read as the last group.
  *
  * Quantization rule used everywhere (int8 codes, bit-exact):
  *     q = clamp(RNE(v / s), -128, 127)
@@ -178,6 +179,7 @@ typedef struct qssm_scan_args {
 size_t qssm_scan_workspace_size(const qssm_scan_args* a);
 qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
 
 /* ---------------------------------------------------------------------------------------------
  * a5-a7 (S4D form). Diagonal LTI scan with int8 parameters and input.

@@ -212,6 +212,13 @@ def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_sca
     xdt = torch.int8 if x_code == QSSM_X_INT8 else torch.uint8
     ydt = {torch.float32: QSSM_F32, torch.float16: QSSM_F16, torch.int8: QSSM_I8}.get(y.dtype, -1)
     yq = ydt == QSSM_I8
+    if yq:
+        if y_group_of is None or y_scales is None:
+            raise ValueError("an int8 y needs y_group_of and y_scales")
+        if y_group_of.numel() != D or (y_bias is not None and y_bias.numel() != D):
+            raise ValueError("y_group_of and y_bias must have one entry per channel")
+    if x_group_of.numel() != D:
+        raise ValueError("x_group_of must have one entry per channel")
     keep = (x, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last,
             y_group_of, y_scales, y_bias)
     return _fill(ScanArgs(), keep=keep, batch=B, seqlen=L, dim=D, dstate=N, x_code=x_code,

@@ -59,7 +59,7 @@ __device__ __forceinline__ int64_t div_fast(int64_t a, int64_t b) {
 
 template <int MAP>
 __device__ __forceinline__ int scale_index(const Geometry& g, int64_t c) {
-  if (MAP == MAP_GROUP) return g.group_of[c];
+  if (MAP == MAP_GROUP) return min((int)g.group_of[c], g.nscales - 1);
   const int64_t grp = div_fast(c, g.N), n = c - grp * g.N;
   return (int)(grp * g.ngs + div_fast(n, g.gs));
 }
@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
       for (int k = 0; k < kChunks; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          ch[k].si[j % (Chunk<MAP, LAYOUT>::kUniform ? 1 : 4)] = (int)((gidw[k] >> (8 * j)) & 0xFFu);
+          ch[k].si[j % (Chunk<MAP, LAYOUT>::kUniform ? 1 : 4)] =
+              min((int)((gidw[k] >> (8 * j)) & 0xFFu), g.nscales - 1);
     }
   }
   // The per-group scales are staged after the chunk loads are issued, so that the two memory
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_softedge_decode(
 #pragma unroll
   for (int k = 0; k < kDecVec; ++k) {
     if (k < n) {
-      v[k] = softedge_value(b[k], s_scale[group_of[c]]);
+      v[k] = softedge_value(b[k], s_scale[min((int)group_of[c], nscales - 1)]);
       if (++i == inner) { i = 0; if (++c == C) c = 0; }
     }
   }

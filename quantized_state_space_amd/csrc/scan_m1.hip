@@ -35,6 +35,7 @@ typedef const uint32_t __attribute__((address_space(4))) cu32;  // constant (sca
 struct ScanParams {
   int64_t B, L, D, N;
   int32_t G, Gbc, gs, dpg;  // dpg = D / Gbc channels per B/C group
+  int32_t Gy;               // int8 output: number of output groups
   const void* x;
   const uint8_t* x_group_of;
   const float* x_scales;
@@ -146,13 +147,18 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   // state group when fp16 codes are staged), so each step adds dt * x_code * B; su and the C scale
   // multiply the wave's partial output once, in the combine. An invalid B or C scale is 0 (its
   // codes are staged as 0 as well); a zero su (no input reaches the chain) is replaced by 1.
-  float sx = p.x_scales[p.x_group_of[dc]];
+  // su is kept as m * 2^e (m = the product of the two scales' significands): two valid scales can
+  // have a product outside the normal fp32 range (2^-80 * 2^-80), and then the factors below are
+  // formed from the exponent sum with ldexp, so an output that fp32 can represent stays exact.
+  // Group indices at or above the group count are clamped to the last group.
+  float sx = p.x_scales[min((int)p.x_group_of[dc], p.G - 1)];
   const bool sx_ok = scale_ok(sx);
   const uint32_t xmask = sx_ok ? 0xFFFFFFFFu : 0u;
   if (!sx_ok) sx = 0.0f;
   const int ngs = (int)(p.N / p.gs);
-  float cf[W];     // factor of each wave's partial output (C scale x that wave's su)
-  float su = 1.0f;  // this wave's su
+  float cf[W];        // factor of each wave's partial output (C scale x that wave's su)
+  float sum_ = 1.0f;  // this wave's su as m * 2^se
+  int se = 0;
 #pragma unroll
   for (int ww = 0; ww < W; ++ww) {
     float sb = 1.0f, sc = 1.0f;
@@ -162,17 +168,25 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       sc = p.C_scales[g * ngs + (ww * NS) / p.gs];
       sc = scale_ok(sc) ? sc : 0.0f;
     }
-    float s = sx * sb;
-    if (s == 0.0f) s = 1.0f;
-    cf[ww] = sc * s;
-    if (ww == w) su = s;
+    int ex = 0, eb = 0;
+    float m = frexpf(sx, &ex) * frexpf(sb, &eb);
+    int e = ex + eb;
+    if (m == 0.0f) {
+      m = 1.0f;
+      e = 0;
+    }
+    cf[ww] = ldexpf(sc * m, e);
+    if (ww == w) {
+      sum_ = m;
+      se = e;
+    }
   }
   const float Dsx = (p.Dskip ? p.Dskip[dc] : 0.0f) * sx;
   // int8 output: this channel's output scale (its reciprocal, 0 for an invalid scale) and
   // correction term
   float sy = 1.0f, ry = 0.0f, yb = 0.0f;
   if (YOUT == kYI8) {
-    sy = p.y_scales[p.y_group_of[dc]];
+    sy = p.y_scales[min((int)p.y_group_of[dc], p.Gy - 1)];
     ry = recip_or_zero(sy);
     yb = p.y_bias ? p.y_bias[dc] : 0.0f;
   }
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   for (int k = 0; k < NS; ++k) {
     const int n = w * NS + k;
     a2[k] = p.A[dc * p.N + n] * kLog2e;
-    h[k] = p.h0 ? p.h0[(b * p.D + dc) * p.N + n] / su : 0.0f;
+    h[k] = p.h0 ? ldexpf(p.h0[(b * p.D + dc) * p.N + n] / sum_, -se) : 0.0f;
   }
 
   const float* __restrict__ drow = p.delta + (b * p.D + dc) * L;
@@ -430,7 +444,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 
   if (valid && p.h_last) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) p.h_last[(b * p.D + d) * p.N + w * NS + k] = h[k] * su;
+    for (int k = 0; k < NS; ++k) p.h_last[(b * p.D + d) * p.N + w * NS + k] = ldexpf(h[k] * sum_, se);
   }
 }
 
@@ -466,18 +480,47 @@ size_t stage_bytes(const qssm_scan_args* a) {
          (size_t)(a->seqlen + kPadRows) * 2 * sizeof(float);
 }
 
-}  // namespace
+// Validation, B/C staging and the scan launch; `stage` is 256-byte aligned and holds
+// stage_bytes(a) bytes (it may be null when that is 0).
+qssm_status scan_impl(const qssm_scan_args* a, void* stage_mem, hipStream_t stream) {
+  const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
+  const int64_t dpg = D / a->bc_groups;
+  float* stage = reinterpret_cast<float*>(stage_mem);
+  const int ns = states_per_wave(N);
+  // fp16 codes when every wave's states lie inside one B/C state group
+  const bool code16 = (a->bc_group_size % ns) == 0;
+  const int64_t nstage = B * a->bc_groups * N * (L + kPadRows);
+  if (nstage > 0) {
+    if (code16)
+      k_stage_bc<true><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
+          a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
+          ns, stage);
+    else
+      k_stage_bc<false><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
+          a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
+          ns, stage);
+    if (qssm_status s = launch_status("scan_w8a8 staging")) return s;
+  }
 
-extern "C" {
-
-size_t qssm_scan_workspace_size(const qssm_scan_args* a) {
-  if (!a || a->batch < 0 || a->seqlen < 0 || a->bc_groups < 1 || a->dstate < 1) return 0;
-  return stage_bytes(a) + 256;
+  ScanParams p{B, L, D, N, a->x_groups, a->bc_groups, a->bc_group_size, (int32_t)dpg,
+               a->y_dtype == QSSM_I8 ? a->y_groups : 1,
+               a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->B_scales,
+               a->C_scales, a->Dskip, a->h0, a->y, a->h_last, a->y_group_of, a->y_scales,
+               a->y_bias};
+  const int yout = a->y_dtype == QSSM_F16 ? kYF16 : (a->y_dtype == QSSM_I8 ? kYI8 : kYF32);
+  switch (N) {
+    case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yout, code16, stream);
+    case 8: return launch_scan<2, 4, 16, 16>(p, a->x_code, yout, code16, stream);
+    case 16: return launch_scan<4, 4, 8, 8>(p, a->x_code, yout, code16, stream);
+    case 32: return launch_scan<4, 8, 8, 8>(p, a->x_code, yout, code16, stream);
+    default: return launch_scan<8, 8, 4, 4>(p, a->x_code, yout, code16, stream);
+  }
 }
 
-qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
-  clear_error();
+// Argument checks shared by both entry points; QSSM_OK means "launch", and *done is set when the
+// call has nothing to do (B == 0).
+qssm_status validate(const qssm_scan_args* a, bool* done) {
+  *done = false;
   if (!a) return fail(QSSM_ERR_INVALID_ARG, "args is null");
   const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
   if (B < 0 || L < 0 || D < 1 || N < 1) return fail(QSSM_ERR_INVALID_ARG, "bad shape");
@@ -502,48 +545,41 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
     return fail(QSSM_ERR_UNSUPPORTED, "with bc_groups > 1, D / bc_groups must be a multiple of 64");
   if (N != 4 && N != 8 && N != 16 && N != 32 && N != 64)
     return fail(QSSM_ERR_UNSUPPORTED, "dstate must be 4, 8, 16, 32 or 64");
-  if (B == 0) return QSSM_OK;
+  if (B == 0) {
+    *done = true;
+    return QSSM_OK;
+  }
   // the per-step buffers are not touched when L == 0 and may then be null
   if (!a->x_group_of || !a->x_scales || !a->A || !a->B_scales || !a->C_scales ||
       (L > 0 && (!a->x || !a->delta || !a->Bq || !a->Cq || !a->y)))
     return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
   if (((uintptr_t)a->x | (uintptr_t)a->delta | (uintptr_t)a->y) % 16 != 0)
     return fail(QSSM_ERR_INVALID_ARG, "x, delta and y must be 16-byte aligned");
+  return QSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qssm_scan_workspace_size(const qssm_scan_args* a) {
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->bc_groups < 1 || a->dstate < 1) return 0;
+  return stage_bytes(a) + 256;
+}
+
+qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  clear_error();
+  bool done = false;
+  if (qssm_status s = validate(a, &done)) return s;
+  if (done) return QSSM_OK;
   const size_t need = stage_bytes(a);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QSSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  float* stage = reinterpret_cast<float*>(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  void* stage = reinterpret_cast<void*>(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   if ((size_t)((char*)stage - (char*)ws) + need > ws_bytes)
     return fail(QSSM_ERR_WORKSPACE, "workspace too small after 256-byte alignment");
-
-  const int ns = states_per_wave(N);
-  // fp16 codes when every wave's states lie inside one B/C state group
-  const bool code16 = (a->bc_group_size % ns) == 0;
-  const int64_t nstage = B * a->bc_groups * N * (L + kPadRows);
-  if (nstage > 0) {
-    if (code16)
-      k_stage_bc<true><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
-          a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
-          ns, stage);
-    else
-      k_stage_bc<false><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
-          a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
-          ns, stage);
-    if (qssm_status s = launch_status("scan_w8a8 staging")) return s;
-  }
-
-  ScanParams p{B, L, D, N, a->x_groups, a->bc_groups, a->bc_group_size, (int32_t)dpg,
-               a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->B_scales,
-               a->C_scales, a->Dskip, a->h0, a->y, a->h_last, a->y_group_of, a->y_scales,
-               a->y_bias};
-  const int yout = a->y_dtype == QSSM_F16 ? kYF16 : (a->y_dtype == QSSM_I8 ? kYI8 : kYF32);
-  switch (N) {
-    case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yout, code16, stream);
-    case 8: return launch_scan<2, 4, 16, 16>(p, a->x_code, yout, code16, stream);
-    case 16: return launch_scan<4, 4, 8, 8>(p, a->x_code, yout, code16, stream);
-    case 32: return launch_scan<4, 8, 8, 8>(p, a->x_code, yout, code16, stream);
-    default: return launch_scan<8, 8, 4, 4>(p, a->x_code, yout, code16, stream);
-  }
+  return scan_impl(a, stage, stream);
 }
 
 }  // extern "C"

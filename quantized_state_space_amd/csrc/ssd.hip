@@ -64,7 +64,7 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 struct SsdParams {
   int64_t B, L, nh, nc;
-  int32_t Gbc, hpg, yf16;
+  int32_t Gbc, hpg, yf16, G;
   const int8_t* xq;
   const uint8_t* x_group_of;
   const float* x_scales;
@@ -142,7 +142,7 @@ __device__ __forceinline__ void fetch_head(const SsdParams& p, int64_t b, int64_
                                               uint32_t (&x)[16], float& sx) {
   const int jb = tid / 16, p4 = tid % 16;
   dt = (tid < q) ? p.delta[(b * p.L + t0 + tid) * p.nh + h] : 0.0f;
-  sx = valid_or_zero(p.x_scales[p.x_group_of[h * kP + (tid & (kP - 1))]]);
+  sx = valid_or_zero(p.x_scales[min((int)p.x_group_of[h * kP + (tid & (kP - 1))], p.G - 1)]);
   // rows advance by one time step; the opaque stride keeps the 16 row addresses from being
   // precomputed once for all heads (they would stay live across the caller's head loop)
   int64_t step = p.nh * kP;
@@ -872,6 +872,7 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   char* base = reinterpret_cast<char*>(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   const int64_t nc = (L + kQ - 1) / kQ;
   SsdParams p{B, L, nh, nc, a->ngroups, (int32_t)(nh / a->ngroups), a->y_dtype == QSSM_F16,
+              a->x_groups,
               a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
               reinterpret_cast<_Float16*>(base), reinterpret_cast<float*>(base + wl.f_off),

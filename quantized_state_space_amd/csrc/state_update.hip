@@ -21,7 +21,7 @@ constexpr int kThreads = 256;
 
 struct UpdParams {
   int64_t B, nh, P, N;
-  int32_t Gbc, hpg, gs;
+  int32_t Gbc, hpg, gs, G;
   const float* x;
   const uint8_t* x_group_of;
   const float* x_scales;
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
 
   for (int64_t k = threadIdx.x; k < p.P; k += kThreads) {
     const int64_t i = bh * p.P + k;
-    const float s = p.x_scales[p.x_group_of[h * p.P + k]];
+    const float s = p.x_scales[min((int)p.x_group_of[h * p.P + k], p.G - 1)];
     const int8_t q = quant8(p.x[i], s);
     if (p.xq_out) p.xq_out[i] = q;
     xs[k] = scale_ok(s) ? (float)q * s : 0.0f;
@@ -182,7 +182,7 @@ extern "C" qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t 
     return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
   if ((uintptr_t)a->state % 16 != 0) return fail(QSSM_ERR_INVALID_ARG, "state must be 16-byte aligned");
   if (B * nh > 0x7fffffffLL) return fail(QSSM_ERR_INVALID_ARG, "batch * nheads too large");
-  UpdParams p{B, nh, P, N, a->ngroups, (int32_t)(nh / a->ngroups), a->bc_group_size, a->x,
+  UpdParams p{B, nh, P, N, a->ngroups, (int32_t)(nh / a->ngroups), a->bc_group_size, a->x_groups, a->x,
               a->x_group_of, a->x_scales, a->B, a->C, a->B_scales, a->C_scales, a->delta, a->A,
               a->Dskip, a->state, a->y, a->xq_out, a->Bq_out, a->Cq_out};
   const int f16 = a->state_dtype == QSSM_F16;

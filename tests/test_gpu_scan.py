@@ -204,3 +204,29 @@ def test_several_bc_groups(dev, D, N, Gbc):
     check_codes(lay, ref)
     assert_rows_close(lay.y.cpu().numpy(), ref["y"], TOL_F32)
     assert_rows_close(lay.h_last.cpu().numpy(), ref["h_last"], TOL_F32, "h_last")
+
+
+@pytest.mark.parametrize("sxb,sc", [(2.0 ** -80, 2.0 ** 70), (2.0 ** 70, 2.0 ** -70)])
+def test_scan_extreme_valid_scales(dev, sxb, sc):
+    """x and B scales that are valid on their own but whose product leaves the normal fp32 range
+    (2^-160, 2^140), with a C scale that brings y back into range. The fp16-code chains run in
+    units of that product, so the kernel keeps it as a significand and an exponent. No D term, so
+    y is the state readout alone; h_last itself is outside the fp32 range here and not compared."""
+    import torch
+    print(f"\n[scan extreme scales sx = sB = {sxb:g}, sC = {sc:g}]", flush=True)
+    inp = synth.mamba1_inputs(cfg=71, batch=2, seqlen=100, dim=64, dstate=16, calib_batch=1)
+    inp["D"] = np.zeros_like(inp["D"])
+    cal = op.mamba1_calib(inp, 2, 4)
+    cal["xs"] = np.full_like(cal["xs"], sxb)
+    cal["bs"] = np.full_like(cal["bs"], sxb)
+    cal["cs"] = np.full_like(cal["cs"], sc)
+    lay = layer(dev, inp, G=2, gs=4)
+    for t, v in ((lay.xs, cal["xs"]), (lay.bs, cal["bs"]), (lay.cs, cal["cs"])):
+        t.copy_(torch.from_numpy(v))
+    lay.step()
+    ref = op.mamba1(inp, G=2, gs=4, calib=cal)
+    check_codes(lay, ref)
+    y = lay.y.cpu().numpy()
+    assert np.all(np.isfinite(y))
+    e = assert_rows_close(y, ref["y"], TOL_F32)
+    print(f"  max row error y {e:.2e}", flush=True)
