@@ -14,6 +14,7 @@ def assert_rows_close(y, ref, tol, what="y"):
     err = oracle.rowwise_error(y, ref)
     worst = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= tol, f"{what}: max row error {err.max():.3e} at row {worst}"
+    return err.max()
 
 
 # ------------------------------------------------------------------------------------------------
@@ -175,24 +176,36 @@ def test_decode_state_sizes(dev, N, state):
     assert_rows_close(got["state"], ref["state"], tol, "state")
 
 
-def test_decode_full_size_sampled(dev):
-    """Mamba2-8B-shaped decode (B=256, nh=128, P=64, N=128, fp32 state), 8 steps, launched as the
-    benchmark does; codes of every sequence bit-exact, y and state of sampled sequences."""
+@pytest.mark.parametrize("state", ["f32", "f16"])
+def test_decode_full_size_64_tokens(dev, state):
+    """The Mamba2-8B-shaped decode as configured: B=256 sequences, nh=128, P=64, N=128, 64 tokens,
+    launched as the benchmark does. At every token the codes of every sequence are bit-exact
+    against the oracle's quantization of that token's inputs; y (rows over the 64 tokens) and the
+    final state of sampled sequences are within 2e-3 (fp32 state) or 1e-2 (fp16 state)."""
     import quantized_state_space_amd as qs
-    print("\n[decode full size]", flush=True)
+    print(f"\n[decode full size, 64 tokens, {state} state]", flush=True)
     params = synth.decode_params(cfg=5)
-    steps = [synth.decode_step_inputs(k, cfg=5) for k in range(8)]
-    sample = np.array([0, 77, 255])
-    lay, got = decode_run(dev, params, steps, qs.QSSM_F32, sample=sample)
+    steps = [synth.decode_step_inputs(k, cfg=5) for k in range(64)]
+    sd = qs.QSSM_F32 if state == "f32" else qs.QSSM_F16
+    if sd == qs.QSSM_F16:  # the fp16 state starts from the fp16-rounded initial state on both sides
+        params["state0"] = params["state0"].astype(np.float16).astype(np.float32)
+    sample = np.array([0, 77, 130, 255])
+    lay, got = decode_run(dev, params, steps, sd, sample=sample)
     ref = op.decode(params, steps, batches=sample)
-    full = op.decode(params, steps[:1], batches=np.arange(256))  # codes of every sequence, step 0
-    for name in ("xq", "Bq", "Cq"):
-        assert np.array_equal(got[name][0], full[name][0]), name
-    for k in range(len(steps)):
-        for name in ("xq", "Bq", "Cq"):
-            assert np.array_equal(got[name][k][sample], ref[name][k]), (name, k)
-        assert_rows_close(got["y"][k], ref["y"][k], 2e-3)
-    assert_rows_close(got["state"], ref["state"], 2e-3, "state")
+    B, nh, P, N, Gbc = lay.shape
+    for k, inp in enumerate(steps):
+        xq = oracle.quant_group_x(inp["x"].reshape(B, nh * P, 1), ref["group_of"],
+                                  ref["xs"]).reshape(B, nh, P)
+        Bq = oracle.quant_state_group(inp["B"][..., None], 16, ref["bs"])[..., 0]
+        Cq = oracle.quant_state_group(inp["C"][..., None], 16, ref["cs"])[..., 0]
+        for name, want in (("xq", xq), ("Bq", Bq), ("Cq", Cq)):
+            assert np.array_equal(got[name][k], want), (name, k)
+    tol = 2e-3 if state == "f32" else 1e-2
+    y = np.stack(got["y"], axis=-1)          # [sample, nh, P, token]
+    yr = np.stack(ref["y"], axis=-1)
+    e = assert_rows_close(y.reshape(-1, len(steps)), yr.reshape(-1, len(steps)), tol)
+    es = assert_rows_close(got["state"], ref["state"], tol, "state")
+    print(f"  max row error y {e:.2e}, state {es:.2e}", flush=True)
 
 
 def test_s4d_empty_sequence(dev):

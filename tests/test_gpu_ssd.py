@@ -112,22 +112,26 @@ def test_ssd_int8_state_generic(dev):
 def test_ssd_invalid_scales_one_head_per_group(dev):
     """One head per B/C group (the head loops run once), and scales outside [2^-100, 2^100]: an x
     group (its channels then carry only the inter-chunk state and no D term), a B state group and a
-    C state group contribute zeros. The oracle takes the same scales."""
+    C state group contribute zeros. The group map and scales are the oracle's own calibration with
+    three scales replaced; both sides take them."""
     import torch
     print("\n[ssd invalid scales, one head per group]", flush=True)
     inp = synth.ssd_inputs(cfg=47, batch=2, seqlen=300, nheads=3, headdim=64, dstate=128,
                            ngroups=3, calib_len=256, with_h0=True)
-    import quantized_state_space_amd.workloads as wl
-    lay = wl.SsdLayer(inp, dev, with_h0=True)
-    xs, bs, cs = (t.cpu().numpy().copy() for t in (lay.xs, lay.bs, lay.cs))
+    cal = op.ssd(inp, with_h0=True, heads=np.array([0]))
+    group_of = cal["group_of"].copy()
+    xs, bs, cs = (cal[k].copy() for k in ("xs", "bs", "cs"))
     xs[2] = 0.0
     bs[5] = np.float32(1e-35)
     cs[9] = np.float32(2.0 ** 101)
-    for t, v in ((lay.xs, xs), (lay.bs, bs), (lay.cs, cs)):
+    import quantized_state_space_amd.workloads as wl
+    lay = wl.SsdLayer(inp, dev, with_h0=True)
+    lay.group_of = group_of
+    for t, v in ((lay.group_t, group_of), (lay.xs, xs), (lay.bs, bs), (lay.cs, cs)):
         t.copy_(torch.from_numpy(v))
     lay.step()
     torch.cuda.synchronize()
-    ref = op.ssd(inp, with_h0=True, calib=(lay.group_of, xs, bs, cs))
+    ref = op.ssd(inp, with_h0=True, calib=(group_of, xs, bs, cs))
     check(lay, ref)
 
 
