@@ -29,8 +29,9 @@
  *  - Launches are asynchronous on the given stream; nothing synchronizes. A device fault shows up
  *    at the caller's next synchronization. A failed launch returns QSSM_ERR_DEVICE.
  *  - No C++ exception ever crosses this boundary.
- *  - The library allocates no device memory. Entry points that need scratch take a caller-provided
- *    workspace whose size a *_workspace_size call reports.
+ *  - The library allocates no device memory at run time. Entry points that need scratch take a
+ *    caller-provided workspace whose size a *_workspace_size call reports; the one exception,
+ *    qssm_scan_w8a8_noalloc, uses a fixed-size array that is part of the library's device code.
  *  - Group maps hold indices below the group count; a larger index is read as the last group.
  *
  * Quantization rule used everywhere (int8 codes, bit-exact):
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 110 /* 1.1.0: int8 scan output fields appended to qssm_scan_args */
+#define QSSM_VERSION 120 /* 1.2.0: qssm_scan_w8a8_noalloc */
 
 typedef int32_t qssm_status;
 enum {
@@ -180,6 +181,18 @@ size_t qssm_scan_workspace_size(const qssm_scan_args* a);
 qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Allocation-free variant of qssm_scan_w8a8, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments
+ * (minus the workspace), same kernels, same results. The B/C staging goes to a library-owned
+ * device array of QSSM_SCAN_SCRATCH_BYTES bytes, one per GPU, which exists from the library's
+ * loading on that GPU until the process ends. A call whose staging needs more
+ * (qssm_scan_workspace_size(a) - 256 bytes) returns QSSM_ERR_UNSUPPORTED and launches nothing.
+ * All calls on one GPU share its array and it keeps the last call's contents (every call rewrites
+ * what it reads): calls that overlap in time on one GPU (other streams, other host threads) race,
+ * so the caller serializes them. The first call on each device looks up the array's address
+ * (thread-safe). */
+#define QSSM_SCAN_SCRATCH_BYTES (32u << 20)
+qssm_status qssm_scan_w8a8_noalloc(const qssm_scan_args* a, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * a5-a7 (S4D form). Diagonal LTI scan with int8 parameters and input.

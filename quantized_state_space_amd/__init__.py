@@ -75,6 +75,7 @@ SIGNATURES = {
     "qssm_softedge_decode": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P]),
     "qssm_scan_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScanArgs)]),
     "qssm_scan_w8a8": (_I32, [ctypes.POINTER(ScanArgs), _P, ctypes.c_size_t, _P]),
+    "qssm_scan_w8a8_noalloc": (_I32, [ctypes.POINTER(ScanArgs), _P]),
     "qssm_s4d_scan": (_I32, [ctypes.POINTER(S4dArgs), _P]),
     "qssm_ssd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SsdArgs)]),
     "qssm_ssd_chunk_int8": (_I32, [ctypes.POINTER(SsdArgs), _P, ctypes.c_size_t, _P]),
@@ -247,6 +248,17 @@ def qssm_scan_w8a8(args, workspace, stream=None):
     _check("qssm_scan_w8a8", load().qssm_scan_w8a8(
         ctypes.byref(args), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream)))
+
+
+# Size of the library-owned staging array used by qssm_scan_w8a8_noalloc (QSSM_SCAN_SCRATCH_BYTES).
+QSSM_SCAN_SCRATCH_BYTES = 32 << 20
+
+
+def qssm_scan_w8a8_noalloc(args, stream=None):
+    """The scan without a caller workspace (the library's fixed staging array; calls on one GPU
+    must not overlap)."""
+    _check("qssm_scan_w8a8_noalloc", load().qssm_scan_w8a8_noalloc(ctypes.byref(args),
+                                                                    _stream(stream)))
 
 
 def s4d_args(uq, u_scale, params, scales, log_dt, y, wq=None, w_scale=None, Dskip=None,

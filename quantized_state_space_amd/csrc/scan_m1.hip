@@ -19,6 +19,8 @@
 //  * exp(delta A) is evaluated as exp2(delta * A log2(e)) with the hardware v_exp_f32.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 using namespace qssm;
@@ -480,6 +482,8 @@ size_t stage_bytes(const qssm_scan_args* a) {
          (size_t)(a->seqlen + kPadRows) * 2 * sizeof(float);
 }
 
+constexpr size_t kScanScratchBytes = (size_t)QSSM_SCAN_SCRATCH_BYTES;
+
 // Validation, B/C staging and the scan launch; `stage` is 256-byte aligned and holds
 // stage_bytes(a) bytes (it may be null when that is 0).
 qssm_status scan_impl(const qssm_scan_args* a, void* stage_mem, hipStream_t stream) {
@@ -560,6 +564,40 @@ qssm_status validate(const qssm_scan_args* a, bool* done) {
 
 }  // namespace
 
+// Allocation-free variant: the staging buffer lives in a library-owned device array of fixed size,
+// one copy per GPU. Host code reaches it only through the address hipGetSymbolAddress returns for
+// the current device (the array's own name is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[kScanScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // per device, set once under the mutex
+
+// Device address of the scratch array on the current device (looked up once per device, with that
+// device current).
+qssm_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(QSSM_ERR_DEVICE, "cannot query the current device");
+  if (dev >= kMaxScratchDevices)
+    return fail(QSSM_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(QSSM_ERR_DEVICE, "hipGetSymbolAddress of the scan scratch array: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QSSM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t qssm_scan_workspace_size(const qssm_scan_args* a) {
@@ -579,6 +617,21 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
   void* stage = reinterpret_cast<void*>(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   if ((size_t)((char*)stage - (char*)ws) + need > ws_bytes)
     return fail(QSSM_ERR_WORKSPACE, "workspace too small after 256-byte alignment");
+  return scan_impl(a, stage, stream);
+}
+
+qssm_status qssm_scan_w8a8_noalloc(const qssm_scan_args* a, hipStream_t stream) {
+  clear_error();
+  bool done = false;
+  if (qssm_status s = validate(a, &done)) return s;
+  if (done) return QSSM_OK;
+  const size_t need = stage_bytes(a);
+  if (need > kScanScratchBytes)
+    return fail(QSSM_ERR_UNSUPPORTED,
+                "the B/C staging needs %zu bytes, above the %zu-byte scratch array of the "
+                "allocation-free entry point", need, kScanScratchBytes);
+  void* stage = nullptr;
+  if (qssm_status s = scratch_address(&stage)) return s;
   return scan_impl(a, stage, stream);
 }
 
