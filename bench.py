@@ -262,7 +262,7 @@ class Ssd(Workload):
     def __init__(self, f16=False):
         self.f16 = f16
         self.name = "mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "")
-        self.dominant = "qssm_ssd_chunk_int8: k_ssd_chunk_state + k_ssd_state_pass + k_ssd_output"
+        self.dominant = "qssm_ssd_chunk_int8: k_ssd_state + k_ssd_output"
 
     def setup(self, dev):
         import qssm_synth as synth

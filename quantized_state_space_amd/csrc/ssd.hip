@@ -8,25 +8,25 @@
 //   Y_intra = (G o exp(cum_i - cum_j) [j<=i] o delta_j) . xh           fp16 MFMA, fp32 accumulate
 //   S       = sum_j w_j xh_j Bh_j^T,  w_j = delta_j e^{cum_Q - cum_j}
 //             fp16 MFMA over time on fp16(w_j qx) and the B codes (default), or int8 MFMA on the
-//             requantized r = sat8(RNE(qx * w_j / w_max)) (option); kept as F sx sB S16, S16 in
-//             fp16, code units over a per-head bound that rules out overflow
+//             requantized r = sat8(RNE(qx * w_j / w_max)) with int32 accumulate (option; the
+//             weights and the rounding decisions in fp64)
 //   H_c     = exp(cum_Q) H_{c-1} + S                  fp32 state passing
 //   Y_inter = exp(cum_i) Ch . H_{c-1}^T               fp16 MFMA
 //   y       = Y_intra + Y_inter + D_h xh
 //
-// Three kernels (the chunk states make one round trip through the workspace):
-//   K1 k_ssd_chunk_state  one workgroup per (b, chunk, B/C group): B chunk transposed once into
-//                         fp16 operands held in registers, then per head the chunk's cumsum
-//                         (also written out for K3), the weighted x tile and a 64x128x256 MFMA.
-//   K2 k_ssd_state_pass   per (b, h) state element: sequential over chunks, writes the state
-//                         entering each chunk (fp16, C-scaled) and the final state.
-//   K3 k_ssd_output       one workgroup per (b, chunk, B/C group): G^T is built once with int8 MFMA
-//                         and kept in registers (8 waves, one query block of causal 32x32 tiles
-//                         each, two waves per SIMD); per head the inter-chunk product, the
-//                         intra-chunk product and the D term, with the next head's inputs
-//                         arriving in LDS by direct loads meanwhile.
-// The chunk states (K1) and y (K3) are written with nontemporal stores: they stream past the
-// caches instead of evicting staged inputs or leaving dirty lines for the next kernel.
+// Two kernels:
+//   K1 k_ssd_state   one workgroup per (b, head), chunks in order: per chunk the cumsum (written
+//                    out for K2), the weights, the transposed B chunk and weighted x tile in LDS, the
+//                    chunk state S^T (rows n, columns p) on MFMA, then the state entering the chunk
+//                    is written out for K2 (fp16, C-scaled, in the exact register order of K2's MFMA
+//                    operand) and H is updated in fp32 registers. The final H is h_last.
+//   K2 k_ssd_output  one workgroup per (b, chunk, B/C group): G^T is built once with int8 MFMA
+//                    and kept in registers (8 waves, one query block of causal 32x32 tiles
+//                    each, two waves per SIMD); per head the inter-chunk product, the
+//                    intra-chunk product and the D term, with the next head's inputs
+//                    arriving in LDS by direct loads meanwhile.
+// y is written with nontemporal stores: it streams past the caches instead of evicting staged
+// inputs or leaving dirty lines for the next kernel.
 // MFMA lane layouts (verified on gfx950): operand lane l holds row/column l%32 and a run of
 // consecutive k at offset (K/2)*(l/32); the 32x32 accumulator register r of lane l is element
 // (8*(r/4) + 4*(l/32) + r%4, l%32).
@@ -48,7 +48,6 @@ constexpr int kNSG = kN / kGS;
 constexpr int kRow256 = 272;  // padded bytes of a [*][256] int8 LDS row
 constexpr int kRow128 = 136;  // padded bytes of a [*][128] int8 LDS row
 constexpr int kXtRow = 260;   // padded halves of a [*][256] fp16 LDS row (520 bytes)
-constexpr int kHsRow = 136;   // padded halves of a [*][128] fp16 LDS row (272 bytes)
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 constexpr int kYPolicy = 2;  // cache policy of the y stores: nontemporal (streaming)
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued through the builtin, not
@@ -78,41 +77,19 @@ struct SsdParams {
   const float* h0;
   void* y;
   float* h_last;
-  _Float16* S;    // [B, nc, nh, P, N]: chunk states in code units over F, fp16 (see K1)
-  float* F;       // [B, nc, nh]: chunk state factor, S = F * sx[p] * sB[n] * S16
-  float* dec;     // [B, nc, nh]: exp(cum at the last step of the chunk)
-  _Float16* Hh;   // [B, nc, nh, P, N]: sC(n) * state entering the chunk, fp16 (K3's operand)
-  float* sxt;     // [nh, P]: x scale of each channel, 0 where invalid (written by K1, read by K3)
-  float* cumw;    // [B, nc, nh, Q]: cumulative sum of delta * A within the chunk (K1 -> K3)
+  _Float16* Hh;   // [B, nc, nh, 16 KB]: sC(n) * state entering the chunk, fp16, K2's operand order
+  float* sxt;     // [nh, P]: x scale of each channel, 0 where invalid (written by K1, read by K2)
+  float* cumw;    // [B, nc, nh, Q]: cumulative sum of delta * A within the chunk (K1 -> K2)
 };
 
 __device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
 
-// Inclusive prefix sum over the 256 threads of the block (one value each, in thread order).
-__device__ __forceinline__ float block_scan(float v, float* sh) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) sh[w] = v;
-  __syncthreads();
-  float pre = 0.0f;
-  for (int k = 0; k < w; ++k) pre += sh[k];
-  __syncthreads();
-  return v + pre;
-}
-
-__device__ __forceinline__ float block_max(float v, float* sh) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  __syncthreads();
-  return m;
+// Workgroup barrier that orders LDS only: outstanding global loads and stores are not waited for
+// (direct LDS loads are waited for with vmcnt by every wave before it arrives, where needed).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t d, int e) { return (d >> (8 * e)) & 0xFFu; }
@@ -135,245 +112,369 @@ __device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
   return o;
 }
 
-// Loads of one head's delta (step tid) and x codes (rows 16 (tid / 16) .. + 15, codes
-// 4 (tid % 16) .. + 3) into registers, issued one head ahead of their use in K1.
-__device__ __forceinline__ void fetch_head(const SsdParams& p, int64_t b, int64_t c, int64_t t0,
-                                              int q, int64_t h, int tid, float& dt,
-                                              uint32_t (&x)[16], float& sx) {
-  const int jb = tid / 16, p4 = tid % 16;
-  dt = (tid < q) ? p.delta[(b * p.L + t0 + tid) * p.nh + h] : 0.0f;
-  sx = valid_or_zero(p.x_scales[min((int)p.x_group_of[h * kP + (tid & (kP - 1))], p.G - 1)]);
-  // rows advance by one time step; the opaque stride keeps the 16 row addresses from being
-  // precomputed once for all heads (they would stay live across the caller's head loop)
-  int64_t step = p.nh * kP;
-  __asm__ volatile("" : "+s"(step));
-  const int8_t* row = p.xq + ((b * p.L + t0 + jb * 16) * p.nh + h) * kP + p4 * 4;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int jj = jb * 16 + r;
-    x[r] = (jj < q) ? *reinterpret_cast<const uint32_t*>(row + r * step) : 0u;
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
-// K1: chunk states, S[p][n] = sum_j w_j xh_j[p] Bh_j[n], w_j = delta_j exp(cum_last - cum_j).
-// I8 = false: fp16 operands fp16(w_j * qx[j][p]) and the exact B codes, fp32 accumulate. The
-//             accumulator is at most 127^2 sum_j w_j (times 1 + 2^-11 for the fp16 operand) in
-//             magnitude, so acc / sum_j w_j fits fp16 (|.| < 16200); it is stored so, with
-//             F = sum_j w_j.
-// I8 = true:  the weighted x is requantized per (b, chunk, head), r = sat8(RNE(qx * w_j / w_max)),
-//             int8 MFMA with int32 accumulate (|acc| <= 127^2 * 256); stored as fp16(acc / 256)
-//             with F = 256 w_max.
-// Either way S = F * sx[p] * sB[n] * S16 (fp16 keeps a relative precision of 2^-11; the factors
-// are applied in fp32 by K2).
+// K1: chunk states and their passing. One workgroup (8 waves) per pair of heads of one (b, B/C
+// group): waves 0-3 run head 2k, waves 4-7 head 2k + 1 (a half with no head, when the group has an
+// odd number of heads, repeats head 2k), chunks in order. The two heads share
+// the transposed B chunk. In a half, wave w owns states n in [32w, 32w + 32) and the state H^T
+// lives in two 32x32 fp32 accumulator tiles per wave (columns p in [0, 32) and [32, 64)): register
+// r of lane l holds H[p = 32 pt + l % 32][n = 32 w + 8 (r / 4) + 4 (l / 32) + r % 4]. Per chunk:
+//   S^T[n][p] = sum_j qB_j[n] * v_j[p], on MFMA with K = time:
+//     I8 = false: v = fp16(w_j qx_j[p]) and the B codes in fp16, fp32 accumulate; S^T = sB sx acc.
+//     I8 = true:  v = r_j[p] = sat8(RNE(qx_j[p] w_j / w_max)), w_j, w_max and the decision in
+//                 fp64 (cum in fp64 from the exact products delta * A); int8 MFMA with int32
+//                 accumulate; S^T = w_max sB sx acc.
+//   The state entering the chunk goes out first: registers 8 kb .. 8 kb + 7 of tile pt hold, for
+//   ks = 2 w + kb, the states n = 16 ks + 4 (l / 32) + {0..3, 8..11} of column p: exactly the fp16
+//   B operand K2's lane l needs for its inter-chunk product (column p, K block ks, in that
+//   within-block order), so each (pt, ks) pair is stored as 1 KB, 16 bytes per lane.
+//   Then H = exp(cum_last) H + S (fp32, sB and sx applied as two products: their own product
+//   can leave the fp32 range while H does not).
+// Loads run one chunk ahead, into registers (B, x codes, delta), with no wait before their first
+// use; the barriers order LDS only.
 constexpr int kXwRow = 264;  // padded halves of a [*][256] fp16 LDS row (528 bytes)
 
 template <bool I8>
 struct K1Smem {
-  int8_t qBT[kN * kRow256];  // B chunk transposed, [n][j]
-  int8_t rT[I8 ? kP * kRow256 : 16];                  // requantized x, [p][j] (I8)
-  _Float16 xw[I8 ? 8 : kP * kXwRow];                  // weighted x, [p][j] (fp16)
-  float wv[kQ];                                       // w_j (fp16 path) or w_j / w_max (I8)
-  float sh[12];
+  int8_t qBT[kN * kRow256];                 // B chunk transposed, [n][j]
+  int8_t rT[I8 ? 2 * kP * kRow256 : 16];    // requantized x per head, [p][j] (I8)
+  _Float16 xw[I8 ? 8 : 2 * kP * kXwRow];    // weighted x per head, [p][j] (fp16)
+  double ratio[I8 ? 2 * kQ : 1];            // w_j / w_max per head (I8)
+  float wv[I8 ? 1 : 2 * kQ];                // w_j per head (fp16 path)
+  float sxp[2 * kP];                        // x scale of each channel of each head (0: invalid)
+  float sh[16];
+  double shd[16];
 };
 
-template <bool I8>
-__global__ __launch_bounds__(256) void k_ssd_chunk_state(SsdParams p) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  K1Smem<I8>& s = *reinterpret_cast<K1Smem<I8>*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t c = blockIdx.x;
-  const int64_t b = blockIdx.y / p.Gbc;
-  const int g = (int)(blockIdx.y % p.Gbc);
+// Register loads of the B chunk c of (b, g) for the transposition: thread tid takes rows
+// 16 (tid / 32) .. + 15, bytes 4 (tid % 32) .. + 3. Branch-free: rows past the sequence are clamped
+// to the last valid row and masked by the consumer.
+__device__ __forceinline__ void fetch_b(const SsdParams& p, int64_t b, int g, int64_t c, int tid,
+                                        uint32_t (&bq)[16]) {
   const int64_t t0 = c * kQ;
   const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
-
-  // B chunk of group g, transposed to [n][j]; rows past the sequence are zero
-  for (int u = tid; u < 16 * (kN / 4); u += 256) {
-    const int jb = u / (kN / 4), n4 = u % (kN / 4);
-    uint32_t d[16];
+  const int ub = tid / (kN / 4), n4 = tid % (kN / 4);
+  const int8_t* bbase = p.Bq + ((b * p.L + t0) * p.Gbc + g) * kN + n4 * 4;
+  const int64_t bstep = (int64_t)p.Gbc * kN;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = jb * 16 + r;
-      d[r] = (j < q) ? *reinterpret_cast<const uint32_t*>(
-                           p.Bq + ((b * p.L + t0 + j) * p.Gbc + g) * kN + n4 * 4)
-                     : 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      *reinterpret_cast<uint4*>(s.qBT + (n4 * 4 + e) * kRow256 + jb * 16) = column16(d, e);
-  }
+  for (int r = 0; r < 16; ++r)
+    bq[r] = *reinterpret_cast<const uint32_t*>(bbase + min(ub * 16 + r, q - 1) * bstep);
+}
 
-  const int n = w * 32 + (lane & 31);  // this lane's output column (state)
+// Register loads of one head's chunk inputs: delta of steps 4 lane .. 4 lane + 3 (every wave holds
+// the whole chunk's delta); x codes of rows 16 (lt / 16) .. + 15, bytes 4 (lt % 16) .. + 3 (lt =
+// thread index within the half). Branch-free: rows past the sequence are clamped to the last
+// valid row and masked by the consumer, so that no wait for the loads is needed before their first
+// use one chunk later.
+__device__ __forceinline__ void fetch_x(const SsdParams& p, int64_t b, int64_t h, int64_t c, int lt,
+                                        float (&dt)[4], uint32_t (&x)[16]) {
+  const int64_t t0 = c * kQ;
+  const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
+  const int lane = lt & 63;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dt[k] = p.delta[(b * p.L + t0 + min(4 * lane + k, q - 1)) * p.nh + h];
+  const int jb = lt / 16, p4 = lt % 16;
+  const int8_t* xbase = p.xq + ((b * p.L + t0) * p.nh + h) * kP + p4 * 4;
+  const int64_t xstep = p.nh * kP;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    x[r] = *reinterpret_cast<const uint32_t*>(xbase + min(jb * 16 + r, q - 1) * xstep);
+}
+
+template <bool I8>
+__global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  K1Smem<I8>& s = *reinterpret_cast<K1Smem<I8>*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int hs = uniform(wave >> 2);   // half: which head of the pair
+  const int w = uniform(wave & 3);     // wave within the half
+  const int lt = tid & 255;            // thread within the half
+  // the pairs of one (b, group) run on one XCD (blocks are dealt to the 8 XCDs in turn), so that
+  // the group's B chunks are read from memory once and then from that XCD's L2
+  const int pairs = (p.hpg + 1) / 2;
+  const int64_t nblk = p.B * p.Gbc * pairs;
+  int64_t id = blockIdx.x;
+  if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;
+  const int64_t bg = id / pairs;
+  const int64_t b = bg / p.Gbc;
+  const int g = (int)(bg % p.Gbc);
+  const int hl = 2 * (int)(id % pairs) + hs;
+  // a half with no head computes head 2k again; its per-chunk stores write the same values to the
+  // same places as the other half's (unconditional stores keep the waits for the loads exact)
+  const bool active = hl < p.hpg;
+  const int64_t h = (int64_t)g * p.hpg + (active ? hl : hl - 1);
   const int kh = lane >> 5;
-  // fp16 path: the B codes of this lane's column as fp16 B operands, converted once for all heads
-  v8h BB[I8 ? 1 : kQ / 16];
-  if (!I8) {
-    __syncthreads();
+  const float Ah = p.A[h];
+  float* const sxp = s.sxp + hs * kP;
+
+  if (lt < kP) {
+    const float sx = valid_or_zero(p.x_scales[min((int)p.x_group_of[h * kP + lt], p.G - 1)]);
+    sxp[lt] = sx;
+    if (b == 0 && active) p.sxt[h * kP + lt] = sx;
+  }
+  // B and C scales of this wave's two state groups (ks = 2 w + kb), wave-uniform
+  float sB[2], sC[2];
 #pragma unroll
-    for (int ks = 0; ks < kQ / 16; ++ks)
-      BB[ks] = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qBT + n * kRow256 + ks * 16 + 8 * kh));
+  for (int kb = 0; kb < 2; ++kb) {
+    sB[kb] = valid_or_zero(p.B_scales[g * kNSG + 2 * w + kb]);
+    sC[kb] = valid_or_zero(p.C_scales[g * kNSG + 2 * w + kb]);
   }
 
-  float pf_dt, pf_sx;
-  uint32_t pf_x[16];
-  fetch_head(p, b, c, t0, q, (int64_t)g * p.hpg, tid, pf_dt, pf_x, pf_sx);
-  for (int hh = 0; hh < p.hpg; ++hh) {
-    const int64_t h = (int64_t)g * p.hpg + hh;
-    const float Ah = p.A[h];
-    const int j = tid;
-    const float dt = pf_dt;
-    const float cum = block_scan(dt * Ah, s.sh);
-    p.cumw[((b * p.nc + c) * p.nh + h) * kQ + j] = cum;
-    if (j == q - 1) s.sh[4] = cum;
-    __syncthreads();
-    const float cum_last = s.sh[4];
-    const float wj = (j < q) ? dt * expf(cum_last - cum) : 0.0f;
-    float wmax = 1.0f;
-    if (I8) {
-      wmax = block_max(wj, s.sh);
-      s.wv[j] = (wmax > 0.0f) ? wj / wmax : 0.0f;
-    } else {
-      s.wv[j] = wj;
-      // per-wave partial sums of w_j, combined after the barrier below
-      float ws = wj;
+  // H^T tiles from h0 (rows n = 32 w + 8 q + 4 kh + 0..3 of column p in one 16-byte read)
+  v16f H[2];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off, 64);
-      if (lane == 0) s.sh[8 + w] = ws;
+  for (int pt = 0; pt < 2; ++pt) {
+    const int pc = pt * 32 + (lane & 31);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p.h0)
+        v = *reinterpret_cast<const float4*>(p.h0 + ((b * p.nh + h) * kP + pc) * kN + 32 * w +
+                                             8 * qd + 4 * kh);
+      H[pt][4 * qd] = v.x; H[pt][4 * qd + 1] = v.y; H[pt][4 * qd + 2] = v.z; H[pt][4 * qd + 3] = v.w;
     }
-    if (tid == 0) p.dec[(b * p.nc + c) * p.nh + h] = expf(cum_last);
-    if (b == 0 && c == 0 && tid < kP) p.sxt[h * kP + tid] = pf_sx;
-    __syncthreads();
+  }
 
-    // weighted x tile, transposed [p][j]
+  // Two register sets for the loads, swapping roles from one chunk to the next (the chunk loop is
+  // unrolled twice), so that the loaded registers are never copied: a copy would wait for the
+  // loads at the end of every chunk instead of at their use one chunk later.
+  float dtA[4] = {}, dtB[4] = {};
+  uint32_t xA[16], xB[16], bA[16], bB[16];
+  if (p.nc > 0) {
+    fetch_b(p, b, g, 0, tid, bA);
+    fetch_x(p, b, h, 0, lt, dtA, xA);
+  }
+  lds_barrier();  // s.sxp
+  auto chunk = [&](const int64_t c, const float (&pf_dt)[4], const uint32_t (&pf_x)[16],
+                   const uint32_t (&pf_b)[16], float (&nx_dt)[4], uint32_t (&nx_x)[16],
+                   uint32_t (&nx_b)[16]) {
+    const int64_t t0 = c * kQ;
+    const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
+    // B chunk, transposed to [n][j]: unit tid takes rows 16 (tid / 32) .. + 15, bytes
+    // 4 (tid % 32) .. + 3; rows past the sequence are zero
     {
-      const int jb = tid / 16, p4 = tid % 16;
-      const uint32_t (&raw)[16] = pf_x;
+      const int ub = tid / (kN / 4), n4 = tid % (kN / 4);
+      uint32_t d[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) d[r] = (ub * 16 + r < q) ? pf_b[r] : 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint4*>(s.qBT + (n4 * 4 + e) * kRow256 + ub * 16) = column16(d, e);
+    }
+    // this chunk's delta and x codes (steps past the sequence are zero)
+    float dt[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dt[k] = (4 * lane + k < q) ? pf_dt[k] : 0.0f;
+    uint32_t xc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xc[r] = ((lt / 16) * 16 + r < q) ? pf_x[r] : 0u;
+    if (c + 1 < p.nc) {
+      fetch_b(p, b, g, c + 1, tid, nx_b);
+      fetch_x(p, b, h, c + 1, lt, nx_dt, nx_x);
+    }
+    // the state entering chunk c, C-scaled fp16, in K2's operand order (after the next chunk's
+    // loads, so that waiting for those does not wait for these stores)
+    {
+      _Float16* dst = p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          v8h o;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) o[m] = (_Float16)(sC[kb] * H[pt][8 * kb + m]);
+          const int ks = 2 * w + kb;
+          __builtin_nontemporal_store(o, reinterpret_cast<v8h*>(dst + ((pt * 8 + ks) * 64 + lane) * 8));
+        }
+    }
+
+
+    // Cumulative decay over the chunk, computed whole by every wave (lane l holds steps 4 l .. 4 l + 3:
+    // a serial prefix of four, then a wave scan of the lane totals), so no barrier is needed; each
+    // wave then publishes the weights of its own 64 steps (the rows of its part of the x tile) in
+    // its own LDS slice and writes their cumulative sums for K2.
+    const bool own = (lane >> 4) == w;  // lanes 16 w .. 16 w + 15 hold this wave's steps
+    float* const cw = p.cumw + ((b * p.nc + c) * p.nh + h) * kQ + 4 * lane;
+    float dec, wmax_f = 1.0f;
+    if (I8) {
+      // weights and requantization ratios in fp64 (delta * A is exact there)
+      double cs[4];
+      cs[0] = (double)dt[0] * (double)Ah;
+#pragma unroll
+      for (int k = 1; k < 4; ++k) cs[k] = cs[k - 1] + (double)dt[k] * (double)Ah;
+      double incl = cs[3];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const double excl = incl - cs[3];
+      const double tot = __shfl(incl, 63, 64);
+      double wj[4];
+      double wmax = 0.0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cs[k] += excl;
+        wj[k] = (double)dt[k] * exp(tot - cs[k]);
+        wmax = fmax(wmax, wj[k]);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) wmax = fmax(wmax, __shfl_xor(wmax, off, 64));
+      if (own) {
+        double* rt = s.ratio + hs * kQ + 4 * lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rt[k] = (wmax > 0.0) ? wj[k] / wmax : 0.0;
+        *reinterpret_cast<float4*>(cw) =
+            make_float4((float)cs[0], (float)cs[1], (float)cs[2], (float)cs[3]);
+      }
+      dec = (float)exp(tot);
+      wmax_f = (float)wmax;
+    } else {
+      float cs[4];
+      cs[0] = dt[0] * Ah;
+#pragma unroll
+      for (int k = 1; k < 4; ++k) cs[k] = fmaf(dt[k], Ah, cs[k - 1]);
+      float incl = cs[3];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const float excl = incl - cs[3];
+      const float tot = __shfl(incl, 63, 64);
+      if (own) {
+        float* wv = s.wv + hs * kQ + 4 * lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          cs[k] += excl;
+          wv[k] = dt[k] * expf(tot - cs[k]);
+        }
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(v4f{cs[0], cs[1], cs[2], cs[3]}, reinterpret_cast<v4f*>(cw));
+      }
+      dec = expf(tot);
+    }
+    // weighted (or requantized) x tile of this half's head, transposed [p][j] (a channel with an
+    // invalid scale has sx = 0 and contributes nothing)
+    {
+      const int jb = lt / 16, p4 = lt % 16;
       if (I8) {
+        const double* rt = s.ratio + hs * kQ + jb * 16;
         uint32_t d[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float rt = s.wv[jb * 16 + r];
           uint32_t word = 0u;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = (float)(int8_t)byte_of(raw[r], e) * rt;
-            const int rq = (int)fminf(fmaxf(rintf(v), -128.0f), 127.0f);
+            const double v = (double)(int8_t)byte_of(xc[r], e) * rt[r];
+            const int rq = (int)fmin(fmax(rint(v), -128.0), 127.0);
             word |= ((uint32_t)rq & 0xFFu) << (8 * e);
           }
           d[r] = word;
         }
+        int8_t* rT = s.rT + hs * (kP * kRow256);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint4*>(s.rT + (p4 * 4 + e) * kRow256 + jb * 16) = column16(d, e);
+          *reinterpret_cast<uint4*>(rT + (p4 * 4 + e) * kRow256 + jb * 16) = column16(d, e);
       } else {
+        const float* wv = s.wv + hs * kQ + jb * 16;
+        _Float16* xw = s.xw + hs * (kP * kXwRow);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           v8h lo, hi;
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            lo[r] = (_Float16)((float)(int8_t)byte_of(raw[r], e) * s.wv[jb * 16 + r]);
-            hi[r] = (_Float16)((float)(int8_t)byte_of(raw[8 + r], e) * s.wv[jb * 16 + 8 + r]);
+            lo[r] = (_Float16)((float)(int8_t)byte_of(xc[r], e) * wv[r]);
+            hi[r] = (_Float16)((float)(int8_t)byte_of(xc[8 + r], e) * wv[8 + r]);
           }
-          _Float16* dst = s.xw + (p4 * 4 + e) * kXwRow + jb * 16;
-          *reinterpret_cast<v8h*>(dst) = lo;
-          *reinterpret_cast<v8h*>(dst + 8) = hi;
+          // lanes with p4 / 4 odd write the two halves in the other order: with the 528-byte rows
+          // the 64 lanes of each write then cover every bank four times (the minimum)
+          _Float16* dst = xw + (p4 * 4 + e) * kXwRow + jb * 16;
+          const bool swap = (p4 >> 2) & 1;
+          *reinterpret_cast<v8h*>(dst + (swap ? 8 : 0)) = swap ? hi : lo;
+          *reinterpret_cast<v8h*>(dst + (swap ? 0 : 8)) = swap ? lo : hi;
         }
       }
     }
-    __syncthreads();
-    if (hh + 1 < p.hpg) fetch_head(p, b, c, t0, q, h + 1, tid, pf_dt, pf_x, pf_sx);
+    lds_barrier();
 
-    // S16[p][n] for p in two 32-row tiles; wave w owns state columns [32w, 32w + 32)
-    _Float16* Sout = p.S + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
+    // S^T tiles on MFMA
+    v16f acc[2];
+    const int nrow = 32 * w + (lane & 31);
     if (I8) {
-      v16i acc0 = {}, acc1 = {};
+      const int8_t* rT = s.rT + hs * (kP * kRow256);
+      v16i ai[2] = {};
 #pragma unroll
       for (int ks = 0; ks < kQ / 32; ++ks) {
         const int ko = ks * 32 + 16 * kh;
-        const v4i bv = *reinterpret_cast<const v4i*>(s.qBT + n * kRow256 + ko);
-        const v4i a0 = *reinterpret_cast<const v4i*>(s.rT + (lane & 31) * kRow256 + ko);
-        const v4i a1 = *reinterpret_cast<const v4i*>(s.rT + (32 + (lane & 31)) * kRow256 + ko);
-        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bv, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bv, acc1, 0, 0, 0);
-      }
-      if (tid == 0) p.F[(b * p.nc + c) * p.nh + h] = 256.0f * wmax;
+        const v4i av = *reinterpret_cast<const v4i*>(s.qBT + nrow * kRow256 + ko);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        __builtin_nontemporal_store((_Float16)((float)acc0[r] * (1.0f / 256.0f)), &Sout[prow * kN + n]);
-        __builtin_nontemporal_store((_Float16)((float)acc1[r] * (1.0f / 256.0f)),
-                                    &Sout[(32 + prow) * kN + n]);
+        for (int pt = 0; pt < 2; ++pt) {
+          const v4i bv = *reinterpret_cast<const v4i*>(rT + (pt * 32 + (lane & 31)) * kRow256 + ko);
+          ai[pt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, ai[pt], 0, 0, 0);
+        }
       }
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[pt][r] = (float)ai[pt][r] * wmax_f;
     } else {
-      v16f acc0 = {}, acc1 = {};
+      const _Float16* xw = s.xw + hs * (kP * kXwRow);
+      acc[0] = v16f{};
+      acc[1] = v16f{};
 #pragma unroll
       for (int ks = 0; ks < kQ / 16; ++ks) {
         const int ko = ks * 16 + 8 * kh;
-        const v8h bv = BB[ks];
-        const v8h a0 = *reinterpret_cast<const v8h*>(s.xw + (lane & 31) * kXwRow + ko);
-        const v8h a1 = *reinterpret_cast<const v8h*>(s.xw + (32 + (lane & 31)) * kXwRow + ko);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bv, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bv, acc1, 0, 0, 0);
-      }
-      const float wsum = s.sh[8] + s.sh[9] + s.sh[10] + s.sh[11];
-      const float inv = (wsum > 0.0f) ? 1.0f / wsum : 0.0f;
-      if (tid == 0) p.F[(b * p.nc + c) * p.nh + h] = wsum;
+        const v8h av = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qBT + nrow * kRow256 + ko));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int prow = 8 * (r / 4) + 4 * kh + (r % 4);
-        __builtin_nontemporal_store((_Float16)(acc0[r] * inv), &Sout[prow * kN + n]);
-        __builtin_nontemporal_store((_Float16)(acc1[r] * inv), &Sout[(32 + prow) * kN + n]);
+        for (int pt = 0; pt < 2; ++pt) {
+          const v8h bv = *reinterpret_cast<const v8h*>(xw + (pt * 32 + (lane & 31)) * kXwRow + ko);
+          acc[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[pt], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();
+    // H = dec H + (S sB) sx
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const float sx = sxp[pt * 32 + (lane & 31)];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) H[pt][r] = fmaf(dec, H[pt][r], (acc[pt][r] * sB[r / 8]) * sx);
+    }
+    lds_barrier();  // qBT and the x tiles are rewritten by the next chunk
+  };
+  for (int64_t c = 0; c < p.nc; c += 2) {
+    chunk(c, dtA, xA, bA, dtB, xB, bB);
+    if (c + 1 < p.nc) chunk(c + 1, dtB, xB, bB, dtA, xA, bA);
+  }
+
+  if (p.h_last && active) {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const int pc = pt * 32 + (lane & 31);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<float4*>(p.h_last + ((b * p.nh + h) * kP + pc) * kN + 32 * w + 8 * qd +
+                                   4 * kh) =
+            make_float4(H[pt][4 * qd], H[pt][4 * qd + 1], H[pt][4 * qd + 2], H[pt][4 * qd + 3]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// K2: inter-chunk state passing, H_c = dec_c H_{c-1} + S_c in fp32, S_c = F sx[p] sB[n] S16. The
-// state entering chunk c, scaled by the C scale of its state group, goes to slot c of Hh in fp16:
-// exactly the operand of the inter-chunk product in K3 (which rounds it to fp16 anyway), at half
-// the bytes.
-__global__ __launch_bounds__(256) void k_ssd_state_pass(SsdParams p) {
-  constexpr int kE4 = kP * kN / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= p.B * p.nh * kE4) return;
-  const int64_t e4 = idx % kE4, bh = idx / kE4;
-  const int64_t b = bh / p.nh, h = bh % p.nh;
-  const int g = (int)(h / p.hpg);
-  const int sgi = g * kNSG + (int)((4 * e4) % kN) / kGS;  // the 4 states share one state group
-  const float sc = valid_or_zero(p.C_scales[sgi]);
-  const float sxb = p.sxt[h * kP + (4 * e4) / kN] * valid_or_zero(p.B_scales[sgi]);
-  float4 H = p.h0 ? reinterpret_cast<const float4*>(p.h0)[bh * kE4 + e4]
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t c = 0; c < p.nc; ++c) {
-    const int64_t slot = ((b * p.nc + c) * p.nh + h) * (int64_t)kE4 + e4;
-    const v4h s16 = reinterpret_cast<const v4h*>(p.S)[slot];
-    const float f = p.F[(b * p.nc + c) * p.nh + h] * sxb;
-    const float4 s = make_float4(f * (float)s16[0], f * (float)s16[1], f * (float)s16[2],
-                                 f * (float)s16[3]);
-    const v4h hv = {(_Float16)(sc * H.x), (_Float16)(sc * H.y), (_Float16)(sc * H.z),
-                    (_Float16)(sc * H.w)};
-    reinterpret_cast<v4h*>(p.Hh)[slot] = hv;
-    const float d = p.dec[(b * p.nc + c) * p.nh + h];
-    H = make_float4(fmaf(d, H.x, s.x), fmaf(d, H.y, s.y), fmaf(d, H.z, s.z), fmaf(d, H.w, s.w));
-  }
-  if (p.h_last) reinterpret_cast<float4*>(p.h_last)[bh * kE4 + e4] = H;
-}
-
-// ---------------------------------------------------------------------------------------------
-// K3: chunk outputs.
-struct K3Smem {
+// K2: chunk outputs.
+struct K2Smem {
   int8_t qB[kQ * kRow128];  // B chunk rows [j][n]
   int8_t qC[kQ * kRow128];  // C chunk rows [i][n]
   _Float16 xT[kP * kXtRow];  // x codes of the head, [p][j] (exact in fp16)
-  _Float16 Hs[kP * kHsRow];  // sC(n) * H_prev[p][n]
-  // The next head's inputs, written by direct global-to-LDS loads while the current head computes:
-  // x codes in 1 KB blocks of 16 rows (row r of block jb at slot (r + jb) % 16, so that the
-  // transposing reads below hit distinct banks), the entering state as stored in Hh, delta, sx.
+  // The entering state of heads hh (buffer hh % 2) as stored by K1: the inter-chunk product's B
+  // operands, 1 KB per (column tile, K block); the next head's arrives by direct loads while the
+  // current head's is read.
+  _Float16 sth[2][kP * kN];
+  // The next head's other inputs, written by direct global-to-LDS loads while the current head
+  // computes: x codes in 1 KB blocks of 16 rows (row r of block jb at slot (r + jb) % 16, so that
+  // the transposing reads below hit distinct banks), delta, the cumulative decay exponents, sx.
   int8_t stx[kQ * kP];
-  _Float16 sth[kP * kN];
   float stdt[kQ];
   float stcum[kQ];
   float stsx[kP];
@@ -385,16 +486,16 @@ struct K3Smem {
   float stad;  // staged D_h
   float dh;    // D_h of the current head
 };
-static_assert(offsetof(K3Smem, stcum) % 16 == 0 && offsetof(K3Smem, cum) % 16 == 0 &&
-                  offsetof(K3Smem, dtv) % 16 == 0 &&
-                  offsetof(K3Smem, ecum) % 16 == 0 && offsetof(K3Smem, cjv) % 16 == 0,
+static_assert(offsetof(K2Smem, stcum) % 16 == 0 && offsetof(K2Smem, cum) % 16 == 0 &&
+                  offsetof(K2Smem, dtv) % 16 == 0 &&
+                  offsetof(K2Smem, ecum) % 16 == 0 && offsetof(K2Smem, cjv) % 16 == 0,
               "16-byte vector reads of the decay terms");
 
 
 // Compiler-only fence: keeps one tile's work from being interleaved with the next tile's.
 __device__ __forceinline__ void tile_fence() { __asm__ volatile("" ::: "memory"); }
 
-__device__ __forceinline__ void build_g_tile(v16f& G, const K3Smem& s, const float* sBC, int I,
+__device__ __forceinline__ void build_g_tile(v16f& G, const K2Smem& s, const float* sBC, int I,
                                              int J, int lane) {
   const int kofs = 8 * (lane >> 5);
   G = v16f{};
@@ -431,7 +532,7 @@ __device__ __forceinline__ GTile pack_g(const v16f& G) {
 // j = 32 J + 4 (l / 32) + 8 (r / 4) + r % 4, so the column terms come in runs of four (16-byte
 // reads, the same address for each half-wave). Each element is one mixed-precision fma from the
 // fp16 G value, rounded once to fp16.
-__device__ __forceinline__ void m_tile(const GTile& Gt, const K3Smem& s, int I, int J, int lane,
+__device__ __forceinline__ void m_tile(const GTile& Gt, const K2Smem& s, int I, int J, int lane,
                                        v8h& a0, v8h& a1) {
   typedef float v4f __attribute__((ext_vector_type(4)));
   const int i = I * 32 + (lane & 31);  // this lane's query row
@@ -470,20 +571,12 @@ __device__ __forceinline__ void m_tile(const GTile& Gt, const K3Smem& s, int I, 
 
 // x B operand for MFMA mm of tile column block J: lane l supplies column p and the 8 j's whose G
 // accumulator rows sit in registers 8 mm .. 8 mm + 7 of the same lane half
-__device__ __forceinline__ v8h x_operand(const K3Smem& s, int J, int mm, int pt, int lane) {
+__device__ __forceinline__ v8h x_operand(const K2Smem& s, int J, int mm, int pt, int lane) {
   const int j0 = J * 32 + 16 * mm + 4 * (lane >> 5);
   const _Float16* row = s.xT + (pt * 32 + (lane & 31)) * kXtRow;
   const v4h lo = *reinterpret_cast<const v4h*>(row + j0);
   const v4h hi = *reinterpret_cast<const v4h*>(row + j0 + 8);
   return v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// Workgroup barrier that orders LDS only: outstanding global stores (and the direct LDS loads,
-// which every wave waits for itself with vmcnt before it arrives) are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Row r (0..15) of a 16-row x block jb sits at slot ((r ^ ((r >> 3) << 1)) + jb) & 15 of its 1 KB
@@ -498,8 +591,9 @@ __device__ __forceinline__ int stx_row(int slot, int jb) {
 // Issues the direct global-to-LDS loads of head h's inputs into the staging area (no registers
 // are held: the loads complete in the background and are waited for with vmcnt before use). Rows
 // past the sequence are clamped to the last valid row here and masked by the consumer.
-__device__ __forceinline__ void stage_head(const SsdParams& p, K3Smem& s, int64_t b, int64_t c,
-                                           int64_t t0, int q, int64_t h, int wave, int lane) {
+__device__ __forceinline__ void stage_head(const SsdParams& p, K2Smem& s, int64_t b, int64_t c,
+                                           int64_t t0, int q, int64_t h, int hbuf, int wave,
+                                           int lane) {
   // LDS destinations are wave-uniform (they go to M0): byte offsets from the staging base, made
   // uniform explicitly
   unsigned char* const base = reinterpret_cast<unsigned char*>(&s);
@@ -514,30 +608,30 @@ __device__ __forceinline__ void stage_head(const SsdParams& p, K3Smem& s, int64_
     const int r = stx_row(lane >> 2, jb);
     const int j = min(jb * 16 + r, q - 1);
     const int8_t* src = p.xq + ((b * p.L + t0 + j) * p.nh + h) * kP + (lane & 3) * 16;
-    const int dst = uniform((int)offsetof(K3Smem, stx) + jb * 1024);
+    const int dst = uniform((int)offsetof(K2Smem, stx) + jb * 1024);
     __builtin_amdgcn_global_load_lds(src, base + dst, 16, 0, 0);
   }
-  // entering state: 16 KB contiguous, 1 KB per instruction
+  // entering state: 16 KB contiguous, 1 KB per instruction, into buffer hbuf
   const _Float16* hsrc = p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int blk = 2 * wave + k;
-    const int dst = uniform((int)offsetof(K3Smem, sth) + blk * 1024);
+    const int dst = uniform((int)offsetof(K2Smem, sth) + hbuf * (kP * kN * 2) + blk * 1024);
     __builtin_amdgcn_global_load_lds(hsrc + blk * 512 + lane * 8, base + dst, 16, 0, 0);
   }
   if (wave < 4) {  // delta of steps 64 w .. 64 w + 63
     const int j = min(wave * 64 + lane, q - 1);
-    const int dst = uniform((int)offsetof(K3Smem, stdt) + wave * 256);
+    const int dst = uniform((int)offsetof(K2Smem, stdt) + wave * 256);
     __builtin_amdgcn_global_load_lds(p.delta + (b * p.L + t0 + j) * p.nh + h, base + dst, 4, 0, 0);
   } else if (wave == 4) {
-    const int dst = uniform((int)offsetof(K3Smem, stsx));
+    const int dst = uniform((int)offsetof(K2Smem, stsx));
     __builtin_amdgcn_global_load_lds(p.sxt + h * kP + lane, base + dst, 4, 0, 0);
   } else if (wave == 5) {  // the chunk's cumulative decay exponents, 1 KB contiguous
-    const int dst = uniform((int)offsetof(K3Smem, stcum));
+    const int dst = uniform((int)offsetof(K2Smem, stcum));
     __builtin_amdgcn_global_load_lds(p.cumw + ((b * p.nc + c) * p.nh + h) * kQ + lane * 4, base + dst,
                                      16, 0, 0);
   } else if (wave == 6 && lane == 0 && p.Dskip) {
-    const int dst = uniform((int)offsetof(K3Smem, stad));
+    const int dst = uniform((int)offsetof(K2Smem, stad));
     __builtin_amdgcn_global_load_lds(p.Dskip + h, base + dst, 4, 0, 0);
   }
 }
@@ -548,7 +642,7 @@ __device__ __forceinline__ void stage_head(const SsdParams& p, K3Smem& s, int64_
 // head's inputs arrive in LDS by direct loads issued during the previous head's products.
 __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  K3Smem& s = *reinterpret_cast<K3Smem*>(smem_raw);
+  K2Smem& s = *reinterpret_cast<K2Smem*>(smem_raw);
   const int tid = threadIdx.x;
   const int64_t c = blockIdx.x;
   const int64_t b = blockIdx.y / p.Gbc;
@@ -573,7 +667,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     sBC[sg] = valid_or_zero(p.B_scales[g * kNSG + sg]) * valid_or_zero(p.C_scales[g * kNSG + sg]);
   lds_barrier();
   // the first head's inputs load while G is built
-  stage_head(p, s, b, c, t0, q, (int64_t)g * p.hpg, uniform(tid >> 6), tid & 63);
+  stage_head(p, s, b, c, t0, q, (int64_t)g * p.hpg, 0, uniform(tid >> 6), tid & 63);
 
   GTile G[8];
   {
@@ -591,15 +685,19 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     }
   }
   // the C codes of this wave's query block as fp16 A operands of the inter-chunk product (the
-  // same for every head)
+  // same for every head), in the K order of the stored entering state: slot m of lane half kh in
+  // K block ks is state n = 16 ks + 4 kh + (m < 4 ? m : m + 4)
   v8h QC[kN / 16];
   {
     const int lane = tid & 63;
     const int I = uniform(uniform(tid >> 6) < 4 ? uniform(tid >> 6) : 11 - uniform(tid >> 6));
+    const int8_t* crow = s.qC + (I * 32 + (lane & 31)) * kRow128 + 4 * (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kN / 16; ++ks)
-      QC[ks] = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qC + (I * 32 + (lane & 31)) * kRow128 +
-                                                           ks * 16 + 8 * (lane >> 5)));
+    for (int ks = 0; ks < kN / 16; ++ks) {
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(crow + ks * 16);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(crow + ks * 16 + 8);
+      QC[ks] = i8x8_to_h((int64_t)(((uint64_t)hi << 32) | lo));
+    }
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
@@ -623,13 +721,6 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     }
     if (tid < kP) s.sxs[tid] = s.stsx[tid];
     if (tid == 0) s.dh = p.Dskip ? s.stad : 0.0f;
-    // state entering the chunk (sC-scaled fp16 rows [p][n] of 128 halves), into padded rows
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int u = tid + 512 * k;
-      *reinterpret_cast<uint4*>(s.Hs + (u / 16) * kHsRow + (u % 16) * 8) =
-          *reinterpret_cast<const uint4*>(s.sth + u * 8);
-    }
     {
       // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale and past the
       // sequence): thread (jh, p4) takes rows 8 jh .. 8 jh + 7, channels 4 p4 .. 4 p4 + 3
@@ -658,7 +749,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     }
     lds_barrier();
     // the staging area is free: the next head's inputs load during this head's products
-    if (hh + 1 < p.hpg) stage_head(p, s, b, c, t0, q, h + 1, uniform(tid >> 6), tid & 63);
+    if (hh + 1 < p.hpg) stage_head(p, s, b, c, t0, q, h + 1, (hh + 1) & 1, uniform(tid >> 6), tid & 63);
 
     // Opaque copies of the lane and wave ids: the tile addresses below do not depend on the head,
     // and hoisting all of them out of the head loop would keep them live across it (spills).
@@ -667,15 +758,15 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     int v = uniform(tid >> 6);
     __asm__ volatile("" : "+s"(v));
     const int I = uniform(v < 4 ? v : 11 - v);  // (the asm output is not known to be uniform)
-    const int kofs = 8 * (lane >> 5);
     v16f Y[2] = {};
-    // Y_inter = exp(cum_i) * qC[i, :] . Hs[:, p]
+    // Y_inter = exp(cum_i) * qC[i, :] . (sC H)[:, p], operands straight from the staged state
+    const _Float16* hs = s.sth[hh & 1];
 #pragma unroll
     for (int ks = 0; ks < kN / 16; ++ks) {
       const v8h a = QC[ks];
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        const v8h bv = *reinterpret_cast<const v8h*>(s.Hs + (pt * 32 + (lane & 31)) * kHsRow + ks * 16 + kofs);
+        const v8h bv = *reinterpret_cast<const v8h*>(hs + ((pt * 8 + ks) * 64 + lane) * 8);
         Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bv, Y[pt], 0, 0, 0);
       }
     }
@@ -792,7 +883,7 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
 // The dynamic-LDS limit of a kernel is raised once per device (hipFuncSetAttribute applies on the
 // current device; two threads racing both make the same idempotent call).
 constexpr int kMaxDevices = 64;
-enum { kAttrK1F16 = 0, kAttrK1I8 = 1, kAttrK3 = 2 };
+enum { kAttrK1F16 = 0, kAttrK1I8 = 1, kAttrK2 = 2 };
 std::atomic<bool> g_lds_raised[3][kMaxDevices];
 
 bool raise_lds_limit(int which, const void* fn, size_t bytes) {
@@ -807,20 +898,15 @@ bool raise_lds_limit(int which, const void* fn, size_t bytes) {
 }
 
 struct WsLayout {
-  size_t s_bytes, f_off, dec_off, hh_off, sx_off, cum_off, total;
+  size_t sx_off, cum_off, total;  // Hh at offset 0
 };
 
-// workspace: S16 (fp16 chunk states), F, dec, Hh (fp16 entering states), sxt, cumw, each
-// 256-byte aligned
+// workspace: Hh (fp16 entering states), sxt, cumw, each 256-byte aligned
 WsLayout ws_layout(const qssm_ssd_args* a) {
   const int64_t nc = (a->seqlen + kQ - 1) / kQ;
   const size_t elems = (size_t)a->batch * nc * a->nheads * kP * kN;
   WsLayout w;
-  w.s_bytes = elems * sizeof(_Float16);
-  w.f_off = (w.s_bytes + 255) & ~(size_t)255;
-  w.dec_off = (w.f_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
-  w.hh_off = (w.dec_off + (size_t)a->batch * nc * a->nheads * sizeof(float) + 255) & ~(size_t)255;
-  w.sx_off = (w.hh_off + elems * sizeof(_Float16) + 255) & ~(size_t)255;
+  w.sx_off = (elems * sizeof(_Float16) + 255) & ~(size_t)255;
   w.cum_off = (w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 255) & ~(size_t)255;
   w.total = w.cum_off + (size_t)a->batch * nc * a->nheads * kQ * sizeof(float) + 256;
   return w;
@@ -875,31 +961,28 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
               a->x_groups,
               a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
-              reinterpret_cast<_Float16*>(base), reinterpret_cast<float*>(base + wl.f_off),
-              reinterpret_cast<float*>(base + wl.dec_off),
-              reinterpret_cast<_Float16*>(base + wl.hh_off),
-              reinterpret_cast<float*>(base + wl.sx_off),
+              reinterpret_cast<_Float16*>(base), reinterpret_cast<float*>(base + wl.sx_off),
               reinterpret_cast<float*>(base + wl.cum_off)};
-  if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff)
+  if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff || B * nh > 0x7fffffff)
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
-  const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
-  if (nc > 0) {
+  // K1 runs even for an empty sequence: it writes h_last = h0 (or zeros)
+  {
     const int i8 = a->state_mma == QSSM_MMA_I8;
-    const void* k1 = i8 ? reinterpret_cast<const void*>(&k_ssd_chunk_state<true>)
-                        : reinterpret_cast<const void*>(&k_ssd_chunk_state<false>);
+    const void* k1 = i8 ? reinterpret_cast<const void*>(&k_ssd_state<true>)
+                        : reinterpret_cast<const void*>(&k_ssd_state<false>);
     const size_t k1_lds = i8 ? sizeof(K1Smem<true>) : sizeof(K1Smem<false>);
     if (!raise_lds_limit(i8 ? kAttrK1I8 : kAttrK1F16, k1, k1_lds))
-      return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD chunk-state kernel");
-    if (i8) k_ssd_chunk_state<true><<<grid, 256, k1_lds, stream>>>(p);
-    else k_ssd_chunk_state<false><<<grid, 256, k1_lds, stream>>>(p);
-    if (qssm_status s = launch_status("ssd chunk state")) return s;
+      return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD state kernel");
+    const unsigned k1_grid = (unsigned)(B * a->ngroups * ((nh / a->ngroups + 1) / 2));
+    if (i8) k_ssd_state<true><<<k1_grid, 512, k1_lds, stream>>>(p);
+    else k_ssd_state<false><<<k1_grid, 512, k1_lds, stream>>>(p);
+    if (qssm_status s = launch_status("ssd chunk states")) return s;
   }
-  k_ssd_state_pass<<<(unsigned)cdiv(B * nh * (kP * kN / 4), 256), 256, 0, stream>>>(p);
-  if (qssm_status s = launch_status("ssd state passing")) return s;
   if (nc > 0) {
-    if (!raise_lds_limit(kAttrK3, reinterpret_cast<const void*>(&k_ssd_output), sizeof(K3Smem)))
+    if (!raise_lds_limit(kAttrK2, reinterpret_cast<const void*>(&k_ssd_output), sizeof(K2Smem)))
       return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD output kernel");
-    k_ssd_output<<<grid, 512, sizeof(K3Smem), stream>>>(p);
+    const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
+    k_ssd_output<<<grid, 512, sizeof(K2Smem), stream>>>(p);
     if (qssm_status s = launch_status("ssd output")) return s;
   }
   return QSSM_OK;

@@ -53,7 +53,7 @@ def test_mamba1_layer_step_replays(dev):
 
 
 def test_ssd_layer_step_replays(dev):
-    """Quantize x, B, C, then the three SSD kernels."""
+    """Quantize x, B, C, then the two SSD kernels."""
     import torch
     import quantized_state_space_amd.workloads as wl
     print("\n[graph: ssd layer step]", flush=True)
