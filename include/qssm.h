@@ -362,6 +362,30 @@ qssm_status qssm_calib_softedge(const float* v, int64_t n, double alpha, int32_t
 qssm_status qssm_calib_channel_error_mean(const float* ref, const float* approx, int64_t outer,
                                           int64_t C, int64_t inner, float* mean_out);
 
+/* out[g] = largest absmax[c] over the channels c with group_of[c] == g (0 for an empty group), the
+ * group absmax from which qssm_calib_scales makes per-group scales. absmax values must be finite
+ * and >= 0; group_of[c] < G <= 256. */
+qssm_status qssm_calib_group_absmax(const float* absmax, const uint8_t* group_of, int64_t C,
+                                    int32_t G, float* out);
+
+/* out[k] = largest of absmax[k * block .. k * block + block - 1] (contiguous state groups of B or C:
+ * absmax over the Gbc * N states, block = gs). block must divide n; values finite and >= 0. */
+qssm_status qssm_calib_block_absmax(const float* absmax, int64_t n, int32_t block, float* out);
+
+/* Per-channel scale of the int16 S4D state ("Quantizing Small-Scale State-Space Models for Edge
+ * AI", abstract: the internal state is a sensitive part), from the quantized parameters alone:
+ * for each state n of channel h, with Re A = A_re_s[h] A_re[h,n], B = B_re_s[h] B_re[h,n] +
+ * i B_im_s[h] B_im[h,n],
+ * dt = exp(log_dt[h]) and |u| <= umax[h], the state obeys |h_t| <= dt |B| e^{max(0, dt Re A)}
+ * umax sum_{k < L} |Abar|^k with |Abar| = e^{dt Re A} (the sum is 1 / (1 - |Abar|) at most when
+ * |Abar| < 1). out[h] = headroom * max_n(bound) / 32767, clamped to [2^-100, 2^100], so the int16
+ * codes of both parts never saturate. Planes [H, N] int8, scales [H]; headroom >= 1. */
+qssm_status qssm_calib_s4d_state_scale(int64_t H, int64_t N, int64_t L, const int8_t* A_re,
+                                       const float* A_re_s, const int8_t* B_re,
+                                       const float* B_re_s, const int8_t* B_im,
+                                       const float* B_im_s, const float* log_dt,
+                                       const float* umax, double headroom, float* out);
+
 /* ---------------------------------------------------------------------------------------------
  * Library information. */
 const char* qssm_status_string(qssm_status s);

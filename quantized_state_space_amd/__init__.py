@@ -85,6 +85,10 @@ SIGNATURES = {
     "qssm_calib_cluster_channels": (_I32, [_P, _I32, _I32, _P, _P]),
     "qssm_calib_softedge": (_I32, [_P, _I64, ctypes.c_double, _I32, _P, _P, _P, _P]),
     "qssm_calib_channel_error_mean": (_I32, [_P, _P, _I64, _I64, _I64, _P]),
+    "qssm_calib_group_absmax": (_I32, [_P, _P, _I64, _I32, _P]),
+    "qssm_calib_block_absmax": (_I32, [_P, _I64, _I32, _P]),
+    "qssm_calib_s4d_state_scale": (_I32, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_double, _P]),
     "qssm_status_string": (ctypes.c_char_p, [_I32]),
     "qssm_last_error": (ctypes.c_char_p, []),
     "qssm_version": (_I32, []),
@@ -409,3 +413,44 @@ def qssm_calib_softedge(v, alpha=0.1, ema_state=None):
         _np_ptr(v), v.size, float(alpha), int(ema_state is not None), _np_ptr(st), _np_ptr(s),
         _np_ptr(L), _np_ptr(H)))
     return s[0], L[0], H[0], st
+
+
+def qssm_calib_group_absmax(absmax, group_of, G):
+    """Per-group maximum of channel absmax values (host arrays)."""
+    import numpy as np
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    g = np.ascontiguousarray(group_of, dtype=np.uint8).reshape(-1)
+    if a.size != g.size:
+        raise ValueError("absmax and group_of must have one entry per channel")
+    out = np.empty(G, np.float32)
+    _check("qssm_calib_group_absmax",
+           load().qssm_calib_group_absmax(_np_ptr(a), _np_ptr(g), a.size, G, _np_ptr(out)))
+    return out
+
+
+def qssm_calib_block_absmax(absmax, block):
+    """Maximum of each contiguous block of `block` values (host array)."""
+    import numpy as np
+    a = np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)
+    out = np.empty(a.size // block if block > 0 else 0, np.float32)
+    _check("qssm_calib_block_absmax",
+           load().qssm_calib_block_absmax(_np_ptr(a), a.size, block, _np_ptr(out)))
+    return out
+
+
+def qssm_calib_s4d_state_scale(L, A_re, A_re_s, B_re, B_re_s, B_im, B_im_s, log_dt, umax,
+                               headroom=1.25):
+    """Per-channel int16 S4D state scale from the quantized parameters (host arrays: int8 planes
+    [H, N], fp32 scales [H], log_dt [H], umax [H])."""
+    import numpy as np
+    c8 = lambda a: np.ascontiguousarray(a, dtype=np.int8)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32).reshape(-1)
+    planes = [c8(A_re), c8(B_re), c8(B_im)]
+    H, N = planes[0].shape
+    sc = [f32(A_re_s), f32(B_re_s), f32(B_im_s), f32(log_dt), f32(umax)]
+    out = np.empty(H, np.float32)
+    _check("qssm_calib_s4d_state_scale", load().qssm_calib_s4d_state_scale(
+        H, N, L, _np_ptr(planes[0]), _np_ptr(sc[0]), _np_ptr(planes[1]), _np_ptr(sc[1]),
+        _np_ptr(planes[2]), _np_ptr(sc[2]), _np_ptr(sc[3]), _np_ptr(sc[4]), float(headroom),
+        _np_ptr(out)))
+    return out

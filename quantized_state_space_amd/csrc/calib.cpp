@@ -174,4 +174,80 @@ qssm_status qssm_calib_channel_error_mean(const float* ref, const float* approx,
   return QSSM_OK;
 }
 
+qssm_status qssm_calib_group_absmax(const float* absmax, const uint8_t* group_of, int64_t C,
+                                    int32_t G, float* out) {
+  qssm::clear_error();
+  if (C < 0 || G < 1 || G > 256) return fail(QSSM_ERR_INVALID_ARG, "bad C or G");
+  if (!out || (C > 0 && (!absmax || !group_of))) return fail(QSSM_ERR_INVALID_ARG, "null pointer");
+  for (int32_t g = 0; g < G; ++g) out[g] = 0.0f;
+  for (int64_t c = 0; c < C; ++c) {
+    const int g = group_of[c];
+    if (g >= G) return fail(QSSM_ERR_INVALID_ARG, "group_of[%lld] = %d is not below G", (long long)c, g);
+    if (!(absmax[c] >= 0.0f) || std::isinf(absmax[c]))
+      return fail(QSSM_ERR_INVALID_ARG, "absmax[%lld] is not finite and >= 0", (long long)c);
+    if (absmax[c] > out[g]) out[g] = absmax[c];
+  }
+  return QSSM_OK;
+}
+
+qssm_status qssm_calib_block_absmax(const float* absmax, int64_t n, int32_t block, float* out) {
+  qssm::clear_error();
+  if (n < 0 || block < 1 || n % block != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "block must divide n");
+  if (!out || (n > 0 && !absmax)) return fail(QSSM_ERR_INVALID_ARG, "null pointer");
+  for (int64_t k = 0; k < n / block; ++k) {
+    float m = 0.0f;
+    for (int32_t i = 0; i < block; ++i) {
+      const float a = absmax[k * block + i];
+      if (!(a >= 0.0f) || std::isinf(a))
+        return fail(QSSM_ERR_INVALID_ARG, "absmax[%lld] is not finite and >= 0",
+                    (long long)(k * block + i));
+      if (a > m) m = a;
+    }
+    out[k] = m;
+  }
+  return QSSM_OK;
+}
+
+qssm_status qssm_calib_s4d_state_scale(int64_t H, int64_t N, int64_t L, const int8_t* A_re,
+                                       const float* A_re_s, const int8_t* B_re,
+                                       const float* B_re_s, const int8_t* B_im,
+                                       const float* B_im_s, const float* log_dt,
+                                       const float* umax, double headroom, float* out) {
+  qssm::clear_error();
+  if (H < 1 || N < 1 || L < 0) return fail(QSSM_ERR_INVALID_ARG, "bad shape");
+  if (!A_re || !A_re_s || !B_re || !B_re_s || !B_im || !B_im_s || !log_dt || !umax || !out)
+    return fail(QSSM_ERR_INVALID_ARG, "null pointer");
+  if (!(headroom >= 1.0)) return fail(QSSM_ERR_INVALID_ARG, "headroom must be >= 1");
+  const double steps = (double)(L > 0 ? L : 1);
+  for (int64_t h = 0; h < H; ++h) {
+    const double dt = std::exp((double)log_dt[h]);
+    double m = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const int64_t i = h * N + n;
+      const double are = (double)A_re_s[h] * (double)A_re[i];
+      const double bre = (double)B_re_s[h] * (double)B_re[i];
+      const double bim = (double)B_im_s[h] * (double)B_im[i];
+      // |Bbar| = |exp(dt A) - 1| / |A| |B| <= dt |B| exp(max(0, dt Re A)); |Abar| = exp(dt Re A)
+      const double ab = std::exp(dt * are);
+      const double bbar = dt * std::sqrt(bre * bre + bim * bim) * (ab > 1.0 ? ab : 1.0);
+      // sum over at most L steps of |Abar|^k
+      double geo;
+      if (ab < 1.0) {
+        geo = 1.0 / (1.0 - ab);
+        if (geo > steps) geo = steps;
+      } else {
+        geo = steps * std::pow(ab, steps - 1.0);
+      }
+      const double bound = bbar * (double)umax[h] * geo;
+      if (bound > m) m = bound;
+    }
+    double s = headroom * m / 32767.0;
+    if (!(s >= 0x1p-100)) s = 0x1p-100;
+    if (s > 0x1p100) s = 0x1p100;
+    out[h] = (float)s;
+  }
+  return QSSM_OK;
+}
+
 }  // extern "C"

@@ -11,8 +11,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (QSSM_F16, QSSM_F32, QSSM_I16, QSSM_X_INT8, QSSM_X_SOFTEDGE, qssm_calib_channel_absmax,
-               qssm_calib_cluster_channels, qssm_calib_scales, qssm_calib_softedge,
+from . import (QSSM_F16, QSSM_F32, QSSM_I16, QSSM_X_INT8, QSSM_X_SOFTEDGE, qssm_calib_block_absmax,
+               qssm_calib_channel_absmax, qssm_calib_cluster_channels, qssm_calib_group_absmax,
+               qssm_calib_s4d_state_scale, qssm_calib_scales, qssm_calib_softedge,
                qssm_quant_group_x, qssm_quant_state_group_BC, qssm_s4d_scan, qssm_scan_w8a8,
                qssm_scan_workspace_size, qssm_softedge_encode, qssm_ssd_chunk_int8,
                qssm_ssd_workspace_size, qssm_state_update, s4d_args, scan_args, ssd_args,
@@ -35,17 +36,14 @@ def calib_x_groups(x_cal, G):
     cluster into G groups, one scale per group. Returns (perm, group_of, scales)."""
     ch = qssm_calib_channel_absmax(x_cal)
     perm, group_of = qssm_calib_cluster_channels(ch, G)
-    g_abs = np.zeros(G, dtype=np.float32)
-    np.maximum.at(g_abs, group_of.astype(np.int64), ch[perm])
-    return perm, group_of, qssm_calib_scales(g_abs)
+    return perm, group_of, qssm_calib_scales(qssm_calib_group_absmax(ch[perm], group_of, G))
 
 
 def calib_state_groups(bc_cal, gs):
     """Per-(group, state group) scales of B or C from a calibration tensor [outer, Gbc, N, inner]."""
     outer, Gbc, N, inner = bc_cal.shape
     ch = qssm_calib_channel_absmax(np.ascontiguousarray(bc_cal).reshape(outer, Gbc * N, inner))
-    g_abs = ch.reshape(Gbc, N // gs, gs).max(axis=2).reshape(-1)
-    return qssm_calib_scales(g_abs)
+    return qssm_calib_scales(qssm_calib_block_absmax(ch, gs))
 
 
 def calib_y_groups(y_cal, G):
@@ -56,9 +54,7 @@ def calib_y_groups(y_cal, G):
     perm, grp = qssm_calib_cluster_channels(ch, G)
     group_of = np.empty(ch.size, np.uint8)
     group_of[perm] = grp
-    g_abs = np.zeros(G, dtype=np.float32)
-    np.maximum.at(g_abs, group_of.astype(np.int64), ch)
-    return group_of, qssm_calib_scales(g_abs)
+    return group_of, qssm_calib_scales(qssm_calib_group_absmax(ch, group_of, G))
 
 
 def calib_softedge(x_cal, perm, group_of, G):
@@ -201,7 +197,19 @@ class S4dLayer:
         self.log_dt = _dev(inp["log_dt"], dev)
         self.D = _dev(inp["D"], dev)
         self.state_dtype = state_dtype
-        self.state_scale = None if state_scale is None else _dev(np.asarray(state_scale, np.float32), dev)
+        if state_dtype == QSSM_I16 and state_scale is None:
+            # int16 state without a given scale: the library's bound from the quantized parameters
+            # (|u| <= u_scale * w_scale * 128 * |w code| per channel, headroom 1.25)
+            host = {k: self.params[k].cpu().numpy() for k in ("A_re", "B_re", "B_im")}
+            hs = {k: self.scales[k].cpu().numpy() for k in ("A_re", "B_re", "B_im")}
+            wq = self.wq.cpu().numpy().reshape(-1).astype(np.float32)
+            umax = (self.u_scale.cpu().numpy()[0] * self.w_scale.cpu().numpy()[0] * np.float32(128.0)
+                    * np.abs(wq)).astype(np.float32)
+            state_scale = qssm_calib_s4d_state_scale(L, host["A_re"], hs["A_re"], host["B_re"],
+                                                     hs["B_re"], host["B_im"], hs["B_im"],
+                                                     inp["log_dt"], umax)
+        self.state_scale_host = None if state_scale is None else np.asarray(state_scale, np.float32)
+        self.state_scale = None if state_scale is None else _dev(self.state_scale_host, dev)
         sdt = torch.float32 if state_dtype == QSSM_F32 else torch.int16
         self.h0 = None
         if with_h0:
@@ -245,16 +253,14 @@ def calib_ssd_x_groups(x_cal, nheads, headdim, ngroups, groups_per_block):
     ch = qssm_calib_channel_absmax(xc)
     per_block = C // ngroups
     group_of = np.empty(C, np.uint8)
-    g_abs = np.zeros(ngroups * groups_per_block, np.float32)
     for k in range(ngroups):
         sl = slice(k * per_block, (k + 1) * per_block)
         perm, grp = qssm_calib_cluster_channels(ch[sl], groups_per_block)
-        gid = grp.astype(np.int64) + k * groups_per_block
-        blk = np.empty(per_block, np.int64)
-        blk[perm] = gid
-        group_of[sl] = blk.astype(np.uint8)
-        np.maximum.at(g_abs, blk, ch[sl])
-    return group_of, qssm_calib_scales(g_abs)
+        blk = np.empty(per_block, np.uint8)
+        blk[perm] = grp + np.uint8(k * groups_per_block)
+        group_of[sl] = blk
+    return group_of, qssm_calib_scales(qssm_calib_group_absmax(ch, group_of,
+                                                               ngroups * groups_per_block))
 
 
 class SsdLayer:

@@ -173,3 +173,69 @@ def test_softedge_thresholds_match_oracle():
     s2, L2, H2, _ = qs.qssm_calib_softedge(v2, ema_state=st)
     os2, oL2, oH2, _ = oracle.softedge_thresholds(v2, prev=ost)
     assert (s2, L2, H2) == (os2, oL2, oH2)
+
+
+def test_group_and_block_absmax():
+    r = np.random.default_rng(10)
+    a = np.abs(r.standard_normal(300)).astype(np.float32)
+    g = r.integers(0, 7, 300).astype(np.uint8)
+    got = qs.qssm_calib_group_absmax(a, g, 9)
+    for k in range(9):
+        sel = a[g == k]
+        assert got[k] == (sel.max() if sel.size else 0.0)
+    assert np.array_equal(qs.qssm_calib_block_absmax(a, 4), a.reshape(75, 4).max(axis=1))
+    with pytest.raises(qs.QssmError, match="below G"):
+        qs.qssm_calib_group_absmax(a, g, 5)
+    with pytest.raises(qs.QssmError, match="divide"):
+        qs.qssm_calib_block_absmax(a, 7)
+
+
+def test_layer_calibrations_match_oracle():
+    """The workload drivers' calibration (library helpers) equals the oracle's, bit for bit: the
+    Mamba1 x groups and B/C state groups, the SSD head-block x groups, the int8 output groups."""
+    import oracle.pipelines as op
+    import quantized_state_space_amd.workloads as wl
+    inp = synth.mamba1_inputs(cfg=81, batch=1, seqlen=200, dim=192, dstate=16, x_dist="student_t",
+                              calib_batch=2)
+    p1, g1, s1 = wl.calib_x_groups(inp["x_cal"], 8)
+    p2, g2, s2 = op.calib_x(inp["x_cal"], 8)
+    assert np.array_equal(p1, p2) and np.array_equal(g1, g2) and np.array_equal(s1, s2)
+    assert np.array_equal(wl.calib_state_groups(inp["B_cal"], 4),
+                          oracle.state_group_scales(inp["B_cal"], 4))
+    x = synth.rng(82, 0).standard_normal((300, 8, 64)).astype(np.float32) * \
+        np.exp(synth.rng(82, 1).uniform(-2, 2, (8, 64))).astype(np.float32)
+    ga, sa = wl.calib_ssd_x_groups(x, 8, 64, 2, 8)
+    gb, sb = op.calib_ssd_x(x, 8, 64, 2, 8)
+    assert np.array_equal(ga, gb) and np.array_equal(sa, sb)
+    yg, ys = wl.calib_y_groups(inp["x_cal"], 5)
+    absmax = oracle.finite_absmax(inp["x_cal"], axis=(0, 2))
+    perm, grp = oracle.cluster_channels(absmax, 5)
+    want_g = np.empty(absmax.size, np.uint8)
+    want_g[perm] = grp
+    want_s = oracle.group_scales(inp["x_cal"], want_g, 5)
+    assert np.array_equal(yg, want_g) and np.array_equal(ys, want_s)
+
+
+def test_s4d_state_scale_bounds_the_fp64_state():
+    """The int16 state scale from the quantized parameters bounds the fp64 state of the oracle's
+    run: with headroom 1, max |Re h|, |Im h| of every channel <= 32767 * scale; and the scale
+    follows the stated formula (evaluated here in numpy)."""
+    import oracle.pipelines as op
+    inp = synth.s4d_inputs(cfg=2, batch=4, seqlen=300, channels=12, dstate=64)
+    ref = op.s4d(inp)
+    c, sc = ref["codes"], ref["scales"]
+    umax = (np.float32(ref["su"]) * np.float32(ref["sw"]) * np.float32(128.0) *
+            np.abs(ref["wq"].astype(np.float32))).astype(np.float32)
+    L = inp["u"].shape[1]
+    got = qs.qssm_calib_s4d_state_scale(L, c["A_re"], sc["A_re"], c["B_re"], sc["B_re"], c["B_im"],
+                                        sc["B_im"], inp["log_dt"], umax, headroom=1.0)
+    actual = op.s4d_state_scale(inp, headroom=1.0) * 32767.0    # max |part| of the fp64 state
+    assert np.all(actual <= got.astype(np.float64) * 32767.0 * (1 + 1e-6))
+    dt = np.exp(inp["log_dt"].astype(np.float64))[:, None]
+    are = sc["A_re"].astype(np.float64)[:, None] * c["A_re"]
+    bb = np.hypot(sc["B_re"].astype(np.float64)[:, None] * c["B_re"],
+                  sc["B_im"].astype(np.float64)[:, None] * c["B_im"])
+    ab = np.exp(dt * are)
+    geo = np.where(ab < 1, np.minimum(1 / np.maximum(1 - ab, 1e-300), L), L * ab ** (L - 1))
+    want = (dt * bb * np.maximum(ab, 1) * umax.astype(np.float64)[:, None] * geo).max(axis=1) / 32767
+    np.testing.assert_allclose(got, want.astype(np.float32), rtol=1e-6)
