@@ -1,17 +1,26 @@
 """Benchmark of the quantized state-space hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c3se|c3i8y|c1|c2|c4|c4f16|c5|c5f16]
-                [--only] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only] [--no-cpu-baseline]
 
 One step = one pass of the whole hot path of the workload over one batch of synthetic input that is
-already resident in HBM: for the Mamba1 layers, quantize x (gathered into cluster order), quantize B
-and C, run the W8A8 scan; for S4D, quantize the input then scan; for the SSD layer, quantize x, B, C
-then run the chunked SSD; for decode, one fused state update of every sequence.
+already resident in HBM: for the SSD layer (the default, the largest configuration: Mamba2-8B-shaped,
+B 4, L 4096, 128 heads x 64, N 128, 8 groups), quantize x, B and C, then run the chunked SSD; for
+the Mamba1 layers, quantize x (gathered into cluster order), quantize B and C, run the W8A8 scan;
+for S4D, quantize the input then scan; for decode, one fused state update of every sequence.
 
-Prints one JSON line: throughput in state-updates/s (B*L*D*N per step), the dominant kernel's
-roofline figures measured with HIP events on the launch stream, and the oracle timed on this host.
-Unless --only is given, the line also carries a short run of the other configurations
-(other_configs: S4D, soft-edge Mamba1, SSD, decode fp32 and fp16) with their own rooflines.
+Per workload, in order:
+  1. one step on the GPU;
+  2. the oracle on a bounded sample of the same workload, repeated for a few seconds: its rate is
+     the cpu_baseline, and its result is the parity reference;
+  3. the parity gate: codes bit-exact, outputs of the sample within the stated tolerance (the
+     process exits with status 3 on a mismatch, before any timing);
+  4. W warmup and K timed steps; `value` from the wall clock over the K steps, and HIP events on the
+     launch stream around every 2nd call of the dominant entry point (mean for the roofline,
+     median and min reported).
+
+Prints one JSON line. Unless --only is given it also carries the other configurations
+(other_configs), each with its own parity result, roofline and cpu_baseline, and a row for the
+quantizers alone with the soft-edge / int8 encode ratio.
 """
 from __future__ import annotations
 
@@ -34,20 +43,59 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "quantized scan state-updates/s (B·L·D·N) + % of HBM peak, 1 MI355X"
 
 
+class ParityError(RuntimeError):
+    pass
+
+
+def row_error(y, ref, axis=-1):
+    """Per-row normwise error max|y - r| / max(max|r|, 1e-6 max_all|r|) (complex: modulus)."""
+    y = np.asarray(y)
+    ref = np.asarray(ref)
+    dt = np.complex128 if (np.iscomplexobj(y) or np.iscomplexobj(ref)) else np.float64
+    y = y.astype(dt)
+    ref = ref.astype(dt)
+    floor = 1e-6 * max(np.abs(ref).max(initial=0.0), 1e-300)
+    return np.abs(y - ref).max(axis=axis) / np.maximum(np.abs(ref).max(axis=axis), floor)
+
+
+def require(cond, what):
+    if not cond:
+        raise ParityError(what)
+
+
+def codes_equal(got, want, name):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    require(got.shape == want.shape, f"{name}: shape {got.shape} vs {want.shape}")
+    n = int(np.count_nonzero(got.view(np.uint8) != want.view(np.uint8)))
+    require(n == 0, f"{name}: {n} codes differ")
+    return int(got.size)
+
+
+def rows_close(got, want, tol, name, axis=-1):
+    e = float(row_error(got, want, axis=axis).max(initial=0.0))
+    require(e <= tol, f"{name}: max row error {e:.3e} above {tol:g}")
+    return e
+
+
 # ------------------------------------------------------------------------------------------------
 # workloads
 
 class Workload:
     name = ""
-    dominant = ""           # kernel timed for the roofline
+    dominant = ""           # the entry point timed for the roofline
     bound = "hbm"
+    tol = 2e-3
     config: dict = {}
+    sample_desc = ""
 
     def setup(self, dev): ...
     def step(self, timer): ...
     def updates(self): ...
     def dominant_bytes(self): ...
-    def cpu_baseline(self): ...
+    def oracle_ref(self): ...          # the oracle on the sample (timed as the cpu baseline)
+    def sample_updates(self): ...      # state updates the sample computes
+    def check(self, ref): ...          # parity of the GPU state after the first step
 
 
 class Mamba1(Workload):
@@ -69,13 +117,10 @@ class Mamba1(Workload):
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.c3_inputs()
         xc = qs.QSSM_X_SOFTEDGE if self.soft else qs.QSSM_X_INT8
-        # two copies of every buffer, used in turn, so that one step's 350 MB of traffic cannot be
-        # served from the previous step's lines in the 256 MB last-level cache
         y_out = None
         if self.y_int8:
             # int8 output for the next W8A8 module: 8 clustered output groups calibrated on one
             # fp32-output pass, and a seeded per-channel correction term (~1% of a channel's range)
-            import numpy as np
             import torch
             cal = wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc)
             cal.step()
@@ -86,6 +131,9 @@ class Mamba1(Workload):
             ch = qs.qssm_calib_channel_absmax(y)
             yb = (synth.rng(3, 12).standard_normal(ch.size) * 0.01 * ch).astype(np.float32)
             y_out = (yg, ys, yb)
+        self.y_out = y_out
+        # two copies of every buffer, used in turn, so that one step's 350 MB of traffic cannot be
+        # served from the previous step's lines in the 256 MB last-level cache
         self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc, y_out=y_out)
                        for _ in range(2)]
         self.k = 0
@@ -96,6 +144,7 @@ class Mamba1(Workload):
                        "bc_state_groups": N // 4, "state": "f32",
                        "y": "int8, 8 output groups + per-channel correction" if self.y_int8
                        else "f32"}
+        self.sample_desc = "full workload (8 x 1536 channels x 2048 steps): quantize, dequantize, fp64 scan"
 
     def step(self, timer):
         lay = self.layers[self.k % len(self.layers)]
@@ -109,6 +158,8 @@ class Mamba1(Workload):
         B, D, L, N, _ = self.dims
         return B * D * L * N
 
+    sample_updates = updates
+
     def ops(self):
         return self.ops_per_update * self.updates()
 
@@ -121,17 +172,43 @@ class Mamba1(Workload):
         return (B * D * L * (1 + 4 + yb) + 2 * B * Gbc * N * L + 4 * D * N + 4 * D + 4 * B * D * N
                 + extra)
 
-    def cpu_baseline(self):
+    def oracle_ref(self):
         import oracle.pipelines as op
-        cal = op.mamba1_calib(self.inp, 8, 4, soft_edge=self.soft)
-        reps, dt = timed_reps(lambda: op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=cal))
-        return reps * self.updates() / dt, f"full workload (8 x 1536 channels x 2048 steps) x {reps}: " \
-            "quantize, dequantize, fp64 scan"
+        if not hasattr(self, "_cal"):
+            self._cal = op.mamba1_calib(self.inp, 8, 4, soft_edge=self.soft)
+        return op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=self._cal)
+
+    def check(self, ref):
+        lay = self.layers[0]  # ran the first step
+        n = codes_equal(lay.xq.cpu().numpy(), ref["xq"], "x codes")
+        n += codes_equal(lay.Bq.cpu().numpy(), ref["Bq"], "B codes")
+        n += codes_equal(lay.Cq.cpu().numpy(), ref["Cq"], "C codes")
+        out = {"codes_bit_exact": n}
+        out["h_last_row_error"] = rows_close(lay.h_last.cpu().numpy(), ref["h_last"], self.tol,
+                                             "h_last")
+        if not self.y_int8:
+            out["y_row_error"] = rows_close(lay.y.float().cpu().numpy(), ref["y"], self.tol, "y")
+        else:
+            # decode the int8 codes with the static output scales and correction term: every
+            # unsaturated code is within half a step (plus the fp32-state tolerance of the row) of
+            # the oracle's y + bias
+            yg, ys, yb = self.y_out
+            codes = lay.y.cpu().numpy().astype(np.float64)
+            s = np.asarray(ys, np.float64)[np.asarray(yg, np.int64)][None, :, None]
+            v = np.asarray(ref["y"], np.float64) + np.asarray(yb, np.float64)[None, :, None]
+            inside = (codes > -128) & (codes < 127)
+            rowmax = np.abs(ref["y"]).max(axis=-1, keepdims=True)
+            dev = np.abs(codes * s - v) - (0.5 * s + self.tol * rowmax)
+            bad = int(np.count_nonzero((dev > 1e-9 * s) & inside))
+            require(bad == 0, f"int8 y: {bad} codes off by more than half a step")
+            out["y_int8_codes_within_half_step"] = int(np.count_nonzero(inside))
+        return out
 
 
 class Tiny(Mamba1):
     def __init__(self):
         self.soft = False
+        self.y_int8 = False
         self.name = "tiny-mamba1-w8a8"
         self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
         self.bound = "alu"
@@ -146,33 +223,39 @@ class Tiny(Mamba1):
         B, D, L, N, _ = self.dims
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
                        "x_groups": 1, "bc_state_groups": 4, "state": "f32", "y": "f32"}
+        self.sample_desc = "full workload, on-device scales"
 
-    def cpu_baseline(self):
+    def oracle_ref(self):
         import oracle.pipelines as op
-        reps, dt = timed_reps(lambda: op.mamba1(self.inp, G=1, gs=4, dynamic=True))
-        return reps * self.updates() / dt, f"full workload x {reps}"
+        return op.mamba1(self.inp, G=1, gs=4, dynamic=True)
 
 
 class S4d(Workload):
+    # per complex state update, in the cheapest form the kernel uses (the chain on g = h / Bbar'):
+    # Abar g + q (4 FMA-class) and Re(C' g) (2 FMA-class)
+    ops_per_update = 6
+
     def __init__(self, i16=False):
         self.i16 = i16
         self.name = "s4d-smnist-shaped" + ("-int16-state" if i16 else "")
         self.dominant = "qssm_s4d_scan: k_s4d"
         self.bound = "alu"
+        self.tol = 1e-2 if i16 else 2e-3
 
     def setup(self, dev):
         import qssm_synth as synth
         import quantized_state_space_amd as qs
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.s4d_inputs()
-        ss = None
-        self.lay = wl.S4dLayer(self.inp, dev, state_dtype=qs.QSSM_I16 if self.i16 else qs.QSSM_F32,
-                               state_scale=ss)
-        self.ss = ss
+        # int16 state: the per-channel scale from the library's host calibration (the recurrence's
+        # geometric bound on the quantized parameters)
+        self.lay = wl.S4dLayer(self.inp, dev, state_dtype=qs.QSSM_I16 if self.i16 else qs.QSSM_F32)
         B, L, H, N = self.lay.shape
         self.dims = (B, L, H, N)
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "channels": H,
                        "d_state_complex": N, "state": "int16" if self.i16 else "f32", "y": "f32"}
+        self.sample_desc = "full workload, fp64 complex scan" + (
+            " with the same int16 state grid" if self.i16 else "")
 
     def step(self, timer):
         import quantized_state_space_amd as qs
@@ -186,76 +269,29 @@ class S4d(Workload):
         B, L, H, N = self.dims
         return B * L * H * N
 
-    def dominant_bytes(self):
-        B, L, H, N = self.dims
-        return B * L + H + 6 * H * N + 4 * 8 * H + 4 * B * H * L + 8 * B * H * N
-
-    # per complex state update, in the cheapest form the kernel uses (the chain on g = h / Bbar'):
-    # Abar g + q (4 FMA-class) and Re(C' g) (2 FMA-class)
-    ops_per_update = 6
+    sample_updates = updates
 
     def ops(self):
         return self.ops_per_update * self.updates()
 
-    def cpu_baseline(self):
-        import oracle.pipelines as op
-        reps, dt = timed_reps(lambda: op.s4d(self.inp, state_scale=self.ss))
-        return reps * self.updates() / dt, f"full workload x {reps}, fp64 complex scan"
-
-
-class Decode(Workload):
-    def __init__(self, f16=False):
-        self.f16 = f16
-        self.name = "mamba2-8b-decode" + ("-fp16-state" if f16 else "")
-        self.dominant = "qssm_state_update: k_state_update"
-
-    def setup(self, dev):
-        import torch
-        import qssm_synth as synth
-        import quantized_state_space_amd as qs
-        import quantized_state_space_amd.workloads as wl
-        self.params = synth.decode_params()
-        self.lay = wl.DecodeLayer(self.params, dev, state_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32)
-        B, nh, P, N, Gbc = self.lay.shape
-        self.dims = self.lay.shape
-        self.nsteps = 64
-        self.inputs = [synth.decode_step_inputs(k) for k in range(self.nsteps)]
-        # all 64 tokens resident in HBM; one argument block per token
-        self.dev_inputs = []
-        self.args = []
-        for k, inp in enumerate(self.inputs):
-            d = {n: torch.from_numpy(inp[n]).to(dev) for n in ("x", "B", "C", "delta")}
-            self.dev_inputs.append(d)
-            self.args.append(qs.update_args(d["x"], self.lay.group_t, self.lay.xs, d["B"], d["C"],
-                                            self.lay.bs, self.lay.cs, 16, d["delta"], self.lay.A,
-                                            self.lay.state, self.lay.y, Dskip=self.lay.D))
-        self.k = 0
-        self.config = {"workload": self.name, "batch": B, "heads": nh, "headdim": P, "d_state": N,
-                       "ngroups": Gbc, "tokens": self.nsteps, "state": "f16" if self.f16 else "f32"}
-
-    def step(self, timer):
-        import quantized_state_space_amd as qs
-        timer.start()
-        qs.qssm_state_update(self.args[self.k % self.nsteps])
-        timer.stop()
-        self.k += 1
-
-    def updates(self):
-        B, nh, P, N, _ = self.dims
-        return B * nh * P * N
-
     def dominant_bytes(self):
-        B, nh, P, N, Gbc = self.dims
-        sb = 2 if self.f16 else 4
-        return 2 * sb * B * nh * P * N + 4 * (2 * B * nh * P + 2 * B * Gbc * N + B * nh)
+        B, L, H, N = self.dims
+        sb = 4 if self.i16 else 8
+        return B * L + H + 6 * H * N + 4 * 8 * H + 4 * B * H * L + sb * B * H * N
 
-    def cpu_baseline(self):
+    def oracle_ref(self):
         import oracle.pipelines as op
-        sample = np.arange(16)
-        reps, dt = timed_reps(lambda: op.decode(self.params, self.inputs[:8], batches=sample))
-        B, nh, P, N, _ = self.dims
-        return reps * 8 * len(sample) * nh * P * N / dt, \
-            f"16 of 256 sequences x 8 tokens (fp64 state) x {reps}"
+        return op.s4d(self.inp, state_scale=self.lay.state_scale_host if self.i16 else None)
+
+    def check(self, ref):
+        out = {"codes_bit_exact": codes_equal(self.lay.uq.cpu().numpy()[:, 0, :], ref["uq"],
+                                              "input codes")}
+        out["y_row_error"] = rows_close(self.lay.y.cpu().numpy(), ref["y"], self.tol, "y")
+        if not self.i16:
+            hl = self.lay.h_last.cpu().numpy()
+            out["h_last_row_error"] = rows_close(hl[..., 0] + 1j * hl[..., 1], ref["h_last"],
+                                                 self.tol, "h_last")
+        return out
 
 
 class Ssd(Workload):
@@ -263,6 +299,7 @@ class Ssd(Workload):
         self.f16 = f16
         self.name = "mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "")
         self.dominant = "qssm_ssd_chunk_int8: k_ssd_state + k_ssd_output"
+        self.heads = np.array([0, 64])
 
     def setup(self, dev):
         import qssm_synth as synth
@@ -275,6 +312,8 @@ class Ssd(Workload):
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "heads": nh, "headdim": P,
                        "d_state": N, "ngroups": Gbc, "chunk": 256, "x_groups": int(self.lay.G),
                        "bc_state_groups": N // 16, "state": "f32", "y": "f16" if self.f16 else "f32"}
+        self.sample_desc = (f"{len(self.heads)} of {nh} heads (all batches, full length): the fp64 "
+                            "chunked form, including quantizing the layer's whole x, B and C")
 
     def step(self, timer):
         self.lay.quantize()
@@ -286,6 +325,10 @@ class Ssd(Workload):
         B, L, nh, P, N, _ = self.dims
         return B * L * nh * P * N
 
+    def sample_updates(self):
+        B, L, nh, P, N, _ = self.dims
+        return B * L * len(self.heads) * P * N
+
     def dominant_bytes(self):
         B, L, nh, P, N, Gbc = self.dims
         yb = 2 if self.f16 else 4
@@ -293,27 +336,121 @@ class Ssd(Workload):
         return B * L * nh * P * (1 + yb) + 4 * B * L * nh + 2 * B * L * Gbc * N + 8 * nh + \
             4 * B * nh * P * N
 
-    def cpu_baseline(self):
+    def oracle_ref(self):
         import oracle.pipelines as op
-        heads = np.array([0, 64])
-        reps, dt = timed_reps(lambda: op.ssd(self.inp, heads=heads))
-        B, L, nh, P, N, _ = self.dims
-        return reps * B * L * len(heads) * P * N / dt, f"2 of 128 heads (all batches, full " \
-            f"length) x {reps}: fp64 chunked form incl. quantizing the layer's x, B, C"
+        return op.ssd(self.inp, heads=self.heads)
+
+    def check(self, ref):
+        lay = self.lay
+        n = codes_equal(lay.xq.cpu().numpy(), ref["xq"], "x codes")
+        n += codes_equal(lay.Bq.cpu().numpy(), ref["Bq"], "B codes")
+        n += codes_equal(lay.Cq.cpu().numpy(), ref["Cq"], "C codes")
+        import torch
+        hsel = torch.as_tensor(self.heads, device=lay.y.device)
+        y = lay.y[:, :, hsel].float().cpu().numpy().astype(np.float64)
+        rows = lambda a: np.asarray(a, np.float64).transpose(0, 2, 3, 1).reshape(-1, a.shape[1])
+        out = {"codes_bit_exact": n, "y_row_error": rows_close(rows(y), rows(ref["y"]), self.tol, "y")}
+        hl = lay.h_last[:, hsel].cpu().numpy()
+        out["h_last_row_error"] = rows_close(hl.reshape(-1, hl.shape[-1]),
+                                             ref["h_last"].reshape(-1, hl.shape[-1]), self.tol,
+                                             "h_last")
+        return out
+
+
+class Decode(Workload):
+    def __init__(self, f16=False):
+        self.f16 = f16
+        self.name = "mamba2-8b-decode" + ("-fp16-state" if f16 else "")
+        self.dominant = "qssm_state_update: k_state_update"
+        self.tol = 1e-2 if f16 else 2e-3
+        self.sample = np.array([0, 77, 130, 255])
+        self.base_sample = np.arange(16)
+
+    def setup(self, dev):
+        import torch
+        import qssm_synth as synth
+        import quantized_state_space_amd as qs
+        import quantized_state_space_amd.workloads as wl
+        self.params = synth.decode_params()
+        if self.f16:  # the fp16 state starts from the fp16-rounded initial state on both sides
+            self.params["state0"] = self.params["state0"].astype(np.float16).astype(np.float32)
+        self.lay = wl.DecodeLayer(self.params, dev, state_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32)
+        B, nh, P, N, Gbc = self.lay.shape
+        self.dims = self.lay.shape
+        self.nsteps = 64
+        self.inputs = [synth.decode_step_inputs(k) for k in range(self.nsteps)]
+        # all 64 tokens resident in HBM; one argument block per token (the first also publishes the
+        # codes, for the parity gate)
+        self.codes = (torch.empty((B, nh, P), dtype=torch.int8, device=dev),
+                      torch.empty((B, Gbc, N), dtype=torch.int8, device=dev),
+                      torch.empty((B, Gbc, N), dtype=torch.int8, device=dev))
+        self.dev_inputs = []
+        self.args = []
+        for k, inp in enumerate(self.inputs):
+            d = {n: torch.from_numpy(inp[n]).to(dev) for n in ("x", "B", "C", "delta")}
+            self.dev_inputs.append(d)
+            self.args.append(qs.update_args(d["x"], self.lay.group_t, self.lay.xs, d["B"], d["C"],
+                                            self.lay.bs, self.lay.cs, 16, d["delta"], self.lay.A,
+                                            self.lay.state, self.lay.y, Dskip=self.lay.D))
+        d = self.dev_inputs[0]
+        self.gate_args = qs.update_args(d["x"], self.lay.group_t, self.lay.xs, d["B"], d["C"],
+                                        self.lay.bs, self.lay.cs, 16, d["delta"], self.lay.A,
+                                        self.lay.state, self.lay.y, Dskip=self.lay.D,
+                                        xq_out=self.codes[0], Bq_out=self.codes[1],
+                                        Cq_out=self.codes[2])
+        self.k = 0
+        self.config = {"workload": self.name, "batch": B, "heads": nh, "headdim": P, "d_state": N,
+                       "ngroups": Gbc, "tokens": self.nsteps, "state": "f16" if self.f16 else "f32"}
+        self.sample_desc = (f"{len(self.base_sample)} of {B} sequences x 8 tokens, fp64 state "
+                            "(parity: the first token of 4 sequences, codes of all 256)")
+
+    def step(self, timer):
+        import quantized_state_space_amd as qs
+        timer.start()
+        qs.qssm_state_update(self.gate_args if self.k == 0 else self.args[self.k % self.nsteps])
+        timer.stop()
+        self.k += 1
+
+    def updates(self):
+        B, nh, P, N, _ = self.dims
+        return B * nh * P * N
+
+    def sample_updates(self):
+        B, nh, P, N, _ = self.dims
+        return 8 * len(self.base_sample) * nh * P * N
+
+    def dominant_bytes(self):
+        B, nh, P, N, Gbc = self.dims
+        sb = 2 if self.f16 else 4
+        return 2 * sb * B * nh * P * N + 4 * (2 * B * nh * P + 2 * B * Gbc * N + B * nh)
+
+    def oracle_ref(self):
+        import oracle.pipelines as op
+        op.decode(self.params, self.inputs[:8], batches=self.base_sample)  # the timed sample
+        return op.decode(self.params, self.inputs[:1], batches=self.sample)
+
+    def check(self, ref):
+        import oracle
+        B, nh, P, N, Gbc = self.dims
+        inp = self.inputs[0]
+        # codes of every sequence for the first token, by the oracle's quantizer and calibration
+        xq = oracle.quant_group_x(inp["x"].reshape(B, nh * P, 1), ref["group_of"],
+                                  ref["xs"]).reshape(B, nh, P)
+        Bq = oracle.quant_state_group(inp["B"][..., None], 16, ref["bs"])[..., 0]
+        Cq = oracle.quant_state_group(inp["C"][..., None], 16, ref["cs"])[..., 0]
+        n = codes_equal(self.codes[0].cpu().numpy(), xq, "x codes")
+        n += codes_equal(self.codes[1].cpu().numpy(), Bq, "B codes")
+        n += codes_equal(self.codes[2].cpu().numpy(), Cq, "C codes")
+        import torch
+        sel = torch.as_tensor(self.sample, device=self.lay.y.device)
+        y = self.lay.y[sel].cpu().numpy()
+        st = self.lay.state[sel].float().cpu().numpy()
+        return {"codes_bit_exact": n,
+                "y_row_error": rows_close(y, ref["y"][0], self.tol, "y"),
+                "state_row_error": rows_close(st, ref["state"], self.tol, "state")}
 
 
 _zc = {}
-
-
-def timed_reps(fn, min_seconds=10.0):
-    """Runs fn until at least min_seconds of wall time have passed; returns (reps, seconds)."""
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        fn()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            return reps, dt
 
 
 def _zero(device):
@@ -324,11 +461,11 @@ def _zero(device):
     return _zc[k]
 
 
-WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True),
-             "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
-             "c2": lambda: S4d(False), "c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
-             "c5": lambda: Decode(False),
+WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True), "c3": lambda: Mamba1(False),
+             "c3se": lambda: Mamba1(True), "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
+             "c2": lambda: S4d(False), "c2i16": lambda: S4d(True), "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True)}
+OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3i8y", "c4f16", "c5", "c5f16")
 
 
 # ------------------------------------------------------------------------------------------------
@@ -336,7 +473,7 @@ WORKLOADS = {"c3": lambda: Mamba1(False), "c3se": lambda: Mamba1(True),
 # HBM traffic of one call of the dominant entry point, from two rocprofv3 counter runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, summed over the call's kernels), each divided by
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
-# workload: (fetch bytes, write bytes, sha256 of the kernel sources when the counters were taken).
+# workload: (fetch bytes, write bytes, digest of the kernel sources when the counters were taken).
 TRAFFIC = {
     "c3": (152089444, 132508472, "82855a741382f2d7"),
     "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
@@ -349,7 +486,7 @@ TRAFFIC = {
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
-    "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"],
+    "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"], "c2i16": ["s4d.hip"],
     "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c5": ["state_update.hip"],
     "c5f16": ["state_update.hip"],
 }
@@ -390,10 +527,10 @@ def copy_probe(torch, dev, nbytes=1 << 30, reps=3):
 
 class EventTimer:
     """HIP events around the dominant call, recorded on the stream the library launches on, for
-    every `every`-th timed call (a pair of event records costs ~6 us of stream time per call, which
-    would otherwise be charged to the step)."""
+    every `every`-th timed call (a pair of event records adds a few us of stream time to the step it
+    brackets)."""
 
-    def __init__(self, torch, every=4):
+    def __init__(self, torch, every=2):
         self.torch = torch
         self.pairs = []
         self.active = False
@@ -414,14 +551,47 @@ class EventTimer:
                 self.pairs[-1][1] = e
             self.calls += 1
 
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+    def samples_ms(self):
+        return np.array([a.elapsed_time(b) for a, b in self.pairs])
 
 
-def run_workload(torch, dev, name, steps, warmup):
-    """Sets up workload `name`, runs warmup + timed steps; returns (workload, results)."""
+class _NoTimer:
+    def start(self):
+        pass
+
+    def stop(self):
+        pass
+
+
+def cpu_and_parity(wl, budget_s, with_baseline=True):
+    """Runs the oracle on the workload's sample (repeated for budget_s for the rate) and gates on
+    parity. Returns (cpu_baseline dict or None, parity dict)."""
+    import oracle
+    t0 = time.perf_counter()
+    ref = wl.oracle_ref()
+    reps = 1
+    while with_baseline and time.perf_counter() - t0 < budget_s:
+        wl.oracle_ref()
+        reps += 1
+    dt = time.perf_counter() - t0
+    parity = wl.check(ref)
+    parity["tolerance"] = wl.tol
+    base = None
+    if with_baseline:
+        base = {"value": reps * wl.sample_updates() / dt, "unit": "state-updates/s",
+                "cores": oracle.max_threads(), "kind": "oracle",
+                "sample": f"{wl.sample_desc}; {reps} rep(s) in {dt:.1f} s"}
+    return base, parity
+
+
+def run_workload(torch, dev, name, steps, warmup, budget_s, with_baseline=True):
+    """Sets up workload `name`, gates it on parity, runs warmup + timed steps; returns
+    (workload, results)."""
     wl = WORKLOADS[name]()
     wl.setup(dev)
+    wl.step(_NoTimer())
+    torch.cuda.synchronize()
+    base, parity = cpu_and_parity(wl, budget_s, with_baseline)
     timer = EventTimer(torch)
     for _ in range(warmup):
         wl.step(timer)
@@ -432,7 +602,8 @@ def run_workload(torch, dev, name, steps, warmup):
         wl.step(timer)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_ms = timer.mean_ms()
+    samples = timer.samples_ms()
+    kern_ms = float(samples.mean())
     nbytes = wl.dominant_bytes()
     if wl.bound == "alu":
         achieved = wl.ops() / (kern_ms * 1e-3) / 1e12
@@ -445,13 +616,67 @@ def run_workload(torch, dev, name, steps, warmup):
     roof["traffic"] = measured_traffic(name)
     roof["kernel"] = wl.dominant
     roof["kernel_us"] = round(kern_ms * 1e3, 2)
+    roof["kernel_us_median"] = round(float(np.median(samples)) * 1e3, 2)
+    roof["kernel_us_min"] = round(float(samples.min()) * 1e3, 2)
+    roof["kernel_samples"] = int(samples.size)
     roof["algorithmic_bytes"] = int(nbytes)
     if wl.bound == "alu":
         roof["ops_per_update"] = wl.ops_per_update
     res = {"value": wl.updates() * steps / elapsed, "ms_per_step": elapsed * 1e3 / steps,
-           "roofline": roof,
+           "roofline": roof, "parity": parity,
            "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if base is not None:
+        res["cpu_baseline"] = base
     return wl, res
+
+
+def quantizer_row(torch, dev, reps=20):
+    """The x quantizers alone on the Mamba1-130M x (8 x 1536 x 2048, cluster gather, 8 groups):
+    int8 and soft-edge encode on the same bytes, event-timed, codes checked against the oracle."""
+    import oracle
+    import qssm_synth as synth
+    import quantized_state_space_amd as qs
+    import quantized_state_space_amd.workloads as wl
+    inp = synth.c3_inputs()
+    lay = wl.Mamba1Layer(inp, 8, 4, dev)
+    s, Lt, Ht = wl.calib_softedge(inp["x_cal"], lay.perm, lay.group_of, 8)
+    st, Lt_t, Ht_t = (torch.from_numpy(a).to(dev) for a in (s, Lt, Ht))
+    code = torch.empty(lay.xq.shape, dtype=torch.uint8, device=dev)
+    calls = {"int8": lambda: qs.qssm_quant_group_x(lay.x, lay.group_t, 8, lay.xs, lay.xq,
+                                                   perm=lay.perm_t),
+             "softedge": lambda: qs.qssm_softedge_encode(lay.x, lay.group_t, 8, st, Lt_t, Ht_t,
+                                                         code, perm=lay.perm_t)}
+    for f in calls.values():
+        f()
+    torch.cuda.synchronize()
+    # parity: the codes of both encoders against the oracle's (with its own calibration), bit for bit
+    import oracle.pipelines as op
+    perm, group_of, xs = op.calib_x(inp["x_cal"], 8)
+    se = op.calib_softedge(inp["x_cal"], perm, group_of, 8)
+    want8 = oracle.quant_group_x(inp["x"], group_of, xs, perm=perm)
+    codes_equal(lay.xq.cpu().numpy(), want8, "int8 x codes")
+    wantse = oracle.softedge_encode(inp["x"], group_of, se[0], se[1], se[2], perm=perm)
+    codes_equal(code.cpu().numpy(), wantse, "soft-edge x codes")
+    stream = torch.cuda.current_stream()
+    out = {}
+    n = inp["x"].size
+    for k, f in calls.items():
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        ts = np.array(ts)
+        out[k] = {"us_median": round(float(np.median(ts)), 2), "us_min": round(float(ts.min()), 2),
+                  "GB_s": round(5 * n / (np.median(ts) * 1e-6) / 1e9, 1)}
+    out["softedge_over_int8"] = round(out["softedge"]["us_median"] / out["int8"]["us_median"], 3)
+    out["workload"] = "mamba1-130m x: 8 x 1536 x 2048 fp32 -> codes, cluster gather, 8 groups"
+    out["parity"] = "codes of both encoders bit-exact against the oracle"
+    return out
 
 
 def main():
@@ -459,10 +684,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c4", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", dest="all_configs", action="store_true", default=True,
-                    help="also run the other configurations briefly (default)")
+                    help="also run the other configurations (default)")
     ap.add_argument("--only", dest="all_configs", action="store_false",
                     help="run the selected workload only")
     ap.add_argument("--copy-probe", action="store_true",
@@ -485,36 +710,43 @@ def main():
     if args.copy_probe:
         copy_probe(torch, dev)
         return
-    wl, res = run_workload(torch, dev, args.workload, args.steps, args.warmup)
-    out = {"metric": METRIC, "value": res["value"], "unit": "state-updates/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-           "data": "synthetic", "config": wl.config, "roofline": res["roofline"],
-           "hbm_frac_dominant": res["hbm_frac_dominant"],
-           "timing": "HIP events on the launch stream around every 4th timed call of the "
-                     "dominant entry point; value from the wall clock over the timed steps"}
-    if not args.no_cpu_baseline:
-        v, sample = wl.cpu_baseline()
-        import oracle
-        threads = oracle.max_threads()
-        out["cpu_baseline"] = {"value": v, "unit": "state-updates/s", "cores": threads,
-                               "kind": "oracle", "sample": sample}
-    del wl
-    if args.all_configs:
-        # the other configurations of the same metric, briefly (same protocol, fewer steps)
-        others = {}
-        for name in ("c2", "c3se", "c3i8y", "c4", "c5", "c5f16"):
-            if name == args.workload:
-                continue
-            w2, r2 = run_workload(torch, dev, name, min(args.steps, 30), min(args.warmup, 3))
-            others[name] = {"workload": w2.config["workload"], "value": r2["value"],
-                            "ms_per_step": r2["ms_per_step"],
-                            "roofline": {k: r2["roofline"][k] for k in
-                                         ("bound", "achieved", "peak", "unit", "frac", "traffic",
-                                          "kernel_us")}}
-            del w2
-            torch.cuda.empty_cache()
-        out["other_configs"] = others
+    try:
+        wl, res = run_workload(torch, dev, args.workload, args.steps, args.warmup, 10.0,
+                               not args.no_cpu_baseline)
+        out = {"metric": METRIC, "value": res["value"], "unit": "state-updates/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+               "data": "synthetic", "config": wl.config, "roofline": res["roofline"],
+               "parity": res["parity"], "hbm_frac_dominant": res["hbm_frac_dominant"],
+               "timing": "value: wall clock over the timed steps; roofline: HIP events on the "
+                         "launch stream around every 2nd timed call of the dominant entry point "
+                         "(mean; median and min also given)"}
+        if "cpu_baseline" in res:
+            out["cpu_baseline"] = res["cpu_baseline"]
+        del wl
+        if args.all_configs:
+            others = {}
+            for name in OTHERS:
+                if name == args.workload:
+                    continue
+                w2, r2 = run_workload(torch, dev, name, min(args.steps, 30), min(args.warmup, 3),
+                                      2.0, not args.no_cpu_baseline)
+                e = {"workload": w2.config["workload"], "value": r2["value"],
+                     "ms_per_step": r2["ms_per_step"], "parity": r2["parity"],
+                     "roofline": {k: r2["roofline"][k] for k in
+                                  ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                   "kernel_us", "kernel_us_median", "kernel_us_min")}}
+                if "cpu_baseline" in r2:
+                    e["cpu_baseline"] = r2["cpu_baseline"]
+                others[name] = e
+                del w2
+                torch.cuda.empty_cache()
+            others["quantizers"] = quantizer_row(torch, dev)
+            out["other_configs"] = others
+    except ParityError as e:
+        print(json.dumps({"error": "parity gate failed", "detail": str(e)}), file=sys.stderr,
+              flush=True)
+        sys.exit(3)
     print(json.dumps(out), flush=True)
 
 
