@@ -295,9 +295,11 @@ class S4d(Workload):
 
 
 class Ssd(Workload):
-    def __init__(self, f16=False):
+    def __init__(self, f16=False, y_int8=False):
         self.f16 = f16
-        self.name = "mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "")
+        self.y_int8 = y_int8
+        self.name = ("mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "") +
+                     ("-int8-y" if y_int8 else ""))
         self.dominant = "qssm_ssd_chunk_int8: k_ssd_state + k_ssd_output"
         self.heads = np.array([0, 64])
 
@@ -306,12 +308,32 @@ class Ssd(Workload):
         import quantized_state_space_amd as qs
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.ssd_inputs(cfg=4, calib_len=256)
-        self.lay = wl.SsdLayer(self.inp, dev, y_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32)
+        y_out = None
+        if self.y_int8:
+            # int8 output for the next W8A8 module: 8 clustered output groups per head block,
+            # calibrated on one fp32-output pass, and a seeded per-channel correction term (~1% of
+            # a channel's range)
+            import torch
+            cal = wl.SsdLayer(self.inp, dev)
+            cal.step()
+            B, L, nh, P, N, Gbc = cal.shape
+            y = cal.y.cpu().numpy().reshape(B * L, nh * P)
+            del cal
+            torch.cuda.empty_cache()
+            yg, ys = wl.calib_ssd_x_groups(y, nh, P, Gbc, 8)
+            ch = qs.qssm_calib_channel_absmax(y.reshape(B * L, nh * P, 1))
+            yb = (synth.rng(4, 12).standard_normal(ch.size) * 0.01 * ch).astype(np.float32)
+            y_out = (yg, ys, yb)
+        self.y_out = y_out
+        self.lay = wl.SsdLayer(self.inp, dev, y_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32,
+                               y_out=y_out)
         B, L, nh, P, N, Gbc = self.lay.shape
         self.dims = self.lay.shape
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "heads": nh, "headdim": P,
                        "d_state": N, "ngroups": Gbc, "chunk": 256, "x_groups": int(self.lay.G),
-                       "bc_state_groups": N // 16, "state": "f32", "y": "f16" if self.f16 else "f32"}
+                       "bc_state_groups": N // 16, "state": "f32",
+                       "y": "int8, 8 output groups per head block + per-channel correction"
+                       if self.y_int8 else ("f16" if self.f16 else "f32")}
         self.sample_desc = (f"{len(self.heads)} of {nh} heads (all batches, full length): the fp64 "
                             "chunked form, including quantizing the layer's whole x, B and C")
 
@@ -331,7 +353,7 @@ class Ssd(Workload):
 
     def dominant_bytes(self):
         B, L, nh, P, N, Gbc = self.dims
-        yb = 2 if self.f16 else 4
+        yb = 1 if self.y_int8 else (2 if self.f16 else 4)
         # x codes, delta, B/C codes, A, D in; y out; h_last out (each once)
         return B * L * nh * P * (1 + yb) + 4 * B * L * nh + 2 * B * L * Gbc * N + 8 * nh + \
             4 * B * nh * P * N
@@ -347,9 +369,29 @@ class Ssd(Workload):
         n += codes_equal(lay.Cq.cpu().numpy(), ref["Cq"], "C codes")
         import torch
         hsel = torch.as_tensor(self.heads, device=lay.y.device)
-        y = lay.y[:, :, hsel].float().cpu().numpy().astype(np.float64)
         rows = lambda a: np.asarray(a, np.float64).transpose(0, 2, 3, 1).reshape(-1, a.shape[1])
-        out = {"codes_bit_exact": n, "y_row_error": rows_close(rows(y), rows(ref["y"]), self.tol, "y")}
+        out = {"codes_bit_exact": n}
+        if not self.y_int8:
+            y = lay.y[:, :, hsel].float().cpu().numpy().astype(np.float64)
+            out["y_row_error"] = rows_close(rows(y), rows(ref["y"]), self.tol, "y")
+        else:
+            # decode the int8 codes with the static output scales and correction term: every
+            # unsaturated code is within half a step (plus the fp32-state tolerance of the row) of
+            # the oracle's y + bias
+            yg, ys, yb = self.y_out
+            P = self.dims[3]
+            ch = (self.heads[:, None] * P + np.arange(P)[None, :]).reshape(-1)
+            codes = rows(lay.y[:, :, hsel].cpu().numpy().astype(np.float64))
+            yr = rows(ref["y"])
+            nrow = yr.shape[0] // len(ch)                      # rows are (b, head, p)
+            s = np.tile(np.asarray(ys, np.float64)[np.asarray(yg, np.int64)][ch], nrow)[:, None]
+            v = yr + np.tile(np.asarray(yb, np.float64)[ch], nrow)[:, None]
+            inside = (codes > -128) & (codes < 127)
+            rowmax = np.abs(yr).max(axis=-1, keepdims=True)
+            dev = np.abs(codes * s - v) - (0.5 * s + self.tol * rowmax)
+            bad = int(np.count_nonzero((dev > 1e-9 * s) & inside))
+            require(bad == 0, f"int8 y: {bad} codes off by more than half a step")
+            out["y_int8_codes_within_half_step"] = int(np.count_nonzero(inside))
         hl = lay.h_last[:, hsel].cpu().numpy()
         out["h_last_row_error"] = rows_close(hl.reshape(-1, hl.shape[-1]),
                                              ref["h_last"].reshape(-1, hl.shape[-1]), self.tol,
@@ -461,11 +503,12 @@ def _zero(device):
     return _zc[k]
 
 
-WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True), "c3": lambda: Mamba1(False),
+WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
+             "c4i8y": lambda: Ssd(False, True), "c3": lambda: Mamba1(False),
              "c3se": lambda: Mamba1(True), "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
              "c2": lambda: S4d(False), "c2i16": lambda: S4d(True), "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True)}
-OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3i8y", "c4f16", "c5", "c5f16")
+OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3i8y", "c4f16", "c4i8y", "c5", "c5f16")
 
 
 # ------------------------------------------------------------------------------------------------
@@ -487,7 +530,7 @@ TRAFFIC = {
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
     "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"], "c2i16": ["s4d.hip"],
-    "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c5": ["state_update.hip"],
+    "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c4i8y": ["ssd.hip"], "c5": ["state_update.hip"],
     "c5f16": ["state_update.hip"],
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 120 /* 1.2.0: qssm_scan_w8a8_noalloc */
+#define QSSM_VERSION 130 /* 1.3.0: int8 output fields appended to qssm_ssd_args and qssm_update_args */
 
 typedef int32_t qssm_status;
 enum {
@@ -250,6 +250,12 @@ qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
  *   the rounding of r is a floating-point decision inside the contraction);
  *   inter-chunk state passing in fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;
  *   y = Y_intra + Y_inter + Dskip * xh.
+ * y is fp32 or fp16 (y_dtype), or int8 codes for the next W8A8 module (QSSM_I8; SSDi8, abstract:
+ * a persistent int8 path and an error-correction term from per-channel error statistics):
+ *   y_code[b,t,h,p] = clamp(RNE(v / s), -128, 127),  v = fl32(y[b,t,h,p] + y_bias[h*P + p]),
+ *   s = y_scales[y_group_of[h*P + p]]
+ * by the quantization rule above, where y is the fp32 value the QSSM_F32 output would hold. The y_*
+ * fields are read only for QSSM_I8.
  * Requires chunk == 256, P == 64, N == 128, gs == 16 in this version (else QSSM_ERR_UNSUPPORTED).
  * seqlen == 0 is valid: xq, delta, Bq, Cq and y are then not accessed (they may be NULL) and
  * h_last receives h0 (or zeros).
@@ -274,10 +280,14 @@ typedef struct qssm_ssd_args {
   const float* C_scales;                          /* [Gbc * N / gs] */
   const float* h0;                                /* [B, nh, P, N] or NULL */
   void* y;                                        /* [B, L, nh, P], y_dtype */
-  int32_t y_dtype;                                /* QSSM_F32 or QSSM_F16 */
+  int32_t y_dtype;                                /* QSSM_F32, QSSM_F16 or QSSM_I8 */
   float* h_last;                                  /* [B, nh, P, N] or NULL */
   int32_t fused;                                  /* reserved, must be 0 */
   int32_t state_mma;                              /* QSSM_MMA_F16 (default) or QSSM_MMA_I8 */
+  int32_t y_groups;                               /* QSSM_I8: Gy, 1..256 */
+  const uint8_t* y_group_of;                      /* QSSM_I8: [nh * P] output group of each channel */
+  const float* y_scales;                          /* QSSM_I8: [Gy] static output scales */
+  const float* y_bias;                            /* QSSM_I8: [nh * P] correction term, or NULL */
 } qssm_ssd_args;
 
 size_t qssm_ssd_workspace_size(const qssm_ssd_args* a);
@@ -294,7 +304,10 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* workspace, size_t 
  *     dA = exp(delta[b,h] * A[h]);  state = dA * state + delta[b,h] * xh[p] * Bh[n]
  *     y[b,h,p] = sum_n Ch[n] * state + Dskip[h] * xh[p]
  * state [B, nh, P, N] is read and written in place, fp32 or fp16 (state_dtype; fp16 is rounded
- * to nearest even on store, arithmetic is fp32). y: fp32 [B, nh, P].
+ * to nearest even on store, arithmetic is fp32). y: fp32 [B, nh, P], or int8 codes for the next
+ * W8A8 module (y_dtype QSSM_I8; SSDi8, abstract: persistent int8 path, per-channel error
+ * correction): y_code = clamp(RNE(fl32(y + y_bias[h*P + p]) / y_scales[y_group_of[h*P + p]]),
+ * -128, 127) by the quantization rule above.
  * xq_out [B, nh, P], Bq_out / Cq_out [B, Gbc, N] receive the codes when not NULL.
  * Supported: N = 4 * 2^k with 4 <= N <= 256 (N >= 8 for an fp16 state), (P rounded up to a
  * multiple of 4, + 2N) * 4 bytes <= 64 KiB; state 16-byte aligned. Other shapes return
@@ -317,10 +330,15 @@ typedef struct qssm_update_args {
   const float* Dskip;                     /* [nh] or NULL */
   int32_t state_dtype;                    /* QSSM_F32 or QSSM_F16 */
   void* state;                            /* [B, nh, P, N] in/out */
-  float* y;                               /* [B, nh, P] */
+  void* y;                                /* [B, nh, P], fp32 or int8 codes (y_dtype) */
   int8_t* xq_out;                         /* [B, nh, P] or NULL */
   int8_t* Bq_out;                         /* [B, Gbc, N] or NULL */
   int8_t* Cq_out;                         /* [B, Gbc, N] or NULL */
+  int32_t y_dtype;                        /* QSSM_F32 (0, the default) or QSSM_I8 */
+  int32_t y_groups;                       /* QSSM_I8: Gy, 1..256 */
+  const uint8_t* y_group_of;              /* QSSM_I8: [nh * P] output group of each channel */
+  const float* y_scales;                  /* QSSM_I8: [Gy] static output scales */
+  const float* y_bias;                    /* QSSM_I8: [nh * P] correction term, or NULL */
 } qssm_update_args;
 
 qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t stream);

@@ -53,7 +53,8 @@ class SsdArgs(ctypes.Structure):
                 ("xq", _P), ("x_group_of", _P), ("x_scales", _P), ("delta", _P), ("A", _P),
                 ("Dskip", _P), ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P),
                 ("C_scales", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
-                ("fused", _I32), ("state_mma", _I32)]
+                ("fused", _I32), ("state_mma", _I32), ("y_groups", _I32), ("y_group_of", _P),
+                ("y_scales", _P), ("y_bias", _P)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -62,7 +63,8 @@ class UpdateArgs(ctypes.Structure):
                 ("x_scales", _P), ("B", _P), ("C", _P), ("bc_group_size", _I32),
                 ("B_scales", _P), ("C_scales", _P), ("delta", _P), ("A", _P), ("Dskip", _P),
                 ("state_dtype", _I32), ("state", _P), ("y", _P), ("xq_out", _P), ("Bq_out", _P),
-                ("Cq_out", _P)]
+                ("Cq_out", _P), ("y_dtype", _I32), ("y_groups", _I32), ("y_group_of", _P),
+                ("y_scales", _P), ("y_bias", _P)]
 
 
 ARG_STRUCTS = {0: ScanArgs, 1: S4dArgs, 2: SsdArgs, 3: UpdateArgs}
@@ -293,14 +295,34 @@ def qssm_s4d_scan(args, stream=None):
     _check("qssm_s4d_scan", load().qssm_s4d_scan(ctypes.byref(args), _stream(stream)))
 
 
+def _y_out_fields(y, nch, y_group_of, y_scales, y_bias):
+    """The int8-output fields of an argument block (y is int8), checked for size."""
+    torch = _t()
+    yq = y.dtype == torch.int8
+    if yq:
+        if y_group_of is None or y_scales is None:
+            raise ValueError("an int8 y needs y_group_of and y_scales")
+        if y_group_of.numel() != nch or (y_bias is not None and y_bias.numel() != nch):
+            raise ValueError("y_group_of and y_bias must have one entry per channel")
+    return dict(y_groups=int(y_scales.numel()) if yq else 0,
+                y_group_of=_ptr(y_group_of, torch.uint8, "y_group_of", not yq),
+                y_scales=_ptr(y_scales, torch.float32, "y_scales", not yq),
+                y_bias=_ptr(y_bias, torch.float32, "y_bias", True))
+
+
 def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, chunk, y,
-             Dskip=None, h0=None, h_last=None, state_mma=QSSM_MMA_F16):
+             Dskip=None, h0=None, h_last=None, state_mma=QSSM_MMA_F16, y_group_of=None,
+             y_scales=None, y_bias=None):
+    """y is float32, float16 or int8 (then y_group_of [nh * P], y_scales [Gy] and the optional
+    correction y_bias [nh * P] are given)."""
     torch = _t()
     B, L, nh, P = xq.shape
     Gbc, N = Bq.shape[2], Bq.shape[3]
-    ydt = QSSM_F32 if y.dtype == torch.float32 else QSSM_F16
-    keep = (xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last)
-    return _fill(SsdArgs(), keep=keep, batch=B, seqlen=L, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
+    ydt = {torch.float32: QSSM_F32, torch.float16: QSSM_F16, torch.int8: QSSM_I8}.get(y.dtype, -1)
+    keep = (xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, y, Dskip, h0, h_last,
+            y_group_of, y_scales, y_bias)
+    return _fill(SsdArgs(), keep=keep, **_y_out_fields(y, nh * P, y_group_of, y_scales, y_bias),
+                 batch=B, seqlen=L, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
                  chunk=chunk, x_groups=int(x_scales.numel()), xq=_ptr(xq, torch.int8, "xq"),
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"),
@@ -326,14 +348,19 @@ def qssm_ssd_chunk_int8(args, workspace, stream=None):
 
 
 def update_args(x, x_group_of, x_scales, Bm, Cm, B_scales, C_scales, gs, delta, A, state, y,
-                Dskip=None, xq_out=None, Bq_out=None, Cq_out=None):
+                Dskip=None, xq_out=None, Bq_out=None, Cq_out=None, y_group_of=None,
+                y_scales=None, y_bias=None):
+    """y is float32 or int8 (then y_group_of [nh * P], y_scales [Gy] and the optional correction
+    y_bias [nh * P] are given)."""
     torch = _t()
     B, nh, P = x.shape
     Gbc, N = Bm.shape[1], Bm.shape[2]
     sdt = QSSM_F32 if state.dtype == torch.float32 else QSSM_F16
     keep = (x, x_group_of, x_scales, Bm, Cm, B_scales, C_scales, delta, A, state, y, Dskip, xq_out,
-            Bq_out, Cq_out)
-    return _fill(UpdateArgs(), keep=keep, batch=B, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
+            Bq_out, Cq_out, y_group_of, y_scales, y_bias)
+    ydt = {torch.float32: QSSM_F32, torch.int8: QSSM_I8}.get(y.dtype, -1)
+    return _fill(UpdateArgs(), keep=keep, **_y_out_fields(y, nh * P, y_group_of, y_scales, y_bias),
+                 y_dtype=ydt, batch=B, nheads=nh, headdim=P, dstate=N, ngroups=Gbc,
                  x_groups=int(x_scales.numel()), x=_ptr(x, torch.float32, "x"),
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"), B=_ptr(Bm, torch.float32, "B"),
@@ -342,7 +369,7 @@ def update_args(x, x_group_of, x_scales, Bm, Cm, B_scales, C_scales, gs, delta, 
                  C_scales=_ptr(C_scales, torch.float32, "C_scales"),
                  delta=_ptr(delta, torch.float32, "delta"), A=_ptr(A, torch.float32, "A"),
                  Dskip=_ptr(Dskip, torch.float32, "Dskip", True), state_dtype=sdt,
-                 state=_ptr(state, None, "state"), y=_ptr(y, torch.float32, "y"),
+                 state=_ptr(state, None, "state"), y=_ptr(y, None, "y"),
                  xq_out=_ptr(xq_out, torch.int8, "xq_out", True),
                  Bq_out=_ptr(Bq_out, torch.int8, "Bq_out", True),
                  Cq_out=_ptr(Cq_out, torch.int8, "Cq_out", True))

@@ -80,6 +80,11 @@ struct SsdParams {
   _Float16* Hh;   // [B, nc, nh, 16 KB]: sC(n) * state entering the chunk, fp16, K2's operand order
   float* sxt;     // [nh, P]: x scale of each channel, 0 where invalid (written by K1, read by K2)
   float* cumw;    // [B, nc, nh, Q]: cumulative sum of delta * A within the chunk (K1 -> K2)
+  int32_t yi8, Gy;            // int8 output, number of output groups
+  const uint8_t* y_group_of;  // int8 output: [nh * P]
+  const float* y_scales;      // int8 output: [Gy]
+  const float* y_bias;        // int8 output: [nh * P] or NULL
+  float* syt;                 // [nh, P]: output scale of each channel (written by K1, read by K2)
 };
 
 __device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
@@ -211,7 +216,10 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
   if (lt < kP) {
     const float sx = valid_or_zero(p.x_scales[min((int)p.x_group_of[h * kP + lt], p.G - 1)]);
     sxp[lt] = sx;
-    if (b == 0 && active) p.sxt[h * kP + lt] = sx;
+    if (b == 0 && active) {
+      p.sxt[h * kP + lt] = sx;
+      if (p.yi8) p.syt[h * kP + lt] = p.y_scales[min((int)p.y_group_of[h * kP + lt], p.Gy - 1)];
+    }
   }
   // B and C scales of this wave's two state groups (ks = 2 w + kb), wave-uniform
   float sB[2], sC[2];
@@ -478,11 +486,15 @@ struct K2Smem {
   float stdt[kQ];
   float stcum[kQ];
   float stsx[kP];
+  float stsy[kP];   // int8 output: staged output scale and correction term of each channel
+  float styb[kP];
   float cum[kQ];
   float dtv[kQ];
   float ecum[kQ];   // exp(cum_i)
   float cjv[kQ];    // exp(cum at the end of j's 32-block - cum_j) * delta_j
   float sxs[kP];
+  float sys[kP];
+  float syb[kP];
   float stad;  // staged D_h
   float dh;    // D_h of the current head
 };
@@ -630,9 +642,18 @@ __device__ __forceinline__ void stage_head(const SsdParams& p, K2Smem& s, int64_
     const int dst = uniform((int)offsetof(K2Smem, stcum));
     __builtin_amdgcn_global_load_lds(p.cumw + ((b * p.nc + c) * p.nh + h) * kQ + lane * 4, base + dst,
                                      16, 0, 0);
-  } else if (wave == 6 && lane == 0 && p.Dskip) {
-    const int dst = uniform((int)offsetof(K2Smem, stad));
-    __builtin_amdgcn_global_load_lds(p.Dskip + h, base + dst, 4, 0, 0);
+  } else if (wave == 6) {
+    if (lane == 0 && p.Dskip) {
+      const int dst = uniform((int)offsetof(K2Smem, stad));
+      __builtin_amdgcn_global_load_lds(p.Dskip + h, base + dst, 4, 0, 0);
+    }
+    if (p.yi8) {
+      const int dst = uniform((int)offsetof(K2Smem, stsy));
+      __builtin_amdgcn_global_load_lds(p.syt + h * kP + lane, base + dst, 4, 0, 0);
+    }
+  } else if (wave == 7 && p.yi8 && p.y_bias) {
+    const int dst = uniform((int)offsetof(K2Smem, styb));
+    __builtin_amdgcn_global_load_lds(p.y_bias + h * kP + lane, base + dst, 4, 0, 0);
   }
 }
 
@@ -719,7 +740,13 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       const float cl = __shfl(cum, (tid & 63) | 31, 64);
       s.cjv[j] = expf(cl - cum) * dt;
     }
-    if (tid < kP) s.sxs[tid] = s.stsx[tid];
+    if (tid < kP) {
+      s.sxs[tid] = s.stsx[tid];
+      if (p.yi8) {
+        s.sys[tid] = s.stsy[tid];
+        s.syb[tid] = p.y_bias ? s.styb[tid] : 0.0f;
+      }
+    }
     if (tid == 0) s.dh = p.Dskip ? s.stad : 0.0f;
     {
       // x codes of head h, transposed [p][j] in fp16 (zero for an invalid x scale and past the
@@ -815,65 +842,88 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     // y = sx * acc + D * xh; rows past the sequence (ragged last chunk) are not stored
     const float Dh = s.dh;
     const int64_t base = ((b * p.L + t0) * p.nh + h) * kP;  // y[b, t0, h, 0]
+    float yv[2][16];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       const int pc = pt * 32 + (lane & 31);
       const float sx = s.sxs[pc];
       const float mult = (sx > 0.0f) ? sx : 1.0f;
       const float Dsx = Dh * sx;
-      float yv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const v4h x4 = *reinterpret_cast<const v4h*>(s.xT + pc * kXtRow + I * 32 + 4 * (lane >> 5) + 8 * q);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) yv[4 * q + k] = fmaf(Dsx, (float)x4[k], mult * Y[pt][4 * q + k]);
+        for (int k = 0; k < 4; ++k) yv[pt][4 * q + k] = fmaf(Dsx, (float)x4[k], mult * Y[pt][4 * q + k]);
       }
-      // register r holds row 32 I + 8 (r / 4) + r % 4 + 4 (lane / 32): buffer stores with the
-      // head's y block as the resource, a per-register wave-uniform row offset (soffset) and one
-      // per-lane offset, so the stores need no per-lane 64-bit address arithmetic (all offsets fit
-      // 32 bits: nheads <= 2^14 is checked on the host)
-      const int ilane = 4 * (lane >> 5);
-      const int esz = p.yf16 ? 2 : 4;
-      const uint64_t ya = reinterpret_cast<uint64_t>(static_cast<char*>(p.y) + base * esz);
-      void* const yblk = reinterpret_cast<void*>(
-          ((uint64_t)(uint32_t)uniform((int)(ya >> 32)) << 32) | (uint32_t)uniform((int)ya));
-      const __amdgpu_buffer_rsrc_t yrs =
-          __builtin_amdgcn_make_buffer_rsrc(yblk, (short)0, 0x7FFFFFFF, kBufferWord3);
-      const int voff = (ilane * rs + pc) * esz;
-      // the full-chunk path stores unconditionally; the ragged last chunk masks rows past q
-      if (p.yf16) {
-        if (full) {
+    }
+    // register r holds row 32 I + 8 (r / 4) + r % 4 + 4 (lane / 32): buffer stores with the head's
+    // y block as the resource, a per-register wave-uniform row offset (soffset) and one per-lane
+    // offset, so the stores need no per-lane 64-bit address arithmetic (all offsets fit 32 bits:
+    // nheads <= 2^14 is checked on the host)
+    const int ilane = 4 * (lane >> 5);
+    const int esz = p.yi8 ? 1 : (p.yf16 ? 2 : 4);
+    const uint64_t ya = reinterpret_cast<uint64_t>(static_cast<char*>(p.y) + base * esz);
+    void* const yblk = reinterpret_cast<void*>(
+        ((uint64_t)(uint32_t)uniform((int)(ya >> 32)) << 32) | (uint32_t)uniform((int)ya));
+    const __amdgpu_buffer_rsrc_t yrs =
+        __builtin_amdgcn_make_buffer_rsrc(yblk, (short)0, 0x7FFFFFFF, kBufferWord3);
+    if (!p.yf16 && !p.yi8) {
+      // fp32: each store of a wave writes two full 128-byte lines (rows i and i + 4, 32 channels)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const int voff = (ilane * rs + pt * 32 + (lane & 31)) * 4;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+          if (full || ir + ilane < q)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[pt][r]), yrs,
+                                                  voff, uniform(ir * rs * 4), kYPolicy);
+        }
+      }
+    } else {
+      // fp16 or int8: neighbouring lanes trade one value so that each holds two adjacent channels
+      // of one row: an even lane channels (c, c + 1) of the first 32, an odd lane (32 + c - 1,
+      // 32 + c); one store of a wave then writes rows i and i + 4 whole (64 channels each)
+      const bool odd = lane & 1;
+      const int c0 = lane & 31;
+      const int col = odd ? 32 + c0 - 1 : c0;
+      const int voff = (ilane * rs + col) * esz;
+      uint32_t v0[16], v1[16];  // the element of each tile as bits (fp16 or int8 code)
+      if (p.yi8) {
+        // persistent int8 output: fl32(y + correction term) quantized with the channel's static
+        // output scale by the exact rule (an invalid scale gives 0)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const float sy = s.sys[pt * 32 + c0];
+          const float ry = recip_or_zero(sy);
+          const float yb = s.syb[pt * 32 + c0];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-            __builtin_amdgcn_raw_buffer_store_b16(
-                __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), kYPolicy);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-            if (ir + ilane < q)
-              __builtin_amdgcn_raw_buffer_store_b16(
-                  __builtin_bit_cast(unsigned short, __float2half_rn(yv[r])), yrs, voff, uniform(ir * rs * 2), kYPolicy);
+            const uint32_t cd = (uint8_t)quant8_r(yv[pt][r] + yb, sy, ry);
+            if (pt == 0) v0[r] = cd; else v1[r] = cd;
           }
         }
       } else {
-        if (full) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
-                                                  uniform(ir * rs * 4), kYPolicy);
-          }
-        } else {
+        for (int r = 0; r < 16; ++r) {
+          v0[r] = __builtin_bit_cast(unsigned short, __float2half_rn(yv[0][r]));
+          v1[r] = __builtin_bit_cast(unsigned short, __float2half_rn(yv[1][r]));
+        }
+      }
+      const int shift = p.yi8 ? 8 : 16;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-            if (ir + ilane < q)
-              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[r]), yrs, voff,
-                                                    uniform(ir * rs * 4), kYPolicy);
-          }
+      for (int r = 0; r < 16; ++r) {
+        // DPP quad permutation [1, 0, 3, 2]: the value of the neighbouring lane
+        const uint32_t send = odd ? v0[r] : v1[r];
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+        const uint32_t pair = odd ? (recv | (v1[r] << shift)) : (v0[r] | (recv << shift));
+        const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+        if (full || ir + ilane < q) {
+          if (p.yi8)
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)pair, yrs, voff, uniform(ir * rs),
+                                                  kYPolicy);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(pair, yrs, voff, uniform(ir * rs * 2), kYPolicy);
         }
       }
     }
@@ -898,16 +948,17 @@ bool raise_lds_limit(int which, const void* fn, size_t bytes) {
 }
 
 struct WsLayout {
-  size_t sx_off, cum_off, total;  // Hh at offset 0
+  size_t sx_off, sy_off, cum_off, total;  // Hh at offset 0
 };
 
-// workspace: Hh (fp16 entering states), sxt, cumw, each 256-byte aligned
+// workspace: Hh (fp16 entering states), sxt, syt, cumw, each 256-byte aligned
 WsLayout ws_layout(const qssm_ssd_args* a) {
   const int64_t nc = (a->seqlen + kQ - 1) / kQ;
   const size_t elems = (size_t)a->batch * nc * a->nheads * kP * kN;
   WsLayout w;
   w.sx_off = (elems * sizeof(_Float16) + 255) & ~(size_t)255;
-  w.cum_off = (w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 255) & ~(size_t)255;
+  w.sy_off = (w.sx_off + (size_t)a->nheads * kP * sizeof(float) + 255) & ~(size_t)255;
+  w.cum_off = (w.sy_off + (size_t)a->nheads * kP * sizeof(float) + 255) & ~(size_t)255;
   w.total = w.cum_off + (size_t)a->batch * nc * a->nheads * kQ * sizeof(float) + 256;
   return w;
 }
@@ -933,8 +984,14 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   if (a->x_groups < 1 || a->x_groups > 256) return fail(QSSM_ERR_INVALID_ARG, "x_groups not in 1..256");
   if (a->bc_group_size < 1 || a->dstate % a->bc_group_size != 0)
     return fail(QSSM_ERR_INVALID_ARG, "bc_group_size must divide dstate");
-  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16)
-    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32 or QSSM_F16");
+  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16 && a->y_dtype != QSSM_I8)
+    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32, QSSM_F16 or QSSM_I8");
+  if (a->y_dtype == QSSM_I8) {
+    if (a->y_groups < 1 || a->y_groups > 256)
+      return fail(QSSM_ERR_INVALID_ARG, "y_groups not in 1..256");
+    if (!a->y_group_of || !a->y_scales)
+      return fail(QSSM_ERR_INVALID_ARG, "QSSM_I8 output needs y_group_of and y_scales");
+  }
   if (a->fused != 0) return fail(QSSM_ERR_UNSUPPORTED, "fused must be 0");
   if (a->state_mma != QSSM_MMA_F16 && a->state_mma != QSSM_MMA_I8)
     return fail(QSSM_ERR_INVALID_ARG, "state_mma must be QSSM_MMA_F16 or QSSM_MMA_I8");
@@ -962,7 +1019,9 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
               a->xq, a->x_group_of, a->x_scales, a->delta, a->A, a->Dskip, a->Bq, a->Cq,
               a->B_scales, a->C_scales, a->h0, a->y, a->h_last,
               reinterpret_cast<_Float16*>(base), reinterpret_cast<float*>(base + wl.sx_off),
-              reinterpret_cast<float*>(base + wl.cum_off)};
+              reinterpret_cast<float*>(base + wl.cum_off), a->y_dtype == QSSM_I8,
+              a->y_dtype == QSSM_I8 ? a->y_groups : 1, a->y_group_of, a->y_scales, a->y_bias,
+              reinterpret_cast<float*>(base + wl.sy_off)};
   if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff || B * nh > 0x7fffffff)
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
   // K1 runs even for an empty sequence: it writes h_last = h0 (or zeros)

@@ -33,10 +33,14 @@ struct UpdParams {
   const float* A;
   const float* Dskip;
   void* state;
-  float* y;
+  void* y;
   int8_t* xq_out;
   int8_t* Bq_out;
   int8_t* Cq_out;
+  int32_t yi8, Gy;            // int8 output, number of output groups
+  const uint8_t* y_group_of;  // int8 output: [nh * P]
+  const float* y_scales;      // int8 output: [Gy]
+  const float* y_bias;        // int8 output: [nh * P] or NULL
 };
 
 // CH consecutive states per thread access: 4 for fp32 (16 bytes), 8 for fp16 (16 bytes).
@@ -140,7 +144,19 @@ __global__ __launch_bounds__(kThreads) void k_state_update(UpdParams p) {
     // rows occupy R consecutive lanes (R divides 64 and kThreads): reduce within them
 #pragma unroll
     for (int off = R / 2; off > 0; off >>= 1) yp += __shfl_xor(yp, off, 64);
-    if (on && (lane % R) == 0) p.y[bh * p.P + row] = fmaf(Dh, xs[row], yp);
+    if (on && (lane % R) == 0) {
+      const float yv = fmaf(Dh, xs[row], yp);
+      if (p.yi8) {
+        // persistent int8 output: fl32(y + correction term), the exact rule with the channel's
+        // static output scale
+        const int64_t ch = h * p.P + row;
+        const float sy = p.y_scales[min((int)p.y_group_of[ch], p.Gy - 1)];
+        const float yb = p.y_bias ? p.y_bias[ch] : 0.0f;
+        reinterpret_cast<int8_t*>(p.y)[bh * p.P + row] = quant8_r(yv + yb, sy, recip_or_zero(sy));
+      } else {
+        reinterpret_cast<float*>(p.y)[bh * p.P + row] = yv;
+      }
+    }
   }
 }
 
@@ -170,6 +186,14 @@ extern "C" qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t 
   if (a->x_groups < 1 || a->x_groups > 256) return fail(QSSM_ERR_INVALID_ARG, "x_groups not in 1..256");
   if (a->state_dtype != QSSM_F32 && a->state_dtype != QSSM_F16)
     return fail(QSSM_ERR_INVALID_ARG, "state_dtype must be QSSM_F32 or QSSM_F16");
+  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_I8)
+    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32 or QSSM_I8");
+  if (a->y_dtype == QSSM_I8) {
+    if (a->y_groups < 1 || a->y_groups > 256)
+      return fail(QSSM_ERR_INVALID_ARG, "y_groups not in 1..256");
+    if (!a->y_group_of || !a->y_scales)
+      return fail(QSSM_ERR_INVALID_ARG, "QSSM_I8 output needs y_group_of and y_scales");
+  }
   const int64_t R = N / 4;
   if (N % 4 != 0 || !(R == 1 || R == 2 || R == 4 || R == 8 || R == 16 || R == 32 || R == 64))
     return fail(QSSM_ERR_UNSUPPORTED, "dstate must be 4 * 2^k with 4 <= dstate <= 256");
@@ -184,7 +208,9 @@ extern "C" qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t 
   if (B * nh > 0x7fffffffLL) return fail(QSSM_ERR_INVALID_ARG, "batch * nheads too large");
   UpdParams p{B, nh, P, N, a->ngroups, (int32_t)(nh / a->ngroups), a->bc_group_size, a->x_groups, a->x,
               a->x_group_of, a->x_scales, a->B, a->C, a->B_scales, a->C_scales, a->delta, a->A,
-              a->Dskip, a->state, a->y, a->xq_out, a->Bq_out, a->Cq_out};
+              a->Dskip, a->state, a->y, a->xq_out, a->Bq_out, a->Cq_out,
+              a->y_dtype == QSSM_I8, a->y_dtype == QSSM_I8 ? a->y_groups : 1, a->y_group_of,
+              a->y_scales, a->y_bias};
   const int f16 = a->state_dtype == QSSM_F16;
   switch (R) {
     case 1: return launch_r<1>(p, f16, stream);

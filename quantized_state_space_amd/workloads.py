@@ -268,7 +268,9 @@ class SsdLayer:
     chunked SSD."""
 
     def __init__(self, inp, device, chunk=256, gs=16, groups_per_block=8, y_dtype=QSSM_F32,
-                 with_h0=False, state_mma=0):
+                 with_h0=False, state_mma=0, y_out=None):
+        """y_out = (group_of [nh * P] uint8, scales [Gy] fp32, bias [nh * P] fp32 or None): the
+        layer then writes int8 y codes for the next W8A8 module."""
         import torch
         dev = device
         x = inp["x"]
@@ -292,12 +294,20 @@ class SsdLayer:
         self.xq = torch.empty(x.shape, dtype=torch.int8, device=dev)
         self.Bq = torch.empty(inp["B"].shape, dtype=torch.int8, device=dev)
         self.Cq = torch.empty(inp["C"].shape, dtype=torch.int8, device=dev)
-        self.y = torch.empty(x.shape, dtype=torch.float32 if y_dtype == QSSM_F32 else torch.float16,
-                             device=dev)
+        ydt = torch.float32 if y_dtype == QSSM_F32 else torch.float16
+        yo = (None, None, None)
+        if y_out is not None:
+            ydt = torch.int8
+            yg, ys, yb = y_out
+            yo = (_dev(np.asarray(yg, np.uint8), dev), _dev(np.asarray(ys, np.float32), dev),
+                  None if yb is None else _dev(np.asarray(yb, np.float32), dev))
+        self.y_out = yo
+        self.y = torch.empty(x.shape, dtype=ydt, device=dev)
         self.h_last = torch.empty((B, nh, P, N), dtype=torch.float32, device=dev)
         self.args = ssd_args(self.xq, self.group_t, self.xs, self.delta, self.A, self.Bq, self.Cq,
                              self.bs, self.cs, gs, chunk, self.y, Dskip=self.D, h0=self.h0,
-                             h_last=self.h_last, state_mma=state_mma)
+                             h_last=self.h_last, state_mma=state_mma, y_group_of=yo[0],
+                             y_scales=yo[1], y_bias=yo[2])
         self.ws = torch.empty(max(qssm_ssd_workspace_size(self.args), 1), dtype=torch.uint8,
                               device=dev)
 
@@ -327,7 +337,9 @@ class DecodeLayer:
     One step = one fused state-update call for a new token of every sequence."""
 
     def __init__(self, params, device, gs=16, groups_per_block=8, state_dtype=QSSM_F32,
-                 emit_codes=False):
+                 emit_codes=False, y_out=None):
+        """y_out = (group_of [nh * P] uint8, scales [Gy] fp32, bias [nh * P] fp32 or None): int8
+        y codes for the next W8A8 module."""
         import torch
         dev = device
         st0 = params["state0"]
@@ -345,7 +357,14 @@ class DecodeLayer:
         self.D = _dev(params["D"], dev)
         sdt = torch.float32 if state_dtype == QSSM_F32 else torch.float16
         self.state = _dev(st0, dev, sdt)
-        self.y = torch.empty((B, nh, P), dtype=torch.float32, device=dev)
+        yo = (None, None, None)
+        if y_out is not None:
+            yg, ys, yb = y_out
+            yo = (_dev(np.asarray(yg, np.uint8), dev), _dev(np.asarray(ys, np.float32), dev),
+                  None if yb is None else _dev(np.asarray(yb, np.float32), dev))
+        self.y_out = yo
+        self.y = torch.empty((B, nh, P), dtype=torch.float32 if y_out is None else torch.int8,
+                             device=dev)
         self.x = torch.empty((B, nh, P), dtype=torch.float32, device=dev)
         self.Bm = torch.empty((B, Gbc, N), dtype=torch.float32, device=dev)
         self.Cm = torch.empty((B, Gbc, N), dtype=torch.float32, device=dev)
@@ -358,7 +377,8 @@ class DecodeLayer:
         c = self.codes or (None, None, None)
         self.args = update_args(self.x, self.group_t, self.xs, self.Bm, self.Cm, self.bs, self.cs, gs,
                                 self.delta, self.A, self.state, self.y, Dskip=self.D, xq_out=c[0],
-                                Bq_out=c[1], Cq_out=c[2])
+                                Bq_out=c[1], Cq_out=c[2], y_group_of=yo[0], y_scales=yo[1],
+                                y_bias=yo[2])
 
     def load_inputs(self, step_inputs):
         """Copies one step's host inputs into the resident device buffers (outside timed regions)."""
