@@ -85,6 +85,10 @@ def _declare(L):
     L.orc_s4d_scan.argtypes = [_I64] * 4 + [_P] * 10
     L.orc_ssd_chunked.argtypes = [_I64] * 7 + [_P] * 7 + [_I32, _P, _P, _P, _P]
     L.orc_decode_step.argtypes = [_I64] * 5 + [_P] * 8
+    L.orc_w4_scale_from_absmax.argtypes = [_F]
+    L.orc_w4_scale_from_absmax.restype = _F
+    L.orc_quant_w4.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+    L.orc_gemm_w4a8.argtypes = [_I64, _I64, _I64, _I64, _P, _F, _P, _P, _P, _P]
 
 
 _KEEP = []  # arrays whose addresses were handed to C in the current call
@@ -390,6 +394,43 @@ def decode_step(xh, Bh, Ch, delta, A, state, Dskip=None):
         lib().orc_decode_step(Bsz, nh, P, N, Gbc, _ptr(xh), _ptr(Bh), _ptr(_c(Ch, np.float64)),
                               _ptr(_c(delta, np.float64)), _ptr(_c(A, np.float64)),
                               _ptr(_c(Dskip, np.float64)), _ptr(state), _ptr(y))
+    return y
+
+
+# ------------------------------------------------------------------------------------------------
+# W4A8 linear layer (Quamba2 abstract: W4A8 for large-batch decoding). 4-bit symmetric weights with
+# a scale per (output channel, group of input channels), int8 activations with one scale.
+
+def w4_scales(w, group):
+    """Scales [N, K / group]: fl32(absmax / 7) of each group of `group` consecutive input channels
+    (absmax 0 -> 1, clamped into [2^-100, 2^100])."""
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    a = finite_absmax(w.reshape(N, K // group, group), axis=2)
+    f = lib().orc_w4_scale_from_absmax
+    return np.array([f(float(v)) for v in a.reshape(-1)], np.float32).reshape(N, K // group)
+
+
+def quant_w4(w, group, scales):
+    """Codes [N, K] in [-8, 7]: clamp(RNE(w / s), -8, 7) with the exact quotient (int8 storage)."""
+    w = _c(w, np.float32)
+    N, K = w.shape
+    q = np.empty((N, K), np.int8)
+    with _Call():
+        lib().orc_quant_w4(_ptr(w), N, K, group, _ptr(_c(scales, np.float32)), _ptr(q))
+    return q
+
+
+def gemm_w4a8(qa, sa, qw, sw, group, bias=None):
+    """y [M, N] in fp64: bias[n] + sum_g sa sw[n, g] sum_{k in g} qa[m, k] qw[n, k]."""
+    qa = _c(qa, np.int8)
+    qw = _c(qw, np.int8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    y = np.empty((M, N), np.float64)
+    with _Call():
+        lib().orc_gemm_w4a8(M, N, K, group, _ptr(qa), float(np.float32(sa)), _ptr(qw),
+                            _ptr(_c(sw, np.float32)), _ptr(_c(bias, np.float64)), _ptr(y))
     return y
 
 

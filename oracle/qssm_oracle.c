@@ -409,4 +409,49 @@ EXPORT void orc_decode_step(int64_t B, int64_t nh, int64_t P, int64_t N, int64_t
 }
 
 /* Number of OpenMP threads the parallel loops above use (for reporting the baseline's cores). */
+/* ------------------------------------------------------------------------------------------ */
+/* [Q2] W4A8 linear layer (abstract: W4A8 for large-batch decoding). Reading taken (the page gives
+ * only the bit widths): symmetric 4-bit weights with one scale per output channel n and group of
+ * `group` consecutive input channels, s = fl32(absmax / 7) (absmax 0 -> 1, clamped into the valid
+ * range), codes clamp(RNE(w / s), -8, 7) by the exact quotient; int8 activations with one scale;
+ *   y[m, n] = bias[n] + sum_g (sa * sw[n, g]) * sum_{k in g} qa[m, k] * qw[n, k]
+ * in fp64 (each inner sum is an exact integer). */
+EXPORT float orc_w4_scale_from_absmax(float absmax) {
+  if (absmax == 0.0f) return 1.0f;
+  float s = absmax / 7.0f;
+  if (s < 0x1p-100f) s = 0x1p-100f;
+  if (s > 0x1p100f) s = 0x1p100f;
+  return s;
+}
+
+EXPORT void orc_quant_w4(const float* w, int64_t N, int64_t K, int64_t group, const float* scales,
+                         int8_t* q) {
+  const int64_t ng = K / group;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const float s = scales[n * ng + k / group];
+      q[n * K + k] = scale_valid((double)s) ? (int8_t)round_sat(w[n * K + k], (double)s, -8, 7) : 0;
+    }
+}
+
+EXPORT void orc_gemm_w4a8(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t* qa,
+                          float sa, const int8_t* qw, const float* sw, const double* bias,
+                          double* y) {
+  const int64_t ng = K / group;
+  const double a_s = scale_valid((double)sa) ? (double)sa : 0.0;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = bias ? bias[n] : 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        int64_t dot = 0;
+        for (int64_t k = g * group; k < (g + 1) * group; ++k)
+          dot += (int64_t)qa[m * K + k] * (int64_t)qw[n * K + k];
+        const double s = scale_valid((double)sw[n * ng + g]) ? (double)sw[n * ng + g] : 0.0;
+        acc += (a_s * s) * (double)dot;
+      }
+      y[m * N + n] = acc;
+    }
+}
+
 EXPORT int orc_max_threads(void) { return omp_get_max_threads(); }
