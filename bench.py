@@ -492,6 +492,74 @@ class Decode(Workload):
                 "state_row_error": rows_close(st, ref["state"], self.tol, "state")}
 
 
+class W4A8(Workload):
+    """The W4A8 linear layer on the Mamba2-8B input projection shape (K = 4096 -> N = 18560) at M
+    tokens: quantize the fp32 activations to int8 (static per-tensor scale), then the GEMM. Not a
+    scan: its rate is int8 ops/s, against the int8 MFMA peak."""
+    bound = "mfma"
+    tol = 1e-5
+
+    def __init__(self, M):
+        self.M = M
+        self.name = f"w4a8-mamba2-8b-in-proj-m{M}"
+        self.dominant = "qssm_gemm_w4a8: k_gemm_w4a8"
+        self.rows = np.array([0, M // 2, M - 1])
+
+    def setup(self, dev):
+        import qssm_synth as synth
+        import quantized_state_space_amd.workloads as wl
+        self.inp = synth.w4a8_inputs(cfg=8, M=self.M)
+        self.lay = wl.W4A8Linear(self.inp["w"], self.inp["x"], self.inp["x_cal"], dev,
+                                 bias=self.inp["bias"])
+        M, N, K = self.lay.shape
+        self.dims = (M, N, K)
+        self.config = {"workload": self.name, "tokens": M, "in_features": K, "out_features": N,
+                       "weights": "int4, one scale per output channel", "activations": "int8",
+                       "y": "f32"}
+        self.sample_desc = f"{len(self.rows)} of {M} rows x all {N} outputs, exact integer dots in fp64"
+
+    def step(self, timer):
+        self.lay.quantize()
+        timer.start()
+        self.lay.gemm()
+        timer.stop()
+
+    def updates(self):
+        M, N, K = self.dims
+        return 2 * M * N * K   # int8 ops (a multiply-add counts two)
+
+    def sample_updates(self):
+        M, N, K = self.dims
+        return 2 * len(self.rows) * N * K
+
+    def ops(self):
+        return self.updates()
+
+    def dominant_bytes(self):
+        M, N, K = self.dims
+        return M * K + N * K // 2 + 4 * N * (K // K) + 4 * N + 4 * M * N
+
+    def oracle_ref(self):
+        import oracle
+        inp = self.inp
+        x = inp["x"][self.rows]
+        sa = oracle.scale_from_absmax(oracle.finite_absmax(inp["x_cal"].reshape(1, -1), axis=1))[0]
+        qa = oracle.quant_group_x(x.reshape(1, 1, -1), np.zeros(1, np.uint8), [sa]).reshape(x.shape)
+        K = inp["w"].shape[1]
+        sw = oracle.w4_scales(inp["w"], K)
+        qw = oracle.quant_w4(inp["w"], K, sw)
+        return dict(qa=qa, sw=sw, y=oracle.gemm_w4a8(qa, sa, qw, sw, K,
+                                                      inp["bias"].astype(np.float64)))
+
+    def check(self, ref):
+        import torch
+        sel = torch.as_tensor(self.rows, device=self.lay.y.device)
+        n = codes_equal(self.lay.xq[sel].cpu().numpy(), ref["qa"], "activation codes")
+        require(np.array_equal(self.lay.w_scales_host, ref["sw"]), "weight scales differ")
+        return {"codes_bit_exact": n,
+                "y_row_error": rows_close(self.lay.y[sel].cpu().numpy(), ref["y"], self.tol, "y")}
+
+
 _zc = {}
 
 
@@ -507,8 +575,10 @@ WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
              "c4i8y": lambda: Ssd(False, True), "c3": lambda: Mamba1(False),
              "c3se": lambda: Mamba1(True), "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
              "c2": lambda: S4d(False), "c2i16": lambda: S4d(True), "c5": lambda: Decode(False),
-             "c5f16": lambda: Decode(True)}
-OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3i8y", "c4f16", "c4i8y", "c5", "c5f16")
+             "c5f16": lambda: Decode(True), "w4a8d": lambda: W4A8(256), "w4a8p": lambda: W4A8(16384)}
+OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3i8y", "c4f16", "c4i8y", "c5", "c5f16", "w4a8d",
+          "w4a8p")
+INT8_MFMA_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 
 
 # ------------------------------------------------------------------------------------------------
@@ -621,7 +691,8 @@ def cpu_and_parity(wl, budget_s, with_baseline=True):
     parity["tolerance"] = wl.tol
     base = None
     if with_baseline:
-        base = {"value": reps * wl.sample_updates() / dt, "unit": "state-updates/s",
+        unit = "int8 ops/s" if wl.bound == "mfma" else "state-updates/s"
+        base = {"value": reps * wl.sample_updates() / dt, "unit": unit,
                 "cores": oracle.max_threads(), "kind": "oracle",
                 "sample": f"{wl.sample_desc}; {reps} rep(s) in {dt:.1f} s"}
     return base, parity
@@ -652,6 +723,10 @@ def run_workload(torch, dev, name, steps, warmup, budget_s, with_baseline=True):
         achieved = wl.ops() / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TOPS, 2),
                 "unit": "T VALU lane-ops/s", "frac": round(achieved / VALU_PEAK_TOPS, 4)}
+    elif wl.bound == "mfma":
+        achieved = wl.ops() / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_MFMA_PEAK_TOPS,
+                "unit": "T int8 ops/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4)}
     else:
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -775,6 +850,7 @@ def main():
                 w2, r2 = run_workload(torch, dev, name, min(args.steps, 30), min(args.warmup, 3),
                                       2.0, not args.no_cpu_baseline)
                 e = {"workload": w2.config["workload"], "value": r2["value"],
+                     "unit": "int8 ops/s" if w2.bound == "mfma" else "state-updates/s",
                      "ms_per_step": r2["ms_per_step"], "parity": r2["parity"],
                      "roofline": {k: r2["roofline"][k] for k in
                                   ("bound", "achieved", "peak", "unit", "frac", "traffic",

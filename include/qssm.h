@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 130 /* 1.3.0: int8 output fields appended to qssm_ssd_args and qssm_update_args */
+#define QSSM_VERSION 140 /* 1.4.0: W4A8 linear layer */
 
 typedef int32_t qssm_status;
 enum {
@@ -344,6 +344,33 @@ typedef struct qssm_update_args {
 qssm_status qssm_state_update(const qssm_update_args* a, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * W4A8 linear layer: 4-bit weights x int8 activations on int8 MFMA with int32 accumulation.
+ * Quamba2, abstract (W4A8 for large-batch decoding: the in and out projections around the
+ * recurrence).
+ *   y[m, n] = bias[n] + sum_g (sa * sw[n, g]) * sum_{k in group g} qa[m, k] * qw[n, k]
+ * a: int8 activation codes [M, K] (row-major) with one scale a_scale[0] (device; an invalid scale
+ *    gives y = bias); w: packed 4-bit codes [N, K / 2] as written by qssm_quant_w4 (each run of 8
+ *    input channels k0 .. k0 + 7 in 4 bytes, byte b = code k0 + b in the low nibble and k0 + 4 + b
+ *    in the high nibble, two's complement); w_scales [N, K / group] fp32 (a scale outside the valid
+ *    range gives that group 0); bias [N] fp32 or NULL; y [M, N] fp32 or fp16 (y_dtype).
+ * Requires K a positive multiple of 64, group a multiple of 64 dividing K (group == K: one scale per
+ * output channel), group <= 131072; a and w 16-byte aligned. Each group's integer sum is exact
+ * (int32) and scaled once in fp32. */
+typedef struct qssm_gemm_args {
+  int64_t M, N, K;
+  int32_t group;
+  int32_t y_dtype;          /* QSSM_F32 or QSSM_F16 */
+  const int8_t* a;          /* [M, K] */
+  const float* a_scale;     /* [1] */
+  const uint8_t* w;         /* [N, K / 2] packed */
+  const float* w_scales;    /* [N, K / group] */
+  const float* bias;        /* [N] or NULL */
+  void* y;                  /* [M, N] */
+} qssm_gemm_args;
+
+qssm_status qssm_gemm_w4a8(const qssm_gemm_args* a, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Host-side offline calibration (CPU only; every pointer below is a HOST pointer).
  * Quamba2, method steps 1-2 (offline activation statistics; sort and cluster the x channels);
  * Quamba-SE, section 4.1 (L at the 5th and H at the 99.9th percentile, EMA with alpha = 0.1).
@@ -404,14 +431,22 @@ qssm_status qssm_calib_s4d_state_scale(int64_t H, int64_t N, int64_t L, const in
                                        const float* B_im_s, const float* log_dt,
                                        const float* umax, double headroom, float* out);
 
+/* Offline 4-bit weight quantization for qssm_gemm_w4a8 (host): for weights w [N, K] fp32,
+ * scales[n * (K / group) + g] = fl32(absmax / 7) of the group's finite values (absmax 0 -> 1,
+ * clamped to [2^-100, 2^100]), codes clamp(RNE(w / s), -8, 7) by the exact quotient (NaN -> 0,
+ * +-Inf saturate), packed into packed [N, K / 2] in the layout qssm_gemm_w4a8 reads. group must be a
+ * multiple of 8 dividing K. */
+qssm_status qssm_quant_w4(const float* w, int64_t N, int64_t K, int32_t group, float* scales,
+                          uint8_t* packed);
+
 /* ---------------------------------------------------------------------------------------------
  * Library information. */
 const char* qssm_status_string(qssm_status s);
 /* Message of the last failing call on this host thread ("" if none). */
 const char* qssm_last_error(void);
 int32_t qssm_version(void);
-/* sizeof of the argument structs as compiled (0: scan, 1: s4d, 2: ssd, 3: update), so bindings can
- * check their layout. Returns 0 for an unknown kind. */
+/* sizeof of the argument structs as compiled (0: scan, 1: s4d, 2: ssd, 3: update, 4: gemm), so
+ * bindings can check their layout. Returns 0 for an unknown kind. */
 size_t qssm_args_size(int32_t kind);
 
 #ifdef __cplusplus

@@ -196,3 +196,20 @@ def quantizer_edge_values(cfg=7, n=4096, scale=np.float32(0.0371)):
                         1e30, -1e30, 1e-30, -1e-30], dtype=np.float32)
     rand = (r.standard_normal(n) * 60.0 * float(scale)).astype(np.float32)
     return np.concatenate([t32, up, dn, special, rand]).astype(np.float32)
+
+
+# ------------------------------------------------------------------------------------------------
+# W4A8 linear layer (the Mamba2-8B input projection: K = d_model 4096, N = 18560)
+
+def w4a8_inputs(cfg=8, M=256, N=18560, K=4096):
+    """Weights w [N, K] ~ N(0, 1/K) with a per-output-channel spread exp(U(-1, 1)); activations x
+    [M, K] ~ N(0,1) with 0.1% outliers x10; a calibration draw of the same law [256, K]; bias
+    [N] ~ 0.1 N(0,1)."""
+    r = rng(cfg, BS)
+    w = (r.standard_normal((N, K), dtype=np.float32) / np.float32(np.sqrt(K)) *
+         np.exp(rng(cfg, AS).uniform(-1.0, 1.0, (N, 1))).astype(np.float32))
+    def act(rr, shape):
+        a = rr.standard_normal(shape, dtype=np.float32)
+        return np.where(rr.random(shape) < 0.001, a * np.float32(10.0), a).astype(np.float32)
+    return dict(w=w.astype(np.float32), x=act(rng(cfg, X), (M, K)), x_cal=act(rng(cfg, CAL), (256, K)),
+                bias=(0.1 * rng(cfg, DS).standard_normal(N)).astype(np.float32))

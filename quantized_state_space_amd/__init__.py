@@ -67,7 +67,12 @@ class UpdateArgs(ctypes.Structure):
                 ("y_scales", _P), ("y_bias", _P)]
 
 
-ARG_STRUCTS = {0: ScanArgs, 1: S4dArgs, 2: SsdArgs, 3: UpdateArgs}
+class GemmArgs(ctypes.Structure):
+    _fields_ = [("M", _I64), ("N", _I64), ("K", _I64), ("group", _I32), ("y_dtype", _I32),
+                ("a", _P), ("a_scale", _P), ("w", _P), ("w_scales", _P), ("bias", _P), ("y", _P)]
+
+
+ARG_STRUCTS = {0: ScanArgs, 1: S4dArgs, 2: SsdArgs, 3: UpdateArgs, 4: GemmArgs}
 
 # Every symbol include/qssm.h declares, with its ctypes signature.
 SIGNATURES = {
@@ -82,6 +87,8 @@ SIGNATURES = {
     "qssm_ssd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SsdArgs)]),
     "qssm_ssd_chunk_int8": (_I32, [ctypes.POINTER(SsdArgs), _P, ctypes.c_size_t, _P]),
     "qssm_state_update": (_I32, [ctypes.POINTER(UpdateArgs), _P]),
+    "qssm_gemm_w4a8": (_I32, [ctypes.POINTER(GemmArgs), _P]),
+    "qssm_quant_w4": (_I32, [_P, _I64, _I64, _I32, _P, _P]),
     "qssm_calib_channel_absmax": (_I32, [_P, _I64, _I64, _I64, _P]),
     "qssm_calib_scales": (_I32, [_P, _I64, _P]),
     "qssm_calib_cluster_channels": (_I32, [_P, _I32, _I32, _P, _P]),
@@ -380,7 +387,45 @@ def qssm_state_update(args, stream=None):
 
 
 # ------------------------------------------------------------------------------------------------
+# W4A8 linear layer
+
+def gemm_args(a, a_scale, w_packed, w_scales, group, y, bias=None):
+    """a: int8 [M, K]; a_scale float32 [1]; w_packed uint8 [N, K / 2] (qssm_quant_w4 layout);
+    w_scales float32 [N, K / group]; y float32 or float16 [M, N]; bias float32 [N] or None."""
+    torch = _t()
+    M, K = a.shape
+    N = w_packed.shape[0]
+    if tuple(w_packed.shape) != (N, K // 2) or tuple(y.shape) != (M, N):
+        raise ValueError("shapes of a, w_packed and y do not match")
+    if w_scales.numel() != N * (K // group) or (bias is not None and bias.numel() != N):
+        raise ValueError("w_scales must be [N, K / group] and bias [N]")
+    ydt = {torch.float32: QSSM_F32, torch.float16: QSSM_F16}.get(y.dtype, -1)
+    keep = (a, a_scale, w_packed, w_scales, y, bias)
+    return _fill(GemmArgs(), keep=keep, M=M, N=N, K=K, group=group, y_dtype=ydt,
+                 a=_ptr(a, torch.int8, "a"), a_scale=_ptr(a_scale, torch.float32, "a_scale"),
+                 w=_ptr(w_packed, torch.uint8, "w"),
+                 w_scales=_ptr(w_scales, torch.float32, "w_scales"),
+                 bias=_ptr(bias, torch.float32, "bias", True), y=_ptr(y, None, "y"))
+
+
+def qssm_gemm_w4a8(args, stream=None):
+    _check("qssm_gemm_w4a8", load().qssm_gemm_w4a8(ctypes.byref(args), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------------
 # Host calibration (numpy arrays on the CPU)
+
+def qssm_quant_w4(w, group):
+    """Offline 4-bit weight quantization (host): returns (scales [N, K / group] float32,
+    packed [N, K / 2] uint8)."""
+    import numpy as np
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    scales = np.empty((N, K // group if group > 0 else 0), np.float32)
+    packed = np.empty((N, K // 2), np.uint8)
+    _check("qssm_quant_w4", load().qssm_quant_w4(_np_ptr(w), N, K, group, _np_ptr(scales),
+                                                  _np_ptr(packed)))
+    return scales, packed
 
 def _np_ptr(a):
     return ctypes.c_void_p(a.ctypes.data)

@@ -250,4 +250,37 @@ qssm_status qssm_calib_s4d_state_scale(int64_t H, int64_t N, int64_t L, const in
   return QSSM_OK;
 }
 
+qssm_status qssm_quant_w4(const float* w, int64_t N, int64_t K, int32_t group, float* scales,
+                          uint8_t* packed) {
+  qssm::clear_error();
+  if (N < 0 || K < 0 || group < 8 || group % 8 != 0 || K % group != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "group must be a multiple of 8 that divides K");
+  if ((N * K > 0) && (!w || !scales || !packed)) return fail(QSSM_ERR_INVALID_ARG, "null pointer");
+  const int64_t ng = K / group;
+  std::vector<int8_t> q((size_t)K);
+  for (int64_t n = 0; n < N; ++n) {
+    const float* row = w + n * K;
+    for (int64_t g = 0; g < ng; ++g) {
+      float m = 0.0f;
+      for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+        const float a = std::fabs(row[k]);
+        if (a <= std::numeric_limits<float>::max() && a > m) m = a;
+      }
+      float s = (m == 0.0f) ? 1.0f : m / 7.0f;
+      if (s < 0x1p-100f) s = 0x1p-100f;
+      if (s > 0x1p100f) s = 0x1p100f;
+      scales[n * ng + g] = s;
+      for (int64_t k = g * group; k < (g + 1) * group; ++k)
+        q[(size_t)k] = (int8_t)qssm::rne_sat(row[k], s, -8.0f, 7.0f);
+    }
+    // eight consecutive codes per 4 bytes: byte b = code k0 + b (low nibble), k0 + 4 + b (high)
+    uint8_t* out = packed + n * (K / 2);
+    for (int64_t k0 = 0; k0 < K; k0 += 8)
+      for (int b = 0; b < 4; ++b)
+        out[k0 / 2 + b] = (uint8_t)(((uint8_t)q[(size_t)(k0 + b)] & 0x0Fu) |
+                                    (((uint8_t)q[(size_t)(k0 + 4 + b)] & 0x0Fu) << 4));
+  }
+  return QSSM_OK;
+}
+
 }  // extern "C"

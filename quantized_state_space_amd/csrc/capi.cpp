@@ -54,6 +54,7 @@ size_t qssm_args_size(int32_t kind) {
     case 1: return sizeof(qssm_s4d_args);
     case 2: return sizeof(qssm_ssd_args);
     case 3: return sizeof(qssm_update_args);
+    case 4: return sizeof(qssm_gemm_args);
     default: return 0;
   }
 }

@@ -1,0 +1,221 @@
+// W4A8 linear layer: 4-bit weights x int8 activations on int8 MFMA with int32 accumulation.
+//
+// Quamba2, abstract: W4A8 for large-batch decoding (the in and out projections around the
+// recurrence). Per output channel n and group g of `group` consecutive input channels:
+//     y[m, n] = bias[n] + sum_g (sa * sw[n, g]) * sum_{k in g} qa[m, k] * qw[n, k]
+// with qa int8 activation codes (one scale sa) and qw in [-8, 7] packed two per byte.
+//
+// Packed weight layout (per output channel, K / 2 bytes): each run of 8 consecutive input channels
+// k0 .. k0 + 7 takes 4 bytes, byte b holding k0 + b in its low nibble and k0 + 4 + b in its high
+// nibble (two's complement nibbles). Masking a 32-bit word with 0xF0F0F0F0 after a left shift by 4
+// (low nibbles) or without it (high nibbles) then yields the 8 codes times 16 as int8 bytes, in k
+// order: the unpacking costs two instructions per 8 codes and no sign extension. The factor 16 is
+// exact and divided out of the scale.
+//
+// Tiling (CDNA4, wave64): a workgroup of 4 waves computes a 128 x 128 tile of y, K in steps of 64
+// staged through LDS (double-buffered, the next step's global loads in registers during the
+// current step's products); wave (wm, wn) owns a 64 x 64 block = 2 x 2 tiles of
+// v_mfma_i32_32x32x32_i8 (operand lane l: row or column l % 32, 16 consecutive k at 16 (l / 32)).
+// The int32 sums of a weight group are scaled into fp32 at the group's end.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+using namespace qssm;
+
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kARow = 80;  // padded bytes of an activation row in LDS (64 + 16): no bank conflicts
+constexpr int kWRow = 40;  // padded bytes of a packed weight row in LDS (32 + 8)
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct GemmParams {
+  int64_t M, N, K;
+  int32_t group, yf16;
+  const int8_t* a;
+  const float* a_scale;
+  const uint8_t* w;
+  const float* w_scales;
+  const float* bias;
+  void* y;
+};
+
+struct GemmSmem {
+  int8_t a[2][kBM * kARow];
+  uint8_t w[2][kBN * kWRow];
+};
+
+// Global loads of K step kt: thread t takes activation row t / 2 (32 bytes at (t % 2) * 32) and
+// weight row t / 2 (16 bytes at (t % 2) * 16). Branch-free: rows past M or N load a valid row and
+// are zeroed by the store.
+__device__ __forceinline__ void load_step(const GemmParams& p, int64_t m0, int64_t n0, int64_t kt,
+                                          int tid, uint4 (&ra)[2], uint4& rw) {
+  const int row = tid >> 1, half = tid & 1;
+  const int64_t m = min(m0 + row, p.M - 1), n = min(n0 + row, p.N - 1);
+  const uint4* src = reinterpret_cast<const uint4*>(p.a + m * p.K + kt * kBK + half * 32);
+  ra[0] = src[0];
+  ra[1] = src[1];
+  rw = *reinterpret_cast<const uint4*>(p.w + n * (p.K / 2) + kt * (kBK / 2) + half * 16);
+}
+
+__device__ __forceinline__ uint4 masked(uint4 v, bool on) {
+  return on ? v : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ void store_step(GemmSmem& s, int buf, int tid, bool a_on, bool w_on,
+                                           const uint4 (&ra)[2], const uint4& rw) {
+  const int row = tid >> 1, half = tid & 1;
+  uint4* da = reinterpret_cast<uint4*>(s.a[buf] + row * kARow + half * 32);
+  da[0] = masked(ra[0], a_on);
+  da[1] = masked(ra[1], a_on);
+  *reinterpret_cast<uint4*>(s.w[buf] + row * kWRow + half * 16) = masked(rw, w_on);
+}
+
+// 16 codes (times 16) of 16 consecutive input channels from their 8 packed bytes
+__device__ __forceinline__ v4i unpack16(uint2 d) {
+  v4i o;
+  o[0] = (int)((d.x << 4) & 0xF0F0F0F0u);
+  o[1] = (int)(d.x & 0xF0F0F0F0u);
+  o[2] = (int)((d.y << 4) & 0xF0F0F0F0u);
+  o[3] = (int)(d.y & 0xF0F0F0F0u);
+  return o;
+}
+
+// (sa / 16) * sw[n, g], 0 for a column past N or an invalid weight scale
+__device__ __forceinline__ float group_scale(const GemmParams& p, int64_t n, int64_t ngroups,
+                                             int64_t g, float sa16) {
+  if (n >= p.N) return 0.0f;
+  const float sw = p.w_scales[n * ngroups + g];
+  return scale_ok(sw) ? sa16 * sw : 0.0f;
+}
+
+template <bool GROUPED>
+__global__ __launch_bounds__(256) void k_gemm_w4a8(GemmParams p) {
+  __shared__ __align__(16) GemmSmem s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t nk = p.K / kBK;
+  const int64_t steps_per_group = p.group / kBK;
+  const int kh = lane >> 5;
+  // activation scale over 16 (the unpacked weight codes carry a factor 16); an invalid scale
+  // gives 0 as the activations are then all 0
+  const float sa = p.a_scale[0];
+  const float sa16 = scale_ok(sa) ? sa * 0.0625f : 0.0f;
+
+  v16i acc[2][2];
+  float out[GROUPED ? 2 : 1][GROUPED ? 2 : 1][GROUPED ? 16 : 1];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[mt][nt] = v16i{};
+      if (GROUPED)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) out[GROUPED ? mt : 0][GROUPED ? nt : 0][GROUPED ? r : 0] = 0.0f;
+    }
+
+  // this lane's output column of column tile nt is ncol0 + 32 nt
+  const int64_t ncol0 = n0 + wn * 64 + (lane & 31);
+  const int64_t ngroups = p.K / p.group;
+
+  // rows of this thread's loads inside M and N
+  const bool a_on = m0 + (tid >> 1) < p.M, w_on = n0 + (tid >> 1) < p.N;
+  uint4 ra[2], rw;
+  load_step(p, m0, n0, 0, tid, ra, rw);
+  store_step(s, 0, tid, a_on, w_on, ra, rw);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) load_step(p, m0, n0, kt + 1, tid, ra, rw);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      v4i av[2], bv[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        av[mt] = *reinterpret_cast<const v4i*>(s.a[buf] + (wm * 64 + mt * 32 + (lane & 31)) * kARow +
+                                               ks * 32 + 16 * kh);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        bv[nt] = unpack16(*reinterpret_cast<const uint2*>(
+            s.w[buf] + (wn * 64 + nt * 32 + (lane & 31)) * kWRow + ks * 16 + 8 * kh));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+    if (GROUPED && (kt + 1) % steps_per_group == 0) {
+      // end of a weight group: scale its exact int32 sums into fp32
+      const int64_t g = kt / steps_per_group;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float f = group_scale(p, ncol0 + 32 * nt, ngroups, g, sa16);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            out[GROUPED ? mt : 0][GROUPED ? nt : 0][GROUPED ? r : 0] =
+                fmaf(f, (float)acc[mt][nt][r], out[GROUPED ? mt : 0][GROUPED ? nt : 0][GROUPED ? r : 0]);
+          acc[mt][nt] = v16i{};
+        }
+      }
+    }
+    if (kt + 1 < nk) {
+      store_step(s, buf ^ 1, tid, a_on, w_on, ra, rw);
+      __syncthreads();
+    }
+  }
+
+  // y = bias + out; register r of a tile holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t n = ncol0 + 32 * nt;
+    if (n >= p.N) continue;
+    const float bn = p.bias ? p.bias[n] : 0.0f;
+    const float f = GROUPED ? 0.0f : group_scale(p, n, ngroups, 0, sa16);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + mt * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+        if (m >= p.M) continue;
+        const float v = GROUPED ? out[GROUPED ? mt : 0][GROUPED ? nt : 0][GROUPED ? r : 0] + bn
+                                : fmaf(f, (float)acc[mt][nt][r], bn);
+        if (p.yf16) reinterpret_cast<__half*>(p.y)[m * p.N + n] = __float2half_rn(v);
+        else reinterpret_cast<float*>(p.y)[m * p.N + n] = v;
+      }
+  }
+}
+
+}  // namespace
+
+extern "C" qssm_status qssm_gemm_w4a8(const qssm_gemm_args* a, hipStream_t stream) {
+  clear_error();
+  if (!a) return fail(QSSM_ERR_INVALID_ARG, "args is null");
+  const int64_t M = a->M, N = a->N, K = a->K;
+  if (M < 0 || N < 0 || K < 0) return fail(QSSM_ERR_INVALID_ARG, "negative extent");
+  if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16)
+    return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32 or QSSM_F16");
+  if (K <= 0 || K % kBK != 0) return fail(QSSM_ERR_UNSUPPORTED, "K must be a positive multiple of 64");
+  if (a->group < kBK || a->group % kBK != 0 || K % a->group != 0)
+    return fail(QSSM_ERR_UNSUPPORTED, "group must be a multiple of 64 that divides K");
+  if (a->group > 131072) return fail(QSSM_ERR_UNSUPPORTED, "group above 131072 (int32 sums)");
+  if (M == 0 || N == 0) return QSSM_OK;
+  if (!a->a_scale || !a->w_scales || !a->a || !a->w || !a->y)
+    return fail(QSSM_ERR_INVALID_ARG, "null required pointer");
+  if (((uintptr_t)a->a | (uintptr_t)a->w) % 16 != 0)
+    return fail(QSSM_ERR_INVALID_ARG, "a and w must be 16-byte aligned");
+  const int64_t gx = (N + kBN - 1) / kBN, gy = (M + kBM - 1) / kBM;
+  if (gx > 0x7fffffff || gy > 65535) return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
+  GemmParams p{M, N, K, a->group, a->y_dtype == QSSM_F16, a->a, a->a_scale, a->w, a->w_scales,
+               a->bias, a->y};
+  const dim3 grid((unsigned)gx, (unsigned)gy);
+  if (a->group == K) k_gemm_w4a8<false><<<grid, 256, 0, stream>>>(p);
+  else k_gemm_w4a8<true><<<grid, 256, 0, stream>>>(p);
+  return launch_status("gemm_w4a8");
+}

@@ -17,7 +17,7 @@ from . import (QSSM_F16, QSSM_F32, QSSM_I16, QSSM_X_INT8, QSSM_X_SOFTEDGE, qssm_
                qssm_quant_group_x, qssm_quant_state_group_BC, qssm_s4d_scan, qssm_scan_w8a8,
                qssm_scan_workspace_size, qssm_softedge_encode, qssm_ssd_chunk_int8,
                qssm_ssd_workspace_size, qssm_state_update, s4d_args, scan_args, ssd_args,
-               update_args)
+               update_args, gemm_args, qssm_gemm_w4a8, qssm_quant_w4)
 
 
 def _dev(a, device, dtype=None):
@@ -388,4 +388,47 @@ class DecodeLayer:
 
     def step(self):
         qssm_state_update(self.args)
+        return self.y
+
+
+# ------------------------------------------------------------------------------------------------
+# W4A8 linear layer
+
+class W4A8Linear:
+    """y = x W^T (+ bias) with 4-bit weights [N, K] quantized offline (per output channel and
+    group of input channels) and int8 activations with one static scale. One step = quantize the
+    fp32 activations [M, K] to int8, then the W4A8 GEMM."""
+
+    def __init__(self, w, x, x_cal, device, group=None, bias=None, y_dtype=QSSM_F32):
+        import torch
+        dev = device
+        N, K = w.shape
+        M = x.shape[0]
+        self.group = K if group is None else group
+        self.shape = (M, N, K)
+        ws, wp = qssm_quant_w4(w, self.group)
+        self.w_scales_host, self.w_packed_host = ws, wp
+        self.xs = _dev(qssm_calib_scales(qssm_calib_channel_absmax(
+            np.ascontiguousarray(x_cal, np.float32).reshape(1, 1, -1))), dev)
+        self.x = _dev(np.ascontiguousarray(x, np.float32), dev)
+        self.xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        self.w = _dev(wp, dev)
+        self.ws = _dev(ws, dev)
+        self.bias = None if bias is None else _dev(np.asarray(bias, np.float32), dev)
+        self.y = torch.empty((M, N), dtype=torch.float32 if y_dtype == QSSM_F32 else torch.float16,
+                             device=dev)
+        self.zero_group = torch.zeros(1, dtype=torch.uint8, device=dev)
+        self.args = gemm_args(self.xq, self.xs, self.w, self.ws, self.group, self.y, bias=self.bias)
+
+    def quantize(self):
+        M, N, K = self.shape
+        qssm_quant_group_x(self.x.view(1, 1, M * K), self.zero_group, 1, self.xs,
+                           self.xq.view(1, 1, M * K))
+
+    def gemm(self):
+        qssm_gemm_w4a8(self.args)
+
+    def step(self):
+        self.quantize()
+        self.gemm()
         return self.y

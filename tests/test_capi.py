@@ -42,7 +42,7 @@ def test_struct_layouts_and_version():
     for kind, st in qs.ARG_STRUCTS.items():
         assert lib.qssm_args_size(kind) == ctypes.sizeof(st)
     assert lib.qssm_args_size(99) == 0
-    assert lib.qssm_version() == 130
+    assert lib.qssm_version() == 140
     assert lib.qssm_status_string(qs.QSSM_ERR_WORKSPACE) == b"workspace missing or too small"
 
 
@@ -239,3 +239,44 @@ def test_s4d_state_scale_bounds_the_fp64_state():
     geo = np.where(ab < 1, np.minimum(1 / np.maximum(1 - ab, 1e-300), L), L * ab ** (L - 1))
     want = (dt * bb * np.maximum(ab, 1) * umax.astype(np.float64)[:, None] * geo).max(axis=1) / 32767
     np.testing.assert_allclose(got, want.astype(np.float32), rtol=1e-6)
+
+
+def unpack_w4(packed, K):
+    """Codes [N, K] from the packed layout (each 8 input channels in 4 bytes, byte b = code k0 + b
+    in the low nibble and k0 + 4 + b in the high nibble)."""
+    p = np.asarray(packed, np.uint8).reshape(packed.shape[0], K // 8, 4)
+    lo = (p & 0x0F).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    return np.concatenate([lo, hi], axis=2).reshape(packed.shape[0], K).astype(np.int8)
+
+
+def test_w4_packing_golden():
+    """tests/golden/w4_packing.txt: a hand-worked example of the codes and the byte layout."""
+    rows = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "w4_packing.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            rows[k] = v
+    w = np.array([[float(t) for t in rows["w"]]], np.float32)
+    s, packed = qs.qssm_quant_w4(w, 8)
+    assert s[0, 0] == np.float32(float(rows["scale"][0]))
+    assert packed[0].tolist() == [int(t, 16) for t in rows["bytes"]]
+    codes = [int(t) for t in rows["codes"]]
+    assert unpack_w4(packed, 8)[0].tolist() == codes
+    assert oracle.quant_w4(w, 8, oracle.w4_scales(w, 8))[0].tolist() == codes
+
+
+@pytest.mark.parametrize("N,K,group,seed", [(5, 64, 64, 0), (17, 256, 64, 1), (3, 128, 8, 2)])
+def test_w4_quantizer_matches_oracle(N, K, group, seed):
+    r = np.random.default_rng(seed)
+    w = (r.standard_normal((N, K)) * np.exp(r.uniform(-3, 3, (N, 1)))).astype(np.float32)
+    w[0, :4] = [np.nan, np.inf, -np.inf, 0.0]
+    w[1, :group] = 0.0  # an all-zero group: scale 1, codes 0
+    s, packed = qs.qssm_quant_w4(w, group)
+    ws = oracle.w4_scales(w, group)
+    assert np.array_equal(s, ws)
+    assert np.array_equal(unpack_w4(packed, K), oracle.quant_w4(w, group, ws))
+    with pytest.raises(qs.QssmError, match="group"):
+        qs.qssm_quant_w4(w, 12)
