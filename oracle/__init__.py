@@ -72,13 +72,13 @@ def _declare(L):
     L.orc_quant_state_group.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _P]
     L.orc_scale_from_absmax.argtypes = [_F]
     L.orc_scale_from_absmax.restype = _F
-    L.orc_softedge_code.argtypes = [_F, _F, _F, _F]
+    L.orc_softedge_code.argtypes = [_F, _F, _F, _F, _I32]
     L.orc_softedge_code.restype = ctypes.c_uint8
-    L.orc_softedge_value.argtypes = [ctypes.c_uint8, _F]
+    L.orc_softedge_value.argtypes = [ctypes.c_uint8, _F, _I32]
     L.orc_softedge_value.restype = _D
-    L.orc_softedge_decode_f32.argtypes = [ctypes.c_uint8, _F]
+    L.orc_softedge_decode_f32.argtypes = [ctypes.c_uint8, _F, _I32]
     L.orc_softedge_decode_f32.restype = _F
-    L.orc_softedge_encode.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]
+    L.orc_softedge_encode.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P]
     L.orc_cluster_sorted.argtypes = [_P, _I32, _I32, _P]
     L.orc_selective_scan.argtypes = [_I64] * 5 + [_P] * 9
     L.orc_s4d_zoh.argtypes = [_P, _P, _D, _I64, _P, _P]
@@ -227,38 +227,68 @@ def softedge_thresholds(v, alpha=SOFTEDGE_EMA_ALPHA, prev=None):
     return s, L32, H32, (l, h)
 
 
-def softedge_encode(x, group_of, s, L, H, perm=None):
+SOFTEDGE_RATIOS = (4, 2)  # sections 2.1-2.2: scale/4 and scale*4; section 4.1: scale/2 and scale*2
+
+
+def softedge_track(x, group_of, G, perm=None, alpha=SOFTEDGE_EMA_ALPHA, prev=None):
+    """Per-group thresholds of one mini-batch x [outer, C, inner] in output-channel order (channel
+    c reads x[:, perm[c], :] and belongs to group group_of[c]): softedge_thresholds over the group's
+    values, EMA-blended with prev[g] (an fp64 (L, H) pair, or None for the first batch).
+    A group with no values keeps prev[g] (or gets L = H = 0 and s = 1 without one).
+    Returns s, L, H (fp32 [G]) and the new states (list of fp64 pairs)."""
+    x = np.asarray(x, np.float32)
+    xs = x if perm is None else x[:, np.asarray(perm, np.int64), :]
+    group_of = np.asarray(group_of, np.int64)
+    s = np.ones(G, np.float32)
+    L = np.zeros(G, np.float32)
+    H = np.zeros(G, np.float32)
+    states = []
+    for g in range(G):
+        v = xs[:, group_of == g, :]
+        p = None if prev is None else prev[g]
+        if v.size == 0:
+            st = (0.0, 0.0) if p is None else (float(p[0]), float(p[1]))
+            L[g], H[g] = np.float32(st[0]), np.float32(st[1])
+            s[g] = np.float32(1.0) if H[g] == 0 else np.float32(H[g] / np.float32(63.0))
+        else:
+            s[g], L[g], H[g], st = softedge_thresholds(v, alpha=alpha, prev=p)
+        states.append(st)
+    return s, L, H, states
+
+
+def softedge_encode(x, group_of, s, L, H, perm=None, ratio=4):
     x = _c(x, np.float32)
     outer, C, inner = x.shape
     code = np.empty(x.shape, dtype=np.uint8)
     with _Call():
         lib().orc_softedge_encode(_ptr(x), outer, C, inner, _ptr(_c(perm, np.int32)),
                                   _ptr(_c(group_of, np.uint8)), _ptr(_c(s, np.float32)),
-                                  _ptr(_c(L, np.float32)), _ptr(_c(H, np.float32)), _ptr(code))
+                                  _ptr(_c(L, np.float32)), _ptr(_c(H, np.float32)), int(ratio),
+                                  _ptr(code))
     return code
 
 
-def softedge_value_table(s):
+def softedge_value_table(s, ratio=4):
     """fp64 value of each of the 256 bytes for base scale s."""
     f = lib().orc_softedge_value
-    return np.array([f(b, float(s)) for b in range(256)], dtype=np.float64)
+    return np.array([f(b, float(s), int(ratio)) for b in range(256)], dtype=np.float64)
 
 
-def softedge_values(code, group_of, s):
+def softedge_values(code, group_of, s, ratio=4):
     """fp64 values of codes [outer, C, inner] (exact)."""
     code = np.asarray(code, dtype=np.uint8)
     out = np.empty(code.shape, dtype=np.float64)
     s = np.asarray(s, dtype=np.float32)
     group_of = np.asarray(group_of)
-    tables = {g: softedge_value_table(s[g]) for g in np.unique(group_of)}
+    tables = {g: softedge_value_table(s[g], ratio) for g in np.unique(group_of)}
     for c in range(code.shape[1]):
         out[:, c, :] = tables[group_of[c]][code[:, c, :]]
     return out
 
 
-def softedge_decode_f32(code, group_of, s):
+def softedge_decode_f32(code, group_of, s, ratio=4):
     """The library's fp32 decode: each value rounded once to fp32."""
-    return softedge_values(code, group_of, s).astype(np.float32)
+    return softedge_values(code, group_of, s, ratio).astype(np.float32)
 
 
 # ------------------------------------------------------------------------------------------------

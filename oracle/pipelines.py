@@ -10,8 +10,8 @@ import numpy as np
 
 from . import (cluster_channels, decode_step, dequant_group, dequant_state_group, finite_absmax,
                group_scales, quant_group_x, quant_state_group, s4d_scan, scale_from_absmax,
-               selective_scan, softedge_encode, softedge_thresholds, softedge_values, ssd_chunked,
-               ssd_as_sequential, state_group_scales)
+               selective_scan, softedge_encode, softedge_thresholds, softedge_track,
+               softedge_values, ssd_chunked, ssd_as_sequential, state_group_scales)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -29,13 +29,31 @@ def calib_x(x_cal, G):
     return perm, group_of, scale_from_absmax(g_abs)
 
 
-def calib_softedge(x_cal, perm, group_of, G):
+def calib_softedge(x_cal, perm, group_of, G, with_state=False):
+    """Per-group soft-edge (s, L, H) as a [3, G] array; with_state: also the fp64 (L, H) pairs
+    an EMA continues from."""
     xs = np.asarray(x_cal)[:, perm, :]
     out = np.zeros((3, G), np.float32)
+    states = []
     for g in range(G):
-        s, L, H, _ = softedge_thresholds(xs[:, group_of == g, :])
+        s, L, H, st = softedge_thresholds(xs[:, group_of == g, :])
         out[:, g] = (s, L, H)
-    return out
+        states.append(st)
+    return (out, states) if with_state else out
+
+
+def state_group_map(Gbc, N, gs):
+    """Scale index of each of the Gbc * N states (B/C group g, state n): g * (N / gs) + n / gs."""
+    n = np.arange(Gbc * N)
+    return ((n // N) * (N // gs) + (n % N) // gs).astype(np.uint8)
+
+
+def calib_softedge_state_groups(bc_cal, gs):
+    """Soft-edge (s, L, H) [3, Gbc * N / gs] of B or C [outer, Gbc, N, inner], one per state group."""
+    bc = np.asarray(bc_cal)
+    o, Gbc, N, inner = bc.shape
+    return calib_softedge(bc.reshape(o, Gbc * N, inner), np.arange(Gbc * N),
+                          state_group_map(Gbc, N, gs), Gbc * N // gs)
 
 
 def calib_ssd_x(x_cal, nheads, headdim, ngroups, groups_per_block):
@@ -59,20 +77,40 @@ def calib_ssd_x(x_cal, nheads, headdim, ngroups, groups_per_block):
 # ------------------------------------------------------------------------------------------------
 # Mamba1
 
-def mamba1_calib(inp, G, gs, soft_edge=False):
+def mamba1_calib(inp, G, gs, soft_edge=False, bc_soft_edge=False):
     """Offline calibration of the Mamba1 layer from its calibration draws."""
     perm, group_of, xs = calib_x(inp["x_cal"], G)
     c = dict(perm=perm, group_of=group_of, xs=xs, bs=state_group_scales(inp["B_cal"], gs),
              cs=state_group_scales(inp["C_cal"], gs))
     if soft_edge:
-        c["se"] = calib_softedge(inp["x_cal"], perm, group_of, G)
+        c["se"], c["se_state"] = calib_softedge(inp["x_cal"], perm, group_of, G, with_state=True)
+    if bc_soft_edge:
+        c["bse"] = calib_softedge_state_groups(inp["B_cal"], gs)
+        c["cse"] = calib_softedge_state_groups(inp["C_cal"], gs)
     return c
 
 
-def mamba1(inp, G, gs, soft_edge=False, dynamic=False, rows=None, with_h0=False, calib=None):
+def _bc_softedge(bc, gs, se, ratio):
+    """Soft-edge bytes of B or C [outer, Gbc, N, inner] with per-state-group (s, L, H), and their
+    exact values."""
+    o, Gbc, N, inner = bc.shape
+    sg = state_group_map(Gbc, N, gs)
+    q = softedge_encode(np.asarray(bc, np.float32).reshape(o, Gbc * N, inner), sg, se[0], se[1],
+                        se[2], ratio=ratio)
+    v = softedge_values(q, sg, se[0], ratio=ratio)
+    return q.reshape(bc.shape), v.reshape(bc.shape)
+
+
+def mamba1(inp, G, gs, soft_edge=False, dynamic=False, rows=None, with_h0=False, calib=None,
+           se_ratio=4, bc_soft_edge=0, track=False):
     """Returns dict with perm, group_of, x/B/C scales, codes, and (for the selected (b, d) rows,
     all when rows is None) y and h_last in fp64. rows = (b_index_array, d_index_array).
-    calib: a precomputed mamba1_calib result (static scales)."""
+    calib: a precomputed mamba1_calib result (static scales).
+    soft_edge: x in soft-edge bytes with mode ratio se_ratio (4, or 2 for the shift-only form).
+    track: the x thresholds of this batch come from the section 4.1 EMA update, continuing the
+    calibration's state with this batch's own percentiles (softedge_track).
+    bc_soft_edge: 0 for int8 B/C, else the mode ratio of soft-edge B/C bytes (per-state-group base
+    scales and thresholds from the calibration draws)."""
     x = inp["x"]
     B, D, L = x.shape
     if calib is not None:
@@ -89,15 +127,30 @@ def mamba1(inp, G, gs, soft_edge=False, dynamic=False, rows=None, with_h0=False,
         cs = state_group_scales(inp["C_cal"], gs)
     out = dict(perm=perm, group_of=group_of, bs=bs, cs=cs)
     if soft_edge:
-        s, Lt, Ht = calib["se"] if calib is not None else calib_softedge(inp["x_cal"], perm,
-                                                                          group_of, G)
-        out.update(xs=s, L=Lt, H=Ht)
-        xq = softedge_encode(x, group_of, s, Lt, Ht, perm=perm)
+        if calib is not None and "se" in calib:
+            se, st = calib["se"], calib["se_state"]
+        else:
+            se, st = calib_softedge(inp["x_cal"], perm, group_of, G, with_state=True)
+        s, Lt, Ht = se
+        if track:
+            s, Lt, Ht, st = softedge_track(x, group_of, G, perm=perm, prev=st)
+        out.update(xs=s, L=Lt, H=Ht, se_state=st)
+        xq = softedge_encode(x, group_of, s, Lt, Ht, perm=perm, ratio=se_ratio)
     else:
         out["xs"] = xs
         xq = quant_group_x(x, group_of, xs, perm=perm)
-    Bq = quant_state_group(inp["B"], gs, bs)
-    Cq = quant_state_group(inp["C"], gs, cs)
+    if bc_soft_edge:
+        bse = calib["bse"] if calib is not None and "bse" in calib else \
+            calib_softedge_state_groups(inp["B_cal"], gs)
+        cse = calib["cse"] if calib is not None and "cse" in calib else \
+            calib_softedge_state_groups(inp["C_cal"], gs)
+        Bq, Bv = _bc_softedge(inp["B"], gs, bse, bc_soft_edge)
+        Cq, Cv = _bc_softedge(inp["C"], gs, cse, bc_soft_edge)
+        out.update(bs=bse[0], cs=cse[0], bse=bse, cse=cse)
+    else:
+        Bq = quant_state_group(inp["B"], gs, bs)
+        Cq = quant_state_group(inp["C"], gs, cs)
+        Bv = Cv = None
     out.update(xq=xq, Bq=Bq, Cq=Cq)
     delta, A, Dk = inp["delta"][:, perm], inp["A"][perm], inp["D"][perm]
     h0 = inp["h0"][:, perm] if with_h0 else None
@@ -108,12 +161,12 @@ def mamba1(inp, G, gs, soft_edge=False, dynamic=False, rows=None, with_h0=False,
         ds = dsel[bsel == b] if rows is not None else dsel
         xq_b = xq[b:b + 1][:, ds]
         if soft_edge:
-            xh = softedge_values(xq_b, group_of[ds], out["xs"])
+            xh = softedge_values(xq_b, group_of[ds], out["xs"], ratio=se_ratio)
         else:
             xh = dequant_group(xq_b, group_of[ds], out["xs"])
-        y, hl = selective_scan(xh, delta[b:b + 1][:, ds], A[ds],
-                               dequant_state_group(Bq[b:b + 1], gs, bs),
-                               dequant_state_group(Cq[b:b + 1], gs, cs), Dk[ds],
+        Bh = Bv[b:b + 1] if Bv is not None else dequant_state_group(Bq[b:b + 1], gs, bs)
+        Ch = Cv[b:b + 1] if Cv is not None else dequant_state_group(Cq[b:b + 1], gs, cs)
+        y, hl = selective_scan(xh, delta[b:b + 1][:, ds], A[ds], Bh, Ch, Dk[ds],
                                None if h0 is None else h0[b:b + 1][:, ds])
         ys.append(y[0])
         hs.append(hl[0])

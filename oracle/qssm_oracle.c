@@ -92,18 +92,22 @@ EXPORT float orc_scale_from_absmax(float absmax) {
 
 /* ------------------------------------------------------------------------------------------ */
 /* [SE] 2.1-2.2 soft-edge code of one value. Classification on |v| with strict comparisons;
- * the {small, large} case table: (1,0) -> scale/4, (0,1) -> scale*4, otherwise the base scale. */
-EXPORT uint8_t orc_softedge_code(float v, float s, float L, float H) {
-  if (!scale_valid((double)s) || isnan(v)) return 0x00;
+ * the {small, large} case table: (1,0) -> scale/ratio, (0,1) -> scale*ratio, otherwise the base
+ * scale. ratio is 4 for the form of sections 2.1-2.2 and 2 for the shift-only form that section 4.1
+ * suggests for small hardware (one shift instead of a multiplier); nothing else changes. */
+static int ratio_ok(int32_t ratio) { return ratio == 2 || ratio == 4; }
+
+EXPORT uint8_t orc_softedge_code(float v, float s, float L, float H, int32_t ratio) {
+  if (!ratio_ok(ratio) || !scale_valid((double)s) || isnan(v)) return 0x00;
   float a = fabsf(v);
   int is_small = a < L;
   int is_large = a > H;
   if (is_small && !is_large) {
-    int32_t q = round_sat(v, (double)s / 4.0, -32, 31);
+    int32_t q = round_sat(v, (double)s / (double)ratio, -32, 31);
     return (uint8_t)(0x80 | (q & 0x3F));
   }
   if (is_large && !is_small) {
-    int32_t q = round_sat(v, (double)s * 4.0, -32, 31);
+    int32_t q = round_sat(v, (double)s * (double)ratio, -32, 31);
     return (uint8_t)(0xC0 | (q & 0x3F));
   }
   int32_t q = round_sat(v, (double)s, -64, 63);
@@ -111,31 +115,33 @@ EXPORT uint8_t orc_softedge_code(float v, float s, float L, float H) {
 }
 
 /* Value of a soft-edge byte in fp64 (exact: a small integer times a power-of-two multiple of s). */
-EXPORT double orc_softedge_value(uint8_t b, float s) {
-  if (!scale_valid((double)s)) return 0.0;
+EXPORT double orc_softedge_value(uint8_t b, float s, int32_t ratio) {
+  if (!ratio_ok(ratio) || !scale_valid((double)s)) return 0.0;
   if ((b & 0x80) == 0) {
     int32_t q = (b & 0x40) ? (int32_t)(b & 0x7F) - 128 : (int32_t)(b & 0x7F); /* sign-extend 7 bits */
     return (double)q * (double)s;
   }
   int32_t q = (b & 0x20) ? (int32_t)(b & 0x3F) - 64 : (int32_t)(b & 0x3F); /* sign-extend 6 bits */
-  if ((b & 0x40) == 0) return (double)q * ((double)s / 4.0);
-  return (double)q * ((double)s * 4.0);
+  if ((b & 0x40) == 0) return (double)q * ((double)s / (double)ratio);
+  return (double)q * ((double)s * (double)ratio);
 }
 
 /* The fp32 decode defined by the library contract: the fp64 value rounded once to fp32
  * (the product of a <= 7-bit integer and an fp32 scale is exact in fp64). */
-EXPORT float orc_softedge_decode_f32(uint8_t b, float s) { return (float)orc_softedge_value(b, s); }
+EXPORT float orc_softedge_decode_f32(uint8_t b, float s, int32_t ratio) {
+  return (float)orc_softedge_value(b, s, ratio);
+}
 
 EXPORT void orc_softedge_encode(const float* x, int64_t outer, int64_t C, int64_t inner,
                                 const int32_t* perm, const uint8_t* group_of, const float* s,
-                                const float* L, const float* H, uint8_t* code) {
+                                const float* L, const float* H, int32_t ratio, uint8_t* code) {
   for (int64_t o = 0; o < outer; ++o)
     for (int64_t c = 0; c < C; ++c) {
       int64_t src = perm ? perm[c] : c;
       int g = group_of[c];
       for (int64_t i = 0; i < inner; ++i)
         code[(o * C + c) * inner + i] =
-            orc_softedge_code(x[(o * C + src) * inner + i], s[g], L[g], H[g]);
+            orc_softedge_code(x[(o * C + src) * inner + i], s[g], L[g], H[g], ratio);
     }
 }
 

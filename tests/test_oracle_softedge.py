@@ -13,9 +13,9 @@ from tests.test_oracle_quant import rne_fraction
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def load_layout():
+def load_layout(name="softedge_layout.txt"):
     rows = []
-    for line in open(os.path.join(GOLDEN, "softedge_layout.txt")):
+    for line in open(os.path.join(GOLDEN, name)):
         line = line.strip()
         if not line or line.startswith("#"):
             continue
@@ -34,11 +34,15 @@ def load_thresholds():
     return d
 
 
+LAYOUTS = {4: "softedge_layout.txt", 2: "softedge_layout_shift.txt"}
+
+
+@pytest.mark.parametrize("ratio", [4, 2])
 @pytest.mark.parametrize("s", [np.float32(1.0), np.float32(0.0173), np.float32(2.0 ** -90)])
-def test_decode_table_matches_page_layout(s):
-    table = oracle.softedge_value_table(s)
+def test_decode_table_matches_page_layout(s, ratio):
+    table = oracle.softedge_value_table(s, ratio)
     covered = 0
-    for a, b, mode, lo, hi, mult in load_layout():
+    for a, b, mode, lo, hi, mult in load_layout(LAYOUTS[ratio]):
         assert b - a == hi - lo
         for k, byte in enumerate(range(a, b + 1)):
             want = Fraction(lo + k) * mult * Fraction(float(s))
@@ -47,16 +51,16 @@ def test_decode_table_matches_page_layout(s):
     assert covered == 256
 
 
-def exact_softedge(v, s, L, H):
+def exact_softedge(v, s, L, H, ratio=4):
     v, s, L, H = float(v), float(s), float(L), float(H)
     if not (2.0 ** -100 <= s <= 2.0 ** 100) or math.isnan(v):
         return 0
     a = abs(v)
     small, large = a < L, a > H
     if small and not large:
-        base, lo, hi, tag, mask = Fraction(s) / 4, -32, 31, 0x80, 0x3F
+        base, lo, hi, tag, mask = Fraction(s) / ratio, -32, 31, 0x80, 0x3F
     elif large and not small:
-        base, lo, hi, tag, mask = Fraction(s) * 4, -32, 31, 0xC0, 0x3F
+        base, lo, hi, tag, mask = Fraction(s) * ratio, -32, 31, 0xC0, 0x3F
     else:
         base, lo, hi, tag, mask = Fraction(s), -64, 63, 0x00, 0x7F
     if math.isinf(v):
@@ -66,11 +70,12 @@ def exact_softedge(v, s, L, H):
     return tag | (q & mask)
 
 
-def test_encode_matches_exact_brute_force():
+@pytest.mark.parametrize("ratio", [4, 2])
+def test_encode_matches_exact_brute_force(ratio):
     r = np.random.default_rng(21)
     s, L, H = np.float32(0.05), np.float32(0.2), np.float32(3.1)
     ties = []
-    for base, span in ((float(s) / 4, 34), (float(s), 66), (float(s) * 4, 34)):
+    for base, span in ((float(s) / ratio, 34), (float(s), 66), (float(s) * ratio, 34)):
         k = np.arange(-span, span) + 0.5
         t = (k * base).astype(np.float32)
         ties += [t, np.nextafter(t, np.float32(np.inf)), np.nextafter(t, np.float32(-np.inf))]
@@ -81,8 +86,9 @@ def test_encode_matches_exact_brute_force():
         np.array([L, -L, H, -H, np.nextafter(L, np.float32(0)), np.nextafter(H, np.float32(9)),
                   0.0, -0.0, np.inf, -np.inf, np.nan], dtype=np.float32),
     ]).astype(np.float32)
-    got = oracle.softedge_encode(v.reshape(1, 1, -1), np.zeros(1, np.uint8), [s], [L], [H]).ravel()
-    want = np.array([exact_softedge(a, s, L, H) for a in v], dtype=np.uint8)
+    got = oracle.softedge_encode(v.reshape(1, 1, -1), np.zeros(1, np.uint8), [s], [L], [H],
+                                 ratio=ratio).ravel()
+    want = np.array([exact_softedge(a, s, L, H, ratio) for a in v], dtype=np.uint8)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
 
@@ -152,3 +158,69 @@ def test_invalid_base_scale_encodes_zero():
         c = oracle.softedge_encode(v, np.zeros(1, np.uint8), [np.float32(s)], [np.float32(0.5)],
                                    [np.float32(5.0)])
         assert c.ravel().tolist() == [0, 0, 0]
+
+
+def test_shift_form_special_values():
+    """Section 4.1 form (scale/2, scale*2): worked by hand for s = 1, L = 0.5, H = 60."""
+    s, L, H = np.float32(1.0), np.float32(0.5), np.float32(60.0)
+    v = np.array([np.inf, -np.inf, 0.3, 0.25, 70.0, -70.0, 61.0, 30.0], dtype=np.float32)
+    c = oracle.softedge_encode(v.reshape(1, 1, -1), np.zeros(1, np.uint8), [s], [L], [H],
+                               ratio=2).ravel()
+    # +-Inf saturate in the large mode; 0.3 / 0.5 = 0.6 -> 1; 0.25 / 0.5 = 0.5 -> 0 (even);
+    # 70 / 2 = 35 -> 31 (saturated); -70 / 2 -> -32; 61 / 2 = 30.5 -> 30 (even); 30 standard
+    assert [hex(b) for b in c] == ["0xdf", "0xe0", "0x81", "0x80", "0xdf", "0xe0", "0xde", "0x1e"]
+    # the two forms differ only in the mode scales: standard bytes decode alike
+    t4 = oracle.softedge_value_table(np.float32(0.37), 4)
+    t2 = oracle.softedge_value_table(np.float32(0.37), 2)
+    assert np.array_equal(t4[:128], t2[:128])
+    assert np.array_equal(t4[0x80:0xC0] * 2, t2[0x80:0xC0])
+    assert np.array_equal(t4[0xC0:], t2[0xC0:] * 2)
+
+
+def brute_percentile(vals, pct):
+    """Linear-interpolation percentile by the textbook definition, with exact rationals: sorted
+    values a_0 <= ... <= a_{n-1}, position (n - 1) p / 100, interpolation between its neighbours."""
+    a = sorted(Fraction(abs(float(v))) for v in vals)
+    pos = Fraction(len(a) - 1) * Fraction(pct) / 100
+    k = int(pos)
+    if k >= len(a) - 1:
+        return a[-1]
+    return a[k] + (a[k + 1] - a[k]) * (pos - k)
+
+
+def test_track_groups_and_permutation_by_brute_force():
+    """softedge_track gathers each group's values through the permutation: against group-wise
+    exact-rational percentiles of hand-collected values on a tiny tensor. The tolerance is the fp64
+    rounding of the interpolation position (0.999 is not a binary fraction): about 1e-13 relative
+    here, far below the gap between neighbouring order statistics that a wrong rank would show."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((3, 6, 37)) * np.array([0.1, 5, 1, 30, 2, 0.5])[None, :, None])
+    x = x.astype(np.float32)
+    perm = np.array([3, 0, 5, 1, 4, 2], np.int32)
+    group_of = np.array([0, 1, 1, 2, 0, 2], np.uint8)
+    s, L, H, st = oracle.softedge_track(x, group_of, 3, perm=perm)
+    for g in range(3):
+        vals = [x[o, perm[c], i] for o in range(3) for c in range(6) if group_of[c] == g
+                for i in range(37)]
+        lw, hw = brute_percentile(vals, 5), brute_percentile(vals, Fraction(999, 10))
+        assert abs(st[g][0] - float(lw)) <= 1e-12 * float(lw)
+        assert abs(st[g][1] - float(hw)) <= 1e-12 * float(hw)
+        assert H[g] == np.float32(st[g][1]) and s[g] == np.float32(H[g] / np.float32(63))
+
+
+def test_track_ema_chain_and_empty_group():
+    """Three batches: the state follows L_t = 0.1 P5_t + 0.9 L_{t-1} from the first batch's own
+    percentiles; a group with no channels keeps its state."""
+    v = [np.arange(1001, dtype=np.float32) * k for k in (1, 2, 4)]
+    st = None
+    lw = hw = None
+    for k, vk in enumerate(v):
+        s, L, H, st = oracle.softedge_track(vk.reshape(1, 1, -1), np.zeros(1, np.uint8), 2,
+                                            prev=st)
+        p5, p999 = 50.0 * (1, 2, 4)[k], 999.0 * (1, 2, 4)[k]
+        lw = p5 if lw is None else 0.1 * p5 + 0.9 * lw
+        hw = p999 if hw is None else 0.1 * p999 + 0.9 * hw
+        # the fp64 position of P99.9 carries one rounding (0.999 is not a binary fraction)
+        assert st[0][0] == lw and abs(st[0][1] - hw) <= 1e-13 * hw
+        assert (L[0], H[0]) == (np.float32(lw), np.float32(hw))
+        assert (L[1], H[1], s[1]) == (0, 0, 1) and st[1] == (0.0, 0.0)
