@@ -103,10 +103,13 @@ class Mamba1(Workload):
     # and readout)
     ops_per_update = 5
 
-    def __init__(self, soft_edge=False, y_int8=False):
+    def __init__(self, soft_edge=False, y_int8=False, ratio=4, bc_soft_edge=False):
         self.soft = soft_edge
         self.y_int8 = y_int8
+        self.ratio = ratio
+        self.bc_soft = bc_soft_edge
         self.name = ("mamba1-130m-layer-w8a8" + ("-softedge-x" if soft_edge else "") +
+                     ("-shift" if ratio == 2 else "") + ("-softedge-bc" if bc_soft_edge else "") +
                      ("-int8-y" if y_int8 else ""))
         self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
         self.bound = "alu"
@@ -116,7 +119,9 @@ class Mamba1(Workload):
         import quantized_state_space_amd as qs
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.c3_inputs()
-        xc = qs.QSSM_X_SOFTEDGE if self.soft else qs.QSSM_X_INT8
+        form = qs.QSSM_X_SOFTEDGE2 if self.ratio == 2 else qs.QSSM_X_SOFTEDGE
+        xc = form if self.soft else qs.QSSM_X_INT8
+        bc = form if self.bc_soft else qs.QSSM_X_INT8
         y_out = None
         if self.y_int8:
             # int8 output for the next W8A8 module: 8 clustered output groups calibrated on one
@@ -134,13 +139,17 @@ class Mamba1(Workload):
         self.y_out = y_out
         # two copies of every buffer, used in turn, so that one step's 350 MB of traffic cannot be
         # served from the previous step's lines in the 256 MB last-level cache
-        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc, y_out=y_out)
+        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc, y_out=y_out, bc_code=bc)
                        for _ in range(2)]
         self.k = 0
         B, D, L, N, Gbc = self.layers[0].shape
         self.dims = (B, D, L, N, Gbc)
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
-                       "x_groups": 8, "x_code": "soft-edge 3-scale u8" if self.soft else "int8",
+                       "x_groups": 8,
+                       "x_code": (f"soft-edge 3-scale u8, ratio {self.ratio}" if self.soft
+                                  else "int8"),
+                       "bc_code": (f"soft-edge 3-scale u8, ratio {self.ratio}" if self.bc_soft
+                                   else "int8"),
                        "bc_state_groups": N // 4, "state": "f32",
                        "y": "int8, 8 output groups + per-channel correction" if self.y_int8
                        else "f32"}
@@ -175,14 +184,16 @@ class Mamba1(Workload):
     def oracle_ref(self):
         import oracle.pipelines as op
         if not hasattr(self, "_cal"):
-            self._cal = op.mamba1_calib(self.inp, 8, 4, soft_edge=self.soft)
-        return op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=self._cal)
+            self._cal = op.mamba1_calib(self.inp, 8, 4, soft_edge=self.soft,
+                                        bc_soft_edge=self.bc_soft)
+        return op.mamba1(self.inp, G=8, gs=4, soft_edge=self.soft, calib=self._cal,
+                         se_ratio=self.ratio, bc_soft_edge=self.ratio if self.bc_soft else 0)
 
     def check(self, ref):
         lay = self.layers[0]  # ran the first step
         n = codes_equal(lay.xq.cpu().numpy(), ref["xq"], "x codes")
-        n += codes_equal(lay.Bq.cpu().numpy(), ref["Bq"], "B codes")
-        n += codes_equal(lay.Cq.cpu().numpy(), ref["Cq"], "C codes")
+        n += codes_equal(lay.Bq.cpu().numpy().view(np.uint8), ref["Bq"].view(np.uint8), "B codes")
+        n += codes_equal(lay.Cq.cpu().numpy().view(np.uint8), ref["Cq"].view(np.uint8), "C codes")
         out = {"codes_bit_exact": n}
         out["h_last_row_error"] = rows_close(lay.h_last.cpu().numpy(), ref["h_last"], self.tol,
                                              "h_last")
@@ -365,8 +376,8 @@ class Ssd(Workload):
     def check(self, ref):
         lay = self.lay
         n = codes_equal(lay.xq.cpu().numpy(), ref["xq"], "x codes")
-        n += codes_equal(lay.Bq.cpu().numpy(), ref["Bq"], "B codes")
-        n += codes_equal(lay.Cq.cpu().numpy(), ref["Cq"], "C codes")
+        n += codes_equal(lay.Bq.cpu().numpy().view(np.uint8), ref["Bq"].view(np.uint8), "B codes")
+        n += codes_equal(lay.Cq.cpu().numpy().view(np.uint8), ref["Cq"].view(np.uint8), "C codes")
         import torch
         hsel = torch.as_tensor(self.heads, device=lay.y.device)
         rows = lambda a: np.asarray(a, np.float64).transpose(0, 2, 3, 1).reshape(-1, a.shape[1])
@@ -574,10 +585,11 @@ def _zero(device):
 WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
              "c4i8y": lambda: Ssd(False, True), "c3": lambda: Mamba1(False),
              "c3se": lambda: Mamba1(True), "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
+             "c3se2bc": lambda: Mamba1(True, ratio=2, bc_soft_edge=True),
              "c2": lambda: S4d(False), "c2i16": lambda: S4d(True), "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True), "w4a8d": lambda: W4A8(256), "w4a8p": lambda: W4A8(16384)}
-OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3i8y", "c4f16", "c4i8y", "c5", "c5f16", "w4a8d",
-          "w4a8p")
+OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3se2bc", "c3i8y", "c4f16", "c4i8y", "c5", "c5f16",
+          "w4a8d", "w4a8p")
 INT8_MFMA_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 
 
@@ -599,6 +611,7 @@ TRAFFIC = {
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
+    "c3se2bc": ["scan_m1.hip"],
     "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"], "c2i16": ["s4d.hip"],
     "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c4i8y": ["ssd.hip"], "c5": ["state_update.hip"],
     "c5f16": ["state_update.hip"],
@@ -757,24 +770,47 @@ def quantizer_row(torch, dev, reps=20):
     import quantized_state_space_amd.workloads as wl
     inp = synth.c3_inputs()
     lay = wl.Mamba1Layer(inp, 8, 4, dev)
-    s, Lt, Ht = wl.calib_softedge(inp["x_cal"], lay.perm, lay.group_of, 8)
+    s, Lt, Ht, st0 = wl.calib_softedge(inp["x_cal"], lay.perm, lay.group_of, 8, with_state=True)
     st, Lt_t, Ht_t = (torch.from_numpy(a).to(dev) for a in (s, Lt, Ht))
     code = torch.empty(lay.xq.shape, dtype=torch.uint8, device=dev)
+    code2 = torch.empty(lay.xq.shape, dtype=torch.uint8, device=dev)
+    # threshold tracking into its own buffers, from the calibration state every call
+    ema0 = torch.from_numpy(st0).to(dev)
+    ema = ema0.clone()
+    ts_, tL, tH = (torch.empty(8, dtype=torch.float32, device=dev) for _ in range(3))
+    tws = torch.empty(qs.qssm_softedge_track_workspace_size(8), dtype=torch.uint8, device=dev)
+
+    def track():
+        ema.copy_(ema0)
+        qs.qssm_softedge_track(lay.x, lay.group_t, 8, ema, ts_, tL, tH, tws, ema_valid=True,
+                               perm=lay.perm_t)
+
     calls = {"int8": lambda: qs.qssm_quant_group_x(lay.x, lay.group_t, 8, lay.xs, lay.xq,
                                                    perm=lay.perm_t),
              "softedge": lambda: qs.qssm_softedge_encode(lay.x, lay.group_t, 8, st, Lt_t, Ht_t,
-                                                         code, perm=lay.perm_t)}
+                                                         code, perm=lay.perm_t),
+             "softedge_shift": lambda: qs.qssm_softedge_encode(
+                 lay.x, lay.group_t, 8, st, Lt_t, Ht_t, code2, perm=lay.perm_t,
+                 form=qs.QSSM_X_SOFTEDGE2),
+             "track": track}
     for f in calls.values():
         f()
     torch.cuda.synchronize()
     # parity: the codes of both encoders against the oracle's (with its own calibration), bit for bit
     import oracle.pipelines as op
     perm, group_of, xs = op.calib_x(inp["x_cal"], 8)
-    se = op.calib_softedge(inp["x_cal"], perm, group_of, 8)
+    se, se_state = op.calib_softedge(inp["x_cal"], perm, group_of, 8, with_state=True)
     want8 = oracle.quant_group_x(inp["x"], group_of, xs, perm=perm)
     codes_equal(lay.xq.cpu().numpy(), want8, "int8 x codes")
     wantse = oracle.softedge_encode(inp["x"], group_of, se[0], se[1], se[2], perm=perm)
     codes_equal(code.cpu().numpy(), wantse, "soft-edge x codes")
+    wantse2 = oracle.softedge_encode(inp["x"], group_of, se[0], se[1], se[2], perm=perm, ratio=2)
+    codes_equal(code2.cpu().numpy(), wantse2, "shift-form soft-edge x codes")
+    ws_, wL, wH, wst = oracle.softedge_track(inp["x"], group_of, 8, perm=perm, prev=se_state)
+    require(np.array_equal(ts_.cpu().numpy(), ws_) and np.array_equal(tL.cpu().numpy(), wL)
+            and np.array_equal(tH.cpu().numpy(), wH)
+            and np.array_equal(ema.cpu().numpy(), np.array(wst)),
+            "tracked thresholds differ from the oracle's")
     stream = torch.cuda.current_stream()
     out = {}
     n = inp["x"].size
@@ -792,8 +828,12 @@ def quantizer_row(torch, dev, reps=20):
         out[k] = {"us_median": round(float(np.median(ts)), 2), "us_min": round(float(ts.min()), 2),
                   "GB_s": round(5 * n / (np.median(ts) * 1e-6) / 1e9, 1)}
     out["softedge_over_int8"] = round(out["softedge"]["us_median"] / out["int8"]["us_median"], 3)
+    out["track"]["GB_s"] = round(4 * 4 * n / (out["track"]["us_median"] * 1e-6) / 1e9, 1)
     out["workload"] = "mamba1-130m x: 8 x 1536 x 2048 fp32 -> codes, cluster gather, 8 groups"
-    out["parity"] = "codes of both encoders bit-exact against the oracle"
+    out["parity"] = ("codes of the three encoders bit-exact against the oracle; tracked "
+                     "thresholds and EMA state equal to the oracle's")
+    out["note"] = ("GB_s counts 5 bytes per value for the encoders and 4 reads of x for the "
+                   "tracker (plus a state copy of 128 bytes)")
     return out
 
 

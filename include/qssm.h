@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 140 /* 1.4.0: W4A8 linear layer */
+#define QSSM_VERSION 150 /* 1.5.0: soft-edge ratio 2, soft-edge B/C, device threshold tracking */
 
 typedef int32_t qssm_status;
 enum {
@@ -69,7 +69,8 @@ enum { QSSM_F32 = 0, QSSM_F16 = 1, QSSM_I16 = 2, QSSM_I8 = 3 };
 /* Encodings of the scan input x. */
 enum {
   QSSM_X_INT8 = 0,    /* int8 code, value = s[g] * q */
-  QSSM_X_SOFTEDGE = 1 /* three-scale soft-edge byte, see qssm_softedge_encode */
+  QSSM_X_SOFTEDGE = 1, /* three-scale soft-edge byte, mode ratio 4, see qssm_softedge_encode */
+  QSSM_X_SOFTEDGE2 = 2 /* the same byte with the shift-only mode ratio 2 */
 };
 
 /* ---------------------------------------------------------------------------------------------
@@ -109,25 +110,57 @@ qssm_status qssm_quant_state_group_BC(const float* bc, int64_t outer, int32_t Gb
 /* ---------------------------------------------------------------------------------------------
  * a3. Soft-edge three-scale 8-bit code. Quamba-SE blog, section 2.1 (three modes: scale/4 for
  * |v| < L, scale for the middle, scale*4 for |v| > H), section 2.2 (classifier and byte layout:
- * 0xxxxxxx standard, 10xxxxxx small, 11xxxxxx large), section 4.1 (thresholds).
+ * 0xxxxxxx standard, 10xxxxxx small, 11xxxxxx large), section 4.1 (thresholds; on small hardware
+ * scale/2 and scale*2, one shift instead of a multiplier).
  *
- * Per group g with base scale s = s[g] and thresholds L = L[g], H = H[g]:
- *   small    (|v| < L and not |v| > H): q = clamp(RNE(v / (s/4)), -32, 31), byte = 0x80 | (q & 0x3F)
- *   large    (|v| > H and not |v| < L): q = clamp(RNE(v / (s*4)), -32, 31), byte = 0xC0 | (q & 0x3F)
+ * form selects the mode ratio m: QSSM_X_SOFTEDGE (m = 4) or QSSM_X_SOFTEDGE2 (m = 2); nothing
+ * else depends on it. Per group g with base scale s = s[g] and thresholds L = L[g], H = H[g]:
+ *   small    (|v| < L and not |v| > H): q = clamp(RNE(v / (s/m)), -32, 31), byte = 0x80 | (q & 0x3F)
+ *   large    (|v| > H and not |v| < L): q = clamp(RNE(v / (s*m)), -32, 31), byte = 0xC0 | (q & 0x3F)
  *   standard (otherwise):               q = clamp(RNE(v / s),     -64, 63), byte = q & 0x7F
  * NaN encodes as 0x00; +-Inf fall in the large mode and saturate (0xDF / 0xE0). A group whose
  * base scale is not valid (see above) encodes every value as 0x00.
  * x / out: fp32 [outer, C, inner]; code: uint8 [outer, C, inner]; perm and group_of as in a1.
- * Decode: 0xxxxxxx -> sext7 * s, 10xxxxxx -> sext6 * (s/4), 11xxxxxx -> sext6 * (s*4), each one
+ * Decode: 0xxxxxxx -> sext7 * s, 10xxxxxx -> sext6 * (s/m), 11xxxxxx -> sext6 * (s*m), each one
  * fp32 multiply (correctly rounded). A group with an invalid scale decodes to 0.
  */
 qssm_status qssm_softedge_encode(const float* x, int64_t outer, int64_t C, int64_t inner,
                                  const int32_t* perm, const uint8_t* group_of, int32_t G,
-                                 const float* s, const float* L, const float* H, uint8_t* code,
-                                 hipStream_t stream);
+                                 const float* s, const float* L, const float* H, int32_t form,
+                                 uint8_t* code, hipStream_t stream);
 qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, int64_t inner,
-                                 const uint8_t* group_of, int32_t G, const float* s, float* out,
-                                 hipStream_t stream);
+                                 const uint8_t* group_of, int32_t G, const float* s, int32_t form,
+                                 float* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * f3. On-device soft-edge threshold tracking. Quamba-SE blog, section 4.1: L at the 5th and H at
+ * the 99.9th percentile of the activations, followed over mini-batches by an exponential moving
+ * average with factor alpha (0.1 there).
+ *
+ * For each group g, over the values of x [outer, C, inner] (device fp32) whose output channel c
+ * (reading input channel perm[c]; perm NULL = identity) has group_of[c] == g:
+ *   L_new = P5(|v|), H_new = P99.9(|v|), linear interpolation between order statistics:
+ *     vi = (n - 1)*q with q = p/100 (fp64), k = floor(vi), t = vi - k,
+ *     P = a + (b - a)*t if t < 1/2 else b - (b - a)*(1 - t), a, b = the k-th and (k+1)-th smallest
+ *     (P = the largest when vi >= n - 1), every step rounded in fp64 as written;
+ *   ema_valid != 0: L = alpha*L_new + (1 - alpha)*L_prev (same for H), else L = L_new;
+ *   ema_state[2g], ema_state[2g+1] (device fp64, in/out): the previous and then the new (L, H);
+ *   L[g], H[g] = fl32 of them; s[g] = fl32(H[g] / 63) (1 when H[g] is 0): the arguments
+ *   qssm_softedge_encode reads, so an encode queued after this call uses the updated thresholds.
+ * These are the numbers qssm_calib_softedge computes on the host from the same values.
+ * A group with no values keeps its ema_state (0, 0 when ema_valid == 0) and gets L, H, s from it.
+ * Values must be finite; a NaN or Inf yields unspecified thresholds (no fault).
+ * 1 <= G <= 32; 0 <= alpha <= 1. Group indices >= G count as the last group.
+ * Workspace: qssm_softedge_track_workspace_size(G) bytes of device memory (histograms and
+ * selection state; the call clears what it uses). No synchronization: four counting passes over x
+ * and five small selection kernels on the stream.
+ */
+size_t qssm_softedge_track_workspace_size(int32_t G);
+qssm_status qssm_softedge_track(const float* x, int64_t outer, int64_t C, int64_t inner,
+                                const int32_t* perm, const uint8_t* group_of, int32_t G,
+                                double alpha, int32_t ema_valid, double* ema_state, float* s,
+                                float* L, float* H, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * a4-a7. Mamba1 selective scan with int8 (or soft-edge) x and int8 B, C (W8A8 recurrence).
@@ -149,11 +182,16 @@ qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, 
  * is the fp32 value the QSSM_F32 output would hold. y_bias (NULL = no correction) is the
  * calibrated correction term, e.g. from qssm_calib_channel_error_mean. The y_* fields are read
  * only for QSSM_I8.
+ * bc_code selects how Bq and Cq are coded: QSSM_X_INT8 (int8 codes, value = scale * q) or a
+ * soft-edge form (QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2: the bytes of qssm_softedge_encode, with
+ * B_scales / C_scales as the state groups' base scales; the code of the Quamba-SE blog, sections
+ * 2.1-2.2, applied to the input-dependent B and C as well as to x). Bq and Cq then hold those
+ * bytes; their thresholds only matter to the encoder.
  * Workspace: qssm_scan_workspace_size bytes (dequantized B and C staging).
  */
 typedef struct qssm_scan_args {
   int64_t batch, seqlen, dim, dstate; /* B, L, D, N */
-  int32_t x_code;                     /* QSSM_X_INT8 or QSSM_X_SOFTEDGE */
+  int32_t x_code;                     /* QSSM_X_INT8, QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2 */
   int32_t x_groups;                   /* G, 1..256 */
   const void* x;                      /* int8 or soft-edge uint8 codes [B, D, L] */
   const uint8_t* x_group_of;          /* [D] group of each channel */
@@ -175,6 +213,7 @@ typedef struct qssm_scan_args {
   const uint8_t* y_group_of;          /* QSSM_I8: [D] output group (< y_groups) of each channel */
   const float* y_scales;              /* QSSM_I8: [Gy] static output scales */
   const float* y_bias;                /* QSSM_I8: [D] correction added before quantizing, or NULL */
+  int32_t bc_code;                    /* QSSM_X_INT8, QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2 */
 } qssm_scan_args;
 
 size_t qssm_scan_workspace_size(const qssm_scan_args* a);

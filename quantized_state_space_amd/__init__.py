@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libqssm.so")
 
 QSSM_OK, QSSM_ERR_INVALID_ARG, QSSM_ERR_UNSUPPORTED, QSSM_ERR_WORKSPACE, QSSM_ERR_DEVICE = range(5)
 QSSM_F32, QSSM_F16, QSSM_I16, QSSM_I8 = 0, 1, 2, 3
-QSSM_X_INT8, QSSM_X_SOFTEDGE = 0, 1
+QSSM_X_INT8, QSSM_X_SOFTEDGE, QSSM_X_SOFTEDGE2 = 0, 1, 2
 QSSM_MMA_F16, QSSM_MMA_I8 = 0, 1
 
 _P = ctypes.c_void_p
@@ -35,7 +35,8 @@ class ScanArgs(ctypes.Structure):
                 ("x_scales", _P), ("delta", _P), ("A", _P), ("bc_groups", _I32),
                 ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P), ("C_scales", _P),
                 ("Dskip", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
-                ("y_groups", _I32), ("y_group_of", _P), ("y_scales", _P), ("y_bias", _P)]
+                ("y_groups", _I32), ("y_group_of", _P), ("y_scales", _P), ("y_bias", _P),
+                ("bc_code", _I32)]
 
 
 class S4dArgs(ctypes.Structure):
@@ -78,8 +79,11 @@ ARG_STRUCTS = {0: ScanArgs, 1: S4dArgs, 2: SsdArgs, 3: UpdateArgs, 4: GemmArgs}
 SIGNATURES = {
     "qssm_quant_group_x": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I32, _P, _P]),
     "qssm_quant_state_group_BC": (_I32, [_P, _I64, _I32, _I32, _I64, _I32, _P, _I32, _P, _P]),
-    "qssm_softedge_encode": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _P, _P]),
-    "qssm_softedge_decode": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P]),
+    "qssm_softedge_encode": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _I32, _P, _P]),
+    "qssm_softedge_decode": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P]),
+    "qssm_softedge_track_workspace_size": (ctypes.c_size_t, [_I32]),
+    "qssm_softedge_track": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, ctypes.c_double, _I32, _P,
+                                   _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "qssm_scan_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScanArgs)]),
     "qssm_scan_w8a8": (_I32, [ctypes.POINTER(ScanArgs), _P, ctypes.c_size_t, _P]),
     "qssm_scan_w8a8_noalloc": (_I32, [ctypes.POINTER(ScanArgs), _P]),
@@ -183,24 +187,48 @@ def qssm_quant_state_group_BC(bc, gs, scales, q, compute_scales=False, stream=No
     return q
 
 
-def qssm_softedge_encode(x, group_of, G, s, L, H, code, perm=None, stream=None):
+def qssm_softedge_encode(x, group_of, G, s, L, H, code, perm=None, form=QSSM_X_SOFTEDGE,
+                         stream=None):
     torch = _t()
     outer, C, inner = x.shape
     _check("qssm_softedge_encode", load().qssm_softedge_encode(
         _ptr(x, torch.float32, "x"), outer, C, inner, _ptr(perm, torch.int32, "perm", True),
         _ptr(group_of, torch.uint8, "group_of"), G, _ptr(s, torch.float32, "s"),
-        _ptr(L, torch.float32, "L"), _ptr(H, torch.float32, "H"), _ptr(code, torch.uint8, "code"),
-        _stream(stream)))
+        _ptr(L, torch.float32, "L"), _ptr(H, torch.float32, "H"), int(form),
+        _ptr(code, torch.uint8, "code"), _stream(stream)))
     return code
 
 
-def qssm_softedge_decode(code, group_of, G, s, out, stream=None):
+def qssm_softedge_decode(code, group_of, G, s, out, form=QSSM_X_SOFTEDGE, stream=None):
     torch = _t()
     outer, C, inner = code.shape
     _check("qssm_softedge_decode", load().qssm_softedge_decode(
         _ptr(code, torch.uint8, "code"), outer, C, inner, _ptr(group_of, torch.uint8, "group_of"),
-        G, _ptr(s, torch.float32, "s"), _ptr(out, torch.float32, "out"), _stream(stream)))
+        G, _ptr(s, torch.float32, "s"), int(form), _ptr(out, torch.float32, "out"),
+        _stream(stream)))
     return out
+
+
+def qssm_softedge_track_workspace_size(G):
+    return load().qssm_softedge_track_workspace_size(int(G))
+
+
+def qssm_softedge_track(x, group_of, G, ema_state, s, L, H, workspace, ema_valid, perm=None,
+                        alpha=0.1, stream=None):
+    """Per-group P5 / P99.9 thresholds of x [outer, C, inner] on the device, EMA-blended with
+    ema_state (float64 [G, 2], updated in place) when ema_valid; writes s, L, H (float32 [G])."""
+    torch = _t()
+    outer, C, inner = x.shape
+    if group_of.numel() != C:
+        raise ValueError("group_of must have one entry per channel")
+    if ema_state.numel() != 2 * G or s.numel() != G or L.numel() != G or H.numel() != G:
+        raise ValueError("ema_state must hold 2 G values and s, L, H G values each")
+    _check("qssm_softedge_track", load().qssm_softedge_track(
+        _ptr(x, torch.float32, "x"), outer, C, inner, _ptr(perm, torch.int32, "perm", True),
+        _ptr(group_of, torch.uint8, "group_of"), int(G), float(alpha), int(bool(ema_valid)),
+        _ptr(ema_state, torch.float64, "ema_state"), _ptr(s, torch.float32, "s"),
+        _ptr(L, torch.float32, "L"), _ptr(H, torch.float32, "H"),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------------------------
@@ -216,14 +244,17 @@ def _fill(st, keep=(), **kw):
 
 
 def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, y,
-              Dskip=None, h0=None, h_last=None, y_group_of=None, y_scales=None, y_bias=None):
-    """Builds ScanArgs for x [B, D, L] codes, Bq/Cq [B, Gbc, N, L]. An int8 y takes the output
-    group map, scales and (optional) correction bias."""
+              Dskip=None, h0=None, h_last=None, y_group_of=None, y_scales=None, y_bias=None,
+              bc_code=QSSM_X_INT8):
+    """Builds ScanArgs for x [B, D, L] codes, Bq/Cq [B, Gbc, N, L] (int8, or uint8 soft-edge bytes
+    when bc_code is a soft-edge form). An int8 y takes the output group map, scales and
+    (optional) correction bias."""
     torch = _t()
     B, D, L = x.shape
     N = A.shape[1]
     Gbc = Bq.shape[1]
     xdt = torch.int8 if x_code == QSSM_X_INT8 else torch.uint8
+    bdt = torch.int8 if bc_code == QSSM_X_INT8 else torch.uint8
     ydt = {torch.float32: QSSM_F32, torch.float16: QSSM_F16, torch.int8: QSSM_I8}.get(y.dtype, -1)
     yq = ydt == QSSM_I8
     if yq:
@@ -244,8 +275,8 @@ def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_sca
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"),
                  delta=_ptr(delta, torch.float32, "delta"), A=_ptr(A, torch.float32, "A"),
-                 bc_groups=Gbc, bc_group_size=gs, Bq=_ptr(Bq, torch.int8, "Bq"),
-                 Cq=_ptr(Cq, torch.int8, "Cq"), B_scales=_ptr(B_scales, torch.float32, "B_scales"),
+                 bc_groups=Gbc, bc_group_size=gs, bc_code=int(bc_code), Bq=_ptr(Bq, bdt, "Bq"),
+                 Cq=_ptr(Cq, bdt, "Cq"), B_scales=_ptr(B_scales, torch.float32, "B_scales"),
                  C_scales=_ptr(C_scales, torch.float32, "C_scales"),
                  Dskip=_ptr(Dskip, torch.float32, "Dskip", True),
                  h0=_ptr(h0, torch.float32, "h0", True), y=_ptr(y, None, "y"), y_dtype=ydt,

@@ -26,11 +26,11 @@ float calib_scale(float absmax) {
 }
 
 // Percentile with linear interpolation between order statistics (the "linear" rule:
-// virtual index (n-1) q, written as n q + (1 - q) - 1), on ascending values.
+// virtual index (n-1) q), on ascending values.
 double percentile_linear(const std::vector<double>& sorted, double pct) {
   const int64_t n = (int64_t)sorted.size();
   const double q = pct / 100.0;
-  const double vi = (double)n * q + (1.0 + q * -1.0) - 1.0;
+  const double vi = (double)(n - 1) * q;
   if (vi >= (double)(n - 1)) return sorted[n - 1];
   if (vi < 0.0) return sorted[0];
   const double lo = std::floor(vi);

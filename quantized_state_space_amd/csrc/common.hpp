@@ -82,27 +82,19 @@ __host__ __device__ __forceinline__ int8_t quant8_r(float v, float s, float r) {
   return (r != 0.0f) ? (int8_t)rne_sat_recip(v, s, r, -128, 127) : (int8_t)0;
 }
 
-// Soft-edge byte (Quamba-SE blog, 2.1 and 2.2): strict |v| < L selects scale/4 with a 6-bit
-// payload (tag 10), |v| > H selects scale*4 (tag 11), anything else (including both tests true)
-// the base scale with a 7-bit payload (tag 0). Payloads are two's complement.
-__host__ __device__ __forceinline__ uint8_t softedge_code(float v, float s, float L, float H) {
-  if (!scale_ok(s) || v != v) return 0;
-  float a = fabsf(v);
-  bool small = a < L, large = a > H;
-  if (small && !large) return (uint8_t)(0x80 | (rne_sat(v, s * 0.25f, -32.0f, 31.0f) & 0x3F));
-  if (large && !small) return (uint8_t)(0xC0 | (rne_sat(v, s * 4.0f, -32.0f, 31.0f) & 0x3F));
-  return (uint8_t)(rne_sat(v, s, -64.0f, 63.0f) & 0x7F);
-}
-
-// softedge_code from a reciprocal (r = recip_or_zero(s)): the small and large modes scale s and r
-// by exact powers of two.
-__host__ __device__ __forceinline__ uint8_t softedge_code_r(float v, float s, float r, float L, float H) {
+// Soft-edge byte (Quamba-SE blog, 2.1 and 2.2): strict |v| < L selects scale/m with a 6-bit
+// payload (tag 10), |v| > H selects scale*m (tag 11), anything else (including both tests true)
+// the base scale with a 7-bit payload (tag 0). Payloads are two's complement. The mode ratio m is 4
+// (sections 2.1-2.2) or 2 (the shift-only form of section 4.1); im = 1/m. r = recip_or_zero(s):
+// the small and large modes scale s and r by exact powers of two.
+__host__ __device__ __forceinline__ uint8_t softedge_code_r(float v, float s, float r, float L, float H,
+                                                            float m, float im) {
   if (r == 0.0f) return 0;
   const float a = fabsf(v);
   const bool small = a < L, large = a > H;
   const bool sm = small && !large, lg = large && !small;
-  const float ss = sm ? 0.25f * s : (lg ? 4.0f * s : s);
-  const float rr = sm ? 4.0f * r : (lg ? 0.25f * r : r);
+  const float ss = sm ? im * s : (lg ? m * s : s);
+  const float rr = sm ? m * r : (lg ? im * r : r);
   const int lim = (sm || lg) ? 32 : 64;
   const int q = rne_sat_recip(v, ss, rr, -lim, lim - 1);
   const uint32_t code = sm ? (0x80u | ((uint32_t)q & 0x3Fu))
@@ -110,15 +102,25 @@ __host__ __device__ __forceinline__ uint8_t softedge_code_r(float v, float s, fl
   return (uint8_t)code;  // NaN: neither small nor large, payload 0
 }
 
-// Value of a soft-edge byte as one correctly rounded fp32 product (0 for an invalid scale).
-__host__ __device__ __forceinline__ float softedge_value(uint32_t b, float s) {
+// Value of a soft-edge byte in units of the base scale: the payload times 1, 1/m or m (exact).
+__host__ __device__ __forceinline__ float softedge_unit(uint32_t b, float m, float im) {
+  if ((b & 0x80u) == 0) return (float)((b & 0x40u) ? (int)(b & 0x7Fu) - 128 : (int)(b & 0x7Fu));
+  const int q = (b & 0x20u) ? (int)(b & 0x3Fu) - 64 : (int)(b & 0x3Fu);
+  return (float)q * ((b & 0x40u) ? m : im);
+}
+
+// Value of a soft-edge byte as one correctly rounded fp32 product (0 for an invalid scale):
+// the exact unit times s (m * s and im * s are exact for a valid s, so unit * s rounds once).
+__host__ __device__ __forceinline__ float softedge_value(uint32_t b, float s, float m, float im) {
   if (!scale_ok(s)) return 0.0f;
-  if ((b & 0x80u) == 0) {
-    int q = (b & 0x40u) ? (int)(b & 0x7Fu) - 128 : (int)(b & 0x7Fu);
-    return (float)q * s;
-  }
-  int q = (b & 0x20u) ? (int)(b & 0x3Fu) - 64 : (int)(b & 0x3Fu);
-  return (float)q * ((b & 0x40u) ? s * 4.0f : s * 0.25f);
+  if ((b & 0x80u) == 0) return softedge_unit(b, m, im) * s;
+  const int q = (b & 0x20u) ? (int)(b & 0x3Fu) - 64 : (int)(b & 0x3Fu);
+  return (float)q * ((b & 0x40u) ? s * m : s * im);
+}
+
+// Mode ratio of a soft-edge code type (QSSM_X_SOFTEDGE: 4, QSSM_X_SOFTEDGE2: 2).
+__host__ __device__ __forceinline__ float softedge_ratio(int code_type) {
+  return code_type == QSSM_X_SOFTEDGE2 ? 2.0f : 4.0f;
 }
 
 // Scale from a group absmax (device side of compute_scales): fl32(absmax / 127), 0 -> 1,

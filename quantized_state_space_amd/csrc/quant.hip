@@ -47,6 +47,7 @@ struct Geometry {
   // kStride = kThreads * 4 elements apart (set on the host): stride % inner, (stride / inner) % C,
   // stride / inner / C.
   int64_t step_i, step_c, step_o;
+  float se_m = 4.0f, se_im = 0.25f;  // soft-edge mode ratio and its reciprocal (exact)
 };
 
 constexpr int64_t kStride = (int64_t)kThreads * 4;
@@ -99,9 +100,9 @@ __device__ __forceinline__ void load_chunk(const Geometry& g, const float* __res
 }
 
 template <int OP>
-__device__ __forceinline__ uint32_t encode(float v, float2 sr, float2 lh) {
+__device__ __forceinline__ uint32_t encode(float v, float2 sr, float2 lh, float m, float im) {
   if (OP == OP_QUANT) return (uint32_t)(uint8_t)quant8_r(v, sr.x, sr.y);
-  return softedge_code_r(v, sr.x, sr.y, lh.x, lh.y);
+  return softedge_code_r(v, sr.x, sr.y, lh.x, lh.y, m, im);
 }
 
 // Four int8 codes (quant8_r of each value, packed little-endian) with one wave-level branch for
@@ -140,6 +141,52 @@ __device__ __forceinline__ uint32_t quant4(f32x4 v, const float (&s)[4], const f
   const uint32_t lo = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
   const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x0c0c0400u);
   return lo | (hi << 16);
+}
+
+// Four soft-edge bytes (softedge_code_r of each value, packed little-endian), with the mode
+// classification done first and then the arithmetic of quant4 on the mode's scale and reciprocal
+// (exact power-of-two multiples of s and r): one wave-level branch for the rare near-boundary
+// correction instead of one per value.
+__device__ __forceinline__ uint32_t softedge4(f32x4 v, const float (&s)[4], const float (&r)[4],
+                                              const float (&Lt)[4], const float (&Ht)[4], float m,
+                                              float im) {
+  float ss[4], f[4], c[4], hi[4];
+  uint32_t tag[4];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = fabsf(v[i]);
+    const bool small = a < Lt[i], large = a > Ht[i];
+    const bool sm = small && !large, lg = large && !small;
+    ss[i] = sm ? im * s[i] : (lg ? m * s[i] : s[i]);
+    const float rr = sm ? m * r[i] : (lg ? im * r[i] : r[i]);
+    tag[i] = sm ? 0x80u : (lg ? 0xC0u : 0u);
+    hi[i] = (sm || lg) ? 31.0f : 63.0f;
+    f[i] = __builtin_amdgcn_fmed3f(v[i] * rr, -256.0f, 256.0f);
+    c[i] = rintf(f[i]);
+    any |= fabsf(f[i] - c[i]) > 0.5f - 0x1p-14f;
+  }
+  if (any) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t = f[i] - c[i];
+      if (fabsf(t) > 0.5f - 0x1p-14f) {
+        const float h = copysignf(0.5f, t);
+        const float e = fmaf(-(c[i] + h), ss[i], v[i]);
+        const float eh = (h > 0.0f) ? e : -e;
+        const bool odd = (c[i] * 0.5f) != rintf(c[i] * 0.5f);
+        if (eh > 0.0f || (eh == 0.0f && odd)) c[i] += h + h;
+      }
+    }
+  }
+  uint32_t word = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (int)__builtin_amdgcn_fmed3f(c[i], -hi[i] - 1.0f, hi[i]);
+    const uint32_t b = tag[i] | ((uint32_t)q & (tag[i] ? 0x3Fu : 0x7Fu));
+    word |= ((r[i] != 0.0f && v[i] == v[i]) ? b : 0u) << (8 * i);
+  }
+  return word;
 }
 
 template <int OP, int MAP, int LAYOUT, bool LDS>
@@ -269,19 +316,32 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
         rv[i] = sr.y;
       }
       *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(out) + e[k]) = quant4(c.v, sv, rv);
+    } else if (OP == OP_SOFTEDGE && kStepped) {
+      float sv[4], rv[4], lv[4], hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 sr = scale_of(c.si[kUniform ? 0 : i]);
+        const float2 lh = thresholds_of(c.si[kUniform ? 0 : i]);
+        sv[i] = sr.x;
+        rv[i] = sr.y;
+        lv[i] = lh.x;
+        hv[i] = lh.y;
+      }
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(out) + e[k]) =
+          softedge4(c.v, sv, rv, lv, hv, g.se_m, g.se_im);
     } else {
       uint32_t word = 0u;
       if (kUniform) {
         const float2 sr = scale_of(c.si[0]);
         const float2 lh = thresholds_of(c.si[0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) word |= encode<OP>(c.v[i], sr, lh) << (8 * i);
+        for (int i = 0; i < 4; ++i) word |= encode<OP>(c.v[i], sr, lh, g.se_m, g.se_im) << (8 * i);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i < c.n) {
             const int si = c.si[kUniform ? 0 : i];
-            word |= encode<OP>(c.v[i], scale_of(si), thresholds_of(si)) << (8 * i);
+            word |= encode<OP>(c.v[i], scale_of(si), thresholds_of(si), g.se_m, g.se_im) << (8 * i);
           }
         }
       }
@@ -314,8 +374,8 @@ __global__ void k_finalize_scales(float* scales, int n) {
 
 __global__ __launch_bounds__(kThreads) void k_softedge_decode(
     const uint8_t* __restrict__ code, int64_t total, int64_t C, int64_t inner,
-    const uint8_t* __restrict__ group_of, int nscales, const float* __restrict__ s,
-    float* __restrict__ out) {
+    const uint8_t* __restrict__ group_of, int nscales, const float* __restrict__ s, float m,
+    float im, float* __restrict__ out) {
   __shared__ float s_scale[256];
   for (int k = threadIdx.x; k < nscales; k += kThreads) s_scale[k] = s[k];
   __syncthreads();
@@ -331,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_softedge_decode(
 #pragma unroll
   for (int k = 0; k < kDecVec; ++k) {
     if (k < n) {
-      v[k] = softedge_value(b[k], s_scale[min((int)group_of[c], nscales - 1)]);
+      v[k] = softedge_value(b[k], s_scale[min((int)group_of[c], nscales - 1)], m, im);
       if (++i == inner) { i = 0; if (++c == C) c = 0; }
     }
   }
@@ -438,9 +498,11 @@ qssm_status qssm_quant_state_group_BC(const float* bc, int64_t outer, int32_t Gb
 
 qssm_status qssm_softedge_encode(const float* x, int64_t outer, int64_t C, int64_t inner,
                                  const int32_t* perm, const uint8_t* group_of, int32_t G,
-                                 const float* s, const float* L, const float* H, uint8_t* code,
-                                 hipStream_t stream) {
+                                 const float* s, const float* L, const float* H, int32_t form,
+                                 uint8_t* code, hipStream_t stream) {
   clear_error();
+  if (form != QSSM_X_SOFTEDGE && form != QSSM_X_SOFTEDGE2)
+    return fail(QSSM_ERR_INVALID_ARG, "form must be QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2");
   if (qssm_status st = check_extents(outer, C, inner)) return st;
   if (G < 1 || G > 256) return fail(QSSM_ERR_INVALID_ARG, "G must be in 1..256, got %d", G);
   const int64_t total = outer * C * inner;
@@ -448,13 +510,17 @@ qssm_status qssm_softedge_encode(const float* x, int64_t outer, int64_t C, int64
   if (total > 0 && (!x || !code || !group_of))
     return fail(QSSM_ERR_INVALID_ARG, "null tensor pointer");
   Geometry g{total, C, inner, perm, group_of, 1, 1, 1, G};
+  g.se_m = softedge_ratio(form);
+  g.se_im = 1.0f / g.se_m;
   return launch<OP_SOFTEDGE, MAP_GROUP>(x, g, const_cast<float*>(s), 0, L, H, code, stream);
 }
 
 qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, int64_t inner,
-                                 const uint8_t* group_of, int32_t G, const float* s, float* out,
-                                 hipStream_t stream) {
+                                 const uint8_t* group_of, int32_t G, const float* s, int32_t form,
+                                 float* out, hipStream_t stream) {
   clear_error();
+  if (form != QSSM_X_SOFTEDGE && form != QSSM_X_SOFTEDGE2)
+    return fail(QSSM_ERR_INVALID_ARG, "form must be QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2");
   if (qssm_status st = check_extents(outer, C, inner)) return st;
   if (G < 1 || G > 256) return fail(QSSM_ERR_INVALID_ARG, "G must be in 1..256, got %d", G);
   const int64_t total = outer * C * inner;
@@ -463,7 +529,8 @@ qssm_status qssm_softedge_decode(const uint8_t* code, int64_t outer, int64_t C, 
     return fail(QSSM_ERR_INVALID_ARG, "null tensor pointer");
   if (total > 0)
     k_softedge_decode<<<(unsigned)cdiv(total, (int64_t)kThreads * kDecVec), kThreads, 0, stream>>>(
-        code, total, C, inner, group_of, G, s, out);
+        code, total, C, inner, group_of, G, s, softedge_ratio(form), 1.0f / softedge_ratio(form),
+        out);
   return launch_status("softedge_decode");
 }
 

@@ -53,6 +53,7 @@ struct ScanParams {
   const uint8_t* y_group_of;  // int8 output: [D] output group of each channel
   const float* y_scales;      // int8 output: [Gy] static output scales
   const float* y_bias;        // int8 output: [D] correction term, or NULL
+  float se_m, se_im;          // soft-edge x: mode ratio (4 or 2) and its reciprocal
 };
 
 enum { kYF32 = 0, kYF16 = 1, kYI8 = 2 };  // output forms of the scan
@@ -61,16 +62,20 @@ enum { kYF32 = 0, kYF16 = 1, kYI8 = 2 };  // output forms of the scan
 // planes of `ns` consecutive states (the states one wave owns), and each plane stores per step the
 // ns B values followed by the ns C values.
 //  * CODE16 = false: dequantized fp32 values, [B, Gbc, N/ns, L + pad, 2*ns] floats.
-//  * CODE16 = true: the int8 codes as fp16 (exact), [B, Gbc, N/ns, L + pad, 2*ns] halves; used
+//  * CODE16 = true: the code units as fp16 (exact), [B, Gbc, N/ns, L + pad, 2*ns] halves; used
 //    when every plane lies inside one state group, so that its scales factor out of the plane's
 //    chains (the scan applies them once per output). Codes of a group whose scale is not valid
 //    are staged as 0.
+// The unit of a code is the int8 value, or for soft-edge bytes (se != 0) the payload times 1, 1/m
+// or m (at most 128 in magnitude and a multiple of 1/4: exact in fp16); the value is unit * scale,
+// one rounding (m * scale is exact), as the soft-edge decoder defines it.
 template <bool CODE16>
 __global__ __launch_bounds__(256) void k_stage_bc(const int8_t* __restrict__ Bq,
                                                   const int8_t* __restrict__ Cq,
                                                   const float* __restrict__ Bs,
                                                   const float* __restrict__ Cs, int64_t B,
                                                   int Gbc, int N, int64_t L, int gs, int ns,
+                                                  int se, float m, float im,
                                                   void* __restrict__ stage) {
   const int64_t Lp = L + kPadRows;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over (b, g, n, t < Lp)
@@ -86,31 +91,35 @@ __global__ __launch_bounds__(256) void k_stage_bc(const int8_t* __restrict__ Bq,
   const int plane = n / ns, k = n % ns;
   const int64_t row = ((bg * (N / ns) + plane) * Lp + t) * (2 * ns);
   // rows past L are zero (read by the last batches, times delta = 0)
-  const int qb = (t < L && scale_ok(sb)) ? (int)Bq[r * L + t] : 0;
-  const int qc = (t < L && scale_ok(sc)) ? (int)Cq[r * L + t] : 0;
+  const uint32_t bb = t < L ? (uint32_t)(uint8_t)Bq[r * L + t] : 0u;
+  const uint32_t cb = t < L ? (uint32_t)(uint8_t)Cq[r * L + t] : 0u;
+  const float ub = se ? softedge_unit(bb, m, im) : (float)(int8_t)bb;
+  const float uc = se ? softedge_unit(cb, m, im) : (float)(int8_t)cb;
+  const float qb = scale_ok(sb) ? ub : 0.0f;
+  const float qc = scale_ok(sc) ? uc : 0.0f;
   if (CODE16) {
     _Float16* dst = reinterpret_cast<_Float16*>(stage) + row;
     dst[k] = (_Float16)qb;
     dst[ns + k] = (_Float16)qc;
   } else {
     float* dst = reinterpret_cast<float*>(stage) + row;
-    dst[k] = scale_ok(sb) ? (float)qb * sb : 0.0f;
-    dst[ns + k] = scale_ok(sc) ? (float)qc * sc : 0.0f;
+    dst[k] = qb * sb;
+    dst[ns + k] = qc * sc;
   }
 }
 
 // Unscaled x value of a code byte: the int8 code, or the soft-edge code times its mode factor
-// (1, 1/4 or 4; exact), so that the dequantized value is sx * xunit.
+// (1, 1/m or m; exact), so that the dequantized value is sx * xunit.
 // Branch-free soft-edge decode for base scale 1: tag 0 -> 7-bit payload, tag 10 -> 6-bit payload
-// times 1/4, tag 11 -> 6-bit payload times 4 (the layout of softedge_value).
+// times 1/m, tag 11 -> 6-bit payload times m (the layout of softedge_value).
 template <int XCODE>
-__device__ __forceinline__ float xunit(uint32_t byte) {
+__device__ __forceinline__ float xunit(uint32_t byte, float m, float im) {
   if (XCODE == QSSM_X_SOFTEDGE) {
     const int q7 = __builtin_amdgcn_sbfe((int)byte, 0, 7);
     const int q6 = __builtin_amdgcn_sbfe((int)byte, 0, 6);
     const bool tagged = (byte & 0x80u) != 0;
-    const float m = tagged ? ((byte & 0x40u) ? 4.0f : 0.25f) : 1.0f;
-    return (float)(tagged ? q6 : q7) * m;
+    const float f = tagged ? ((byte & 0x40u) ? m : im) : 1.0f;
+    return (float)(tagged ? q6 : q7) * f;
   }
   return (float)(int8_t)(byte & 0xFFu);
 }
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
         uint32_t word = 0u;            // by selecting the word with uniform compares
 #pragma unroll
         for (int k = 0; k < kT / 4; ++k) word = (t / 4 == k) ? codes[k] : word;
-        v[j] = xunit<XCODE>((word & xmask) >> (8 * (t % 4)));
+        v[j] = xunit<XCODE>((word & xmask) >> (8 * (t % 4)), p.se_m, p.se_im);
       }
 #pragma unroll
       for (int j = 0; j < kPerX; ++j) xd[nb][lane][w * kPerX + j] = v[j];
@@ -353,7 +362,8 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       for (int s2 = 0; s2 < kBatch; ++s2) {
         const int t = bt + s2;
         const float dt = dl[t];
-        const float u = dt * (kShareX ? xcur[kShareX ? t : 0] : xunit<XCODE>(xq[t / 4] >> (8 * (t % 4))));
+        const float u = dt * (kShareX ? xcur[kShareX ? t : 0]
+                                      : xunit<XCODE>(xq[t / 4] >> (8 * (t % 4)), p.se_m, p.se_im));
         float dA[NS];
 #pragma unroll
         for (int k = 0; k < NS; ++k) dA[k] = dAr[t % 2][k];
@@ -391,7 +401,8 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
 #pragma unroll
       for (int ww = 0; ww < W; ++ww)
         sum = fmaf(cf[ww], ybuf[buf][ww][t][lane], sum);
-      const float xu = kShareX ? xd[buf][lane][kShareX ? t : 0] : xunit<XCODE>(xq[t / 4] >> (8 * (t % 4)));
+      const float xu = kShareX ? xd[buf][lane][kShareX ? t : 0]
+                               : xunit<XCODE>(xq[t / 4] >> (8 * (t % 4)), p.se_m, p.se_im);
       yo[j] = fmaf(Dsx, xu, sum);
     }
     const int64_t t0 = tb + w * kPer;
@@ -494,15 +505,17 @@ qssm_status scan_impl(const qssm_scan_args* a, void* stage_mem, hipStream_t stre
   // fp16 codes when every wave's states lie inside one B/C state group
   const bool code16 = (a->bc_group_size % ns) == 0;
   const int64_t nstage = B * a->bc_groups * N * (L + kPadRows);
+  const int bse = a->bc_code != QSSM_X_INT8;
+  const float bm = softedge_ratio(a->bc_code), bim = 1.0f / bm;
   if (nstage > 0) {
     if (code16)
       k_stage_bc<true><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
           a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
-          ns, stage);
+          ns, bse, bm, bim, stage);
     else
       k_stage_bc<false><<<(unsigned)cdiv(nstage, 256), 256, 0, stream>>>(
           a->Bq, a->Cq, a->B_scales, a->C_scales, B, a->bc_groups, (int)N, L, a->bc_group_size,
-          ns, stage);
+          ns, bse, bm, bim, stage);
     if (qssm_status s = launch_status("scan_w8a8 staging")) return s;
   }
 
@@ -510,7 +523,7 @@ qssm_status scan_impl(const qssm_scan_args* a, void* stage_mem, hipStream_t stre
                a->y_dtype == QSSM_I8 ? a->y_groups : 1,
                a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->B_scales,
                a->C_scales, a->Dskip, a->h0, a->y, a->h_last, a->y_group_of, a->y_scales,
-               a->y_bias};
+               a->y_bias, softedge_ratio(a->x_code), 1.0f / softedge_ratio(a->x_code)};
   const int yout = a->y_dtype == QSSM_F16 ? kYF16 : (a->y_dtype == QSSM_I8 ? kYI8 : kYF32);
   switch (N) {
     case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yout, code16, stream);
@@ -529,8 +542,10 @@ qssm_status validate(const qssm_scan_args* a, bool* done) {
   const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
   if (B < 0 || L < 0 || D < 1 || N < 1) return fail(QSSM_ERR_INVALID_ARG, "bad shape");
   if (L > 0x7fffff00LL) return fail(QSSM_ERR_UNSUPPORTED, "seqlen must be below 2^31 - 256");
-  if (a->x_code != QSSM_X_INT8 && a->x_code != QSSM_X_SOFTEDGE)
-    return fail(QSSM_ERR_INVALID_ARG, "x_code must be QSSM_X_INT8 or QSSM_X_SOFTEDGE");
+  if (a->x_code != QSSM_X_INT8 && a->x_code != QSSM_X_SOFTEDGE && a->x_code != QSSM_X_SOFTEDGE2)
+    return fail(QSSM_ERR_INVALID_ARG, "x_code must be QSSM_X_INT8, QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2");
+  if (a->bc_code != QSSM_X_INT8 && a->bc_code != QSSM_X_SOFTEDGE && a->bc_code != QSSM_X_SOFTEDGE2)
+    return fail(QSSM_ERR_INVALID_ARG, "bc_code must be QSSM_X_INT8, QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2");
   if (a->y_dtype != QSSM_F32 && a->y_dtype != QSSM_F16 && a->y_dtype != QSSM_I8)
     return fail(QSSM_ERR_INVALID_ARG, "y_dtype must be QSSM_F32, QSSM_F16 or QSSM_I8");
   if (a->y_dtype == QSSM_I8) {

@@ -14,6 +14,7 @@ import numpy as np
 from . import (QSSM_F16, QSSM_F32, QSSM_I16, QSSM_X_INT8, QSSM_X_SOFTEDGE, qssm_calib_block_absmax,
                qssm_calib_channel_absmax, qssm_calib_cluster_channels, qssm_calib_group_absmax,
                qssm_calib_s4d_state_scale, qssm_calib_scales, qssm_calib_softedge,
+               qssm_softedge_track, qssm_softedge_track_workspace_size,
                qssm_quant_group_x, qssm_quant_state_group_BC, qssm_s4d_scan, qssm_scan_w8a8,
                qssm_scan_workspace_size, qssm_softedge_encode, qssm_ssd_chunk_int8,
                qssm_ssd_workspace_size, qssm_state_update, s4d_args, scan_args, ssd_args,
@@ -57,15 +58,31 @@ def calib_y_groups(y_cal, G):
     return group_of, qssm_calib_scales(qssm_calib_group_absmax(ch, group_of, G))
 
 
-def calib_softedge(x_cal, perm, group_of, G):
-    """Per-group soft-edge (s, L, H) from the calibration tensor in cluster order."""
+def calib_softedge(x_cal, perm, group_of, G, with_state=False):
+    """Per-group soft-edge (s, L, H) from the calibration tensor in cluster order; with_state:
+    also the fp64 EMA state [G, 2] an on-device tracker continues from."""
     xs = np.asarray(x_cal)[:, perm, :]
     s = np.zeros(G, np.float32)
     L = np.zeros(G, np.float32)
     H = np.zeros(G, np.float32)
+    st = np.zeros((G, 2), np.float64)
     for g in range(G):
-        s[g], L[g], H[g], _ = qssm_calib_softedge(xs[:, group_of == g, :])
-    return s, L, H
+        s[g], L[g], H[g], st[g] = qssm_calib_softedge(xs[:, group_of == g, :])
+    return (s, L, H, st) if with_state else (s, L, H)
+
+
+def state_group_map(Gbc, N, gs):
+    """Scale index of each of the Gbc * N states of B or C: g * (N / gs) + n / gs."""
+    n = np.arange(Gbc * N)
+    return ((n // N) * (N // gs) + (n % N) // gs).astype(np.uint8)
+
+
+def calib_softedge_state_groups(bc_cal, gs):
+    """Per-state-group soft-edge (s, L, H) of B or C [outer, Gbc, N, inner]."""
+    bc = np.asarray(bc_cal)
+    o, Gbc, N, inner = bc.shape
+    return calib_softedge(bc.reshape(o, Gbc * N, inner), np.arange(Gbc * N),
+                          state_group_map(Gbc, N, gs), Gbc * N // gs)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -76,9 +93,14 @@ class Mamba1Layer:
     cluster order), quantize B and C, run the W8A8 scan."""
 
     def __init__(self, inp, G, gs, device, x_code=QSSM_X_INT8, dynamic_scales=False,
-                 y_dtype=QSSM_F32, with_h0=False, perm=True, y_out=None):
+                 y_dtype=QSSM_F32, with_h0=False, perm=True, y_out=None, bc_code=QSSM_X_INT8,
+                 track=False):
         """y_out = (group_of [D] uint8, scales [Gy] fp32, bias [D] fp32 or None), in the layer's
-        channel order: the scan then writes int8 y codes for the next W8A8 module."""
+        channel order: the scan then writes int8 y codes for the next W8A8 module.
+        x_code / bc_code: int8 or a soft-edge form (QSSM_X_SOFTEDGE, QSSM_X_SOFTEDGE2) for x and
+        for B/C (soft-edge B/C: per-state-group base scales and thresholds from the calibration
+        draws). track (soft-edge x): every step first updates the x thresholds on the device from
+        the step's own x (P5 / P99.9 with the EMA, continuing the calibration's state)."""
         import torch
         self.inp = inp
         self.G, self.gs, self.x_code = G, gs, x_code
@@ -102,9 +124,21 @@ class Mamba1Layer:
             self.perm, self.group_of, xs = calib_x_groups(inp["x_cal"], G)
             bs = calib_state_groups(inp["B_cal"], gs)
             cs = calib_state_groups(inp["C_cal"], gs)
-        if x_code == QSSM_X_SOFTEDGE:
-            xs, sL, sH = calib_softedge(inp["x_cal"], self.perm, self.group_of, G)
+        self.bc_code, self.track = bc_code, track
+        if track and x_code == QSSM_X_INT8:
+            raise ValueError("threshold tracking needs soft-edge x")
+        if x_code != QSSM_X_INT8:
+            xs, sL, sH, st = calib_softedge(inp["x_cal"], self.perm, self.group_of, G, with_state=True)
             self.sL, self.sH = _dev(sL, device), _dev(sH, device)
+            self.ema = _dev(st, device)
+            if track:
+                self.track_ws = torch.empty(qssm_softedge_track_workspace_size(G), dtype=torch.uint8,
+                                            device=device)
+        if bc_code != QSSM_X_INT8:
+            self.sg_map = _dev(state_group_map(Gbc, N, gs), device)
+            bs, bL, bH = calib_softedge_state_groups(inp["B_cal"], gs)
+            cs, cL, cH = calib_softedge_state_groups(inp["C_cal"], gs)
+            self.bL, self.bH, self.cL, self.cH = (_dev(a, device) for a in (bL, bH, cL, cH))
         p = self.perm
         dev = device
         self.x = _dev(x, dev)
@@ -121,8 +155,9 @@ class Mamba1Layer:
         self.cs = _dev(cs, dev)
         self.xq = torch.empty((B, D, L), dtype=torch.int8 if x_code == QSSM_X_INT8 else torch.uint8,
                               device=dev)
-        self.Bq = torch.empty(inp["B"].shape, dtype=torch.int8, device=dev)
-        self.Cq = torch.empty(inp["C"].shape, dtype=torch.int8, device=dev)
+        bdt = torch.int8 if bc_code == QSSM_X_INT8 else torch.uint8
+        self.Bq = torch.empty(inp["B"].shape, dtype=bdt, device=dev)
+        self.Cq = torch.empty(inp["C"].shape, dtype=bdt, device=dev)
         ydt = torch.float32 if y_dtype == QSSM_F32 else torch.float16
         self.y_out = None
         if y_out is not None:
@@ -135,7 +170,8 @@ class Mamba1Layer:
         yo = self.y_out or (None, None, None)
         self.args = scan_args(self.xq, x_code, self.group_t, self.xs, self.delta, self.A, self.Bq,
                               self.Cq, self.bs, self.cs, gs, self.y, Dskip=self.D, h0=self.h0,
-                              h_last=self.h_last, y_group_of=yo[0], y_scales=yo[1], y_bias=yo[2])
+                              h_last=self.h_last, y_group_of=yo[0], y_scales=yo[1], y_bias=yo[2],
+                              bc_code=bc_code)
         self.ws = torch.empty(qssm_scan_workspace_size(self.args), dtype=torch.uint8, device=dev)
 
     def quantize(self):
@@ -144,10 +180,23 @@ class Mamba1Layer:
             qssm_quant_group_x(x3, self.group_t, self.G, self.xs, self.xq, perm=self.perm_t,
                                compute_scales=self.dynamic)
         else:
+            if self.track:
+                qssm_softedge_track(x3, self.group_t, self.G, self.ema, self.xs, self.sL, self.sH,
+                                    self.track_ws, ema_valid=True, perm=self.perm_t)
             qssm_softedge_encode(x3, self.group_t, self.G, self.xs, self.sL, self.sH, self.xq,
-                                 perm=self.perm_t)
-        qssm_quant_state_group_BC(self.Bf, self.gs, self.bs, self.Bq, compute_scales=self.dynamic)
-        qssm_quant_state_group_BC(self.Cf, self.gs, self.cs, self.Cq, compute_scales=self.dynamic)
+                                 perm=self.perm_t, form=self.x_code)
+        if self.bc_code == QSSM_X_INT8:
+            qssm_quant_state_group_BC(self.Bf, self.gs, self.bs, self.Bq,
+                                      compute_scales=self.dynamic)
+            qssm_quant_state_group_BC(self.Cf, self.gs, self.cs, self.Cq,
+                                      compute_scales=self.dynamic)
+        else:
+            B, Gbc, N, L = self.Bf.shape
+            ng = Gbc * N // self.gs
+            for src, dst, sc, lo, hi in ((self.Bf, self.Bq, self.bs, self.bL, self.bH),
+                                         (self.Cf, self.Cq, self.cs, self.cL, self.cH)):
+                qssm_softedge_encode(src.view(B, Gbc * N, L), self.sg_map, ng, sc, lo, hi,
+                                     dst.view(B, Gbc * N, L), form=self.bc_code)
 
     def scan(self):
         qssm_scan_w8a8(self.args, self.ws)

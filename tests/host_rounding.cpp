@@ -13,9 +13,11 @@ void host_quant8_div(const float* v, int64_t n, float s, int8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = qssm::quant8(v[i], s);
 }
 
-void host_softedge(const float* v, int64_t n, float s, float L, float H, uint8_t* out) {
+void host_softedge(const float* v, int64_t n, float s, float L, float H, int32_t ratio,
+                   uint8_t* out) {
   const float r = qssm::recip_or_zero(s);
-  for (int64_t i = 0; i < n; ++i) out[i] = qssm::softedge_code_r(v[i], s, r, L, H);
+  const float m = (float)ratio, im = 1.0f / (float)ratio;
+  for (int64_t i = 0; i < n; ++i) out[i] = qssm::softedge_code_r(v[i], s, r, L, H, m, im);
 }
 
 }  // extern "C"

@@ -42,7 +42,7 @@ def test_struct_layouts_and_version():
     for kind, st in qs.ARG_STRUCTS.items():
         assert lib.qssm_args_size(kind) == ctypes.sizeof(st)
     assert lib.qssm_args_size(99) == 0
-    assert lib.qssm_version() == 140
+    assert lib.qssm_version() == 150
     assert lib.qssm_status_string(qs.QSSM_ERR_WORKSPACE) == b"workspace missing or too small"
 
 
@@ -64,8 +64,34 @@ def test_quantizer_argument_errors_return_before_launch():
     s, msg = status("qssm_quant_state_group_BC", dummy, 1, 2, 16, 4, 5, dummy, 0, dummy, None)
     assert s == qs.QSSM_ERR_INVALID_ARG and "divide" in msg
     s, msg = status("qssm_softedge_encode", dummy, 1, 4, 4, None, dummy, 1, None, dummy, dummy,
-                    dummy, None)
+                    qs.QSSM_X_SOFTEDGE, dummy, None)
     assert s == qs.QSSM_ERR_INVALID_ARG
+    s, msg = status("qssm_softedge_encode", dummy, 1, 4, 4, None, dummy, 1, dummy, dummy, dummy,
+                    qs.QSSM_X_INT8, dummy, None)
+    assert s == qs.QSSM_ERR_INVALID_ARG and "form" in msg
+    s, msg = status("qssm_softedge_decode", dummy, 1, 4, 4, dummy, 1, dummy, 7, dummy, None)
+    assert s == qs.QSSM_ERR_INVALID_ARG and "form" in msg
+
+
+def test_softedge_track_argument_errors():
+    lib = qs.load()
+    assert lib.qssm_softedge_track_workspace_size(0) == 0
+    assert lib.qssm_softedge_track_workspace_size(33) == 0
+    need = lib.qssm_softedge_track_workspace_size(8)
+    assert need >= 8 * 4 * 256 * 8
+    dummy = ctypes.c_void_p(256)
+    s, msg = status("qssm_softedge_track", dummy, 1, 4, 4, None, dummy, 33, 0.1, 0, dummy, dummy,
+                    dummy, dummy, dummy, 1 << 20, None)
+    assert s == qs.QSSM_ERR_INVALID_ARG and "G must be" in msg
+    s, msg = status("qssm_softedge_track", dummy, 1, 4, 4, None, dummy, 2, 1.5, 0, dummy, dummy,
+                    dummy, dummy, dummy, 1 << 20, None)
+    assert s == qs.QSSM_ERR_INVALID_ARG and "alpha" in msg
+    s, msg = status("qssm_softedge_track", dummy, 1, 4, 4, None, dummy, 8, 0.1, 0, dummy, dummy,
+                    dummy, dummy, dummy, need - 1, None)
+    assert s == qs.QSSM_ERR_WORKSPACE
+    s, msg = status("qssm_softedge_track", dummy, 1, 4, 4, None, dummy, 8, 0.1, 0, None, dummy,
+                    dummy, dummy, dummy, need, None)
+    assert s == qs.QSSM_ERR_INVALID_ARG and "null" in msg
 
 
 def test_scan_argument_errors():
@@ -74,6 +100,10 @@ def test_scan_argument_errors():
                     bc_group_size=4, y_dtype=0)
     assert lib.qssm_scan_w8a8(ctypes.byref(a), None, 0, None) == qs.QSSM_ERR_INVALID_ARG
     a.x_code = 0
+    a.bc_code = 3
+    assert lib.qssm_scan_w8a8(ctypes.byref(a), None, 0, None) == qs.QSSM_ERR_INVALID_ARG
+    assert "bc_code" in lib.qssm_last_error().decode()
+    a.bc_code = qs.QSSM_X_SOFTEDGE2
     a.dstate = 12
     assert lib.qssm_scan_w8a8(ctypes.byref(a), None, 0, None) == qs.QSSM_ERR_UNSUPPORTED
     a.dstate = 16
@@ -164,15 +194,22 @@ def test_cluster_matches_oracle(C, G, seed):
 
 
 def test_softedge_thresholds_match_oracle():
+    """The fp32 thresholds and the fp64 EMA state, bit for bit, over many sample sizes (the
+    interpolation position (n - 1) q and each rounding of the blend must agree)."""
     r = np.random.default_rng(9)
     v1 = r.standard_t(3, 100001).astype(np.float32)
     v2 = (r.standard_normal(77777) * 2).astype(np.float32)
     s, L, H, st = qs.qssm_calib_softedge(v1)
     os_, oL, oH, ost = oracle.softedge_thresholds(v1)
-    assert (s, L, H) == (os_, oL, oH)
-    s2, L2, H2, _ = qs.qssm_calib_softedge(v2, ema_state=st)
-    os2, oL2, oH2, _ = oracle.softedge_thresholds(v2, prev=ost)
-    assert (s2, L2, H2) == (os2, oL2, oH2)
+    assert (s, L, H) == (os_, oL, oH) and tuple(st) == ost
+    s2, L2, H2, st2 = qs.qssm_calib_softedge(v2, ema_state=st)
+    os2, oL2, oH2, ost2 = oracle.softedge_thresholds(v2, prev=ost)
+    assert (s2, L2, H2) == (os2, oL2, oH2) and tuple(st2) == ost2
+    for seed in range(60):
+        r = np.random.default_rng(100 + seed)
+        v = (r.standard_t(3, int(r.integers(1, 20000))) * np.exp(r.uniform(-3, 3))).astype(np.float32)
+        _, _, _, st = qs.qssm_calib_softedge(v)
+        assert tuple(st) == oracle.softedge_thresholds(v)[3], v.size
 
 
 def test_group_and_block_absmax():

@@ -42,8 +42,9 @@ def _p(a):
 
 
 def softedge_oracle(lib, xs, os_, zero, extra):
-    s, L, H = extra
-    lib.orc_softedge_encode(_p(xs), 1, 1, xs.size, None, _p(zero), _p(s), _p(L), _p(H), _p(os_))
+    s, L, H, ratio = extra
+    lib.orc_softedge_encode(_p(xs), 1, 1, xs.size, None, _p(zero), _p(s), _p(L), _p(H),
+                            int(ratio[0]), _p(os_))
 
 
 def quant_oracle(lib, xs, os_, zero, extra):
@@ -51,7 +52,7 @@ def quant_oracle(lib, xs, os_, zero, extra):
     lib.orc_quant_group_x(_p(xs), 1, 1, xs.size, None, _p(zero), _p(s), _p(os_))
 
 
-@pytest.mark.parametrize("kind", ["softedge", "int8"])
+@pytest.mark.parametrize("kind", ["softedge", "softedge2", "int8"])
 def test_all_fp32_patterns(dev, kind):
     import torch
     import quantized_state_space_amd as qs
@@ -62,15 +63,19 @@ def test_all_fp32_patterns(dev, kind):
     g = torch.zeros(1, dtype=torch.uint8, device=dev)
     s_d, L_d, H_d = (torch.from_numpy(v).to(dev) for v in (s, L, H))
     x_d = torch.empty(CHUNK, dtype=torch.float32, device=dev)
-    c_d = torch.empty(CHUNK, dtype=torch.uint8 if kind == "softedge" else torch.int8, device=dev)
-    want = np.empty(CHUNK, np.uint8 if kind == "softedge" else np.int8)
+    se = kind.startswith("softedge")
+    ratio = np.int32([2 if kind == "softedge2" else 4])
+    form = qs.QSSM_X_SOFTEDGE2 if kind == "softedge2" else qs.QSSM_X_SOFTEDGE
+    c_d = torch.empty(CHUNK, dtype=torch.uint8 if se else torch.int8, device=dev)
+    want = np.empty(CHUNK, np.uint8 if se else np.int8)
     for k in range((1 << 32) // CHUNK):
         bits = np.arange(k * CHUNK, (k + 1) * CHUNK, dtype=np.uint32)
         x = bits.view(np.float32)
         x_d.copy_(torch.from_numpy(x))
-        if kind == "softedge":
-            qs.qssm_softedge_encode(x_d.view(1, 1, CHUNK), g, 1, s_d, L_d, H_d, c_d.view(1, 1, CHUNK))
-            oracle_chunk(softedge_oracle, x, want, (s, L, H))
+        if se:
+            qs.qssm_softedge_encode(x_d.view(1, 1, CHUNK), g, 1, s_d, L_d, H_d, c_d.view(1, 1, CHUNK),
+                                    form=form)
+            oracle_chunk(softedge_oracle, x, want, (s, L, H, ratio))
         else:
             qs.qssm_quant_group_x(x_d.view(1, 1, CHUNK), g, 1, s_d, c_d.view(1, 1, CHUNK))
             oracle_chunk(quant_oracle, x, want, (s,))

@@ -29,7 +29,7 @@ def hr(tmp_path_factory):
     P, I64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
     lib.host_quant8.argtypes = [P, I64, F, P]
     lib.host_quant8_div.argtypes = [P, I64, F, P]
-    lib.host_softedge.argtypes = [P, I64, F, F, F, P]
+    lib.host_softedge.argtypes = [P, I64, F, F, F, ctypes.c_int32, P]
     return lib
 
 
@@ -43,7 +43,8 @@ def binade(e, sign=1.0):
 def host_codes(hr, fn, v, *args):
     v = np.ascontiguousarray(v, dtype=np.float32)
     out = np.empty(v.shape, np.uint8 if fn == "host_softedge" else np.int8)
-    getattr(hr, fn)(v.ctypes.data, v.size, *[float(a) for a in args], out.ctypes.data)
+    args = [int(a) if isinstance(a, int) else float(a) for a in args]
+    getattr(hr, fn)(v.ctypes.data, v.size, *args, out.ctypes.data)
     return out
 
 
@@ -53,10 +54,10 @@ def oracle_codes(v, s):
                                 np.float32([s])).reshape(-1)
 
 
-def oracle_softedge(v, s, L, H):
+def oracle_softedge(v, s, L, H, ratio=4):
     v = np.ascontiguousarray(v, dtype=np.float32)
     return oracle.softedge_encode(v.reshape(1, 1, -1), np.zeros(1, np.uint8), np.float32([s]),
-                                  np.float32([L]), np.float32([H])).reshape(-1)
+                                  np.float32([L]), np.float32([H]), ratio=ratio).reshape(-1)
 
 
 def ties_and_neighbours(s, rng, n=200000):
@@ -105,20 +106,23 @@ def test_quant_invalid_scales_give_zero(hr, s):
     assert not host_codes(hr, "host_quant8", v, s).any()
 
 
+@pytest.mark.parametrize("ratio", [4, 2])
 @pytest.mark.parametrize("s,L,H", [(np.float32(0.05), np.float32(0.1), np.float32(3.15)),
                                    (np.float32(1.0), np.float32(0.0), np.float32(63.0)),
-                                   (np.float32(0.02), np.float32(0.5), np.float32(0.25))])
-def test_softedge_matches_oracle(hr, s, L, H):
+                                   (np.float32(0.02), np.float32(0.5), np.float32(0.25)),
+                                   (np.float32(2.0 ** -100), np.float32(1e-30), np.float32(3e-29))])
+def test_softedge_matches_oracle(hr, s, L, H, ratio):
     rng = np.random.default_rng(5)
-    parts = [ties_and_neighbours(s, rng, 50000), ties_and_neighbours(np.float32(s * 0.25), rng, 50000),
-             ties_and_neighbours(np.float32(s * 4.0), rng, 50000),
+    parts = [ties_and_neighbours(s, rng, 50000),
+             ties_and_neighbours(np.float32(s / ratio), rng, 50000),
+             ties_and_neighbours(np.float32(s * ratio), rng, 50000),
              synth.quantizer_edge_values(scale=s, n=20000),
              np.float32([L, -L, H, -H, np.nextafter(L, 0), np.nextafter(H, np.inf), 0.0, -0.0,
                          np.inf, -np.inf, np.nan])]
     e = exponent_of(np.float32(16.0) * s)
     parts += [binade(e), binade(e, -1.0), binade(exponent_of(np.float32(4.0) * H))]
     v = np.concatenate(parts).astype(np.float32)
-    got = host_codes(hr, "host_softedge", v, s, L, H)
-    want = oracle_softedge(v, s, L, H)
+    got = host_codes(hr, "host_softedge", v, s, L, H, ratio)
+    want = oracle_softedge(v, s, L, H, ratio)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
