@@ -371,12 +371,14 @@ def s4d_scan(u, Ah, Bh, Ch, dt, Dskip=None, state_scale=None, h0=None):
 
 
 def ssd_chunked(xh, delta, A, Bh, Ch, chunk, Dskip=None, h0=None, int8_state=False, qx=None,
-                sx=None):
+                sx=None, int8_intra=False):
     """Mamba2 SSD chunked form in fp64. xh [B, L, nh, P]; delta [B, L, nh]; A [nh];
     Bh, Ch [B, L, Gbc, N]; h0 [B, nh, P, N]. int8_state=True selects the requantized chunk state
     (needs the codes qx [B, L, nh, P] and per-channel scales sx [nh*P]); that mode is exact in its
     special case (integral weighted codes) and otherwise pinned by its requantization error bound
-    and the absence of rounding bias.
+    and the absence of rounding bias. int8_intra=True selects the int8 intra-chunk output (each
+    row of the intra-chunk weights requantized with its own max / 127 scale, times the x codes;
+    same inputs), pinned the same way.
     Returns (y [B, L, nh, P], h_last [B, nh, P, N])."""
     xh = _c(xh, np.float64)
     Bsz, L, nh, P = xh.shape
@@ -388,7 +390,8 @@ def ssd_chunked(xh, delta, A, Bh, Ch, chunk, Dskip=None, h0=None, int8_state=Fal
         lib().orc_ssd_chunked(Bsz, L, nh, P, N, Gbc, chunk, _ptr(xh), _ptr(_c(delta, np.float64)),
                               _ptr(_c(A, np.float64)), _ptr(Bh), _ptr(_c(Ch, np.float64)),
                               _ptr(_c(Dskip, np.float64)), _ptr(_c(h0, np.float64)),
-                              1 if int8_state else 0, _ptr(_c(qx, np.int8)), _ptr(_c(sx, np.float64)),
+                              (1 if int8_state else 0) | (2 if int8_intra else 0),
+                              _ptr(_c(qx, np.int8)), _ptr(_c(sx, np.float64)),
                               _ptr(y), _ptr(hl))
     return y, hl
 

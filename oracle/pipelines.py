@@ -249,10 +249,11 @@ def s4d_state_scale(inp, headroom=1.25, with_h0=False):
 # SSD
 
 def ssd(inp, chunk=256, gs=16, groups_per_block=8, with_h0=False, heads=None, int8_state=False,
-        exact=False, calib=None):
+        exact=False, calib=None, int8_intra=False):
     """Oracle SSD layer. heads: optional subset of head indices (the recurrence of each head is
-    independent; B/C groups follow the head). int8_state selects the requantized int8 chunk state;
-    exact=True runs the plain sequential scan instead of the chunked form. calib: optional
+    independent; B/C groups follow the head). int8_state selects the requantized int8 chunk state,
+    int8_intra the row-requantized int8 intra-chunk output; exact=True runs the plain sequential
+    scan instead of the chunked form. calib: optional
     (group_of, xs, bs, cs) used instead of the calibration from inp (tests set scales outside the
     valid range this way). Returns codes, scales and fp64 y / h_last (for the selected heads:
     y [B, L, len(heads), P])."""
@@ -286,12 +287,45 @@ def ssd(inp, chunk=256, gs=16, groups_per_block=8, with_h0=False, heads=None, in
             y, hl = ssd_as_sequential(*args, Dskip=inp["D"][h:h + 1], h0=h0)
         else:
             y, hl = ssd_chunked(*args, chunk, Dskip=inp["D"][h:h + 1], h0=h0,
-                                int8_state=int8_state, qx=xq[:, :, h:h + 1, :], sx=sx[h])
+                                int8_state=int8_state, qx=xq[:, :, h:h + 1, :], sx=sx[h],
+                                int8_intra=int8_intra)
         ys.append(y[:, :, 0])
         hls.append(hl[:, 0])
+        if int8_intra:
+            out.setdefault("intra_w", []).append((h, Bh[:, :, 0], Ch[:, :, 0], xh[:, :, 0]))
     out["y"] = np.stack(ys, axis=2)
     out["h_last"] = np.stack(hls, axis=1)
     return out
+
+
+def ssd_intra_near_boundary(inp, ref, eps_rel, eps_abs, chunk=256):
+    """For a run of ssd(..., int8_intra=True): per output [B, L, len(heads), P], the sum over the
+    row's requantized weights whose scaled value t = W * 127 / m_i lies within
+    eps_rel |t| + eps_abs of a rounding boundary of (m_i / 127) |xh_j[p]|: how far a computation
+    of W carrying relative error eps_rel can move that output by deciding those codes the other
+    way. W, m_i and xh are the oracle's own (fp64, from the dequantized codes). Also returns the
+    number of such codes and of all codes."""
+    B, L = inp["x"].shape[:2]
+    P = inp["x"].shape[3]
+    out = np.zeros((B, L, len(ref["intra_w"]), P))
+    near_total = codes_total = 0
+    for k, (h, Bh, Ch, xh) in enumerate(ref["intra_w"]):
+        for b in range(B):
+            for t0 in range(0, L, chunk):
+                q = min(chunk, L - t0)
+                dt = np.asarray(inp["delta"][b, t0:t0 + q, h], np.float64)
+                cum = np.cumsum(dt * np.float64(inp["A"][h]))
+                CB = Ch[b, t0:t0 + q] @ Bh[b, t0:t0 + q].T
+                W = np.tril(CB * np.exp(cum[:, None] - cum[None, :]) * dt[None, :])
+                m = np.abs(W).max(axis=1)
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    t = np.where(m[:, None] > 0, W * 127 / m[:, None], 0.0)
+                near = np.abs(t - np.floor(t) - 0.5) < eps_rel * np.abs(t) + eps_abs
+                near &= np.tri(q, dtype=bool)
+                near_total += int(near.sum())
+                codes_total += q * (q + 1) // 2
+                out[b, t0:t0 + q, k, :] = (m / 127)[:, None] * (near @ np.abs(xh[b, t0:t0 + q]))
+    return out, near_total, codes_total
 
 
 # ------------------------------------------------------------------------------------------------

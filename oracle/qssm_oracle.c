@@ -303,7 +303,12 @@ EXPORT void orc_s4d_scan(int64_t B, int64_t L, int64_t H, int64_t N, const doubl
  *   w_j = delta_j * exp(cum_last - cum_j), w_max = max_j w_j,
  *   r[j,p] = clamp(RNE(qx[j,p] * w_j / w_max), -128, 127)  (decided in fp64),
  *   S[p, n] = w_max * sx[p] * sum_j r[j,p] * Bh_j[n].
- * Mode 1 needs the x codes (qx [B, L, nh, P]) and per-channel x scales (sx [nh * P]). */
+ * Mode 2 (int8 intra-chunk output, the SSDi8 persistent int8 path through Y_intra; combinable with
+ * mode 1): row i of the intra-chunk weights W[i, j] = (Ch_i . Bh_j) exp(cum_i - cum_j) delta_j
+ * (j <= i) is requantized with its own scale: m_i = max_j |W[i, j]|,
+ *   r[i, j] = clamp(RNE(W[i, j] * 127 / m_i), -127, 127)  (0 when m_i = 0; decided in fp64),
+ *   Y_intra[i, p] = (m_i / 127) * sx[p] * sum_j r[i, j] * qx[j, p].
+ * Modes 1 and 2 need the x codes (qx [B, L, nh, P]) and per-channel x scales (sx [nh * P]). */
 EXPORT void orc_ssd_chunked(int64_t B, int64_t L, int64_t nh, int64_t P, int64_t N, int64_t Gbc,
                             int64_t Q, const double* xh, const double* delta, const double* A,
                             const double* Bh, const double* Ch, const double* Dskip,
@@ -319,6 +324,8 @@ EXPORT void orc_ssd_chunked(int64_t B, int64_t L, int64_t nh, int64_t P, int64_t
       double* cum = malloc(sizeof(double) * (size_t)Q);
       double* w = malloc(sizeof(double) * (size_t)Q);
       double* G = malloc(sizeof(double) * (size_t)(Q * Q));
+      double* wrow = malloc(sizeof(double) * (size_t)Q);
+      double* rrow = malloc(sizeof(double) * (size_t)Q);
       for (int64_t k = 0; k < P * N; ++k) Hs[k] = h0 ? h0[(b * nh + h) * P * N + k] : 0.0;
 #define XH(t, p) xh[((b * L + (t)) * nh + h) * P + (p)]
 #define QX(t, p) qx[((b * L + (t)) * nh + h) * P + (p)]
@@ -337,27 +344,49 @@ EXPORT void orc_ssd_chunked(int64_t B, int64_t L, int64_t nh, int64_t P, int64_t
             G[i * Q + j] = cb;
           }
         /* outputs of this chunk use the state entering it */
-        for (int64_t i = 0; i < q; ++i)
+        for (int64_t i = 0; i < q; ++i) {
+          /* mode & 2: the intra-chunk weights W[i, j] = G exp(cum_i - cum_j) delta_j of row i are
+           * requantized to int8 with the row's own scale m_i / 127 (m_i = max_j |W[i, j]|), and
+           * multiply the x codes: intra = (m_i / 127) sx[p] sum_j r[i, j] qx[j, p] */
+          double mi = 0.0;
+          if (mode & 2) {
+            for (int64_t j = 0; j <= i; ++j) {
+              wrow[j] = G[i * Q + j] * exp(cum[i] - cum[j]) * DT(t0 + j);
+              if (fabs(wrow[j]) > mi) mi = fabs(wrow[j]);
+            }
+            for (int64_t j = 0; j <= i; ++j) {
+              double r = (mi > 0.0) ? rint(wrow[j] * 127.0 / mi) : 0.0;
+              if (r < -127.0) r = -127.0;
+              if (r > 127.0) r = 127.0;
+              rrow[j] = r;
+            }
+          }
           for (int64_t p = 0; p < P; ++p) {
             double intra = 0.0;
-            for (int64_t j = 0; j <= i; ++j)
-              intra += G[i * Q + j] * exp(cum[i] - cum[j]) * DT(t0 + j) * XH(t0 + j, p);
+            if (mode & 2) {
+              for (int64_t j = 0; j <= i; ++j) intra += rrow[j] * (double)QX(t0 + j, p);
+              intra *= (mi / 127.0) * sx[h * P + p];
+            } else {
+              for (int64_t j = 0; j <= i; ++j)
+                intra += G[i * Q + j] * exp(cum[i] - cum[j]) * DT(t0 + j) * XH(t0 + j, p);
+            }
             double inter = 0.0;
             for (int64_t n = 0; n < N; ++n) inter += CH(t0 + i, n) * Hs[p * N + n];
             inter *= exp(cum[i]);
             y[((b * L + t0 + i) * nh + h) * P + p] =
                 intra + inter + (Dskip ? Dskip[h] : 0.0) * XH(t0 + i, p);
           }
+        }
         /* chunk state and state passing */
         for (int64_t j = 0; j < q; ++j) w[j] = DT(t0 + j) * exp(cum[q - 1] - cum[j]);
-        if (mode == 0) {
+        if (!(mode & 1)) {
           for (int64_t p = 0; p < P; ++p)
             for (int64_t n = 0; n < N; ++n) {
               double acc = 0.0;
               for (int64_t j = 0; j < q; ++j) acc += w[j] * XH(t0 + j, p) * BH(t0 + j, n);
               S[p * N + n] = acc;
             }
-        } else {
+        } else if (mode & 1) {
           double wmax = 0.0;
           for (int64_t j = 0; j < q; ++j) if (w[j] > wmax) wmax = w[j];
           for (int64_t p = 0; p < P; ++p)
@@ -382,7 +411,7 @@ EXPORT void orc_ssd_chunked(int64_t B, int64_t L, int64_t nh, int64_t P, int64_t
 #undef DT
 #undef BH
 #undef CH
-      free(Hs); free(S); free(cum); free(w); free(G);
+      free(Hs); free(S); free(cum); free(w); free(G); free(wrow); free(rrow);
     }
 }
 

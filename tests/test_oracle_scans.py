@@ -485,3 +485,116 @@ def test_s4d_int16_error_bound_against_fp64():
     grid = np.concatenate([hq.real.ravel(), hq.imag.ravel()]) / s[0]
     assert np.array_equal(grid, np.rint(grid))
     assert not np.array_equal(hq, hl)
+
+
+# ------------------------------------------------------------------------------------------------
+# int8 intra-chunk output (row-requantized intra-chunk weights times the x codes)
+
+def intra_weights(p, b, h, t0, q, hpg):
+    """W[i, j] = (C_i . B_j) exp(cum_i - cum_j) delta_j [j <= i] of one chunk, from the method's
+    definitions written out in numpy."""
+    g = h // hpg
+    dt = p["delta"][b, t0:t0 + q, h]
+    cum = np.cumsum(dt * p["A"][h])
+    CB = p["Ch"][b, t0:t0 + q, g, :] @ p["Bh"][b, t0:t0 + q, g, :].T
+    return np.tril(CB * np.exp(cum[:, None] - cum[None, :]) * dt[None, :])
+
+
+def test_ssd_int8_intra_exact_in_its_special_case():
+    """A = 0 and delta = 1 make W = C B^T; with one-hot C (state 0) and B[:, 0] integral with
+    B[0, 0] = 127, every row's largest |W| is 127, so each requantized weight equals W itself and
+    the int8 intra-chunk output is exact (the state, x codes and D term unchanged)."""
+    r = np.random.default_rng(31)
+    p = ssd_small(seed=31, L=48)
+    B, L, nh, P = p["xh"].shape
+    Gbc, N = p["Bh"].shape[2], p["Bh"].shape[3]
+    qx = r.integers(-128, 128, (B, L, nh, P)).astype(np.int8)
+    sx = r.uniform(0.01, 0.1, nh * P)
+    Ch = np.zeros((B, L, Gbc, N))
+    Ch[..., 0] = 1.0
+    Bh = np.zeros((B, L, Gbc, N))
+    Bh[..., 0] = r.integers(-127, 128, (B, L, Gbc))
+    Bh[:, ::16, :, 0] = 127.0  # the first step of every 16-step chunk
+    p.update(xh=qx * sx.reshape(nh, P), delta=np.ones((B, L, nh)), A=np.zeros(nh), Ch=Ch, Bh=Bh)
+    y0, h0_ = oracle.ssd_chunked(chunk=16, **p)
+    y1, h1_ = oracle.ssd_chunked(chunk=16, int8_intra=True, qx=qx, sx=sx, **p)
+    np.testing.assert_allclose(y1, y0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(h1_, h0_)
+
+
+@pytest.mark.parametrize("L,chunk", [(40, 64), (64, 16), (50, 7)])
+def test_ssd_int8_intra_within_its_requantization_bound(L, chunk):
+    """Generic pin. Each requantized weight is within half a step m_i / 254 of W[i, j] (|W| <=
+    m_i keeps it inside +-127), so per output
+        |y_int8[i, p] - y_exact[i, p]| <= (m_i / 254) * sum_{j <= i} |xh_j[p]|,
+    with m_i the row's largest |W| computed here from the definitions; the state is untouched.
+    The error must also reach a sizeable fraction of the bound (an exact or smoothed output
+    would not)."""
+    r = np.random.default_rng(32)
+    p = ssd_small(seed=32, L=L, P=6, N=7, h0=True)
+    B, _, nh, P = p["xh"].shape
+    Gbc = p["Bh"].shape[2]
+    sx = r.uniform(0.005, 0.05, nh * P)
+    qx = r.integers(-128, 128, (B, L, nh, P)).astype(np.int8)
+    p["xh"] = qx * sx.reshape(nh, P)
+    y_exact, h_exact = oracle.ssd_chunked(chunk=chunk, **p)
+    y_int8, h_int8 = oracle.ssd_chunked(chunk=chunk, int8_intra=True, qx=qx, sx=sx, **p)
+    np.testing.assert_array_equal(h_int8, h_exact)
+    hpg = nh // Gbc
+    worst = 0.0
+    for b, h in itertools.product(range(B), range(nh)):
+        for t0 in range(0, L, chunk):
+            q = min(chunk, L - t0)
+            W = intra_weights(p, b, h, t0, q, hpg)
+            m = np.abs(W).max(axis=1)
+            ax = np.abs(p["xh"][b, t0:t0 + q, h, :])
+            bound = (m / 254)[:, None] * np.cumsum(ax, axis=0)
+            err = np.abs(y_int8[b, t0:t0 + q, h, :] - y_exact[b, t0:t0 + q, h, :])
+            assert np.all(err <= bound * (1 + 1e-9) + 1e-13), (b, h, t0)
+            worst = max(worst, (err / np.maximum(bound, 1e-300)).max())
+    assert worst > 0.05
+
+
+def test_ssd_int8_intra_rounding_is_unbiased():
+    """With W >= 0 (C, B >= 0) and x codes >= 0 every rounding error of the requantized weights
+    enters with the same sign of weight: a floor, ceiling or truncation would shift the outputs by
+    a large part of the bound above in one direction, while round-to-nearest-even errors average
+    out."""
+    r = np.random.default_rng(33)
+    p = ssd_small(seed=33, L=64, P=6, N=7, h0=False)
+    B, L, nh, P = p["xh"].shape
+    Gbc = p["Bh"].shape[2]
+    p["Bh"] = np.abs(p["Bh"])
+    p["Ch"] = np.abs(p["Ch"])
+    p["A"] = np.full(nh, -0.01)
+    p["delta"] = r.uniform(0.3, 0.6, (B, L, nh))
+    sx = r.uniform(0.005, 0.05, nh * P)
+    qx = r.integers(0, 128, (B, L, nh, P)).astype(np.int8)
+    p["xh"] = qx * sx.reshape(nh, P)
+    y_exact, _ = oracle.ssd_chunked(chunk=L, **p)
+    y_int8, _ = oracle.ssd_chunked(chunk=L, int8_intra=True, qx=qx, sx=sx, **p)
+    signed, bounds = [], []
+    for b, h in itertools.product(range(B), range(nh)):
+        W = intra_weights(p, b, h, 0, L, nh // Gbc)
+        m = np.abs(W).max(axis=1)
+        bounds.append((m / 254)[:, None] * np.cumsum(np.abs(p["xh"][b, :, h, :]), axis=0))
+        signed.append(y_int8[b, :, h, :] - y_exact[b, :, h, :])
+    ratio = np.mean(signed) / np.mean(bounds)
+    assert abs(ratio) < 0.2, ratio
+
+
+def test_ssd_int8_intra_and_state_modes_compose():
+    """Both int8 modes at once: the intra-chunk output of the combined run equals that of the
+    intra-only run where the state does not enter (first chunk, no h0), and its state equals the
+    state-only run's."""
+    r = np.random.default_rng(34)
+    p = ssd_small(seed=34, L=40, P=6, N=7, h0=False)
+    B, L, nh, P = p["xh"].shape
+    sx = r.uniform(0.005, 0.05, nh * P)
+    qx = r.integers(-128, 128, (B, L, nh, P)).astype(np.int8)
+    p["xh"] = qx * sx.reshape(nh, P)
+    y_i, _ = oracle.ssd_chunked(chunk=16, int8_intra=True, qx=qx, sx=sx, **p)
+    _, h_s = oracle.ssd_chunked(chunk=16, int8_state=True, qx=qx, sx=sx, **p)
+    y_b, h_b = oracle.ssd_chunked(chunk=16, int8_intra=True, int8_state=True, qx=qx, sx=sx, **p)
+    np.testing.assert_array_equal(y_b[:, :16], y_i[:, :16])
+    np.testing.assert_array_equal(h_b, h_s)
