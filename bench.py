@@ -305,12 +305,18 @@ class S4d(Workload):
         return out
 
 
+# Near-boundary margin of the int8 intra-chunk codes: the kernel forms W from G carried in fp16
+# (2^-11) and decides its row scale from that W (2^-11 again), decay factors ~1e-5.
+INTRA8_EPS_REL, INTRA8_EPS_ABS = 1.2e-3, 1e-4
+
+
 class Ssd(Workload):
-    def __init__(self, f16=False, y_int8=False):
+    def __init__(self, f16=False, y_int8=False, intra8=False):
         self.f16 = f16
         self.y_int8 = y_int8
+        self.intra8 = intra8
         self.name = ("mamba2-8b-ssd-layer-w8a8" + ("-fp16-y" if f16 else "") +
-                     ("-int8-y" if y_int8 else ""))
+                     ("-int8-y" if y_int8 else "") + ("-int8-intra" if intra8 else ""))
         self.dominant = "qssm_ssd_chunk_int8: k_ssd_state + k_ssd_output"
         self.heads = np.array([0, 64])
 
@@ -337,14 +343,17 @@ class Ssd(Workload):
             y_out = (yg, ys, yb)
         self.y_out = y_out
         self.lay = wl.SsdLayer(self.inp, dev, y_dtype=qs.QSSM_F16 if self.f16 else qs.QSSM_F32,
-                               y_out=y_out)
+                               y_out=y_out,
+                               intra_mma=qs.QSSM_MMA_I8 if self.intra8 else qs.QSSM_MMA_F16)
         B, L, nh, P, N, Gbc = self.lay.shape
         self.dims = self.lay.shape
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "heads": nh, "headdim": P,
                        "d_state": N, "ngroups": Gbc, "chunk": 256, "x_groups": int(self.lay.G),
                        "bc_state_groups": N // 16, "state": "f32",
                        "y": "int8, 8 output groups per head block + per-channel correction"
-                       if self.y_int8 else ("f16" if self.f16 else "f32")}
+                       if self.y_int8 else ("f16" if self.f16 else "f32"),
+                       "intra_chunk": "int8 MFMA, row-requantized weights" if self.intra8
+                       else "fp16 MFMA"}
         self.sample_desc = (f"{len(self.heads)} of {nh} heads (all batches, full length): the fp64 "
                             "chunked form, including quantizing the layer's whole x, B and C")
 
@@ -362,6 +371,21 @@ class Ssd(Workload):
         B, L, nh, P, N, _ = self.dims
         return B * L * len(self.heads) * P * N
 
+    def mfma_ops(self):
+        """Algorithmic matrix ops of the dominant call by operand type (multiply-add = 2, causal
+        halves counted once): C B^T in int8 per (b, chunk, group); the intra-chunk product, the
+        chunk state and the inter-chunk product per (b, chunk, head). Peak: dense MFMA T ops/s."""
+        B, L, nh, P, N, Gbc = self.dims
+        nc = -(-L // 256)
+        tri = 256 * 257 // 2
+        cb = 2 * B * nc * Gbc * tri * N
+        intra = 2 * B * nc * nh * tri * P
+        state = 2 * B * nc * nh * 256 * P * N
+        inter = 2 * B * nc * nh * 256 * N * P
+        i8 = cb + (intra if self.intra8 else 0)
+        f16 = state + inter + (0 if self.intra8 else intra)
+        return {"int8": (INT8_MFMA_PEAK_TOPS, i8), "fp16": (FP16_MFMA_PEAK_TFLOPS, f16)}
+
     def dominant_bytes(self):
         B, L, nh, P, N, Gbc = self.dims
         yb = 1 if self.y_int8 else (2 if self.f16 else 4)
@@ -371,7 +395,7 @@ class Ssd(Workload):
 
     def oracle_ref(self):
         import oracle.pipelines as op
-        return op.ssd(self.inp, heads=self.heads)
+        return op.ssd(self.inp, heads=self.heads, int8_intra=self.intra8)
 
     def check(self, ref):
         lay = self.lay
@@ -382,7 +406,20 @@ class Ssd(Workload):
         hsel = torch.as_tensor(self.heads, device=lay.y.device)
         rows = lambda a: np.asarray(a, np.float64).transpose(0, 2, 3, 1).reshape(-1, a.shape[1])
         out = {"codes_bit_exact": n}
-        if not self.y_int8:
+        if self.intra8:
+            # each output within the row tolerance plus one requantization step times |xh_j| for
+            # every weight code of its row that lies within the kernel's error of a boundary
+            import oracle.pipelines as op
+            y = rows(lay.y[:, :, hsel].float().cpu().numpy())
+            yr = rows(ref["y"])
+            slack, near, total = op.ssd_intra_near_boundary(self.inp, ref, INTRA8_EPS_REL,
+                                                            INTRA8_EPS_ABS)
+            allow = self.tol * np.abs(yr).max(axis=1, keepdims=True) + rows(slack)
+            used = float(np.max(np.abs(y - yr) / allow))
+            require(used <= 1.0, f"int8 intra-chunk y beyond its allowance ({used:.3f})")
+            out["y_within_allowance"] = round(used, 4)
+            out["near_boundary_codes"] = f"{near} of {total}"
+        elif not self.y_int8:
             y = lay.y[:, :, hsel].float().cpu().numpy().astype(np.float64)
             out["y_row_error"] = rows_close(rows(y), rows(ref["y"]), self.tol, "y")
         else:
@@ -583,14 +620,16 @@ def _zero(device):
 
 
 WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
-             "c4i8y": lambda: Ssd(False, True), "c3": lambda: Mamba1(False),
+             "c4i8y": lambda: Ssd(False, True), "c4i8i": lambda: Ssd(False, False, True),
+             "c3": lambda: Mamba1(False),
              "c3se": lambda: Mamba1(True), "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
              "c3se2bc": lambda: Mamba1(True, ratio=2, bc_soft_edge=True),
              "c2": lambda: S4d(False), "c2i16": lambda: S4d(True), "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True), "w4a8d": lambda: W4A8(256), "w4a8p": lambda: W4A8(16384)}
-OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3se2bc", "c3i8y", "c4f16", "c4i8y", "c5", "c5f16",
-          "w4a8d", "w4a8p")
+OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3se2bc", "c3i8y", "c4f16", "c4i8y", "c4i8i", "c5",
+          "c5f16", "w4a8d", "w4a8p")
 INT8_MFMA_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 
 
 # ------------------------------------------------------------------------------------------------
@@ -613,7 +652,8 @@ TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
     "c3se2bc": ["scan_m1.hip"],
     "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"], "c2i16": ["s4d.hip"],
-    "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c4i8y": ["ssd.hip"], "c5": ["state_update.hip"],
+    "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c4i8y": ["ssd.hip"], "c4i8i": ["ssd.hip"],
+    "c5": ["state_update.hip"],
     "c5f16": ["state_update.hip"],
 }
 
@@ -756,6 +796,10 @@ def run_workload(torch, dev, name, steps, warmup, budget_s, with_baseline=True):
     res = {"value": wl.updates() * steps / elapsed, "ms_per_step": elapsed * 1e3 / steps,
            "roofline": roof, "parity": parity,
            "hbm_frac_dominant": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if hasattr(wl, "mfma_ops"):
+        res["mfma"] = {k: {"ops": int(v[1]), "T_ops_s": round(v[1] / (kern_ms * 1e-3) / 1e12, 1),
+                           "frac_of_dense_peak": round(v[1] / (kern_ms * 1e-3) / 1e12 / v[0], 4)}
+                       for k, v in wl.mfma_ops().items()}
     if base is not None:
         res["cpu_baseline"] = base
     return wl, res
@@ -881,6 +925,8 @@ def main():
                          "(mean; median and min also given)"}
         if "cpu_baseline" in res:
             out["cpu_baseline"] = res["cpu_baseline"]
+        if "mfma" in res:
+            out["mfma"] = res["mfma"]
         del wl
         if args.all_configs:
             others = {}
@@ -897,6 +943,8 @@ def main():
                                    "kernel_us", "kernel_us_median", "kernel_us_min")}}
                 if "cpu_baseline" in r2:
                     e["cpu_baseline"] = r2["cpu_baseline"]
+                if "mfma" in r2:
+                    e["mfma"] = r2["mfma"]
                 others[name] = e
                 del w2
                 torch.cuda.empty_cache()

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 150 /* 1.5.0: soft-edge ratio 2, soft-edge B/C, device threshold tracking */
+#define QSSM_VERSION 160 /* 1.6.0: int8 intra-chunk SSD output */
 
 typedef int32_t qssm_status;
 enum {
@@ -289,6 +289,13 @@ qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
  *   the rounding of r is a floating-point decision inside the contraction);
  *   inter-chunk state passing in fp32;  Y_inter = exp(cum_i) * Ch . H_prev^T;
  *   y = Y_intra + Y_inter + Dskip * xh.
+ * intra_mma == QSSM_MMA_I8 runs Y_intra on int8 MFMA (the SSDi8 persistent int8 path through the
+ *   intra-chunk product): row i of the weights W[i, j] = G[i, j] exp(cum_i - cum_j) delta_j
+ *   (j <= i) is requantized with its own scale, m_i = max_j |W[i, j]| (fp32),
+ *   r[i, j] = clamp(rint(W[i, j] * 127 / m_i), -127, 127) (0 when m_i = 0), and
+ *   Y_intra[i, p] = (m_i / 127) * sx[p] * sum_j r[i, j] * qx[j, p] (int32 accumulate). The codes
+ *   are floating-point decisions inside the contraction (fp32 W); the requantization error per
+ *   output is at most (m_i / 254) sum_j |xh_j|.
  * y is fp32 or fp16 (y_dtype), or int8 codes for the next W8A8 module (QSSM_I8; SSDi8, abstract:
  * a persistent int8 path and an error-correction term from per-channel error statistics):
  *   y_code[b,t,h,p] = clamp(RNE(v / s), -128, 127),  v = fl32(y[b,t,h,p] + y_bias[h*P + p]),
@@ -327,6 +334,7 @@ typedef struct qssm_ssd_args {
   const uint8_t* y_group_of;                      /* QSSM_I8: [nh * P] output group of each channel */
   const float* y_scales;                          /* QSSM_I8: [Gy] static output scales */
   const float* y_bias;                            /* QSSM_I8: [nh * P] correction term, or NULL */
+  int32_t intra_mma;                              /* QSSM_MMA_F16 (default) or QSSM_MMA_I8 */
 } qssm_ssd_args;
 
 size_t qssm_ssd_workspace_size(const qssm_ssd_args* a);

@@ -55,7 +55,7 @@ class SsdArgs(ctypes.Structure):
                 ("Dskip", _P), ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P),
                 ("C_scales", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
                 ("fused", _I32), ("state_mma", _I32), ("y_groups", _I32), ("y_group_of", _P),
-                ("y_scales", _P), ("y_bias", _P)]
+                ("y_scales", _P), ("y_bias", _P), ("intra_mma", _I32)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -350,7 +350,7 @@ def _y_out_fields(y, nch, y_group_of, y_scales, y_bias):
 
 def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, chunk, y,
              Dskip=None, h0=None, h_last=None, state_mma=QSSM_MMA_F16, y_group_of=None,
-             y_scales=None, y_bias=None):
+             y_scales=None, y_bias=None, intra_mma=QSSM_MMA_F16):
     """y is float32, float16 or int8 (then y_group_of [nh * P], y_scales [Gy] and the optional
     correction y_bias [nh * P] are given)."""
     torch = _t()
@@ -371,7 +371,7 @@ def ssd_args(xq, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs,
                  C_scales=_ptr(C_scales, torch.float32, "C_scales"),
                  h0=_ptr(h0, torch.float32, "h0", True), y=_ptr(y, None, "y"), y_dtype=ydt,
                  h_last=_ptr(h_last, torch.float32, "h_last", True), fused=0,
-                 state_mma=state_mma)
+                 state_mma=state_mma, intra_mma=intra_mma)
 
 
 def qssm_ssd_workspace_size(args):

@@ -85,6 +85,7 @@ struct SsdParams {
   const float* y_scales;      // int8 output: [Gy]
   const float* y_bias;        // int8 output: [nh * P] or NULL
   float* syt;                 // [nh, P]: output scale of each channel (written by K1, read by K2)
+  int32_t intra8;             // int8 intra-chunk output (row-requantized weights, int8 MFMA)
 };
 
 __device__ __forceinline__ float valid_or_zero(float s) { return scale_ok(s) ? s : 0.0f; }
@@ -474,7 +475,12 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
 struct K2Smem {
   int8_t qB[kQ * kRow128];  // B chunk rows [j][n]
   int8_t qC[kQ * kRow128];  // C chunk rows [i][n]
-  _Float16 xT[kP * kXtRow];  // x codes of the head, [p][j] (exact in fp16)
+  // x codes of the head, [p][j]: fp16 (exact) for the fp16 intra-chunk product, int8 rows of
+  // kRow256 bytes for the int8 one
+  union {
+    _Float16 xT[kP * kXtRow];
+    int8_t xT8[kP * kRow256];
+  };
   // The entering state of heads hh (buffer hh % 2) as stored by K1: the inter-chunk product's B
   // operands, 1 KB per (column tile, K block); the next head's arrives by direct loads while the
   // current head's is read.
@@ -497,6 +503,7 @@ struct K2Smem {
   float syb[kP];
   float stad;  // staged D_h
   float dh;    // D_h of the current head
+  float sig[8][32];  // int8 intra-chunk output: row scales of each wave's query block
 };
 static_assert(offsetof(K2Smem, stcum) % 16 == 0 && offsetof(K2Smem, cum) % 16 == 0 &&
                   offsetof(K2Smem, dtv) % 16 == 0 &&
@@ -539,18 +546,16 @@ __device__ __forceinline__ GTile pack_g(const v16f& G) {
   return t;
 }
 
-// M tile = G o exp(cum_i - cum_j) [j <= i] o delta_j as two fp16 A operands (k-slots follow the
-// accumulator rows of G, see the B operand gather below). Register r of lane l holds column
+// Decay factors of tile (I, J): f[r] = exp(cum_i - cum_j) delta_j [j <= i] in the order of the G
+// accumulator: register r of lane l holds row i = 32 I + l % 32 and column
 // j = 32 J + 4 (l / 32) + 8 (r / 4) + r % 4, so the column terms come in runs of four (16-byte
-// reads, the same address for each half-wave). Each element is one mixed-precision fma from the
-// fp16 G value, rounded once to fp16.
-__device__ __forceinline__ void m_tile(const GTile& Gt, const K2Smem& s, int I, int J, int lane,
-                                       v8h& a0, v8h& a1) {
+// reads, the same address for each half-wave).
+__device__ __forceinline__ void tile_factors(const K2Smem& s, int I, int J, int lane,
+                                             float (&f)[16]) {
   typedef float v4f __attribute__((ext_vector_type(4)));
   const int i = I * 32 + (lane & 31);  // this lane's query row
   const int jb = J * 32 + 4 * (lane >> 5);
   const float ci = s.cum[i];
-  float f[16];
   if (J < I) {
     // both factors are at most 1 (cum does not increase): no overflow for long decays
     const float ri = __expf(ci - s.cum[J * 32 + 31]);
@@ -574,11 +579,31 @@ __device__ __forceinline__ void m_tile(const GTile& Gt, const K2Smem& s, int I, 
       }
     }
   }
+}
+
+// M tile = G o exp(cum_i - cum_j) [j <= i] o delta_j as two fp16 A operands (k-slots follow the
+// accumulator rows of G, see the B operand gather below). Each element is one mixed-precision fma
+// from the fp16 G value, rounded once to fp16.
+__device__ __forceinline__ void m_tile(const GTile& Gt, const K2Smem& s, int I, int J, int lane,
+                                       v8h& a0, v8h& a1) {
+  float f[16];
+  tile_factors(s, I, J, lane, f);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     a0[e] = (_Float16)fmaf((float)Gt.lo[e], f[e], 0.0f);
     a1[e] = (_Float16)fmaf((float)Gt.hi[e], f[8 + e], 0.0f);
   }
+}
+
+// int8 B operand of the int8 intra-chunk product (K = 32, the whole tile column block J): lane l
+// supplies column p and, as bytes 4 q + k, the x codes of j = 32 J + 4 (l / 32) + 8 q + k, the
+// column order of the A operand (the G accumulator order, byte r for register r).
+__device__ __forceinline__ v4i x8_operand(const K2Smem& s, int J, int pt, int lane) {
+  const int8_t* row = s.xT8 + (pt * 32 + (lane & 31)) * kRow256 + J * 32 + 4 * (lane >> 5);
+  v4i o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = *reinterpret_cast<const int*>(row + 8 * q);
+  return o;
 }
 
 // x B operand for MFMA mm of tile column block J: lane l supplies column p and the 8 j's whose G
@@ -661,6 +686,12 @@ __device__ __forceinline__ void stage_head(const SsdParams& p, K2Smem& s, int64_
 // on one SIMD (v and v + 4) hold blocks s and 7 - s: 9 causal tiles per SIMD. A wave keeps the
 // G tiles (I, J <= I) of its block in registers and produces all 64 output columns of it. Each
 // head's inputs arrive in LDS by direct loads issued during the previous head's products.
+// I8I: the intra-chunk product on int8 MFMA. Each query row's weights W[i, j] = G exp(cum_i -
+// cum_j) delta_j are requantized with the row's own scale (m_i = max_j |W[i, j]|, codes
+// rint(W * 127 / m_i) in [-127, 127]); int8 MFMA against the x codes with int32 accumulate over
+// the whole row, then m_i / 127 per row. W is formed from the fp16 G tiles kept in registers (as
+// for the fp16 product), and the row maximum takes a first pass over the row's tiles.
+template <bool I8I>
 __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   K2Smem& s = *reinterpret_cast<K2Smem*>(smem_raw);
@@ -708,8 +739,9 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   // the C codes of this wave's query block as fp16 A operands of the inter-chunk product (the
   // same for every head), in the K order of the stored entering state: slot m of lane half kh in
   // K block ks is state n = 16 ks + 4 kh + (m < 4 ? m : m + 4)
-  v8h QC[kN / 16];
-  {
+  // (the int8 intra-chunk variant reads them from LDS at each head instead: registers are short)
+  v8h QC[I8I ? 1 : kN / 16];
+  if constexpr (!I8I) {
     const int lane = tid & 63;
     const int I = uniform(uniform(tid >> 6) < 4 ? uniform(tid >> 6) : 11 - uniform(tid >> 6));
     const int8_t* crow = s.qC + (I * 32 + (lane & 31)) * kRow128 + 4 * (lane >> 5);
@@ -763,14 +795,26 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       for (int e = 0; e < 4; ++e) {
         const int pc = p4 * 4 + e;
         const bool on = s.stsx[pc] > 0.0f;
-        _Float16* dst = s.xT + pc * kXtRow + jh * 8;
+        if constexpr (I8I) {
+          // bytes e of the 8 rows, as two words
+          uint32_t w[2];
 #pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-          v4h vv;
+          for (int r4 = 0; r4 < 2; ++r4) {
+            const uint32_t lo = __builtin_amdgcn_perm(raw[4 * r4 + 1], raw[4 * r4], 0x0c0c0400u + 0x00000101u * e);
+            const uint32_t hi = __builtin_amdgcn_perm(raw[4 * r4 + 3], raw[4 * r4 + 2], 0x0c0c0400u + 0x00000101u * e);
+            w[r4] = on ? (lo | (hi << 16)) : 0u;
+          }
+          *reinterpret_cast<uint2*>(s.xT8 + pc * kRow256 + jh * 8) = make_uint2(w[0], w[1]);
+        } else {
+          _Float16* dst = s.xT + pc * kXtRow + jh * 8;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            vv[k] = on ? (_Float16)(float)(int8_t)byte_of(raw[4 * r4 + k], e) : (_Float16)0.0f;
-          *reinterpret_cast<v4h*>(dst + 4 * r4) = vv;
+          for (int r4 = 0; r4 < 2; ++r4) {
+            v4h vv;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              vv[k] = on ? (_Float16)(float)(int8_t)byte_of(raw[4 * r4 + k], e) : (_Float16)0.0f;
+            *reinterpret_cast<v4h*>(dst + 4 * r4) = vv;
+          }
         }
       }
     }
@@ -790,7 +834,15 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     const _Float16* hs = s.sth[hh & 1];
 #pragma unroll
     for (int ks = 0; ks < kN / 16; ++ks) {
-      const v8h a = QC[ks];
+      v8h a;
+      if constexpr (I8I) {
+        const int8_t* crow = s.qC + (I * 32 + (lane & 31)) * kRow128 + 4 * (lane >> 5);
+        const uint32_t lo = *reinterpret_cast<const uint32_t*>(crow + ks * 16);
+        const uint32_t hi = *reinterpret_cast<const uint32_t*>(crow + ks * 16 + 8);
+        a = i8x8_to_h((int64_t)(((uint64_t)hi << 32) | lo));
+      } else {
+        a = QC[ks];
+      }
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const v8h bv = *reinterpret_cast<const v8h*>(hs + ((pt * 8 + ks) * 64 + lane) * 8);
@@ -816,23 +868,87 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
         for (int r = 0; r < 16; ++r) Y[pt][r] *= er[r] * inv;
       }
     }
-    // Y_intra on top, tile by tile
+    if constexpr (!I8I) {
+      // Y_intra on top, tile by tile
 #pragma unroll
-    for (int J = 0; J < 8; ++J) {
-      tile_fence();
-      if (J <= I) {
-        // opaque per head: keeps the fp32 widening of the G tile inside the head loop (hoisted,
-        // the widened copies of all tiles would stay live and spill)
-        __asm__ volatile("" : "+v"(G[J].lo), "+v"(G[J].hi));
-        v8h a0, a1;
-        m_tile(G[J], s, I, J, lane, a0, a1);
+      for (int J = 0; J < 8; ++J) {
+        tile_fence();
+        if (J <= I) {
+          // opaque per head: keeps the fp32 widening of the G tile inside the head loop
+          // (hoisted, the widened copies of all tiles would stay live and spill)
+          __asm__ volatile("" : "+v"(G[J].lo), "+v"(G[J].hi));
+          v8h a0, a1;
+          m_tile(G[J], s, I, J, lane, a0, a1);
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const v8h b0 = x_operand(s, J, 0, pt, lane);
-          const v8h b1 = x_operand(s, J, 1, pt, lane);
-          Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[pt], 0, 0, 0);
-          Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[pt], 0, 0, 0);
+          for (int pt = 0; pt < 2; ++pt) {
+            const v8h b0 = x_operand(s, J, 0, pt, lane);
+            const v8h b1 = x_operand(s, J, 1, pt, lane);
+            Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[pt], 0, 0, 0);
+            Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[pt], 0, 0, 0);
+          }
         }
+      }
+    } else {
+      // opaque per head, as above
+#pragma unroll
+      for (int J = 0; J < 8; ++J)
+        if (J <= I) __asm__ volatile("" : "+v"(G[J].lo), "+v"(G[J].hi));
+      // row maximum of |W| over the row's tiles (lane l and l + 32 hold the two column halves)
+      float mx = 0.0f;
+#pragma unroll
+      for (int J = 0; J < 8; ++J) {
+        tile_fence();
+        if (J <= I) {
+          float f[16];
+          tile_factors(s, I, J, lane, f);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            mx = fmaxf(mx, fabsf(fmaf((float)G[J].lo[r], f[r], 0.0f)));
+            mx = fmaxf(mx, fabsf(fmaf((float)G[J].hi[r], f[8 + r], 0.0f)));
+          }
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float inv = mx > 0.0f ? 127.0f / mx : 0.0f;
+      if (lane < 32) s.sig[v][lane] = mx / 127.0f;
+      v16i acc8[2] = {};
+#pragma unroll
+      for (int J = 0; J < 8; ++J) {
+        tile_fence();
+        if (J <= I) {
+          float f[16];
+          tile_factors(s, I, J, lane, f);
+          // |W * inv| <= 127 (1 + 2^-22): the rounded code is in [-127, 127] without a clamp; it
+          // is packed as the unsigned byte code + 128 and the bias removed from all four bytes
+          v4i a;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int r = 4 * q + k;
+              const float wv = fmaf(r < 8 ? (float)G[J].lo[r] : (float)G[J].hi[r - 8], f[r], 0.0f);
+              w = __builtin_amdgcn_cvt_pk_u8_f32(rintf(wv * inv) + 128.0f, k, w);
+            }
+            a[q] = (int)(w ^ 0x80808080u);
+          }
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt)
+            acc8[pt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, x8_operand(s, J, pt, lane), acc8[pt],
+                                                            0, 0, 0);
+        }
+      }
+      // register r holds row 32 I + 4 (lane / 32) + 8 (r / 4) + r % 4: its scale from the wave's
+      // row scales (written by the lanes that own the rows)
+      typedef float v4f __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f g4 = *reinterpret_cast<const v4f*>(&s.sig[v][4 * (lane >> 5) + 8 * q]);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            Y[pt][4 * q + k] = fmaf(g4[k], (float)acc8[pt][4 * q + k], Y[pt][4 * q + k]);
       }
     }
     tile_fence();
@@ -851,9 +967,18 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       const float Dsx = Dh * sx;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const v4h x4 = *reinterpret_cast<const v4h*>(s.xT + pc * kXtRow + I * 32 + 4 * (lane >> 5) + 8 * q);
+        float xc[4];
+        if constexpr (I8I) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(s.xT8 + pc * kRow256 + I * 32 + 4 * (lane >> 5) + 8 * q);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) yv[pt][4 * q + k] = fmaf(Dsx, (float)x4[k], mult * Y[pt][4 * q + k]);
+          for (int k = 0; k < 4; ++k) xc[k] = (float)(int8_t)byte_of(w, k);
+        } else {
+          const v4h x4 = *reinterpret_cast<const v4h*>(s.xT + pc * kXtRow + I * 32 + 4 * (lane >> 5) + 8 * q);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) xc[k] = (float)x4[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) yv[pt][4 * q + k] = fmaf(Dsx, xc[k], mult * Y[pt][4 * q + k]);
       }
     }
     // register r holds row 32 I + 8 (r / 4) + r % 4 + 4 (lane / 32): buffer stores with the head's
@@ -933,8 +1058,8 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
 // The dynamic-LDS limit of a kernel is raised once per device (hipFuncSetAttribute applies on the
 // current device; two threads racing both make the same idempotent call).
 constexpr int kMaxDevices = 64;
-enum { kAttrK1F16 = 0, kAttrK1I8 = 1, kAttrK2 = 2 };
-std::atomic<bool> g_lds_raised[3][kMaxDevices];
+enum { kAttrK1F16 = 0, kAttrK1I8 = 1, kAttrK2 = 2, kAttrK2I8 = 3 };
+std::atomic<bool> g_lds_raised[4][kMaxDevices];
 
 bool raise_lds_limit(int which, const void* fn, size_t bytes) {
   int dev = 0;
@@ -995,6 +1120,8 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
   if (a->fused != 0) return fail(QSSM_ERR_UNSUPPORTED, "fused must be 0");
   if (a->state_mma != QSSM_MMA_F16 && a->state_mma != QSSM_MMA_I8)
     return fail(QSSM_ERR_INVALID_ARG, "state_mma must be QSSM_MMA_F16 or QSSM_MMA_I8");
+  if (a->intra_mma != QSSM_MMA_F16 && a->intra_mma != QSSM_MMA_I8)
+    return fail(QSSM_ERR_INVALID_ARG, "intra_mma must be QSSM_MMA_F16 or QSSM_MMA_I8");
   if (a->chunk != kQ || a->headdim != kP || a->dstate != kN || a->bc_group_size != kGS)
     return fail(QSSM_ERR_UNSUPPORTED,
                 "the library implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
@@ -1021,7 +1148,7 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
               reinterpret_cast<_Float16*>(base), reinterpret_cast<float*>(base + wl.sx_off),
               reinterpret_cast<float*>(base + wl.cum_off), a->y_dtype == QSSM_I8,
               a->y_dtype == QSSM_I8 ? a->y_groups : 1, a->y_group_of, a->y_scales, a->y_bias,
-              reinterpret_cast<float*>(base + wl.sy_off)};
+              reinterpret_cast<float*>(base + wl.sy_off), a->intra_mma == QSSM_MMA_I8};
   if ((int64_t)B * a->ngroups > 65535 || nc > 0x7fffffff || B * nh > 0x7fffffff)
     return fail(QSSM_ERR_UNSUPPORTED, "grid too large");
   // K1 runs even for an empty sequence: it writes h_last = h0 (or zeros)
@@ -1038,10 +1165,14 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
     if (qssm_status s = launch_status("ssd chunk states")) return s;
   }
   if (nc > 0) {
-    if (!raise_lds_limit(kAttrK2, reinterpret_cast<const void*>(&k_ssd_output), sizeof(K2Smem)))
+    const bool i8 = p.intra8 != 0;
+    const void* k2 = i8 ? reinterpret_cast<const void*>(&k_ssd_output<true>)
+                        : reinterpret_cast<const void*>(&k_ssd_output<false>);
+    if (!raise_lds_limit(i8 ? kAttrK2I8 : kAttrK2, k2, sizeof(K2Smem)))
       return fail(QSSM_ERR_DEVICE, "cannot raise the LDS limit of the SSD output kernel");
     const dim3 grid((unsigned)nc, (unsigned)(B * a->ngroups));
-    k_ssd_output<<<grid, 512, sizeof(K2Smem), stream>>>(p);
+    if (i8) k_ssd_output<true><<<grid, 512, sizeof(K2Smem), stream>>>(p);
+    else k_ssd_output<false><<<grid, 512, sizeof(K2Smem), stream>>>(p);
     if (qssm_status s = launch_status("ssd output")) return s;
   }
   return QSSM_OK;

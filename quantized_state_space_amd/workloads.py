@@ -317,9 +317,10 @@ class SsdLayer:
     chunked SSD."""
 
     def __init__(self, inp, device, chunk=256, gs=16, groups_per_block=8, y_dtype=QSSM_F32,
-                 with_h0=False, state_mma=0, y_out=None):
+                 with_h0=False, state_mma=0, y_out=None, intra_mma=0):
         """y_out = (group_of [nh * P] uint8, scales [Gy] fp32, bias [nh * P] fp32 or None): the
-        layer then writes int8 y codes for the next W8A8 module."""
+        layer then writes int8 y codes for the next W8A8 module. state_mma / intra_mma select
+        int8 MFMA (QSSM_MMA_I8) for the chunk state / the intra-chunk product."""
         import torch
         dev = device
         x = inp["x"]
@@ -355,7 +356,8 @@ class SsdLayer:
         self.h_last = torch.empty((B, nh, P, N), dtype=torch.float32, device=dev)
         self.args = ssd_args(self.xq, self.group_t, self.xs, self.delta, self.A, self.Bq, self.Cq,
                              self.bs, self.cs, gs, chunk, self.y, Dskip=self.D, h0=self.h0,
-                             h_last=self.h_last, state_mma=state_mma, y_group_of=yo[0],
+                             h_last=self.h_last, state_mma=state_mma, intra_mma=intra_mma,
+                             y_group_of=yo[0],
                              y_scales=yo[1], y_bias=yo[2])
         self.ws = torch.empty(max(qssm_ssd_workspace_size(self.args), 1), dtype=torch.uint8,
                               device=dev)
