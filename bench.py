@@ -103,14 +103,16 @@ class Mamba1(Workload):
     # and readout)
     ops_per_update = 5
 
-    def __init__(self, soft_edge=False, y_int8=False, ratio=4, bc_soft_edge=False):
+    def __init__(self, soft_edge=False, y_int8=False, ratio=4, bc_soft_edge=False, time_blocks=0):
         self.soft = soft_edge
         self.y_int8 = y_int8
         self.ratio = ratio
         self.bc_soft = bc_soft_edge
+        self.time_blocks = time_blocks
         self.name = ("mamba1-130m-layer-w8a8" + ("-softedge-x" if soft_edge else "") +
                      ("-shift" if ratio == 2 else "") + ("-softedge-bc" if bc_soft_edge else "") +
-                     ("-int8-y" if y_int8 else ""))
+                     ("-int8-y" if y_int8 else "") +
+                     (f"-{time_blocks}-time-windows" if time_blocks > 1 else ""))
         self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
         self.bound = "alu"
 
@@ -139,8 +141,8 @@ class Mamba1(Workload):
         self.y_out = y_out
         # two copies of every buffer, used in turn, so that one step's 350 MB of traffic cannot be
         # served from the previous step's lines in the 256 MB last-level cache
-        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc, y_out=y_out, bc_code=bc)
-                       for _ in range(2)]
+        self.layers = [wl.Mamba1Layer(self.inp, 8, 4, dev, x_code=xc, y_out=y_out, bc_code=bc,
+                                      time_blocks=self.time_blocks) for _ in range(2)]
         self.k = 0
         B, D, L, N, Gbc = self.layers[0].shape
         self.dims = (B, D, L, N, Gbc)
@@ -217,23 +219,31 @@ class Mamba1(Workload):
 
 
 class Tiny(Mamba1):
-    def __init__(self):
+    """time_blocks: 0 = the library's choice (time windows at this size), 1 = one chain per state
+    in time order."""
+    def __init__(self, time_blocks=0):
         self.soft = False
         self.y_int8 = False
-        self.name = "tiny-mamba1-w8a8"
-        self.dominant = "qssm_scan_w8a8: k_stage_bc + k_scan_m1"
+        self.time_blocks = time_blocks
+        self.name = "tiny-mamba1-w8a8" + ("-chain-form" if time_blocks == 1 else "")
+        self.dominant = ("qssm_scan_w8a8: k_stage_bc + k_scan_m1" if time_blocks == 1 else
+                         "qssm_scan_w8a8: k_stage_bc + k_scan_m1 (window states) + k_scan_carry "
+                         "+ k_scan_m1 (windows)")
         self.bound = "alu"
 
     def setup(self, dev):
         import qssm_synth as synth
         import quantized_state_space_amd.workloads as wl
         self.inp = synth.c1_inputs()
-        self.layers = [wl.Mamba1Layer(self.inp, 1, 4, dev, dynamic_scales=True)]
+        self.layers = [wl.Mamba1Layer(self.inp, 1, 4, dev, dynamic_scales=True,
+                                      time_blocks=self.time_blocks)]
         self.k = 0
         self.dims = self.layers[0].shape
         B, D, L, N, _ = self.dims
         self.config = {"workload": self.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N,
-                       "x_groups": 1, "bc_state_groups": 4, "state": "f32", "y": "f32"}
+                       "x_groups": 1, "bc_state_groups": 4, "state": "f32", "y": "f32",
+                       "scan_form": "chain" if self.time_blocks == 1 else
+                       "library choice (time windows)"}
         self.sample_desc = "full workload, on-device scales"
 
     def oracle_ref(self):
@@ -624,10 +634,11 @@ WORKLOADS = {"c4": lambda: Ssd(False), "c4f16": lambda: Ssd(True),
              "c3": lambda: Mamba1(False),
              "c3se": lambda: Mamba1(True), "c3i8y": lambda: Mamba1(False, True), "c1": Tiny,
              "c3se2bc": lambda: Mamba1(True, ratio=2, bc_soft_edge=True),
+             "c1chain": lambda: Tiny(1), "c3w4": lambda: Mamba1(False, time_blocks=4),
              "c2": lambda: S4d(False), "c2i16": lambda: S4d(True), "c5": lambda: Decode(False),
              "c5f16": lambda: Decode(True), "w4a8d": lambda: W4A8(256), "w4a8p": lambda: W4A8(16384)}
-OTHERS = ("c1", "c2", "c2i16", "c3", "c3se", "c3se2bc", "c3i8y", "c4f16", "c4i8y", "c4i8i", "c5",
-          "c5f16", "w4a8d", "w4a8p")
+OTHERS = ("c1", "c1chain", "c2", "c2i16", "c3", "c3w4", "c3se", "c3se2bc", "c3i8y", "c4f16",
+          "c4i8y", "c4i8i", "c5", "c5f16", "w4a8d", "w4a8p")
 INT8_MFMA_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 
@@ -650,7 +661,7 @@ TRAFFIC = {
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
-    "c3se2bc": ["scan_m1.hip"],
+    "c3se2bc": ["scan_m1.hip"], "c1chain": ["scan_m1.hip"], "c3w4": ["scan_m1.hip"],
     "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"], "c2i16": ["s4d.hip"],
     "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c4i8y": ["ssd.hip"], "c4i8i": ["ssd.hip"],
     "c5": ["state_update.hip"],

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 160 /* 1.6.0: int8 intra-chunk SSD output */
+#define QSSM_VERSION 170 /* 1.7.0: time-windowed Mamba1 scan */
 
 typedef int32_t qssm_status;
 enum {
@@ -187,7 +187,18 @@ qssm_status qssm_softedge_track(const float* x, int64_t outer, int64_t C, int64_
  * B_scales / C_scales as the state groups' base scales; the code of the Quamba-SE blog, sections
  * 2.1-2.2, applied to the input-dependent B and C as well as to x). Bq and Cq then hold those
  * bytes; their thresholds only matter to the encoder.
- * Workspace: qssm_scan_workspace_size bytes (dequantized B and C staging).
+ * Time windows (the scan's second form, an associative scan over time blocks with a carry
+ * between blocks): the recurrence h_t = a_t h_{t-1} + u_t composes over a block of steps into
+ * h_end = (prod a_t) h_start + (the block's state from h_start = 0). With K windows the library
+ * runs every window from 0 in parallel, then runs every window again from its entering state,
+ * which it folds from h0 and the earlier windows' end states in order
+ * (h_in[k + 1] = exp(A * sum of delta over window k) h_in[k] + end[k], per chain), and writes y. This doubles the recurrence work for
+ * K-fold parallelism over time; time_blocks = 0 uses it when batch x channel blocks of 64 are
+ * fewer than 128 (small layers), choosing K for about 256 workgroups. K <= 16, and K <= the
+ * number of 16-step blocks of the sequence. The int8 output (QSSM_I8)
+ * always uses one chain. Results agree with the chain form to fp32 rounding.
+ * Workspace: qssm_scan_workspace_size bytes (dequantized B and C staging, and with windows the
+ * carries: K * B * D * (N + 1) floats).
  */
 typedef struct qssm_scan_args {
   int64_t batch, seqlen, dim, dstate; /* B, L, D, N */
@@ -214,6 +225,8 @@ typedef struct qssm_scan_args {
   const float* y_scales;              /* QSSM_I8: [Gy] static output scales */
   const float* y_bias;                /* QSSM_I8: [D] correction added before quantizing, or NULL */
   int32_t bc_code;                    /* QSSM_X_INT8, QSSM_X_SOFTEDGE or QSSM_X_SOFTEDGE2 */
+  int32_t time_blocks;                /* 0: library choice, 1: one chain per (b, d, n) in time
+                                         order, K >= 2: K time windows (see above) */
 } qssm_scan_args;
 
 size_t qssm_scan_workspace_size(const qssm_scan_args* a);

@@ -36,7 +36,7 @@ class ScanArgs(ctypes.Structure):
                 ("bc_group_size", _I32), ("Bq", _P), ("Cq", _P), ("B_scales", _P), ("C_scales", _P),
                 ("Dskip", _P), ("h0", _P), ("y", _P), ("y_dtype", _I32), ("h_last", _P),
                 ("y_groups", _I32), ("y_group_of", _P), ("y_scales", _P), ("y_bias", _P),
-                ("bc_code", _I32)]
+                ("bc_code", _I32), ("time_blocks", _I32)]
 
 
 class S4dArgs(ctypes.Structure):
@@ -245,10 +245,10 @@ def _fill(st, keep=(), **kw):
 
 def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_scales, gs, y,
               Dskip=None, h0=None, h_last=None, y_group_of=None, y_scales=None, y_bias=None,
-              bc_code=QSSM_X_INT8):
+              bc_code=QSSM_X_INT8, time_blocks=0):
     """Builds ScanArgs for x [B, D, L] codes, Bq/Cq [B, Gbc, N, L] (int8, or uint8 soft-edge bytes
     when bc_code is a soft-edge form). An int8 y takes the output group map, scales and
-    (optional) correction bias."""
+    (optional) correction bias. time_blocks: 0 library choice, 1 chain form, K >= 2 windows."""
     torch = _t()
     B, D, L = x.shape
     N = A.shape[1]
@@ -275,7 +275,8 @@ def scan_args(x, x_code, x_group_of, x_scales, delta, A, Bq, Cq, B_scales, C_sca
                  x_group_of=_ptr(x_group_of, torch.uint8, "x_group_of"),
                  x_scales=_ptr(x_scales, torch.float32, "x_scales"),
                  delta=_ptr(delta, torch.float32, "delta"), A=_ptr(A, torch.float32, "A"),
-                 bc_groups=Gbc, bc_group_size=gs, bc_code=int(bc_code), Bq=_ptr(Bq, bdt, "Bq"),
+                 bc_groups=Gbc, bc_group_size=gs, bc_code=int(bc_code), time_blocks=int(time_blocks),
+                 Bq=_ptr(Bq, bdt, "Bq"),
                  Cq=_ptr(Cq, bdt, "Cq"), B_scales=_ptr(B_scales, torch.float32, "B_scales"),
                  C_scales=_ptr(C_scales, torch.float32, "C_scales"),
                  Dskip=_ptr(Dskip, torch.float32, "Dskip", True),

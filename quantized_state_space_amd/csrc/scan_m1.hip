@@ -31,6 +31,7 @@ constexpr int kT = 16;          // time steps per block
 constexpr int kPadRows = 64;    // zero rows after L in every staged plane (>= kT + largest batch)
 constexpr int kLanes = 64;      // channels per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxWindows = 16;  // time windows of the scan's window form, at most
 
 typedef const uint32_t __attribute__((address_space(4))) cu32;  // constant (scalar-loadable) memory
 
@@ -54,6 +55,14 @@ struct ScanParams {
   const float* y_scales;      // int8 output: [Gy] static output scales
   const float* y_bias;        // int8 output: [D] correction term, or NULL
   float se_m, se_im;          // soft-edge x: mode ratio (4 or 2) and its reciprocal
+  // Time windows (blockIdx.z = window k covers steps [k Lw, min(L, (k + 1) Lw))):
+  //   phase 1: each window from h = 0, no y; writes its end state and its delta sum;
+  //   phase 2: each window from its entering state, folded from h0 and the earlier windows' end
+  //            states, with y; the last window writes h_last.
+  int64_t Lw;
+  int32_t phase;
+  float* carry;  // [K, B, D, N] window end states from zero (real units)
+  float* dsum;   // [K, B, D] sum of delta over each window
 };
 
 enum { kYF32 = 0, kYF16 = 1, kYI8 = 2 };  // output forms of the scan
@@ -124,7 +133,7 @@ __device__ __forceinline__ float xunit(uint32_t byte, float m, float im) {
   return (float)(int8_t)(byte & 0xFFu);
 }
 
-template <int NS, int W, int XCODE, int YOUT, int kBatch, int PFD, bool CODE16>
+template <int NS, int W, int XCODE, int YOUT, int kBatch, int PFD, bool CODE16, bool WIN>
 __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   __shared__ float ybuf[2][W][kT][kLanes];
   constexpr int kS = CODE16 ? NS : 2 * NS;  // staged 32-bit words per step
@@ -202,13 +211,40 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     yb = p.y_bias ? p.y_bias[dc] : 0.0f;
   }
 
+  // WIN = false: the chain form (phase 0, steps [0, L)); true: phases 1 and 2 on window
+  // blockIdx.z
+  const int64_t kw = WIN ? (int64_t)blockIdx.z : 0;
+  const int64_t tbeg = WIN ? kw * p.Lw : 0;
+  const int64_t tend = WIN ? ((tbeg + p.Lw < L) ? tbeg + p.Lw : L) : L;
+  const bool local = WIN && p.phase == 1;  // window end states only
   float a2[NS], h[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const int n = w * NS + k;
     a2[k] = p.A[dc * p.N + n] * kLog2e;
-    h[k] = p.h0 ? ldexpf(p.h0[(b * p.D + dc) * p.N + n] / sum_, -se) : 0.0f;
+    if (!WIN) {
+      h[k] = p.h0 ? ldexpf(p.h0[(b * p.D + dc) * p.N + n] / sum_, -se) : 0.0f;
+    } else if (local) {
+      h[k] = 0.0f;
+    } else {
+      // entering state of window kw: h0 carried through the earlier windows, window k2 scaling
+      // it by exp(A * its delta sum) and adding its end state from zero
+      // (at most kMaxWindows terms, all loads issued before the dependent chain)
+      float hv = p.h0 ? p.h0[(b * p.D + dc) * p.N + n] : 0.0f;
+      float ds[kMaxWindows], ce[kMaxWindows];
+#pragma unroll
+      for (int k2 = 0; k2 < kMaxWindows; ++k2) {
+        const int64_t kk = k2 < kw ? k2 : 0;
+        ds[k2] = p.dsum[(kk * p.B + b) * p.D + dc];
+        ce[k2] = p.carry[((kk * p.B + b) * p.D + dc) * p.N + n];
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < kMaxWindows; ++k2)
+        if (k2 < kw) hv = fmaf(__builtin_amdgcn_exp2f(a2[k] * ds[k2]), hv, ce[k2]);
+      h[k] = ldexpf(hv / sum_, -se);
+    }
   }
+  float dacc = 0.0f;  // phase 1: sum of delta over the window
 
   const float* __restrict__ drow = p.delta + (b * p.D + dc) * L;
   const uint8_t* __restrict__ xrow = reinterpret_cast<const uint8_t*>(p.x) + (b * p.D + dc) * L;
@@ -278,8 +314,8 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
   for (int k = 0; k < kT; ++k) dlB[k] = 0.0f;
 #pragma unroll
   for (int k = 0; k < kT / 4; ++k) xqB[k] = 0u;
-  load_block(0, dlA, xqA);
-  sload(0, bcur);
+  load_block(tbeg, dlA, xqA);
+  sload(tbeg, bcur);
   // decoded x units of the next block, this wave's share, into LDS buffer nb
   auto share_x = [&](const uint32_t (&codes)[kT / 4], int nb) {
     if (kShareX) {
@@ -335,7 +371,11 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     // loads in flight during this block's arithmetic)
 #pragma unroll
     for (int k = 0; k < kT / 4; ++k) xq[k] &= xmask;
-    if (tb + kT < L) load_block(tb + kT, dn, xn);
+    if (tb + kT < tend) load_block(tb + kT, dn, xn);
+    if (local) {
+#pragma unroll
+      for (int k = 0; k < kT; ++k) dacc += dl[k];
+    }
     // Pull the staged rows of the block PFD blocks ahead into L2 with one vector load per
     // 128-byte line, so that the scalar loads of that block hit L2 instead of going to memory.
     // The loaded value is only consumed (without use) after this block's arithmetic.
@@ -388,8 +428,9 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
         for (int j = 0; j < kS; ++j) bcur[s2][j] = bnxt[s2][j];
     }
     if (PFD > 0) asm volatile("" ::"v"(pf));
-    if (kShareX && tb + kT < L) share_x(xn, buf ^ 1);
+    if (kShareX && tb + kT < tend) share_x(xn, buf ^ 1);
     __syncthreads();
+    if (local) return;
 
     // combine: wave w finalizes steps [w*kT/W, (w+1)*kT/W) of every channel of the block
     constexpr int kPer = kT / W;
@@ -445,9 +486,9 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
       }
     }
   };
-  for (int64_t tb = 0; tb < L; tb += 2 * kT) {
+  for (int64_t tb = tbeg; tb < tend; tb += 2 * kT) {
     block(tb, dlA, dlB, xqA, xqB, 0);
-    if (tb + kT < L) block(tb + kT, dlB, dlA, xqB, xqA, 1);
+    if (tb + kT < tend) block(tb + kT, dlB, dlA, xqB, xqA, 1);
   }
   if (kGather && L > 0) {
     // the last (possibly partial) group
@@ -455,17 +496,28 @@ __global__ __launch_bounds__(64 * W) void k_scan_m1(ScanParams p) {
     flush_codes((L - 1) / (kGrpBlocks * kT));
   }
 
-  if (valid && p.h_last) {
+  if (valid && p.h_last && (!WIN || (!local && kw == (int64_t)gridDim.z - 1))) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) p.h_last[(b * p.D + d) * p.N + w * NS + k] = ldexpf(h[k] * sum_, se);
+  }
+  if (valid && local) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      p.carry[((kw * p.B + b) * p.D + d) * p.N + w * NS + k] = ldexpf(h[k] * sum_, se);
+    if (w == 0) p.dsum[(kw * p.B + b) * p.D + d] = dacc;
   }
 }
 
 template <int NS, int W, int BATCH, bool CODE16, int XCODE>
 void launch_scan_x(const ScanParams& p, int yout, dim3 grid, dim3 block, hipStream_t st) {
-  if (yout == kYF16) k_scan_m1<NS, W, XCODE, kYF16, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
-  else if (yout == kYI8) k_scan_m1<NS, W, XCODE, kYI8, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
-  else k_scan_m1<NS, W, XCODE, kYF32, BATCH, 1, CODE16><<<grid, block, 0, st>>>(p);
+  if (grid.z > 1) {  // time windows (never with the int8 output)
+    if (yout == kYF16) k_scan_m1<NS, W, XCODE, kYF16, BATCH, 1, CODE16, true><<<grid, block, 0, st>>>(p);
+    else k_scan_m1<NS, W, XCODE, kYF32, BATCH, 1, CODE16, true><<<grid, block, 0, st>>>(p);
+    return;
+  }
+  if (yout == kYF16) k_scan_m1<NS, W, XCODE, kYF16, BATCH, 1, CODE16, false><<<grid, block, 0, st>>>(p);
+  else if (yout == kYI8) k_scan_m1<NS, W, XCODE, kYI8, BATCH, 1, CODE16, false><<<grid, block, 0, st>>>(p);
+  else k_scan_m1<NS, W, XCODE, kYF32, BATCH, 1, CODE16, false><<<grid, block, 0, st>>>(p);
 }
 
 template <int NS, int W, int BATCH, bool CODE16>
@@ -477,8 +529,9 @@ void launch_scan_t(const ScanParams& p, int xcode, int yout, dim3 grid, dim3 blo
 // BATCH16 / BATCH32: steps per scalar-load batch with fp16 codes / fp32 values staged (two
 // batches of kS words per step must fit the SGPR budget next to the kernel's other scalars)
 template <int NS, int W, int BATCH16, int BATCH32>
-qssm_status launch_scan(const ScanParams& p, int xcode, int yout, bool code16, hipStream_t st) {
-  dim3 grid((unsigned)cdiv(p.D, kLanes), (unsigned)p.B);
+qssm_status launch_scan(const ScanParams& p, int xcode, int yout, bool code16, int nwin,
+                        hipStream_t st) {
+  dim3 grid((unsigned)cdiv(p.D, kLanes), (unsigned)p.B, (unsigned)nwin);
   dim3 block(64 * W);
   if (code16) launch_scan_t<NS, W, BATCH16, true>(p, xcode, yout, grid, block, st);
   else launch_scan_t<NS, W, BATCH32, false>(p, xcode, yout, grid, block, st);
@@ -493,14 +546,67 @@ size_t stage_bytes(const qssm_scan_args* a) {
          (size_t)(a->seqlen + kPadRows) * 2 * sizeof(float);
 }
 
+// Time windows of the scan: (count, length). One window is the chain form. More windows cut each
+// chain into pieces that run in parallel (each piece's end state from zero; then each piece again
+// from its entering state, which it folds from h0 and the earlier pieces' end states): twice the
+// recurrence arithmetic, for parallelism when batch x channel blocks leave the GPU mostly idle. time_blocks = 0 chooses:
+// windows when fewer than kWindowWgs channel blocks exist, enough for about 2 x kWindowWgs
+// workgroups; time_blocks = 1 forces the chain form, K >= 2 asks for K windows (at most
+// kMaxWindows; fewer when the sequence has fewer 16-step blocks). The int8 output
+// always uses the chain form (its codes are gathered over 128-step groups of the chain).
+constexpr int64_t kWindowWgs = 128;
+
+struct Windows {
+  int64_t count, len;
+};
+
+Windows scan_windows(const qssm_scan_args* a) {
+  const int64_t L = a->seqlen;
+  const int64_t blocks = (L + kT - 1) / kT;
+  int64_t K = 1;
+  if (a->y_dtype != QSSM_I8 && blocks >= 2) {
+    if (a->time_blocks >= 2) {
+      K = a->time_blocks;
+    } else if (a->time_blocks == 0) {
+      const int64_t wgs = (a->dim + kLanes - 1) / kLanes * a->batch;
+      if (wgs < kWindowWgs) K = (2 * kWindowWgs + wgs - 1) / (wgs > 0 ? wgs : 1);
+    }
+  }
+  if (K > blocks) K = blocks;
+  if (K > kMaxWindows) K = kMaxWindows;
+  if (K < 2) return Windows{1, L};
+  const int64_t len = ((L + K - 1) / K + kT - 1) / kT * kT;
+  return Windows{(L + len - 1) / len, len};
+}
+
+// Workspace: the B/C staging, then (with windows) the carries [K, B, D, N] and the window delta
+// sums [K, B, D], each 256-byte aligned.
+struct ScanWs {
+  size_t carry_off, dsum_off, total;
+};
+
+ScanWs scan_ws(const qssm_scan_args* a) {
+  const Windows win = scan_windows(a);
+  ScanWs w;
+  w.carry_off = (stage_bytes(a) + 255) & ~(size_t)255;
+  w.dsum_off = w.carry_off;
+  w.total = stage_bytes(a);
+  if (win.count > 1) {
+    const size_t nc = (size_t)win.count * a->batch * a->dim;
+    w.dsum_off = (w.carry_off + nc * a->dstate * sizeof(float) + 255) & ~(size_t)255;
+    w.total = w.dsum_off + nc * sizeof(float);
+  }
+  return w;
+}
+
 constexpr size_t kScanScratchBytes = (size_t)QSSM_SCAN_SCRATCH_BYTES;
 
-// Validation, B/C staging and the scan launch; `stage` is 256-byte aligned and holds
-// stage_bytes(a) bytes (it may be null when that is 0).
-qssm_status scan_impl(const qssm_scan_args* a, void* stage_mem, hipStream_t stream) {
+// Validation, B/C staging and the scan launch; `ws` is 256-byte aligned and holds
+// scan_ws(a).total bytes (it may be null when that is 0).
+qssm_status scan_impl(const qssm_scan_args* a, void* ws, hipStream_t stream) {
   const int64_t B = a->batch, L = a->seqlen, D = a->dim, N = a->dstate;
   const int64_t dpg = D / a->bc_groups;
-  float* stage = reinterpret_cast<float*>(stage_mem);
+  float* stage = reinterpret_cast<float*>(ws);
   const int ns = states_per_wave(N);
   // fp16 codes when every wave's states lie inside one B/C state group
   const bool code16 = (a->bc_group_size % ns) == 0;
@@ -518,20 +624,32 @@ qssm_status scan_impl(const qssm_scan_args* a, void* stage_mem, hipStream_t stre
           ns, bse, bm, bim, stage);
     if (qssm_status s = launch_status("scan_w8a8 staging")) return s;
   }
-
+  const Windows win = scan_windows(a);
+  const ScanWs wl = scan_ws(a);
+  char* wsb = reinterpret_cast<char*>(ws);
   ScanParams p{B, L, D, N, a->x_groups, a->bc_groups, a->bc_group_size, (int32_t)dpg,
                a->y_dtype == QSSM_I8 ? a->y_groups : 1,
                a->x, a->x_group_of, a->x_scales, a->delta, a->A, stage, a->B_scales,
                a->C_scales, a->Dskip, a->h0, a->y, a->h_last, a->y_group_of, a->y_scales,
-               a->y_bias, softedge_ratio(a->x_code), 1.0f / softedge_ratio(a->x_code)};
+               a->y_bias, softedge_ratio(a->x_code), 1.0f / softedge_ratio(a->x_code),
+               win.len, 0, win.count > 1 ? reinterpret_cast<float*>(wsb + wl.carry_off) : nullptr,
+               win.count > 1 ? reinterpret_cast<float*>(wsb + wl.dsum_off) : nullptr};
   const int yout = a->y_dtype == QSSM_F16 ? kYF16 : (a->y_dtype == QSSM_I8 ? kYI8 : kYF32);
-  switch (N) {
-    case 4: return launch_scan<4, 1, 8, 8>(p, a->x_code, yout, code16, stream);
-    case 8: return launch_scan<2, 4, 16, 16>(p, a->x_code, yout, code16, stream);
-    case 16: return launch_scan<4, 4, 8, 8>(p, a->x_code, yout, code16, stream);
-    case 32: return launch_scan<4, 8, 8, 8>(p, a->x_code, yout, code16, stream);
-    default: return launch_scan<8, 8, 4, 4>(p, a->x_code, yout, code16, stream);
-  }
+  auto run = [&](const ScanParams& q, int nwin) -> qssm_status {
+    switch (N) {
+      case 4: return launch_scan<4, 1, 8, 8>(q, a->x_code, yout, code16, nwin, stream);
+      case 8: return launch_scan<2, 4, 16, 16>(q, a->x_code, yout, code16, nwin, stream);
+      case 16: return launch_scan<4, 4, 8, 8>(q, a->x_code, yout, code16, nwin, stream);
+      case 32: return launch_scan<4, 8, 8, 8>(q, a->x_code, yout, code16, nwin, stream);
+      default: return launch_scan<8, 8, 4, 4>(q, a->x_code, yout, code16, nwin, stream);
+    }
+  };
+  if (win.count == 1) return run(p, 1);
+  const int K = (int)win.count;
+  p.phase = 1;
+  if (qssm_status s = run(p, K)) return s;
+  p.phase = 2;
+  return run(p, K);
 }
 
 // Argument checks shared by both entry points; QSSM_OK means "launch", and *done is set when the
@@ -616,8 +734,9 @@ qssm_status scratch_address(void** out) {
 extern "C" {
 
 size_t qssm_scan_workspace_size(const qssm_scan_args* a) {
-  if (!a || a->batch < 0 || a->seqlen < 0 || a->bc_groups < 1 || a->dstate < 1) return 0;
-  return stage_bytes(a) + 256;
+  if (!a || a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->bc_groups < 1 || a->dstate < 1)
+    return 0;
+  return scan_ws(a).total + 256;
 }
 
 qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
@@ -626,7 +745,7 @@ qssm_status qssm_scan_w8a8(const qssm_scan_args* a, void* ws, size_t ws_bytes,
   bool done = false;
   if (qssm_status s = validate(a, &done)) return s;
   if (done) return QSSM_OK;
-  const size_t need = stage_bytes(a);
+  const size_t need = scan_ws(a).total;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QSSM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   void* stage = reinterpret_cast<void*>(((uintptr_t)ws + 255) & ~(uintptr_t)255);
@@ -640,11 +759,11 @@ qssm_status qssm_scan_w8a8_noalloc(const qssm_scan_args* a, hipStream_t stream) 
   bool done = false;
   if (qssm_status s = validate(a, &done)) return s;
   if (done) return QSSM_OK;
-  const size_t need = stage_bytes(a);
+  const size_t need = scan_ws(a).total;
   if (need > kScanScratchBytes)
     return fail(QSSM_ERR_UNSUPPORTED,
-                "the B/C staging needs %zu bytes, above the %zu-byte scratch array of the "
-                "allocation-free entry point", need, kScanScratchBytes);
+                "the scan needs %zu bytes of scratch (B/C staging and window carries), above the "
+                "%zu-byte array of the allocation-free entry point", need, kScanScratchBytes);
   void* stage = nullptr;
   if (qssm_status s = scratch_address(&stage)) return s;
   return scan_impl(a, stage, stream);

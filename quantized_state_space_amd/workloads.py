@@ -94,7 +94,7 @@ class Mamba1Layer:
 
     def __init__(self, inp, G, gs, device, x_code=QSSM_X_INT8, dynamic_scales=False,
                  y_dtype=QSSM_F32, with_h0=False, perm=True, y_out=None, bc_code=QSSM_X_INT8,
-                 track=False):
+                 track=False, time_blocks=0):
         """y_out = (group_of [D] uint8, scales [Gy] fp32, bias [D] fp32 or None), in the layer's
         channel order: the scan then writes int8 y codes for the next W8A8 module.
         x_code / bc_code: int8 or a soft-edge form (QSSM_X_SOFTEDGE, QSSM_X_SOFTEDGE2) for x and
@@ -171,7 +171,7 @@ class Mamba1Layer:
         self.args = scan_args(self.xq, x_code, self.group_t, self.xs, self.delta, self.A, self.Bq,
                               self.Cq, self.bs, self.cs, gs, self.y, Dskip=self.D, h0=self.h0,
                               h_last=self.h_last, y_group_of=yo[0], y_scales=yo[1], y_bias=yo[2],
-                              bc_code=bc_code)
+                              bc_code=bc_code, time_blocks=time_blocks)
         self.ws = torch.empty(qssm_scan_workspace_size(self.args), dtype=torch.uint8, device=dev)
 
     def quantize(self):

@@ -64,13 +64,14 @@ def test_c1_tiny_dynamic_scales(dev):
                                                 (1, 64, 70, 16, 2, False, 16),
                                                 (2, 130, 301, 16, 4, True, 4),
                                                 (1, 70, 99, 16, 3, True, 1)])
-def test_ragged_shapes_static_scales(dev, B, D, L, N, G, soft, gs):
-    print(f"\n[mamba1 B={B} D={D} L={L} N={N} G={G} softedge={soft} gs={gs}]", flush=True)
+@pytest.mark.parametrize("tb", [0, 1])  # the library's choice (time windows here), the chain form
+def test_ragged_shapes_static_scales(dev, B, D, L, N, G, soft, gs, tb):
+    print(f"\n[mamba1 B={B} D={D} L={L} N={N} G={G} softedge={soft} gs={gs} tb={tb}]", flush=True)
     import quantized_state_space_amd as qs
     inp = synth.mamba1_inputs(cfg=11, batch=B, seqlen=L, dim=D, dstate=N, x_dist="student_t",
                               calib_batch=1, with_h0=True)
     xc = qs.QSSM_X_SOFTEDGE if soft else qs.QSSM_X_INT8
-    lay = layer(dev, inp, G=G, gs=gs, x_code=xc, with_h0=True)
+    lay = layer(dev, inp, G=G, gs=gs, x_code=xc, with_h0=True, time_blocks=tb)
     lay.step()
     ref = op.mamba1(inp, G=G, gs=gs, soft_edge=soft, with_h0=True)
     if soft:
