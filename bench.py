@@ -36,10 +36,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# fp32 VALU issue rate of MI355X without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-# (lane-instructions per second; an FMA counts once). The recurrences' instruction mix (an exp per
-# update, dependent FMAs) is compiled without packed fp32 instructions.
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# fp32 vector peak of MI355X as lane-operations per second: the published 157.3 TFLOP/s counts a
+# fused multiply-add as two flops, so 78.6 T FMA lane-ops/s (256 CUs x 4 SIMDs x 32 lanes per clock
+# x 2.4 GHz). The instruction-rate probe measures plain (unpacked) v_fma_f32 above the 16-lane
+# figure (256 x 4 x 16 x 2.4 GHz = 39.3 T/s), so that figure is no ceiling; v_exp_f32 issues at
+# about a quarter of the FMA rate.
+VALU_PEAK_TOPS = 157.3 / 2
 METRIC = "quantized scan state-updates/s (B·L·D·N) + % of HBM peak, 1 MI355X"
 
 
@@ -816,6 +818,49 @@ def run_workload(torch, dev, name, steps, warmup, budget_s, with_baseline=True):
     return wl, res
 
 
+def probe_row(torch, dev, reps=5):
+    """Instruction-rate loops (qssm_probe_rate): v_exp_f32 alone, v_fma_f32 alone, both
+    interleaved (whether the exp co-issues with FMA), and the dense int8 / fp16 MFMA rates,
+    event-timed, median of reps, against the peaks used for the rooflines."""
+    import quantized_state_space_amd as qs
+    blocks, iters, miters = 2048, 4096, 128
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    lanes = blocks * 256
+    kinds = {"exp": (qs.QSSM_PROBE_EXP, iters, lanes * iters * 8, "T v_exp_f32/s",
+                     VALU_PEAK_TOPS),
+             "fma": (qs.QSSM_PROBE_FMA, iters, lanes * iters * 8, "T v_fma_f32/s", VALU_PEAK_TOPS),
+             "exp_plus_fma": (qs.QSSM_PROBE_EXP_FMA, iters, lanes * iters * 16,
+                              "T VALU instructions/s (half exp, half fma)", VALU_PEAK_TOPS),
+             "mfma_i8": (qs.QSSM_PROBE_MFMA_I8, miters, blocks * 4 * miters * 2 * 32768 * 2,
+                         "T int8 ops/s", INT8_MFMA_PEAK_TOPS),
+             "mfma_f16": (qs.QSSM_PROBE_MFMA_F16, miters, blocks * 4 * miters * 2 * 16384 * 2,
+                          "T fp16 flops/s", FP16_MFMA_PEAK_TFLOPS)}
+    out = {}
+    for name, (kind, iters, ops, unit, peak) in kinds.items():
+        qs.qssm_probe_rate(kind, iters, blocks, sink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            qs.qssm_probe_rate(kind, iters, blocks, sink)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        t = float(np.median(ts))
+        rate = ops / t / 1e12
+        out[name] = {"rate": round(rate, 2), "unit": unit, "of_peak": round(rate / peak, 3),
+                     "us": round(t * 1e6, 1)}
+    out["exp_co_issues_with_fma"] = bool(out["exp_plus_fma"]["us"] <
+                                         0.9 * (out["exp"]["us"] + out["fma"]["us"]))
+    out["note"] = (f"{blocks} workgroups x 256 threads; VALU peak {VALU_PEAK_TOPS:.1f} T "
+                   "lane-ops/s (the published fp32 vector 157.3 TFLOP/s, an FMA as one op); "
+                   "MFMA peaks dense")
+    return out
+
+
 def quantizer_row(torch, dev, reps=20):
     """The x quantizers alone on the Mamba1-130M x (8 x 1536 x 2048, cluster gather, 8 groups):
     int8 and soft-edge encode on the same bytes, event-timed, codes checked against the oracle."""
@@ -960,6 +1005,7 @@ def main():
                 del w2
                 torch.cuda.empty_cache()
             others["quantizers"] = quantizer_row(torch, dev)
+            others["instruction_rates"] = probe_row(torch, dev)
             out["other_configs"] = others
     except ParityError as e:
         print(json.dumps({"error": "parity gate failed", "detail": str(e)}), file=sys.stderr,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QSSM_VERSION 170 /* 1.7.0: time-windowed Mamba1 scan */
+#define QSSM_VERSION 180 /* 1.8.0: instruction-rate probes */
 
 typedef int32_t qssm_status;
 enum {
@@ -508,6 +508,21 @@ int32_t qssm_version(void);
 /* sizeof of the argument structs as compiled (0: scan, 1: s4d, 2: ssd, 3: update, 4: gemm), so
  * bindings can check their layout. Returns 0 for an unknown kind. */
 size_t qssm_args_size(int32_t kind);
+
+/* ---------------------------------------------------------------------------------------------
+ * Measurement support (not part of the method): instruction-rate loops behind the roofline
+ * figures. `blocks` workgroups of 256 threads each run `iters` iterations of:
+ *   QSSM_PROBE_EXP       8 v_exp_f32 per thread (8 independent chains),
+ *   QSSM_PROBE_FMA       8 v_fma_f32 per thread,
+ *   QSSM_PROBE_EXP_FMA   8 v_exp_f32 and 8 v_fma_f32 per thread (interleaved, independent),
+ *   QSSM_PROBE_MFMA_I8   2 v_mfma_i32_32x32x32_i8 per wave (32768 int8 multiply-adds each),
+ *   QSSM_PROBE_MFMA_F16  2 v_mfma_f32_32x32x16_f16 per wave (16384 fp16 multiply-adds each).
+ * sink (device, blocks * 256 floats) receives values that keep the loops from being removed.
+ * Time the call with events on the stream; rate = operations / time. */
+enum { QSSM_PROBE_EXP = 0, QSSM_PROBE_FMA = 1, QSSM_PROBE_EXP_FMA = 2, QSSM_PROBE_MFMA_I8 = 3,
+       QSSM_PROBE_MFMA_F16 = 4 };
+qssm_status qssm_probe_rate(int32_t kind, int64_t iters, int32_t blocks, float* sink,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

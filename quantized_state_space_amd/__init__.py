@@ -82,6 +82,7 @@ SIGNATURES = {
     "qssm_softedge_encode": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _P, _I32, _P, _P]),
     "qssm_softedge_decode": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P]),
     "qssm_softedge_track_workspace_size": (ctypes.c_size_t, [_I32]),
+    "qssm_probe_rate": (_I32, [_I32, _I64, _I32, _P, _P]),
     "qssm_softedge_track": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, ctypes.c_double, _I32, _P,
                                    _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "qssm_scan_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ScanArgs)]),
@@ -207,6 +208,19 @@ def qssm_softedge_decode(code, group_of, G, s, out, form=QSSM_X_SOFTEDGE, stream
         G, _ptr(s, torch.float32, "s"), int(form), _ptr(out, torch.float32, "out"),
         _stream(stream)))
     return out
+
+
+QSSM_PROBE_EXP, QSSM_PROBE_FMA, QSSM_PROBE_EXP_FMA, QSSM_PROBE_MFMA_I8, QSSM_PROBE_MFMA_F16 = range(5)
+
+
+def qssm_probe_rate(kind, iters, blocks, sink, stream=None):
+    """Instruction-rate loop (measurement support); sink: float32 device tensor of blocks * 256."""
+    torch = _t()
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink must hold blocks * 256 floats")
+    _check("qssm_probe_rate", load().qssm_probe_rate(int(kind), int(iters), int(blocks),
+                                                    _ptr(sink, torch.float32, "sink"),
+                                                    _stream(stream)))
 
 
 def qssm_softedge_track_workspace_size(G):
