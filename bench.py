@@ -652,14 +652,19 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, digest of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c3": (152089444, 132508472, "82855a741382f2d7"),
-    "c2": (374806, 7472096, "a1d2ef04c9625eb6"),
-    "c4": (692105038, 858799064, "1771bfe3189ad294"),
-    "c5": (1100171354, 1082578296, "2d61ee22651a7256"),
-    "c3se": (152357308, 132879688, "82855a741382f2d7"),
-    "c3i8y": (135567360, 27820032, "82855a741382f2d7"),
-    "c4f16": (683357980, 694246608, "1771bfe3189ad294"),
-    "c5f16": (563235239, 545288304, "2d61ee22651a7256"),
+    "c4": (481827754, 696427690, "17c7d36516d2b93e"),
+    "c4f16": (480146005, 427851946, "17c7d36516d2b93e"),
+    "c4i8y": (481443413, 293958741, "17c7d36516d2b93e"),
+    "c4i8i": (480359808, 696290176, "17c7d36516d2b93e"),
+    "c3": (153177301, 134756394, "3cdf3e90c9d61e8b"),
+    "c3se": (156280789, 134674357, "3cdf3e90c9d61e8b"),
+    "c3i8y": (135517269, 27820032, "3cdf3e90c9d61e8b"),
+    "c2": (373760, 7472128, "8dbafe7953cbf0db"),
+    "c2i16": (391168, 6947200, "8dbafe7953cbf0db"),
+    "c5": (1100235776, 1082524586, "3f9c130349ee8131"),
+    "c5f16": (563252224, 545275178, "3f9c130349ee8131"),
+    "w4a8p": (6501291690, 1216348202, "91846fb4969f6afb"),
+    "c1": (1788928, 221184, "3cdf3e90c9d61e8b"),
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
@@ -667,7 +672,7 @@ TRAFFIC_SOURCES = {
     "c3i8y": ["scan_m1.hip"], "c2": ["s4d.hip"], "c2i16": ["s4d.hip"],
     "c4": ["ssd.hip"], "c4f16": ["ssd.hip"], "c4i8y": ["ssd.hip"], "c4i8i": ["ssd.hip"],
     "c5": ["state_update.hip"],
-    "c5f16": ["state_update.hip"],
+    "c5f16": ["state_update.hip"], "w4a8p": ["gemm_w4a8.hip"], "w4a8d": ["gemm_w4a8.hip"],
 }
 
 
