@@ -60,6 +60,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 struct SsdParams {
   int64_t B, L, nh, nc;
@@ -137,12 +138,14 @@ __device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
 //   Then H = exp(cum_last) H + S (fp32, sB and sx applied as two products: their own product
 //   can leave the fp32 range while H does not).
 // Loads run one chunk ahead, into registers (B, x codes, delta), with no wait before their first
-// use; the barriers order LDS only.
+// use; the barriers order LDS only. They go through buffer resources that end with the batch's
+// sequence, so that rows past it read as zero with no clamp or mask.
 constexpr int kXwRow = 264;  // padded halves of a [*][256] fp16 LDS row (528 bytes)
 
 template <bool I8>
 struct K1Smem {
-  int8_t qBT[kN * kRow256];                 // B chunk transposed, [n][j]
+  _Float16 qBh[I8 ? 8 : kN * kXwRow];        // B chunk transposed, [n][j], fp16 (fp16 path)
+  int8_t qBT[I8 ? kN * kRow256 : 16];        // B chunk transposed, [n][j], int8 (I8)
   int8_t rT[I8 ? 2 * kP * kRow256 : 16];    // requantized x per head, [p][j] (I8)
   _Float16 xw[I8 ? 8 : 2 * kP * kXwRow];    // weighted x per head, [p][j] (fp16)
   double ratio[I8 ? 2 * kQ : 1];            // w_j / w_max per head (I8)
@@ -152,39 +155,61 @@ struct K1Smem {
   double shd[16];
 };
 
-// Register loads of the B chunk c of (b, g) for the transposition: thread tid takes rows
-// 16 (tid / 32) .. + 15, bytes 4 (tid % 32) .. + 3. Branch-free: rows past the sequence are clamped
-// to the last valid row and masked by the consumer.
-__device__ __forceinline__ void fetch_b(const SsdParams& p, int64_t b, int g, int64_t c, int tid,
-                                        uint32_t (&bq)[16]) {
-  const int64_t t0 = c * kQ;
-  const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
+// Raw buffer resource over n bytes at ptr (offsets are 32-bit: the host checks that one
+// sequence's codes, steps and deltas stay below 2^31 bytes); loads past n bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void* ptr, int64_t n) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  void* const u = reinterpret_cast<void*>(((uint64_t)(uint32_t)uniform((int)(a >> 32)) << 32) |
+                                          (uint32_t)uniform((int)a));
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)uniform((int)n), kBufferWord3);
+}
+
+// Register loads of the B chunk c of group g for the transposition: thread tid takes rows
+// 16 (tid / 32) .. + 15, bytes 4 (tid % 32) .. + 3. rs covers the batch's [L, Gbc, N] codes.
+__device__ __forceinline__ void fetch_b(const SsdParams& p, __amdgpu_buffer_rsrc_t rs, int g,
+                                        int64_t c, int tid, uint32_t (&bq)[16]) {
   const int ub = tid / (kN / 4), n4 = tid % (kN / 4);
-  const int8_t* bbase = p.Bq + ((b * p.L + t0) * p.Gbc + g) * kN + n4 * 4;
-  const int64_t bstep = (int64_t)p.Gbc * kN;
+  const int bstep = p.Gbc * kN;
+  int voff = ((ub * 16) * p.Gbc + g) * kN + n4 * 4;
+  // opaque per call: the per-row offsets are formed here, one add each, instead of being hoisted
+  // out of the chunk loop (16 registers held across it)
+  __asm__ volatile("" : "+v"(voff));
+  voff += (int)c * kQ * bstep;
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    bq[r] = *reinterpret_cast<const uint32_t*>(bbase + min(ub * 16 + r, q - 1) * bstep);
+  for (int r = 0; r < 16; ++r) {
+    bq[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0);
+    voff += bstep;
+  }
 }
 
 // Register loads of one head's chunk inputs: delta of steps 4 lane .. 4 lane + 3 (every wave holds
 // the whole chunk's delta); x codes of rows 16 (lt / 16) .. + 15, bytes 4 (lt % 16) .. + 3 (lt =
-// thread index within the half). Branch-free: rows past the sequence are clamped to the last
-// valid row and masked by the consumer, so that no wait for the loads is needed before their first
-// use one chunk later.
-__device__ __forceinline__ void fetch_x(const SsdParams& p, int64_t b, int64_t h, int64_t c, int lt,
+// thread index within the half). rx covers the batch's [L, nh, P] codes, rd its [L, nh] deltas.
+__device__ __forceinline__ void fetch_x(const SsdParams& p, __amdgpu_buffer_rsrc_t rx,
+                                        __amdgpu_buffer_rsrc_t rd, int64_t h, int64_t c, int lt,
                                         float (&dt)[4], uint32_t (&x)[16]) {
-  const int64_t t0 = c * kQ;
-  const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
+  const int t0 = (int)c * kQ;
   const int lane = lt & 63;
+  const int nh = (int)p.nh;
+  // opaque per call, as in fetch_b
+  int doff = (4 * lane * nh + (int)h) * 4;
+  __asm__ volatile("" : "+v"(doff));
+  doff += t0 * nh * 4;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) dt[k] = p.delta[(b * p.L + t0 + min(4 * lane + k, q - 1)) * p.nh + h];
+  for (int k = 0; k < 4; ++k) {
+    dt[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, doff, 0, 0));
+    doff += nh * 4;
+  }
   const int jb = lt / 16, p4 = lt % 16;
-  const int8_t* xbase = p.xq + ((b * p.L + t0) * p.nh + h) * kP + p4 * 4;
-  const int64_t xstep = p.nh * kP;
+  const int xstep = nh * kP;
+  int voff = (jb * 16 * nh + (int)h) * kP + p4 * 4;
+  __asm__ volatile("" : "+v"(voff));
+  voff += t0 * xstep;
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    x[r] = *reinterpret_cast<const uint32_t*>(xbase + min(jb * 16 + r, q - 1) * xstep);
+  for (int r = 0; r < 16; ++r) {
+    x[r] = __builtin_amdgcn_raw_buffer_load_b32(rx, voff, 0, 0);
+    voff += xstep;
+  }
 }
 
 template <bool I8>
@@ -250,42 +275,63 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
   // loads at the end of every chunk instead of at their use one chunk later.
   float dtA[4] = {}, dtB[4] = {};
   uint32_t xA[16], xB[16], bA[16], bB[16];
+  const __amdgpu_buffer_rsrc_t rsb = seq_rsrc(p.Bq + b * p.L * p.Gbc * kN, p.L * p.Gbc * kN);
+  const __amdgpu_buffer_rsrc_t rsx = seq_rsrc(p.xq + b * p.L * p.nh * kP, p.L * p.nh * kP);
+  const __amdgpu_buffer_rsrc_t rsd = seq_rsrc(p.delta + b * p.L * p.nh, p.L * p.nh * 4);
+
   if (p.nc > 0) {
-    fetch_b(p, b, g, 0, tid, bA);
-    fetch_x(p, b, h, 0, lt, dtA, xA);
+    fetch_b(p, rsb, g, 0, tid, bA);
+    fetch_x(p, rsx, rsd, h, 0, lt, dtA, xA);
   }
   lds_barrier();  // s.sxp
   auto chunk = [&](const int64_t c, const float (&pf_dt)[4], const uint32_t (&pf_x)[16],
                    const uint32_t (&pf_b)[16], float (&nx_dt)[4], uint32_t (&nx_x)[16],
                    uint32_t (&nx_b)[16]) {
-    const int64_t t0 = c * kQ;
-    const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
-    // B chunk, transposed to [n][j]: unit tid takes rows 16 (tid / 32) .. + 15, bytes
-    // 4 (tid % 32) .. + 3; rows past the sequence are zero
+    // B chunk, transposed to [n][j] (rows past the sequence were loaded as zero): unit tid takes
+    // rows 16 (tid / 32) .. + 15, bytes 4 (tid % 32) .. + 3. The fp16 path stores it as fp16 (the
+    // codes are exact), converted once for both heads; unit n4 writes its four columns starting
+    // at column n4 % 4, which spreads the writes of neighbouring units over the banks.
     {
       const int ub = tid / (kN / 4), n4 = tid % (kN / 4);
-      uint32_t d[16];
+      if constexpr (I8) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) d[r] = (ub * 16 + r < q) ? pf_b[r] : 0u;
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint4*>(s.qBT + (n4 * 4 + e) * kRow256 + ub * 16) = column16(pf_b, e);
+      } else {
+        const int rot = 8 * (n4 & 3);
+        uint32_t d[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint4*>(s.qBT + (n4 * 4 + e) * kRow256 + ub * 16) = column16(d, e);
+        for (int r = 0; r < 16; ++r) d[r] = __builtin_amdgcn_alignbit(pf_b[r], pf_b[r], rot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v8h lo, hi;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            lo[r] = (_Float16)(float)(int8_t)byte_of(d[r], e);
+            hi[r] = (_Float16)(float)(int8_t)byte_of(d[8 + r], e);
+          }
+          _Float16* dst = s.qBh + (n4 * 4 + ((e + n4) & 3)) * kXwRow + ub * 16;
+          *reinterpret_cast<v8h*>(dst) = lo;
+          *reinterpret_cast<v8h*>(dst + 8) = hi;
+        }
+      }
     }
-    // this chunk's delta and x codes (steps past the sequence are zero)
+    // this chunk's delta and x codes (steps past the sequence were loaded as zero)
     float dt[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dt[k] = (4 * lane + k < q) ? pf_dt[k] : 0.0f;
+    for (int k = 0; k < 4; ++k) dt[k] = pf_dt[k];
     uint32_t xc[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xc[r] = ((lt / 16) * 16 + r < q) ? pf_x[r] : 0u;
+    for (int r = 0; r < 16; ++r) xc[r] = pf_x[r];
     if (c + 1 < p.nc) {
-      fetch_b(p, b, g, c + 1, tid, nx_b);
-      fetch_x(p, b, h, c + 1, lt, nx_dt, nx_x);
+      fetch_b(p, rsb, g, c + 1, tid, nx_b);
+      fetch_x(p, rsx, rsd, h, c + 1, lt, nx_dt, nx_x);
     }
     // the state entering chunk c, C-scaled fp16, in K2's operand order (after the next chunk's
     // loads, so that waiting for those does not wait for these stores)
     {
-      _Float16* dst = p.Hh + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN);
+      // a wave-uniform base and 32-bit lane offsets (no 64-bit addresses held in registers)
+      char* const dst = reinterpret_cast<char*>(p.Hh) + ((b * p.nc + c) * p.nh + h) * (int64_t)(kP * kN * 2);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -294,7 +340,8 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
 #pragma unroll
           for (int m = 0; m < 8; ++m) o[m] = (_Float16)(sC[kb] * H[pt][8 * kb + m]);
           const int ks = 2 * w + kb;
-          __builtin_nontemporal_store(o, reinterpret_cast<v8h*>(dst + ((pt * 8 + ks) * 64 + lane) * 8));
+          __builtin_nontemporal_store(
+              o, reinterpret_cast<v8h*>(dst + (uint32_t)(((pt * 8 + ks) * 64 + lane) * 16)));
         }
     }
 
@@ -304,7 +351,7 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
     // wave then publishes the weights of its own 64 steps (the rows of its part of the x tile) in
     // its own LDS slice and writes their cumulative sums for K2.
     const bool own = (lane >> 4) == w;  // lanes 16 w .. 16 w + 15 hold this wave's steps
-    float* const cw = p.cumw + ((b * p.nc + c) * p.nh + h) * kQ + 4 * lane;
+    char* const cw = reinterpret_cast<char*>(p.cumw) + ((b * p.nc + c) * p.nh + h) * (int64_t)(kQ * 4);
     float dec, wmax_f = 1.0f;
     if (I8) {
       // weights and requantization ratios in fp64 (delta * A is exact there)
@@ -334,8 +381,8 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
         double* rt = s.ratio + hs * kQ + 4 * lane;
 #pragma unroll
         for (int k = 0; k < 4; ++k) rt[k] = (wmax > 0.0) ? wj[k] / wmax : 0.0;
-        *reinterpret_cast<float4*>(cw) =
-            make_float4((float)cs[0], (float)cs[1], (float)cs[2], (float)cs[3]);
+        __builtin_nontemporal_store(v4f{(float)cs[0], (float)cs[1], (float)cs[2], (float)cs[3]},
+                                    reinterpret_cast<v4f*>(cw + (uint32_t)(lane * 16)));
       }
       dec = (float)exp(tot);
       wmax_f = (float)wmax;
@@ -359,8 +406,8 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
           cs[k] += excl;
           wv[k] = dt[k] * expf(tot - cs[k]);
         }
-        typedef float v4f __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(v4f{cs[0], cs[1], cs[2], cs[3]}, reinterpret_cast<v4f*>(cw));
+        __builtin_nontemporal_store(v4f{cs[0], cs[1], cs[2], cs[3]},
+                                    reinterpret_cast<v4f*>(cw + (uint32_t)(lane * 16)));
       }
       dec = expf(tot);
     }
@@ -435,7 +482,7 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
 #pragma unroll
       for (int ks = 0; ks < kQ / 16; ++ks) {
         const int ko = ks * 16 + 8 * kh;
-        const v8h av = i8x8_to_h(*reinterpret_cast<const int64_t*>(s.qBT + nrow * kRow256 + ko));
+        const v8h av = *reinterpret_cast<const v8h*>(s.qBh + nrow * kXwRow + ko);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
           const v8h bv = *reinterpret_cast<const v8h*>(xw + (pt * 32 + (lane & 31)) * kXwRow + ko);
@@ -852,7 +899,6 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
     // row scale exp(cum_i), column scale 1 / sx[p] (the intra part accumulates raw x codes);
     // register r holds row i = 32 I + 4 (lane / 32) + 8 (r / 4) + r % 4
     {
-      typedef float v4f __attribute__((ext_vector_type(4)));
       float er[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1127,6 +1173,11 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
                 "the library implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
   if (L > ((int64_t)1 << 40)) return fail(QSSM_ERR_UNSUPPORTED, "seqlen too large");
   if (nh > (1 << 14)) return fail(QSSM_ERR_UNSUPPORTED, "nheads too large");
+  // the state kernel addresses one sequence's x and B codes and deltas with 32-bit offsets
+  // (whole chunks: the entering states of one sequence take nc * 256 * nh * 64 bytes)
+  const int64_t Lc = (L + kQ - 1) / kQ * kQ;
+  if (Lc * nh * kP >= ((int64_t)1 << 31) || Lc * a->ngroups * kN >= ((int64_t)1 << 31))
+    return fail(QSSM_ERR_UNSUPPORTED, "one sequence's x or B codes exceed 2^31 bytes");
   if (B == 0) return QSSM_OK;
   // the per-step buffers are not touched when L == 0 and may then be null
   if (!a->x_group_of || !a->x_scales || !a->A || !a->B_scales || !a->C_scales ||
