@@ -48,6 +48,8 @@ constexpr int kNSG = kN / kGS;
 constexpr int kRow256 = 272;  // padded bytes of a [*][256] int8 LDS row
 constexpr int kRow128 = 136;  // padded bytes of a [*][128] int8 LDS row
 constexpr int kXtRow = 260;   // padded halves of a [*][256] fp16 LDS row (520 bytes)
+constexpr int kSlotsA = 5;    // causal tiles of the waves of the first half (fp16 intra product)
+constexpr int kSlotsB = 4;    // causal tiles of the waves of the second half
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 constexpr int kYPolicy = 2;  // cache policy of the y stores: nontemporal (streaming)
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued through the builtin, not
@@ -520,7 +522,12 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
 // ---------------------------------------------------------------------------------------------
 // K2: chunk outputs.
 struct K2Smem {
-  int8_t qB[kQ * kRow128];  // B chunk rows [j][n]
+  union {
+    int8_t qB[kQ * kRow128];  // B chunk rows [j][n] (prologue only)
+    // fp16 intra-chunk product: the partial outputs that wave s (s < 4) computes for query block
+    // 7 - s, handed to wave s + 4 (after the prologue)
+    float part[4][2 * 16 * 64];
+  };
   int8_t qC[kQ * kRow128];  // C chunk rows [i][n]
   // x codes of the head, [p][j]: fp16 (exact) for the fp16 intra-chunk product, int8 rows of
   // kRow256 bytes for the int8 one
@@ -749,15 +756,24 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   const int64_t t0 = c * kQ;
   const int q = (int)((p.L - t0) < kQ ? (p.L - t0) : kQ);
 
-  // B and C chunk rows of group g (zero past the sequence), 8-byte LDS stores
-  if (tid < kQ) {
-    const int j = tid;
-    const int64_t* bsrc = reinterpret_cast<const int64_t*>(p.Bq + ((b * p.L + t0 + j) * p.Gbc + g) * kN);
-    const int64_t* csrc = reinterpret_cast<const int64_t*>(p.Cq + ((b * p.L + t0 + j) * p.Gbc + g) * kN);
+  // B and C chunk rows of group g (zero past the sequence): all eight waves, eight 16-byte loads
+  // per thread issued together (rows clamped into the sequence), then masked and stored to LDS
+  {
+    uint4 v[8];
 #pragma unroll
-    for (int k = 0; k < kN / 8; ++k) {
-      *reinterpret_cast<int64_t*>(s.qB + j * kRow128 + 8 * k) = (j < q) ? bsrc[k] : 0;
-      *reinterpret_cast<int64_t*>(s.qC + j * kRow128 + 8 * k) = (j < q) ? csrc[k] : 0;
+    for (int m = 0; m < 8; ++m) {
+      const int row = (tid >> 3) + 64 * (m & 3), c16 = tid & 7;
+      const int8_t* src = (m < 4 ? p.Bq : p.Cq) +
+                          ((b * p.L + t0 + min(row, q - 1)) * p.Gbc + g) * kN + c16 * 16;
+      v[m] = *reinterpret_cast<const uint4*>(src);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int row = (tid >> 3) + 64 * (m & 3), c16 = tid & 7;
+      const bool on = row < q;
+      int8_t* dst = (m < 4 ? s.qB : s.qC) + row * kRow128 + c16 * 16;
+      *reinterpret_cast<uint2*>(dst) = on ? make_uint2(v[m].x, v[m].y) : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(dst + 8) = on ? make_uint2(v[m].z, v[m].w) : make_uint2(0u, 0u);
     }
   }
   float sBC[kNSG];  // sB * sC per state group (wave-uniform)
@@ -768,17 +784,33 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
   // the first head's inputs load while G is built
   stage_head(p, s, b, c, t0, q, (int64_t)g * p.hpg, 0, uniform(tid >> 6), tid & 63);
 
+  // G tiles held by this wave. int8 intra-chunk product: the tiles (I, J <= I) of the wave's own
+  // query block I. fp16 product: the 9 causal tiles of the two blocks s and 7 - s on one SIMD
+  // (waves s and s + 4) are split 5 + 4, so that both waves carry the same work: wave s takes
+  // tile slots k = 0..4 = (s, 0..s) then (7 - s, 0..3 - s); wave s + 4 takes (7 - s, 4 - s + k)
+  // for k = 0..3, and adds wave s's partial sums for block 7 - s before its output.
   GTile G[8];
   {
     const int lane = tid & 63;
     const int v = uniform(tid >> 6);
     const int I = v < 4 ? v : 11 - v;
 #pragma unroll
-    for (int J = 0; J < 8; ++J) {
-      if (J <= I) {
-        v16f Gf;
-        build_g_tile(Gf, s, sBC, I, J, lane);
-        G[J] = pack_g(Gf);
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (I8I) {
+        if (k <= I) {
+          v16f Gf;
+          build_g_tile(Gf, s, sBC, I, k, lane);
+          G[k] = pack_g(Gf);
+        }
+      } else if (k < kSlotsA) {
+        const int sw = v & 3;
+        if (k < (v < 4 ? kSlotsA : kSlotsB)) {
+          const int Ik = v < 4 ? (k <= sw ? sw : 7 - sw) : 7 - sw;
+          const int Jk = v < 4 ? (k <= sw ? k : k - sw - 1) : 4 - sw + k;
+          v16f Gf;
+          build_g_tile(Gf, s, sBC, Ik, Jk, lane);
+          G[k] = pack_g(Gf);
+        }
       }
       tile_fence();
     }
@@ -803,10 +835,133 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
 
   const int rs = (int)(p.nh * kP);  // row stride of y in elements
   const bool full = q == kQ;
+  // a head's output values, computed at its end and stored after the next head's first barrier
+  float yv[2][16], ep_mult[2], ep_sy[2] = {}, ep_yb[2] = {};
+  auto finish = [&](int hprev) {
+    const int lane = tid & 63;
+    const int v = uniform(tid >> 6);
+    const int I = v < 4 ? v : 11 - v;
+    if constexpr (!I8I) {
+      if (v >= 4) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            yv[pt][r] = fmaf(ep_mult[pt], s.part[v & 3][(pt * 16 + r) * 64 + lane], yv[pt][r]);
+      }
+    }
+    const int64_t base = ((b * p.L + t0) * p.nh + (int64_t)g * p.hpg + hprev) * kP;  // y[b, t0, h, 0]
+    // register r holds row 32 I + 8 (r / 4) + r % 4 + 4 (lane / 32): buffer stores with the head's
+    // y block as the resource, a per-register wave-uniform row offset (soffset) and one per-lane
+    // offset, so the stores need no per-lane 64-bit address arithmetic (all offsets fit 32 bits:
+    // nheads <= 2^14 is checked on the host)
+    const int ilane = 4 * (lane >> 5);
+    const int esz = p.yi8 ? 1 : (p.yf16 ? 2 : 4);
+    const uint64_t ya = reinterpret_cast<uint64_t>(static_cast<char*>(p.y) + base * esz);
+    void* const yblk = reinterpret_cast<void*>(
+        ((uint64_t)(uint32_t)uniform((int)(ya >> 32)) << 32) | (uint32_t)uniform((int)ya));
+    const __amdgpu_buffer_rsrc_t yrs =
+        __builtin_amdgcn_make_buffer_rsrc(yblk, (short)0, 0x7FFFFFFF, kBufferWord3);
+    if (!p.yf16 && !p.yi8) {
+      // fp32: each store of a wave writes two full 128-byte lines (rows i and i + 4, 32 channels)
+      // (a whole chunk stores with no per-row test: one branch per head instead of one per store)
+      if (full) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const int voff = (ilane * rs + pt * 32 + (lane & 31)) * 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[pt][r]), yrs,
+                                                  voff, uniform(ir * rs * 4), kYPolicy);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const int voff = (ilane * rs + pt * 32 + (lane & 31)) * 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+            if (ir + ilane < q)
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[pt][r]),
+                                                    yrs, voff, uniform(ir * rs * 4), kYPolicy);
+          }
+        }
+      }
+    } else {
+      // fp16 or int8: neighbouring lanes trade one value so that each holds two adjacent channels
+      // of one row: an even lane channels (c, c + 1) of the first 32, an odd lane (32 + c - 1,
+      // 32 + c); one store of a wave then writes rows i and i + 4 whole (64 channels each)
+      const bool odd = lane & 1;
+      const int c0 = lane & 31;
+      const int col = odd ? 32 + c0 - 1 : c0;
+      const int voff = (ilane * rs + col) * esz;
+      uint32_t v0[16], v1[16];  // the element of each tile as bits (fp16 or int8 code)
+      if (p.yi8) {
+        // persistent int8 output: fl32(y + correction term) quantized with the channel's static
+        // output scale by the exact rule (an invalid scale gives 0)
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const float sy = ep_sy[pt];
+          const float ry = recip_or_zero(sy);
+          const float yb = ep_yb[pt];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t cd = (uint8_t)quant8_r(yv[pt][r] + yb, sy, ry);
+            if (pt == 0) v0[r] = cd; else v1[r] = cd;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v0[r] = __builtin_bit_cast(unsigned short, __float2half_rn(yv[0][r]));
+          v1[r] = __builtin_bit_cast(unsigned short, __float2half_rn(yv[1][r]));
+        }
+      }
+      const int shift = p.yi8 ? 8 : 16;
+      uint32_t pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // DPP quad permutation [1, 0, 3, 2]: the value of the neighbouring lane
+        const uint32_t send = odd ? v0[r] : v1[r];
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+        pr[r] = odd ? (recv | (v1[r] << shift)) : (v0[r] | (recv << shift));
+      }
+      // (a whole chunk stores with no per-row test, as above)
+      if (full && p.yi8) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)pr[r], yrs, voff,
+                                                uniform((I * 32 + 8 * (r / 4) + (r % 4)) * rs),
+                                                kYPolicy);
+      } else if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(pr[r], yrs, voff,
+                                                uniform((I * 32 + 8 * (r / 4) + (r % 4)) * rs * 2),
+                                                kYPolicy);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
+          if (ir + ilane < q) {
+            if (p.yi8)
+              __builtin_amdgcn_raw_buffer_store_b16((unsigned short)pr[r], yrs, voff,
+                                                    uniform(ir * rs), kYPolicy);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(pr[r], yrs, voff, uniform(ir * rs * 2),
+                                                    kYPolicy);
+          }
+        }
+      }
+    }
+  };
   for (int hh = 0; hh < p.hpg; ++hh) {
     const int64_t h = (int64_t)g * p.hpg + hh;
     // every wave has waited for its own staging loads of head h and is done with head h - 1
     lds_barrier();
+    if (hh > 0) finish(hh - 1);
     // decay terms of head h
     if (tid < kQ) {
       const int j = tid;
@@ -915,24 +1070,46 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       }
     }
     if constexpr (!I8I) {
-      // Y_intra on top, tile by tile
+      // Y_intra on top, tile slot by tile slot (see the prologue for the assignment); wave s < 4
+      // accumulates its slots past s, the tiles of block 7 - s, into Yp
+      const int sw = v & 3;
+      const bool wa = v < 4;
+      v16f Yp[2] = {};
 #pragma unroll
-      for (int J = 0; J < 8; ++J) {
+      for (int k = 0; k < kSlotsA; ++k) {
         tile_fence();
-        if (J <= I) {
+        if (k < (wa ? kSlotsA : kSlotsB)) {
+          const bool own = !wa || k <= sw;
+          const int Ik = wa ? (k <= sw ? sw : 7 - sw) : 7 - sw;
+          const int Jk = wa ? (k <= sw ? k : k - sw - 1) : 4 - sw + k;
           // opaque per head: keeps the fp32 widening of the G tile inside the head loop
           // (hoisted, the widened copies of all tiles would stay live and spill)
-          __asm__ volatile("" : "+v"(G[J].lo), "+v"(G[J].hi));
+          __asm__ volatile("" : "+v"(G[k].lo), "+v"(G[k].hi));
           v8h a0, a1;
-          m_tile(G[J], s, I, J, lane, a0, a1);
+          m_tile(G[k], s, Ik, Jk, lane, a0, a1);
 #pragma unroll
           for (int pt = 0; pt < 2; ++pt) {
-            const v8h b0 = x_operand(s, J, 0, pt, lane);
-            const v8h b1 = x_operand(s, J, 1, pt, lane);
-            Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[pt], 0, 0, 0);
-            Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[pt], 0, 0, 0);
+            const v8h b0 = x_operand(s, Jk, 0, pt, lane);
+            const v8h b1 = x_operand(s, Jk, 1, pt, lane);
+            if (own) {
+              Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Y[pt], 0, 0, 0);
+              Y[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Y[pt], 0, 0, 0);
+            } else {
+              Yp[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, Yp[pt], 0, 0, 0);
+              Yp[pt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, Yp[pt], 0, 0, 0);
+            }
           }
         }
+      }
+      tile_fence();
+      // hand wave s's partial sums for block 7 - s to wave s + 4, which adds them after the next
+      // barrier (the area is free: wave s + 4 read the previous head's before this head's second
+      // barrier)
+      if (wa) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s.part[sw][(pt * 16 + r) * 64 + lane] = Yp[pt][r];
       }
     } else {
       // opaque per head, as above
@@ -998,106 +1175,47 @@ __global__ __launch_bounds__(512) void k_ssd_output(SsdParams p) {
       }
     }
     tile_fence();
-    // the staging loads were issued long before; waiting here keeps the y stores below out of
-    // the count waited for at the next head's start
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    // y = sx * acc + D * xh; rows past the sequence (ragged last chunk) are not stored
-    const float Dh = s.dh;
-    const int64_t base = ((b * p.L + t0) * p.nh + h) * kP;  // y[b, t0, h, 0]
-    float yv[2][16];
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      const int pc = pt * 32 + (lane & 31);
-      const float sx = s.sxs[pc];
-      const float mult = (sx > 0.0f) ? sx : 1.0f;
-      const float Dsx = Dh * sx;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float xc[4];
-        if constexpr (I8I) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(s.xT8 + pc * kRow256 + I * 32 + 4 * (lane >> 5) + 8 * q);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) xc[k] = (float)(int8_t)byte_of(w, k);
-        } else {
-          const v4h x4 = *reinterpret_cast<const v4h*>(s.xT + pc * kXtRow + I * 32 + 4 * (lane >> 5) + 8 * q);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) xc[k] = (float)x4[k];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) yv[pt][4 * q + k] = fmaf(Dsx, xc[k], mult * Y[pt][4 * q + k]);
-      }
-    }
-    // register r holds row 32 I + 8 (r / 4) + r % 4 + 4 (lane / 32): buffer stores with the head's
-    // y block as the resource, a per-register wave-uniform row offset (soffset) and one per-lane
-    // offset, so the stores need no per-lane 64-bit address arithmetic (all offsets fit 32 bits:
-    // nheads <= 2^14 is checked on the host)
-    const int ilane = 4 * (lane >> 5);
-    const int esz = p.yi8 ? 1 : (p.yf16 ? 2 : 4);
-    const uint64_t ya = reinterpret_cast<uint64_t>(static_cast<char*>(p.y) + base * esz);
-    void* const yblk = reinterpret_cast<void*>(
-        ((uint64_t)(uint32_t)uniform((int)(ya >> 32)) << 32) | (uint32_t)uniform((int)ya));
-    const __amdgpu_buffer_rsrc_t yrs =
-        __builtin_amdgcn_make_buffer_rsrc(yblk, (short)0, 0x7FFFFFFF, kBufferWord3);
-    if (!p.yf16 && !p.yi8) {
-      // fp32: each store of a wave writes two full 128-byte lines (rows i and i + 4, 32 channels)
+    // y = sx * acc + D * xh, from this head's LDS values (the next head rewrites them); wave
+    // s + 4 of the fp16 path adds wave s's partial sums (times sx) after the next barrier, and
+    // every wave stores its rows there
+    {
+      const float Dh = s.dh;
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        const int voff = (ilane * rs + pt * 32 + (lane & 31)) * 4;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-          if (full || ir + ilane < q)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, yv[pt][r]), yrs,
-                                                  voff, uniform(ir * rs * 4), kYPolicy);
+        const int pc = pt * 32 + (lane & 31);
+        const float sx = s.sxs[pc];
+        const float mult = (sx > 0.0f) ? sx : 1.0f;
+        const float Dsx = Dh * sx;
+        ep_mult[pt] = mult;
+        if (p.yi8) {
+          ep_sy[pt] = s.sys[pc];
+          ep_yb[pt] = s.syb[pc];
         }
-      }
-    } else {
-      // fp16 or int8: neighbouring lanes trade one value so that each holds two adjacent channels
-      // of one row: an even lane channels (c, c + 1) of the first 32, an odd lane (32 + c - 1,
-      // 32 + c); one store of a wave then writes rows i and i + 4 whole (64 channels each)
-      const bool odd = lane & 1;
-      const int c0 = lane & 31;
-      const int col = odd ? 32 + c0 - 1 : c0;
-      const int voff = (ilane * rs + col) * esz;
-      uint32_t v0[16], v1[16];  // the element of each tile as bits (fp16 or int8 code)
-      if (p.yi8) {
-        // persistent int8 output: fl32(y + correction term) quantized with the channel's static
-        // output scale by the exact rule (an invalid scale gives 0)
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const float sy = s.sys[pt * 32 + c0];
-          const float ry = recip_or_zero(sy);
-          const float yb = s.syb[pt * 32 + c0];
+        for (int q = 0; q < 4; ++q) {
+          float xc[4];
+          if constexpr (I8I) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(s.xT8 + pc * kRow256 + I * 32 + 4 * (lane >> 5) + 8 * q);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t cd = (uint8_t)quant8_r(yv[pt][r] + yb, sy, ry);
-            if (pt == 0) v0[r] = cd; else v1[r] = cd;
+            for (int k = 0; k < 4; ++k) xc[k] = (float)(int8_t)byte_of(w, k);
+          } else {
+            const v4h x4 = *reinterpret_cast<const v4h*>(s.xT + pc * kXtRow + I * 32 + 4 * (lane >> 5) + 8 * q);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) xc[k] = (float)x4[k];
           }
-        }
-      } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v0[r] = __builtin_bit_cast(unsigned short, __float2half_rn(yv[0][r]));
-          v1[r] = __builtin_bit_cast(unsigned short, __float2half_rn(yv[1][r]));
-        }
-      }
-      const int shift = p.yi8 ? 8 : 16;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // DPP quad permutation [1, 0, 3, 2]: the value of the neighbouring lane
-        const uint32_t send = odd ? v0[r] : v1[r];
-        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-        const uint32_t pair = odd ? (recv | (v1[r] << shift)) : (v0[r] | (recv << shift));
-        const int ir = I * 32 + 8 * (r / 4) + (r % 4);
-        if (full || ir + ilane < q) {
-          if (p.yi8)
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)pair, yrs, voff, uniform(ir * rs),
-                                                  kYPolicy);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(pair, yrs, voff, uniform(ir * rs * 2), kYPolicy);
+          for (int k = 0; k < 4; ++k) yv[pt][4 * q + k] = fmaf(Dsx, xc[k], mult * Y[pt][4 * q + k]);
         }
       }
     }
+    // the staging loads were issued long before; waiting here keeps the y stores out of the count
+    // waited for at the next head's start
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  }
+  // the last head's output
+  if (p.hpg > 0) {
+    lds_barrier();
+    finish(p.hpg - 1);
   }
 }
 
