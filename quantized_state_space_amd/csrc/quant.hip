@@ -18,14 +18,17 @@ using namespace qssm;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunks = 2;        // chunks of 4 elements per thread
-constexpr int kBlockElems = kThreads * kChunks * 4;
 constexpr int kMaxLdsGroups = 1024;
 constexpr int kDecVec = 16;       // elements per thread of the soft-edge decoder
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Op { OP_QUANT = 0, OP_ABSMAX = 1, OP_SOFTEDGE = 2 };
+// Chunks of 4 elements per thread: two for the int8 quantizer and the absmax pass, four for the
+// soft-edge encoder, whose longer per-value arithmetic needs more values in flight per thread
+// (measured on the Mamba1-130M x: int8 fastest with two, soft-edge with four).
+template <int OP>
+constexpr int chunks_of() { return OP == OP_SOFTEDGE ? 4 : 2; }
 enum Map { MAP_GROUP = 0, MAP_STATE = 1 };
 // Work split: thread t of block x handles chunks k = 0..kChunks-1 of 4 consecutive elements at
 // e = x * kBlockElems + (k * kThreads + t) * 4, so that every load and store instruction of a
@@ -150,18 +153,17 @@ __device__ __forceinline__ uint32_t quant4(f32x4 v, const float (&s)[4], const f
 __device__ __forceinline__ uint32_t softedge4(f32x4 v, const float (&s)[4], const float (&r)[4],
                                               const float (&Lt)[4], const float (&Ht)[4], float m,
                                               float im) {
-  float ss[4], f[4], c[4], hi[4];
-  uint32_t tag[4];
+  float f[4], c[4];
+  bool sm[4], lg[4];
   bool any = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float a = fabsf(v[i]);
     const bool small = a < Lt[i], large = a > Ht[i];
-    const bool sm = small && !large, lg = large && !small;
-    ss[i] = sm ? im * s[i] : (lg ? m * s[i] : s[i]);
-    const float rr = sm ? m * r[i] : (lg ? im * r[i] : r[i]);
-    tag[i] = sm ? 0x80u : (lg ? 0xC0u : 0u);
-    hi[i] = (sm || lg) ? 31.0f : 63.0f;
+    sm[i] = small && !large;
+    lg[i] = large && !small;
+    // the mode's reciprocal unit; the unit itself is only needed near a rounding boundary
+    const float rr = sm[i] ? m * r[i] : (lg[i] ? im * r[i] : r[i]);
     f[i] = __builtin_amdgcn_fmed3f(v[i] * rr, -256.0f, 256.0f);
     c[i] = rintf(f[i]);
     any |= fabsf(f[i] - c[i]) > 0.5f - 0x1p-14f;
@@ -171,8 +173,9 @@ __device__ __forceinline__ uint32_t softedge4(f32x4 v, const float (&s)[4], cons
     for (int i = 0; i < 4; ++i) {
       const float t = f[i] - c[i];
       if (fabsf(t) > 0.5f - 0x1p-14f) {
+        const float ss = sm[i] ? im * s[i] : (lg[i] ? m * s[i] : s[i]);
         const float h = copysignf(0.5f, t);
-        const float e = fmaf(-(c[i] + h), ss[i], v[i]);
+        const float e = fmaf(-(c[i] + h), ss, v[i]);
         const float eh = (h > 0.0f) ? e : -e;
         const bool odd = (c[i] * 0.5f) != rintf(c[i] * 0.5f);
         if (eh > 0.0f || (eh == 0.0f && odd)) c[i] += h + h;
@@ -182,8 +185,12 @@ __device__ __forceinline__ uint32_t softedge4(f32x4 v, const float (&s)[4], cons
   uint32_t word = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int q = (int)__builtin_amdgcn_fmed3f(c[i], -hi[i] - 1.0f, hi[i]);
-    const uint32_t b = tag[i] | ((uint32_t)q & (tag[i] ? 0x3Fu : 0x7Fu));
+    // payload: 7-bit two's complement in [-64, 63] (standard), 6-bit in [-32, 31] under the mode
+    // bits 10 (small) or 11 (large); the integer clamp is one med3
+    const bool md = sm[i] || lg[i];
+    const int lim = md ? 31 : 63;
+    const int q = min(max((int)c[i], ~lim), lim);
+    const uint32_t b = ((uint32_t)q & (uint32_t)(2 * lim + 1)) | (md ? (lg[i] ? 0xC0u : 0x80u) : 0u);
     word |= ((r[i] != 0.0f && v[i] == v[i]) ? b : 0u) << (8 * i);
   }
   return word;
@@ -208,6 +215,8 @@ __global__ __launch_bounds__(kThreads) void k_elementwise(
   };
   constexpr bool kUniform = Chunk<MAP, LAYOUT>::kUniform;
   constexpr bool kStepped = LAYOUT != L_GENERIC;
+  constexpr int kChunks = chunks_of<OP>();
+  constexpr int64_t kBlockElems = (int64_t)kThreads * kChunks * 4;
   Chunk<MAP, LAYOUT> ch[kChunks];
   int64_t e[kChunks];
   // position of the thread's first chunk; later chunks step by kStride elements
@@ -425,7 +434,7 @@ int choose_layout(const Geometry& g) {
 template <int OP, int MAP, int LAYOUT>
 void launch_elementwise(const float* x, const Geometry& g, const float* scales, const float* L,
                         const float* H, void* out, hipStream_t st) {
-  const unsigned blocks = (unsigned)cdiv(g.total, (int64_t)kBlockElems);
+  const unsigned blocks = (unsigned)cdiv(g.total, (int64_t)kThreads * chunks_of<OP>() * 4);
   if (g.nscales <= kMaxLdsGroups)
     k_elementwise<OP, MAP, LAYOUT, true><<<blocks, kThreads, 0, st>>>(x, g, scales, L, H, out);
   else
