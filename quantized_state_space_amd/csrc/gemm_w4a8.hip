@@ -26,6 +26,7 @@ using namespace qssm;
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int64_t kWideMinM = 1024;  // tokens from which the wide-tile form is used
 constexpr int kARow = 80;  // padded bytes of an activation row in LDS (64 + 16): no bank conflicts
 constexpr int kWRow = 40;  // padded bytes of a packed weight row in LDS (32 + 8)
 
@@ -192,6 +193,147 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(GemmParams p) {
   }
 }
 
+// Large-M form (one weight scale per output channel): 128 x 256 tiles of y, four waves each
+// owning a 64 x 128 block (2 x 4 tiles of v_mfma_i32_32x32x32_i8, 16 MFMAs per K step of 64), and
+// the global loads run two K steps ahead of the products (two register sets; the LDS stages are
+// double-buffered), so that a load's latency is covered by two steps of products. The tiles are
+// ordered in groups of 8 row tiles (row tile fastest) and the order is cut into 8 contiguous
+// ranges, one per XCD (workgroups are dealt to the XCDs in turn), so that the workgroups that run
+// together on one XCD share their A rows and weight columns in that XCD's L2.
+constexpr int kBN2 = 256;
+
+struct GemmSmem2 {
+  int8_t a[2][kBM * kARow];
+  int8_t w[2][kBN2 * kARow];  // weight codes times 16, unpacked once per step: rows of 64 + 16 bytes
+};
+
+struct Stage2 {
+  uint4 a[2], w[2];
+};
+
+// K step kt: thread t takes A chunks c = t, t + 256 (row c / 4, 16 bytes at 16 (c % 4)) and
+// weight chunks c = t, t + 256 (row c / 2, 16 packed bytes at 16 (c % 2)); rows past M or N load
+// a valid row and are zeroed by the store.
+__device__ __forceinline__ void load2(const GemmParams& p, int64_t m0, int64_t n0, int64_t kt,
+                                      int tid, Stage2& st) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    const int64_t m = min(m0 + (c >> 2), p.M - 1);
+    st.a[i] = *reinterpret_cast<const uint4*>(p.a + m * p.K + kt * kBK + (c & 3) * 16);
+    const int64_t n = min(n0 + (c >> 1), p.N - 1);
+    st.w[i] = *reinterpret_cast<const uint4*>(p.w + n * (p.K / 2) + kt * (kBK / 2) + (c & 1) * 16);
+  }
+}
+
+// Stores a K step into LDS stage buf: the A chunks as they are, the weight chunks unpacked (16
+// packed bytes -> 32 code bytes, 32 k in order); an interior tile stores without masks.
+__device__ __forceinline__ void store2(const GemmParams& p, GemmSmem2& s, int buf, int64_t m0,
+                                       int64_t n0, bool interior, int tid, const Stage2& st) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    uint4 av = st.a[i], wv = st.w[i];
+    if (!interior) {
+      av = masked(av, m0 + (c >> 2) < p.M);
+      wv = masked(wv, n0 + (c >> 1) < p.N);
+    }
+    *reinterpret_cast<uint4*>(s.a[buf] + (c >> 2) * kARow + (c & 3) * 16) = av;
+    const v4i lo = unpack16(make_uint2(wv.x, wv.y)), hi = unpack16(make_uint2(wv.z, wv.w));
+    int8_t* wd = s.w[buf] + (c >> 1) * kARow + (c & 1) * 32;
+    *reinterpret_cast<v4i*>(wd) = lo;
+    *reinterpret_cast<v4i*>(wd + 16) = hi;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_gemm_w4a8_wide(GemmParams p) {
+  __shared__ __align__(16) GemmSmem2 s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kh = lane >> 5;
+  // tile of this workgroup
+  const int64_t nm = (p.M + kBM - 1) / kBM, nn = (p.N + kBN2 - 1) / kBN2, T = nm * nn;
+  int64_t id = blockIdx.x;
+  if (T % 8 == 0) id = (id % 8) * (T / 8) + id / 8;
+  constexpr int64_t kGM = 8;
+  const int64_t grp = id / (kGM * nn), fm = grp * kGM;
+  const int64_t gsz = min(nm - fm, kGM), within = id - grp * kGM * nn;
+  const int64_t m0 = (fm + within % gsz) * kBM, n0 = (within / gsz) * kBN2;
+  const int64_t nk = p.K / kBK;
+  const bool interior = m0 + kBM <= p.M && n0 + kBN2 <= p.N;
+  const float sa = p.a_scale[0];
+  const float sa16 = scale_ok(sa) ? sa * 0.0625f : 0.0f;
+
+  v16i acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = v16i{};
+
+  Stage2 st[2];
+  load2(p, m0, n0, 0, tid, st[0]);
+  load2(p, m0, n0, min((int64_t)1, nk - 1), tid, st[1]);
+  store2(p, s, 0, m0, n0, interior, tid, st[0]);
+  load2(p, m0, n0, min((int64_t)2, nk - 1), tid, st[0]);
+  __syncthreads();
+  // one K step: the products from LDS stage kt % 2, then step kt + 1 (loaded two steps ago, held
+  // in nx) into the other stage and step kt + 3 into the registers it leaves free
+  auto step = [&](int64_t kt, Stage2& nx) {
+    const int buf = (int)(kt & 1);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      v4i av[2], bv[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        av[mt] = *reinterpret_cast<const v4i*>(s.a[buf] + (wm * 64 + mt * 32 + (lane & 31)) * kARow +
+                                               ks * 32 + 16 * kh);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bv[nt] = *reinterpret_cast<const v4i*>(s.w[buf] + (wn * 128 + nt * 32 + (lane & 31)) * kARow +
+                                               ks * 32 + 16 * kh);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+    }
+    // unconditional, so that the compiler's wait for these registers stays exact (the last steps
+    // store into the unused stage and reload the last step)
+    store2(p, s, buf ^ 1, m0, n0, interior, tid, nx);
+    load2(p, m0, n0, min(kt + 3, nk - 1), tid, nx);
+    __syncthreads();
+  };
+  // the loop is unrolled twice so that the register sets are named statically (step kt + 1 lives
+  // in st[1] when kt is even, in st[0] when it is odd)
+  // (nk is even here: the host takes this form only for K % 128 == 0)
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    step(kt, st[1]);
+    step(kt + 1, st[0]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the reloads of the last steps have landed
+
+  // y = bias + (sa / 16) sw[n] acc; register r of a tile holds row 8 (r / 4) + 4 (l / 32) + r % 4,
+  // column l % 32
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int64_t n = n0 + wn * 128 + nt * 32 + (lane & 31);
+    if (n >= p.N) continue;
+    const float bn = p.bias ? p.bias[n] : 0.0f;
+    const float f = group_scale(p, n, 1, 0, sa16);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + mt * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+        if (m >= p.M) continue;
+        const float v = fmaf(f, (float)acc[mt][nt][r], bn);
+        if (p.yf16) reinterpret_cast<__half*>(p.y)[m * p.N + n] = __float2half_rn(v);
+        else reinterpret_cast<float*>(p.y)[m * p.N + n] = v;
+      }
+  }
+}
+
 }  // namespace
 
 extern "C" qssm_status qssm_gemm_w4a8(const qssm_gemm_args* a, hipStream_t stream) {
@@ -215,7 +357,12 @@ extern "C" qssm_status qssm_gemm_w4a8(const qssm_gemm_args* a, hipStream_t strea
   GemmParams p{M, N, K, a->group, a->y_dtype == QSSM_F16, a->a, a->a_scale, a->w, a->w_scales,
                a->bias, a->y};
   const dim3 grid((unsigned)gx, (unsigned)gy);
-  if (a->group == K) k_gemm_w4a8<false><<<grid, 256, 0, stream>>>(p);
+  // the wide-tile form for many tokens with one scale per output channel (enough tiles to fill the
+  // GPU), the 128 x 128 form otherwise
+  const int64_t wide_tiles = gy * ((N + kBN2 - 1) / kBN2);
+  if (a->group == K && M >= kWideMinM && K % (2 * kBK) == 0 && wide_tiles <= 0x7fffffff)
+    k_gemm_w4a8_wide<<<(unsigned)wide_tiles, 256, 0, stream>>>(p);
+  else if (a->group == K) k_gemm_w4a8<false><<<grid, 256, 0, stream>>>(p);
   else k_gemm_w4a8<true><<<grid, 256, 0, stream>>>(p);
   return launch_status("gemm_w4a8");
 }
