@@ -1009,7 +1009,10 @@ def main():
                 others[name] = e
                 del w2
                 torch.cuda.empty_cache()
+                print(f"[bench] {name}: {r2['ms_per_step']:.4f} ms/step", file=sys.stderr,
+                      flush=True)
             others["quantizers"] = quantizer_row(torch, dev)
+            print("[bench] quantizers done", file=sys.stderr, flush=True)
             others["instruction_rates"] = probe_row(torch, dev)
             out["other_configs"] = others
     except ParityError as e:
