@@ -652,10 +652,10 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, digest of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c4": (481827754, 696427690, "17c7d36516d2b93e"),
-    "c4f16": (480146005, 427851946, "17c7d36516d2b93e"),
-    "c4i8y": (481443413, 293958741, "17c7d36516d2b93e"),
-    "c4i8i": (480359808, 696290176, "17c7d36516d2b93e"),
+    "c4": (481139626, 696865152, "e4a8a68b6b467f30"),
+    "c4f16": (479848704, 427872554, "e4a8a68b6b467f30"),
+    "c4i8y": (481101738, 294114346, "e4a8a68b6b467f30"),
+    "c4i8i": (480848853, 696924842, "e4a8a68b6b467f30"),
     "c3": (153177301, 134756394, "3cdf3e90c9d61e8b"),
     "c3se": (156280789, 134674357, "3cdf3e90c9d61e8b"),
     "c3i8y": (135517269, 27820032, "3cdf3e90c9d61e8b"),
@@ -663,8 +663,9 @@ TRAFFIC = {
     "c2i16": (391168, 6947200, "8dbafe7953cbf0db"),
     "c5": (1100235776, 1082524586, "3f9c130349ee8131"),
     "c5f16": (563252224, 545275178, "3f9c130349ee8131"),
-    "w4a8p": (6501291690, 1216348202, "91846fb4969f6afb"),
+    "w4a8p": (1861543850, 1216348160, "1908ecb0d4d416c2"),
     "c1": (1788928, 221184, "3cdf3e90c9d61e8b"),
+    "w4a8d": (84992213, 19005440, "1908ecb0d4d416c2"),
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],
