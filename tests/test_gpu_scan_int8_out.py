@@ -59,19 +59,26 @@ def check_codes_vs_oracle(got, y64, group_of, scales, bias):
     assert np.count_nonzero(near) < 0.01 * got.size
 
 
-@pytest.mark.parametrize("B,D,L,N,G,gs,Gy,spread", [(2, 128, 300, 16, 4, 4, 4, (1.0, 0.5)),
-                                                    (1, 64, 77, 4, 2, 4, 1, (1.0,)),
-                                                    (2, 192, 64, 8, 5, 4, 3, (0.3, 1.0, 1.0)),
-                                                    (1, 128, 200, 64, 4, 8, 2, (1.0, 0.7)),
-                                                    (1, 70, 99, 16, 3, 1, 2, (1.0,))])
-def test_int8_output_vs_oracle(dev, B, D, L, N, G, gs, Gy, spread):
+@pytest.mark.parametrize("B,D,L,N,G,gs,Gy,spread,soft",
+                         [(2, 128, 300, 16, 4, 4, 4, (1.0, 0.5), False),
+                          (1, 64, 77, 4, 2, 4, 1, (1.0,), False),
+                          (2, 192, 64, 8, 5, 4, 3, (0.3, 1.0, 1.0), False),
+                          (1, 128, 200, 64, 4, 8, 2, (1.0, 0.7), False),
+                          (1, 70, 99, 16, 3, 1, 2, (1.0,), False),
+                          # soft-edge x with the int8 output: eight waves of states (N = 64, the
+                          # largest LDS use), ragged lengths and channel counts
+                          (1, 128, 77, 64, 4, 8, 2, (1.0, 0.7), True),
+                          (2, 70, 300, 32, 3, 4, 2, (1.0,), True)])
+def test_int8_output_vs_oracle(dev, B, D, L, N, G, gs, Gy, spread, soft):
     import torch
-    print(f"\n[mamba1 int8 y B={B} D={D} L={L} N={N} Gy={Gy}]", flush=True)
+    import quantized_state_space_amd as qs
+    print(f"\n[mamba1 int8 y B={B} D={D} L={L} N={N} Gy={Gy} softedge={soft}]", flush=True)
     inp = synth.mamba1_inputs(cfg=31, batch=B, seqlen=L, dim=D, dstate=N, x_dist="student_t",
                               calib_batch=1, with_h0=True)
-    ref = op.mamba1(inp, G=G, gs=gs, with_h0=True)
+    ref = op.mamba1(inp, G=G, gs=gs, soft_edge=soft, with_h0=True)
     yg, ys, yb = y_calib(ref["y"], Gy, 31, spread)
-    lay = layer(dev, inp, G=G, gs=gs, with_h0=True, y_out=(yg, ys, yb))
+    lay = layer(dev, inp, G=G, gs=gs, with_h0=True, y_out=(yg, ys, yb),
+                x_code=qs.QSSM_X_SOFTEDGE if soft else qs.QSSM_X_INT8)
     lay.step()
     torch.cuda.synchronize()
     assert lay.y.dtype == torch.int8

@@ -43,7 +43,8 @@ def oracle_ref(inp, group, bias=True, rows=None):
                                                   # the wide-tile form (M >= 1024, one scale per
                                                   # output channel): ragged row and column tiles
                                                   (1100, 300, 256, 256, True, False),
-                                                  (1030, 520, 512, 512, False, True)])
+                                                  (1030, 520, 512, 512, False, True),
+                                                  (77, 130, 512, 512, True, True)])
 def test_w4a8_small(dev, M, N, K, group, bias, f16):
     print(f"\n[w4a8 M={M} N={N} K={K} group={group} bias={bias} f16={f16}]", flush=True)
     inp, lay = run(dev, M, N, K, group, 61, bias, f16)
