@@ -652,10 +652,10 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA, MI355X
 # the ratio the same counter reads for a plain 1 GiB device copy (bench.py --copy-probe). Keyed by
 # workload: (fetch bytes, write bytes, digest of the kernel sources when the counters were taken).
 TRAFFIC = {
-    "c4": (481139626, 696865152, "e4a8a68b6b467f30"),
-    "c4f16": (479848704, 427872554, "e4a8a68b6b467f30"),
-    "c4i8y": (481101738, 294114346, "e4a8a68b6b467f30"),
-    "c4i8i": (480848853, 696924842, "e4a8a68b6b467f30"),
+    "c4": (480808192, 696804650, "19659ed6fdd72e73"),
+    "c4f16": (479886421, 427856938, "19659ed6fdd72e73"),
+    "c4i8y": (481114794, 294124373, "19659ed6fdd72e73"),
+    "c4i8i": (480786346, 696856277, "19659ed6fdd72e73"),
     "c3": (153177301, 134756394, "3cdf3e90c9d61e8b"),
     "c3se": (156280789, 134674357, "3cdf3e90c9d61e8b"),
     "c3i8y": (135517269, 27820032, "3cdf3e90c9d61e8b"),

@@ -315,7 +315,9 @@ qssm_status qssm_s4d_scan(const qssm_s4d_args* a, hipStream_t stream);
  *   s = y_scales[y_group_of[h*P + p]]
  * by the quantization rule above, where y is the fp32 value the QSSM_F32 output would hold. The y_*
  * fields are read only for QSSM_I8.
- * Requires chunk == 256, P == 64, N == 128, gs == 16 in this version (else QSSM_ERR_UNSUPPORTED).
+ * Requires chunk == 256, P == 64, N == 128, gs == 16 in this version (else QSSM_ERR_UNSUPPORTED),
+ * and Lc * nh * P < 2^31 and Lc * ngroups * N < 2^31 with Lc = seqlen rounded up to a multiple of
+ * 256, plus 256 (one sequence's codes are addressed with 32-bit offsets; else QSSM_ERR_UNSUPPORTED).
  * seqlen == 0 is valid: xq, delta, Bq, Cq and y are then not accessed (they may be NULL) and
  * h_last receives h0 (or zeros).
  */

@@ -63,6 +63,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 struct SsdParams {
   int64_t B, L, nh, nc;
@@ -111,13 +112,14 @@ __device__ __forceinline__ v8h i8x8_to_h(int64_t v) {
 }
 
 
-// 16 dwords (row r holds 4 bytes, columns 0..3) -> column e as 16 bytes (rows 0..15).
-__device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
-  uint4 o;
-  o.x = byte_of(d[0], e) | byte_of(d[1], e) << 8 | byte_of(d[2], e) << 16 | byte_of(d[3], e) << 24;
-  o.y = byte_of(d[4], e) | byte_of(d[5], e) << 8 | byte_of(d[6], e) << 16 | byte_of(d[7], e) << 24;
-  o.z = byte_of(d[8], e) | byte_of(d[9], e) << 8 | byte_of(d[10], e) << 16 | byte_of(d[11], e) << 24;
-  o.w = byte_of(d[12], e) | byte_of(d[13], e) << 8 | byte_of(d[14], e) << 16 | byte_of(d[15], e) << 24;
+// 8 rows of 8 bytes (d[r] holds row r) -> column e (0..7) as 8 bytes (rows 0..7).
+__device__ __forceinline__ uint2 column8(const v2u (&d)[8], int e) {
+  const int k = e >> 2, b = e & 3;
+  uint2 o;
+  o.x = byte_of(d[0][k], b) | byte_of(d[1][k], b) << 8 | byte_of(d[2][k], b) << 16 |
+        byte_of(d[3][k], b) << 24;
+  o.y = byte_of(d[4][k], b) | byte_of(d[5][k], b) << 8 | byte_of(d[6][k], b) << 16 |
+        byte_of(d[7][k], b) << 24;
   return o;
 }
 
@@ -139,9 +141,13 @@ __device__ __forceinline__ uint4 column16(const uint32_t (&d)[16], int e) {
 //   within-block order), so each (pt, ks) pair is stored as 1 KB, 16 bytes per lane.
 //   Then H = exp(cum_last) H + S (fp32, sB and sx applied as two products: their own product
 //   can leave the fp32 range while H does not).
-// Loads run one chunk ahead, into registers (B, x codes, delta), with no wait before their first
-// use; the barriers order LDS only. They go through buffer resources that end with the batch's
-// sequence, so that rows past it read as zero with no clamp or mask.
+// Loads run one chunk ahead, into registers (B and x codes as 8 rows of 8 bytes per thread, one
+// delta per thread), with no wait before their first use; the barriers order LDS only. They go
+// through buffer resources that end with the batch's sequence, so that rows past it read as zero
+// with no clamp or mask. Each step's delta is loaded once per workgroup and shared through LDS
+// (written at the end of the chunk before, read after its closing barrier): a delta load touches
+// one cache line per lane, so loading the whole chunk's deltas in every wave cost more cache
+// lookups than the B and x codes together.
 constexpr int kXwRow = 264;  // padded halves of a [*][256] fp16 LDS row (528 bytes)
 
 template <bool I8>
@@ -152,6 +158,7 @@ struct K1Smem {
   _Float16 xw[I8 ? 8 : 2 * kP * kXwRow];    // weighted x per head, [p][j] (fp16)
   double ratio[I8 ? 2 * kQ : 1];            // w_j / w_max per head (I8)
   float wv[I8 ? 1 : 2 * kQ];                // w_j per head (fp16 path)
+  float dts[2 * kQ];                        // delta of the chunk per head
   float sxp[2 * kP];                        // x scale of each channel of each head (0: invalid)
   float sh[16];
   double shd[16];
@@ -167,49 +174,46 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void* ptr, int6
 }
 
 // Register loads of the B chunk c of group g for the transposition: thread tid takes rows
-// 16 (tid / 32) .. + 15, bytes 4 (tid % 32) .. + 3. rs covers the batch's [L, Gbc, N] codes.
+// 8 (tid / 16) .. + 7, bytes 8 (tid % 16) .. + 7. rs covers the batch's [L, Gbc, N] codes.
 __device__ __forceinline__ void fetch_b(const SsdParams& p, __amdgpu_buffer_rsrc_t rs, int g,
-                                        int64_t c, int tid, uint32_t (&bq)[16]) {
-  const int ub = tid / (kN / 4), n4 = tid % (kN / 4);
+                                        int64_t c, int tid, v2u (&bq)[8]) {
+  const int ub = tid / (kN / 8), n8 = tid % (kN / 8);
   const int bstep = p.Gbc * kN;
-  int voff = ((ub * 16) * p.Gbc + g) * kN + n4 * 4;
+  int voff = ((ub * 8) * p.Gbc + g) * kN + n8 * 8;
   // opaque per call: the per-row offsets are formed here, one add each, instead of being hoisted
-  // out of the chunk loop (16 registers held across it)
+  // out of the chunk loop (8 registers held across it)
   __asm__ volatile("" : "+v"(voff));
   voff += (int)c * kQ * bstep;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    bq[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0);
+  for (int r = 0; r < 8; ++r) {
+    bq[r] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0);
     voff += bstep;
   }
 }
 
-// Register loads of one head's chunk inputs: delta of steps 4 lane .. 4 lane + 3 (every wave holds
-// the whole chunk's delta); x codes of rows 16 (lt / 16) .. + 15, bytes 4 (lt % 16) .. + 3 (lt =
-// thread index within the half). rx covers the batch's [L, nh, P] codes, rd its [L, nh] deltas.
-__device__ __forceinline__ void fetch_x(const SsdParams& p, __amdgpu_buffer_rsrc_t rx,
-                                        __amdgpu_buffer_rsrc_t rd, int64_t h, int64_t c, int lt,
-                                        float (&dt)[4], uint32_t (&x)[16]) {
-  const int t0 = (int)c * kQ;
-  const int lane = lt & 63;
+// Register load of one head's delta at step lt of chunk c (lt = thread index within the half).
+// rd covers the batch's [L, nh] deltas.
+__device__ __forceinline__ float fetch_dt(const SsdParams& p, __amdgpu_buffer_rsrc_t rd, int64_t h,
+                                          int64_t c, int lt) {
   const int nh = (int)p.nh;
-  // opaque per call, as in fetch_b
-  int doff = (4 * lane * nh + (int)h) * 4;
-  __asm__ volatile("" : "+v"(doff));
-  doff += t0 * nh * 4;
+  int doff = (lt * nh + (int)h) * 4;
+  __asm__ volatile("" : "+v"(doff));  // as in fetch_b
+  doff += (int)c * kQ * nh * 4;
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, doff, 0, 0));
+}
+
+// Register loads of one head's x codes of chunk c: rows 8 (lt / 8) .. + 7, bytes 8 (lt % 8) .. + 7.
+// rx covers the batch's [L, nh, P] codes.
+__device__ __forceinline__ void fetch_x(const SsdParams& p, __amdgpu_buffer_rsrc_t rx, int64_t h,
+                                        int64_t c, int lt, v2u (&x)[8]) {
+  const int jb = lt / 8, p8 = lt % 8;
+  const int xstep = (int)p.nh * kP;
+  int voff = (jb * 8 * (int)p.nh + (int)h) * kP + p8 * 8;
+  __asm__ volatile("" : "+v"(voff));  // as in fetch_b
+  voff += (int)c * kQ * xstep;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    dt[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, doff, 0, 0));
-    doff += nh * 4;
-  }
-  const int jb = lt / 16, p4 = lt % 16;
-  const int xstep = nh * kP;
-  int voff = (jb * 16 * nh + (int)h) * kP + p4 * 4;
-  __asm__ volatile("" : "+v"(voff));
-  voff += t0 * xstep;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    x[r] = __builtin_amdgcn_raw_buffer_load_b32(rx, voff, 0, 0);
+  for (int r = 0; r < 8; ++r) {
+    x[r] = __builtin_amdgcn_raw_buffer_load_b64(rx, voff, 0, 0);
     voff += xstep;
   }
 }
@@ -275,60 +279,50 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
   // Two register sets for the loads, swapping roles from one chunk to the next (the chunk loop is
   // unrolled twice), so that the loaded registers are never copied: a copy would wait for the
   // loads at the end of every chunk instead of at their use one chunk later.
-  float dtA[4] = {}, dtB[4] = {};
-  uint32_t xA[16], xB[16], bA[16], bB[16];
+  float dtA = 0.0f, dtB = 0.0f;
+  v2u xA[8], xB[8], bA[8], bB[8];
   const __amdgpu_buffer_rsrc_t rsb = seq_rsrc(p.Bq + b * p.L * p.Gbc * kN, p.L * p.Gbc * kN);
   const __amdgpu_buffer_rsrc_t rsx = seq_rsrc(p.xq + b * p.L * p.nh * kP, p.L * p.nh * kP);
   const __amdgpu_buffer_rsrc_t rsd = seq_rsrc(p.delta + b * p.L * p.nh, p.L * p.nh * 4);
 
   if (p.nc > 0) {
+    dtA = fetch_dt(p, rsd, h, 0, lt);
     fetch_b(p, rsb, g, 0, tid, bA);
-    fetch_x(p, rsx, rsd, h, 0, lt, dtA, xA);
+    fetch_x(p, rsx, h, 0, lt, xA);
   }
-  lds_barrier();  // s.sxp
-  auto chunk = [&](const int64_t c, const float (&pf_dt)[4], const uint32_t (&pf_x)[16],
-                   const uint32_t (&pf_b)[16], float (&nx_dt)[4], uint32_t (&nx_x)[16],
-                   uint32_t (&nx_b)[16]) {
+  s.dts[hs * kQ + lt] = dtA;
+  lds_barrier();  // s.sxp, s.dts
+  auto chunk = [&](const int64_t c, const v2u (&pf_x)[8], const v2u (&pf_b)[8], float& nx_dt,
+                   v2u (&nx_x)[8], v2u (&nx_b)[8]) {
     // B chunk, transposed to [n][j] (rows past the sequence were loaded as zero): unit tid takes
-    // rows 16 (tid / 32) .. + 15, bytes 4 (tid % 32) .. + 3. The fp16 path stores it as fp16 (the
-    // codes are exact), converted once for both heads; unit n4 writes its four columns starting
-    // at column n4 % 4, which spreads the writes of neighbouring units over the banks.
+    // rows 8 (tid / 16) .. + 7, bytes 8 (tid % 16) .. + 7. The fp16 path stores it as fp16 (the
+    // codes are exact), converted once for both heads.
     {
-      const int ub = tid / (kN / 4), n4 = tid % (kN / 4);
-      if constexpr (I8) {
+      const int ub = tid / (kN / 8), n8 = tid % (kN / 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint4*>(s.qBT + (n4 * 4 + e) * kRow256 + ub * 16) = column16(pf_b, e);
-      } else {
-        const int rot = 8 * (n4 & 3);
-        uint32_t d[16];
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (I8) {
+          *reinterpret_cast<uint2*>(s.qBT + (n8 * 8 + e) * kRow256 + ub * 8) = column8(pf_b, e);
+        } else {
+          v8h col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) d[r] = __builtin_amdgcn_alignbit(pf_b[r], pf_b[r], rot);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v8h lo, hi;
-#pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            lo[r] = (_Float16)(float)(int8_t)byte_of(d[r], e);
-            hi[r] = (_Float16)(float)(int8_t)byte_of(d[8 + r], e);
-          }
-          _Float16* dst = s.qBh + (n4 * 4 + ((e + n4) & 3)) * kXwRow + ub * 16;
-          *reinterpret_cast<v8h*>(dst) = lo;
-          *reinterpret_cast<v8h*>(dst + 8) = hi;
+          for (int r = 0; r < 8; ++r) col[r] = (_Float16)(float)(int8_t)byte_of(pf_b[r][e >> 2], e & 3);
+          *reinterpret_cast<v8h*>(s.qBh + (n8 * 8 + e) * kXwRow + ub * 8) = col;
         }
       }
     }
-    // this chunk's delta and x codes (steps past the sequence were loaded as zero)
+    // this chunk's delta of steps 4 lane .. 4 lane + 3 (steps past the sequence were loaded as zero)
     float dt[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dt[k] = pf_dt[k];
-    uint32_t xc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xc[r] = pf_x[r];
-    if (c + 1 < p.nc) {
-      fetch_b(p, rsb, g, c + 1, tid, nx_b);
-      fetch_x(p, rsx, rsd, h, c + 1, lt, nx_dt, nx_x);
+    {
+      const v4f d4 = *reinterpret_cast<const v4f*>(s.dts + hs * kQ + 4 * lane);
+      dt[0] = d4[0]; dt[1] = d4[1]; dt[2] = d4[2]; dt[3] = d4[3];
     }
+    // the next chunk's loads, also after the last chunk (rows past the sequence read as zero): a
+    // branch around them would leave the compiler's waits for this chunk's x codes counted for the
+    // path without them, i.e. waiting for most of these loads as well
+    nx_dt = fetch_dt(p, rsd, h, c + 1, lt);
+    fetch_b(p, rsb, g, c + 1, tid, nx_b);
+    fetch_x(p, rsx, h, c + 1, lt, nx_x);
     // the state entering chunk c, C-scaled fp16, in K2's operand order (after the next chunk's
     // loads, so that waiting for those does not wait for these stores)
     {
@@ -414,44 +408,43 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
       dec = expf(tot);
     }
     // weighted (or requantized) x tile of this half's head, transposed [p][j] (a channel with an
-    // invalid scale has sx = 0 and contributes nothing)
+    // invalid scale has sx = 0 and contributes nothing): unit lt takes rows 8 (lt / 8) .. + 7,
+    // channels 8 (lt % 8) .. + 7
     {
-      const int jb = lt / 16, p4 = lt % 16;
+      const int jb = lt / 8, p8 = lt % 8;
       if (I8) {
-        const double* rt = s.ratio + hs * kQ + jb * 16;
-        uint32_t d[16];
+        const double* rt = s.ratio + hs * kQ + jb * 8;
+        v2u d[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          uint32_t word = 0u;
+        for (int r = 0; r < 8; ++r) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const double v = (double)(int8_t)byte_of(xc[r], e) * rt[r];
-            const int rq = (int)fmin(fmax(rint(v), -128.0), 127.0);
-            word |= ((uint32_t)rq & 0xFFu) << (8 * e);
+          for (int k = 0; k < 2; ++k) {
+            uint32_t word = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const double v = (double)(int8_t)byte_of(pf_x[r][k], e) * rt[r];
+              const int rq = (int)fmin(fmax(rint(v), -128.0), 127.0);
+              word |= ((uint32_t)rq & 0xFFu) << (8 * e);
+            }
+            d[r][k] = word;
           }
-          d[r] = word;
         }
         int8_t* rT = s.rT + hs * (kP * kRow256);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint4*>(rT + (p4 * 4 + e) * kRow256 + jb * 16) = column16(d, e);
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint2*>(rT + (p8 * 8 + e) * kRow256 + jb * 8) = column8(d, e);
       } else {
-        const float* wv = s.wv + hs * kQ + jb * 16;
+        const v4f wlo = *reinterpret_cast<const v4f*>(s.wv + hs * kQ + jb * 8);
+        const v4f whi = *reinterpret_cast<const v4f*>(s.wv + hs * kQ + jb * 8 + 4);
+        const float wr[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
         _Float16* xw = s.xw + hs * (kP * kXwRow);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v8h lo, hi;
+        for (int e = 0; e < 8; ++e) {
+          v8h col;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            lo[r] = (_Float16)((float)(int8_t)byte_of(xc[r], e) * wv[r]);
-            hi[r] = (_Float16)((float)(int8_t)byte_of(xc[8 + r], e) * wv[8 + r]);
-          }
-          // lanes with p4 / 4 odd write the two halves in the other order: with the 528-byte rows
-          // the 64 lanes of each write then cover every bank four times (the minimum)
-          _Float16* dst = xw + (p4 * 4 + e) * kXwRow + jb * 16;
-          const bool swap = (p4 >> 2) & 1;
-          *reinterpret_cast<v8h*>(dst + (swap ? 8 : 0)) = swap ? hi : lo;
-          *reinterpret_cast<v8h*>(dst + (swap ? 0 : 8)) = swap ? lo : hi;
+          for (int r = 0; r < 8; ++r)
+            col[r] = (_Float16)((float)(int8_t)byte_of(pf_x[r][e >> 2], e & 3) * wr[r]);
+          *reinterpret_cast<v8h*>(xw + (p8 * 8 + e) * kXwRow + jb * 8) = col;
         }
       }
     }
@@ -499,11 +492,13 @@ __global__ __launch_bounds__(512) void k_ssd_state(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) H[pt][r] = fmaf(dec, H[pt][r], (acc[pt][r] * sB[r / 8]) * sx);
     }
+    // the next chunk's deltas (every wave has read this chunk's before the barrier above)
+    s.dts[hs * kQ + lt] = nx_dt;
     lds_barrier();  // qBT and the x tiles are rewritten by the next chunk
   };
   for (int64_t c = 0; c < p.nc; c += 2) {
-    chunk(c, dtA, xA, bA, dtB, xB, bB);
-    if (c + 1 < p.nc) chunk(c + 1, dtB, xB, bB, dtA, xA, bA);
+    chunk(c, xA, bA, dtB, xB, bB);
+    if (c + 1 < p.nc) chunk(c + 1, xB, bB, dtA, xA, bA);
   }
 
   if (p.h_last && active) {
@@ -1291,9 +1286,9 @@ qssm_status qssm_ssd_chunk_int8(const qssm_ssd_args* a, void* ws, size_t ws_byte
                 "the library implements chunk=256, headdim=64, dstate=128, bc_group_size=16");
   if (L > ((int64_t)1 << 40)) return fail(QSSM_ERR_UNSUPPORTED, "seqlen too large");
   if (nh > (1 << 14)) return fail(QSSM_ERR_UNSUPPORTED, "nheads too large");
-  // the state kernel addresses one sequence's x and B codes and deltas with 32-bit offsets
-  // (whole chunks: the entering states of one sequence take nc * 256 * nh * 64 bytes)
-  const int64_t Lc = (L + kQ - 1) / kQ * kQ;
+  // the state kernel addresses one sequence's x and B codes and deltas with 32-bit offsets, over
+  // whole chunks and one chunk past the last (its loads run one chunk ahead)
+  const int64_t Lc = (L + kQ - 1) / kQ * kQ + kQ;
   if (Lc * nh * kP >= ((int64_t)1 << 31) || Lc * a->ngroups * kN >= ((int64_t)1 << 31))
     return fail(QSSM_ERR_UNSUPPORTED, "one sequence's x or B codes exceed 2^31 bytes");
   if (B == 0) return QSSM_OK;

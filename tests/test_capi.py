@@ -141,6 +141,14 @@ def test_other_entry_point_argument_errors():
     sd.nheads, sd.ngroups = (1 << 14) + 2, 2
     assert lib.qssm_ssd_chunk_int8(ctypes.byref(sd), None, 0, None) == qs.QSSM_ERR_UNSUPPORTED
     assert b"nheads" in lib.qssm_last_error()
+    # the chunk-state kernel addresses one sequence's x codes with 32-bit offsets, over whole
+    # chunks plus the one its loads run ahead into: (ceil(L / 256) + 1) * 256 * nh * 64 < 2^31
+    sd.nheads, sd.ngroups, sd.batch = 1 << 14, 1, 1
+    sd.seqlen = 1537  # (7 + 1) * 256 * 2^14 * 64 = 2^31
+    assert lib.qssm_ssd_chunk_int8(ctypes.byref(sd), None, 0, None) == qs.QSSM_ERR_UNSUPPORTED
+    assert b"2^31" in lib.qssm_last_error()
+    sd.seqlen = 1536  # (6 + 1) * 256 * 2^14 * 64 < 2^31: refused later, for the null pointers
+    assert lib.qssm_ssd_chunk_int8(ctypes.byref(sd), None, 0, None) == qs.QSSM_ERR_INVALID_ARG
     # the workspace size covers the fp16 chunk states, their factors and the staged tables
     sd.nheads, sd.ngroups, sd.seqlen, sd.batch = 4, 1, 600, 2
     nc, nh = 3, 4
