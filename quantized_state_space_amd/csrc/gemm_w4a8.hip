@@ -193,6 +193,152 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(GemmParams p) {
   }
 }
 
+// Few-token form (one weight scale per output channel): BM x 128 tiles of y (BM = 64 or 128; four
+// waves, wave (wm, wn) owning a BM / 2 x 64 block), with the global loads of each K step issued
+// kDeep steps ahead (kDeep register sets, named statically by unrolling the K loop kDeep times; the
+// LDS stages stay double-buffered). With few tokens a tile's K loop is a chain of short steps (8 or
+// 4 MFMAs per wave) and a load issued one step ahead is not back in time: the loop waits out a
+// memory latency per step. The loads are unconditional (the steps past the end reload the last
+// one), so that the compiler's waits for each register set stay exact. The row tiles that share
+// weight columns run on one XCD: the tiles, row tile fastest, are cut into 8 contiguous ranges, one
+// per XCD (workgroups are dealt to the XCDs in turn; the grid is padded to a multiple of 8 and the
+// padding exits at once).
+constexpr int kDeep = 8;
+// the form's register sets allow two workgroups per CU: it is taken when all its tiles fit at once
+constexpr int64_t kDeepMaxTiles = 512;
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
+
+// Raw buffer resource over the n bytes at ptr (a kernel argument: wave-uniform); loads past n
+// bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* ptr, int64_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), (short)0, (int)n, kBufferWord3);
+}
+
+// One K step of a BM-row tile in registers: activation chunks c = tid + 256 i (row c / 4, 16 bytes
+// at 16 (c % 4)) and the weight chunk of row tid / 2 (16 packed bytes at 16 (tid % 2)).
+template <int BM>
+struct StageD {
+  uint4 a[BM / 64];
+  uint4 w;
+};
+
+// Buffer loads of K step kt, at byte offsets aoff[i] and woff of step 0. Rows past M or N lie past
+// the resources' ends and read as zero, so the stores to LDS need no mask (a mask is a select on
+// the loaded registers, which the scheduler may hoist into earlier steps together with a wait for
+// these loads).
+template <int BM>
+__device__ __forceinline__ void load_deep(__amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsw,
+                                          const int (&aoff)[BM / 64], int woff, int kt,
+                                          StageD<BM>& st) {
+#pragma unroll
+  for (int i = 0; i < BM / 64; ++i)
+    st.a[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kt * kBK, 0, 0));
+  st.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsw, woff + kt * (kBK / 2), 0, 0));
+}
+
+template <int BM>
+__device__ __forceinline__ void store_deep(GemmSmem& s, int buf, int tid, const StageD<BM>& st) {
+#pragma unroll
+  for (int i = 0; i < BM / 64; ++i) {
+    const int c = tid + 256 * i;
+    *reinterpret_cast<uint4*>(s.a[buf] + (c >> 2) * kARow + (c & 3) * 16) = st.a[i];
+  }
+  *reinterpret_cast<uint4*>(s.w[buf] + (tid >> 1) * kWRow + (tid & 1) * 16) = st.w;
+}
+
+template <int BM>
+__global__ __launch_bounds__(256) void k_gemm_w4a8_deep(GemmParams p) {
+  constexpr int MT = BM / 64;  // 32-row MFMA tiles per wave
+  __shared__ __align__(16) GemmSmem s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kh = lane >> 5;
+  const int64_t nm = (p.M + BM - 1) / BM, T = nm * ((p.N + kBN - 1) / kBN);
+  const int64_t id = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  if (id >= T) return;  // grid padding (the whole workgroup)
+  const int64_t m0 = (id % nm) * BM, n0 = (id / nm) * kBN;
+  const int nk1 = (int)(p.K / kBK) - 1;  // nk is a multiple of kDeep (host)
+  const float sa = p.a_scale[0];
+  const float sa16 = scale_ok(sa) ? sa * 0.0625f : 0.0f;
+
+  v16i acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = v16i{};
+
+  // 32-bit offsets: the host checks M * K < 2^31 and N * K / 2 < 2^31 for this form
+  const __amdgpu_buffer_rsrc_t rsa = tensor_rsrc(p.a, p.M * p.K);
+  const __amdgpu_buffer_rsrc_t rsw = tensor_rsrc(p.w, p.N * (p.K / 2));
+  int aoff[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int c = tid + 256 * i;
+    aoff[i] = (int)((m0 + (c >> 2)) * p.K) + (c & 3) * 16;
+  }
+  const int woff = (int)((n0 + (tid >> 1)) * (p.K / 2)) + (tid & 1) * 16;
+  // register set d holds K step kt with kt % kDeep == d, until it is stored to LDS
+  StageD<BM> st[kDeep];
+#pragma unroll
+  for (int d = 0; d < kDeep; ++d) load_deep<BM>(rsa, rsw, aoff, woff, min(d, nk1), st[d]);
+  store_deep<BM>(s, 0, tid, st[0]);
+  load_deep<BM>(rsa, rsw, aoff, woff, min(kDeep, nk1), st[0]);
+  __syncthreads();
+  for (int k0 = 0; k0 <= nk1; k0 += kDeep) {
+#pragma unroll
+    for (int d = 0; d < kDeep; ++d) {
+      const int kt = k0 + d;
+      const int buf = d & 1;  // kt & 1: k0 is even
+#pragma unroll
+      for (int ks = 0; ks < kBK / 32; ++ks) {
+        v4i av[MT], bv[2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          av[mt] = *reinterpret_cast<const v4i*>(
+              s.a[buf] + (wm * (BM / 2) + mt * 32 + (lane & 31)) * kARow + ks * 32 + 16 * kh);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          bv[nt] = unpack16(*reinterpret_cast<const uint2*>(
+              s.w[buf] + (wn * 64 + nt * 32 + (lane & 31)) * kWRow + ks * 16 + 8 * kh));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+      }
+      // step kt + 1 (loaded kDeep steps ago) into the other stage, then step kt + 1 + kDeep into
+      // the registers it leaves free (after the last step: an unused stage and the last step again)
+      const int nx = (d + 1) % kDeep;
+      store_deep<BM>(s, buf ^ 1, tid, st[nx]);
+      load_deep<BM>(rsa, rsw, aoff, woff, min(kt + 1 + kDeep, nk1), st[nx]);
+      __syncthreads();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the reloads of the last steps have landed
+
+  // y = bias + (sa / 16) sw[n] acc; register r of a tile holds row 8 (r / 4) + 4 (l / 32) + r % 4,
+  // column l % 32
+  const int64_t ncol0 = n0 + wn * 64 + (lane & 31);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t n = ncol0 + 32 * nt;
+    if (n >= p.N) continue;
+    const float bn = p.bias ? p.bias[n] : 0.0f;
+    const float f = group_scale(p, n, 1, 0, sa16);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * (BM / 2) + mt * 32 + 8 * (r / 4) + 4 * kh + (r % 4);
+        if (m >= p.M) continue;
+        const float v = fmaf(f, (float)acc[mt][nt][r], bn);
+        if (p.yf16) reinterpret_cast<__half*>(p.y)[m * p.N + n] = __float2half_rn(v);
+        else reinterpret_cast<float*>(p.y)[m * p.N + n] = v;
+      }
+  }
+}
+
 // Large-M form (one weight scale per output channel): 128 x 256 tiles of y, four waves each
 // owning a 64 x 128 block (2 x 4 tiles of v_mfma_i32_32x32x32_i8, 16 MFMAs per K step of 64), and
 // the global loads run two K steps ahead of the products (two register sets; the LDS stages are
@@ -357,11 +503,20 @@ extern "C" qssm_status qssm_gemm_w4a8(const qssm_gemm_args* a, hipStream_t strea
   GemmParams p{M, N, K, a->group, a->y_dtype == QSSM_F16, a->a, a->a_scale, a->w, a->w_scales,
                a->bias, a->y};
   const dim3 grid((unsigned)gx, (unsigned)gy);
-  // the wide-tile form for many tokens with one scale per output channel (enough tiles to fill the
-  // GPU), the 128 x 128 form otherwise
+  // one scale per output channel: the wide-tile form for many tokens (enough tiles to fill the
+  // GPU); for few tokens the form with loads kDeep steps ahead when K allows it and its tiles all
+  // run at once; the 128 x 128 form with one step ahead otherwise and for weight groups
   const int64_t wide_tiles = gy * ((N + kBN2 - 1) / kBN2);
+  const bool deep64 = M <= 64;  // 64-row tiles: no MFMA work on rows past M
+  const int64_t deep_tiles = gx * (deep64 ? (M + 63) / 64 : gy);
   if (a->group == K && M >= kWideMinM && K % (2 * kBK) == 0 && wide_tiles <= 0x7fffffff)
     k_gemm_w4a8_wide<<<(unsigned)wide_tiles, 256, 0, stream>>>(p);
+  else if (a->group == K && (K / kBK) % kDeep == 0 && deep_tiles <= kDeepMaxTiles &&
+           M * K < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31)) {
+    const unsigned grid_deep = (unsigned)((deep_tiles + 7) / 8 * 8);
+    if (deep64) k_gemm_w4a8_deep<64><<<grid_deep, 256, 0, stream>>>(p);
+    else k_gemm_w4a8_deep<128><<<grid_deep, 256, 0, stream>>>(p);
+  }
   else if (a->group == K) k_gemm_w4a8<false><<<grid, 256, 0, stream>>>(p);
   else k_gemm_w4a8<true><<<grid, 256, 0, stream>>>(p);
   return launch_status("gemm_w4a8");
