@@ -663,9 +663,9 @@ TRAFFIC = {
     "c2i16": (391168, 6947200, "8dbafe7953cbf0db"),
     "c5": (1100235776, 1082524586, "3f9c130349ee8131"),
     "c5f16": (563252224, 545275178, "3f9c130349ee8131"),
-    "w4a8p": (1861924266, 1216348160, "642c9b7be554802a"),
+    "w4a8p": (1861718101, 1216348160, "6fc507f8368b7514"),
     "c1": (1788928, 221184, "3cdf3e90c9d61e8b"),
-    "w4a8d": (47873920, 19005440, "642c9b7be554802a"),
+    "w4a8d": (47269290, 19005440, "6fc507f8368b7514"),
 }
 TRAFFIC_SOURCES = {
     "c1": ["scan_m1.hip"], "c3": ["scan_m1.hip"], "c3se": ["scan_m1.hip"],

@@ -193,19 +193,23 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8(GemmParams p) {
   }
 }
 
-// Few-token form (one weight scale per output channel): BM x 128 tiles of y (BM = 64 or 128; four
-// waves, wave (wm, wn) owning a BM / 2 x 64 block), with the global loads of each K step issued
-// kDeep steps ahead (kDeep register sets, named statically by unrolling the K loop kDeep times; the
-// LDS stages stay double-buffered). With few tokens a tile's K loop is a chain of short steps (8 or
-// 4 MFMAs per wave) and a load issued one step ahead is not back in time: the loop waits out a
-// memory latency per step. The loads are unconditional (the steps past the end reload the last
-// one), so that the compiler's waits for each register set stay exact. The row tiles that share
-// weight columns run on one XCD: the tiles, row tile fastest, are cut into 8 contiguous ranges, one
-// per XCD (workgroups are dealt to the XCDs in turn; the grid is padded to a multiple of 8 and the
-// padding exits at once).
-constexpr int kDeep = 8;
-// the form's register sets allow two workgroups per CU: it is taken when all its tiles fit at once
-constexpr int64_t kDeepMaxTiles = 512;
+// Few-token form (one weight scale per output channel): BM x BN tiles of y (BM = 64 or 128, BN =
+// 64 or 128; four waves, wave (wm, wn) owning a BM / 2 x BN / 2 block), K in steps of 128 through
+// double-buffered LDS (rows padded to 144 and 72 bytes), with the global loads of each step issued
+// kDeep steps ahead (kDeep register sets, named statically by unrolling the K loop kDeep times).
+// With few tokens a tile's K loop is a chain of short steps and a load issued one step ahead is
+// not back in time: the loop waits out a memory latency per step. The loads are unconditional
+// (the steps past the end reload the last one), so that the compiler's waits for each register
+// set stay exact, and they go through buffer resources that end at the tensors' ends: rows past M
+// or N read as zero, and the stores to LDS need no mask (a mask is a select on the loaded
+// registers, which the scheduler may hoist into earlier steps together with a wait for those
+// loads). The row tiles that share weight columns run on one XCD: the tiles, row tile fastest,
+// are cut into 8 contiguous ranges, one per XCD (workgroups are dealt to the XCDs in turn; the grid
+// is padded to a multiple of 8 and the padding exits at once).
+constexpr int kBKd = 128;   // K step
+constexpr int kARowD = 144;  // padded bytes of an activation row in LDS (128 + 16)
+constexpr int kWRowD = 72;   // padded bytes of a packed weight row in LDS (64 + 8)
+constexpr int kDeep = 4;     // steps the loads run ahead
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit access (gfx9)
 
 // Raw buffer resource over the n bytes at ptr (a kernel argument: wave-uniform); loads past n
@@ -214,76 +218,90 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* ptr, i
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), (short)0, (int)n, kBufferWord3);
 }
 
-// One K step of a BM-row tile in registers: activation chunks c = tid + 256 i (row c / 4, 16 bytes
-// at 16 (c % 4)) and the weight chunk of row tid / 2 (16 packed bytes at 16 (tid % 2)).
-template <int BM>
-struct StageD {
-  uint4 a[BM / 64];
-  uint4 w;
+template <int BM, int BN>
+struct GemmSmemD {
+  int8_t a[2][BM * kARowD];
+  uint8_t w[2][BN * kWRowD];
 };
 
-// Buffer loads of K step kt, at byte offsets aoff[i] and woff of step 0. Rows past M or N lie past
-// the resources' ends and read as zero, so the stores to LDS need no mask (a mask is a select on
-// the loaded registers, which the scheduler may hoist into earlier steps together with a wait for
-// these loads).
-template <int BM>
+// One K step in registers: activation chunks c = tid + 256 i (row c / 8, 16 bytes at 16 (c % 8))
+// and weight chunks c = tid + 256 i (row c / 4, 16 packed bytes at 16 (c % 4)).
+template <int BM, int BN>
+struct StageD {
+  uint4 a[BM / 32];
+  uint4 w[BN / 64];
+};
+
+// Buffer loads of K step kt, at the byte offsets aoff and woff of step 0.
+template <int BM, int BN>
 __device__ __forceinline__ void load_deep(__amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsw,
-                                          const int (&aoff)[BM / 64], int woff, int kt,
-                                          StageD<BM>& st) {
+                                          const int (&aoff)[BM / 32], const int (&woff)[BN / 64],
+                                          int kt, StageD<BM, BN>& st) {
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
-    st.a[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kt * kBK, 0, 0));
-  st.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsw, woff + kt * (kBK / 2), 0, 0));
+  for (int i = 0; i < BM / 32; ++i)
+    st.a[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsa, aoff[i] + kt * kBKd, 0, 0));
+#pragma unroll
+  for (int i = 0; i < BN / 64; ++i)
+    st.w[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsw, woff[i] + kt * (kBKd / 2), 0, 0));
 }
 
-template <int BM>
-__device__ __forceinline__ void store_deep(GemmSmem& s, int buf, int tid, const StageD<BM>& st) {
+template <int BM, int BN>
+__device__ __forceinline__ void store_deep(GemmSmemD<BM, BN>& s, int buf, int tid,
+                                           const StageD<BM, BN>& st) {
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i) {
+  for (int i = 0; i < BM / 32; ++i) {
     const int c = tid + 256 * i;
-    *reinterpret_cast<uint4*>(s.a[buf] + (c >> 2) * kARow + (c & 3) * 16) = st.a[i];
+    *reinterpret_cast<uint4*>(s.a[buf] + (c >> 3) * kARowD + (c & 7) * 16) = st.a[i];
   }
-  *reinterpret_cast<uint4*>(s.w[buf] + (tid >> 1) * kWRow + (tid & 1) * 16) = st.w;
+#pragma unroll
+  for (int i = 0; i < BN / 64; ++i) {
+    const int c = tid + 256 * i;
+    *reinterpret_cast<uint4*>(s.w[buf] + (c >> 2) * kWRowD + (c & 3) * 16) = st.w[i];
+  }
 }
 
-template <int BM>
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void k_gemm_w4a8_deep(GemmParams p) {
-  constexpr int MT = BM / 64;  // 32-row MFMA tiles per wave
-  __shared__ __align__(16) GemmSmem s;
+  constexpr int MT = BM / 64, NT = BN / 64;  // 32 x 32 MFMA tiles of a wave's block
+  __shared__ __align__(16) GemmSmemD<BM, BN> s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int kh = lane >> 5;
-  const int64_t nm = (p.M + BM - 1) / BM, T = nm * ((p.N + kBN - 1) / kBN);
+  const int64_t nm = (p.M + BM - 1) / BM, T = nm * ((p.N + BN - 1) / BN);
   const int64_t id = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   if (id >= T) return;  // grid padding (the whole workgroup)
-  const int64_t m0 = (id % nm) * BM, n0 = (id / nm) * kBN;
-  const int nk1 = (int)(p.K / kBK) - 1;  // nk is a multiple of kDeep (host)
+  const int64_t m0 = (id % nm) * BM, n0 = (id / nm) * BN;
+  const int nk1 = (int)(p.K / kBKd) - 1;  // K / kBKd is a multiple of kDeep (host)
   const float sa = p.a_scale[0];
   const float sa16 = scale_ok(sa) ? sa * 0.0625f : 0.0f;
 
-  v16i acc[MT][2];
+  v16i acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = v16i{};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v16i{};
 
   // 32-bit offsets: the host checks M * K < 2^31 and N * K / 2 < 2^31 for this form
   const __amdgpu_buffer_rsrc_t rsa = tensor_rsrc(p.a, p.M * p.K);
   const __amdgpu_buffer_rsrc_t rsw = tensor_rsrc(p.w, p.N * (p.K / 2));
-  int aoff[MT];
+  int aoff[BM / 32], woff[BN / 64];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+  for (int i = 0; i < BM / 32; ++i) {
     const int c = tid + 256 * i;
-    aoff[i] = (int)((m0 + (c >> 2)) * p.K) + (c & 3) * 16;
+    aoff[i] = (int)((m0 + (c >> 3)) * p.K) + (c & 7) * 16;
   }
-  const int woff = (int)((n0 + (tid >> 1)) * (p.K / 2)) + (tid & 1) * 16;
-  // register set d holds K step kt with kt % kDeep == d, until it is stored to LDS
-  StageD<BM> st[kDeep];
 #pragma unroll
-  for (int d = 0; d < kDeep; ++d) load_deep<BM>(rsa, rsw, aoff, woff, min(d, nk1), st[d]);
-  store_deep<BM>(s, 0, tid, st[0]);
-  load_deep<BM>(rsa, rsw, aoff, woff, min(kDeep, nk1), st[0]);
+  for (int i = 0; i < BN / 64; ++i) {
+    const int c = tid + 256 * i;
+    woff[i] = (int)((n0 + (c >> 2)) * (p.K / 2)) + (c & 3) * 16;
+  }
+  // register set d holds K step kt with kt % kDeep == d, until it is stored to LDS
+  StageD<BM, BN> st[kDeep];
+#pragma unroll
+  for (int d = 0; d < kDeep; ++d) load_deep<BM, BN>(rsa, rsw, aoff, woff, min(d, nk1), st[d]);
+  store_deep<BM, BN>(s, 0, tid, st[0]);
+  load_deep<BM, BN>(rsa, rsw, aoff, woff, min(kDeep, nk1), st[0]);
   __syncthreads();
   for (int k0 = 0; k0 <= nk1; k0 += kDeep) {
 #pragma unroll
@@ -291,27 +309,27 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8_deep(GemmParams p) {
       const int kt = k0 + d;
       const int buf = d & 1;  // kt & 1: k0 is even
 #pragma unroll
-      for (int ks = 0; ks < kBK / 32; ++ks) {
-        v4i av[MT], bv[2];
+      for (int ks = 0; ks < kBKd / 32; ++ks) {
+        v4i av[MT], bv[NT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           av[mt] = *reinterpret_cast<const v4i*>(
-              s.a[buf] + (wm * (BM / 2) + mt * 32 + (lane & 31)) * kARow + ks * 32 + 16 * kh);
+              s.a[buf] + (wm * (BM / 2) + mt * 32 + (lane & 31)) * kARowD + ks * 32 + 16 * kh);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
           bv[nt] = unpack16(*reinterpret_cast<const uint2*>(
-              s.w[buf] + (wn * 64 + nt * 32 + (lane & 31)) * kWRow + ks * 16 + 8 * kh));
+              s.w[buf] + (wn * (BN / 2) + nt * 32 + (lane & 31)) * kWRowD + ks * 16 + 8 * kh));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
             acc[mt][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
       }
       // step kt + 1 (loaded kDeep steps ago) into the other stage, then step kt + 1 + kDeep into
       // the registers it leaves free (after the last step: an unused stage and the last step again)
       const int nx = (d + 1) % kDeep;
-      store_deep<BM>(s, buf ^ 1, tid, st[nx]);
-      load_deep<BM>(rsa, rsw, aoff, woff, min(kt + 1 + kDeep, nk1), st[nx]);
+      store_deep<BM, BN>(s, buf ^ 1, tid, st[nx]);
+      load_deep<BM, BN>(rsa, rsw, aoff, woff, min(kt + 1 + kDeep, nk1), st[nx]);
       __syncthreads();
     }
   }
@@ -319,9 +337,9 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8_deep(GemmParams p) {
 
   // y = bias + (sa / 16) sw[n] acc; register r of a tile holds row 8 (r / 4) + 4 (l / 32) + r % 4,
   // column l % 32
-  const int64_t ncol0 = n0 + wn * 64 + (lane & 31);
+  const int64_t ncol0 = n0 + wn * (BN / 2) + (lane & 31);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const int64_t n = ncol0 + 32 * nt;
     if (n >= p.N) continue;
     const float bn = p.bias ? p.bias[n] : 0.0f;
@@ -337,6 +355,21 @@ __global__ __launch_bounds__(256) void k_gemm_w4a8_deep(GemmParams p) {
         else reinterpret_cast<float*>(p.y)[m * p.N + n] = v;
       }
   }
+}
+
+// Launches the few-token form with BM-row tiles: 128-column tiles when they all fit one per CU,
+// else 64-column tiles when they fit three per CU (their registers and LDS allow three), else
+// 128-column tiles when they fit two per CU (128 x 128: two per CU). Returns false when none fits.
+template <int BM>
+bool launch_deep(const GemmParams& p, hipStream_t stream) {
+  const int64_t nm = (p.M + BM - 1) / BM;
+  const int64_t t128 = nm * ((p.N + 127) / 128), t64 = nm * ((p.N + 63) / 64);
+  const auto grid = [](int64_t t) { return (unsigned)((t + 7) / 8 * 8); };
+  if (t128 <= 256) k_gemm_w4a8_deep<BM, 128><<<grid(t128), 256, 0, stream>>>(p);
+  else if (t64 <= 768) k_gemm_w4a8_deep<BM, 64><<<grid(t64), 256, 0, stream>>>(p);
+  else if (t128 <= 512) k_gemm_w4a8_deep<BM, 128><<<grid(t128), 256, 0, stream>>>(p);
+  else return false;
+  return true;
 }
 
 // Large-M form (one weight scale per output channel): 128 x 256 tiles of y, four waves each
@@ -505,19 +538,16 @@ extern "C" qssm_status qssm_gemm_w4a8(const qssm_gemm_args* a, hipStream_t strea
   const dim3 grid((unsigned)gx, (unsigned)gy);
   // one scale per output channel: the wide-tile form for many tokens (enough tiles to fill the
   // GPU); for few tokens the form with loads kDeep steps ahead when K allows it and its tiles all
-  // run at once; the 128 x 128 form with one step ahead otherwise and for weight groups
+  // run at once (64-row tiles up to 64 tokens: no MFMA work on rows past M); the 128 x 128 form
+  // with one step ahead otherwise and for weight groups
   const int64_t wide_tiles = gy * ((N + kBN2 - 1) / kBN2);
-  const bool deep64 = M <= 64;  // 64-row tiles: no MFMA work on rows past M
-  const int64_t deep_tiles = gx * (deep64 ? (M + 63) / 64 : gy);
-  if (a->group == K && M >= kWideMinM && K % (2 * kBK) == 0 && wide_tiles <= 0x7fffffff)
+  const bool deep = a->group == K && M < kWideMinM && K % (kBKd * kDeep) == 0 &&
+                    M * K < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31);
+  if (a->group == K && M >= kWideMinM && K % (2 * kBK) == 0 && wide_tiles <= 0x7fffffff) {
     k_gemm_w4a8_wide<<<(unsigned)wide_tiles, 256, 0, stream>>>(p);
-  else if (a->group == K && (K / kBK) % kDeep == 0 && deep_tiles <= kDeepMaxTiles &&
-           M * K < ((int64_t)1 << 31) && N * (K / 2) < ((int64_t)1 << 31)) {
-    const unsigned grid_deep = (unsigned)((deep_tiles + 7) / 8 * 8);
-    if (deep64) k_gemm_w4a8_deep<64><<<grid_deep, 256, 0, stream>>>(p);
-    else k_gemm_w4a8_deep<128><<<grid_deep, 256, 0, stream>>>(p);
+  } else if (!deep || !(M <= 64 ? launch_deep<64>(p, stream) : launch_deep<128>(p, stream))) {
+    if (a->group == K) k_gemm_w4a8<false><<<grid, 256, 0, stream>>>(p);
+    else k_gemm_w4a8<true><<<grid, 256, 0, stream>>>(p);
   }
-  else if (a->group == K) k_gemm_w4a8<false><<<grid, 256, 0, stream>>>(p);
-  else k_gemm_w4a8<true><<<grid, 256, 0, stream>>>(p);
   return launch_status("gemm_w4a8");
 }

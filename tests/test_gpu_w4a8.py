@@ -44,13 +44,15 @@ def oracle_ref(inp, group, bias=True, rows=None):
                                                   # output channel): ragged row and column tiles
                                                   (1100, 300, 256, 256, True, False),
                                                   (1030, 520, 512, 512, False, True),
-                                                  # the few-token form (loads eight K steps ahead):
-                                                  # 128-row tiles, then 64-row tiles (M <= 64),
-                                                  # one and two rounds of eight steps
+                                                  # the few-token form (loads four K steps of 128
+                                                  # ahead): 128-row tiles, 64-row tiles (M <= 64),
+                                                  # one and two rounds of four steps, 64-column
+                                                  # tiles (more than 256 tiles of 128 columns)
                                                   (77, 130, 512, 512, True, True),
                                                   (200, 260, 1024, 1024, True, False),
                                                   (33, 300, 512, 512, False, False),
-                                                  (64, 257, 1024, 1024, True, True)])
+                                                  (64, 257, 1024, 1024, True, True),
+                                                  (130, 16450, 512, 512, True, False)])
 def test_w4a8_small(dev, M, N, K, group, bias, f16):
     print(f"\n[w4a8 M={M} N={N} K={K} group={group} bias={bias} f16={f16}]", flush=True)
     inp, lay = run(dev, M, N, K, group, 61, bias, f16)
