@@ -64,6 +64,18 @@ def test_ssd_small(dev, L, with_h0):
     print(f"  vs the sequential scan: max row error {e:.2e}", flush=True)
 
 
+def test_ssd_odd_heads_per_group(dev):
+    """Three heads per B/C group in two groups: the second half of each group's last pair of heads
+    has no head of its own and repeats the first's work; an odd, ragged number of chunks (520
+    steps: 3 chunks, the last of 8 steps), whose next-chunk loads run past the sequence."""
+    print("\n[ssd 3 heads per group, L=520]", flush=True)
+    inp = synth.ssd_inputs(cfg=49, batch=3, seqlen=520, nheads=6, headdim=64, dstate=128,
+                           ngroups=2, calib_len=256, with_h0=True)
+    lay = run_layer(dev, inp, with_h0=True)
+    ref = op.ssd(inp, with_h0=True)
+    check(lay, ref)
+
+
 def special_case_inputs(cfg, L, with_h0, kind):
     """A = 0, so every decay factor is exactly one and w_j = delta_j. kind "const": a per-head
     constant delta, the requantization ratio w_j / w_max is exactly one and the requantized operand
